@@ -1,0 +1,163 @@
+/*
+ * CPU oracle for the Mamba-2 SSD layer scan -- TEST INFRASTRUCTURE ONLY.
+ *
+ * Only the test suite, the smoke check and the benchmark's CPU-baseline leg
+ * may load this library.  The product path (the HIP library) never calls it
+ * and shares no code, header or table with it.
+ *
+ * What it computes is the plain definition of the layer, token by token, in
+ * float64 ("Accelerating Mamba-2 with High-Performance Forward Pass Kernels in
+ * NVIDIA CUDA Tile", section "Mamba-2 architecture"; the same update is the
+ * decode step of "Optimizing Nemotron v3 Super in TensorRT-LLM", section 6.1
+ * "The SSU Math"):
+ *
+ *     h_t = exp(A_h * dt_t) * h_{t-1} + dt_t * x_t (outer) B_t      (P x N)
+ *     y_t = h_t C_t + D_h * x_t                                      (P)
+ *
+ * The output uses the updated state h_t (the diagonal of the causal mask is
+ * included).  Head h reads B and C of group h / (H / G).  The state of head h
+ * is stored [P][N] (N contiguous).  The chunked SSD form the GPU path uses is
+ * an algebraic rearrangement of exactly this recurrence, so the recurrence is
+ * the reference.
+ *
+ * Rows p of one (b, h) never interact, so the unit of work is one (b, h, p)
+ * row: an N-vector of state carried over all T tokens.  Rows are handed out
+ * to a pool of POSIX threads through an atomic counter.
+ *
+ * Inputs are float32 arrays (bf16 inputs arrive exactly upcast); the state,
+ * every product and every sum are float64, and exp is the host libm exp.
+ */
+#define _GNU_SOURCE
+#include <math.h>
+#include <pthread.h>
+#include <sched.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#include <unistd.h>
+
+typedef struct {
+    const float *x, *dt, *A, *B, *C, *D;
+    const double *init;     /* [npairs][P][N] or NULL */
+    double *y;              /* [npairs][T][P] or NULL */
+    double *fin;            /* [npairs][P][N] or NULL */
+    int64_t Bt, T, H, P, N, G;
+    const int64_t *pairs;   /* flattened b*H + h, npairs entries, or NULL = all */
+    int64_t npairs;
+    int64_t nunits;         /* npairs * P */
+    int64_t next;           /* work counter */
+} fwd_job;
+
+static void run_row(const fwd_job *j, int64_t unit, double *s)
+{
+    const int64_t pi = unit / j->P, p = unit % j->P;
+    const int64_t bh = j->pairs ? j->pairs[pi] : pi;
+    const int64_t b = bh / j->H, h = bh % j->H;
+    const int64_t hpg = j->H / j->G, g = h / hpg;
+    const int64_t T = j->T, H = j->H, P = j->P, N = j->N, G = j->G;
+    const double A = (double)j->A[h], D = (double)j->D[h];
+
+    if (j->init)
+        for (int64_t n = 0; n < N; ++n) s[n] = j->init[(pi * P + p) * N + n];
+    else
+        for (int64_t n = 0; n < N; ++n) s[n] = 0.0;
+
+    for (int64_t t = 0; t < T; ++t) {
+        const int64_t bt = b * T + t;
+        const double dt = (double)j->dt[bt * H + h];
+        const double xv = (double)j->x[(bt * H + h) * P + p];
+        const float *Bv = j->B + (bt * G + g) * N;
+        const float *Cv = j->C + (bt * G + g) * N;
+        const double alpha = exp(A * dt);
+        const double u = dt * xv;
+        double acc = 0.0;
+        for (int64_t n = 0; n < N; ++n) {
+            const double v = alpha * s[n] + u * (double)Bv[n];
+            s[n] = v;
+            acc += (double)Cv[n] * v;
+        }
+        if (j->y) j->y[(pi * T + t) * P + p] = acc + D * xv;
+    }
+    if (j->fin)
+        for (int64_t n = 0; n < N; ++n) j->fin[(pi * P + p) * N + n] = s[n];
+}
+
+static void *worker(void *arg)
+{
+    fwd_job *j = (fwd_job *)arg;
+    double *s = (double *)malloc(sizeof(double) * (size_t)j->N);
+    if (!s) return NULL;
+    for (;;) {
+        int64_t u = __atomic_fetch_add(&j->next, 1, __ATOMIC_RELAXED);
+        if (u >= j->nunits) break;
+        run_row(j, u, s);
+    }
+    free(s);
+    return NULL;
+}
+
+/* Number of host threads this process may run on (affinity mask). */
+int ssd_oracle_host_threads(void)
+{
+    cpu_set_t set;
+    if (sched_getaffinity(0, sizeof(set), &set) == 0) {
+        int c = CPU_COUNT(&set);
+        if (c > 0) return c;
+    }
+    long n = sysconf(_SC_NPROCESSORS_ONLN);
+    return n > 0 ? (int)n : 1;
+}
+
+/*
+ * Token-by-token forward over the (b, h) pairs listed in `pairs` (b*H + h;
+ * NULL = all Bt*H pairs in order).  x [Bt,T,H,P], dt [Bt,T,H], A [H],
+ * B and C [Bt,T,G,N], D [H]; init [npairs,P,N] (NULL = zeros); outputs
+ * y [npairs,T,P] and fin [npairs,P,N] (either may be NULL).  init may alias
+ * fin.  Returns the number of threads used, or a negative value on a bad
+ * argument.
+ */
+int ssd_oracle_fwd(const float *x, const float *dt, const float *A, const float *B,
+                   const float *C, const float *D, const double *init,
+                   int64_t Bt, int64_t T, int64_t H, int64_t P, int64_t N, int64_t G,
+                   const int64_t *pairs, int64_t npairs, double *y, double *fin,
+                   int nthreads)
+{
+    if (!x || !dt || !A || !B || !C || !D) return -1;
+    if (Bt < 1 || T < 0 || H < 1 || P < 1 || N < 1 || G < 1 || H % G) return -2;
+    if (!pairs) npairs = Bt * H;
+    for (int64_t i = 0; pairs && i < npairs; ++i)
+        if (pairs[i] < 0 || pairs[i] >= Bt * H) return -3;
+
+    fwd_job j = {x, dt, A, B, C, D, init, y, fin, Bt, T, H, P, N, G, pairs, npairs,
+                 npairs * P, 0};
+    if (nthreads <= 0) nthreads = ssd_oracle_host_threads();
+    if (nthreads > j.nunits) nthreads = (int)(j.nunits > 0 ? j.nunits : 1);
+
+    pthread_t *th = (pthread_t *)malloc(sizeof(pthread_t) * (size_t)nthreads);
+    if (!th) return -4;
+    int started = 0;
+    for (int i = 1; i < nthreads; ++i) {
+        if (pthread_create(&th[i], NULL, worker, &j) != 0) break;
+        ++started;
+    }
+    worker(&j);
+    for (int i = 1; i <= started; ++i) pthread_join(th[i], NULL);
+    free(th);
+    return started + 1;
+}
+
+/*
+ * One recurrent decode step ("Optimizing Nemotron v3 Super in TensorRT-LLM",
+ * section 6.1): the forward body for a single token, with the state read from
+ * and written back to `state` [npairs,P,N].  x_t [Bt,H,P], dt_t [Bt,H],
+ * B_t and C_t [Bt,G,N]; y_t [npairs,P].
+ */
+int ssd_oracle_decode(double *state, const float *x_t, const float *dt_t, const float *B_t,
+                      const float *C_t, const float *A, const float *D,
+                      int64_t Bt, int64_t H, int64_t P, int64_t N, int64_t G,
+                      const int64_t *pairs, int64_t npairs, double *y_t, int nthreads)
+{
+    if (!state) return -1;
+    return ssd_oracle_fwd(x_t, dt_t, A, B_t, C_t, D, state, Bt, 1, H, P, N, G, pairs, npairs,
+                          y_t, state, nthreads);
+}

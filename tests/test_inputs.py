@@ -1,0 +1,58 @@
+"""The seeded generator: determinism, value recipe, bf16 exactness (no GPU)."""
+
+import math
+
+import numpy as np
+
+from selective_state_space_amd import inputs as gen
+
+
+def test_deterministic_and_seed_sensitive():
+    w = gen.WORKLOADS[0]
+    a, b = gen.make_fwd(w, 0), gen.make_fwd(w, 0)
+    for k in ("x", "dt", "A", "B", "C", "D"):
+        np.testing.assert_array_equal(getattr(a, k), getattr(b, k))
+    c = gen.make_fwd(w, 1)
+    assert not np.array_equal(a.x, c.x)
+
+
+def test_value_recipe():
+    w = gen.WORKLOADS[1].with_(batch=1, seqlen=2048)
+    inp = gen.make_fwd(w, 0)
+    assert np.all(inp.A < 0) and np.all(inp.A >= -16.0001) and np.all(inp.A <= -0.9999)
+    assert np.all(inp.dt > 0)
+    q = np.quantile(inp.dt, [0.5])
+    assert 1e-3 < q[0] < 1e-1
+    assert abs(float(np.std(inp.x)) - 1.0) < 0.01
+    assert abs(float(np.std(inp.B)) * math.sqrt(128) - 1.0) < 0.02
+    assert inp.init_state is None
+
+
+def test_bf16_values_are_exact():
+    w = gen.WORKLOADS[1].with_(batch=1, seqlen=64)
+    inp = gen.make_fwd(w, 0)
+    for a in (inp.x, inp.B, inp.C):
+        assert np.all((a.view(np.uint32) & 0xFFFF) == 0)
+
+
+def test_bf16_round_nearest_even():
+    v = np.array([1.0, 1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, -2.5, 1.0 + 2 ** -9], np.float32)
+    r = gen.bf16_round(v)
+    # 1 + 2^-8 is a tie between 1 and 1 + 2^-7 -> even (1); 1 + 3*2^-8 -> 1 + 2^-6
+    np.testing.assert_array_equal(r, np.array([1.0, 1.0, 1.0 + 2 ** -6, -2.5, 1.0], np.float32))
+
+
+def test_init_state_only_where_asked():
+    w = gen.WORKLOADS[2].with_(batch=1, seqlen=256, nheads=4)
+    inp = gen.make_fwd(w, 0)
+    assert inp.init_state.shape == (1, 4, 64, 128)
+    assert abs(float(np.std(inp.init_state)) - 0.1) < 0.005
+
+
+def test_decode_steps_differ_and_repeat():
+    w = gen.WORKLOADS[4].with_(batch=2)
+    prm = gen.decode_params(w, 0)
+    s0, s0b, s1 = (gen.make_decode_step(w, k, prm) for k in (0, 0, 1))
+    np.testing.assert_array_equal(s0.x_t, s0b.x_t)
+    assert not np.array_equal(s0.x_t, s1.x_t)
+    assert s0.x_t.shape == (2, 128, 64) and s0.B_t.shape == (2, 8, 128)
