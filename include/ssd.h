@@ -1,0 +1,174 @@
+/*
+ * ssd.h -- C ABI of the MI355X (gfx950) Mamba-2 SSD layer scan library
+ * (libssd.so).
+ *
+ * The layer ("Accelerating Mamba-2 with High-Performance Forward Pass Kernels
+ * in NVIDIA CUDA Tile", section "Mamba-2 architecture"; "Optimizing Nemotron
+ * v3 Super in TensorRT-LLM", section 6.1 "The SSU Math"), per batch row b and
+ * head h, with g = h / (H / G) the head's group:
+ *
+ *     h_t = exp(A_h dt_t) h_{t-1} + dt_t x_t (outer) B_t     state [P][N]
+ *     y_t = h_t C_t + D_h x_t                                 output [P]
+ *
+ * The output uses the updated state h_t.  The forward computes this chunk by
+ * chunk (the SSD form of the same page, sections "Kernel 1" to "Kernel 3"):
+ *
+ *   chunk_cumsum   G = log2(e) * chunk-local inclusive cumsum of A dt
+ *   chunk_state    S_c = sum_j exp2(G_last - G_j) dt_j x_j (outer) B_j
+ *   state_passing  h_prev[c] = h;  h <- exp2(G_last) h + S_c
+ *   chunk_scan     y = exp2(G) C h_prev^T
+ *                      + (exp2(G_i - G_j) (C B^T)_ij dt_j [j <= i]) X + D X
+ *
+ * CONVENTIONS (every entry point)
+ *   - All tensors are dense, contiguous, row-major, in DEVICE memory owned by
+ *     the caller.  The library never allocates, frees or synchronizes.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = the default
+ *     stream) and the call returns at once.
+ *   - Arguments are validated on the host before any HIP call.  On a
+ *     validation error nothing is launched or written, and
+ *     ssd_last_error_detail() names the field and value.
+ *   - Sizes and offsets are 64-bit throughout.
+ *   - Unchecked preconditions: A <= 0, dt >= 0, all inputs finite.
+ *   - Supported instantiation: headdim P = 64; dstate N in {64, 128};
+ *     chunk_size L in {64, 128, 256}; io dtype SSD_F32 or SSD_BF16.
+ *     batch and seqlen may be 0 (nothing to compute).
+ *   - Every pointer must be 16-byte aligned.
+ *   - Results are deterministic: no floating-point atomics; reruns are
+ *     bitwise identical.
+ */
+#ifndef SSD_H
+#define SSD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    SSD_OK = 0,
+    SSD_ERR_NULL = -1,         /* a required pointer is NULL */
+    SSD_ERR_SHAPE = -2,        /* a dimension is out of range, or H % G != 0 */
+    SSD_ERR_UNSUPPORTED = -3,  /* P, N, chunk_size or dtype not instantiated */
+    SSD_ERR_ALIGN = -4,        /* a pointer is not 16-byte aligned */
+    SSD_ERR_WORKSPACE = -5,    /* workspace smaller than the queried size */
+    SSD_ERR_HIP = -6           /* a HIP launch reported an error */
+} ssd_status;
+
+/* Element type of x, B, C, y (and x_t, B_t, C_t, y_t).  dt, A, D and every
+ * state are always float32. */
+typedef enum { SSD_F32 = 0, SSD_BF16 = 1 } ssd_dtype;
+
+typedef struct {
+    int64_t batch;     /* Bt >= 0 */
+    int64_t seqlen;    /* T >= 0 (ignored by the decode step) */
+    int64_t nheads;    /* H >= 1 */
+    int64_t headdim;   /* P, must be 64 */
+    int64_t dstate;    /* N, 64 or 128 */
+    int64_t ngroups;   /* G >= 1, H % G == 0; head h uses group h / (H / G) */
+    int32_t io_dtype;  /* an ssd_dtype */
+} ssd_dims;
+
+/*
+ * Chunked forward (the whole hot path: the four stages below, in order, on
+ * `stream`).
+ *
+ *   x           [Bt, T, H, P]  io dtype      in
+ *   dt          [Bt, T, H]     float32       in   (after any softplus)
+ *   A, D        [H]            float32       in   (A natural-log decay rate)
+ *   B, C        [Bt, T, G, N]  io dtype      in
+ *   chunk_size  L in {64, 128, 256}
+ *   init_state  [Bt, H, P, N]  float32       in   NULL = zeros
+ *   y           [Bt, T, H, P]  io dtype      out
+ *   final_state [Bt, H, P, N]  float32       out  NULL = not written
+ *   workspace   ssd_chunked_fwd_workspace_size() bytes of device memory
+ *
+ * With batch or seqlen 0 the token tensors (x, dt, B, C, y) are empty and may
+ * be NULL; with seqlen 0 final_state receives init_state (or zeros).
+ *
+ * init_state may equal final_state (in-place continuation: a sequence split
+ * at a chunk boundary and run in two calls gives the state of one call);
+ * any other overlap between arguments is undefined.  T need not be a
+ * multiple of L: a ragged last chunk is computed as if padded with dt = 0.
+ */
+ssd_status ssd_chunked_fwd(const void *x, const float *dt, const float *A, const void *B,
+                           const void *C, const float *D, int64_t chunk_size,
+                           const float *init_state, void *y, float *final_state,
+                           const ssd_dims *dims, void *workspace, size_t workspace_bytes,
+                           void *stream);
+
+/* Bytes of device workspace ssd_chunked_fwd and the stage calls need
+ * (0 for an invalid or empty shape). */
+size_t ssd_chunked_fwd_workspace_size(const ssd_dims *dims, int64_t chunk_size);
+
+/*
+ * Byte offsets of the four workspace regions, so that tests can read the
+ * intermediates.  With nc = ceil(T / L):
+ *   offsets[0]  G       float32 [Bt, H, nc, L]   log2(e) * chunk-local cumsum of A dt
+ *   offsets[1]  DT      float32 [Bt, H, nc, L]   dt transposed, 0 past T
+ *   offsets[2]  S       float32 [Bt, H, nc, P, N] per-chunk states
+ *   offsets[3]  h_prev  io dtype [Bt, H, nc, P, N] state entering each chunk
+ * Each region starts on a 256-byte boundary.
+ */
+ssd_status ssd_chunked_fwd_workspace_layout(const ssd_dims *dims, int64_t chunk_size,
+                                            size_t offsets[4]);
+
+/*
+ * The four stages of ssd_chunked_fwd, callable one at a time (same
+ * arguments and workspace; each reads what the previous stage left in the
+ * workspace).  ssd_chunked_fwd is exactly these four calls in this order.
+ *
+ * chunk_cumsum: reads dt, A; writes G and DT.  One wavefront-level prefix
+ *   sum per (b, h, chunk) ("Accelerating Mamba-2 ...", section "Kernel 1").
+ * chunk_state: reads x, B, G, DT; writes S.  S_c = X^T diag(w) B with
+ *   w_j = dt_j exp2(G_last - G_j) ("Kernel 2", the jump formula with decay).
+ * state_passing: reads S, G, init_state; writes h_prev and final_state
+ *   ("Kernel 2", the sequential loop over chunks).
+ * chunk_scan: reads x, B, C, D, G, DT, h_prev; writes y ("Kernel 3").
+ */
+ssd_status ssd_chunk_cumsum(const float *dt, const float *A, int64_t chunk_size,
+                            const ssd_dims *dims, void *workspace, size_t workspace_bytes,
+                            void *stream);
+ssd_status ssd_chunk_state(const void *x, const void *B, int64_t chunk_size,
+                           const ssd_dims *dims, void *workspace, size_t workspace_bytes,
+                           void *stream);
+ssd_status ssd_state_passing(const float *init_state, float *final_state, int64_t chunk_size,
+                             const ssd_dims *dims, void *workspace, size_t workspace_bytes,
+                             void *stream);
+ssd_status ssd_chunk_scan(const void *x, const void *B, const void *C, const float *D, void *y,
+                          int64_t chunk_size, const ssd_dims *dims, void *workspace,
+                          size_t workspace_bytes, void *stream);
+
+/*
+ * One recurrent decode step ("Optimizing Nemotron v3 Super in TensorRT-LLM",
+ * section 6.1; "mamba-metal: running Mamba on Apple Silicon", section on
+ * O(L) incremental decoding): for every (b, h),
+ *     state <- exp(A_h dt_t) state + dt_t x_t (outer) B_t;  y_t = state C_t + D_h x_t
+ *
+ *   state  [Bt, H, P, N]  float32   in/out, updated in place
+ *   x_t    [Bt, H, P]     io dtype  in
+ *   dt_t   [Bt, H]        float32   in
+ *   B_t, C_t [Bt, G, N]   io dtype  in
+ *   A, D   [H]            float32   in
+ *   y_t    [Bt, H, P]     io dtype  out
+ * dims->seqlen is ignored.
+ */
+ssd_status ssd_decode_step(float *state, const void *x_t, const float *dt_t, const void *B_t,
+                           const void *C_t, const float *A, const float *D, void *y_t,
+                           const ssd_dims *dims, void *stream);
+
+/* Static text for a status code. */
+const char *ssd_status_string(ssd_status status);
+
+/* Detail of the last error returned on the calling thread ("" if none). */
+const char *ssd_last_error_detail(void);
+
+/* Library version, major * 10000 + minor * 100 + patch. */
+int ssd_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SSD_H */

@@ -1,0 +1,125 @@
+// chunk_cumsum: G = log2(e) * chunk-local inclusive prefix sum of A_h dt_t.
+//
+// "Accelerating Mamba-2 with High-Performance Forward Pass Kernels in NVIDIA
+// CUDA Tile", section "Kernel 1": the decay A*dt is summed cumulatively inside
+// each chunk only (not over the whole sequence), once, for the two later
+// stages; the sums are kept in log2 units so that later stages use exp2.  The
+// same page's performance section stores dt and the cumulative decay head
+// major, [batch, head, token], for contiguous per-head access: this kernel is
+// where that transpose happens.
+//
+// Layout: reads dt [Bt, T, H] (heads contiguous); writes G and DT, both
+// float32 [Bt, H, nc, L] (tokens contiguous).  Positions past T get dt = 0,
+// so a ragged last chunk carries its last valid G to the end of the chunk.
+//
+// One workgroup of 256 threads per (b, chunk, block of 16 heads).  dt rows of
+// 16 heads are read coalesced, transposed through LDS, and each wavefront then
+// scans 4 heads: a lane sums L/64 consecutive tokens serially, a wave-wide
+// log-depth scan (6 shuffle steps) combines the lane totals, and each lane
+// adds its exclusive prefix back.
+
+#include "ssd_device.h"
+#include "ssd_launch.h"
+
+namespace ssd {
+
+namespace {
+
+constexpr int kHeadsPerBlock = 16;
+
+template <int L>
+__global__ __launch_bounds__(256) void chunk_cumsum_kernel(
+    const float *__restrict__ dt, const float *__restrict__ A, float *__restrict__ Gws,
+    float *__restrict__ DTws, int64_t T, int32_t H, int32_t nc, int32_t nhb, uint32_t nblk) {
+    constexpr int V = L / 64;  // tokens per lane
+    __shared__ float tile[kHeadsPerBlock][L + 1];
+
+    const uint32_t lid = xcd_remap(blockIdx.x, nblk);
+    const int32_t hb = lid % nhb;
+    const int32_t c = (lid / nhb) % nc;
+    const int64_t b = lid / ((uint32_t)nhb * nc);
+    const int32_t h0 = hb * kHeadsPerBlock;
+    const int tid = threadIdx.x;
+
+    // coalesced load of dt[b, c*L + t, h0 .. h0+15]
+    {
+        const int hh = tid % kHeadsPerBlock;
+        const int h = h0 + hh;
+#pragma unroll
+        for (int k = 0; k < L / 16; ++k) {
+            const int t = tid / kHeadsPerBlock + 16 * k;
+            const int64_t tg = (int64_t)c * L + t;
+            float v = 0.f;
+            if (tg < T && h < H) v = dt[(b * T + tg) * H + h];
+            tile[hh][t] = v;
+        }
+    }
+    __syncthreads();
+
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+#pragma unroll
+    for (int k = 0; k < kHeadsPerBlock / 4; ++k) {
+        const int hh = wave + 4 * k;
+        const int h = h0 + hh;
+        if (h >= H) break;  // wave-uniform
+        const float a2 = A[h] * kLog2e;
+        float d[V], g[V];
+        float run = 0.f;
+#pragma unroll
+        for (int v = 0; v < V; ++v) {
+            d[v] = tile[hh][lane * V + v];
+            run += a2 * d[v];
+            g[v] = run;
+        }
+        // inclusive scan of the lane totals across the wavefront
+        float incl = run;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const float o = __shfl_up(incl, off, 64);
+            if (lane >= off) incl += o;
+        }
+        const float excl = incl - run;
+        const int64_t base = (((int64_t)b * H + h) * nc + c) * L + lane * V;
+        if constexpr (V == 4) {
+            *reinterpret_cast<float4 *>(Gws + base) =
+                make_float4(g[0] + excl, g[1] + excl, g[2] + excl, g[3] + excl);
+            *reinterpret_cast<float4 *>(DTws + base) = make_float4(d[0], d[1], d[2], d[3]);
+        } else if constexpr (V == 2) {
+            *reinterpret_cast<float2 *>(Gws + base) = make_float2(g[0] + excl, g[1] + excl);
+            *reinterpret_cast<float2 *>(DTws + base) = make_float2(d[0], d[1]);
+        } else {
+            Gws[base] = g[0] + excl;
+            DTws[base] = d[0];
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_chunk_cumsum(const Shape &s, const float *dt, const float *A, float *Gws,
+                               float *DTws, hipStream_t st) {
+    if (s.Bt == 0 || s.nc == 0) return hipSuccess;
+    const int32_t nhb = (int32_t)((s.H + kHeadsPerBlock - 1) / kHeadsPerBlock);
+    const uint64_t nblk = (uint64_t)s.Bt * s.nc * nhb;
+    const dim3 grid((uint32_t)nblk), block(256);
+    switch (s.L) {
+    case 64:
+        hipLaunchKernelGGL(chunk_cumsum_kernel<64>, grid, block, 0, st, dt, A, Gws, DTws, s.T,
+                           (int32_t)s.H, (int32_t)s.nc, nhb, (uint32_t)nblk);
+        break;
+    case 128:
+        hipLaunchKernelGGL(chunk_cumsum_kernel<128>, grid, block, 0, st, dt, A, Gws, DTws, s.T,
+                           (int32_t)s.H, (int32_t)s.nc, nhb, (uint32_t)nblk);
+        break;
+    case 256:
+        hipLaunchKernelGGL(chunk_cumsum_kernel<256>, grid, block, 0, st, dt, A, Gws, DTws, s.T,
+                           (int32_t)s.H, (int32_t)s.nc, nhb, (uint32_t)nblk);
+        break;
+    default:
+        return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace ssd

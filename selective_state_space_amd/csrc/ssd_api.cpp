@@ -1,0 +1,341 @@
+// C ABI of libssd.so: host-side validation, workspace layout, and the launch
+// sequence of the chunked forward (chunk_cumsum -> chunk_state ->
+// state_passing -> chunk_scan, "Accelerating Mamba-2 with High-Performance
+// Forward Pass Kernels in NVIDIA CUDA Tile", sections "Kernel 1" to "Kernel
+// 3") and of the decode step ("Optimizing Nemotron v3 Super in
+// TensorRT-LLM", section 6.1).
+//
+// Every check runs on the host before the first HIP call, so a rejected call
+// launches and writes nothing; the "mamba3" kernel card ("Requirements and
+// limits") likewise checks its requirements up front and names the figures.
+
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+
+#include "../../include/ssd.h"
+#include "ssd_launch.h"
+
+namespace {
+
+thread_local char g_detail[512] = "";
+
+ssd_status fail(ssd_status st, const char *fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_detail, sizeof(g_detail), fmt, ap);
+    va_end(ap);
+    return st;
+}
+
+ssd_status ok() {
+    g_detail[0] = '\0';
+    return SSD_OK;
+}
+
+bool debug_sync() {
+    static const int on = [] {
+        const char *e = getenv("SSD_DEBUG_SYNC");
+        return (e && e[0] && e[0] != '0') ? 1 : 0;
+    }();
+    return on != 0;
+}
+
+constexpr int64_t kMaxDim = int64_t(1) << 30;
+constexpr uint64_t kMaxGrid = (uint64_t(1) << 31) - 1;
+
+bool misaligned(const void *p) { return p && (reinterpret_cast<uintptr_t>(p) & 15u); }
+
+size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
+
+// Validates dims (and chunk_size when L > 0) and fills `s`.
+ssd_status check_dims(const ssd_dims *d, int64_t L, bool need_seq, ssd::Shape *s) {
+    if (!d) return fail(SSD_ERR_NULL, "dims is NULL");
+    if (d->batch < 0 || d->batch > kMaxDim)
+        return fail(SSD_ERR_SHAPE, "batch = %lld out of range [0, 2^30]", (long long)d->batch);
+    if (need_seq && (d->seqlen < 0 || d->seqlen > (int64_t(1) << 40)))
+        return fail(SSD_ERR_SHAPE, "seqlen = %lld out of range [0, 2^40]", (long long)d->seqlen);
+    if (d->nheads < 1 || d->nheads > kMaxDim)
+        return fail(SSD_ERR_SHAPE, "nheads = %lld must be >= 1", (long long)d->nheads);
+    if (d->ngroups < 1 || d->ngroups > d->nheads)
+        return fail(SSD_ERR_SHAPE, "ngroups = %lld must be in [1, nheads = %lld]",
+                    (long long)d->ngroups, (long long)d->nheads);
+    if (d->nheads % d->ngroups)
+        return fail(SSD_ERR_SHAPE, "nheads = %lld is not a multiple of ngroups = %lld",
+                    (long long)d->nheads, (long long)d->ngroups);
+    if (d->headdim < 1 || d->dstate < 1)
+        return fail(SSD_ERR_SHAPE, "headdim = %lld and dstate = %lld must be >= 1",
+                    (long long)d->headdim, (long long)d->dstate);
+    if (d->headdim != 64)
+        return fail(SSD_ERR_UNSUPPORTED, "headdim = %lld; only 64 is instantiated",
+                    (long long)d->headdim);
+    if (d->dstate != 64 && d->dstate != 128)
+        return fail(SSD_ERR_UNSUPPORTED, "dstate = %lld; only 64 and 128 are instantiated",
+                    (long long)d->dstate);
+    if (d->io_dtype != SSD_F32 && d->io_dtype != SSD_BF16)
+        return fail(SSD_ERR_UNSUPPORTED, "io_dtype = %d; only SSD_F32 (0) and SSD_BF16 (1)",
+                    (int)d->io_dtype);
+    if (L > 0 || need_seq) {
+        if (L != 64 && L != 128 && L != 256)
+            return fail(SSD_ERR_UNSUPPORTED, "chunk_size = %lld; only 64, 128, 256 are instantiated",
+                        (long long)L);
+    }
+    s->Bt = d->batch;
+    s->T = need_seq ? d->seqlen : 1;
+    s->H = d->nheads;
+    s->P = d->headdim;
+    s->N = d->dstate;
+    s->G = d->ngroups;
+    s->L = L > 0 ? L : 64;
+    s->nc = need_seq ? (s->T + s->L - 1) / s->L : 0;
+    s->bf16 = d->io_dtype == SSD_BF16;
+    if (s->nc > kMaxDim) return fail(SSD_ERR_SHAPE, "too many chunks (%lld)", (long long)s->nc);
+    const uint64_t grid_chunks = (uint64_t)s->Bt * (uint64_t)s->nc * (uint64_t)s->H;
+    const uint64_t grid_heads = (uint64_t)s->Bt * (uint64_t)s->H * 8u;
+    if (grid_chunks > kMaxGrid || grid_heads > kMaxGrid)
+        return fail(SSD_ERR_SHAPE, "problem too large for one launch (batch*chunks*heads = %llu)",
+                    (unsigned long long)grid_chunks);
+    return SSD_OK;
+}
+
+struct Layout {
+    size_t off[4];
+    size_t total;
+};
+
+Layout layout_of(const ssd::Shape &s) {
+    Layout l;
+    const size_t units = (size_t)s.Bt * s.H * s.nc;
+    const size_t g = units * s.L * sizeof(float);
+    const size_t st = units * s.P * s.N * sizeof(float);
+    const size_t hp = units * s.P * s.N * (s.bf16 ? 2 : 4);
+    l.off[0] = 0;
+    l.off[1] = align256(l.off[0] + g);
+    l.off[2] = align256(l.off[1] + g);
+    l.off[3] = align256(l.off[2] + st);
+    l.total = units ? align256(l.off[3] + hp) : 0;
+    return l;
+}
+
+struct Ws {
+    float *G, *DT, *S;
+    void *hprev;
+};
+
+ssd_status check_ws(const ssd::Shape &s, void *ws, size_t bytes, Ws *w) {
+    const Layout l = layout_of(s);
+    if (l.total && !ws) return fail(SSD_ERR_NULL, "workspace is NULL (%zu bytes needed)", l.total);
+    if (misaligned(ws)) return fail(SSD_ERR_ALIGN, "workspace is not 16-byte aligned");
+    if (bytes < l.total)
+        return fail(SSD_ERR_WORKSPACE, "workspace_bytes = %zu < %zu required", bytes, l.total);
+    char *base = static_cast<char *>(ws);
+    w->G = reinterpret_cast<float *>(base + l.off[0]);
+    w->DT = reinterpret_cast<float *>(base + l.off[1]);
+    w->S = reinterpret_cast<float *>(base + l.off[2]);
+    w->hprev = base + l.off[3];
+    return SSD_OK;
+}
+
+#define REQUIRE_PTR(p)                                                          \
+    do {                                                                        \
+        if (!(p)) return fail(SSD_ERR_NULL, "%s is NULL", #p);                  \
+        if (misaligned(p)) return fail(SSD_ERR_ALIGN, "%s is not 16-byte aligned", #p); \
+    } while (0)
+#define OPTIONAL_PTR(p)                                                         \
+    do {                                                                        \
+        if (misaligned(p)) return fail(SSD_ERR_ALIGN, "%s is not 16-byte aligned", #p); \
+    } while (0)
+
+ssd_status hip_result(hipError_t e, const char *what, hipStream_t st) {
+    if (e == hipSuccess && debug_sync()) {
+        e = hipStreamSynchronize(st);
+        if (e == hipSuccess) e = hipGetLastError();
+    }
+    if (e != hipSuccess) return fail(SSD_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+    return SSD_OK;
+}
+
+// Stage runners on validated arguments.
+ssd_status run_cumsum(const ssd::Shape &s, const float *dt, const float *A, const Ws &w,
+                      hipStream_t st) {
+    return hip_result(ssd::launch_chunk_cumsum(s, dt, A, w.G, w.DT, st), "chunk_cumsum", st);
+}
+ssd_status run_state(const ssd::Shape &s, const void *x, const void *B, const Ws &w,
+                     hipStream_t st) {
+    return hip_result(ssd::launch_chunk_state(s, x, B, w.G, w.DT, w.S, st), "chunk_state", st);
+}
+ssd_status run_passing(const ssd::Shape &s, const float *init, float *fin, const Ws &w,
+                       hipStream_t st) {
+    return hip_result(ssd::launch_state_passing(s, w.S, w.G, init, w.hprev, fin, st),
+                      "state_passing", st);
+}
+ssd_status run_scan(const ssd::Shape &s, const void *x, const void *B, const void *C,
+                    const float *D, void *y, const Ws &w, hipStream_t st) {
+    return hip_result(ssd::launch_chunk_scan(s, x, B, C, D, w.G, w.DT, w.hprev, y, st),
+                      "chunk_scan", st);
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t ssd_chunked_fwd_workspace_size(const ssd_dims *dims, int64_t chunk_size) {
+    ssd::Shape s;
+    if (check_dims(dims, chunk_size, true, &s) != SSD_OK) return 0;
+    return layout_of(s).total;
+}
+
+ssd_status ssd_chunked_fwd_workspace_layout(const ssd_dims *dims, int64_t chunk_size,
+                                            size_t offsets[4]) {
+    if (!offsets) return fail(SSD_ERR_NULL, "offsets is NULL");
+    ssd::Shape s;
+    const ssd_status r = check_dims(dims, chunk_size, true, &s);
+    if (r != SSD_OK) return r;
+    const Layout l = layout_of(s);
+    for (int i = 0; i < 4; ++i) offsets[i] = l.off[i];
+    return ok();
+}
+
+ssd_status ssd_chunk_cumsum(const float *dt, const float *A, int64_t chunk_size,
+                            const ssd_dims *dims, void *workspace, size_t workspace_bytes,
+                            void *stream) {
+    ssd::Shape s;
+    ssd_status r = check_dims(dims, chunk_size, true, &s);
+    if (r != SSD_OK) return r;
+    REQUIRE_PTR(dt);
+    REQUIRE_PTR(A);
+    Ws w;
+    if ((r = check_ws(s, workspace, workspace_bytes, &w)) != SSD_OK) return r;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if ((r = run_cumsum(s, dt, A, w, st)) != SSD_OK) return r;
+    return ok();
+}
+
+ssd_status ssd_chunk_state(const void *x, const void *B, int64_t chunk_size, const ssd_dims *dims,
+                           void *workspace, size_t workspace_bytes, void *stream) {
+    ssd::Shape s;
+    ssd_status r = check_dims(dims, chunk_size, true, &s);
+    if (r != SSD_OK) return r;
+    REQUIRE_PTR(x);
+    REQUIRE_PTR(B);
+    Ws w;
+    if ((r = check_ws(s, workspace, workspace_bytes, &w)) != SSD_OK) return r;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if ((r = run_state(s, x, B, w, st)) != SSD_OK) return r;
+    return ok();
+}
+
+ssd_status ssd_state_passing(const float *init_state, float *final_state, int64_t chunk_size,
+                             const ssd_dims *dims, void *workspace, size_t workspace_bytes,
+                             void *stream) {
+    ssd::Shape s;
+    ssd_status r = check_dims(dims, chunk_size, true, &s);
+    if (r != SSD_OK) return r;
+    OPTIONAL_PTR(init_state);
+    OPTIONAL_PTR(final_state);
+    Ws w;
+    if ((r = check_ws(s, workspace, workspace_bytes, &w)) != SSD_OK) return r;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if ((r = run_passing(s, init_state, final_state, w, st)) != SSD_OK) return r;
+    return ok();
+}
+
+ssd_status ssd_chunk_scan(const void *x, const void *B, const void *C, const float *D, void *y,
+                          int64_t chunk_size, const ssd_dims *dims, void *workspace,
+                          size_t workspace_bytes, void *stream) {
+    ssd::Shape s;
+    ssd_status r = check_dims(dims, chunk_size, true, &s);
+    if (r != SSD_OK) return r;
+    REQUIRE_PTR(x);
+    REQUIRE_PTR(B);
+    REQUIRE_PTR(C);
+    REQUIRE_PTR(D);
+    REQUIRE_PTR(y);
+    Ws w;
+    if ((r = check_ws(s, workspace, workspace_bytes, &w)) != SSD_OK) return r;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if ((r = run_scan(s, x, B, C, D, y, w, st)) != SSD_OK) return r;
+    return ok();
+}
+
+ssd_status ssd_chunked_fwd(const void *x, const float *dt, const float *A, const void *B,
+                           const void *C, const float *D, int64_t chunk_size,
+                           const float *init_state, void *y, float *final_state,
+                           const ssd_dims *dims, void *workspace, size_t workspace_bytes,
+                           void *stream) {
+    ssd::Shape s;
+    ssd_status r = check_dims(dims, chunk_size, true, &s);
+    if (r != SSD_OK) return r;
+    if (s.Bt > 0 && s.T > 0) {
+        REQUIRE_PTR(x);
+        REQUIRE_PTR(dt);
+        REQUIRE_PTR(A);
+        REQUIRE_PTR(B);
+        REQUIRE_PTR(C);
+        REQUIRE_PTR(D);
+        REQUIRE_PTR(y);
+    } else {  // no tokens: the token tensors are empty and may be NULL
+        OPTIONAL_PTR(x);
+        OPTIONAL_PTR(dt);
+        OPTIONAL_PTR(A);
+        OPTIONAL_PTR(B);
+        OPTIONAL_PTR(C);
+        OPTIONAL_PTR(D);
+        OPTIONAL_PTR(y);
+    }
+    OPTIONAL_PTR(init_state);
+    OPTIONAL_PTR(final_state);
+    Ws w;
+    if ((r = check_ws(s, workspace, workspace_bytes, &w)) != SSD_OK) return r;
+    if (s.Bt == 0) return ok();
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if ((r = run_cumsum(s, dt, A, w, st)) != SSD_OK) return r;
+    if ((r = run_state(s, x, B, w, st)) != SSD_OK) return r;
+    if ((r = run_passing(s, init_state, final_state, w, st)) != SSD_OK) return r;
+    if ((r = run_scan(s, x, B, C, D, y, w, st)) != SSD_OK) return r;
+    return ok();
+}
+
+ssd_status ssd_decode_step(float *state, const void *x_t, const float *dt_t, const void *B_t,
+                           const void *C_t, const float *A, const float *D, void *y_t,
+                           const ssd_dims *dims, void *stream) {
+    ssd::Shape s;
+    ssd_status r = check_dims(dims, 0, false, &s);
+    if (r != SSD_OK) return r;
+    REQUIRE_PTR(state);
+    REQUIRE_PTR(x_t);
+    REQUIRE_PTR(dt_t);
+    REQUIRE_PTR(B_t);
+    REQUIRE_PTR(C_t);
+    REQUIRE_PTR(A);
+    REQUIRE_PTR(D);
+    REQUIRE_PTR(y_t);
+    if (s.Bt == 0) return ok();
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    r = hip_result(ssd::launch_decode_step(s, state, x_t, dt_t, B_t, C_t, A, D, y_t, st),
+                   "decode_step", st);
+    if (r != SSD_OK) return r;
+    return ok();
+}
+
+const char *ssd_status_string(ssd_status status) {
+    switch (status) {
+    case SSD_OK: return "SSD_OK";
+    case SSD_ERR_NULL: return "SSD_ERR_NULL: a required pointer is NULL";
+    case SSD_ERR_SHAPE: return "SSD_ERR_SHAPE: a dimension is out of range";
+    case SSD_ERR_UNSUPPORTED: return "SSD_ERR_UNSUPPORTED: shape or dtype not instantiated";
+    case SSD_ERR_ALIGN: return "SSD_ERR_ALIGN: pointer not 16-byte aligned";
+    case SSD_ERR_WORKSPACE: return "SSD_ERR_WORKSPACE: workspace too small";
+    case SSD_ERR_HIP: return "SSD_ERR_HIP: a HIP call failed";
+    }
+    return "unknown ssd_status";
+}
+
+const char *ssd_last_error_detail(void) { return g_detail; }
+
+int ssd_version(void) { return 100; }
+
+}  // extern "C"

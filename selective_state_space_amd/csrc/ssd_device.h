@@ -1,0 +1,65 @@
+// Device-side helpers shared by the SSD kernels (gfx950 / CDNA4 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ssd {
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+// MFMA operand / accumulator registers.
+typedef short bf16x8 __attribute__((ext_vector_type(8)));  // 8 bf16, 4 VGPRs
+typedef float f32x4 __attribute__((ext_vector_type(4)));   // 16x16 accumulator slice
+
+// bf16 <-> float.  bf16 is carried as its 16-bit pattern.
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ float bf16_to_f32(uint16_t v) { return __uint_as_float((uint32_t)v << 16); }
+
+// float -> bf16 bits, round to nearest even (inputs are finite).
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+    uint32_t u = __float_as_uint(f);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+}
+
+// 2^x on the transcendental unit (v_exp_f32).
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Workgroups are dispatched round-robin over the 8 XCDs (id % 8).  Map the
+// hardware id to a logical id so that consecutive logical ids share an XCD
+// (and its L2): logical [x*per, (x+1)*per) runs on XCD x.  Ids past the last
+// multiple of 8 map to themselves.
+__device__ __forceinline__ uint32_t xcd_remap(uint32_t bid, uint32_t nblk) {
+    const uint32_t full = nblk & ~7u;
+    if (bid >= full) return bid;
+    const uint32_t per = full >> 3;
+    return (bid & 7u) * per + (bid >> 3);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) {
+    bf16x8 r;
+    __builtin_memcpy(&r, &v, sizeof(r));
+    return r;
+}
+
+__device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// Transpose helpers for building MFMA operands from row-major tiles.
+// Given two 32-bit words each holding a bf16 pair (lo = element 0, hi =
+// element 1) from two consecutive rows r0, r1, produce the word holding
+// element 0 of both rows, or element 1 of both rows.
+__device__ __forceinline__ uint32_t pair_lo(uint32_t r0, uint32_t r1) {
+    return (r0 & 0xffffu) | (r1 << 16);
+}
+__device__ __forceinline__ uint32_t pair_hi(uint32_t r0, uint32_t r1) {
+    return (r0 >> 16) | (r1 & 0xffff0000u);
+}
+
+}  // namespace ssd

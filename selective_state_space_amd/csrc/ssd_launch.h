@@ -1,0 +1,28 @@
+// Host-side launchers of the SSD kernels (internal to libssd.so).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ssd {
+
+// A validated problem shape.  P is always 64.
+struct Shape {
+    int64_t Bt, T, H, P, N, G, L, nc;  // nc = ceil(T / L)
+    bool bf16;                          // io dtype: bf16 (else float32)
+};
+
+hipError_t launch_chunk_cumsum(const Shape &s, const float *dt, const float *A, float *Gws,
+                               float *DTws, hipStream_t st);
+hipError_t launch_chunk_state(const Shape &s, const void *x, const void *B, const float *Gws,
+                              const float *DTws, float *S, hipStream_t st);
+hipError_t launch_state_passing(const Shape &s, const float *S, const float *Gws,
+                                const float *init, void *hprev, float *fin, hipStream_t st);
+hipError_t launch_chunk_scan(const Shape &s, const void *x, const void *B, const void *C,
+                             const float *D, const float *Gws, const float *DTws,
+                             const void *hprev, void *y, hipStream_t st);
+hipError_t launch_decode_step(const Shape &s, float *state, const void *x, const float *dt,
+                              const void *B, const void *C, const float *A, const float *D,
+                              void *y, hipStream_t st);
+
+}  // namespace ssd

@@ -20,15 +20,21 @@ Recipe (the shapes and value distributions of the five workloads):
 * For bf16 workloads, x, B and C are rounded once to bfloat16 on the host
   (round to nearest even); the arrays returned hold those exact values in
   float32, so an exact upcast is all either side needs.
-* Seed 0 by default; one ``numpy.random.default_rng(seed)`` per workload with
-  the fixed draw order A, D, dt_bias, x, z, B, C, h0.  Decode steps draw their
-  per-token inputs from ``default_rng([seed, step])``.
+* Seed 0 by default.  Every tensor has its own NumPy PCG64 stream keyed by
+  (seed, tensor id, block): the per-head parameters A, D, dt_bias are drawn in
+  that order from ``default_rng([seed, 0])``; the per-token tensors x, z, B, C
+  and h0 (ids 1..5) are drawn in blocks of 2^22 elements, block k from
+  ``default_rng([seed, id, k])``, so blocks can be drawn in parallel threads
+  and the values do not depend on the thread count.  Decode step s uses the
+  ids 1000 + 8 s + (1, 2, 3, 4) for its x, z, B, C.
 """
 
 from __future__ import annotations
 
+import concurrent.futures as cf
 import dataclasses
 import math
+import os
 from typing import Optional
 
 import numpy as np
@@ -102,8 +108,66 @@ def bf16_bits(a: np.ndarray) -> np.ndarray:
 
 def _softplus_thresholded(v: np.ndarray) -> np.ndarray:
     # log1p(exp(v)) for v <= 20, v itself above (input recipe, not the scan)
-    out = np.where(v > 20.0, v, np.log1p(np.exp(np.minimum(v, 20.0))))
-    return out
+    return np.where(v > 20.0, v, np.log1p(np.exp(np.minimum(v, 20.0))))
+
+
+BLOCK = 1 << 22
+_ID_X, _ID_Z, _ID_B, _ID_C, _ID_H0 = 1, 2, 3, 4, 5
+_pool = None
+
+
+def _threads() -> int:
+    try:
+        return max(1, min(16, len(os.sched_getaffinity(0))))
+    except AttributeError:  # pragma: no cover
+        return max(1, min(16, os.cpu_count() or 1))
+
+
+def _blocked(key, shape, fill) -> np.ndarray:
+    """A float32 array of `shape`; block k is written by fill(rng_k, view, start)."""
+    global _pool
+    n = int(np.prod(shape))
+    out = np.empty(n, np.float32)
+    nb = -(-n // BLOCK)
+
+    def work(k):
+        rng = np.random.default_rng(list(key) + [k])
+        fill(rng, out[k * BLOCK: min(n, (k + 1) * BLOCK)], k * BLOCK)
+
+    if nb <= 1:
+        for k in range(nb):
+            work(k)
+    else:
+        if _pool is None:
+            _pool = cf.ThreadPoolExecutor(_threads())
+        list(_pool.map(work, range(nb)))
+    return out.reshape(shape)
+
+
+def _normal(key, shape, scale: float = 1.0, bf16: bool = False) -> np.ndarray:
+    sc = np.float32(scale)
+
+    def fill(rng, v, start):
+        rng.standard_normal(out=v, dtype=np.float32)
+        if scale != 1.0:
+            np.multiply(v, sc, out=v)
+        if bf16:
+            v[:] = bf16_round(v)
+
+    return _blocked(key, shape, fill)
+
+
+def _dt(key, shape, dt_bias: np.ndarray) -> np.ndarray:
+    # dt = softplus(z + dt_bias[h]), z ~ N(0, 1); heads are the last axis
+    H = dt_bias.shape[0]
+    flat_bias = dt_bias.astype(np.float64)
+
+    def fill(rng, v, start):
+        z = rng.standard_normal(v.shape[0], dtype=np.float32).astype(np.float64)
+        h = (start + np.arange(v.shape[0])) % H     # flat index -> head
+        v[:] = _softplus_thresholded(z + flat_bias[h]).astype(np.float32)
+
+    return _blocked(key, shape, fill)
 
 
 @dataclasses.dataclass
@@ -126,7 +190,8 @@ class FwdInputs:
     init_state: Optional[np.ndarray]  # [Bt, H, P, N] float32 or None
 
 
-def _params(rng: np.random.Generator, H: int) -> Params:
+def _params(seed: int, H: int) -> Params:
+    rng = np.random.default_rng([seed, 0])
     A = (-np.exp(rng.uniform(math.log(1.0), math.log(16.0), size=H))).astype(np.float32)
     D = rng.standard_normal(H).astype(np.float32)
     dt0 = np.exp(rng.uniform(math.log(1e-3), math.log(1e-1), size=H))
@@ -134,28 +199,17 @@ def _params(rng: np.random.Generator, H: int) -> Params:
     return Params(A, D, dt_bias)
 
 
-def _draw_dt(rng: np.random.Generator, shape, dt_bias: np.ndarray) -> np.ndarray:
-    z = rng.standard_normal(shape, dtype=np.float32).astype(np.float64)
-    return _softplus_thresholded(z + dt_bias).astype(np.float32)
-
-
-def _maybe_bf16(a: np.ndarray, io_dtype: str) -> np.ndarray:
-    return bf16_round(a) if io_dtype == BF16 else np.ascontiguousarray(a, dtype=np.float32)
-
-
 def make_fwd(w: Workload, seed: int = 0) -> FwdInputs:
     """Inputs of one chunked-forward call for workload ``w``."""
     Bt, T, H, P, N, G = w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.ngroups
-    rng = np.random.default_rng(seed)
-    prm = _params(rng, H)
-    x = _maybe_bf16(rng.standard_normal((Bt, T, H, P), dtype=np.float32), w.io_dtype)
-    dt = _draw_dt(rng, (Bt, T, H), prm.dt_bias)
-    s = np.float32(1.0 / math.sqrt(N))
-    B = _maybe_bf16(rng.standard_normal((Bt, T, G, N), dtype=np.float32) * s, w.io_dtype)
-    C = _maybe_bf16(rng.standard_normal((Bt, T, G, N), dtype=np.float32) * s, w.io_dtype)
-    h0 = None
-    if w.init_state:
-        h0 = (rng.standard_normal((Bt, H, P, N), dtype=np.float32) * np.float32(0.1))
+    prm = _params(seed, H)
+    bf = w.io_dtype == BF16
+    x = _normal((seed, _ID_X), (Bt, T, H, P), bf16=bf)
+    dt = _dt((seed, _ID_Z), (Bt, T, H), prm.dt_bias)
+    s = 1.0 / math.sqrt(N)
+    B = _normal((seed, _ID_B), (Bt, T, G, N), s, bf16=bf)
+    C = _normal((seed, _ID_C), (Bt, T, G, N), s, bf16=bf)
+    h0 = _normal((seed, _ID_H0), (Bt, H, P, N), 0.1) if w.init_state else None
     return FwdInputs(x, dt, prm.A, B, C, prm.D, h0)
 
 
@@ -169,18 +223,19 @@ class DecodeInputs:
 
 def decode_params(w: Workload, seed: int = 0) -> Params:
     """A, D and dt_bias of a decode workload (shared by all its steps)."""
-    return _params(np.random.default_rng(seed), w.nheads)
+    return _params(seed, w.nheads)
 
 
 def make_decode_step(w: Workload, step: int, prm: Params, seed: int = 0) -> DecodeInputs:
     """Per-token inputs of decode step ``step`` of workload ``w``."""
     Bt, H, P, N, G = w.batch, w.nheads, w.headdim, w.dstate, w.ngroups
-    rng = np.random.default_rng([seed, step])
-    x = _maybe_bf16(rng.standard_normal((Bt, H, P), dtype=np.float32), w.io_dtype)
-    dt = _draw_dt(rng, (Bt, H), prm.dt_bias)
-    s = np.float32(1.0 / math.sqrt(N))
-    B = _maybe_bf16(rng.standard_normal((Bt, G, N), dtype=np.float32) * s, w.io_dtype)
-    C = _maybe_bf16(rng.standard_normal((Bt, G, N), dtype=np.float32) * s, w.io_dtype)
+    base = 1000 + 8 * step
+    bf = w.io_dtype == BF16
+    x = _normal((seed, base + 1), (Bt, H, P), bf16=bf)
+    dt = _dt((seed, base + 2), (Bt, H), prm.dt_bias)
+    s = 1.0 / math.sqrt(N)
+    B = _normal((seed, base + 3), (Bt, G, N), s, bf16=bf)
+    C = _normal((seed, base + 4), (Bt, G, N), s, bf16=bf)
     return DecodeInputs(x, dt, B, C)
 
 

@@ -1,0 +1,273 @@
+"""Python binding of libssd.so (ctypes).
+
+Argument marshalling only: shapes and dtypes are checked, tensors made
+contiguous, output and workspace memory allocated with torch on the input's
+device, and the C entry points of ``include/ssd.h`` called with raw device
+pointers and torch's current stream.  Every step of the computation runs in
+the HIP kernels of libssd.so; if the library is missing this module raises,
+it never falls back to another implementation.
+
+The functions carry the C names:
+
+* :func:`ssd_chunked_fwd` -- chunked forward (the four stages in order);
+* :func:`ssd_chunk_cumsum`, :func:`ssd_chunk_state`, :func:`ssd_state_passing`,
+  :func:`ssd_chunk_scan` -- the stages one at a time, on a shared workspace;
+* :func:`ssd_decode_step` -- one recurrent token, state updated in place;
+* :func:`ssd_chunked_fwd_workspace_size`, :func:`ssd_chunked_fwd_workspace_layout`.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+from typing import Optional, Tuple
+
+import torch
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libssd.so")
+HEADER = os.path.join(os.path.dirname(PKG), "include", "ssd.h")
+
+SSD_F32, SSD_BF16 = 0, 1
+STATUS = {0: "SSD_OK", -1: "SSD_ERR_NULL", -2: "SSD_ERR_SHAPE", -3: "SSD_ERR_UNSUPPORTED",
+          -4: "SSD_ERR_ALIGN", -5: "SSD_ERR_WORKSPACE", -6: "SSD_ERR_HIP"}
+
+
+class SSDError(RuntimeError):
+    """A libssd.so entry point returned a non-zero ssd_status."""
+
+    def __init__(self, fn: str, status: int, detail: str):
+        super().__init__("%s -> %s (%d): %s" % (fn, STATUS.get(status, "?"), status, detail))
+        self.status = status
+        self.detail = detail
+
+
+class Dims(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int64), ("seqlen", ctypes.c_int64),
+                ("nheads", ctypes.c_int64), ("headdim", ctypes.c_int64),
+                ("dstate", ctypes.c_int64), ("ngroups", ctypes.c_int64),
+                ("io_dtype", ctypes.c_int32)]
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Loads libssd.so (built in-tree by ``python -m selective_state_space_amd.build``)."""
+    global _lib
+    if _lib is not None and path == LIB_PATH:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError("libssd.so is not built (%s); run `python -m "
+                           "selective_state_space_amd.build` -- there is no fallback" % path)
+    lib = ctypes.CDLL(path)
+    vp, i64, sz, dp = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t, ctypes.POINTER(Dims)
+    st = ctypes.c_int
+    sig = {
+        "ssd_chunked_fwd": ([vp, vp, vp, vp, vp, vp, i64, vp, vp, vp, dp, vp, sz, vp], st),
+        "ssd_chunked_fwd_workspace_size": ([dp, i64], sz),
+        "ssd_chunked_fwd_workspace_layout": ([dp, i64, ctypes.POINTER(ctypes.c_size_t)], st),
+        "ssd_chunk_cumsum": ([vp, vp, i64, dp, vp, sz, vp], st),
+        "ssd_chunk_state": ([vp, vp, i64, dp, vp, sz, vp], st),
+        "ssd_state_passing": ([vp, vp, i64, dp, vp, sz, vp], st),
+        "ssd_chunk_scan": ([vp, vp, vp, vp, vp, i64, dp, vp, sz, vp], st),
+        "ssd_decode_step": ([vp, vp, vp, vp, vp, vp, vp, vp, dp, vp], st),
+        "ssd_status_string": ([st], ctypes.c_char_p),
+        "ssd_last_error_detail": ([], ctypes.c_char_p),
+        "ssd_version": ([], ctypes.c_int),
+    }
+    for name, (args, res) in sig.items():
+        f = getattr(lib, name)
+        f.argtypes = args
+        f.restype = res
+    if path == LIB_PATH:
+        _lib = lib
+    return lib
+
+
+def header_functions(path: str = HEADER):
+    """Names of the functions ``include/ssd.h`` declares."""
+    text = open(path).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ssd_[a-z_0-9]+)\s*\(", text)))
+
+
+def _check(fn: str, status: int):
+    if status != 0:
+        detail = load_library().ssd_last_error_detail().decode()
+        raise SSDError(fn, status, detail)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _io_code(dtype: torch.dtype) -> int:
+    if dtype == torch.float32:
+        return SSD_F32
+    if dtype == torch.bfloat16:
+        return SSD_BF16
+    raise TypeError("x, B, C must be float32 or bfloat16, got %s" % dtype)
+
+
+def _need(t: torch.Tensor, name: str, dtype: torch.dtype, shape, device) -> torch.Tensor:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if t.device != device:
+        raise ValueError("%s is on %s, expected %s" % (name, t.device, device))
+    if t.dtype != dtype:
+        raise TypeError("%s has dtype %s, expected %s" % (name, t.dtype, dtype))
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError("%s has shape %s, expected %s" % (name, tuple(t.shape), tuple(shape)))
+    return t.contiguous()
+
+
+def fwd_dims(x: torch.Tensor, B: torch.Tensor) -> Dims:
+    Bt, T, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    return Dims(Bt, T, H, P, N, G, _io_code(x.dtype))
+
+
+def ssd_chunked_fwd_workspace_size(dims: Dims, chunk_size: int) -> int:
+    return int(load_library().ssd_chunked_fwd_workspace_size(ctypes.byref(dims), chunk_size))
+
+
+def ssd_chunked_fwd_workspace_layout(dims: Dims, chunk_size: int) -> Tuple[int, int, int, int]:
+    off = (ctypes.c_size_t * 4)()
+    _check("ssd_chunked_fwd_workspace_layout",
+           load_library().ssd_chunked_fwd_workspace_layout(ctypes.byref(dims), chunk_size, off))
+    return tuple(int(v) for v in off)
+
+
+class FwdArgs:
+    """Checked, contiguous arguments of one chunked forward (shared by the stage calls)."""
+
+    def __init__(self, x, dt, A, B, C, D, chunk_size, init_state=None, y=None,
+                 final_state=None, want_final=True, workspace=None):
+        if x.dim() != 4 or B.dim() != 4:
+            raise ValueError("x must be [Bt,T,H,P] and B, C [Bt,T,G,N]")
+        dev = x.device
+        if dev.type != "cuda":
+            raise ValueError("tensors must live on a GPU device, got %s" % dev)
+        Bt, T, H, P = x.shape
+        G, N = B.shape[2], B.shape[3]
+        io = x.dtype
+        self.x = x.contiguous()
+        self.dt = _need(dt, "dt", torch.float32, (Bt, T, H), dev)
+        self.A = _need(A, "A", torch.float32, (H,), dev)
+        self.B = _need(B, "B", io, (Bt, T, G, N), dev)
+        self.C = _need(C, "C", io, (Bt, T, G, N), dev)
+        self.D = _need(D, "D", torch.float32, (H,), dev)
+        self.init = None if init_state is None else _need(init_state, "init_state", torch.float32,
+                                                         (Bt, H, P, N), dev)
+        self.y = (torch.empty_like(self.x) if y is None
+                  else _need(y, "y", io, (Bt, T, H, P), dev))
+        if final_state is not None:
+            self.final = _need(final_state, "final_state", torch.float32, (Bt, H, P, N), dev)
+        elif want_final:
+            self.final = torch.empty((Bt, H, P, N), dtype=torch.float32, device=dev)
+        else:
+            self.final = None
+        self.L = int(chunk_size)
+        self.dims = fwd_dims(self.x, self.B)
+        need = ssd_chunked_fwd_workspace_size(self.dims, self.L)
+        if workspace is None:
+            workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+        self.ws = workspace
+        self.device = dev
+
+
+def ssd_chunked_fwd(x, dt, A, B, C, D, chunk_size: int, init_state=None, y=None,
+                    final_state=None, want_final: bool = True, workspace=None):
+    """Chunked forward.  Returns (y, final_state or None).
+
+    x [Bt,T,H,P] (float32 or bfloat16), dt [Bt,T,H] f32, A/D [H] f32,
+    B/C [Bt,T,G,N] (x's dtype), init_state [Bt,H,P,N] f32 or None.  ``y``,
+    ``final_state`` and ``workspace`` may be passed in to avoid allocation;
+    ``final_state`` may be the same tensor as ``init_state``.
+    """
+    a = x if isinstance(x, FwdArgs) else FwdArgs(x, dt, A, B, C, D, chunk_size, init_state, y,
+                                                 final_state, want_final, workspace)
+    lib = load_library()
+    st = lib.ssd_chunked_fwd(_ptr(a.x), _ptr(a.dt), _ptr(a.A), _ptr(a.B), _ptr(a.C), _ptr(a.D),
+                             a.L, _ptr(a.init), _ptr(a.y), _ptr(a.final), ctypes.byref(a.dims),
+                             _ptr(a.ws), a.ws.numel(), _stream(a.device))
+    _check("ssd_chunked_fwd", st)
+    return a.y, a.final
+
+
+def ssd_chunk_cumsum(a: FwdArgs):
+    lib = load_library()
+    _check("ssd_chunk_cumsum", lib.ssd_chunk_cumsum(_ptr(a.dt), _ptr(a.A), a.L,
+                                                    ctypes.byref(a.dims), _ptr(a.ws),
+                                                    a.ws.numel(), _stream(a.device)))
+
+
+def ssd_chunk_state(a: FwdArgs):
+    lib = load_library()
+    _check("ssd_chunk_state", lib.ssd_chunk_state(_ptr(a.x), _ptr(a.B), a.L, ctypes.byref(a.dims),
+                                                  _ptr(a.ws), a.ws.numel(), _stream(a.device)))
+
+
+def ssd_state_passing(a: FwdArgs):
+    lib = load_library()
+    _check("ssd_state_passing", lib.ssd_state_passing(_ptr(a.init), _ptr(a.final), a.L,
+                                                      ctypes.byref(a.dims), _ptr(a.ws),
+                                                      a.ws.numel(), _stream(a.device)))
+
+
+def ssd_chunk_scan(a: FwdArgs):
+    lib = load_library()
+    _check("ssd_chunk_scan", lib.ssd_chunk_scan(_ptr(a.x), _ptr(a.B), _ptr(a.C), _ptr(a.D),
+                                                _ptr(a.y), a.L, ctypes.byref(a.dims), _ptr(a.ws),
+                                                a.ws.numel(), _stream(a.device)))
+
+
+def workspace_views(a: FwdArgs):
+    """Views of the intermediates a forward left in ``a.ws``: G, DT, S, h_prev."""
+    Bt, T, H, P = a.x.shape
+    N = a.B.shape[3]
+    nc = -(-T // a.L)
+    off = ssd_chunked_fwd_workspace_layout(a.dims, a.L)
+
+    def view(o, n, dtype, shape):
+        nbytes = n * torch.empty((), dtype=dtype).element_size()
+        return a.ws[o:o + nbytes].view(dtype).view(shape)
+
+    units = Bt * H * nc
+    return {
+        "G": view(off[0], units * a.L, torch.float32, (Bt, H, nc, a.L)),
+        "DT": view(off[1], units * a.L, torch.float32, (Bt, H, nc, a.L)),
+        "S": view(off[2], units * P * N, torch.float32, (Bt, H, nc, P, N)),
+        "h_prev": view(off[3], units * P * N, a.x.dtype, (Bt, H, nc, P, N)),
+    }
+
+
+def ssd_decode_step(state, x_t, dt_t, B_t, C_t, A, D, y_t=None):
+    """One decode step; ``state`` [Bt,H,P,N] f32 is updated in place.  Returns y_t [Bt,H,P]."""
+    dev = state.device
+    if dev.type != "cuda":
+        raise ValueError("tensors must live on a GPU device, got %s" % dev)
+    if not state.is_contiguous() or state.dtype != torch.float32 or state.dim() != 4:
+        raise ValueError("state must be a contiguous float32 [Bt,H,P,N] tensor (updated in place)")
+    Bt, H, P, N = state.shape
+    io = x_t.dtype
+    G = B_t.shape[1]
+    x_t = _need(x_t, "x_t", io, (Bt, H, P), dev)
+    dt_t = _need(dt_t, "dt_t", torch.float32, (Bt, H), dev)
+    B_t = _need(B_t, "B_t", io, (Bt, G, N), dev)
+    C_t = _need(C_t, "C_t", io, (Bt, G, N), dev)
+    A = _need(A, "A", torch.float32, (H,), dev)
+    D = _need(D, "D", torch.float32, (H,), dev)
+    y_t = torch.empty_like(x_t) if y_t is None else _need(y_t, "y_t", io, (Bt, H, P), dev)
+    dims = Dims(Bt, 1, H, P, N, G, _io_code(io))
+    lib = load_library()
+    _check("ssd_decode_step", lib.ssd_decode_step(_ptr(state), _ptr(x_t), _ptr(dt_t), _ptr(B_t),
+                                                  _ptr(C_t), _ptr(A), _ptr(D), _ptr(y_t),
+                                                  ctypes.byref(dims), _stream(dev)))
+    return y_t

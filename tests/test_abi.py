@@ -1,0 +1,177 @@
+"""The C-ABI boundary without a GPU: the library loads, exports every symbol
+include/ssd.h declares, sizes its workspace, and rejects every invalid call on
+the host (status code + detail) before any HIP call is made."""
+
+import ctypes
+import os
+import subprocess
+
+import pytest
+
+from selective_state_space_amd import ssd
+
+pytestmark = pytest.mark.skipif(not os.path.exists(ssd.LIB_PATH),
+                                reason="libssd.so not built (python -m selective_state_space_amd.build)")
+
+# Fake, 16-byte aligned, never dereferenced: every call below fails validation first.
+P16 = ctypes.c_void_p(0x1000)
+P_MIS = ctypes.c_void_p(0x1004)
+
+
+def lib():
+    return ssd.load_library()
+
+
+def dims(Bt=2, T=300, H=8, P=64, N=128, G=2, io=ssd.SSD_BF16):
+    return ssd.Dims(Bt, T, H, P, N, G, io)
+
+
+def test_exports_every_declared_symbol():
+    names = ssd.header_functions()
+    assert {"ssd_chunked_fwd", "ssd_decode_step", "ssd_chunked_fwd_workspace_size"} <= set(names)
+    out = subprocess.run(["nm", "-D", "--defined-only", ssd.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {l.split()[-1] for l in out.splitlines() if " T " in l}
+    missing = [n for n in names if n not in exported]
+    assert not missing, missing
+    for n in names:
+        assert hasattr(lib(), n)
+
+
+def test_version_and_status_strings():
+    assert lib().ssd_version() >= 100
+    for code in ssd.STATUS:
+        assert lib().ssd_status_string(code).decode().startswith(ssd.STATUS[code])
+
+
+def test_workspace_size_and_layout():
+    d = dims(8, 4096, 80, 64, 128, 1)
+    nc = 16
+    units = 8 * 80 * nc
+    size = ssd.ssd_chunked_fwd_workspace_size(d, 256)
+    off = ssd.ssd_chunked_fwd_workspace_layout(d, 256)
+    assert off[0] == 0
+    assert off[1] >= units * 256 * 4 and off[1] % 256 == 0
+    assert off[2] >= off[1] + units * 256 * 4 and off[2] % 256 == 0
+    assert off[3] >= off[2] + units * 64 * 128 * 4 and off[3] % 256 == 0
+    assert size >= off[3] + units * 64 * 128 * 2
+    # fp32 io keeps h_prev in fp32
+    d32 = dims(8, 4096, 80, 64, 128, 1, ssd.SSD_F32)
+    assert ssd.ssd_chunked_fwd_workspace_size(d32, 256) >= off[3] + units * 64 * 128 * 4
+    # ragged T rounds up to whole chunks
+    assert (ssd.ssd_chunked_fwd_workspace_size(dims(1, 257, 4), 256)
+            == ssd.ssd_chunked_fwd_workspace_size(dims(1, 512, 4), 256))
+    # empty and invalid shapes need none
+    assert ssd.ssd_chunked_fwd_workspace_size(dims(Bt=0), 256) == 0
+    assert ssd.ssd_chunked_fwd_workspace_size(dims(T=0), 256) == 0
+    assert ssd.ssd_chunked_fwd_workspace_size(dims(N=100), 256) == 0
+    assert ssd.ssd_chunked_fwd_workspace_size(dims(), 96) == 0
+
+
+def _fwd(d, L=256, x=P16, dt=P16, A=P16, B=P16, C=P16, D=P16, init=None, y=P16, fin=None,
+         ws=P16, wsb=1 << 40):
+    return lib().ssd_chunked_fwd(x, dt, A, B, C, D, L, init, y, fin,
+                                 None if d is None else ctypes.byref(d), ws, wsb, None)
+
+
+def _detail():
+    return lib().ssd_last_error_detail().decode()
+
+
+@pytest.mark.parametrize("field", ["x", "dt", "A", "B", "C", "D", "y", "ws"])
+def test_null_pointers(field):
+    st = _fwd(dims(), **{field: None})
+    assert st == -1
+    assert (field if field != "ws" else "workspace") in _detail()
+
+
+def test_null_dims():
+    assert _fwd(None) == -1
+
+
+@pytest.mark.parametrize("kw,code,word", [
+    (dict(H=6, G=4), -2, "multiple"),
+    (dict(H=0), -2, "nheads"),
+    (dict(G=0), -2, "ngroups"),
+    (dict(Bt=-1), -2, "batch"),
+    (dict(T=-5), -2, "seqlen"),
+    (dict(P=32), -3, "headdim"),
+    (dict(N=256), -3, "dstate"),
+    (dict(io=7), -3, "io_dtype"),
+])
+def test_bad_shapes(kw, code, word):
+    assert _fwd(dims(**kw)) == code
+    assert word in _detail()
+
+
+@pytest.mark.parametrize("L", [0, 32, 100, 512])
+def test_unsupported_chunk_size(L):
+    assert _fwd(dims(), L=L) == -3
+    assert "chunk_size" in _detail()
+
+
+@pytest.mark.parametrize("field", ["x", "dt", "A", "B", "C", "D", "y", "init", "fin", "ws"])
+def test_misaligned(field):
+    assert _fwd(dims(), **{field: P_MIS}) == -4
+    assert "aligned" in _detail()
+
+
+def test_short_workspace():
+    d = dims()
+    need = ssd.ssd_chunked_fwd_workspace_size(d, 256)
+    assert _fwd(d, wsb=need - 1) == -5
+    assert str(need) in _detail()
+
+
+def test_too_large_for_one_launch():
+    assert _fwd(dims(Bt=1 << 20, T=1 << 20, H=1 << 10, G=1)) == -2
+
+
+def test_stage_calls_validate_too():
+    d = dims()
+    L = lib()
+    assert L.ssd_chunk_cumsum(None, P16, 256, ctypes.byref(d), P16, 1 << 40, None) == -1
+    assert L.ssd_chunk_state(P16, P_MIS, 256, ctypes.byref(d), P16, 1 << 40, None) == -4
+    assert L.ssd_state_passing(None, None, 256, ctypes.byref(d), P16, 10, None) == -5
+    assert L.ssd_chunk_scan(P16, P16, P16, None, P16, 256, ctypes.byref(d), P16, 1 << 40,
+                            None) == -1
+
+
+def _dec(d, state=P16, x=P16, dt=P16, B=P16, C=P16, A=P16, D=P16, y=P16):
+    return lib().ssd_decode_step(state, x, dt, B, C, A, D, y,
+                                 None if d is None else ctypes.byref(d), None)
+
+
+@pytest.mark.parametrize("field", ["state", "x", "dt", "B", "C", "A", "D", "y"])
+def test_decode_null_and_misaligned(field):
+    assert _dec(dims(), **{field: None}) == -1
+    assert _dec(dims(), **{field: P_MIS}) == -4
+
+
+def test_decode_shapes():
+    assert _dec(dims(H=8, G=3)) == -2
+    assert _dec(dims(N=32)) == -3
+    assert _dec(None) == -1
+
+
+def test_empty_batch_is_a_no_op():
+    # batch 0: valid, nothing to launch, no workspace needed
+    assert _fwd(dims(Bt=0), ws=None, wsb=0) == 0
+    assert _dec(dims(Bt=0)) == 0
+
+
+def test_detail_cleared_on_success():
+    _fwd(dims(), x=None)
+    assert _detail()
+    assert _fwd(dims(Bt=0), ws=None, wsb=0) == 0
+    assert _detail() == ""
+
+
+def test_empty_sequence_allows_null_token_tensors():
+    # seqlen 0: nothing to read but the state; validation passes up to the
+    # state pointers (a misaligned final_state is still caught)
+    d = dims(T=0)
+    assert _fwd(d, x=None, dt=None, A=None, B=None, C=None, D=None, y=None, ws=None, wsb=0,
+                fin=P_MIS) == -4
+    # with tokens present the same NULLs are errors
+    assert _fwd(dims(), x=None) == -1

@@ -56,3 +56,14 @@ def test_decode_steps_differ_and_repeat():
     np.testing.assert_array_equal(s0.x_t, s0b.x_t)
     assert not np.array_equal(s0.x_t, s1.x_t)
     assert s0.x_t.shape == (2, 128, 64) and s0.B_t.shape == (2, 8, 128)
+
+
+def test_dt_per_head_median_tracks_its_bias():
+    # softplus is monotone and z is symmetric, so the median of dt for head h
+    # is softplus(dt_bias_h) = dt0_h; this pins the token -> head mapping
+    w = gen.WORKLOADS[2].with_(batch=1, seqlen=4096)
+    inp = gen.make_fwd(w, 0)
+    prm = gen.decode_params(w, 0)
+    want = np.log1p(np.exp(prm.dt_bias))
+    med = np.median(inp.dt[0], axis=0)
+    np.testing.assert_allclose(med, want, rtol=0.08)
