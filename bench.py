@@ -1,0 +1,331 @@
+"""Benchmark of the SSD hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload mamba2_2p7b]
+
+One step = one chunked forward over one batch of the workload (the four
+stages chunk_cumsum -> chunk_state -> state_passing -> chunk_scan, called
+through the C ABI on torch's current stream, with HIP events between the
+stages so each kernel's duration is measured inside the timed region).  The
+inputs are generated, uploaded and resident in HBM before timing starts.
+
+Prints one JSON line (stdout): tokens/s of the forward, the roofline of the
+dominant kernel, per-kernel times and rooflines, the decode step's HBM
+bandwidth on the decode workload, and the CPU oracle's tokens/s on a bounded
+sample of the same workload.  Progress goes to stderr.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import subprocess
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, published
+BF16_PEAK_TFLOPS = 2500.0       # MI355X dense bf16 MFMA, published
+FP32_VALU_PEAK_TFLOPS = 157.3   # MI355X fp32 vector, published
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+# ---- algorithmic work (what the method must move / compute, per launch) -----------
+
+def algorithmic(w, io_bytes: int):
+    """Bytes and useful flops each stage must move/compute for workload w.
+
+    Per (b, h, chunk) unit, L tokens, P = 64, N: see DESIGN.md ("Algorithmic
+    bytes and flops").  B and C are per group and chunk, so their bytes are
+    shared by the heads_per_group heads of a group.
+    """
+    Bt, T, H, P, N, G, L = w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.ngroups, w.chunk_size
+    nc = -(-T // L)
+    units = Bt * H * nc
+    hpg = H // G
+    tok_x = Bt * T * H * P * io_bytes
+    tok_bc = Bt * T * G * N * io_bytes
+    gdt = 2 * units * L * 4
+    state = Bt * H * P * N * 4
+    out = {}
+    out["chunk_cumsum"] = dict(bytes=Bt * T * H * 4 + gdt, flops=2 * Bt * T * H)
+    out["chunk_state"] = dict(bytes=tok_x + tok_bc + gdt + units * P * N * 4,
+                              flops=2 * P * N * L * units)
+    out["state_passing"] = dict(
+        bytes=units * P * N * 4 + units * P * N * io_bytes + units * 4
+        + (state if w.init_state else 0) + state,
+        flops=2 * units * P * N)
+    tri = L * (L + 1) // 2
+    tok_y = Bt * T * H * P * 4           # y is written fp32
+    out["chunk_scan"] = dict(
+        bytes=tok_x + tok_y + 2 * tok_bc + units * P * N * io_bytes + gdt,
+        flops=units * (2 * L * P * N + 2 * tri * P) + (Bt * G * nc) * 2 * tri * N)
+    return out
+
+
+def decode_bytes(w, io_bytes=2):
+    Bt, H, P, N, G = w.batch, w.nheads, w.headdim, w.dstate, w.ngroups
+    # state read + write, x_t in, y_t out (fp32), dt_t, B_t and C_t
+    return (2 * Bt * H * P * N * 4 + Bt * H * P * (io_bytes + 4) + Bt * H * 4
+            + 2 * Bt * G * N * io_bytes)
+
+
+# ---- the GPU legs ----------------------------------------------------------------------
+
+def run_forward(w, steps: int, warmup: int):
+    import torch
+    from selective_state_space_amd import inputs as gen
+    from selective_state_space_amd import ssd
+
+    dev = torch.device("cuda:0")
+    t0 = time.time()
+    inp = gen.make_fwd(w, 0)
+    bf = torch.bfloat16 if w.io_dtype == gen.BF16 else torch.float32
+
+    def up(a, dt=torch.float32):
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dt).to(dev)
+
+    a = ssd.FwdArgs(up(inp.x, bf), up(inp.dt), up(inp.A), up(inp.B, bf), up(inp.C, bf),
+                    up(inp.D), w.chunk_size,
+                    None if inp.init_state is None else up(inp.init_state))
+    log("inputs generated and resident in HBM (%.1f s)" % (time.time() - t0))
+    stages = [("chunk_cumsum", ssd.ssd_chunk_cumsum), ("chunk_state", ssd.ssd_chunk_state),
+              ("state_passing", ssd.ssd_state_passing), ("chunk_scan", ssd.ssd_chunk_scan)]
+    for _ in range(warmup):
+        for _, f in stages:
+            f(a)
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)]
+          for _ in range(steps)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for k in range(steps):
+        ev[k][0].record()
+        for i, (_, f) in enumerate(stages):
+            f(a)
+            ev[k][i + 1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    per = np.array([[ev[k][i].elapsed_time(ev[k][i + 1]) for i in range(len(stages))]
+                    for k in range(steps)])          # ms
+    step_ms = np.array([ev[k][0].elapsed_time(ev[k][-1]) for k in range(steps)])
+    kern = {name: float(per[:, i].mean()) for i, (name, _) in enumerate(stages)}
+    del a
+    torch.cuda.empty_cache()
+    return wall, step_ms, kern
+
+
+def run_decode(w, steps: int, warmup: int):
+    import torch
+    from selective_state_space_amd import inputs as gen
+    from selective_state_space_amd import ssd
+
+    dev = torch.device("cuda:0")
+    prm = gen.decode_params(w, 0)
+    nset = 8   # distinct per-token input sets, cycled
+
+    def up(a, dt=torch.float32):
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dt).to(dev)
+
+    sets = []
+    for k in range(nset):
+        s = gen.make_decode_step(w, k, prm, 0)
+        sets.append((up(s.x_t, torch.bfloat16), up(s.dt_t), up(s.B_t, torch.bfloat16),
+                     up(s.C_t, torch.bfloat16)))
+    A, D = up(prm.A), up(prm.D)
+    state = torch.zeros((w.batch, w.nheads, w.headdim, w.dstate), device=dev)
+    y = torch.empty((w.batch, w.nheads, w.headdim), dtype=torch.float32, device=dev)
+    for k in range(warmup):
+        ssd.ssd_decode_step(state, *sets[k % nset], A, D, y_t=y)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    ev[0].record()
+    for k in range(steps):
+        ssd.ssd_decode_step(state, *sets[k % nset], A, D, y_t=y)
+        ev[k + 1].record()
+    torch.cuda.synchronize()
+    t = np.array([ev[k].elapsed_time(ev[k + 1]) for k in range(steps)])
+    del state
+    torch.cuda.empty_cache()
+    return float(np.median(t)), float(np.mean(t))
+
+
+def run_copy_reference(nbytes: int = 1 << 30, reps: int = 10):
+    """HBM bandwidth of torch's device copy (read + write), for context."""
+    import torch
+    a = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    a.fill_(1.0)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        b.copy_(a)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    del a, b
+    torch.cuda.empty_cache()
+    return 2 * nbytes / (ms * 1e-3) / 1e9
+
+
+# ---- the CPU baseline: the oracle on a bounded sample ------------------------------------
+
+def run_cpu_baseline(w, target_s: float = 12.0):
+    import oracle
+    from selective_state_space_amd import inputs as gen
+
+    inp = gen.make_fwd(w, 0)
+    Bt, H = w.batch, w.nheads
+    npairs_all = Bt * H
+    rng = np.random.default_rng(1)
+    order = rng.permutation(npairs_all)
+    # calibrate on a few pairs, then size the sample to about target_s seconds
+    k = min(16, npairs_all)
+    t0 = time.perf_counter()
+    _, _, nth = oracle.token_fwd(inp.x, inp.dt, inp.A, inp.B, inp.C, inp.D, inp.init_state,
+                                 pairs=sorted(order[:k]))
+    t_cal = time.perf_counter() - t0
+    per_pair = t_cal / k
+    k2 = int(min(npairs_all, max(k, target_s / max(per_pair, 1e-9))))
+    k2 = max(nth, (k2 // nth) * nth) if k2 > nth else k2
+    t0 = time.perf_counter()
+    _, _, nth = oracle.token_fwd(inp.x, inp.dt, inp.A, inp.B, inp.C, inp.D, inp.init_state,
+                                 pairs=sorted(order[:k2]))
+    t = time.perf_counter() - t0
+    frac = k2 / npairs_all
+    tokens = Bt * w.seqlen * frac       # the sampled share of the whole job's tokens
+    return dict(value=tokens / t, unit="tokens/s", cores=int(nth), kind="oracle",
+                sample="float64 token recurrence over %d of the %d (batch, head) pairs, all %d "
+                       "tokens each (%.1f%% of the job), %.2f s wall; value = sampled share of "
+                       "the job's tokens / wall time" % (k2, npairs_all, w.seqlen, 100 * frac, t))
+
+
+# ---- main ----------------------------------------------------------------------------------
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="mamba2_2p7b")
+    ap.add_argument("--decode-steps", type=int, default=50)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build targets a single MI355X "
+              "(no multi-GPU path); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from selective_state_space_amd import inputs as gen
+    from selective_state_space_amd import ssd
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    ssd.load_library()   # fails loudly if libssd.so is missing
+
+    w = gen.BY_NAME[args.workload]
+    io_bytes = 2 if w.io_dtype == gen.BF16 else 4
+    log("workload %s: %s" % (w.name, w.description))
+
+    wall, step_ms, kern = run_forward(w, args.steps, args.warmup)
+    tokens = w.batch * w.seqlen
+    value = tokens * args.steps / wall
+    alg = algorithmic(w, io_bytes)
+    kernels = {}
+    for name, ms in kern.items():
+        a = alg[name]
+        kernels[name] = dict(
+            us=round(ms * 1e3, 2),
+            GBps=round(a["bytes"] / (ms * 1e-3) / 1e9, 1),
+            hbm_frac=round(a["bytes"] / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+            TFLOPs=round(a["flops"] / (ms * 1e-3) / 1e12, 2),
+            bf16_mfma_frac=round(a["flops"] / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+            alg_bytes=int(a["bytes"]), alg_flops=int(a["flops"]))
+    dom = max(kern, key=kern.get)
+    dms = kern[dom]
+    achieved = alg[dom]["bytes"] / (dms * 1e-3) / 1e9
+    roofline = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1),
+                "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                "traffic": None,
+                "avg_launch_us": round(dms * 1e3, 2), "alg_bytes_per_launch": int(alg[dom]["bytes"])}
+    chunk_flops = alg["chunk_state"]["flops"] + alg["chunk_scan"]["flops"]
+    chunk_ms = kern["chunk_state"] + kern["chunk_scan"]
+    fwd_flops = sum(a["flops"] for a in alg.values())
+    log("forward: %.1f us/step, %.3e tokens/s; dominant %s %.1f us" %
+        (float(np.mean(step_ms)) * 1e3, value, dom, dms * 1e3))
+
+    decode = None
+    if not args.no_decode:
+        wd = gen.WORKLOADS[4]
+        med, mean = run_decode(wd, args.decode_steps, 5)
+        byt = decode_bytes(wd)
+        decode = dict(workload=wd.name, us_per_step=round(med * 1e3, 2),
+                      GBps=round(byt / (med * 1e-3) / 1e9, 1),
+                      hbm_frac=round(byt / (med * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+                      tokens_per_s=round(wd.batch / (med * 1e-3), 1),
+                      alg_bytes_per_step=int(byt), steps_timed=args.decode_steps)
+        log("decode: %.1f us/step, %.0f GB/s" % (med * 1e3, decode["GBps"]))
+    copy_gbps = run_copy_reference()
+    log("device copy reference: %.0f GB/s" % copy_gbps)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a bounded sample ...")
+        cpu = run_cpu_baseline(w)
+        log("oracle: %.3e tokens/s on %d threads" % (cpu["value"], cpu["cores"]))
+
+    try:
+        sha = subprocess.run(["git", "rev-parse", "--short", "HEAD"], cwd=ROOT,
+                             capture_output=True, text=True).stdout.strip() or None
+    except Exception:
+        sha = None
+
+    rec = {
+        "metric": "SSD forward tokens/sec at 2.7B-layer shape + % bf16 MFMA roofline; decode GB/s",
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(float(np.mean(step_ms)), 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "seqlen": w.seqlen, "nheads": w.nheads,
+                   "headdim": w.headdim, "dstate": w.dstate, "ngroups": w.ngroups,
+                   "chunk_size": w.chunk_size, "io_dtype": w.io_dtype,
+                   "init_state": w.init_state, "parallelism": "single GPU"},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "forward_bf16_mfma_frac": round(fwd_flops / (float(np.mean(step_ms)) * 1e-3) / 1e12
+                                        / BF16_PEAK_TFLOPS, 4),
+        "chunk_kernels_bf16_mfma_frac": round(chunk_flops / (chunk_ms * 1e-3) / 1e12
+                                              / BF16_PEAK_TFLOPS, 4),
+        "kernels": kernels,
+        "decode": decode,
+        "hbm_copy_reference_GBps": round(copy_gbps, 1),
+        "wall_s_timed": round(wall, 4),
+        "git": sha,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

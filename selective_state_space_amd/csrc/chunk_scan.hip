@@ -12,24 +12,27 @@
 // the drain of the first product's accumulator.
 //
 // bf16 path (MFMA, v_mfma_f32_16x16x32_bf16): one workgroup of 4 wavefronts
-// per (b, h, chunk), heads fastest and kept on one XCD so B and C of the
-// group come from L2.  A wavefront owns 16-row blocks of the chunk, paired
-// (I, L/16-1-I) so that every wavefront has the same number of causal tiles.
-// For a row block I (rows i0 = 16 I ...):
-//   1. inter:  acc = C_I h_prev^T (K = N).  C rows are the A operand as
-//      loaded (16 bytes a lane); h_prev rows (N contiguous) are the B operand
-//      as loaded.  Output column m of MFMA s is p = 4m + s.
-//   2. rows scaled by exp2(G_i).
-//   3. intra: per 32-token step, two 16x16 tiles of (C B^T)^T = B C^T are
-//      formed with MFMA (A = B rows, B = the C fragments of step 1).  The
-//      accumulator layout of a transposed tile (lane m: column i, rows j =
-//      4q..4q+3) is exactly a 4-element K slice of an A operand for row i,
-//      so the drain -- times exp2(G_i - G_j) dt_j, select j <= i, round to
-//      bf16 -- leaves the A operand of the second product in place, with no
-//      LDS round trip.  The matching B operand (x rows of the same 8 tokens,
-//      4 p per lane) is transposed in registers.  Tiles above the diagonal
-//      are skipped.
-//   4. y += D x, stored as bf16 (8 bytes a lane and row).
+// per (b, h, chunk), heads fastest and kept on one XCD so the group's B and C
+// come from L2.  Wavefront w owns the 16-row blocks I = w, w+4, ... of the
+// chunk and keeps their C rows in registers (A operand of the inter product,
+// B operand of the C B^T tiles).  h_prev, G, dt and the column factors V are
+// staged in LDS once; B and x go through LDS in 32-token slabs, the next slab
+// loaded while the current one is used (all wavefronts in lockstep).
+//   1. inter: acc = C h_prev^T (K = N); output column m of MFMA s is p = 4m+s.
+//      Rows are then scaled by exp2(G_i).
+//   2. intra, per slab: two 16x16 tiles of (C B^T)^T = B C^T per row block
+//      (A = B rows from LDS).  The accumulator layout of a transposed tile
+//      (lane m: column i, rows j = 4q..4q+3) is a 4-element K slice of the A
+//      operand for row i, so the drain -- times exp2(G_i - G_j) dt_j, select
+//      j <= i, round to bf16 -- leaves the A operand of the second product in
+//      place, with no LDS round trip.  The matching B operand (x rows of the
+//      same tokens, 4 p per lane) is transposed in registers.  Tiles above the
+//      diagonal are skipped.  Below the diagonal the decay factors through
+//      the last token a of the column block: exp2(G_i - G_j) = exp2(G_i - G_a)
+//      * exp2(G_a - G_j), both exponents <= 0, so a tile needs one exp2 per
+//      lane (V_j = exp2(G_a - G_j) dt_j is staged per token).  Diagonal tiles
+//      use the exact pairwise exponent with a causal select.
+//   3. y = acc + D x, written fp32 (16 bytes a lane and row).
 //
 // fp32 path (VALU): one workgroup per (b, h, chunk), 16-row tiles: the
 // decayed, masked C B^T rows are built in LDS, then each thread forms y for
@@ -43,148 +46,31 @@ namespace ssd {
 namespace {
 
 template <int L, int N>
-__device__ __forceinline__ void scan_row_block(
-    int I, const uint16_t *__restrict__ x, const uint16_t *__restrict__ Bm,
-    const uint16_t *__restrict__ Cm, const float *__restrict__ Gp, const float *__restrict__ Dp,
-    const uint16_t *__restrict__ Hp, uint16_t *__restrict__ y, float Dh, int64_t T, int64_t t0,
-    int64_t b, int32_t h, int32_t H, int32_t g, int32_t G, int m, int q) {
-    constexpr int P = 64;
-    constexpr int NK = N / 32;  // K steps over n
-    const int i0 = 16 * I;
-
-    // C rows i0 + m, n = 32 kn + 8q .. +7: A operand of the inter product
-    // and B operand of the B C^T tiles.
-    uint4 cf[NK];
-    {
-        const int64_t tok = t0 + i0 + m;
-        const bool ok = tok < T;
-        const uint16_t *cp = Cm + ((b * T + tok) * G + g) * N + 8 * q;
-#pragma unroll
-        for (int kn = 0; kn < NK; ++kn)
-            cf[kn] = ok ? *reinterpret_cast<const uint4 *>(cp + 32 * kn) : make_uint4(0, 0, 0, 0);
-    }
-
-    f32x4 acc[4];
-#pragma unroll
-    for (int s = 0; s < 4; ++s) acc[s] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    // 1. inter: acc[s][e] = sum_n C[i0+4q+e][n] h_prev[4m+s][n]
-#pragma unroll
-    for (int kn = 0; kn < NK; ++kn) {
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            const uint4 hv =
-                *reinterpret_cast<const uint4 *>(Hp + (4 * m + s) * N + 32 * kn + 8 * q);
-            acc[s] = mfma16x16x32(as_bf16x8(cf[kn]), as_bf16x8(hv), acc[s]);
-        }
-    }
-    // 2. rows i = i0 + 4q + e scaled by exp2(G_i)
-    {
-        const float4 gi = *reinterpret_cast<const float4 *>(Gp + i0 + 4 * q);
-        const float sc[4] = {fast_exp2(gi.x), fast_exp2(gi.y), fast_exp2(gi.z), fast_exp2(gi.w)};
-#pragma unroll
-        for (int s = 0; s < 4; ++s)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) acc[s][e] *= sc[e];
-    }
-
-    // 3. intra
-    const float gcol = Gp[i0 + m];  // G of this lane's column i = i0 + m
-    for (int jb2 = 0; 2 * jb2 <= I; ++jb2) {
-        uint32_t cbw[2][2];
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            const int J = 2 * jb2 + u;
-            if (J <= I) {
-                f32x4 cbt = f32x4{0.f, 0.f, 0.f, 0.f};
-                const int64_t tok = t0 + 16 * J + m;
-                const bool ok = tok < T;
-                const uint16_t *bp = Bm + ((b * T + tok) * G + g) * N + 8 * q;
-#pragma unroll
-                for (int kn = 0; kn < NK; ++kn) {
-                    const uint4 bv = ok ? *reinterpret_cast<const uint4 *>(bp + 32 * kn)
-                                        : make_uint4(0, 0, 0, 0);
-                    cbt = mfma16x16x32(as_bf16x8(bv), as_bf16x8(cf[kn]), cbt);
-                }
-                // cbt[e] = (C B^T)[i = i0 + m][j = 16J + 4q + e]
-                const float4 gj = *reinterpret_cast<const float4 *>(Gp + 16 * J + 4 * q);
-                const float4 dj = *reinterpret_cast<const float4 *>(Dp + 16 * J + 4 * q);
-                const float gjv[4] = {gj.x, gj.y, gj.z, gj.w};
-                const float djv[4] = {dj.x, dj.y, dj.z, dj.w};
-                float v[4];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const float d = fminf(gcol - gjv[e], 0.f);
-                    const float val = cbt[e] * fast_exp2(d) * djv[e];
-                    const bool keep = (J < I) || (4 * q + e <= m);
-                    v[e] = keep ? val : 0.f;
-                }
-                cbw[u][0] = pack_bf16x2(v[0], v[1]);
-                cbw[u][1] = pack_bf16x2(v[2], v[3]);
-            } else {
-                cbw[u][0] = 0u;
-                cbw[u][1] = 0u;
-            }
-        }
-        const uint4 aw = make_uint4(cbw[0][0], cbw[0][1], cbw[1][0], cbw[1][1]);
-        const bf16x8 af = as_bf16x8(aw);
-
-        // x rows for the same K slots: slot r < 4 -> j = 32 jb2 + 4q + r,
-        // slot r >= 4 -> j = 32 jb2 + 16 + 4q + (r - 4); 4 p (4m .. 4m+3) each.
-        const bool second = (2 * jb2 + 1) <= I;
-        uint2 xr[8];
-#pragma unroll
-        for (int r = 0; r < 8; ++r) {
-            const int jl = 32 * jb2 + ((r < 4) ? 0 : 16) + 4 * q + (r & 3);
-            const int64_t tok = t0 + jl;
-            const bool ok = (tok < T) && (r < 4 || second);
-            xr[r] = ok ? *reinterpret_cast<const uint2 *>(x + ((b * T + tok) * H + h) * P + 4 * m)
-                       : make_uint2(0u, 0u);
-        }
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            uint4 v;
-            uint32_t *vw = reinterpret_cast<uint32_t *>(&v);
-#pragma unroll
-            for (int rr = 0; rr < 4; ++rr) {
-                const uint32_t a0 = (s < 2) ? xr[2 * rr].x : xr[2 * rr].y;
-                const uint32_t a1 = (s < 2) ? xr[2 * rr + 1].x : xr[2 * rr + 1].y;
-                vw[rr] = (s & 1) ? pair_hi(a0, a1) : pair_lo(a0, a1);
-            }
-            acc[s] = mfma16x16x32(af, as_bf16x8(v), acc[s]);
-        }
-    }
-
-    // 4. y = acc + D x for rows i0 + 4q + e, p = 4m .. 4m+3
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        const int64_t tok = t0 + i0 + 4 * q + e;
-        if (tok < T) {
-            const int64_t off = ((b * T + tok) * H + h) * P + 4 * m;
-            const uint2 xv = *reinterpret_cast<const uint2 *>(x + off);
-            uint2 o;
-            o.x = pack_bf16x2(acc[0][e] + Dh * bf16_lo(xv.x), acc[1][e] + Dh * bf16_hi(xv.x));
-            o.y = pack_bf16x2(acc[2][e] + Dh * bf16_lo(xv.y), acc[3][e] + Dh * bf16_hi(xv.y));
-            *reinterpret_cast<uint2 *>(y + off) = o;
-        }
-    }
-}
-
-template <int L, int N>
-__global__ __launch_bounds__(256) void chunk_scan_bf16_kernel(
+__global__ __launch_bounds__(256, 2) void chunk_scan_bf16_kernel(
     const uint16_t *__restrict__ x, const uint16_t *__restrict__ Bm,
     const uint16_t *__restrict__ Cm, const float *__restrict__ D, const float *__restrict__ Gws,
-    const float *__restrict__ DTws, const uint16_t *__restrict__ hprev, uint16_t *__restrict__ y,
+    const float *__restrict__ DTws, const uint16_t *__restrict__ hprev, float *__restrict__ y,
     int64_t T, int32_t H, int32_t G, int32_t nc, uint32_t nblk) {
     constexpr int P = 64;
-    constexpr int NB = L / 16;
+    constexpr int NB = L / 16;       // 16-row blocks
+    constexpr int RBW = NB / 4;      // row blocks per wavefront
+    constexpr int NK = N / 32;       // K steps over n
+    constexpr int NS = L / 32;       // 32-token slabs
+    constexpr int HS = N + 8;        // padded LDS row strides (bf16 elements)
+    constexpr int XS = P + 8;
+    __shared__ float Gs[L], Vs[L], DTs[L];
+    __shared__ __attribute__((aligned(16))) uint16_t Hs[P * HS];
+    __shared__ __attribute__((aligned(16))) uint16_t Bs[2][32 * HS];
+    __shared__ __attribute__((aligned(16))) uint16_t Xs[2][32 * XS];
+
     const uint32_t lid = xcd_remap(blockIdx.x, nblk);
     const int32_t h = lid % H;
     const int32_t c = (lid / H) % nc;
     const int64_t b = lid / ((uint32_t)H * nc);
     const int32_t g = h / (H / G);
-    const int wave = threadIdx.x >> 6;
-    const int lane = threadIdx.x & 63;
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6;
+    const int lane = tid & 63;
     const int m = lane & 15, q = lane >> 4;
 
     const int64_t bhc = ((int64_t)b * H + h) * nc + c;
@@ -194,13 +80,195 @@ __global__ __launch_bounds__(256) void chunk_scan_bf16_kernel(
     const float Dh = D[h];
     const int64_t t0 = (int64_t)c * L;
 
-    if constexpr (NB == 4) {
-        scan_row_block<L, N>(wave, x, Bm, Cm, Gp, Dp, Hp, y, Dh, T, t0, b, h, H, g, G, m, q);
-    } else {
-        for (int pi = wave; pi < NB / 2; pi += 4) {
-            scan_row_block<L, N>(pi, x, Bm, Cm, Gp, Dp, Hp, y, Dh, T, t0, b, h, H, g, G, m, q);
-            scan_row_block<L, N>(NB - 1 - pi, x, Bm, Cm, Gp, Dp, Hp, y, Dh, T, t0, b, h, H, g, G,
-                                 m, q);
+    // ---- staging: G, dt, the column weights V, h_prev, slab 0 of B and x ----
+    // V_j = exp2(G_a - G_j) dt_j with a = the last token of j's 16-block
+    // (exponent <= 0): the column factor of the decay between blocks.
+    if (tid < L) {
+        const float gj = Gp[tid];
+        const float dj = Dp[tid];
+        Gs[tid] = gj;
+        DTs[tid] = dj;
+        Vs[tid] = fast_exp2(Gp[(tid | 15)] - gj) * dj;
+    }
+    for (int e = tid; e < P * (N / 8); e += 256) {
+        const int r = e / (N / 8), cc = (e % (N / 8)) * 8;
+        *reinterpret_cast<uint4 *>(&Hs[r * HS + cc]) =
+            *reinterpret_cast<const uint4 *>(Hp + r * N + cc);
+    }
+    // slab staging: B rows (N/8 16-byte pieces each) then x rows (8 pieces each)
+    constexpr int BPC = 32 * (N / 8);         // B pieces per slab
+    constexpr int XPC = 32 * 8;               // x pieces per slab
+    constexpr int PPT = (BPC + XPC) / 256;    // pieces per thread
+    static_assert((BPC + XPC) % 256 == 0, "slab pieces must spread evenly");
+    auto slab_load = [&](int js, uint4 (&v)[PPT]) {
+#pragma unroll
+        for (int k = 0; k < PPT; ++k) {
+            const int e = tid + 256 * k;
+            const bool isb = e < BPC;
+            const int ee = isb ? e : e - BPC;
+            const int r = isb ? ee / (N / 8) : ee / 8;
+            const int cc = isb ? (ee % (N / 8)) * 8 : (ee % 8) * 8;
+            const int64_t tok = t0 + 32 * js + r;
+            uint4 val = make_uint4(0u, 0u, 0u, 0u);
+            if (tok < T)
+                val = isb ? *reinterpret_cast<const uint4 *>(Bm + ((b * T + tok) * G + g) * N + cc)
+                          : *reinterpret_cast<const uint4 *>(x + ((b * T + tok) * H + h) * P + cc);
+            v[k] = val;
+        }
+    };
+    auto slab_store = [&](int buf, const uint4 (&v)[PPT]) {
+#pragma unroll
+        for (int k = 0; k < PPT; ++k) {
+            const int e = tid + 256 * k;
+            const bool isb = e < BPC;
+            const int ee = isb ? e : e - BPC;
+            if (isb)
+                *reinterpret_cast<uint4 *>(&Bs[buf][(ee / (N / 8)) * HS + (ee % (N / 8)) * 8]) = v[k];
+            else
+                *reinterpret_cast<uint4 *>(&Xs[buf][(ee / 8) * XS + (ee % 8) * 8]) = v[k];
+        }
+    };
+    {
+        uint4 v[PPT];
+        slab_load(0, v);
+        slab_store(0, v);
+    }
+
+    // C rows of this wavefront's row blocks I_k = wave + 4k (rows 16 I_k + m,
+    // n = 32 kn + 8q .. +7): A operand of the inter product and B operand of
+    // the C B^T tiles, kept in registers for the whole chunk.
+    uint4 cf[RBW][NK];
+#pragma unroll
+    for (int k = 0; k < RBW; ++k) {
+        const int64_t tok = t0 + 16 * (wave + 4 * k) + m;
+        const uint16_t *cp = Cm + ((b * T + tok) * G + g) * N + 8 * q;
+#pragma unroll
+        for (int kn = 0; kn < NK; ++kn)
+            cf[k][kn] = tok < T ? *reinterpret_cast<const uint4 *>(cp + 32 * kn)
+                                : make_uint4(0u, 0u, 0u, 0u);
+    }
+    __syncthreads();
+
+    // ---- inter: acc = C h_prev^T, then rows scaled by exp2(G_i) ----
+    // acc[k][s][e] = y[i = 16 I_k + 4q + e][p = 4m + s]
+    f32x4 acc[RBW][4];
+#pragma unroll
+    for (int k = 0; k < RBW; ++k)
+#pragma unroll
+        for (int s = 0; s < 4; ++s) acc[k][s] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kn = 0; kn < NK; ++kn)
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            const uint4 hv = *reinterpret_cast<const uint4 *>(&Hs[(4 * m + s) * HS + 32 * kn + 8 * q]);
+#pragma unroll
+            for (int k = 0; k < RBW; ++k)
+                acc[k][s] = mfma16x16x32(as_bf16x8(cf[k][kn]), as_bf16x8(hv), acc[k][s]);
+        }
+#pragma unroll
+    for (int k = 0; k < RBW; ++k) {
+        const int i0 = 16 * (wave + 4 * k) + 4 * q;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float sc = fast_exp2(Gs[i0 + e]);
+#pragma unroll
+            for (int s = 0; s < 4; ++s) acc[k][s][e] *= sc;
+        }
+    }
+
+    // ---- intra: 32-token slabs in lockstep, next slab loaded during this one ----
+    for (int js = 0; js < NS; ++js) {
+        const int buf = js & 1;
+        uint4 nxt[PPT];
+        if (js + 1 < NS) slab_load(js + 1, nxt);
+
+        // x rows of the slab as B operands: K slot r -> token (r < 4 ? 0 : 16) + 4q + (r & 3),
+        // column m of MFMA s -> p = 4m + s (transposed in registers)
+        bf16x8 xf[4];
+        {
+            uint2 xr[8];
+#pragma unroll
+            for (int r = 0; r < 8; ++r)
+                xr[r] = *reinterpret_cast<const uint2 *>(
+                    &Xs[buf][((r < 4 ? 0 : 16) + 4 * q + (r & 3)) * XS + 4 * m]);
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                uint4 v;
+                uint32_t *vw = reinterpret_cast<uint32_t *>(&v);
+#pragma unroll
+                for (int rr = 0; rr < 4; ++rr) {
+                    const uint32_t a0 = (s < 2) ? xr[2 * rr].x : xr[2 * rr].y;
+                    const uint32_t a1 = (s < 2) ? xr[2 * rr + 1].x : xr[2 * rr + 1].y;
+                    vw[rr] = (s & 1) ? pair_hi(a0, a1) : pair_lo(a0, a1);
+                }
+                xf[s] = as_bf16x8(v);
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < RBW; ++k) {
+            const int I = wave + 4 * k;
+            if (I < 2 * js) continue;  // wave-uniform: no causal tile in this slab
+            const int icol = 16 * I + m;             // this lane's output row i
+            const float gi = Gs[icol];
+            uint32_t cw[2][2];
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const int J = 2 * js + u;
+                if (J > I) {
+                    cw[u][0] = 0u;
+                    cw[u][1] = 0u;
+                    continue;
+                }
+                // (C B^T)^T tile: cbt[e] = C_i . B_j, i = 16I + m, j = 16J + 4q + e
+                f32x4 cbt = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kn = 0; kn < NK; ++kn) {
+                    const uint4 bv = *reinterpret_cast<const uint4 *>(
+                        &Bs[buf][(16 * u + m) * HS + 32 * kn + 8 * q]);
+                    cbt = mfma16x16x32(as_bf16x8(bv), as_bf16x8(cf[k][kn]), cbt);
+                }
+                const int j0 = 16 * J + 4 * q;
+                float v[4];
+                if (J < I) {
+                    // exp2(G_i - G_j) dt_j = exp2(G_i - G_a) * V_j, a = 16J + 15
+                    const float ui = fast_exp2(gi - Gs[16 * J + 15]);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) v[e] = cbt[e] * (Vs[j0 + e] * ui);
+                } else {
+                    // diagonal block: exact pairwise decay, causal select (j <= i)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const float d = fminf(gi - Gs[j0 + e], 0.f);
+                        const float val = cbt[e] * fast_exp2(d) * DTs[j0 + e];
+                        v[e] = (4 * q + e <= m) ? val : 0.f;
+                    }
+                }
+                cw[u][0] = pack_bf16x2(v[0], v[1]);
+                cw[u][1] = pack_bf16x2(v[2], v[3]);
+            }
+            const bf16x8 af = as_bf16x8(make_uint4(cw[0][0], cw[0][1], cw[1][0], cw[1][1]));
+#pragma unroll
+            for (int s = 0; s < 4; ++s) acc[k][s] = mfma16x16x32(af, xf[s], acc[k][s]);
+        }
+        if (js + 1 < NS) slab_store(buf ^ 1, nxt);
+        __syncthreads();
+    }
+
+    // ---- y = acc + D x, fp32, 16 bytes per lane and row ----
+#pragma unroll
+    for (int k = 0; k < RBW; ++k) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int64_t tok = t0 + 16 * (wave + 4 * k) + 4 * q + e;
+            if (tok < T) {
+                const int64_t off = ((b * T + tok) * H + h) * P + 4 * m;
+                const uint2 xv = *reinterpret_cast<const uint2 *>(x + off);
+                const float4 o = make_float4(acc[k][0][e] + Dh * bf16_lo(xv.x),
+                                             acc[k][1][e] + Dh * bf16_hi(xv.x),
+                                             acc[k][2][e] + Dh * bf16_lo(xv.y),
+                                             acc[k][3][e] + Dh * bf16_hi(xv.y));
+                *reinterpret_cast<float4 *>(y + off) = o;
+            }
         }
     }
 }
@@ -284,7 +352,7 @@ hipError_t launch_scan(const Shape &s, const void *x, const void *B, const void 
     if (s.bf16)
         hipLaunchKernelGGL((chunk_scan_bf16_kernel<L, N>), dim3((uint32_t)nblk), dim3(256), 0, st,
                            (const uint16_t *)x, (const uint16_t *)B, (const uint16_t *)C, D, Gws,
-                           DTws, (const uint16_t *)hprev, (uint16_t *)y, s.T, (int32_t)s.H,
+                           DTws, (const uint16_t *)hprev, (float *)y, s.T, (int32_t)s.H,
                            (int32_t)s.G, (int32_t)s.nc, (uint32_t)nblk);
     else
         hipLaunchKernelGGL((chunk_scan_f32_kernel<L, N>), dim3((uint32_t)nblk), dim3(256), 0, st,

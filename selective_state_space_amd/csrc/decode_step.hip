@@ -18,7 +18,8 @@
 // 8 (N = 64) independent 16-byte loads per lane are in flight.  y[p] is the
 // sum over the N/4 lanes of a row, formed with xor shuffles inside the
 // wavefront: no LDS, no atomics.  B_t and C_t of the head's group (N values)
-// are read once per lane as 4-element vectors.
+// are read once per lane as 4-element vectors.  y is written fp32 (for bf16
+// inputs too: a bf16 y would carry a rounding of up to 2^-8 |y|).
 
 #include "ssd_device.h"
 #include "ssd_launch.h"
@@ -40,16 +41,12 @@ __device__ __forceinline__ float4 load4<uint16_t>(const uint16_t *p) {
 }
 __device__ __forceinline__ float load1(const float *p) { return *p; }
 __device__ __forceinline__ float load1(const uint16_t *p) { return bf16_to_f32(*p); }
-__device__ __forceinline__ void store1(float *p, float v) { *p = v; }
-__device__ __forceinline__ void store1(uint16_t *p, float v) {
-    *p = (uint16_t)f32_to_bf16_bits(v);
-}
 
 template <int N, typename Tio>
 __global__ __launch_bounds__(256) void decode_step_kernel(
     float *__restrict__ state, const Tio *__restrict__ x, const float *__restrict__ dt,
     const Tio *__restrict__ B, const Tio *__restrict__ C, const float *__restrict__ A,
-    const float *__restrict__ D, Tio *__restrict__ y, int32_t H, int32_t G) {
+    const float *__restrict__ D, float *__restrict__ y, int32_t H, int32_t G) {
     constexpr int P = 64;
     constexpr int LPR = N / 4;         // lanes per state row
     constexpr int RPI = 64 / LPR;      // rows per wavefront iteration
@@ -90,7 +87,7 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
         float part = ns.x * Cv.x + ns.y * Cv.y + ns.z * Cv.z + ns.w * Cv.w;
 #pragma unroll
         for (int off = LPR / 2; off > 0; off >>= 1) part += __shfl_xor(part, off, 64);
-        if (sub == 0) store1(y + bh * P + p, part + Dh * xv[k]);
+        if (sub == 0) y[bh * P + p] = part + Dh * xv[k];
     }
 }
 
@@ -101,7 +98,7 @@ hipError_t launch_dec(const Shape &s, float *state, const void *x, const float *
     if (s.bf16)
         hipLaunchKernelGGL((decode_step_kernel<N, uint16_t>), dim3((uint32_t)nblk), dim3(256), 0,
                            st, state, (const uint16_t *)x, dt, (const uint16_t *)B,
-                           (const uint16_t *)C, A, D, (uint16_t *)y, (int32_t)s.H, (int32_t)s.G);
+                           (const uint16_t *)C, A, D, (float *)y, (int32_t)s.H, (int32_t)s.G);
     else
         hipLaunchKernelGGL((decode_step_kernel<N, float>), dim3((uint32_t)nblk), dim3(256), 0, st,
                            state, (const float *)x, dt, (const float *)B, (const float *)C, A, D,

@@ -165,8 +165,8 @@ class FwdArgs:
         self.D = _need(D, "D", torch.float32, (H,), dev)
         self.init = None if init_state is None else _need(init_state, "init_state", torch.float32,
                                                          (Bt, H, P, N), dev)
-        self.y = (torch.empty_like(self.x) if y is None
-                  else _need(y, "y", io, (Bt, T, H, P), dev))
+        self.y = (torch.empty((Bt, T, H, P), dtype=torch.float32, device=dev) if y is None
+                  else _need(y, "y", torch.float32, (Bt, T, H, P), dev))
         if final_state is not None:
             self.final = _need(final_state, "final_state", torch.float32, (Bt, H, P, N), dev)
         elif want_final:
@@ -187,7 +187,8 @@ def ssd_chunked_fwd(x, dt, A, B, C, D, chunk_size: int, init_state=None, y=None,
     """Chunked forward.  Returns (y, final_state or None).
 
     x [Bt,T,H,P] (float32 or bfloat16), dt [Bt,T,H] f32, A/D [H] f32,
-    B/C [Bt,T,G,N] (x's dtype), init_state [Bt,H,P,N] f32 or None.  ``y``,
+    B/C [Bt,T,G,N] (x's dtype), init_state [Bt,H,P,N] f32 or None.  y is
+    float32 [Bt,T,H,P] whatever the input dtype.  ``y``,
     ``final_state`` and ``workspace`` may be passed in to avoid allocation;
     ``final_state`` may be the same tensor as ``init_state``.
     """
@@ -249,7 +250,7 @@ def workspace_views(a: FwdArgs):
 
 
 def ssd_decode_step(state, x_t, dt_t, B_t, C_t, A, D, y_t=None):
-    """One decode step; ``state`` [Bt,H,P,N] f32 is updated in place.  Returns y_t [Bt,H,P]."""
+    """One decode step; ``state`` [Bt,H,P,N] f32 is updated in place.  Returns y_t [Bt,H,P] f32."""
     dev = state.device
     if dev.type != "cuda":
         raise ValueError("tensors must live on a GPU device, got %s" % dev)
@@ -264,7 +265,8 @@ def ssd_decode_step(state, x_t, dt_t, B_t, C_t, A, D, y_t=None):
     C_t = _need(C_t, "C_t", io, (Bt, G, N), dev)
     A = _need(A, "A", torch.float32, (H,), dev)
     D = _need(D, "D", torch.float32, (H,), dev)
-    y_t = torch.empty_like(x_t) if y_t is None else _need(y_t, "y_t", io, (Bt, H, P), dev)
+    y_t = (torch.empty((Bt, H, P), dtype=torch.float32, device=dev) if y_t is None
+           else _need(y_t, "y_t", torch.float32, (Bt, H, P), dev))
     dims = Dims(Bt, 1, H, P, N, G, _io_code(io))
     lib = load_library()
     _check("ssd_decode_step", lib.ssd_decode_step(_ptr(state), _ptr(x_t), _ptr(dt_t), _ptr(B_t),
