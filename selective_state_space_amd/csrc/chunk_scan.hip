@@ -45,107 +45,125 @@ namespace ssd {
 
 namespace {
 
+// LDS image of one (b, h, chunk) unit, every MFMA operand stored in fragment
+// order (16 bytes per lane, lane-linear), so each operand is one
+// conflict-free ds_read_b128 at a constant offset.
 template <int L, int N>
-__global__ __launch_bounds__(256, 2) void chunk_scan_bf16_kernel(
-    const uint16_t *__restrict__ x, const uint16_t *__restrict__ Bm,
-    const uint16_t *__restrict__ Cm, const float *__restrict__ D, const float *__restrict__ Gws,
-    const float *__restrict__ DTws, const uint16_t *__restrict__ hprev, float *__restrict__ y,
-    int64_t T, int32_t H, int32_t G, int32_t nc, uint32_t nblk) {
-    constexpr int P = 64;
+struct ScanSmem {
+    static constexpr int NK = N / 32, NS = L / 32;
+    static constexpr int NBUF = 3;          // B ring: slab js in buffer js % 3
+    float G[L], V[L], DT[L];
+    uint4 XF[NS][4][64];                    // x^T fragments: slab js, p = 4m + s
+    union {
+        uint4 HF[NK][4][64];                // h_prev fragments (inter phase only)
+        uint4 BF[NBUF][2][NK][64];          // B fragments: buffer, 16-token block u, n-step kn
+    };
+};
+static_assert(sizeof(uint4[4][4][64]) <= sizeof(uint4[3][2][4][64]), "h_prev fits the B ring");
+
+template <int L, int N, bool RAGGED>
+__device__ __forceinline__ void chunk_scan_unit(
+    ScanSmem<L, N> &sm, const uint16_t *__restrict__ xb, const uint16_t *__restrict__ bb,
+    const uint16_t *__restrict__ cb, const float *__restrict__ Gp, const float *__restrict__ Dp,
+    const uint16_t *__restrict__ hp, float *__restrict__ yb, float Dh, int32_t nvalid,
+    int32_t XR, int32_t BR) {
     constexpr int NB = L / 16;       // 16-row blocks
-    constexpr int RBW = NB / 4;      // row blocks per wavefront
+    constexpr int RBW = NB / 4;      // row blocks per wavefront (1 when L = 64)
     constexpr int NK = N / 32;       // K steps over n
     constexpr int NS = L / 32;       // 32-token slabs
-    constexpr int HS = N + 8;        // padded LDS row strides (bf16 elements)
-    constexpr int XS = P + 8;
-    __shared__ float Gs[L], Vs[L], DTs[L];
-    __shared__ __attribute__((aligned(16))) uint16_t Hs[P * HS];
-    __shared__ __attribute__((aligned(16))) uint16_t Bs[2][32 * HS];
-    __shared__ __attribute__((aligned(16))) uint16_t Xs[2][32 * XS];
-
-    const uint32_t lid = xcd_remap(blockIdx.x, nblk);
-    const int32_t h = lid % H;
-    const int32_t c = (lid / H) % nc;
-    const int64_t b = lid / ((uint32_t)H * nc);
-    const int32_t g = h / (H / G);
+    constexpr int BPL = (2 * NK + 3) / 4;  // B-slab pieces per thread
     const int tid = threadIdx.x;
-    const int wave = tid >> 6;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
     const int lane = tid & 63;
     const int m = lane & 15, q = lane >> 4;
+    auto valid = [&](int tl) { return !RAGGED || tl < nvalid; };
 
-    const int64_t bhc = ((int64_t)b * H + h) * nc + c;
-    const float *Gp = Gws + bhc * L;
-    const float *Dp = DTws + bhc * L;
-    const uint16_t *Hp = hprev + bhc * (int64_t)(P * N);
-    const float Dh = D[h];
-    const int64_t t0 = (int64_t)c * L;
-
-    // ---- staging: G, dt, the column weights V, h_prev, slab 0 of B and x ----
-    // V_j = exp2(G_a - G_j) dt_j with a = the last token of j's 16-block
-    // (exponent <= 0): the column factor of the decay between blocks.
-    if (tid < L) {
-        const float gj = Gp[tid];
-        const float dj = Dp[tid];
-        Gs[tid] = gj;
-        DTs[tid] = dj;
-        Vs[tid] = fast_exp2(Gp[(tid | 15)] - gj) * dj;
-    }
-    for (int e = tid; e < P * (N / 8); e += 256) {
-        const int r = e / (N / 8), cc = (e % (N / 8)) * 8;
-        *reinterpret_cast<uint4 *>(&Hs[r * HS + cc]) =
-            *reinterpret_cast<const uint4 *>(Hp + r * N + cc);
-    }
-    // slab staging: B rows (N/8 16-byte pieces each) then x rows (8 pieces each)
-    constexpr int BPC = 32 * (N / 8);         // B pieces per slab
-    constexpr int XPC = 32 * 8;               // x pieces per slab
-    constexpr int PPT = (BPC + XPC) / 256;    // pieces per thread
-    static_assert((BPC + XPC) % 256 == 0, "slab pieces must spread evenly");
-    auto slab_load = [&](int js, uint4 (&v)[PPT]) {
+    // ---- staging, all global loads issued before the LDS writes ----
+    // x^T fragments of slabs js = w, w+4, ...: K slot r -> token
+    // 32 js + (r < 4 ? 0 : 16) + 4q + (r & 3), column m of MFMA s -> p = 4m + s
+    constexpr int XSW = (NS + 3) / 4;
+    uint2 xr[XSW][8];
 #pragma unroll
-        for (int k = 0; k < PPT; ++k) {
-            const int e = tid + 256 * k;
-            const bool isb = e < BPC;
-            const int ee = isb ? e : e - BPC;
-            const int r = isb ? ee / (N / 8) : ee / 8;
-            const int cc = isb ? (ee % (N / 8)) * 8 : (ee % 8) * 8;
-            const int64_t tok = t0 + 32 * js + r;
-            uint4 val = make_uint4(0u, 0u, 0u, 0u);
-            if (tok < T)
-                val = isb ? *reinterpret_cast<const uint4 *>(Bm + ((b * T + tok) * G + g) * N + cc)
-                          : *reinterpret_cast<const uint4 *>(x + ((b * T + tok) * H + h) * P + cc);
-            v[k] = val;
+    for (int k = 0; k < XSW; ++k) {
+        const int js = w + 4 * k;
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+            const int tl = 32 * js + ((r < 4) ? 0 : 16) + 4 * q + (r & 3);
+            xr[k][r] = (js < NS && valid(tl))
+                           ? *reinterpret_cast<const uint2 *>(xb + tl * XR + 4 * m)
+                           : make_uint2(0u, 0u);
+        }
+    }
+    constexpr int HPL = (NK * 4 + 3) / 4;   // h_prev pieces per thread
+    uint4 hv[HPL];
+#pragma unroll
+    for (int k = 0; k < HPL; ++k) {
+        const int pc = w + 4 * k, kn = pc >> 2, s = pc & 3;
+        hv[k] = (pc < NK * 4) ? *reinterpret_cast<const uint4 *>(hp + (4 * m + s) * N + 32 * kn + 8 * q)
+                              : make_uint4(0u, 0u, 0u, 0u);
+    }
+    auto bslab_load = [&](int js, uint4 (&v)[BPL]) {
+#pragma unroll
+        for (int k = 0; k < BPL; ++k) {
+            const int pc = w + 4 * k, u = pc / NK, kn = pc % NK;
+            const int tl = 32 * js + 16 * u + m;
+            v[k] = (pc < 2 * NK && valid(tl))
+                       ? *reinterpret_cast<const uint4 *>(bb + tl * BR + 32 * kn + 8 * q)
+                       : make_uint4(0u, 0u, 0u, 0u);
         }
     };
-    auto slab_store = [&](int buf, const uint4 (&v)[PPT]) {
+    auto bslab_store = [&](int buf, const uint4 (&v)[BPL]) {
 #pragma unroll
-        for (int k = 0; k < PPT; ++k) {
-            const int e = tid + 256 * k;
-            const bool isb = e < BPC;
-            const int ee = isb ? e : e - BPC;
-            if (isb)
-                *reinterpret_cast<uint4 *>(&Bs[buf][(ee / (N / 8)) * HS + (ee % (N / 8)) * 8]) = v[k];
-            else
-                *reinterpret_cast<uint4 *>(&Xs[buf][(ee / 8) * XS + (ee % 8) * 8]) = v[k];
+        for (int k = 0; k < BPL; ++k) {
+            const int pc = w + 4 * k;
+            if (pc < 2 * NK) sm.BF[buf][pc / NK][pc % NK][lane] = v[k];
         }
     };
-    {
-        uint4 v[PPT];
-        slab_load(0, v);
-        slab_store(0, v);
-    }
-
-    // C rows of this wavefront's row blocks I_k = wave + 4k (rows 16 I_k + m,
+    uint4 bv0[BPL];
+    bslab_load(0, bv0);
+    // C rows of this wavefront's row blocks I_k = w + 4k (rows 16 I_k + m,
     // n = 32 kn + 8q .. +7): A operand of the inter product and B operand of
     // the C B^T tiles, kept in registers for the whole chunk.
     uint4 cf[RBW][NK];
 #pragma unroll
     for (int k = 0; k < RBW; ++k) {
-        const int64_t tok = t0 + 16 * (wave + 4 * k) + m;
-        const uint16_t *cp = Cm + ((b * T + tok) * G + g) * N + 8 * q;
+        const int tl = 16 * (w + 4 * k) + m;
 #pragma unroll
         for (int kn = 0; kn < NK; ++kn)
-            cf[k][kn] = tok < T ? *reinterpret_cast<const uint4 *>(cp + 32 * kn)
-                                : make_uint4(0u, 0u, 0u, 0u);
+            cf[k][kn] = valid(tl) ? *reinterpret_cast<const uint4 *>(cb + tl * BR + 32 * kn + 8 * q)
+                                  : make_uint4(0u, 0u, 0u, 0u);
+    }
+    // G, dt and V_j = exp2(G_a - G_j) dt_j, a = the last token of j's
+    // 16-block (exponent <= 0): the column factor of the decay between blocks.
+    if (tid < L) {
+        const float gj = Gp[tid];
+        const float dj = Dp[tid];
+        sm.G[tid] = gj;
+        sm.DT[tid] = dj;
+        sm.V[tid] = fast_exp2(Gp[tid | 15] - gj) * dj;
+    }
+#pragma unroll
+    for (int k = 0; k < XSW; ++k) {
+        const int js = w + 4 * k;
+        if (js < NS) {
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                uint4 v;
+                uint32_t *vw = reinterpret_cast<uint32_t *>(&v);
+#pragma unroll
+                for (int rr = 0; rr < 4; ++rr) {
+                    const uint32_t a0 = (s < 2) ? xr[k][2 * rr].x : xr[k][2 * rr].y;
+                    const uint32_t a1 = (s < 2) ? xr[k][2 * rr + 1].x : xr[k][2 * rr + 1].y;
+                    vw[rr] = (s & 1) ? pair_hi(a0, a1) : pair_lo(a0, a1);
+                }
+                sm.XF[js][s][lane] = v;
+            }
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < HPL; ++k) {
+        const int pc = w + 4 * k;
+        if (pc < NK * 4) sm.HF[pc >> 2][pc & 3][lane] = hv[k];
     }
     __syncthreads();
 
@@ -160,56 +178,47 @@ __global__ __launch_bounds__(256, 2) void chunk_scan_bf16_kernel(
     for (int kn = 0; kn < NK; ++kn)
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
-            const uint4 hv = *reinterpret_cast<const uint4 *>(&Hs[(4 * m + s) * HS + 32 * kn + 8 * q]);
+            const bf16x8 hf = as_bf16x8(sm.HF[kn][s][lane]);
 #pragma unroll
             for (int k = 0; k < RBW; ++k)
-                acc[k][s] = mfma16x16x32(as_bf16x8(cf[k][kn]), as_bf16x8(hv), acc[k][s]);
+                acc[k][s] = mfma16x16x32(as_bf16x8(cf[k][kn]), hf, acc[k][s]);
         }
 #pragma unroll
     for (int k = 0; k < RBW; ++k) {
-        const int i0 = 16 * (wave + 4 * k) + 4 * q;
+        const float4 gi = *reinterpret_cast<const float4 *>(&sm.G[16 * (w + 4 * k) + 4 * q]);
+        const float sc[4] = {fast_exp2(gi.x), fast_exp2(gi.y), fast_exp2(gi.z), fast_exp2(gi.w)};
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const float sc = fast_exp2(Gs[i0 + e]);
+        for (int s = 0; s < 4; ++s)
 #pragma unroll
-            for (int s = 0; s < 4; ++s) acc[k][s][e] *= sc;
-        }
+            for (int e = 0; e < 4; ++e) acc[k][s][e] *= sc[e];
     }
 
-    // ---- intra: 32-token slabs in lockstep, next slab loaded during this one ----
-    for (int js = 0; js < NS; ++js) {
-        const int buf = js & 1;
-        uint4 nxt[PPT];
-        if (js + 1 < NS) slab_load(js + 1, nxt);
+    // h_prev fragments are dead: the B ring takes their place.  Slab 0 goes
+    // in now, slab 1 stays in registers until the end of step 0, and each
+    // step loads the slab two ahead, so a B load has two steps to land.
+    __syncthreads();
+    bslab_store(0, bv0);
+    uint4 nb1[BPL];
+    if (NS > 1) bslab_load(1, nb1);
+    __syncthreads();
 
-        // x rows of the slab as B operands: K slot r -> token (r < 4 ? 0 : 16) + 4q + (r & 3),
-        // column m of MFMA s -> p = 4m + s (transposed in registers)
+    // ---- intra: 32-token slabs in lockstep ----
+    for (int js = 0; js < NS; ++js) {
+        const int buf = js % 3;
+        uint4 nb2[BPL];
+        if (js + 2 < NS) bslab_load(js + 2, nb2);
         bf16x8 xf[4];
-        {
-            uint2 xr[8];
 #pragma unroll
-            for (int r = 0; r < 8; ++r)
-                xr[r] = *reinterpret_cast<const uint2 *>(
-                    &Xs[buf][((r < 4 ? 0 : 16) + 4 * q + (r & 3)) * XS + 4 * m]);
+        for (int s = 0; s < 4; ++s) xf[s] = as_bf16x8(sm.XF[js][s][lane]);
+        float4 vj[2];
 #pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                uint4 v;
-                uint32_t *vw = reinterpret_cast<uint32_t *>(&v);
-#pragma unroll
-                for (int rr = 0; rr < 4; ++rr) {
-                    const uint32_t a0 = (s < 2) ? xr[2 * rr].x : xr[2 * rr].y;
-                    const uint32_t a1 = (s < 2) ? xr[2 * rr + 1].x : xr[2 * rr + 1].y;
-                    vw[rr] = (s & 1) ? pair_hi(a0, a1) : pair_lo(a0, a1);
-                }
-                xf[s] = as_bf16x8(v);
-            }
-        }
+        for (int u = 0; u < 2; ++u)
+            vj[u] = *reinterpret_cast<const float4 *>(&sm.V[32 * js + 16 * u + 4 * q]);
 #pragma unroll
         for (int k = 0; k < RBW; ++k) {
-            const int I = wave + 4 * k;
-            if (I < 2 * js) continue;  // wave-uniform: no causal tile in this slab
-            const int icol = 16 * I + m;             // this lane's output row i
-            const float gi = Gs[icol];
+            const int I = w + 4 * k;
+            if (I < 2 * js) continue;  // no causal tile of this row block in the slab
+            const float gi = sm.G[16 * I + m];   // this lane's output row i = 16I + m
             uint32_t cw[2][2];
 #pragma unroll
             for (int u = 0; u < 2; ++u) {
@@ -219,27 +228,29 @@ __global__ __launch_bounds__(256, 2) void chunk_scan_bf16_kernel(
                     cw[u][1] = 0u;
                     continue;
                 }
-                // (C B^T)^T tile: cbt[e] = C_i . B_j, i = 16I + m, j = 16J + 4q + e
+                // (C B^T)^T tile: cbt[e] = C_i . B_j, j = 16J + 4q + e
                 f32x4 cbt = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int kn = 0; kn < NK; ++kn) {
-                    const uint4 bv = *reinterpret_cast<const uint4 *>(
-                        &Bs[buf][(16 * u + m) * HS + 32 * kn + 8 * q]);
-                    cbt = mfma16x16x32(as_bf16x8(bv), as_bf16x8(cf[k][kn]), cbt);
-                }
-                const int j0 = 16 * J + 4 * q;
+                for (int kn = 0; kn < NK; ++kn)
+                    cbt = mfma16x16x32(as_bf16x8(sm.BF[buf][u][kn][lane]), as_bf16x8(cf[k][kn]),
+                                       cbt);
                 float v[4];
                 if (J < I) {
                     // exp2(G_i - G_j) dt_j = exp2(G_i - G_a) * V_j, a = 16J + 15
-                    const float ui = fast_exp2(gi - Gs[16 * J + 15]);
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) v[e] = cbt[e] * (Vs[j0 + e] * ui);
+                    const float ui = fast_exp2(gi - sm.G[16 * J + 15]);
+                    v[0] = cbt[0] * (vj[u].x * ui);
+                    v[1] = cbt[1] * (vj[u].y * ui);
+                    v[2] = cbt[2] * (vj[u].z * ui);
+                    v[3] = cbt[3] * (vj[u].w * ui);
                 } else {
                     // diagonal block: exact pairwise decay, causal select (j <= i)
+                    const float4 gj = *reinterpret_cast<const float4 *>(&sm.G[16 * J + 4 * q]);
+                    const float4 dj = *reinterpret_cast<const float4 *>(&sm.DT[16 * J + 4 * q]);
+                    const float gjv[4] = {gj.x, gj.y, gj.z, gj.w};
+                    const float djv[4] = {dj.x, dj.y, dj.z, dj.w};
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
-                        const float d = fminf(gi - Gs[j0 + e], 0.f);
-                        const float val = cbt[e] * fast_exp2(d) * DTs[j0 + e];
+                        const float val = cbt[e] * fast_exp2(fminf(gi - gjv[e], 0.f)) * djv[e];
                         v[e] = (4 * q + e <= m) ? val : 0.f;
                     }
                 }
@@ -250,27 +261,71 @@ __global__ __launch_bounds__(256, 2) void chunk_scan_bf16_kernel(
 #pragma unroll
             for (int s = 0; s < 4; ++s) acc[k][s] = mfma16x16x32(af, xf[s], acc[k][s]);
         }
-        if (js + 1 < NS) slab_store(buf ^ 1, nxt);
+        if (js + 1 < NS) bslab_store((js + 1) % 3, nb1);
+#pragma unroll
+        for (int k = 0; k < BPL; ++k) nb1[k] = nb2[k];
         __syncthreads();
     }
 
-    // ---- y = acc + D x, fp32, 16 bytes per lane and row ----
+    // ---- y = acc + D x (x from this lane's own fragments), fp32 ----
 #pragma unroll
     for (int k = 0; k < RBW; ++k) {
+        const int I = w + 4 * k;
+        // token il = 16I + 4q + e sits in K slot e + 4 (I & 1) of this lane's
+        // fragment of slab I/2: words (x, y) hold slots 0..3, (z, w) slots 4..7
+        uint2 xw[4];
+        const bool odd = I & 1;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            const uint4 f = sm.XF[I >> 1][s][lane];
+            xw[s] = odd ? make_uint2(f.z, f.w) : make_uint2(f.x, f.y);
+        }
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            const int64_t tok = t0 + 16 * (wave + 4 * k) + 4 * q + e;
-            if (tok < T) {
-                const int64_t off = ((b * T + tok) * H + h) * P + 4 * m;
-                const uint2 xv = *reinterpret_cast<const uint2 *>(x + off);
-                const float4 o = make_float4(acc[k][0][e] + Dh * bf16_lo(xv.x),
-                                             acc[k][1][e] + Dh * bf16_hi(xv.x),
-                                             acc[k][2][e] + Dh * bf16_lo(xv.y),
-                                             acc[k][3][e] + Dh * bf16_hi(xv.y));
-                *reinterpret_cast<float4 *>(y + off) = o;
+            const int il = 16 * I + 4 * q + e;
+            if (valid(il)) {
+                float xv[4];
+#pragma unroll
+                for (int s = 0; s < 4; ++s) {
+                    const uint32_t wd = (e < 2) ? xw[s].x : xw[s].y;
+                    xv[s] = (e & 1) ? bf16_hi(wd) : bf16_lo(wd);
+                }
+                *reinterpret_cast<float4 *>(yb + il * XR + 4 * m) =
+                    make_float4(acc[k][0][e] + Dh * xv[0], acc[k][1][e] + Dh * xv[1],
+                                acc[k][2][e] + Dh * xv[2], acc[k][3][e] + Dh * xv[3]);
             }
         }
     }
+}
+
+template <int L, int N>
+__global__ __launch_bounds__(256, 2) void chunk_scan_bf16_kernel(
+    const uint16_t *__restrict__ x, const uint16_t *__restrict__ Bm,
+    const uint16_t *__restrict__ Cm, const float *__restrict__ D, const float *__restrict__ Gws,
+    const float *__restrict__ DTws, const uint16_t *__restrict__ hprev, float *__restrict__ y,
+    int64_t T, int32_t H, int32_t G, int32_t nc, uint32_t nblk) {
+    constexpr int P = 64;
+    __shared__ ScanSmem<L, N> sm;
+    const uint32_t lid = xcd_remap(blockIdx.x, nblk);
+    const int32_t h = lid % H;
+    const int32_t c = (lid / H) % nc;
+    const int64_t b = lid / ((uint32_t)H * nc);
+    const int32_t g = h / (H / G);
+    const int64_t t0 = (int64_t)c * L;
+    const int64_t bhc = ((int64_t)b * H + h) * nc + c;
+    const int64_t xrow0 = ((b * T + t0) * H + h) * P;      // x, y: token stride H * P
+    const int64_t brow0 = ((b * T + t0) * G + g) * N;      // B, C: token stride G * N
+    const int32_t XR = H * P, BR = G * N;
+    const int64_t rem = T - t0;
+    const int32_t nvalid = rem < L ? (int32_t)rem : L;
+    if (nvalid == L)
+        chunk_scan_unit<L, N, false>(sm, x + xrow0, Bm + brow0, Cm + brow0, Gws + bhc * L,
+                                     DTws + bhc * L, hprev + bhc * (int64_t)(P * N), y + xrow0,
+                                     D[h], nvalid, XR, BR);
+    else
+        chunk_scan_unit<L, N, true>(sm, x + xrow0, Bm + brow0, Cm + brow0, Gws + bhc * L,
+                                    DTws + bhc * L, hprev + bhc * (int64_t)(P * N), y + xrow0,
+                                    D[h], nvalid, XR, BR);
 }
 
 template <int L, int N>

@@ -7,21 +7,24 @@
 // section "Kernel 2" (the same product per chunk, operands scaled by dt and
 // the decay before the matrix product).  Every exponent G_last - G_j is <= 0.
 //
-// bf16 path (MFMA): one workgroup per (b, h, chunk), one wavefront per 64
-// state columns, heads fastest in the launch order (and kept on one XCD) so
-// the group's B tile is served from L2 to all heads that share it.  The
-// product is X^T diag(w) B with K = tokens, so both operands are read along
-// their slow axis.  Instead of an LDS transpose, each lane loads 8-byte row
-// segments (4 bf16) of 8 tokens and transposes them in registers into MFMA
-// operands (v_mfma_f32_16x16x32_bf16, 8 bf16 of K per lane):
-//   A operand, row m of MFMA s   = p = 4m + s        (64 rows in 4 MFMAs)
-//   B operand, col m of MFMA sn  = n = 64t + 4m + sn (64 columns per wavefront)
-// The weights w are folded into x (64 wide rather than N wide).  x*w is not
-// exact in bf16, and rounding it once costs up to 2^-9 of every term of S --
-// enough, where |S| runs far above its rms, to break a 2e-2 rms bound on the
-// final state -- so it is carried as a bf16 head plus a bf16 remainder (two
-// MFMAs, ~16 significant bits); B itself is exact.  The next 32-token slab is
-// loaded while the current one is multiplied.  Accumulation is fp32; S is
+// bf16 path (MFMA): one wavefront per (b, h, chunk), heads fastest in the
+// launch order (and kept on one XCD) so the group's B tile is served from L2
+// to all heads that share it.  The product is X^T diag(w) B with K = tokens,
+// so both operands are read along their slow axis.  Instead of an LDS
+// transpose, each lane loads 8-byte row segments (4 bf16) of 8 tokens and
+// transposes them in registers into MFMA operands (v_mfma_f32_16x16x32_bf16,
+// 8 bf16 of K per lane):
+//   A operand, row m of MFMA s        = p = 4m + s        (64 rows in 4 MFMAs)
+//   B operand, col m of MFMA (t, sn)  = n = 64t + 4m + sn (all N columns)
+// The weights w are folded into x (64 wide rather than N wide), once per slab
+// for all N columns.  x*w is not exact in bf16, and rounding it once costs up
+// to 2^-9 of every term of S -- enough, where |S| runs far above its rms, to
+// break a 2e-2 rms bound on the final state -- so it is carried as a bf16 head
+// plus a bf16 remainder (two MFMAs, ~16 significant bits); B itself is exact.
+// The whole 64 x N accumulator lives in AGPRs, so the wavefront runs alone on
+// its SIMD with a large register budget, and uses it to keep the raw loads of
+// two 32-token slabs in flight ahead of the one being multiplied.  Full chunks
+// take a path without per-token bounds checks.  Accumulation is fp32; S is
 // written fp32, 16 bytes a lane.
 //
 // fp32 path (VALU): one workgroup per (b, h, chunk); 32-token slices of X, B
@@ -34,49 +37,58 @@ namespace ssd {
 
 namespace {
 
-template <int L, int N>
-__global__ __launch_bounds__(N) void chunk_state_bf16_kernel(
-    const uint16_t *__restrict__ x, const uint16_t *__restrict__ B,
-    const float *__restrict__ Gws, const float *__restrict__ DTws, float *__restrict__ S,
-    int64_t T, int32_t H, int32_t G, int32_t nc, uint32_t nblk) {
+template <int L, int N, bool RAGGED>
+__device__ __forceinline__ void chunk_state_unit(
+    const uint16_t *__restrict__ xb, const uint16_t *__restrict__ bb,
+    const float *__restrict__ Gp, const float *__restrict__ Dp, float *__restrict__ Sp,
+    int32_t nvalid, int32_t XR, int32_t BR) {
     constexpr int P = 64;
-    const uint32_t lid = xcd_remap(blockIdx.x, nblk);
-    const int32_t h = lid % H;
-    const int32_t c = (lid / H) % nc;
-    const int64_t b = lid / ((uint32_t)H * nc);
-    const int32_t g = h / (H / G);
-    const int t = threadIdx.x >> 6;          // this wavefront's 64 columns: n = 64t ..
-    const int lane = threadIdx.x & 63;
+    constexpr int NT = N / 64;       // 64-column blocks of n
+    constexpr int KS = L / 32;       // 32-token steps
+    constexpr int DEPTH = 2;         // steps of raw loads in flight ahead of use
+    const int lane = threadIdx.x;
     const int m = lane & 15, q = lane >> 4;
-
-    const int64_t bhc = ((int64_t)b * H + h) * nc + c;
-    const float *Gp = Gws + bhc * L;
-    const float *Dp = DTws + bhc * L;
     const float glast = Gp[L - 1];
 
-    // acc[s][sn]: rows p = 4M + s (M = 4q + i), columns n = 64t + 4m + sn
-    f32x4 acc[4][4];
+    // this lane's rows within a step: token 8q + r, x at column 4m, B at 64t + 4m
+    int32_t xo[8], bo[8];
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+        xo[r] = (8 * q + r) * XR + 4 * m;
+        bo[r] = (8 * q + r) * BR + 4 * m;
+    }
+    struct Raw {
+        uint2 x[8], b[NT][8];
+    };
+    auto load = [&](int ks, Raw &v) {
+        const uint16_t *xs = xb + (32 * ks) * XR;
+        const uint16_t *bs = bb + (32 * ks) * BR;
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+            const bool ok = !RAGGED || 32 * ks + 8 * q + r < nvalid;
+            v.x[r] = ok ? *reinterpret_cast<const uint2 *>(xs + xo[r]) : make_uint2(0u, 0u);
+#pragma unroll
+            for (int t = 0; t < NT; ++t)
+                v.b[t][r] = ok ? *reinterpret_cast<const uint2 *>(bs + bo[r] + 64 * t)
+                               : make_uint2(0u, 0u);
+        }
+    };
+
+    // acc[s][c]: rows p = 4M + s (M = 4q + i), columns n = 64t + 4m + sn, c = 4t + sn
+    f32x4 acc[4][NT * 4];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int k = 0; k < 4; ++k) acc[i][k] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int k = 0; k < NT * 4; ++k) acc[i][k] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    uint2 xr[8], br[8];
-    auto load = [&](int ks) {
-        const int j0 = 32 * ks + 8 * q;
+    Raw ring[DEPTH + 1];
 #pragma unroll
-        for (int r = 0; r < 8; ++r) {
-            const int64_t tok = (int64_t)c * L + j0 + r;
-            const bool ok = tok < T;
-            const int64_t bt = b * T + tok;
-            xr[r] = ok ? *reinterpret_cast<const uint2 *>(x + (bt * H + h) * P + 4 * m)
-                       : make_uint2(0u, 0u);
-            br[r] = ok ? *reinterpret_cast<const uint2 *>(B + (bt * G + g) * N + 64 * t + 4 * m)
-                       : make_uint2(0u, 0u);
-        }
-    };
-    load(0);
-    for (int ks = 0; ks < L / 32; ++ks) {
+    for (int d = 0; d < DEPTH; ++d)
+        if (d < KS) load(d, ring[d]);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+        if (ks + DEPTH < KS) load(ks + DEPTH, ring[(ks + DEPTH) % (DEPTH + 1)]);
+        const Raw &cur = ring[ks % (DEPTH + 1)];
         const int j0 = 32 * ks + 8 * q;  // this lane's 8 tokens: j0 .. j0+7
         float w[8];
         {
@@ -93,9 +105,8 @@ __global__ __launch_bounds__(N) void chunk_state_bf16_kernel(
             w[6] = d1.z * fast_exp2(glast - g1.z);
             w[7] = d1.w * fast_exp2(glast - g1.w);
         }
-        // A operands: x * w transposed (row m of MFMA s is p = 4m + s), split
-        // into a bf16 head and the bf16 rounding of the remainder, so the
-        // product carries ~16 significant bits; B is exact in bf16.
+        // A operands: x * w transposed (row m of MFMA s is p = 4m + s), as a
+        // bf16 head and the bf16 rounding of the remainder
         bf16x8 ahi[4], alo[4];
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
@@ -104,8 +115,8 @@ __global__ __launch_bounds__(N) void chunk_state_bf16_kernel(
             uint32_t *wl = reinterpret_cast<uint32_t *>(&vl);
 #pragma unroll
             for (int rr = 0; rr < 4; ++rr) {
-                const uint32_t a0 = (s < 2) ? xr[2 * rr].x : xr[2 * rr].y;
-                const uint32_t a1 = (s < 2) ? xr[2 * rr + 1].x : xr[2 * rr + 1].y;
+                const uint32_t a0 = (s < 2) ? cur.x[2 * rr].x : cur.x[2 * rr].y;
+                const uint32_t a1 = (s < 2) ? cur.x[2 * rr + 1].x : cur.x[2 * rr + 1].y;
                 const float e0 = ((s & 1) ? bf16_hi(a0) : bf16_lo(a0)) * w[2 * rr];
                 const float e1 = ((s & 1) ? bf16_hi(a1) : bf16_lo(a1)) * w[2 * rr + 1];
                 const uint32_t hw = pack_bf16x2(e0, e1);
@@ -115,40 +126,68 @@ __global__ __launch_bounds__(N) void chunk_state_bf16_kernel(
             ahi[s] = as_bf16x8(vh);
             alo[s] = as_bf16x8(vl);
         }
-        // B operands: B rows transposed (column m of MFMA sn is n = 64t + 4m + sn)
-        bf16x8 bfr[4];
+        // B operands: B rows transposed (column m of MFMA (t, sn) is n = 64t + 4m + sn)
 #pragma unroll
-        for (int sn = 0; sn < 4; ++sn) {
-            uint4 v;
-            uint32_t *vw = reinterpret_cast<uint32_t *>(&v);
+        for (int t = 0; t < NT; ++t)
 #pragma unroll
-            for (int rr = 0; rr < 4; ++rr) {
-                const uint32_t a0 = (sn < 2) ? br[2 * rr].x : br[2 * rr].y;
-                const uint32_t a1 = (sn < 2) ? br[2 * rr + 1].x : br[2 * rr + 1].y;
-                vw[rr] = (sn & 1) ? pair_hi(a0, a1) : pair_lo(a0, a1);
-            }
-            bfr[sn] = as_bf16x8(v);
-        }
-        if (ks + 1 < L / 32) load(ks + 1);   // next slab in flight during the MFMAs
+            for (int sn = 0; sn < 4; ++sn) {
+                uint4 v;
+                uint32_t *vw = reinterpret_cast<uint32_t *>(&v);
 #pragma unroll
-        for (int sn = 0; sn < 4; ++sn)
+                for (int rr = 0; rr < 4; ++rr) {
+                    const uint32_t a0 = (sn < 2) ? cur.b[t][2 * rr].x : cur.b[t][2 * rr].y;
+                    const uint32_t a1 =
+                        (sn < 2) ? cur.b[t][2 * rr + 1].x : cur.b[t][2 * rr + 1].y;
+                    vw[rr] = (sn & 1) ? pair_hi(a0, a1) : pair_lo(a0, a1);
+                }
+                const bf16x8 bfr = as_bf16x8(v);
 #pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                acc[s][sn] = mfma16x16x32(ahi[s], bfr[sn], acc[s][sn]);
-                acc[s][sn] = mfma16x16x32(alo[s], bfr[sn], acc[s][sn]);
+                for (int s = 0; s < 4; ++s) {
+                    acc[s][4 * t + sn] = mfma16x16x32(ahi[s], bfr, acc[s][4 * t + sn]);
+                    acc[s][4 * t + sn] = mfma16x16x32(alo[s], bfr, acc[s][4 * t + sn]);
+                }
             }
     }
 
     // D layout: lane holds rows M = 4q + i (i = 0..3) of column m.
-    float *Sp = S + bhc * (int64_t)(P * N);
 #pragma unroll
     for (int s = 0; s < 4; ++s)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int p = 4 * (4 * q + i) + s;
-            const float4 v = make_float4(acc[s][0][i], acc[s][1][i], acc[s][2][i], acc[s][3][i]);
-            *reinterpret_cast<float4 *>(Sp + p * N + 64 * t + 4 * m) = v;
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+                const float4 v = make_float4(acc[s][4 * t + 0][i], acc[s][4 * t + 1][i],
+                                             acc[s][4 * t + 2][i], acc[s][4 * t + 3][i]);
+                *reinterpret_cast<float4 *>(Sp + p * N + 64 * t + 4 * m) = v;
+            }
         }
+}
+
+template <int L, int N>
+__global__ __launch_bounds__(64, 1) void chunk_state_bf16_kernel(
+    const uint16_t *__restrict__ x, const uint16_t *__restrict__ B,
+    const float *__restrict__ Gws, const float *__restrict__ DTws, float *__restrict__ S,
+    int64_t T, int32_t H, int32_t G, int32_t nc, uint32_t nblk) {
+    constexpr int P = 64;
+    const uint32_t lid = xcd_remap(blockIdx.x, nblk);
+    const int32_t h = lid % H;
+    const int32_t c = (lid / H) % nc;
+    const int64_t b = lid / ((uint32_t)H * nc);
+    const int32_t g = h / (H / G);
+    const int64_t t0 = (int64_t)c * L;
+    const int64_t bhc = ((int64_t)b * H + h) * nc + c;
+    const int64_t rem = T - t0;
+    const int32_t nvalid = rem < L ? (int32_t)rem : L;
+    const uint16_t *xb = x + ((b * T + t0) * H + h) * P;
+    const uint16_t *bb = B + ((b * T + t0) * G + g) * N;
+    float *Sp = S + bhc * (int64_t)(P * N);
+    if (nvalid == L)
+        chunk_state_unit<L, N, false>(xb, bb, Gws + bhc * L, DTws + bhc * L, Sp, nvalid, H * P,
+                                      G * N);
+    else
+        chunk_state_unit<L, N, true>(xb, bb, Gws + bhc * L, DTws + bhc * L, Sp, nvalid, H * P,
+                                     G * N);
 }
 
 template <int L, int N>
@@ -212,7 +251,7 @@ hipError_t launch_cs(const Shape &s, const void *x, const void *B, const float *
                      const float *DTws, float *S, hipStream_t st) {
     const uint64_t nblk = (uint64_t)s.Bt * s.nc * s.H;
     if (s.bf16) {
-        hipLaunchKernelGGL((chunk_state_bf16_kernel<L, N>), dim3((uint32_t)nblk), dim3(N), 0, st,
+        hipLaunchKernelGGL((chunk_state_bf16_kernel<L, N>), dim3((uint32_t)nblk), dim3(64), 0, st,
                            (const uint16_t *)x, (const uint16_t *)B, Gws, DTws, S, s.T,
                            (int32_t)s.H, (int32_t)s.G, (int32_t)s.nc, (uint32_t)nblk);
     } else {
