@@ -30,6 +30,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, published
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_mamba2_2p7b.json")
 BF16_PEAK_TFLOPS = 2500.0       # MI355X dense bf16 MFMA, published
 FP32_VALU_PEAK_TFLOPS = 157.3   # MI355X fp32 vector, published
 
@@ -76,6 +77,31 @@ def decode_bytes(w, io_bytes=2):
     # state read + write, x_t in, y_t out (fp32), dt_t, B_t and C_t
     return (2 * Bt * H * P * N * 4 + Bt * H * P * (io_bytes + 4) + Bt * H * 4
             + 2 * Bt * G * N * io_bytes)
+
+
+def kernel_source_sha(kernel: str) -> str:
+    """Hash of the sources a kernel is built from (its .hip file and the shared headers)."""
+    import hashlib
+    csrc = os.path.join(ROOT, "selective_state_space_amd", "csrc")
+    h = hashlib.sha256()
+    for f in (kernel + ".hip", "ssd_device.h", "ssd_launch.h"):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE
+    summary, or None if there is none for this kernel or its source changed since."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            rec = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    k = rec.get("kernels", {}).get(kernel)
+    if not k or rec.get("workload") != workload or k.get("source_sha") != kernel_source_sha(kernel):
+        return None
+    return int(k["hbm_bytes_per_launch"])
 
 
 # ---- the GPU legs ----------------------------------------------------------------------
@@ -261,7 +287,7 @@ def main():
     achieved = alg[dom]["bytes"] / (dms * 1e-3) / 1e9
     roofline = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1),
                 "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                "traffic": None,
+                "traffic": measured_traffic(dom, w.name),
                 "avg_launch_us": round(dms * 1e3, 2), "alg_bytes_per_launch": int(alg[dom]["bytes"])}
     chunk_flops = alg["chunk_state"]["flops"] + alg["chunk_scan"]["flops"]
     chunk_ms = kern["chunk_state"] + kern["chunk_scan"]
