@@ -11,28 +11,30 @@
 // "mamba3" kernel card ("Method") folds the causal weight and the decay into
 // the drain of the first product's accumulator.
 //
-// bf16 path (MFMA, v_mfma_f32_16x16x32_bf16): one workgroup of 4 wavefronts
-// per (b, h, chunk), heads fastest and kept on one XCD so the group's B and C
-// come from L2.  Wavefront w owns the 16-row blocks I = w, w+4, ... of the
-// chunk and keeps their C rows in registers (A operand of the inter product,
-// B operand of the C B^T tiles).  h_prev, G, dt and the column factors V are
-// staged in LDS once; B and x go through LDS in 32-token slabs, the next slab
-// loaded while the current one is used (all wavefronts in lockstep).
+// bf16 path (MFMA, v_mfma_f32_16x16x32_bf16): one workgroup per (b, chunk,
+// group, block of heads), heads of the block processed in turn.  C B^T depends
+// only on the group, so it is formed once per workgroup and reused by every
+// head: the chunk's B and C are staged in LDS as MFMA fragments (16 bytes per
+// lane, lane-linear: every operand read is one conflict-free ds_read_b128),
+// and each wavefront computes the causal 16x16 tiles of its row blocks --
+// paired (I, L/16-1-I) so every wavefront holds the same number of tiles --
+// and keeps them in registers as packed bf16 for all heads.  Row-block
+// ownership is a template parameter (the wavefront index is dispatched once),
+// so every tile index is a compile-time register index.
+// Per head (its x^T fragments, h_prev fragments, G, dt and column factors V
+// staged in LDS; the next head's loads are in flight while this one runs):
 //   1. inter: acc = C h_prev^T (K = N); output column m of MFMA s is p = 4m+s.
 //      Rows are then scaled by exp2(G_i).
-//   2. intra, per slab: two 16x16 tiles of (C B^T)^T = B C^T per row block
-//      (A = B rows from LDS).  The accumulator layout of a transposed tile
-//      (lane m: column i, rows j = 4q..4q+3) is a 4-element K slice of the A
-//      operand for row i, so the drain -- times exp2(G_i - G_j) dt_j, select
-//      j <= i, round to bf16 -- leaves the A operand of the second product in
-//      place, with no LDS round trip.  The matching B operand (x rows of the
-//      same tokens, 4 p per lane) is transposed in registers.  Tiles above the
-//      diagonal are skipped.  Below the diagonal the decay factors through
-//      the last token a of the column block: exp2(G_i - G_j) = exp2(G_i - G_a)
-//      * exp2(G_a - G_j), both exponents <= 0, so a tile needs one exp2 per
-//      lane (V_j = exp2(G_a - G_j) dt_j is staged per token).  Diagonal tiles
-//      use the exact pairwise exponent with a causal select.
-//   3. y = acc + D x, written fp32 (16 bytes a lane and row).
+//   2. intra: each cached tile (C B^T)^T (lane m: column i, rows j = 4q..4q+3)
+//      is a 4-element K slice of the A operand for row i, so the drain --
+//      times exp2(G_i - G_j) dt_j, select j <= i, round to bf16 -- produces the
+//      A operand of the second product in registers, with no LDS round trip.
+//      Below the diagonal the decay factors through the last token a of the
+//      column block: exp2(G_i - G_j) = exp2(G_i - G_a) * exp2(G_a - G_j), both
+//      exponents <= 0, so a tile needs one exp2 per lane (V_j = exp2(G_a - G_j)
+//      dt_j is staged per token).  Diagonal tiles use the exact pairwise
+//      exponent with a causal select.  Tiles above the diagonal do not exist.
+//   3. y = acc + D x (x from the lane's own fragment), written fp32.
 //
 // fp32 path (VALU): one workgroup per (b, h, chunk), 16-row tiles: the
 // decayed, masked C B^T rows are built in LDS, then each thread forms y for
@@ -45,106 +47,117 @@ namespace ssd {
 
 namespace {
 
-// LDS image of one (b, h, chunk) unit, every MFMA operand stored in fragment
-// order (16 bytes per lane, lane-linear), so each operand is one
-// conflict-free ds_read_b128 at a constant offset.
+// Wavefronts per workgroup: 8 for 256-token chunks (each owns one row-block
+// pair), 4 otherwise.
+template <int L>
+struct ScanWaves {
+    static constexpr int NW = L == 256 ? 8 : 4;
+};
+
+// Row blocks (16 rows each) owned by wavefront W of NW, paired (I, NB-1-I) so
+// that every wavefront holds the same number of causal tiles (NB + 1 per pair).
+template <int NB, int NW, int W>
+struct RowBlocks {
+    static constexpr int RBW = NB >= 2 * NW ? NB / NW : 1;
+    static constexpr int at(int k) {
+        // NB == 2 NW: one pair per wavefront; NB == 4 NW: two pairs; NB == NW: one block
+        return NB == NW ? W
+                        : (NB == 2 * NW ? (k == 0 ? W : NB - 1 - W)
+                                        : (k == 0 ? W : k == 1 ? NB - 1 - W
+                                                        : k == 2 ? W + NW : NB - 1 - NW - W));
+    }
+    static constexpr int tiles_before(int k) {
+        int t = 0;
+        for (int i = 0; i < k; ++i) t += at(i) + 1;
+        return t;
+    }
+    static constexpr int ntiles = tiles_before(RBW);
+};
+
+// LDS of one workgroup: first the chunk's B as MFMA fragments (to form the
+// C B^T tiles once), then -- reusing the same bytes -- two buffers of per-head
+// data, every operand in fragment order (16 bytes per lane, lane-linear), so
+// each operand read is one conflict-free ds_read_b128 at a constant offset.
 template <int L, int N>
 struct ScanSmem {
-    static constexpr int NK = N / 32, NS = L / 32;
-    static constexpr int NBUF = 3;          // B ring: slab js in buffer js % 3
-    float G[L], V[L], DT[L];
-    uint4 XF[NS][4][64];                    // x^T fragments: slab js, p = 4m + s
+    static constexpr int NK = N / 32, NS = L / 32, NB = L / 16;
+    struct Head {
+        uint4 XF[NS][4][64];  // x^T fragments: slab js, p = 4m + s
+        uint4 HF[NK][4][64];  // h_prev fragments: n-step kn, p = 4m + s
+        float G[L], V[L], DT[L];
+    };
+    uint4 CF[NB][NK][64];      // C fragments: 16-token block I, n-step kn (whole workgroup life)
     union {
-        uint4 HF[NK][4][64];                // h_prev fragments (inter phase only)
-        uint4 BF[NBUF][2][NK][64];          // B fragments: buffer, 16-token block u, n-step kn
+        uint4 BF[NB][NK][64];  // B fragments (C B^T phase only)
+        Head hd;               // the head being computed
     };
 };
-static_assert(sizeof(uint4[4][4][64]) <= sizeof(uint4[3][2][4][64]), "h_prev fits the B ring");
+
+template <int L, int N>
+struct ScanArgs {
+    const uint16_t *x, *Bm, *Cm, *hprev;
+    const float *D, *Gws, *DTws;
+    float *y;
+    int64_t T;
+    int32_t H, G, nc, hpg, NH, nhb;
+};
+
+// Everything one head of the workgroup needs, loaded into registers (issued
+// one head ahead of use) and then written to an LDS head buffer.
+template <int L, int N>
+struct HeadRegs {
+    static constexpr int NS = L / 32, NK = N / 32, NW = ScanWaves<L>::NW;
+    static constexpr int XSW = (NS + NW - 1) / NW;
+    static constexpr int HPL = (NK * 4 + NW - 1) / NW;
+    uint2 xr[XSW][8];
+    uint4 hv[HPL];
+    float g, gl, dt;
+};
 
 template <int L, int N, bool RAGGED>
-__device__ __forceinline__ void chunk_scan_unit(
-    ScanSmem<L, N> &sm, const uint16_t *__restrict__ xb, const uint16_t *__restrict__ bb,
-    const uint16_t *__restrict__ cb, const float *__restrict__ Gp, const float *__restrict__ Dp,
-    const uint16_t *__restrict__ hp, float *__restrict__ yb, float Dh, int32_t nvalid,
-    int32_t XR, int32_t BR) {
-    constexpr int NB = L / 16;       // 16-row blocks
-    constexpr int RBW = NB / 4;      // row blocks per wavefront (1 when L = 64)
-    constexpr int NK = N / 32;       // K steps over n
-    constexpr int NS = L / 32;       // 32-token slabs
-    constexpr int BPL = (2 * NK + 3) / 4;  // B-slab pieces per thread
-    const int tid = threadIdx.x;
-    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
-    const int lane = tid & 63;
-    const int m = lane & 15, q = lane >> 4;
-    auto valid = [&](int tl) { return !RAGGED || tl < nvalid; };
-
-    // ---- staging, all global loads issued before the LDS writes ----
-    // x^T fragments of slabs js = w, w+4, ...: K slot r -> token
-    // 32 js + (r < 4 ? 0 : 16) + 4q + (r & 3), column m of MFMA s -> p = 4m + s
-    constexpr int XSW = (NS + 3) / 4;
-    uint2 xr[XSW][8];
+__device__ __forceinline__ void head_load(HeadRegs<L, N> &r, const ScanArgs<L, N> &a, int64_t b,
+                                          int32_t h, int32_t c, int32_t nvalid, int w, int lane) {
+    constexpr int P = 64, NS = L / 32, NK = N / 32, NW = ScanWaves<L>::NW;
+    const int m = lane & 15, q = lane >> 4, tid = 64 * w + lane;
+    const int64_t t0 = (int64_t)c * L;
+    const uint16_t *xb = a.x + ((b * a.T + t0) * a.H + h) * P;
+    const int32_t XR = a.H * P;
 #pragma unroll
-    for (int k = 0; k < XSW; ++k) {
-        const int js = w + 4 * k;
+    for (int k = 0; k < HeadRegs<L, N>::XSW; ++k) {
+        const int js = w + NW * k;
 #pragma unroll
-        for (int r = 0; r < 8; ++r) {
-            const int tl = 32 * js + ((r < 4) ? 0 : 16) + 4 * q + (r & 3);
-            xr[k][r] = (js < NS && valid(tl))
-                           ? *reinterpret_cast<const uint2 *>(xb + tl * XR + 4 * m)
-                           : make_uint2(0u, 0u);
+        for (int rr = 0; rr < 8; ++rr) {
+            const int tl = 32 * js + ((rr < 4) ? 0 : 16) + 4 * q + (rr & 3);
+            r.xr[k][rr] = (js < NS && (!RAGGED || tl < nvalid))
+                              ? *reinterpret_cast<const uint2 *>(xb + tl * XR + 4 * m)
+                              : make_uint2(0u, 0u);
         }
     }
-    constexpr int HPL = (NK * 4 + 3) / 4;   // h_prev pieces per thread
-    uint4 hv[HPL];
+    const int64_t bhc = ((int64_t)b * a.H + h) * a.nc + c;
+    const uint16_t *hp = a.hprev + bhc * (int64_t)(P * N);
 #pragma unroll
-    for (int k = 0; k < HPL; ++k) {
-        const int pc = w + 4 * k, kn = pc >> 2, s = pc & 3;
-        hv[k] = (pc < NK * 4) ? *reinterpret_cast<const uint4 *>(hp + (4 * m + s) * N + 32 * kn + 8 * q)
-                              : make_uint4(0u, 0u, 0u, 0u);
+    for (int k = 0; k < HeadRegs<L, N>::HPL; ++k) {
+        const int pc = w + NW * k, kn = pc >> 2, s = pc & 3;
+        r.hv[k] = (pc < NK * 4)
+                      ? *reinterpret_cast<const uint4 *>(hp + (4 * m + s) * N + 32 * kn + 8 * q)
+                      : make_uint4(0u, 0u, 0u, 0u);
     }
-    auto bslab_load = [&](int js, uint4 (&v)[BPL]) {
-#pragma unroll
-        for (int k = 0; k < BPL; ++k) {
-            const int pc = w + 4 * k, u = pc / NK, kn = pc % NK;
-            const int tl = 32 * js + 16 * u + m;
-            v[k] = (pc < 2 * NK && valid(tl))
-                       ? *reinterpret_cast<const uint4 *>(bb + tl * BR + 32 * kn + 8 * q)
-                       : make_uint4(0u, 0u, 0u, 0u);
-        }
-    };
-    auto bslab_store = [&](int buf, const uint4 (&v)[BPL]) {
-#pragma unroll
-        for (int k = 0; k < BPL; ++k) {
-            const int pc = w + 4 * k;
-            if (pc < 2 * NK) sm.BF[buf][pc / NK][pc % NK][lane] = v[k];
-        }
-    };
-    uint4 bv0[BPL];
-    bslab_load(0, bv0);
-    // C rows of this wavefront's row blocks I_k = w + 4k (rows 16 I_k + m,
-    // n = 32 kn + 8q .. +7): A operand of the inter product and B operand of
-    // the C B^T tiles, kept in registers for the whole chunk.
-    uint4 cf[RBW][NK];
-#pragma unroll
-    for (int k = 0; k < RBW; ++k) {
-        const int tl = 16 * (w + 4 * k) + m;
-#pragma unroll
-        for (int kn = 0; kn < NK; ++kn)
-            cf[k][kn] = valid(tl) ? *reinterpret_cast<const uint4 *>(cb + tl * BR + 32 * kn + 8 * q)
-                                  : make_uint4(0u, 0u, 0u, 0u);
-    }
-    // G, dt and V_j = exp2(G_a - G_j) dt_j, a = the last token of j's
-    // 16-block (exponent <= 0): the column factor of the decay between blocks.
     if (tid < L) {
-        const float gj = Gp[tid];
-        const float dj = Dp[tid];
-        sm.G[tid] = gj;
-        sm.DT[tid] = dj;
-        sm.V[tid] = fast_exp2(Gp[tid | 15] - gj) * dj;
+        const float *Gp = a.Gws + bhc * L;
+        r.g = Gp[tid];
+        r.gl = Gp[tid | 15];
+        r.dt = a.DTws[bhc * L + tid];
     }
+}
+
+template <int L, int N>
+__device__ __forceinline__ void head_store(typename ScanSmem<L, N>::Head &hd,
+                                           const HeadRegs<L, N> &r, int w, int lane) {
+    constexpr int NS = L / 32, NK = N / 32, NW = ScanWaves<L>::NW;
+    const int tid = 64 * w + lane;
 #pragma unroll
-    for (int k = 0; k < XSW; ++k) {
-        const int js = w + 4 * k;
+    for (int k = 0; k < HeadRegs<L, N>::XSW; ++k) {
+        const int js = w + NW * k;
         if (js < NS) {
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
@@ -152,180 +165,262 @@ __device__ __forceinline__ void chunk_scan_unit(
                 uint32_t *vw = reinterpret_cast<uint32_t *>(&v);
 #pragma unroll
                 for (int rr = 0; rr < 4; ++rr) {
-                    const uint32_t a0 = (s < 2) ? xr[k][2 * rr].x : xr[k][2 * rr].y;
-                    const uint32_t a1 = (s < 2) ? xr[k][2 * rr + 1].x : xr[k][2 * rr + 1].y;
+                    const uint32_t a0 = (s < 2) ? r.xr[k][2 * rr].x : r.xr[k][2 * rr].y;
+                    const uint32_t a1 = (s < 2) ? r.xr[k][2 * rr + 1].x : r.xr[k][2 * rr + 1].y;
                     vw[rr] = (s & 1) ? pair_hi(a0, a1) : pair_lo(a0, a1);
                 }
-                sm.XF[js][s][lane] = v;
+                hd.XF[js][s][lane] = v;
             }
         }
     }
 #pragma unroll
-    for (int k = 0; k < HPL; ++k) {
-        const int pc = w + 4 * k;
-        if (pc < NK * 4) sm.HF[pc >> 2][pc & 3][lane] = hv[k];
+    for (int k = 0; k < HeadRegs<L, N>::HPL; ++k) {
+        const int pc = w + NW * k;
+        if (pc < NK * 4) hd.HF[pc >> 2][pc & 3][lane] = r.hv[k];
     }
-    __syncthreads();
+    if (tid < L) {
+        // V_j = exp2(G_a - G_j) dt_j, a = the last token of j's 16-block
+        // (exponent <= 0): the column factor of the decay between blocks.
+        hd.G[tid] = r.g;
+        hd.DT[tid] = r.dt;
+        hd.V[tid] = fast_exp2(r.gl - r.g) * r.dt;
+    }
+}
 
-    // ---- inter: acc = C h_prev^T, then rows scaled by exp2(G_i) ----
-    // acc[k][s][e] = y[i = 16 I_k + 4q + e][p = 4m + s]
-    f32x4 acc[RBW][4];
+template <int L, int N, bool RAGGED, int W>
+__device__ __forceinline__ void chunk_scan_group(ScanSmem<L, N> &sm, const ScanArgs<L, N> &a,
+                                                 int64_t b, int32_t c, int32_t g, int32_t h0,
+                                                 int32_t nh, int32_t nvalid) {
+    constexpr int P = 64;
+    constexpr int NB = L / 16, NK = N / 32, NS = L / 32, NW = ScanWaves<L>::NW;
+    using RB = RowBlocks<NB, NW, W>;
+    constexpr int RBW = RB::RBW;
+    constexpr int NT = RB::ntiles;
+    const int lane = threadIdx.x & 63;
+    const int m = lane & 15, q = lane >> 4, tid = threadIdx.x;
+    const int64_t t0 = (int64_t)c * L;
+    const uint16_t *bb = a.Bm + ((b * a.T + t0) * a.G + g) * N;
+    const uint16_t *cb = a.Cm + ((b * a.T + t0) * a.G + g) * N;
+    const int32_t BR = a.G * N;
+    auto valid = [&](int tl) { return !RAGGED || tl < nvalid; };
+
+    // ---- the group's C B^T tiles, once for all heads of the workgroup ----
+    HeadRegs<L, N> pre;
+    head_load<L, N, RAGGED>(pre, a, b, h0, c, nvalid, W, lane);   // first head, in flight now
+    {
+        constexpr int PPT = NB * NK / NW;   // B (and C) pieces per thread
+        uint4 bv[PPT], cv[PPT];
 #pragma unroll
-    for (int k = 0; k < RBW; ++k)
-#pragma unroll
-        for (int s = 0; s < 4; ++s) acc[k][s] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int kn = 0; kn < NK; ++kn)
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            const bf16x8 hf = as_bf16x8(sm.HF[kn][s][lane]);
-#pragma unroll
-            for (int k = 0; k < RBW; ++k)
-                acc[k][s] = mfma16x16x32(as_bf16x8(cf[k][kn]), hf, acc[k][s]);
+        for (int k = 0; k < PPT; ++k) {
+            const int pc = W + NW * k, J = pc / NK, kn = pc % NK;
+            const int tl = 16 * J + m;
+            const int off = tl * BR + 32 * kn + 8 * q;
+            bv[k] = valid(tl) ? *reinterpret_cast<const uint4 *>(bb + off) : make_uint4(0u, 0u, 0u, 0u);
+            cv[k] = valid(tl) ? *reinterpret_cast<const uint4 *>(cb + off) : make_uint4(0u, 0u, 0u, 0u);
         }
 #pragma unroll
-    for (int k = 0; k < RBW; ++k) {
-        const float4 gi = *reinterpret_cast<const float4 *>(&sm.G[16 * (w + 4 * k) + 4 * q]);
-        const float sc[4] = {fast_exp2(gi.x), fast_exp2(gi.y), fast_exp2(gi.z), fast_exp2(gi.w)};
-#pragma unroll
-        for (int s = 0; s < 4; ++s)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) acc[k][s][e] *= sc[e];
+        for (int k = 0; k < PPT; ++k) {
+            const int pc = W + NW * k;
+            sm.BF[pc / NK][pc % NK][lane] = bv[k];
+            sm.CF[pc / NK][pc % NK][lane] = cv[k];
+        }
     }
-
-    // h_prev fragments are dead: the B ring takes their place.  Slab 0 goes
-    // in now, slab 1 stays in registers until the end of step 0, and each
-    // step loads the slab two ahead, so a B load has two steps to land.
     __syncthreads();
-    bslab_store(0, bv0);
-    uint4 nb1[BPL];
-    if (NS > 1) bslab_load(1, nb1);
+    // (C B^T)^T tiles, kept for all heads as packed bf16: tile t, element e =
+    // C_i . B_j with i = 16I + m, j = 16J + 4q + e (words: e = 0,1 | 2,3)
+    uint2 cbt[NT];
+#pragma unroll
+    for (int k = 0; k < RBW; ++k) {
+#pragma unroll
+        for (int J = 0; J <= RB::at(k); ++J) {
+            f32x4 t = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kn = 0; kn < NK; ++kn)
+                t = mfma16x16x32(as_bf16x8(sm.BF[J][kn][lane]), as_bf16x8(sm.CF[RB::at(k)][kn][lane]), t);
+            cbt[RB::tiles_before(k) + J] = make_uint2(pack_bf16x2(t[0], t[1]), pack_bf16x2(t[2], t[3]));
+            // two tiles' MFMA chains in flight at a time (bounded register life)
+            if (J & 1) __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+    __syncthreads();   // BF is dead; the head buffer takes its place
+    head_store<L, N>(sm.hd, pre, W, lane);
     __syncthreads();
 
-    // ---- intra: 32-token slabs in lockstep ----
-    for (int js = 0; js < NS; ++js) {
-        const int buf = js % 3;
-        uint4 nb2[BPL];
-        if (js + 2 < NS) bslab_load(js + 2, nb2);
-        bf16x8 xf[4];
+    for (int hh = 0; hh < nh; ++hh) {
+        const int h = h0 + hh;
+        auto &hd = sm.hd;
+        if (hh + 1 < nh) head_load<L, N, RAGGED>(pre, a, b, h + 1, c, nvalid, W, lane);
+
+        // ---- inter: acc = C h_prev^T, rows scaled by exp2(G_i) ----
+        // acc[k][s][e] = y[i = 16 I_k + 4q + e][p = 4m + s]
+        f32x4 acc[RBW][4];
 #pragma unroll
-        for (int s = 0; s < 4; ++s) xf[s] = as_bf16x8(sm.XF[js][s][lane]);
-        float4 vj[2];
+        for (int k = 0; k < RBW; ++k)
 #pragma unroll
-        for (int u = 0; u < 2; ++u)
-            vj[u] = *reinterpret_cast<const float4 *>(&sm.V[32 * js + 16 * u + 4 * q]);
+            for (int s = 0; s < 4; ++s) acc[k][s] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kn = 0; kn < NK; ++kn)
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                const bf16x8 hf = as_bf16x8(hd.HF[kn][s][lane]);
+#pragma unroll
+                for (int k = 0; k < RBW; ++k)
+                    acc[k][s] = mfma16x16x32(as_bf16x8(sm.CF[RB::at(k)][kn][lane]), hf, acc[k][s]);
+            }
 #pragma unroll
         for (int k = 0; k < RBW; ++k) {
-            const int I = w + 4 * k;
-            if (I < 2 * js) continue;  // no causal tile of this row block in the slab
-            const float gi = sm.G[16 * I + m];   // this lane's output row i = 16I + m
-            uint32_t cw[2][2];
+            const float4 gi = *reinterpret_cast<const float4 *>(&hd.G[16 * RB::at(k) + 4 * q]);
+            const float sc[4] = {fast_exp2(gi.x), fast_exp2(gi.y), fast_exp2(gi.z),
+                                 fast_exp2(gi.w)};
 #pragma unroll
-            for (int u = 0; u < 2; ++u) {
-                const int J = 2 * js + u;
-                if (J > I) {
-                    cw[u][0] = 0u;
-                    cw[u][1] = 0u;
-                    continue;
-                }
-                // (C B^T)^T tile: cbt[e] = C_i . B_j, j = 16J + 4q + e
-                f32x4 cbt = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int s = 0; s < 4; ++s)
 #pragma unroll
-                for (int kn = 0; kn < NK; ++kn)
-                    cbt = mfma16x16x32(as_bf16x8(sm.BF[buf][u][kn][lane]), as_bf16x8(cf[k][kn]),
-                                       cbt);
-                float v[4];
-                if (J < I) {
-                    // exp2(G_i - G_j) dt_j = exp2(G_i - G_a) * V_j, a = 16J + 15
-                    const float ui = fast_exp2(gi - sm.G[16 * J + 15]);
-                    v[0] = cbt[0] * (vj[u].x * ui);
-                    v[1] = cbt[1] * (vj[u].y * ui);
-                    v[2] = cbt[2] * (vj[u].z * ui);
-                    v[3] = cbt[3] * (vj[u].w * ui);
-                } else {
-                    // diagonal block: exact pairwise decay, causal select (j <= i)
-                    const float4 gj = *reinterpret_cast<const float4 *>(&sm.G[16 * J + 4 * q]);
-                    const float4 dj = *reinterpret_cast<const float4 *>(&sm.DT[16 * J + 4 * q]);
-                    const float gjv[4] = {gj.x, gj.y, gj.z, gj.w};
-                    const float djv[4] = {dj.x, dj.y, dj.z, dj.w};
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const float val = cbt[e] * fast_exp2(fminf(gi - gjv[e], 0.f)) * djv[e];
-                        v[e] = (4 * q + e <= m) ? val : 0.f;
-                    }
-                }
-                cw[u][0] = pack_bf16x2(v[0], v[1]);
-                cw[u][1] = pack_bf16x2(v[2], v[3]);
-            }
-            const bf16x8 af = as_bf16x8(make_uint4(cw[0][0], cw[0][1], cw[1][0], cw[1][1]));
-#pragma unroll
-            for (int s = 0; s < 4; ++s) acc[k][s] = mfma16x16x32(af, xf[s], acc[k][s]);
+                for (int e = 0; e < 4; ++e) acc[k][s][e] *= sc[e];
         }
-        if (js + 1 < NS) bslab_store((js + 1) % 3, nb1);
-#pragma unroll
-        for (int k = 0; k < BPL; ++k) nb1[k] = nb2[k];
-        __syncthreads();
-    }
 
-    // ---- y = acc + D x (x from this lane's own fragments), fp32 ----
+        __builtin_amdgcn_sched_barrier(0);
+        // ---- intra: the cached tiles drained with this head's decay ----
 #pragma unroll
-    for (int k = 0; k < RBW; ++k) {
-        const int I = w + 4 * k;
-        // token il = 16I + 4q + e sits in K slot e + 4 (I & 1) of this lane's
-        // fragment of slab I/2: words (x, y) hold slots 0..3, (z, w) slots 4..7
-        uint2 xw[4];
-        const bool odd = I & 1;
+        for (int js = 0; js < NS; ++js) {
+            bf16x8 xf[4];
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            const uint4 f = sm.XF[I >> 1][s][lane];
-            xw[s] = odd ? make_uint2(f.z, f.w) : make_uint2(f.x, f.y);
-        }
+            for (int s = 0; s < 4; ++s) xf[s] = as_bf16x8(hd.XF[js][s][lane]);
+            const float4 vj0 = *reinterpret_cast<const float4 *>(&hd.V[32 * js + 4 * q]);
+            const float4 vj1 = *reinterpret_cast<const float4 *>(&hd.V[32 * js + 16 + 4 * q]);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int il = 16 * I + 4 * q + e;
-            if (valid(il)) {
-                float xv[4];
+            for (int k = 0; k < RBW; ++k) {
+                const int I = RB::at(k);
+                if (I < 2 * js) continue;   // compile-time
+                const float gi = hd.G[16 * I + m];    // this lane's output row i = 16I + m
+                uint32_t cw[2][2];
 #pragma unroll
-                for (int s = 0; s < 4; ++s) {
-                    const uint32_t wd = (e < 2) ? xw[s].x : xw[s].y;
-                    xv[s] = (e & 1) ? bf16_hi(wd) : bf16_lo(wd);
+                for (int u = 0; u < 2; ++u) {
+                    const int J = 2 * js + u;
+                    if (J > I) {
+                        cw[u][0] = 0u;
+                        cw[u][1] = 0u;
+                        continue;
+                    }
+                    const uint2 cw2 = cbt[RB::tiles_before(k) + J];
+                    const float ct[4] = {bf16_lo(cw2.x), bf16_hi(cw2.x), bf16_lo(cw2.y),
+                                         bf16_hi(cw2.y)};
+                    float v[4];
+                    if (J < I) {
+                        // exp2(G_i - G_j) dt_j = exp2(G_i - G_a) * V_j, a = 16J + 15
+                        const float ui = fast_exp2(gi - hd.G[16 * J + 15]);
+                        const float4 vj = u ? vj1 : vj0;
+                        v[0] = ct[0] * (vj.x * ui);
+                        v[1] = ct[1] * (vj.y * ui);
+                        v[2] = ct[2] * (vj.z * ui);
+                        v[3] = ct[3] * (vj.w * ui);
+                    } else {
+                        // diagonal block: exact pairwise decay, causal select (j <= i)
+                        const float4 gj = *reinterpret_cast<const float4 *>(&hd.G[16 * J + 4 * q]);
+                        const float4 dj = *reinterpret_cast<const float4 *>(&hd.DT[16 * J + 4 * q]);
+                        const float gjv[4] = {gj.x, gj.y, gj.z, gj.w};
+                        const float djv[4] = {dj.x, dj.y, dj.z, dj.w};
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const float val = ct[e] * fast_exp2(fminf(gi - gjv[e], 0.f)) * djv[e];
+                            v[e] = (4 * q + e <= m) ? val : 0.f;
+                        }
+                    }
+                    cw[u][0] = pack_bf16x2(v[0], v[1]);
+                    cw[u][1] = pack_bf16x2(v[2], v[3]);
                 }
-                *reinterpret_cast<float4 *>(yb + il * XR + 4 * m) =
-                    make_float4(acc[k][0][e] + Dh * xv[0], acc[k][1][e] + Dh * xv[1],
-                                acc[k][2][e] + Dh * xv[2], acc[k][3][e] + Dh * xv[3]);
+                const bf16x8 af = as_bf16x8(make_uint4(cw[0][0], cw[0][1], cw[1][0], cw[1][1]));
+#pragma unroll
+                for (int s = 0; s < 4; ++s) acc[k][s] = mfma16x16x32(af, xf[s], acc[k][s]);
             }
+            // keep each slab's LDS reads next to their use (bounded register life)
+            __builtin_amdgcn_sched_barrier(0);
+        }
+
+        __builtin_amdgcn_sched_barrier(0);
+        // ---- y = acc + D x (x from this lane's own fragments), fp32 ----
+        const float Dh = a.D[h];
+        float *yb = a.y + ((b * a.T + t0) * a.H + h) * P;
+        const int32_t XR = a.H * P;
+#pragma unroll
+        for (int k = 0; k < RBW; ++k) {
+            const int I = RB::at(k);
+            // token 16I + 4q + e sits in K slot e + 4 (I & 1) of this lane's
+            // fragment of slab I/2: words (x, y) hold slots 0..3, (z, w) 4..7
+            uint2 xw[4];
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                const uint4 f = hd.XF[I >> 1][s][lane];
+                xw[s] = (I & 1) ? make_uint2(f.z, f.w) : make_uint2(f.x, f.y);
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int il = 16 * I + 4 * q + e;
+                if (valid(il)) {
+                    float xv[4];
+#pragma unroll
+                    for (int s = 0; s < 4; ++s) {
+                        const uint32_t wd = (e < 2) ? xw[s].x : xw[s].y;
+                        xv[s] = (e & 1) ? bf16_hi(wd) : bf16_lo(wd);
+                    }
+                    *reinterpret_cast<float4 *>(yb + il * XR + 4 * m) =
+                        make_float4(acc[k][0][e] + Dh * xv[0], acc[k][1][e] + Dh * xv[1],
+                                    acc[k][2][e] + Dh * xv[2], acc[k][3][e] + Dh * xv[3]);
+                }
+            }
+        }
+        if (hh + 1 < nh) {
+            __syncthreads();   // every wavefront is done with this head's buffer
+            head_store<L, N>(sm.hd, pre, W, lane);
+            __syncthreads();
+        }
+    }
+}
+
+template <int L, int N, bool RAGGED>
+__device__ __forceinline__ void chunk_scan_dispatch(ScanSmem<L, N> &sm, const ScanArgs<L, N> &a,
+                                                    int64_t b, int32_t c, int32_t g, int32_t h0,
+                                                    int32_t nh, int32_t nvalid) {
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    if constexpr (ScanWaves<L>::NW == 8) {
+        switch (w) {
+        case 0: chunk_scan_group<L, N, RAGGED, 0>(sm, a, b, c, g, h0, nh, nvalid); break;
+        case 1: chunk_scan_group<L, N, RAGGED, 1>(sm, a, b, c, g, h0, nh, nvalid); break;
+        case 2: chunk_scan_group<L, N, RAGGED, 2>(sm, a, b, c, g, h0, nh, nvalid); break;
+        case 3: chunk_scan_group<L, N, RAGGED, 3>(sm, a, b, c, g, h0, nh, nvalid); break;
+        case 4: chunk_scan_group<L, N, RAGGED, 4>(sm, a, b, c, g, h0, nh, nvalid); break;
+        case 5: chunk_scan_group<L, N, RAGGED, 5>(sm, a, b, c, g, h0, nh, nvalid); break;
+        case 6: chunk_scan_group<L, N, RAGGED, 6>(sm, a, b, c, g, h0, nh, nvalid); break;
+        default: chunk_scan_group<L, N, RAGGED, 7>(sm, a, b, c, g, h0, nh, nvalid); break;
+        }
+    } else {
+        switch (w) {
+        case 0: chunk_scan_group<L, N, RAGGED, 0>(sm, a, b, c, g, h0, nh, nvalid); break;
+        case 1: chunk_scan_group<L, N, RAGGED, 1>(sm, a, b, c, g, h0, nh, nvalid); break;
+        case 2: chunk_scan_group<L, N, RAGGED, 2>(sm, a, b, c, g, h0, nh, nvalid); break;
+        default: chunk_scan_group<L, N, RAGGED, 3>(sm, a, b, c, g, h0, nh, nvalid); break;
         }
     }
 }
 
 template <int L, int N>
-__global__ __launch_bounds__(256, 2) void chunk_scan_bf16_kernel(
-    const uint16_t *__restrict__ x, const uint16_t *__restrict__ Bm,
-    const uint16_t *__restrict__ Cm, const float *__restrict__ D, const float *__restrict__ Gws,
-    const float *__restrict__ DTws, const uint16_t *__restrict__ hprev, float *__restrict__ y,
-    int64_t T, int32_t H, int32_t G, int32_t nc, uint32_t nblk) {
-    constexpr int P = 64;
+__global__ __launch_bounds__(64 * ScanWaves<L>::NW, 1) void chunk_scan_bf16_kernel(
+    ScanArgs<L, N> a, uint32_t nblk) {
     __shared__ ScanSmem<L, N> sm;
+    // logical id -> (b, chunk, group, head block), head blocks fastest
     const uint32_t lid = xcd_remap(blockIdx.x, nblk);
-    const int32_t h = lid % H;
-    const int32_t c = (lid / H) % nc;
-    const int64_t b = lid / ((uint32_t)H * nc);
-    const int32_t g = h / (H / G);
-    const int64_t t0 = (int64_t)c * L;
-    const int64_t bhc = ((int64_t)b * H + h) * nc + c;
-    const int64_t xrow0 = ((b * T + t0) * H + h) * P;      // x, y: token stride H * P
-    const int64_t brow0 = ((b * T + t0) * G + g) * N;      // B, C: token stride G * N
-    const int32_t XR = H * P, BR = G * N;
-    const int64_t rem = T - t0;
+    const int32_t hb = lid % a.nhb;
+    const uint32_t rest = lid / a.nhb;
+    const int32_t g = rest % a.G;
+    const int32_t c = (rest / a.G) % a.nc;
+    const int64_t b = rest / ((uint32_t)a.G * a.nc);
+    const int32_t h0 = g * a.hpg + hb * a.NH;
+    const int32_t nh = min(a.NH, a.hpg - hb * a.NH);
+    const int64_t rem = a.T - (int64_t)c * L;
     const int32_t nvalid = rem < L ? (int32_t)rem : L;
     if (nvalid == L)
-        chunk_scan_unit<L, N, false>(sm, x + xrow0, Bm + brow0, Cm + brow0, Gws + bhc * L,
-                                     DTws + bhc * L, hprev + bhc * (int64_t)(P * N), y + xrow0,
-                                     D[h], nvalid, XR, BR);
+        chunk_scan_dispatch<L, N, false>(sm, a, b, c, g, h0, nh, nvalid);
     else
-        chunk_scan_unit<L, N, true>(sm, x + xrow0, Bm + brow0, Cm + brow0, Gws + bhc * L,
-                                    DTws + bhc * L, hprev + bhc * (int64_t)(P * N), y + xrow0,
-                                    D[h], nvalid, XR, BR);
+        chunk_scan_dispatch<L, N, true>(sm, a, b, c, g, h0, nh, nvalid);
 }
 
 template <int L, int N>
@@ -399,21 +494,48 @@ __global__ __launch_bounds__(256) void chunk_scan_f32_kernel(
     }
 }
 
+// Heads per workgroup: enough heads share one set of C B^T tiles to amortise
+// them, while the grid keeps about 512 workgroups (two per CU) in flight.
+inline int32_t heads_per_block(const Shape &s) {
+    const int64_t hpg = s.H / s.G;
+    const int64_t groups = s.Bt * s.nc * s.G;
+    int64_t nh = (groups * hpg + 511) / 512;
+    if (nh < 1) nh = 1;
+    if (nh > hpg) nh = hpg;
+    return (int32_t)nh;
+}
+
 template <int L, int N>
 hipError_t launch_scan(const Shape &s, const void *x, const void *B, const void *C,
                        const float *D, const float *Gws, const float *DTws, const void *hprev,
                        void *y, hipStream_t st) {
-    const uint64_t nblk = (uint64_t)s.Bt * s.nc * s.H;
-    if (s.bf16)
-        hipLaunchKernelGGL((chunk_scan_bf16_kernel<L, N>), dim3((uint32_t)nblk), dim3(256), 0, st,
-                           (const uint16_t *)x, (const uint16_t *)B, (const uint16_t *)C, D, Gws,
-                           DTws, (const uint16_t *)hprev, (float *)y, s.T, (int32_t)s.H,
-                           (int32_t)s.G, (int32_t)s.nc, (uint32_t)nblk);
-    else
+    if (s.bf16) {
+        ScanArgs<L, N> a;
+        a.x = (const uint16_t *)x;
+        a.Bm = (const uint16_t *)B;
+        a.Cm = (const uint16_t *)C;
+        a.hprev = (const uint16_t *)hprev;
+        a.D = D;
+        a.Gws = Gws;
+        a.DTws = DTws;
+        a.y = (float *)y;
+        a.T = s.T;
+        a.H = (int32_t)s.H;
+        a.G = (int32_t)s.G;
+        a.nc = (int32_t)s.nc;
+        a.hpg = (int32_t)(s.H / s.G);
+        a.NH = heads_per_block(s);
+        a.nhb = (a.hpg + a.NH - 1) / a.NH;
+        const uint64_t nblk = (uint64_t)s.Bt * s.nc * s.G * a.nhb;
+        hipLaunchKernelGGL((chunk_scan_bf16_kernel<L, N>), dim3((uint32_t)nblk),
+                           dim3(64 * ScanWaves<L>::NW), 0, st, a, (uint32_t)nblk);
+    } else {
+        const uint64_t nblk = (uint64_t)s.Bt * s.nc * s.H;
         hipLaunchKernelGGL((chunk_scan_f32_kernel<L, N>), dim3((uint32_t)nblk), dim3(256), 0, st,
                            (const float *)x, (const float *)B, (const float *)C, D, Gws, DTws,
                            (const float *)hprev, (float *)y, s.T, (int32_t)s.H, (int32_t)s.G,
                            (int32_t)s.nc, (uint32_t)nblk);
+    }
     return hipGetLastError();
 }
 
