@@ -7,25 +7,25 @@
 // section "Kernel 2" (the same product per chunk, operands scaled by dt and
 // the decay before the matrix product).  Every exponent G_last - G_j is <= 0.
 //
-// bf16 path (MFMA): one wavefront per (b, h, chunk), heads fastest in the
-// launch order (and kept on one XCD) so the group's B tile is served from L2
-// to all heads that share it.  The product is X^T diag(w) B with K = tokens,
-// so both operands are read along their slow axis.  Instead of an LDS
-// transpose, each lane loads 8-byte row segments (4 bf16) of 8 tokens and
-// transposes them in registers into MFMA operands (v_mfma_f32_16x16x32_bf16,
-// 8 bf16 of K per lane):
-//   A operand, row m of MFMA s        = p = 4m + s        (64 rows in 4 MFMAs)
-//   B operand, col m of MFMA (t, sn)  = n = 64t + 4m + sn (all N columns)
-// The weights w are folded into x (64 wide rather than N wide), once per slab
-// for all N columns.  x*w is not exact in bf16, and rounding it once costs up
-// to 2^-9 of every term of S -- enough, where |S| runs far above its rms, to
-// break a 2e-2 rms bound on the final state -- so it is carried as a bf16 head
-// plus a bf16 remainder (two MFMAs, ~16 significant bits); B itself is exact.
-// The whole 64 x N accumulator lives in AGPRs, so the wavefront runs alone on
-// its SIMD with a large register budget, and uses it to keep the raw loads of
-// two 32-token slabs in flight ahead of the one being multiplied.  Full chunks
-// take a path without per-token bounds checks.  Accumulation is fp32; S is
-// written fp32, 16 bytes a lane.
+// bf16 path (MFMA): one workgroup of 4 wavefronts per (b, chunk, group, block
+// of heads), two workgroups per CU.  The product is X^T diag(w) B with
+// K = tokens, so both operands are read along their slow axis; lanes load
+// 8-byte row segments (4 bf16) of 8 tokens and transpose them in registers
+// into MFMA operands (v_mfma_f32_16x16x32_bf16, 8 bf16 of K per lane):
+//   A operand, row m of MFMA s       = p = 4m + s
+//   B operand, col m of n-tile 4t+sn = n = 64t + 4m + sn
+// B depends only on the group: each wavefront builds the B fragments of its
+// half of the columns for all slabs once and keeps them in registers for all
+// heads of the block.  Per head, the weights w_j = dt_j exp2(G_last - G_j) are
+// computed once per token into LDS, and the wavefronts build the x*w
+// fragments (folded into x, 64 wide rather than N wide) of two slabs each into
+// LDS in fragment order.  x*w is not exact in bf16, and rounding it once
+// costs up to 2^-9 of every term of S -- enough, where |S| runs far above its
+// rms, to break a 2e-2 rms bound on the final state -- so it is carried as a
+// bf16 head plus a bf16 remainder (two MFMAs, ~16 significant bits); B itself
+// is exact.  Each wavefront then owns a 2 x N/32 block of the 64 x N output
+// tiles and runs all slabs; the next head's x is loaded during the MFMAs.
+// Accumulation is fp32; S is written fp32, 16 bytes a lane.
 //
 // fp32 path (VALU): one workgroup per (b, h, chunk); 32-token slices of X, B
 // and w staged in LDS; each thread owns one n and 64*N/256 values of p.
@@ -37,157 +37,199 @@ namespace ssd {
 
 namespace {
 
+constexpr int kStateWaves = 4;
+
+// LDS of one workgroup: the x*w fragments of the current head in MFMA
+// fragment order (16 bytes per lane, lane-linear).  B's fragments live in the
+// wavefronts' registers for the workgroup's whole life.
+template <int L, int N>
+struct StateSmem {
+    static constexpr int NS = L / 32;
+    uint4 AF[NS][2][4][64];  // slab js, head/remainder, s: row m -> p = 4m + s
+    float w[2][L];           // w_j = dt_j exp2(G_last - G_j), by head parity
+};
+
+struct StateArgs {
+    const uint16_t *x, *B;
+    const float *Gws, *DTws;
+    float *S;
+    int64_t T;
+    int32_t H, G, nc, hpg, NH, nhb;
+};
+
 template <int L, int N, bool RAGGED>
-__device__ __forceinline__ void chunk_state_unit(
-    const uint16_t *__restrict__ xb, const uint16_t *__restrict__ bb,
-    const float *__restrict__ Gp, const float *__restrict__ Dp, float *__restrict__ Sp,
-    int32_t nvalid, int32_t XR, int32_t BR) {
-    constexpr int P = 64;
-    constexpr int NT = N / 64;       // 64-column blocks of n
-    constexpr int KS = L / 32;       // 32-token steps
-    constexpr int DEPTH = 2;         // steps of raw loads in flight ahead of use
-    const int lane = threadIdx.x;
+__device__ __forceinline__ void chunk_state_group(StateSmem<L, N> &sm, const StateArgs &a,
+                                                  int64_t b, int32_t c, int32_t g, int32_t h0,
+                                                  int32_t nh, int32_t nvalid) {
+    constexpr int P = 64, NS = L / 32;
+    constexpr int TPW = N / 32;                  // n-tiles per wavefront (half of N / 16)
+    constexpr int SPW = (NS + kStateWaves - 1) / kStateWaves;   // slabs built per wavefront
+    const int W = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
     const int m = lane & 15, q = lane >> 4;
-    const float glast = Gp[L - 1];
+    const int64_t t0 = (int64_t)c * L;
+    const int32_t XR = a.H * P, BR = a.G * N;
+    auto valid = [&](int tl) { return !RAGGED || tl < nvalid; };
 
-    // this lane's rows within a step: token 8q + r, x at column 4m, B at 64t + 4m
-    int32_t xo[8], bo[8];
-#pragma unroll
-    for (int r = 0; r < 8; ++r) {
-        xo[r] = (8 * q + r) * XR + 4 * m;
-        bo[r] = (8 * q + r) * BR + 4 * m;
-    }
-    struct Raw {
-        uint2 x[8], b[NT][8];
-    };
-    auto load = [&](int ks, Raw &v) {
-        const uint16_t *xs = xb + (32 * ks) * XR;
-        const uint16_t *bs = bb + (32 * ks) * BR;
-#pragma unroll
-        for (int r = 0; r < 8; ++r) {
-            const bool ok = !RAGGED || 32 * ks + 8 * q + r < nvalid;
-            v.x[r] = ok ? *reinterpret_cast<const uint2 *>(xs + xo[r]) : make_uint2(0u, 0u);
-#pragma unroll
-            for (int t = 0; t < NT; ++t)
-                v.b[t][r] = ok ? *reinterpret_cast<const uint2 *>(bs + bo[r] + 64 * t)
-                               : make_uint2(0u, 0u);
-        }
-    };
+    // this wavefront's outputs: rows p = 4M + s for s in {2 sp, 2 sp + 1},
+    // columns n = 64 (nt / 4) + 4m + nt % 4 for n-tiles nt = TPW ch + j
+    const int sp = W & 1, ch = W >> 1;
+    const int nt0 = TPW * ch;
 
-    // acc[s][c]: rows p = 4M + s (M = 4q + i), columns n = 64t + 4m + sn, c = 4t + sn
-    f32x4 acc[4][NT * 4];
+    // ---- B^T fragments of this wavefront's columns, all slabs, in registers ----
+    bf16x8 bfr[NS][TPW];
+    {
+        const uint16_t *bb = a.B + ((b * a.T + t0) * a.G + g) * N + 64 * (nt0 >> 2) + 4 * m;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+        for (int js = 0; js < NS; ++js) {
+            uint2 br[8];
 #pragma unroll
-        for (int k = 0; k < NT * 4; ++k) acc[i][k] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    Raw ring[DEPTH + 1];
-#pragma unroll
-    for (int d = 0; d < DEPTH; ++d)
-        if (d < KS) load(d, ring[d]);
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-        if (ks + DEPTH < KS) load(ks + DEPTH, ring[(ks + DEPTH) % (DEPTH + 1)]);
-        const Raw &cur = ring[ks % (DEPTH + 1)];
-        const int j0 = 32 * ks + 8 * q;  // this lane's 8 tokens: j0 .. j0+7
-        float w[8];
-        {
-            const float4 g0 = *reinterpret_cast<const float4 *>(Gp + j0);
-            const float4 g1 = *reinterpret_cast<const float4 *>(Gp + j0 + 4);
-            const float4 d0 = *reinterpret_cast<const float4 *>(Dp + j0);
-            const float4 d1 = *reinterpret_cast<const float4 *>(Dp + j0 + 4);
-            w[0] = d0.x * fast_exp2(glast - g0.x);
-            w[1] = d0.y * fast_exp2(glast - g0.y);
-            w[2] = d0.z * fast_exp2(glast - g0.z);
-            w[3] = d0.w * fast_exp2(glast - g0.w);
-            w[4] = d1.x * fast_exp2(glast - g1.x);
-            w[5] = d1.y * fast_exp2(glast - g1.y);
-            w[6] = d1.z * fast_exp2(glast - g1.z);
-            w[7] = d1.w * fast_exp2(glast - g1.w);
-        }
-        // A operands: x * w transposed (row m of MFMA s is p = 4m + s), as a
-        // bf16 head and the bf16 rounding of the remainder
-        bf16x8 ahi[4], alo[4];
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            uint4 vh, vl;
-            uint32_t *wh = reinterpret_cast<uint32_t *>(&vh);
-            uint32_t *wl = reinterpret_cast<uint32_t *>(&vl);
-#pragma unroll
-            for (int rr = 0; rr < 4; ++rr) {
-                const uint32_t a0 = (s < 2) ? cur.x[2 * rr].x : cur.x[2 * rr].y;
-                const uint32_t a1 = (s < 2) ? cur.x[2 * rr + 1].x : cur.x[2 * rr + 1].y;
-                const float e0 = ((s & 1) ? bf16_hi(a0) : bf16_lo(a0)) * w[2 * rr];
-                const float e1 = ((s & 1) ? bf16_hi(a1) : bf16_lo(a1)) * w[2 * rr + 1];
-                const uint32_t hw = pack_bf16x2(e0, e1);
-                wh[rr] = hw;
-                wl[rr] = pack_bf16x2(e0 - bf16_lo(hw), e1 - bf16_hi(hw));
+            for (int r = 0; r < 8; ++r) {
+                const int tl = 32 * js + 8 * q + r;
+                br[r] = valid(tl) ? *reinterpret_cast<const uint2 *>(bb + tl * BR)
+                                  : make_uint2(0u, 0u);
             }
-            ahi[s] = as_bf16x8(vh);
-            alo[s] = as_bf16x8(vl);
-        }
-        // B operands: B rows transposed (column m of MFMA (t, sn) is n = 64t + 4m + sn)
 #pragma unroll
-        for (int t = 0; t < NT; ++t)
-#pragma unroll
-            for (int sn = 0; sn < 4; ++sn) {
+            for (int j = 0; j < TPW; ++j) {
+                const int sn = (nt0 + j) & 3;
                 uint4 v;
                 uint32_t *vw = reinterpret_cast<uint32_t *>(&v);
 #pragma unroll
                 for (int rr = 0; rr < 4; ++rr) {
-                    const uint32_t a0 = (sn < 2) ? cur.b[t][2 * rr].x : cur.b[t][2 * rr].y;
-                    const uint32_t a1 =
-                        (sn < 2) ? cur.b[t][2 * rr + 1].x : cur.b[t][2 * rr + 1].y;
+                    const uint32_t a0 = (sn < 2) ? br[2 * rr].x : br[2 * rr].y;
+                    const uint32_t a1 = (sn < 2) ? br[2 * rr + 1].x : br[2 * rr + 1].y;
                     vw[rr] = (sn & 1) ? pair_hi(a0, a1) : pair_lo(a0, a1);
                 }
-                const bf16x8 bfr = as_bf16x8(v);
-#pragma unroll
-                for (int s = 0; s < 4; ++s) {
-                    acc[s][4 * t + sn] = mfma16x16x32(ahi[s], bfr, acc[s][4 * t + sn]);
-                    acc[s][4 * t + sn] = mfma16x16x32(alo[s], bfr, acc[s][4 * t + sn]);
-                }
-            }
-    }
-
-    // D layout: lane holds rows M = 4q + i (i = 0..3) of column m.
-#pragma unroll
-    for (int s = 0; s < 4; ++s)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int p = 4 * (4 * q + i) + s;
-#pragma unroll
-            for (int t = 0; t < NT; ++t) {
-                const float4 v = make_float4(acc[s][4 * t + 0][i], acc[s][4 * t + 1][i],
-                                             acc[s][4 * t + 2][i], acc[s][4 * t + 3][i]);
-                *reinterpret_cast<float4 *>(Sp + p * N + 64 * t + 4 * m) = v;
+                bfr[js][j] = as_bf16x8(v);
             }
         }
+    }
+
+    // raw x of the slabs this wavefront builds, and G, dt of one token per
+    // thread (tid < L), for a head, loaded one head ahead of use
+    struct Raw {
+        uint2 x[SPW][8];
+        float g, dt, glast;
+    };
+    const int tid = threadIdx.x;
+    auto head_load = [&](int32_t h, Raw &r) {
+        const uint16_t *xb = a.x + ((b * a.T + t0) * a.H + h) * P + 4 * m;
+#pragma unroll
+        for (int k = 0; k < SPW; ++k) {
+            const int js = W + kStateWaves * k;
+            const int jw = 32 * js + 8 * q;
+#pragma unroll
+            for (int rr = 0; rr < 8; ++rr)
+                r.x[k][rr] = (js < NS && valid(jw + rr))
+                                 ? *reinterpret_cast<const uint2 *>(xb + (jw + rr) * XR)
+                                 : make_uint2(0u, 0u);
+        }
+        if (tid < L) {
+            const int64_t bhc = ((int64_t)b * a.H + h) * a.nc + c;
+            r.g = a.Gws[bhc * L + tid];
+            r.dt = a.DTws[bhc * L + tid];
+            r.glast = a.Gws[bhc * L + L - 1];
+        }
+    };
+    auto w_store = [&](int buf, const Raw &r) {
+        if (tid < L) sm.w[buf][tid] = r.dt * fast_exp2(r.glast - r.g);
+    };
+    Raw pre;
+    head_load(h0, pre);
+    w_store(0, pre);
+    __syncthreads();
+
+    for (int hh = 0; hh < nh; ++hh) {
+        const int32_t h = h0 + hh;
+        // ---- x*w fragments (transposed; bf16 head + remainder) of slabs W, W+4 ----
+#pragma unroll
+        for (int k = 0; k < SPW; ++k) {
+            const int js = W + kStateWaves * k;
+            if (js < NS) {
+                const int jw = 32 * js + 8 * q;
+                const float4 w0 = *reinterpret_cast<const float4 *>(&sm.w[hh & 1][jw]);
+                const float4 w1 = *reinterpret_cast<const float4 *>(&sm.w[hh & 1][jw + 4]);
+                const float w[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+#pragma unroll
+                for (int s = 0; s < 4; ++s) {
+                    uint4 vh, vl;
+                    uint32_t *wh = reinterpret_cast<uint32_t *>(&vh);
+                    uint32_t *wl = reinterpret_cast<uint32_t *>(&vl);
+#pragma unroll
+                    for (int rr = 0; rr < 4; ++rr) {
+                        const uint32_t a0 = (s < 2) ? pre.x[k][2 * rr].x : pre.x[k][2 * rr].y;
+                        const uint32_t a1 = (s < 2) ? pre.x[k][2 * rr + 1].x : pre.x[k][2 * rr + 1].y;
+                        const float e0 = ((s & 1) ? bf16_hi(a0) : bf16_lo(a0)) * w[2 * rr];
+                        const float e1 = ((s & 1) ? bf16_hi(a1) : bf16_lo(a1)) * w[2 * rr + 1];
+                        const uint32_t hw = pack_bf16x2(e0, e1);
+                        wh[rr] = hw;
+                        wl[rr] = pack_bf16x2(e0 - bf16_lo(hw), e1 - bf16_hi(hw));
+                    }
+                    sm.AF[js][0][s][lane] = vh;
+                    sm.AF[js][1][s][lane] = vl;
+                }
+            }
+        }
+        __syncthreads();
+        if (hh + 1 < nh) head_load(h + 1, pre);   // next head in flight during the MFMAs
+
+        // ---- S tiles: sum over slabs of (x w)^T B, head and remainder ----
+        f32x4 acc[2][TPW];
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int j = 0; j < TPW; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int js = 0; js < NS; ++js) {
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const bf16x8 ahi = as_bf16x8(sm.AF[js][0][2 * sp + i][lane]);
+                const bf16x8 alo = as_bf16x8(sm.AF[js][1][2 * sp + i][lane]);
+#pragma unroll
+                for (int j = 0; j < TPW; ++j) {
+                    acc[i][j] = mfma16x16x32(ahi, bfr[js][j], acc[i][j]);
+                    acc[i][j] = mfma16x16x32(alo, bfr[js][j], acc[i][j]);
+                }
+            }
+        }
+        // D layout: lane holds rows M = 4q + e of column m: p = 4M + s,
+        // n = 64 (nt / 4) + 4m + nt % 4; the TPW n-tiles are adjacent columns
+        const int64_t bhc = ((int64_t)b * a.H + h) * a.nc + c;
+        float *Sp = a.S + bhc * (int64_t)(P * N) + 64 * (nt0 >> 2) + 4 * m + (nt0 & 3);
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int p = 4 * (4 * q + e) + 2 * sp + i;
+                if constexpr (TPW == 4)
+                    *reinterpret_cast<float4 *>(Sp + p * N) =
+                        make_float4(acc[i][0][e], acc[i][1][e], acc[i][2][e], acc[i][3][e]);
+                else
+                    *reinterpret_cast<float2 *>(Sp + p * N) = make_float2(acc[i][0][e], acc[i][1][e]);
+            }
+        if (hh + 1 < nh) w_store((hh + 1) & 1, pre);
+        __syncthreads();   // AF is rewritten for the next head
+    }
 }
 
 template <int L, int N>
-__global__ __launch_bounds__(64, 1) void chunk_state_bf16_kernel(
-    const uint16_t *__restrict__ x, const uint16_t *__restrict__ B,
-    const float *__restrict__ Gws, const float *__restrict__ DTws, float *__restrict__ S,
-    int64_t T, int32_t H, int32_t G, int32_t nc, uint32_t nblk) {
-    constexpr int P = 64;
+__global__ __launch_bounds__(64 * kStateWaves, 2) void chunk_state_bf16_kernel(StateArgs a,
+                                                                               uint32_t nblk) {
+    __shared__ StateSmem<L, N> sm;
     const uint32_t lid = xcd_remap(blockIdx.x, nblk);
-    const int32_t h = lid % H;
-    const int32_t c = (lid / H) % nc;
-    const int64_t b = lid / ((uint32_t)H * nc);
-    const int32_t g = h / (H / G);
-    const int64_t t0 = (int64_t)c * L;
-    const int64_t bhc = ((int64_t)b * H + h) * nc + c;
-    const int64_t rem = T - t0;
+    const int32_t hb = lid % a.nhb;
+    const uint32_t rest = lid / a.nhb;
+    const int32_t g = rest % a.G;
+    const int32_t c = (rest / a.G) % a.nc;
+    const int64_t b = rest / ((uint32_t)a.G * a.nc);
+    const int32_t h0 = g * a.hpg + hb * a.NH;
+    const int32_t nh = min(a.NH, a.hpg - hb * a.NH);
+    const int64_t rem = a.T - (int64_t)c * L;
     const int32_t nvalid = rem < L ? (int32_t)rem : L;
-    const uint16_t *xb = x + ((b * T + t0) * H + h) * P;
-    const uint16_t *bb = B + ((b * T + t0) * G + g) * N;
-    float *Sp = S + bhc * (int64_t)(P * N);
     if (nvalid == L)
-        chunk_state_unit<L, N, false>(xb, bb, Gws + bhc * L, DTws + bhc * L, Sp, nvalid, H * P,
-                                      G * N);
+        chunk_state_group<L, N, false>(sm, a, b, c, g, h0, nh, nvalid);
     else
-        chunk_state_unit<L, N, true>(xb, bb, Gws + bhc * L, DTws + bhc * L, Sp, nvalid, H * P,
-                                     G * N);
+        chunk_state_group<L, N, true>(sm, a, b, c, g, h0, nh, nvalid);
 }
 
 template <int L, int N>
@@ -249,12 +291,29 @@ __global__ __launch_bounds__(256) void chunk_state_f32_kernel(
 template <int L, int N>
 hipError_t launch_cs(const Shape &s, const void *x, const void *B, const float *Gws,
                      const float *DTws, float *S, hipStream_t st) {
-    const uint64_t nblk = (uint64_t)s.Bt * s.nc * s.H;
     if (s.bf16) {
-        hipLaunchKernelGGL((chunk_state_bf16_kernel<L, N>), dim3((uint32_t)nblk), dim3(64), 0, st,
-                           (const uint16_t *)x, (const uint16_t *)B, Gws, DTws, S, s.T,
-                           (int32_t)s.H, (int32_t)s.G, (int32_t)s.nc, (uint32_t)nblk);
+        StateArgs a;
+        a.x = (const uint16_t *)x;
+        a.B = (const uint16_t *)B;
+        a.Gws = Gws;
+        a.DTws = DTws;
+        a.S = S;
+        a.T = s.T;
+        a.H = (int32_t)s.H;
+        a.G = (int32_t)s.G;
+        a.nc = (int32_t)s.nc;
+        a.hpg = (int32_t)(s.H / s.G);
+        // heads per workgroup: share the B fragments while keeping ~512 workgroups
+        int64_t nh = (s.Bt * s.nc * s.H + 511) / 512;
+        if (nh < 1) nh = 1;
+        if (nh > a.hpg) nh = a.hpg;
+        a.NH = (int32_t)nh;
+        a.nhb = (a.hpg + a.NH - 1) / a.NH;
+        const uint64_t nblk = (uint64_t)s.Bt * s.nc * s.G * a.nhb;
+        hipLaunchKernelGGL((chunk_state_bf16_kernel<L, N>), dim3((uint32_t)nblk),
+                           dim3(64 * kStateWaves), 0, st, a, (uint32_t)nblk);
     } else {
+        const uint64_t nblk = (uint64_t)s.Bt * s.nc * s.H;
         hipLaunchKernelGGL((chunk_state_f32_kernel<L, N>), dim3((uint32_t)nblk), dim3(256), 0, st,
                            (const float *)x, (const float *)B, Gws, DTws, S, s.T, (int32_t)s.H,
                            (int32_t)s.G, (int32_t)s.nc, (uint32_t)nblk);
