@@ -12,9 +12,9 @@
 // float32 [Bt, H, nc, L] (tokens contiguous).  Positions past T get dt = 0,
 // so a ragged last chunk carries its last valid G to the end of the chunk.
 //
-// One workgroup of 256 threads per (b, chunk, block of 16 heads).  dt rows of
-// 16 heads are read coalesced, transposed through LDS, and each wavefront then
-// scans 4 heads: a lane sums L/64 consecutive tokens serially, a wave-wide
+// One workgroup of 256 threads per (b, chunk, block of 32 heads).  dt rows of
+// 32 heads (128 bytes) are read with 16-byte loads, transposed through LDS, and
+// each wavefront then scans 8 heads: a lane sums L/64 tokens serially, a wave-wide
 // log-depth scan (6 shuffle steps) combines the lane totals, and each lane
 // adds its exclusive prefix back.
 
@@ -25,7 +25,7 @@ namespace ssd {
 
 namespace {
 
-constexpr int kHeadsPerBlock = 16;
+constexpr int kHeadsPerBlock = 32;
 
 template <int L>
 __global__ __launch_bounds__(256) void chunk_cumsum_kernel(
@@ -41,17 +41,29 @@ __global__ __launch_bounds__(256) void chunk_cumsum_kernel(
     const int32_t h0 = hb * kHeadsPerBlock;
     const int tid = threadIdx.x;
 
-    // coalesced load of dt[b, c*L + t, h0 .. h0+15]
+    // coalesced load of dt[b, c*L + t, h0 .. h0+31]: 8 threads cover one
+    // 128-byte token row with 16-byte loads (when rows are 16-byte aligned)
     {
-        const int hh = tid % kHeadsPerBlock;
-        const int h = h0 + hh;
+        const int c4 = (tid & 7) * 4;
+        const bool vec = (H & 3) == 0;
 #pragma unroll
-        for (int k = 0; k < L / 16; ++k) {
-            const int t = tid / kHeadsPerBlock + 16 * k;
+        for (int k = 0; k < L / 32; ++k) {
+            const int t = (tid >> 3) + 32 * k;
             const int64_t tg = (int64_t)c * L + t;
-            float v = 0.f;
-            if (tg < T && h < H) v = dt[(b * T + tg) * H + h];
-            tile[hh][t] = v;
+            float v[4] = {0.f, 0.f, 0.f, 0.f};
+            if (tg < T) {
+                const float *row = dt + (b * T + tg) * H + h0 + c4;
+                if (vec && h0 + c4 + 3 < H) {
+                    const float4 f = *reinterpret_cast<const float4 *>(row);
+                    v[0] = f.x; v[1] = f.y; v[2] = f.z; v[3] = f.w;
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        if (h0 + c4 + e < H) v[e] = row[e];
+                }
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) tile[c4 + e][t] = v[e];
         }
     }
     __syncthreads();

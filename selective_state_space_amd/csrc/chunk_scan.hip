@@ -362,9 +362,9 @@ __device__ __forceinline__ void chunk_scan_group(ScanSmem<L, N> &sm, const ScanA
                         const uint32_t wd = (e < 2) ? xw[s].x : xw[s].y;
                         xv[s] = (e & 1) ? bf16_hi(wd) : bf16_lo(wd);
                     }
-                    *reinterpret_cast<float4 *>(yb + il * XR + 4 * m) =
-                        make_float4(acc[k][0][e] + Dh * xv[0], acc[k][1][e] + Dh * xv[1],
-                                    acc[k][2][e] + Dh * xv[2], acc[k][3][e] + Dh * xv[3]);
+                    store_nt(yb + il * XR + 4 * m,
+                             make_float4(acc[k][0][e] + Dh * xv[0], acc[k][1][e] + Dh * xv[1],
+                                         acc[k][2][e] + Dh * xv[2], acc[k][3][e] + Dh * xv[3]));
                 }
             }
         }

@@ -202,10 +202,10 @@ __device__ __forceinline__ void chunk_state_group(StateSmem<L, N> &sm, const Sta
             for (int e = 0; e < 4; ++e) {
                 const int p = 4 * (4 * q + e) + 2 * sp + i;
                 if constexpr (TPW == 4)
-                    *reinterpret_cast<float4 *>(Sp + p * N) =
-                        make_float4(acc[i][0][e], acc[i][1][e], acc[i][2][e], acc[i][3][e]);
+                    store_nt(Sp + p * N,
+                             make_float4(acc[i][0][e], acc[i][1][e], acc[i][2][e], acc[i][3][e]));
                 else
-                    *reinterpret_cast<float2 *>(Sp + p * N) = make_float2(acc[i][0][e], acc[i][1][e]);
+                    store_nt(Sp + p * N, make_float2(acc[i][0][e], acc[i][1][e]));
             }
         if (hh + 1 < nh) w_store((hh + 1) & 1, pre);
         __syncthreads();   // AF is rewritten for the next head

@@ -71,7 +71,7 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
 #pragma unroll
     for (int k = 0; k < ITER; ++k) {
         const int p = 16 * wave + RPI * k + rw;
-        sv[k] = *reinterpret_cast<const float4 *>(st + p * N + 4 * sub);
+        sv[k] = load_nt(st + p * N + 4 * sub);
         xv[k] = load1(x + bh * P + p);
     }
 #pragma unroll
@@ -83,7 +83,7 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
         ns.y = dA * sv[k].y + u * Bv.y;
         ns.z = dA * sv[k].z + u * Bv.z;
         ns.w = dA * sv[k].w + u * Bv.w;
-        *reinterpret_cast<float4 *>(st + p * N + 4 * sub) = ns;
+        store_nt(st + p * N + 4 * sub, ns);
         float part = ns.x * Cv.x + ns.y * Cv.y + ns.z * Cv.z + ns.w * Cv.w;
 #pragma unroll
         for (int off = LPR / 2; off > 0; off >>= 1) part += __shfl_xor(part, off, 64);

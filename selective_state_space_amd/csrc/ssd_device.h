@@ -27,6 +27,28 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
     return pack_bf16x2(f, 0.f) & 0xffffu;
 }
 
+// Streaming 16/8-byte accesses (nontemporal hint) for data that one call
+// touches exactly once: the state slabs S, h_prev, y and the decode state.
+// They keep such streams from displacing reused lines in L2 / the MALL.
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ float4 load_nt(const float *p) {
+    const f32x4 v = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(p));
+    return make_float4(v[0], v[1], v[2], v[3]);
+}
+__device__ __forceinline__ void store_nt(float *p, float4 v) {
+    const f32x4 w = {v.x, v.y, v.z, v.w};
+    __builtin_nontemporal_store(w, reinterpret_cast<f32x4 *>(p));
+}
+__device__ __forceinline__ void store_nt(float *p, float2 v) {
+    const f32x2 w = {v.x, v.y};
+    __builtin_nontemporal_store(w, reinterpret_cast<f32x2 *>(p));
+}
+__device__ __forceinline__ void store_nt(uint16_t *p, uint2 v) {
+    const u32x2 w = {v.x, v.y};
+    __builtin_nontemporal_store(w, reinterpret_cast<u32x2 *>(p));
+}
+
 // 2^x on the transcendental unit (v_exp_f32).
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 

@@ -46,7 +46,7 @@ __global__ __launch_bounds__(256) void state_passing_kernel(
 #pragma unroll
     for (int k = 0; k < kPF; ++k) {
         if (k < nc) {
-            sbuf[k] = *reinterpret_cast<const float4 *>(Sb + (int64_t)k * PN);
+            sbuf[k] = load_nt(Sb + (int64_t)k * PN);
             gbuf[k] = Gl[(int64_t)k * L];
         }
     }
@@ -58,7 +58,7 @@ __global__ __launch_bounds__(256) void state_passing_kernel(
                 const float4 s = sbuf[k];
                 const float dec = fast_exp2(gbuf[k]);
                 if (c + kPF < nc) {
-                    sbuf[k] = *reinterpret_cast<const float4 *>(Sb + (int64_t)(c + kPF) * PN);
+                    sbuf[k] = load_nt(Sb + (int64_t)(c + kPF) * PN);
                     gbuf[k] = Gl[(int64_t)(c + kPF) * L];
                 }
                 const int64_t off = (bh * (int64_t)nc + c) * PN + e;
@@ -66,9 +66,9 @@ __global__ __launch_bounds__(256) void state_passing_kernel(
                     uint2 v;
                     v.x = pack_bf16x2(h.x, h.y);
                     v.y = pack_bf16x2(h.z, h.w);
-                    *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(hprev) + off) = v;
+                    store_nt(static_cast<uint16_t *>(hprev) + off, v);
                 } else {
-                    *reinterpret_cast<float4 *>(static_cast<float *>(hprev) + off) = h;
+                    store_nt(static_cast<float *>(hprev) + off, h);
                 }
                 h.x = dec * h.x + s.x;
                 h.y = dec * h.y + s.y;
