@@ -118,9 +118,17 @@ ssd_status ssd_chunked_fwd_workspace_layout(const ssd_dims *dims, int64_t chunk_
                                             size_t offsets[4]);
 
 /*
- * The four stages of ssd_chunked_fwd, callable one at a time (same
+ * The four stages of the chunked forward, callable one at a time (same
  * arguments and workspace; each reads what the previous stage left in the
- * workspace).  ssd_chunked_fwd is exactly these four calls in this order.
+ * workspace): chunk_cumsum, chunk_state, state_passing, chunk_scan in this
+ * order give y, final_state and every intermediate.  ssd_chunked_fwd runs
+ * chunk_cumsum, then either chunk_state and state_passing or the one-pass
+ * ssd_state_fwd stage below, then chunk_scan.  It takes the one-pass stage
+ * for bf16 io when batch * nheads >= 384 (enough independent chains to fill
+ * the GPU while each walks its chunks in order); fp32 io always runs the
+ * four stages.  The environment variable SSD_STATE_FWD_ROWS, read at each
+ * call, overrides the choice: 0 selects the two stages, 4, 2 or 1 the
+ * one-pass stage with that many of the four 16-row sets per workgroup.
  *
  * chunk_cumsum: reads dt, A; writes G and DT.  One wavefront-level prefix
  *   sum per (b, h, chunk) ("Accelerating Mamba-2 ...", section "Kernel 1").
@@ -142,6 +150,24 @@ ssd_status ssd_state_passing(const float *init_state, float *final_state, int64_
 ssd_status ssd_chunk_scan(const void *x, const void *B, const void *C, const float *D, void *y,
                           int64_t chunk_size, const ssd_dims *dims, void *workspace,
                           size_t workspace_bytes, void *stream);
+
+/*
+ * chunk_state and state_passing in one sequential pass over the chunks of
+ * each (b, h) ("Accelerating Mamba-2 ...", section "Kernel 2": the state is
+ * the accumulator of the per-chunk product, stored before each chunk's
+ * update).  Reads x, B, G, DT (left by ssd_chunk_cumsum) and init_state
+ * (NULL = zeros); writes h_prev and final_state (NULL = not written).  The S
+ * region is neither read nor written.  init_state may equal final_state.
+ * h_prev and final_state agree with those of ssd_chunk_state followed by
+ * ssd_state_passing up to fp32 summation order, not bit for bit.
+ * bf16 io only: SSD_ERR_UNSUPPORTED for SSD_F32, and for shapes whose
+ * per-chunk row span does not fit 32-bit offsets (chunk_size * nheads * 64 * 2
+ * or chunk_size * ngroups * dstate * 2 bytes above 2^31 - 1), where
+ * ssd_chunked_fwd runs the two stages instead.
+ */
+ssd_status ssd_state_fwd(const void *x, const void *B, const float *init_state,
+                         float *final_state, int64_t chunk_size, const ssd_dims *dims,
+                         void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * One recurrent decode step ("Optimizing Nemotron v3 Super in TensorRT-LLM",

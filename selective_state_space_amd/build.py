@@ -21,7 +21,8 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libssd.so")
 ARCH = "gfx950"
 
-SOURCES = ["chunk_cumsum.hip", "chunk_state.hip", "state_passing.hip", "chunk_scan.hip",
+SOURCES = ["chunk_cumsum.hip", "chunk_state.hip", "state_passing.hip", "state_fwd.hip",
+           "chunk_scan.hip",
            "decode_step.hip", "ssd_api.cpp"]
 
 # -packed-fp32-ops: keep the compiler from emitting packed fp32 VALU ops.

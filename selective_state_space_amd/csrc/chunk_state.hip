@@ -179,18 +179,19 @@ __device__ __forceinline__ void chunk_state_group(StateSmem<L, N> &sm, const Sta
         for (int i = 0; i < 2; ++i)
 #pragma unroll
             for (int j = 0; j < TPW; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        // per slab all head products, then all remainder products: no MFMA
+        // waits on the one just issued
 #pragma unroll
         for (int js = 0; js < NS; ++js) {
 #pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                const bf16x8 ahi = as_bf16x8(sm.AF[js][0][2 * sp + i][lane]);
-                const bf16x8 alo = as_bf16x8(sm.AF[js][1][2 * sp + i][lane]);
+            for (int hl = 0; hl < 2; ++hl)
 #pragma unroll
-                for (int j = 0; j < TPW; ++j) {
-                    acc[i][j] = mfma16x16x32(ahi, bfr[js][j], acc[i][j]);
-                    acc[i][j] = mfma16x16x32(alo, bfr[js][j], acc[i][j]);
+                for (int i = 0; i < 2; ++i) {
+                    const bf16x8 av = as_bf16x8(sm.AF[js][hl][2 * sp + i][lane]);
+#pragma unroll
+                    for (int j = 0; j < TPW; ++j)
+                        acc[i][j] = mfma16x16x32(av, bfr[js][j], acc[i][j]);
                 }
-            }
         }
         // D layout: lane holds rows M = 4q + e of column m: p = 4M + s,
         // n = 64 (nt / 4) + 4m + nt % 4; the TPW n-tiles are adjacent columns

@@ -2,7 +2,8 @@
 // sequence of the chunked forward (chunk_cumsum -> chunk_state ->
 // state_passing -> chunk_scan, "Accelerating Mamba-2 with High-Performance
 // Forward Pass Kernels in NVIDIA CUDA Tile", sections "Kernel 1" to "Kernel
-// 3") and of the decode step ("Optimizing Nemotron v3 Super in
+// 3"; for bf16 io and enough (batch, head) chains the middle two run as one
+// pass, as in that page's "Kernel 2") and of the decode step ("Optimizing Nemotron v3 Super in
 // TensorRT-LLM", section 6.1).
 //
 // Every check runs on the host before the first HIP call, so a rejected call
@@ -172,6 +173,29 @@ ssd_status run_passing(const ssd::Shape &s, const float *init, float *fin, const
     return hip_result(ssd::launch_state_passing(s, w.S, w.G, init, w.hprev, fin, st),
                       "state_passing", st);
 }
+// SSD_STATE_FWD_ROWS (read at each call; tests use it to cover every path):
+// 4, 2 or 1 forces the one-pass state stage with that row split, also in
+// ssd_chunked_fwd; 0 makes ssd_chunked_fwd use chunk_state + state_passing;
+// unset or empty leaves both choices to the shape.
+int state_fwd_rows() {
+    const char *e = getenv("SSD_STATE_FWD_ROWS");
+    if (!e || !e[0]) return -1;
+    const int v = atoi(e);
+    return (v == 0 || v == 1 || v == 2 || v == 4) ? v : -1;
+}
+bool use_state_fwd(const ssd::Shape &s) {
+    if (!ssd::state_fwd_supported(s)) return false;
+    const int r = state_fwd_rows();
+    if (r >= 0) return r > 0;
+    return ssd::state_fwd_preferred(s);
+}
+ssd_status run_state_fwd(const ssd::Shape &s, const void *x, const void *B, const float *init,
+                         float *fin, const Ws &w, hipStream_t st) {
+    const int r = state_fwd_rows();
+    return hip_result(ssd::launch_state_fwd(s, x, B, w.G, w.DT, init, w.hprev, fin,
+                                            r > 0 ? r : 0, st),
+                      "state_fwd", st);
+}
 ssd_status run_scan(const ssd::Shape &s, const void *x, const void *B, const void *C,
                     const float *D, void *y, const Ws &w, hipStream_t st) {
     return hip_result(ssd::launch_chunk_scan(s, x, B, C, D, w.G, w.DT, w.hprev, y, st),
@@ -261,6 +285,31 @@ ssd_status ssd_chunk_scan(const void *x, const void *B, const void *C, const flo
     return ok();
 }
 
+ssd_status ssd_state_fwd(const void *x, const void *B, const float *init_state,
+                         float *final_state, int64_t chunk_size, const ssd_dims *dims,
+                         void *workspace, size_t workspace_bytes, void *stream) {
+    ssd::Shape s;
+    ssd_status r = check_dims(dims, chunk_size, true, &s);
+    if (r != SSD_OK) return r;
+    if (!ssd::state_fwd_supported(s))
+        return fail(SSD_ERR_UNSUPPORTED,
+                    "ssd_state_fwd needs bf16 io and per-chunk row spans below 2^31 bytes");
+    if (s.Bt > 0 && s.T > 0) {
+        REQUIRE_PTR(x);
+        REQUIRE_PTR(B);
+    } else {
+        OPTIONAL_PTR(x);
+        OPTIONAL_PTR(B);
+    }
+    OPTIONAL_PTR(init_state);
+    OPTIONAL_PTR(final_state);
+    Ws w;
+    if ((r = check_ws(s, workspace, workspace_bytes, &w)) != SSD_OK) return r;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if ((r = run_state_fwd(s, x, B, init_state, final_state, w, st)) != SSD_OK) return r;
+    return ok();
+}
+
 ssd_status ssd_chunked_fwd(const void *x, const float *dt, const float *A, const void *B,
                            const void *C, const float *D, int64_t chunk_size,
                            const float *init_state, void *y, float *final_state,
@@ -293,8 +342,12 @@ ssd_status ssd_chunked_fwd(const void *x, const float *dt, const float *A, const
     if (s.Bt == 0) return ok();
     hipStream_t st = static_cast<hipStream_t>(stream);
     if ((r = run_cumsum(s, dt, A, w, st)) != SSD_OK) return r;
-    if ((r = run_state(s, x, B, w, st)) != SSD_OK) return r;
-    if ((r = run_passing(s, init_state, final_state, w, st)) != SSD_OK) return r;
+    if (use_state_fwd(s)) {
+        if ((r = run_state_fwd(s, x, B, init_state, final_state, w, st)) != SSD_OK) return r;
+    } else {
+        if ((r = run_state(s, x, B, w, st)) != SSD_OK) return r;
+        if ((r = run_passing(s, init_state, final_state, w, st)) != SSD_OK) return r;
+    }
     if ((r = run_scan(s, x, B, C, D, y, w, st)) != SSD_OK) return r;
     return ok();
 }

@@ -77,11 +77,20 @@ __device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
 // Given two 32-bit words each holding a bf16 pair (lo = element 0, hi =
 // element 1) from two consecutive rows r0, r1, produce the word holding
 // element 0 of both rows, or element 1 of both rows.
+// One v_perm_b32 each (byte selectors: 0-3 pick bytes of r0, 4-7 of r1).
 __device__ __forceinline__ uint32_t pair_lo(uint32_t r0, uint32_t r1) {
-    return (r0 & 0xffffu) | (r1 << 16);
+    return __builtin_amdgcn_perm(r1, r0, 0x05040100u);
 }
 __device__ __forceinline__ uint32_t pair_hi(uint32_t r0, uint32_t r1) {
-    return (r0 >> 16) | (r1 & 0xffff0000u);
+    return __builtin_amdgcn_perm(r1, r0, 0x07060302u);
+}
+
+// Raw buffer resource over `bytes` bytes from `base` (gfx9 dword3).  Loads at
+// a VGPR offset at or past `bytes` return 0 without touching memory (the
+// buffer range check), which is how ragged chunks read their missing rows.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
+                                             0x00020000);
 }
 
 }  // namespace ssd

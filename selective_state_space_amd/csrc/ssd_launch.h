@@ -21,6 +21,13 @@ hipError_t launch_state_passing(const Shape &s, const float *S, const float *Gws
 hipError_t launch_chunk_scan(const Shape &s, const void *x, const void *B, const void *C,
                              const float *D, const float *Gws, const float *DTws,
                              const void *hprev, void *y, hipStream_t st);
+// chunk_state + state_passing in one pass (bf16 io).  rows_per_block = 4, 2
+// or 1 row sets of the head per workgroup, 0 = chosen from the shape.
+bool state_fwd_supported(const Shape &s);
+bool state_fwd_preferred(const Shape &s);   // shape heuristic of the fused call
+hipError_t launch_state_fwd(const Shape &s, const void *x, const void *B, const float *Gws,
+                            const float *DTws, const float *init, void *hprev, float *fin,
+                            int rows_per_block, hipStream_t st);
 hipError_t launch_decode_step(const Shape &s, float *state, const void *x, const float *dt,
                               const void *B, const void *C, const float *A, const float *D,
                               void *y, hipStream_t st);

@@ -1,0 +1,389 @@
+// state_fwd: chunk_state and state_passing in one sequential pass over the
+// chunks of each (b, h),
+//     h_prev[c] = h;   h <- exp2(G_last,c) h + sum_j x_j (dt_j exp2(G_last,c - G_j)) B_j^T;
+//     final = h.
+//
+// "Accelerating Mamba-2 with High-Performance Forward Pass Kernels in NVIDIA
+// CUDA Tile", section "Kernel 2": one program per independent (batch, head,
+// state tile) slice walks the chunks in order, stores the state entering each
+// chunk, scales it by exp2 of the chunk's last cumulative decay and adds the
+// chunk's product X^T (dt exp2(G_last - G) B) with the running state as the
+// accumulator of the matrix product; after the last chunk the state is the
+// final state.  The per-chunk states S_c of the four-stage form (section
+// "Mamba-2 architecture", the jump formula) are never written to HBM: that
+// saves a write and a read of Bt*H*nc*P*N fp32.
+//
+// gfx950 mapping (bf16 io only).  One workgroup of 4 wavefronts per (b, h,
+// p-slab): the block owns the state rows p = 4M + s0 + s, s < SPB (SPB = 4,
+// 2 or 1, the head's 64 rows split over 4/SPB workgroups when Bt*H alone
+// would not fill the chip), all N columns.  The state lives in the MFMA
+// accumulators (v_mfma_f32_16x16x32_bf16, K = tokens) for the block's whole
+// life.  Per chunk:
+//   1. store h_prev[c] (bf16) from the accumulators;
+//   2. w_j = dt_j exp2(G_last - G_j), one token per thread, into LDS;
+//   3. build the x*w operand fragments (x is read along its slow axis: lanes
+//      load SPB-wide row pieces of 8 tokens and pair them up in registers),
+//      carried as a bf16 head plus a bf16 remainder (x*w is not exact in
+//      bf16; one rounding costs up to 2^-9 of every term, too much for a
+//      2e-2 rms bound on the final state where |h| runs far above its rms),
+//      in LDS in fragment order; load the next chunk's x meanwhile;
+//   4. scale the accumulators by exp2(G_last) and run the MFMAs over the
+//      chunk's 32-token slabs.  B fragments (exact bf16, shared by the heads
+//      of a group and so L2-resident) come straight from global memory into
+//      registers, one chunk ahead, slab by slab.
+// x and B are read with buffer loads whose range is the chunk's valid rows:
+// a ragged last chunk reads zeros past T (its dt is 0 there as well).
+// Every exponent G_last - G_j and G_last is <= 0.
+
+#include "ssd_device.h"
+#include "ssd_launch.h"
+
+namespace ssd {
+
+namespace {
+
+template <int L, int N, int SPB>
+struct FwdCfg {
+    static constexpr int NS = L / 32;                       // 32-token K slabs per chunk
+    static constexpr int SW = SPB < 2 ? SPB : 2;            // row sets s per wavefront
+    static constexpr int TW = SPB * (N / 16) / (4 * SW);    // n-tiles per wavefront
+    static constexpr int SPW = (NS + 3) / 4;                // x*w slabs built per wavefront
+};
+
+template <int L, int SPB>
+struct FwdSmem {
+    uint4 AF[L / 32][2][SPB][64];  // slab, head/remainder, row set s, lane
+    float w[L];
+};
+
+struct FwdArgs {
+    const uint16_t *x, *B;
+    const float *Gws, *DTws, *init;
+    uint16_t *hprev;
+    float *fin;
+    int64_t T;
+    int32_t H, G, nc, hpg;
+};
+
+// K consecutive bf16 (K = 4, 2, 1) as one or two 32-bit words, by a buffer
+// load at byte offset off (0 past the resource's range).
+template <int K>
+__device__ __forceinline__ uint2 load_bf(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    if constexpr (K == 4) {
+        const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+        return make_uint2(v[0], v[1]);
+    } else if constexpr (K == 2) {
+        return make_uint2(__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0), 0u);
+    } else {
+        return make_uint2((uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0), 0u);
+    }
+}
+// the word of element j of piece v
+__device__ __forceinline__ uint32_t word_of(uint2 v, int j) { return (j < 2) ? v.x : v.y; }
+
+// K consecutive floats of a state row
+template <int K>
+__device__ __forceinline__ void load_f(const float *p, float *v) {
+    if constexpr (K == 4) {
+        const float4 t = *reinterpret_cast<const float4 *>(p);
+        v[0] = t.x; v[1] = t.y; v[2] = t.z; v[3] = t.w;
+    } else if constexpr (K == 2) {
+        const float2 t = *reinterpret_cast<const float2 *>(p);
+        v[0] = t.x; v[1] = t.y;
+    } else {
+        v[0] = *p;
+    }
+}
+template <int K>
+__device__ __forceinline__ void store_f(float *p, const float *v) {
+    if constexpr (K == 4) *reinterpret_cast<float4 *>(p) = make_float4(v[0], v[1], v[2], v[3]);
+    else if constexpr (K == 2) *reinterpret_cast<float2 *>(p) = make_float2(v[0], v[1]);
+    else *p = v[0];
+}
+template <int K>
+__device__ __forceinline__ void store_bf(uint16_t *p, const float *v) {
+    if constexpr (K == 4) store_nt(p, make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])));
+    else if constexpr (K == 2) *reinterpret_cast<uint32_t *>(p) = pack_bf16x2(v[0], v[1]);
+    else *p = (uint16_t)f32_to_bf16_bits(v[0]);
+}
+
+template <int L, int N, int SPB>
+__global__ __launch_bounds__(256, 2) void state_fwd_kernel(FwdArgs a, uint32_t nblk) {
+    using Cfg = FwdCfg<L, N, SPB>;
+    constexpr int P = 64, NS = Cfg::NS, SW = Cfg::SW, TW = Cfg::TW, SPW = Cfg::SPW;
+    constexpr int PSPLIT = 4 / SPB;
+    __shared__ FwdSmem<L, SPB> sm;
+
+    const uint32_t lid = xcd_remap(blockIdx.x, nblk);
+    const int32_t ps = lid % PSPLIT;
+    const uint32_t bh = lid / PSPLIT;
+    const int32_t h = bh % a.H;
+    const int64_t b = bh / a.H;
+    const int32_t g = h / a.hpg;
+    const int W = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int m = lane & 15, q = lane >> 4;
+    const int32_t XR = a.H * P, BR = a.G * N;
+
+    // the block's rows: p = 4M + s0 + s (s < SPB); this wavefront's: s = sb + i
+    // (i < SW); its columns: n = 64 (nt / 4) + 4m + nt % 4, nt = nt0 + j (j < TW)
+    const int s0 = ps * SPB;
+    const int sb = (SPB == 4) ? 2 * (W & 1) : 0;
+    const int nt0 = TW * ((SPB == 4) ? (W >> 1) : W);
+    const int ncol = 64 * (nt0 >> 2) + 4 * m + (nt0 & 3);   // first of TW columns
+    auto prow = [&](int i, int e) { return 4 * (4 * q + e) + s0 + sb + i; };
+
+    const int64_t bhi = (int64_t)b * a.H + h;
+    f32x4 acc[SW][TW];
+#pragma unroll
+    for (int i = 0; i < SW; ++i)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            float v[TW];
+            if (a.init) {
+                load_f<TW>(a.init + (bhi * P + prow(i, e)) * N + ncol, v);
+            } else {
+#pragma unroll
+                for (int j = 0; j < TW; ++j) v[j] = 0.f;
+            }
+#pragma unroll
+            for (int j = 0; j < TW; ++j) acc[i][j][e] = v[j];
+        }
+
+    // raw operands of one chunk: x pieces of the slabs this wavefront builds,
+    // B pieces of its columns for every slab, G and dt of token tid and the
+    // chunk's last G.  All are loaded a chunk ahead, unconditionally (a load
+    // under a branch, or one used right after issue, makes the compiler drain
+    // every outstanding load with vmcnt(0) and serializes the chunks).
+    uint2 xr[SPW][8];
+    uint2 br[NS][8];
+    float gv = 0.f, dtv = 0.f, glv = 0.f;
+    auto nvalid_of = [&](int32_t c) {
+        const int64_t rem = a.T - (int64_t)c * L;
+        return rem < L ? (int32_t)rem : L;
+    };
+    // Each chunk's rows are read through a buffer resource that spans its
+    // valid tokens only: rows past T (ragged last chunk) come back as 0.
+    // The row offset sits in the VGPR offset (the range check covers it); its
+    // uniform part is formed per load, and the stride goes through an empty
+    // asm per call so that the offsets are not hoisted out of the chunk loop
+    // (80 loop-invariant offsets would not fit in registers).
+    auto load_x = [&](int32_t c) {
+        const int32_t nv = nvalid_of(c);
+        int32_t rs = XR * 2;
+        asm volatile("" : "+s"(rs));
+        const auto rx = make_rsrc(a.x + ((b * a.T + (int64_t)c * L) * a.H + h) * P + s0,
+                                  (uint32_t)(nv * rs));
+        const uint32_t lo = (uint32_t)(8 * q * rs + 8 * m);
+#pragma unroll
+        for (int k = 0; k < SPW; ++k) {
+            const int js = W + 4 * k;
+            if (js < NS) {
+#pragma unroll
+                for (int r = 0; r < 8; ++r)
+                    xr[k][r] = load_bf<SPB>(rx, lo + (uint32_t)((32 * js + r) * rs));
+            }
+        }
+        {
+            const int64_t o = (bhi * a.nc + c) * L;
+            gv = a.Gws[o + min(tid, L - 1)];
+            dtv = a.DTws[o + min(tid, L - 1)];
+            glv = a.Gws[o + L - 1];
+        }
+    };
+    auto load_b = [&](int32_t c, int js) {
+        const int32_t nv = nvalid_of(c);
+        int32_t rs = BR * 2;
+        asm volatile("" : "+s"(rs));
+        const auto rb = make_rsrc(a.B + ((b * a.T + (int64_t)c * L) * a.G + g) * N +
+                                      64 * (nt0 >> 2) + (nt0 & 3),
+                                  (uint32_t)(nv * rs));
+        const uint32_t lo = (uint32_t)(8 * q * rs + 8 * m);
+#pragma unroll
+        for (int r = 0; r < 8; ++r)
+            br[js][r] = load_bf<TW>(rb, lo + (uint32_t)((32 * js + r) * rs));
+    };
+
+    if (a.nc > 0) {
+        load_x(0);
+#pragma unroll
+        for (int js = 0; js < NS; ++js) load_b(0, js);
+    }
+    for (int32_t c = 0; c < a.nc; ++c) {
+        const int64_t bhc = bhi * a.nc + c;
+        // 1. the state entering chunk c
+        uint16_t *hp = a.hprev + bhc * (int64_t)(P * N) + ncol;
+#pragma unroll
+        for (int i = 0; i < SW; ++i)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                float v[TW];
+#pragma unroll
+                for (int j = 0; j < TW; ++j) v[j] = acc[i][j][e];
+                store_bf<TW>(hp + prow(i, e) * N, v);
+            }
+        // 2. per-token weights
+        const float glast = glv;
+        if (tid < L) sm.w[tid] = dtv * fast_exp2(glast - gv);
+        __syncthreads();   // w visible; every wavefront is done reading AF of chunk c-1
+        // 3. x*w fragments of this wavefront's slabs, head + remainder
+#pragma unroll
+        for (int k = 0; k < SPW; ++k) {
+            const int js = W + 4 * k;
+            if (js < NS) {
+                const int jw = 32 * js + 8 * q;
+                const float4 w0 = *reinterpret_cast<const float4 *>(&sm.w[jw]);
+                const float4 w1 = *reinterpret_cast<const float4 *>(&sm.w[jw + 4]);
+                const float w[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+#pragma unroll
+                for (int s = 0; s < SPB; ++s) {
+                    uint4 vh, vl;
+                    uint32_t *wh = reinterpret_cast<uint32_t *>(&vh);
+                    uint32_t *wl = reinterpret_cast<uint32_t *>(&vl);
+#pragma unroll
+                    for (int rr = 0; rr < 4; ++rr) {
+                        const uint32_t a0 = word_of(xr[k][2 * rr], s);
+                        const uint32_t a1 = word_of(xr[k][2 * rr + 1], s);
+                        const float e0 = ((s & 1) ? bf16_hi(a0) : bf16_lo(a0)) * w[2 * rr];
+                        const float e1 = ((s & 1) ? bf16_hi(a1) : bf16_lo(a1)) * w[2 * rr + 1];
+                        const uint32_t hw = pack_bf16x2(e0, e1);
+                        wh[rr] = hw;
+                        wl[rr] = pack_bf16x2(e0 - bf16_lo(hw), e1 - bf16_hi(hw));
+                    }
+                    sm.AF[js][0][s][lane] = vh;
+                    sm.AF[js][1][s][lane] = vl;
+                }
+            }
+        }
+        // the next chunk's operands are loaded unconditionally (the last chunk
+        // reloads itself), so no branch lets the compiler move the loads
+        const int32_t cn = min(c + 1, a.nc - 1);
+        load_x(cn);   // in flight during the MFMAs
+        __builtin_amdgcn_sched_barrier(0);
+        __syncthreads();   // AF visible
+        // 4. h <- exp2(G_last) h + (x w)^T B
+        const float dec = fast_exp2(glast);
+#pragma unroll
+        for (int i = 0; i < SW; ++i)
+#pragma unroll
+            for (int j = 0; j < TW; ++j) acc[i][j] *= dec;
+#pragma unroll
+        for (int js = 0; js < NS; ++js) {
+            bf16x8 bfr[TW];
+#pragma unroll
+            for (int j = 0; j < TW; ++j) {
+                const int sn = (nt0 + j) & 3;    // element of the B piece
+                uint4 v;
+                uint32_t *vw = reinterpret_cast<uint32_t *>(&v);
+#pragma unroll
+                for (int rr = 0; rr < 4; ++rr) {
+                    const int el = (TW == 4) ? sn : j;
+                    const uint32_t a0 = word_of(br[js][2 * rr], el);
+                    const uint32_t a1 = word_of(br[js][2 * rr + 1], el);
+                    vw[rr] = (el & 1) ? pair_hi(a0, a1) : pair_lo(a0, a1);
+                }
+                bfr[j] = as_bf16x8(v);
+            }
+            load_b(cn, js);
+            // all head products, then all remainder products: no MFMA waits
+            // on the one just issued
+#pragma unroll
+            for (int hl = 0; hl < 2; ++hl)
+#pragma unroll
+                for (int i = 0; i < SW; ++i) {
+                    const bf16x8 av = as_bf16x8(sm.AF[js][hl][sb + i][lane]);
+#pragma unroll
+                    for (int j = 0; j < TW; ++j) acc[i][j] = mfma16x16x32(av, bfr[j], acc[i][j]);
+                }
+        }
+    }
+    if (a.fin) {
+#pragma unroll
+        for (int i = 0; i < SW; ++i)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                float v[TW];
+#pragma unroll
+                for (int j = 0; j < TW; ++j) v[j] = acc[i][j][e];
+                store_f<TW>(a.fin + (bhi * P + prow(i, e)) * N + ncol, v);
+            }
+    }
+}
+
+template <int L, int N, int SPB>
+hipError_t launch_fwd(const Shape &s, const FwdArgs &a, hipStream_t st) {
+    const uint64_t nblk = (uint64_t)s.Bt * s.H * (4 / SPB);
+    hipLaunchKernelGGL((state_fwd_kernel<L, N, SPB>), dim3((uint32_t)nblk), dim3(256), 0, st, a,
+                       (uint32_t)nblk);
+    return hipGetLastError();
+}
+
+template <int L, int N>
+hipError_t launch_fwd_n(const Shape &s, const FwdArgs &a, int spb, hipStream_t st) {
+    switch (spb) {
+    case 4: return launch_fwd<L, N, 4>(s, a, st);
+    case 2: return launch_fwd<L, N, 2>(s, a, st);
+    case 1: return launch_fwd<L, N, 1>(s, a, st);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+template <int L>
+hipError_t launch_fwd_l(const Shape &s, const FwdArgs &a, int spb, hipStream_t st) {
+    if (s.N == 64) return launch_fwd_n<L, 64>(s, a, spb, st);
+    if (s.N == 128) return launch_fwd_n<L, 128>(s, a, spb, st);
+    return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+int state_fwd_rows_per_block(const Shape &s) {
+    // all 64 rows per workgroup (the x*w operand built once per head and
+    // chunk); the 2- and 1-row-set splits exist for few, long chains
+    (void)s;
+    return 4;
+}
+
+bool state_fwd_preferred(const Shape &s) {
+    // The chunks of a chain run one after another, so the one-pass form only
+    // pays when Bt*H chains keep the GPU busy (two 4-wavefront workgroups per
+    // CU, 512 on 256 CUs); with fewer chains, or very long ones, the
+    // chunk-parallel chunk_state + state_passing pair is faster.
+    return s.Bt * s.H >= 384;
+}
+
+bool state_fwd_supported(const Shape &s) {
+    // per-chunk byte offsets of x and B rows are 32-bit
+    const int64_t lim = (int64_t(1) << 31) - 1;
+    return s.bf16 && s.P == 64 && s.L * s.H * s.P * 2 <= lim && s.L * s.G * s.N * 2 <= lim;
+}
+
+hipError_t launch_state_fwd(const Shape &s, const void *x, const void *B, const float *Gws,
+                            const float *DTws, const float *init, void *hprev, float *fin,
+                            int spb, hipStream_t st) {
+    if (!state_fwd_supported(s)) return hipErrorInvalidValue;
+    if (s.Bt == 0 || s.H == 0) return hipSuccess;
+    if (s.nc == 0 && !fin) return hipSuccess;
+    FwdArgs a;
+    a.x = (const uint16_t *)x;
+    a.B = (const uint16_t *)B;
+    a.Gws = Gws;
+    a.DTws = DTws;
+    a.init = init;
+    a.hprev = (uint16_t *)hprev;
+    a.fin = fin;
+    a.T = s.T;
+    a.H = (int32_t)s.H;
+    a.G = (int32_t)s.G;
+    a.nc = (int32_t)s.nc;
+    a.hpg = (int32_t)(s.H / s.G);
+    if (spb <= 0) spb = state_fwd_rows_per_block(s);
+    switch (s.L) {
+    case 64: return launch_fwd_l<64>(s, a, spb, st);
+    case 128: return launch_fwd_l<128>(s, a, spb, st);
+    case 256: return launch_fwd_l<256>(s, a, spb, st);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace ssd

@@ -72,6 +72,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "ssd_chunk_state": ([vp, vp, i64, dp, vp, sz, vp], st),
         "ssd_state_passing": ([vp, vp, i64, dp, vp, sz, vp], st),
         "ssd_chunk_scan": ([vp, vp, vp, vp, vp, i64, dp, vp, sz, vp], st),
+        "ssd_state_fwd": ([vp, vp, vp, vp, i64, dp, vp, sz, vp], st),
         "ssd_decode_step": ([vp, vp, vp, vp, vp, vp, vp, vp, dp, vp], st),
         "ssd_status_string": ([st], ctypes.c_char_p),
         "ssd_last_error_detail": ([], ctypes.c_char_p),
@@ -220,6 +221,14 @@ def ssd_state_passing(a: FwdArgs):
     _check("ssd_state_passing", lib.ssd_state_passing(_ptr(a.init), _ptr(a.final), a.L,
                                                       ctypes.byref(a.dims), _ptr(a.ws),
                                                       a.ws.numel(), _stream(a.device)))
+
+
+def ssd_state_fwd(a: FwdArgs):
+    """chunk_state + state_passing in one pass (bf16): h_prev and final_state."""
+    lib = load_library()
+    _check("ssd_state_fwd", lib.ssd_state_fwd(_ptr(a.x), _ptr(a.B), _ptr(a.init), _ptr(a.final),
+                                              a.L, ctypes.byref(a.dims), _ptr(a.ws),
+                                              a.ws.numel(), _stream(a.device)))
 
 
 def ssd_chunk_scan(a: FwdArgs):

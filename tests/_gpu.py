@@ -60,3 +60,17 @@ def assert_close(got, ref, io: str, what: str):
     r = err_ratio(got, ref, io)
     log("  %-28s err/tol = %.4f" % (what, r))
     assert r <= 1.0, "%s: error is %.3fx the tolerance" % (what, r)
+
+
+def assert_bf16_stored(got, ref, what: str):
+    """A bf16 intermediate (h_prev) against its fp64 value: storing an fp32
+    value as bf16 (round to nearest even) costs up to 2^-9 of it, so allow
+    2^-8 |ref| per element, plus 2e-3 rms(ref) for the fp32 accumulation."""
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    assert np.all(np.isfinite(got)), "%s: non-finite values" % what
+    rms = float(np.sqrt(np.mean(ref * ref)))
+    excess = np.abs(got - ref) - 2.0 ** -8 * np.abs(ref)
+    r = float(np.max(excess)) / max(2e-3 * rms, 1e-30)
+    log("  %-28s err/tol = %.4f (bf16 storage bound)" % (what, max(r, 0.0)))
+    assert r <= 1.0, "%s: error is %.3fx the bf16 storage bound" % (what, r)

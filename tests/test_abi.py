@@ -135,6 +135,21 @@ def test_stage_calls_validate_too():
     assert L.ssd_state_passing(None, None, 256, ctypes.byref(d), P16, 10, None) == -5
     assert L.ssd_chunk_scan(P16, P16, P16, None, P16, 256, ctypes.byref(d), P16, 1 << 40,
                             None) == -1
+    assert L.ssd_state_fwd(None, P16, None, P16, 256, ctypes.byref(d), P16, 1 << 40, None) == -1
+    assert L.ssd_state_fwd(P16, P16, P_MIS, P16, 256, ctypes.byref(d), P16, 1 << 40, None) == -4
+    assert L.ssd_state_fwd(P16, P16, None, None, 256, ctypes.byref(d), P16, 10, None) == -5
+
+
+def test_state_fwd_needs_bf16_and_32bit_row_spans():
+    L = lib()
+    d = dims(io=ssd.SSD_F32)
+    assert L.ssd_state_fwd(P16, P16, None, P16, 256, ctypes.byref(d), P16, 1 << 40, None) == -3
+    assert "bf16" in L.ssd_last_error_detail().decode()
+    # 256 tokens * 65536 heads * 64 * 2 bytes = 2^31: per-chunk x offsets leave 32 bits
+    d = dims(Bt=1, T=256, H=1 << 16, G=1)
+    assert L.ssd_state_fwd(P16, P16, None, P16, 256, ctypes.byref(d), P16, 1 << 60, None) == -3
+    d = dims(Bt=1, T=256, H=(1 << 16) - 8, G=1)
+    assert L.ssd_state_fwd(P16, P16, None, P16, 256, ctypes.byref(d), P16, 10, None) == -5
 
 
 def _dec(d, state=P16, x=P16, dt=P16, B=P16, C=P16, A=P16, D=P16, y=P16):

@@ -88,18 +88,32 @@ def test_intermediates_against_chunked_reference(io):
     assert_close(host(a.final), ref["final"], io, "final")
 
 
-@pytest.mark.parametrize("io", [gen.F32, gen.BF16])
-def test_fused_call_equals_stage_calls_bitwise(io):
+@pytest.mark.parametrize("io,path", [(gen.F32, "auto"), (gen.BF16, "0"), (gen.BF16, "4")])
+def test_fused_call_equals_stage_calls_bitwise(io, path, monkeypatch):
+    # ssd_chunked_fwd is cumsum, state + passing or the one-pass state stage, scan
+    if path != "auto":
+        monkeypatch.setenv("SSD_STATE_FWD_ROWS", path)
     inp = gen.make_small(2, 300, 8, 64, 128, 2, io, init_state=True, seed=37)
     t = upload_fwd(inp, io)
     y1, f1 = ssd.ssd_chunked_fwd(t["x"], t["dt"], t["A"], t["B"], t["C"], t["D"], 128,
                                  t["init_state"])
     a = ssd.FwdArgs(t["x"], t["dt"], t["A"], t["B"], t["C"], t["D"], 128, t["init_state"])
-    for stage in (ssd.ssd_chunk_cumsum, ssd.ssd_chunk_state, ssd.ssd_state_passing,
-                  ssd.ssd_chunk_scan):
+    mid = (ssd.ssd_state_fwd,) if path == "4" else (ssd.ssd_chunk_state, ssd.ssd_state_passing)
+    for stage in (ssd.ssd_chunk_cumsum,) + mid + (ssd.ssd_chunk_scan,):
         stage(a)
     torch.cuda.synchronize()
     assert torch.equal(y1, a.y) and torch.equal(f1, a.final)
+
+
+@pytest.mark.parametrize("rows", ["0", "4", "2", "1"])
+def test_both_state_paths_against_oracle(rows, monkeypatch):
+    # the same forward through the two stages and through each one-pass split
+    monkeypatch.setenv("SSD_STATE_FWD_ROWS", rows)
+    inp = gen.make_small(2, 3 * 128 + 21, 4, 64, 128, 2, gen.BF16, init_state=True, seed=83)
+    y, fin = run_fwd(inp, gen.BF16, 128)
+    yr, fr = oracle_full(inp)
+    assert_close(host(y), yr, gen.BF16, "y rows=%s" % rows)
+    assert_close(host(fin), fr, gen.BF16, "final rows=%s" % rows)
 
 
 @pytest.mark.parametrize("io", [gen.F32, gen.BF16])
@@ -113,7 +127,9 @@ def test_reruns_are_bitwise_identical(io):
         assert torch.equal(y, outs[0][0]) and torch.equal(f, outs[0][1])
 
 
-def test_init_state_may_alias_final_state():
+@pytest.mark.parametrize("rows", ["0", "4"])
+def test_init_state_may_alias_final_state(rows, monkeypatch):
+    monkeypatch.setenv("SSD_STATE_FWD_ROWS", rows)
     io = gen.BF16
     inp = gen.make_small(2, 256, 4, 64, 128, 1, io, init_state=True, seed=43)
     t = upload_fwd(inp, io)
@@ -127,8 +143,9 @@ def test_init_state_may_alias_final_state():
     assert torch.equal(y1, y2) and torch.equal(f1, st)
 
 
-@pytest.mark.parametrize("io", [gen.F32, gen.BF16])
-def test_chunk_aligned_split_equals_one_call(io):
+@pytest.mark.parametrize("io,rows", [(gen.F32, ""), (gen.BF16, "0"), (gen.BF16, "4")])
+def test_chunk_aligned_split_equals_one_call(io, rows, monkeypatch):
+    monkeypatch.setenv("SSD_STATE_FWD_ROWS", rows)
     L = 64
     inp = gen.make_small(2, 5 * L, 4, 64, 64, 2, io, init_state=True, seed=47)
     t = upload_fwd(inp, io)
@@ -145,8 +162,9 @@ def test_chunk_aligned_split_equals_one_call(io):
     assert torch.equal(fb, f)
 
 
-@pytest.mark.parametrize("io", [gen.F32, gen.BF16])
-def test_empty_sequence_passes_state_through(io):
+@pytest.mark.parametrize("io,rows", [(gen.F32, ""), (gen.BF16, "0"), (gen.BF16, "4")])
+def test_empty_sequence_passes_state_through(io, rows, monkeypatch):
+    monkeypatch.setenv("SSD_STATE_FWD_ROWS", rows)
     dt = torch.bfloat16 if io == gen.BF16 else torch.float32
     x = torch.empty((2, 0, 4, 64), dtype=dt, device="cuda")
     B = torch.empty((2, 0, 1, 64), dtype=dt, device="cuda")
@@ -215,10 +233,13 @@ def _check_sampled(w, inp, y, fin, npairs=12):
     assert_close(fg, fr, w.io_dtype, "%s final" % w.name)
 
 
-@pytest.mark.parametrize("idx", [1, 2, 3])
-def test_full_size_workload(idx):
+@pytest.mark.parametrize("idx,rows", [(1, ""), (2, ""), (2, "0"), (3, "")])
+def test_full_size_workload(idx, rows, monkeypatch):
+    # rows "" = the path the shape selects (two-stage state for 1 and 3,
+    # one-pass for 2); "0" = the two-stage state path for 2 as well
+    monkeypatch.setenv("SSD_STATE_FWD_ROWS", rows)
     w = gen.WORKLOADS[idx]
-    log("workload", w.name, w.description)
+    log("workload", w.name, w.description, "rows", rows or "auto")
     inp = gen.make_fwd(w, 0)
     t = upload_fwd(inp, w.io_dtype)
     y, fin = ssd.ssd_chunked_fwd(t["x"], t["dt"], t["A"], t["B"], t["C"], t["D"], w.chunk_size,
