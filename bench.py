@@ -2,11 +2,15 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload mamba2_2p7b]
 
-One step = one chunked forward over one batch of the workload (the four
-stages chunk_cumsum -> chunk_state -> state_passing -> chunk_scan, called
-through the C ABI on torch's current stream, with HIP events between the
-stages so each kernel's duration is measured inside the timed region).  The
-inputs are generated, uploaded and resident in HBM before timing starts.
+One step = one chunked forward over one batch of the workload: one
+ssd_chunked_fwd call through the C ABI (chunk_cumsum, then the one-pass
+chunk_state + state_passing stage or the two separate stages -- whichever the
+library selects for the shape -- then chunk_scan) on torch's current stream.
+The inputs are generated, uploaded and resident in HBM before timing starts;
+K steps are timed between two synchronizations and give the tokens/s value.
+A second pass runs the same stages one call at a time with HIP events between
+them (on the stream the kernels run on) for each kernel's duration, from
+which the roofline of the dominant kernel is computed.
 
 Prints one JSON line (stdout): tokens/s of the forward, the roofline of the
 dominant kernel, per-kernel times and rooflines, the decode step's HBM
@@ -66,6 +70,11 @@ def algorithmic(w, io_bytes: int):
         flops=2 * units * P * N)
     tri = L * (L + 1) // 2
     tok_y = Bt * T * H * P * 4           # y is written fp32
+    # one pass: x, B, G and DT in, h_prev out, init/final state; S never exists
+    out["state_fwd"] = dict(
+        bytes=tok_x + tok_bc + gdt + units * P * N * io_bytes
+        + (state if w.init_state else 0) + state,
+        flops=2 * P * N * L * units + 2 * units * P * N)
     out["chunk_scan"] = dict(
         bytes=tok_x + tok_y + 2 * tok_bc + units * P * N * io_bytes + gdt,
         flops=units * (2 * L * P * N + 2 * tri * P) + (Bt * G * nc) * 2 * tri * N)
@@ -123,30 +132,46 @@ def run_forward(w, steps: int, warmup: int):
                     up(inp.D), w.chunk_size,
                     None if inp.init_state is None else up(inp.init_state))
     log("inputs generated and resident in HBM (%.1f s)" % (time.time() - t0))
-    stages = [("chunk_cumsum", ssd.ssd_chunk_cumsum), ("chunk_state", ssd.ssd_chunk_state),
-              ("state_passing", ssd.ssd_state_passing), ("chunk_scan", ssd.ssd_chunk_scan)]
+    one_pass = ssd.uses_state_fwd(a.dims, w.chunk_size)
+
+    # the boundary call, K steps between two synchronizations
+    def step():
+        ssd.ssd_chunked_fwd(a)
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t_start = time.perf_counter()
+    e0.record()
+    for _ in range(steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    step_ms = e0.elapsed_time(e1) / steps
+
+    # the same stages one call at a time, HIP events between them
+    mid = ([("state_fwd", ssd.ssd_state_fwd)] if one_pass else
+           [("chunk_state", ssd.ssd_chunk_state), ("state_passing", ssd.ssd_state_passing)])
+    stages = [("chunk_cumsum", ssd.ssd_chunk_cumsum)] + mid + [("chunk_scan", ssd.ssd_chunk_scan)]
     for _ in range(warmup):
         for _, f in stages:
             f(a)
     torch.cuda.synchronize()
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)]
           for _ in range(steps)]
-    torch.cuda.synchronize()
-    t_start = time.perf_counter()
     for k in range(steps):
         ev[k][0].record()
         for i, (_, f) in enumerate(stages):
             f(a)
             ev[k][i + 1].record()
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t_start
     per = np.array([[ev[k][i].elapsed_time(ev[k][i + 1]) for i in range(len(stages))]
                     for k in range(steps)])          # ms
-    step_ms = np.array([ev[k][0].elapsed_time(ev[k][-1]) for k in range(steps)])
     kern = {name: float(per[:, i].mean()) for i, (name, _) in enumerate(stages)}
     del a
     torch.cuda.empty_cache()
-    return wall, step_ms, kern
+    return wall, step_ms, kern, one_pass
 
 
 def run_decode(w, steps: int, warmup: int):
@@ -242,12 +267,14 @@ def run_cpu_baseline(w, target_s: float = 12.0):
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--workload", default="mamba2_2p7b")
     ap.add_argument("--decode-steps", type=int, default=50)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--copy-reference-only", action="store_true",
+                    help="only the 1 GiB device copy (calibrates HBM byte counters)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -262,13 +289,17 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
+    if args.copy_reference_only:
+        print(json.dumps({"hbm_copy_reference_GBps": round(run_copy_reference(), 1),
+                          "bytes_read": 1 << 30, "bytes_written": 1 << 30}), flush=True)
+        return
     ssd.load_library()   # fails loudly if libssd.so is missing
 
     w = gen.BY_NAME[args.workload]
     io_bytes = 2 if w.io_dtype == gen.BF16 else 4
     log("workload %s: %s" % (w.name, w.description))
 
-    wall, step_ms, kern = run_forward(w, args.steps, args.warmup)
+    wall, step_ms, kern, one_pass = run_forward(w, args.steps, args.warmup)
     tokens = w.batch * w.seqlen
     value = tokens * args.steps / wall
     alg = algorithmic(w, io_bytes)
@@ -289,11 +320,13 @@ def main():
                 "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                 "traffic": measured_traffic(dom, w.name),
                 "avg_launch_us": round(dms * 1e3, 2), "alg_bytes_per_launch": int(alg[dom]["bytes"])}
-    chunk_flops = alg["chunk_state"]["flops"] + alg["chunk_scan"]["flops"]
-    chunk_ms = kern["chunk_state"] + kern["chunk_scan"]
-    fwd_flops = sum(a["flops"] for a in alg.values())
-    log("forward: %.1f us/step, %.3e tokens/s; dominant %s %.1f us" %
-        (float(np.mean(step_ms)) * 1e3, value, dom, dms * 1e3))
+    mfma_kernels = [k for k in ("chunk_state", "state_fwd", "chunk_scan") if k in kern]
+    chunk_flops = sum(alg[k]["flops"] for k in mfma_kernels)
+    chunk_ms = sum(kern[k] for k in mfma_kernels)
+    fwd_flops = sum(alg[k]["flops"] for k in kern)
+    log("forward: %.1f us/step (ssd_chunked_fwd), %.3e tokens/s; stages %s; dominant %s %.1f us"
+        % (step_ms * 1e3, value, " ".join("%s %.1f" % (k, v * 1e3) for k, v in kern.items()),
+           dom, dms * 1e3))
 
     decode = None
     if not args.no_decode:
@@ -328,7 +361,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(float(np.mean(step_ms)), 4),
+        "ms_per_step": round(step_ms, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -340,8 +373,8 @@ def main():
                    "init_state": w.init_state, "parallelism": "single GPU"},
         "roofline": roofline,
         "cpu_baseline": cpu,
-        "forward_bf16_mfma_frac": round(fwd_flops / (float(np.mean(step_ms)) * 1e-3) / 1e12
-                                        / BF16_PEAK_TFLOPS, 4),
+        "state_path": "one-pass state_fwd" if one_pass else "chunk_state + state_passing",
+        "forward_bf16_mfma_frac": round(fwd_flops / (step_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
         "chunk_kernels_bf16_mfma_frac": round(chunk_flops / (chunk_ms * 1e-3) / 1e12
                                               / BF16_PEAK_TFLOPS, 4),
         "kernels": kernels,

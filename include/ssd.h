@@ -170,6 +170,14 @@ ssd_status ssd_state_fwd(const void *x, const void *B, const float *init_state,
                          void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * Which state path ssd_chunked_fwd would take for these dims and chunk size
+ * under the current environment: *uses_state_fwd = 1 for the one-pass
+ * ssd_state_fwd stage (the workspace's S region is then left untouched),
+ * 0 for ssd_chunk_state + ssd_state_passing.  Host only; no HIP call.
+ */
+ssd_status ssd_chunked_fwd_path(const ssd_dims *dims, int64_t chunk_size, int *uses_state_fwd);
+
+/*
  * One recurrent decode step ("Optimizing Nemotron v3 Super in TensorRT-LLM",
  * section 6.1; "mamba-metal: running Mamba on Apple Silicon", section on
  * O(L) incremental decoding): for every (b, h),

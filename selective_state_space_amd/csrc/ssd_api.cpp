@@ -310,6 +310,15 @@ ssd_status ssd_state_fwd(const void *x, const void *B, const float *init_state,
     return ok();
 }
 
+ssd_status ssd_chunked_fwd_path(const ssd_dims *dims, int64_t chunk_size, int *uses_state_fwd) {
+    if (!uses_state_fwd) return fail(SSD_ERR_NULL, "uses_state_fwd is NULL");
+    ssd::Shape s;
+    const ssd_status r = check_dims(dims, chunk_size, true, &s);
+    if (r != SSD_OK) return r;
+    *uses_state_fwd = use_state_fwd(s) ? 1 : 0;
+    return ok();
+}
+
 ssd_status ssd_chunked_fwd(const void *x, const float *dt, const float *A, const void *B,
                            const void *C, const float *D, int64_t chunk_size,
                            const float *init_state, void *y, float *final_state,

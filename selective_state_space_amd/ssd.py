@@ -73,6 +73,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "ssd_state_passing": ([vp, vp, i64, dp, vp, sz, vp], st),
         "ssd_chunk_scan": ([vp, vp, vp, vp, vp, i64, dp, vp, sz, vp], st),
         "ssd_state_fwd": ([vp, vp, vp, vp, i64, dp, vp, sz, vp], st),
+        "ssd_chunked_fwd_path": ([dp, i64, ctypes.POINTER(ctypes.c_int)], st),
         "ssd_decode_step": ([vp, vp, vp, vp, vp, vp, vp, vp, dp, vp], st),
         "ssd_status_string": ([st], ctypes.c_char_p),
         "ssd_last_error_detail": ([], ctypes.c_char_p),
@@ -183,18 +184,25 @@ class FwdArgs:
         self.device = dev
 
 
-def ssd_chunked_fwd(x, dt, A, B, C, D, chunk_size: int, init_state=None, y=None,
-                    final_state=None, want_final: bool = True, workspace=None):
+def ssd_chunked_fwd(x, dt=None, A=None, B=None, C=None, D=None, chunk_size=None,
+                    init_state=None, y=None, final_state=None, want_final: bool = True,
+                    workspace=None):
     """Chunked forward.  Returns (y, final_state or None).
 
     x [Bt,T,H,P] (float32 or bfloat16), dt [Bt,T,H] f32, A/D [H] f32,
     B/C [Bt,T,G,N] (x's dtype), init_state [Bt,H,P,N] f32 or None.  y is
     float32 [Bt,T,H,P] whatever the input dtype.  ``y``,
     ``final_state`` and ``workspace`` may be passed in to avoid allocation;
-    ``final_state`` may be the same tensor as ``init_state``.
+    ``final_state`` may be the same tensor as ``init_state``.  ``x`` may
+    instead be a prepared FwdArgs (then the other arguments are ignored).
     """
-    a = x if isinstance(x, FwdArgs) else FwdArgs(x, dt, A, B, C, D, chunk_size, init_state, y,
-                                                 final_state, want_final, workspace)
+    if isinstance(x, FwdArgs):
+        a = x
+    else:
+        if any(v is None for v in (dt, A, B, C, D, chunk_size)):
+            raise ValueError("ssd_chunked_fwd needs x, dt, A, B, C, D and chunk_size")
+        a = FwdArgs(x, dt, A, B, C, D, chunk_size, init_state, y, final_state, want_final,
+                    workspace)
     lib = load_library()
     st = lib.ssd_chunked_fwd(_ptr(a.x), _ptr(a.dt), _ptr(a.A), _ptr(a.B), _ptr(a.C), _ptr(a.D),
                              a.L, _ptr(a.init), _ptr(a.y), _ptr(a.final), ctypes.byref(a.dims),
@@ -229,6 +237,14 @@ def ssd_state_fwd(a: FwdArgs):
     _check("ssd_state_fwd", lib.ssd_state_fwd(_ptr(a.x), _ptr(a.B), _ptr(a.init), _ptr(a.final),
                                               a.L, ctypes.byref(a.dims), _ptr(a.ws),
                                               a.ws.numel(), _stream(a.device)))
+
+
+def uses_state_fwd(dims: Dims, chunk_size: int) -> bool:
+    """True if ssd_chunked_fwd takes the one-pass state stage for this shape."""
+    out = ctypes.c_int(-1)
+    _check("ssd_chunked_fwd_path", load_library().ssd_chunked_fwd_path(
+        ctypes.byref(dims), chunk_size, ctypes.byref(out)))
+    return out.value == 1
 
 
 def ssd_chunk_scan(a: FwdArgs):

@@ -140,6 +140,21 @@ def test_stage_calls_validate_too():
     assert L.ssd_state_fwd(P16, P16, None, None, 256, ctypes.byref(d), P16, 10, None) == -5
 
 
+def test_path_query(monkeypatch):
+    out = ctypes.c_int(-1)
+    q = lambda d: lib().ssd_chunked_fwd_path(ctypes.byref(d), 256, ctypes.byref(out))
+    monkeypatch.delenv("SSD_STATE_FWD_ROWS", raising=False)
+    assert q(dims(Bt=8, T=4096, H=80, G=1)) == 0 and out.value == 1      # 640 chains
+    assert q(dims(Bt=4, T=2048, H=32, G=1)) == 0 and out.value == 0      # 128 chains
+    assert q(dims(Bt=8, T=4096, H=80, G=1, io=ssd.SSD_F32)) == 0 and out.value == 0
+    monkeypatch.setenv("SSD_STATE_FWD_ROWS", "0")
+    assert q(dims(Bt=8, T=4096, H=80, G=1)) == 0 and out.value == 0
+    monkeypatch.setenv("SSD_STATE_FWD_ROWS", "2")
+    assert q(dims(Bt=1, T=4096, H=8, G=1)) == 0 and out.value == 1
+    assert lib().ssd_chunked_fwd_path(ctypes.byref(dims()), 256, None) == -1
+    assert q(dims(P=32)) == -3
+
+
 def test_state_fwd_needs_bf16_and_32bit_row_spans():
     L = lib()
     d = dims(io=ssd.SSD_F32)
