@@ -129,7 +129,7 @@ __device__ __forceinline__ void head_load(HeadRegs<L, N> &r, const ScanArgs<L, N
         for (int rr = 0; rr < 8; ++rr) {
             const int tl = 32 * js + ((rr < 4) ? 0 : 16) + 4 * q + (rr & 3);
             r.xr[k][rr] = (js < NS && (!RAGGED || tl < nvalid))
-                              ? *reinterpret_cast<const uint2 *>(xb + tl * XR + 4 * m)
+                              ? load_nt(xb + tl * XR + 4 * m)
                               : make_uint2(0u, 0u);
         }
     }

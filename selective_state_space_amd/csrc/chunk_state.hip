@@ -121,7 +121,7 @@ __device__ __forceinline__ void chunk_state_group(StateSmem<L, N> &sm, const Sta
 #pragma unroll
             for (int rr = 0; rr < 8; ++rr)
                 r.x[k][rr] = (js < NS && valid(jw + rr))
-                                 ? *reinterpret_cast<const uint2 *>(xb + (jw + rr) * XR)
+                                 ? load_nt(xb + (jw + rr) * XR)
                                  : make_uint2(0u, 0u);
         }
         if (tid < L) {

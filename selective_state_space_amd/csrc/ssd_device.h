@@ -36,6 +36,15 @@ __device__ __forceinline__ float4 load_nt(const float *p) {
     const f32x4 v = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(p));
     return make_float4(v[0], v[1], v[2], v[3]);
 }
+__device__ __forceinline__ uint2 load_nt(const uint16_t *p) {   // 4 bf16
+    const u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(p));
+    return make_uint2(v[0], v[1]);
+}
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 load_nt8(const uint16_t *p) {  // 8 bf16
+    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+    return make_uint4(v[0], v[1], v[2], v[3]);
+}
 __device__ __forceinline__ void store_nt(float *p, float4 v) {
     const f32x4 w = {v.x, v.y, v.z, v.w};
     __builtin_nontemporal_store(w, reinterpret_cast<f32x4 *>(p));

@@ -66,16 +66,19 @@ struct FwdArgs {
 };
 
 // K consecutive bf16 (K = 4, 2, 1) as one or two 32-bit words, by a buffer
-// load at byte offset off (0 past the resource's range).
-template <int K>
+// load at byte offset off (0 past the resource's range).  AUX is the cache
+// policy: kStream (nt) for data read once (x), 0 for data shared across
+// workgroups through L2 (B).
+constexpr int kStream = 2;
+template <int K, int AUX = 0>
 __device__ __forceinline__ uint2 load_bf(__amdgpu_buffer_rsrc_t r, uint32_t off) {
     if constexpr (K == 4) {
-        const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+        const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, AUX);
         return make_uint2(v[0], v[1]);
     } else if constexpr (K == 2) {
-        return make_uint2(__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0), 0u);
+        return make_uint2(__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, AUX), 0u);
     } else {
-        return make_uint2((uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0), 0u);
+        return make_uint2((uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, off, 0, AUX), 0u);
     }
 }
 // the word of element j of piece v
@@ -181,7 +184,7 @@ __global__ __launch_bounds__(256, 2) void state_fwd_kernel(FwdArgs a, uint32_t n
             if (js < NS) {
 #pragma unroll
                 for (int r = 0; r < 8; ++r)
-                    xr[k][r] = load_bf<SPB>(rx, lo + (uint32_t)((32 * js + r) * rs));
+                    xr[k][r] = load_bf<SPB, kStream>(rx, lo + (uint32_t)((32 * js + r) * rs));
             }
         }
         {
