@@ -111,7 +111,9 @@ Layout layout_of(const ssd::Shape &s) {
     Layout l;
     const size_t units = (size_t)s.Bt * s.H * s.nc;
     const size_t g = units * s.L * sizeof(float);
-    const size_t st = units * s.P * s.N * sizeof(float);
+    // S, or on the one-pass state path B in MFMA fragment order
+    size_t st = units * s.P * s.N * sizeof(float);
+    if (ssd::state_fwd_bfrag_bytes(s) > st) st = ssd::state_fwd_bfrag_bytes(s);
     const size_t hp = units * s.P * s.N * (s.bf16 ? 2 : 4);
     l.off[0] = 0;
     l.off[1] = align256(l.off[0] + g);
@@ -192,7 +194,7 @@ bool use_state_fwd(const ssd::Shape &s) {
 ssd_status run_state_fwd(const ssd::Shape &s, const void *x, const void *B, const float *init,
                          float *fin, const Ws &w, hipStream_t st) {
     const int r = state_fwd_rows();
-    return hip_result(ssd::launch_state_fwd(s, x, B, w.G, w.DT, init, w.hprev, fin,
+    return hip_result(ssd::launch_state_fwd(s, x, B, w.G, w.DT, init, w.hprev, fin, w.S,
                                             r > 0 ? r : 0, st),
                       "state_fwd", st);
 }

@@ -25,9 +25,11 @@ hipError_t launch_chunk_scan(const Shape &s, const void *x, const void *B, const
 // or 1 row sets of the head per workgroup, 0 = chosen from the shape.
 bool state_fwd_supported(const Shape &s);
 bool state_fwd_preferred(const Shape &s);   // shape heuristic of the fused call
+// bfrag: scratch of state_fwd_bfrag_bytes(s) bytes (B in fragment order).
+size_t state_fwd_bfrag_bytes(const Shape &s);
 hipError_t launch_state_fwd(const Shape &s, const void *x, const void *B, const float *Gws,
                             const float *DTws, const float *init, void *hprev, float *fin,
-                            int rows_per_block, hipStream_t st);
+                            void *bfrag, int rows_per_block, hipStream_t st);
 hipError_t launch_decode_step(const Shape &s, float *state, const void *x, const float *dt,
                               const void *B, const void *C, const float *A, const float *D,
                               void *y, hipStream_t st);

@@ -30,7 +30,10 @@
 //   4. scale the accumulators by exp2(G_last) and run the MFMAs over the
 //      chunk's 32-token slabs.  B fragments (exact bf16, shared by the heads
 //      of a group and so L2-resident) come straight from global memory into
-//      registers, one chunk ahead, slab by slab.
+//      registers, one chunk ahead, slab by slab: b_fragments_kernel lays B
+//      out in fragment order beforehand (once per (b, chunk, group), in the
+//      workspace region the four-stage form uses for S), so each is one
+//      16-byte load with no transpose.
 // x and B are read with buffer loads whose range is the chunk's valid rows:
 // a ragged last chunk reads zeros past T (its dt is 0 there as well).
 // Every exponent G_last - G_j and G_last is <= 0.
@@ -57,7 +60,8 @@ struct FwdSmem {
 };
 
 struct FwdArgs {
-    const uint16_t *x, *B;
+    const uint16_t *x;
+    const uint4 *BF;   // B in MFMA fragment order, from b_fragments_kernel
     const float *Gws, *DTws, *init;
     uint16_t *hprev;
     float *fin;
@@ -110,6 +114,46 @@ __device__ __forceinline__ void store_bf(uint16_t *p, const float *v) {
     else *p = (uint16_t)f32_to_bf16_bits(v[0]);
 }
 
+// B of one (b, chunk, group) laid out as the MFMA B operand of the state
+// product: fragment (slab js, n-tile nt) is 64 lanes x 16 bytes, lane
+// (m, q) holding B[32 js + 8 q + e][n] for e = 0..7 and
+// n = 64 (nt / 4) + 4 m + nt % 4.  Tokens past T are zero.  One workgroup per
+// (b, chunk, group, slab) stages the 32 x N slab in LDS with coalesced 16-byte
+// row loads and writes the N/16 fragments with 16-byte stores.
+template <int L, int N>
+__global__ __launch_bounds__(256) void b_fragments_kernel(const uint16_t *__restrict__ B,
+                                                          uint4 *__restrict__ BF, int64_t T,
+                                                          int32_t G, int32_t nc) {
+    constexpr int NS = L / 32, NT = N / 16, RW = N / 8;   // 16-byte pieces per row
+    __shared__ uint16_t tile[32][N + 8];
+    const int64_t blk = blockIdx.x;                    // ((b * nc + c) * G + g) * NS + js
+    const int js = (int)(blk % NS);
+    const int64_t bcg = blk / NS;
+    const int32_t g = (int32_t)(bcg % G);
+    const int64_t bc = bcg / G;
+    const int32_t c = (int32_t)(bc % nc);
+    const int64_t b = bc / nc;
+    const int tid = threadIdx.x;
+    for (int k = tid; k < 32 * RW; k += 256) {
+        const int r = k / RW, pc = k % RW;
+        const int64_t tok = (int64_t)c * L + 32 * js + r;
+        uint4 v = make_uint4(0u, 0u, 0u, 0u);
+        if (tok < T) v = *reinterpret_cast<const uint4 *>(B + ((b * T + tok) * G + g) * N + 8 * pc);
+        *reinterpret_cast<uint4 *>(&tile[r][8 * pc]) = v;
+    }
+    __syncthreads();
+    for (int k = tid; k < NT * 64; k += 256) {
+        const int nt = k / 64, l = k % 64, m = l & 15, q = l >> 4;
+        const int n = 64 * (nt >> 2) + 4 * m + (nt & 3);
+        uint4 v;
+        uint32_t *vw = reinterpret_cast<uint32_t *>(&v);
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr)
+            vw[rr] = (uint32_t)tile[8 * q + 2 * rr][n] | ((uint32_t)tile[8 * q + 2 * rr + 1][n] << 16);
+        BF[blk * (NT * 64) + k] = v;
+    }
+}
+
 template <int L, int N, int SPB>
 __global__ __launch_bounds__(256, 2) void state_fwd_kernel(FwdArgs a, uint32_t nblk) {
     using Cfg = FwdCfg<L, N, SPB>;
@@ -126,7 +170,8 @@ __global__ __launch_bounds__(256, 2) void state_fwd_kernel(FwdArgs a, uint32_t n
     const int W = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int tid = threadIdx.x, lane = tid & 63;
     const int m = lane & 15, q = lane >> 4;
-    const int32_t XR = a.H * P, BR = a.G * N;
+    const int32_t XR = a.H * P;
+    constexpr int NT = N / 16;
 
     // the block's rows: p = 4M + s0 + s (s < SPB); this wavefront's: s = sb + i
     // (i < SW); its columns: n = 64 (nt / 4) + 4m + nt % 4, nt = nt0 + j (j < TW)
@@ -154,12 +199,14 @@ __global__ __launch_bounds__(256, 2) void state_fwd_kernel(FwdArgs a, uint32_t n
         }
 
     // raw operands of one chunk: x pieces of the slabs this wavefront builds,
-    // B pieces of its columns for every slab, G and dt of token tid and the
-    // chunk's last G.  All are loaded a chunk ahead, unconditionally (a load
-    // under a branch, or one used right after issue, makes the compiler drain
-    // every outstanding load with vmcnt(0) and serializes the chunks).
+    // the B fragments of its columns for every slab (16 bytes a lane each, so
+    // a chunk's loads stay within the 63 a wavefront can have in flight), G
+    // and dt of token tid and the chunk's last G.  All are loaded a chunk
+    // ahead, unconditionally (a load under a branch, or one used right after
+    // issue, makes the compiler drain every outstanding load with vmcnt(0)
+    // and serializes the chunks).
     uint2 xr[SPW][8];
-    uint2 br[NS][8];
+    bf16x8 br[NS][TW];
     float gv = 0.f, dtv = 0.f, glv = 0.f;
     auto nvalid_of = [&](int32_t c) {
         const int64_t rem = a.T - (int64_t)c * L;
@@ -195,16 +242,14 @@ __global__ __launch_bounds__(256, 2) void state_fwd_kernel(FwdArgs a, uint32_t n
         }
     };
     auto load_b = [&](int32_t c, int js) {
-        const int32_t nv = nvalid_of(c);
-        int32_t rs = BR * 2;
-        asm volatile("" : "+s"(rs));
-        const auto rb = make_rsrc(a.B + ((b * a.T + (int64_t)c * L) * a.G + g) * N +
-                                      64 * (nt0 >> 2) + (nt0 & 3),
-                                  (uint32_t)(nv * rs));
-        const uint32_t lo = (uint32_t)(8 * q * rs + 8 * m);
+        const auto rb = make_rsrc(a.BF + (((b * a.nc + c) * a.G + g) * NS) * (NT * 64),
+                                  (uint32_t)(NS * NT * 64 * 16));
 #pragma unroll
-        for (int r = 0; r < 8; ++r)
-            br[js][r] = load_bf<TW>(rb, lo + (uint32_t)((32 * js + r) * rs));
+        for (int j = 0; j < TW; ++j) {
+            const auto v = __builtin_amdgcn_raw_buffer_load_b128(
+                rb, (uint32_t)(16 * lane), (uint32_t)(((js * NT + nt0 + j) * 64) * 16), 0);
+            br[js][j] = __builtin_bit_cast(bf16x8, v);
+        }
     };
 
     if (a.nc > 0) {
@@ -274,19 +319,7 @@ __global__ __launch_bounds__(256, 2) void state_fwd_kernel(FwdArgs a, uint32_t n
         for (int js = 0; js < NS; ++js) {
             bf16x8 bfr[TW];
 #pragma unroll
-            for (int j = 0; j < TW; ++j) {
-                const int sn = (nt0 + j) & 3;    // element of the B piece
-                uint4 v;
-                uint32_t *vw = reinterpret_cast<uint32_t *>(&v);
-#pragma unroll
-                for (int rr = 0; rr < 4; ++rr) {
-                    const int el = (TW == 4) ? sn : j;
-                    const uint32_t a0 = word_of(br[js][2 * rr], el);
-                    const uint32_t a1 = word_of(br[js][2 * rr + 1], el);
-                    vw[rr] = (el & 1) ? pair_hi(a0, a1) : pair_lo(a0, a1);
-                }
-                bfr[j] = as_bf16x8(v);
-            }
+            for (int j = 0; j < TW; ++j) bfr[j] = br[js][j];
             load_b(cn, js);
             // all head products, then all remainder products: no MFMA waits
             // on the one just issued
@@ -356,20 +389,43 @@ bool state_fwd_preferred(const Shape &s) {
 }
 
 bool state_fwd_supported(const Shape &s) {
-    // per-chunk byte offsets of x and B rows are 32-bit
+    // per-chunk byte offsets of x rows are 32-bit
     const int64_t lim = (int64_t(1) << 31) - 1;
-    return s.bf16 && s.P == 64 && s.L * s.H * s.P * 2 <= lim && s.L * s.G * s.N * 2 <= lim;
+    return s.bf16 && s.P == 64 && s.L * s.H * s.P * 2 <= lim &&
+           (uint64_t)s.Bt * s.nc * s.G * (s.L / 32) <= (uint64_t)lim;
+}
+
+size_t state_fwd_bfrag_bytes(const Shape &s) {
+    return (size_t)s.Bt * s.nc * s.G * s.L * s.N * 2;
 }
 
 hipError_t launch_state_fwd(const Shape &s, const void *x, const void *B, const float *Gws,
                             const float *DTws, const float *init, void *hprev, float *fin,
-                            int spb, hipStream_t st) {
+                            void *bfrag, int spb, hipStream_t st) {
     if (!state_fwd_supported(s)) return hipErrorInvalidValue;
     if (s.Bt == 0 || s.H == 0) return hipSuccess;
     if (s.nc == 0 && !fin) return hipSuccess;
+    if (s.nc > 0) {
+        const uint64_t nfb = (uint64_t)s.Bt * s.nc * s.G * (s.L / 32);
+        auto lb = [&](auto kern) {
+            hipLaunchKernelGGL(kern, dim3((uint32_t)nfb), dim3(256), 0, st, (const uint16_t *)B,
+                               (uint4 *)bfrag, s.T, (int32_t)s.G, (int32_t)s.nc);
+        };
+        if (s.N == 64) {
+            if (s.L == 64) lb(b_fragments_kernel<64, 64>);
+            else if (s.L == 128) lb(b_fragments_kernel<128, 64>);
+            else lb(b_fragments_kernel<256, 64>);
+        } else {
+            if (s.L == 64) lb(b_fragments_kernel<64, 128>);
+            else if (s.L == 128) lb(b_fragments_kernel<128, 128>);
+            else lb(b_fragments_kernel<256, 128>);
+        }
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
     FwdArgs a;
     a.x = (const uint16_t *)x;
-    a.B = (const uint16_t *)B;
+    a.BF = (const uint4 *)bfrag;
     a.Gws = Gws;
     a.DTws = DTws;
     a.init = init;
