@@ -30,7 +30,7 @@
 //   4. scale the accumulators by exp2(G_last) and run the MFMAs over the
 //      chunk's 32-token slabs.  B fragments (exact bf16, shared by the heads
 //      of a group and so L2-resident) come straight from global memory into
-//      registers, one chunk ahead, slab by slab: b_fragments_kernel lays B
+//      registers, four slabs ahead: b_fragments_kernel lays B
 //      out in fragment order beforehand (once per (b, chunk, group), in the
 //      workspace region the four-stage form uses for S), so each is one
 //      16-byte load with no transpose.
@@ -205,8 +205,9 @@ __global__ __launch_bounds__(256, 2) void state_fwd_kernel(FwdArgs a, uint32_t n
     // ahead, unconditionally (a load under a branch, or one used right after
     // issue, makes the compiler drain every outstanding load with vmcnt(0)
     // and serializes the chunks).
+    constexpr int R = NS < 4 ? NS : 4;   // B ring depth (slabs in flight)
     uint2 xr[SPW][8];
-    bf16x8 br[NS][TW];
+    bf16x8 br[R][TW];
     float gv = 0.f, dtv = 0.f, glv = 0.f;
     auto nvalid_of = [&](int32_t c) {
         const int64_t rem = a.T - (int64_t)c * L;
@@ -248,14 +249,14 @@ __global__ __launch_bounds__(256, 2) void state_fwd_kernel(FwdArgs a, uint32_t n
         for (int j = 0; j < TW; ++j) {
             const auto v = __builtin_amdgcn_raw_buffer_load_b128(
                 rb, (uint32_t)(16 * lane), (uint32_t)(((js * NT + nt0 + j) * 64) * 16), 0);
-            br[js][j] = __builtin_bit_cast(bf16x8, v);
+            br[js % R][j] = __builtin_bit_cast(bf16x8, v);
         }
     };
 
     if (a.nc > 0) {
         load_x(0);
 #pragma unroll
-        for (int js = 0; js < NS; ++js) load_b(0, js);
+        for (int js = 0; js < R; ++js) load_b(0, js);
     }
     for (int32_t c = 0; c < a.nc; ++c) {
         const int64_t bhc = bhi * a.nc + c;
@@ -315,22 +316,44 @@ __global__ __launch_bounds__(256, 2) void state_fwd_kernel(FwdArgs a, uint32_t n
         for (int i = 0; i < SW; ++i)
 #pragma unroll
             for (int j = 0; j < TW; ++j) acc[i][j] *= dec;
+        // The x*w fragments of a slab are read from LDS one slab ahead of
+        // their MFMAs, and B runs R slabs ahead through the ring (the slabs
+        // after the chunk's last come from chunk cn), so neither an LDS nor a
+        // global load is waited on right after issue.
+        bf16x8 av[2][SW];
+#pragma unroll
+        for (int hl = 0; hl < 2; ++hl)
+#pragma unroll
+            for (int i = 0; i < SW; ++i) av[hl][i] = as_bf16x8(sm.AF[0][hl][sb + i][lane]);
 #pragma unroll
         for (int js = 0; js < NS; ++js) {
             bf16x8 bfr[TW];
 #pragma unroll
-            for (int j = 0; j < TW; ++j) bfr[j] = br[js][j];
-            load_b(cn, js);
+            for (int j = 0; j < TW; ++j) bfr[j] = br[js % R][j];
+            if (js + R < NS) load_b(c, js + R);
+            else load_b(cn, js + R - NS);
+            bf16x8 an[2][SW];
+            if (js + 1 < NS) {
+#pragma unroll
+                for (int hl = 0; hl < 2; ++hl)
+#pragma unroll
+                    for (int i = 0; i < SW; ++i) an[hl][i] = as_bf16x8(sm.AF[js + 1][hl][sb + i][lane]);
+            }
+            __builtin_amdgcn_sched_barrier(0);   // keep those reads a slab ahead
             // all head products, then all remainder products: no MFMA waits
             // on the one just issued
 #pragma unroll
             for (int hl = 0; hl < 2; ++hl)
 #pragma unroll
-                for (int i = 0; i < SW; ++i) {
-                    const bf16x8 av = as_bf16x8(sm.AF[js][hl][sb + i][lane]);
+                for (int i = 0; i < SW; ++i)
 #pragma unroll
-                    for (int j = 0; j < TW; ++j) acc[i][j] = mfma16x16x32(av, bfr[j], acc[i][j]);
-                }
+                    for (int j = 0; j < TW; ++j) acc[i][j] = mfma16x16x32(av[hl][i], bfr[j], acc[i][j]);
+            if (js + 1 < NS) {
+#pragma unroll
+                for (int hl = 0; hl < 2; ++hl)
+#pragma unroll
+                    for (int i = 0; i < SW; ++i) av[hl][i] = an[hl][i];
+            }
         }
     }
     if (a.fin) {
