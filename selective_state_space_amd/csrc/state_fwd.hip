@@ -19,18 +19,22 @@
 // would not fill the chip), all N columns.  The state lives in the MFMA
 // accumulators (v_mfma_f32_16x16x32_bf16, K = tokens) for the block's whole
 // life.  Per chunk:
-//   1. store h_prev[c] (bf16) from the accumulators;
+//   1. store h_prev[c] (bf16) from the accumulators and scale them by
+//      exp2(G_last);
 //   2. w_j = dt_j exp2(G_last - G_j), one token per thread, into LDS;
 //   3. build the x*w operand fragments (x is read along its slow axis: lanes
 //      load SPB-wide row pieces of 8 tokens and pair them up in registers),
 //      carried as a bf16 head plus a bf16 remainder (x*w is not exact in
 //      bf16; one rounding costs up to 2^-9 of every term, too much for a
 //      2e-2 rms bound on the final state where |h| runs far above its rms),
-//      in LDS in fragment order; load the next chunk's x meanwhile;
-//   4. scale the accumulators by exp2(G_last) and run the MFMAs over the
-//      chunk's 32-token slabs.  B fragments (exact bf16, shared by the heads
-//      of a group and so L2-resident) come straight from global memory into
-//      registers, four slabs ahead: b_fragments_kernel lays B
+//      in LDS in fragment order;
+//   4. run the MFMAs over the chunk's 32-token slabs.
+// Steps 3 and 4 are software-pipelined by half chunks: the fragments of the
+// next half are built (VALU) while the current half is multiplied (MFMA),
+// from two LDS buffers, so the two units overlap inside each wavefront.
+// B fragments (exact bf16, shared by the heads of a group and so
+// L2-resident) come straight from global memory into registers, four slabs
+// ahead: b_fragments_kernel lays B
 //      out in fragment order beforehand (once per (b, chunk, group), in the
 //      workspace region the four-stage form uses for S), so each is one
 //      16-byte load with no transpose.
@@ -48,15 +52,17 @@ namespace {
 template <int L, int N, int SPB>
 struct FwdCfg {
     static constexpr int NS = L / 32;                       // 32-token K slabs per chunk
+    static constexpr int HS = NS / 2;                       // slabs per half chunk
     static constexpr int SW = SPB < 2 ? SPB : 2;            // row sets s per wavefront
     static constexpr int TW = SPB * (N / 16) / (4 * SW);    // n-tiles per wavefront
-    static constexpr int SPW = (NS + 3) / 4;                // x*w slabs built per wavefront
 };
 
+// Two half-chunk buffers of x*w fragments (the half being multiplied and the
+// half being built) and the per-token weights of two chunks.
 template <int L, int SPB>
 struct FwdSmem {
-    uint4 AF[L / 32][2][SPB][64];  // slab, head/remainder, row set s, lane
-    float w[L];
+    uint4 AF[2][L / 64][2][SPB][64];  // half, slab of the half, head/remainder, row set s, lane
+    float w[2][L];                    // by chunk parity
 };
 
 struct FwdArgs {
@@ -157,8 +163,10 @@ __global__ __launch_bounds__(256) void b_fragments_kernel(const uint16_t *__rest
 template <int L, int N, int SPB>
 __global__ __launch_bounds__(256, 2) void state_fwd_kernel(FwdArgs a, uint32_t nblk) {
     using Cfg = FwdCfg<L, N, SPB>;
-    constexpr int P = 64, NS = Cfg::NS, SW = Cfg::SW, TW = Cfg::TW, SPW = Cfg::SPW;
+    constexpr int P = 64, NS = Cfg::NS, HS = Cfg::HS, SW = Cfg::SW, TW = Cfg::TW;
     constexpr int PSPLIT = 4 / SPB;
+    constexpr int NT = N / 16;
+    constexpr int R = NS < 4 ? NS : 4;   // B ring depth (slabs in flight)
     __shared__ FwdSmem<L, SPB> sm;
 
     const uint32_t lid = xcd_remap(blockIdx.x, nblk);
@@ -171,7 +179,7 @@ __global__ __launch_bounds__(256, 2) void state_fwd_kernel(FwdArgs a, uint32_t n
     const int tid = threadIdx.x, lane = tid & 63;
     const int m = lane & 15, q = lane >> 4;
     const int32_t XR = a.H * P;
-    constexpr int NT = N / 16;
+    const bool builds = HS == 4 || W < HS;   // this wavefront builds a slab of each half
 
     // the block's rows: p = 4M + s0 + s (s < SPB); this wavefront's: s = sb + i
     // (i < SW); its columns: n = 64 (nt / 4) + 4m + nt % 4, nt = nt0 + j (j < TW)
@@ -197,50 +205,59 @@ __global__ __launch_bounds__(256, 2) void state_fwd_kernel(FwdArgs a, uint32_t n
 #pragma unroll
             for (int j = 0; j < TW; ++j) acc[i][j][e] = v[j];
         }
+    if (a.nc == 0) {
+        if (a.fin) {
+#pragma unroll
+            for (int i = 0; i < SW; ++i)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    float v[TW];
+#pragma unroll
+                    for (int j = 0; j < TW; ++j) v[j] = acc[i][j][e];
+                    store_f<TW>(a.fin + (bhi * P + prow(i, e)) * N + ncol, v);
+                }
+        }
+        return;
+    }
 
-    // raw operands of one chunk: x pieces of the slabs this wavefront builds,
-    // the B fragments of its columns for every slab (16 bytes a lane each, so
-    // a chunk's loads stay within the 63 a wavefront can have in flight), G
-    // and dt of token tid and the chunk's last G.  All are loaded a chunk
-    // ahead, unconditionally (a load under a branch, or one used right after
-    // issue, makes the compiler drain every outstanding load with vmcnt(0)
-    // and serializes the chunks).
-    constexpr int R = NS < 4 ? NS : 4;   // B ring depth (slabs in flight)
-    uint2 xr[SPW][8];
+    // Raw operands, loaded ahead of use and unconditionally (a load under a
+    // branch, or one used right after issue, makes the compiler drain every
+    // outstanding load with vmcnt(0) and serializes the chunks):
+    //   xr[hf]  x pieces of the slab this wavefront builds in half hf, loaded
+    //           two half-steps before that half is built;
+    //   br      B fragments of this wavefront's columns, R slabs ahead (16
+    //           bytes a lane each, from b_fragments_kernel);
+    //   gv, dtv, glv  G and dt of token tid and the last G of the chunk after
+    //           the one being multiplied.
+    uint2 xr[2][8];
     bf16x8 br[R][TW];
     float gv = 0.f, dtv = 0.f, glv = 0.f;
     auto nvalid_of = [&](int32_t c) {
         const int64_t rem = a.T - (int64_t)c * L;
         return rem < L ? (int32_t)rem : L;
     };
-    // Each chunk's rows are read through a buffer resource that spans its
-    // valid tokens only: rows past T (ragged last chunk) come back as 0.
-    // The row offset sits in the VGPR offset (the range check covers it); its
-    // uniform part is formed per load, and the stride goes through an empty
-    // asm per call so that the offsets are not hoisted out of the chunk loop
-    // (80 loop-invariant offsets would not fit in registers).
-    auto load_x = [&](int32_t c) {
+    // Each chunk's x rows are read through a buffer resource that spans its
+    // valid tokens only: rows past T (ragged last chunk) come back as 0.  The
+    // row offset sits in the VGPR offset (the range check covers it); the
+    // stride goes through an empty asm per call so that the offsets are
+    // formed at each load rather than hoisted out of the chunk loop.
+    auto load_x = [&](int32_t c, int hf) {
         const int32_t nv = nvalid_of(c);
         int32_t rs = XR * 2;
         asm volatile("" : "+s"(rs));
         const auto rx = make_rsrc(a.x + ((b * a.T + (int64_t)c * L) * a.H + h) * P + s0,
                                   (uint32_t)(nv * rs));
         const uint32_t lo = (uint32_t)(8 * q * rs + 8 * m);
+        const int js = HS * hf + W;
 #pragma unroll
-        for (int k = 0; k < SPW; ++k) {
-            const int js = W + 4 * k;
-            if (js < NS) {
-#pragma unroll
-                for (int r = 0; r < 8; ++r)
-                    xr[k][r] = load_bf<SPB, kStream>(rx, lo + (uint32_t)((32 * js + r) * rs));
-            }
-        }
-        {
-            const int64_t o = (bhi * a.nc + c) * L;
-            gv = a.Gws[o + min(tid, L - 1)];
-            dtv = a.DTws[o + min(tid, L - 1)];
-            glv = a.Gws[o + L - 1];
-        }
+        for (int r = 0; r < 8; ++r)
+            xr[hf][r] = load_bf<SPB, kStream>(rx, lo + (uint32_t)((32 * js + r) * rs));
+    };
+    auto load_g = [&](int32_t c) {
+        const int64_t o = (bhi * a.nc + c) * L;
+        gv = a.Gws[o + min(tid, L - 1)];
+        dtv = a.DTws[o + min(tid, L - 1)];
+        glv = a.Gws[o + L - 1];
     };
     auto load_b = [&](int32_t c, int js) {
         const auto rb = make_rsrc(a.BF + (((b * a.nc + c) * a.G + g) * NS) * (NT * 64),
@@ -252,16 +269,102 @@ __global__ __launch_bounds__(256, 2) void state_fwd_kernel(FwdArgs a, uint32_t n
             br[js % R][j] = __builtin_bit_cast(bf16x8, v);
         }
     };
-
-    if (a.nc > 0) {
-        load_x(0);
+    // x*w fragments (head + remainder) of row set s of this wavefront's slab
+    // of half hf, with weights w (8 tokens), into AF[hf]
+    auto build_set = [&](int hf, int s, const float *w) {
+        uint4 vh, vl;
+        uint32_t *wh = reinterpret_cast<uint32_t *>(&vh);
+        uint32_t *wl = reinterpret_cast<uint32_t *>(&vl);
 #pragma unroll
-        for (int js = 0; js < R; ++js) load_b(0, js);
-    }
-    for (int32_t c = 0; c < a.nc; ++c) {
-        const int64_t bhc = bhi * a.nc + c;
-        // 1. the state entering chunk c
-        uint16_t *hp = a.hprev + bhc * (int64_t)(P * N) + ncol;
+        for (int rr = 0; rr < 4; ++rr) {
+            const uint32_t a0 = word_of(xr[hf][2 * rr], s);
+            const uint32_t a1 = word_of(xr[hf][2 * rr + 1], s);
+            const float e0 = ((s & 1) ? bf16_hi(a0) : bf16_lo(a0)) * w[2 * rr];
+            const float e1 = ((s & 1) ? bf16_hi(a1) : bf16_lo(a1)) * w[2 * rr + 1];
+            const uint32_t hw = pack_bf16x2(e0, e1);
+            wh[rr] = hw;
+            wl[rr] = pack_bf16x2(e0 - bf16_lo(hw), e1 - bf16_hi(hw));
+        }
+        sm.AF[hf][W][0][s][lane] = vh;
+        sm.AF[hf][W][1][s][lane] = vl;
+    };
+    auto read_w = [&](int hf, int wb, float *w) {
+        const int jw = 32 * (HS * hf + W) + 8 * q;
+        const float4 w0 = *reinterpret_cast<const float4 *>(&sm.w[wb][jw]);
+        const float4 w1 = *reinterpret_cast<const float4 *>(&sm.w[wb][jw + 4]);
+        w[0] = w0.x; w[1] = w0.y; w[2] = w0.z; w[3] = w0.w;
+        w[4] = w1.x; w[5] = w1.y; w[6] = w1.z; w[7] = w1.w;
+    };
+    auto build = [&](int hf, int wb) {
+        float w[8];
+        read_w(hf, wb, w);
+#pragma unroll
+        for (int s = 0; s < SPB; ++s) build_set(hf, s, w);
+    };
+    // h += the products of half hf of chunk c, while (if bh >= 0) the x*w
+    // fragments of half bh are built with the weights of buffer wb, one row
+    // set per slab, interleaved with the MFMAs (VALU and matrix core work
+    // from one wavefront overlap only when their instructions alternate).
+    // The x*w fragments are read one slab ahead; B comes R slabs ahead
+    // through the ring (slabs past the chunk's last come from chunk cn).
+    auto mfma_half = [&](int hf, int32_t c, int32_t cn, int bh, int wb) {
+        float w[8];
+        if (bh >= 0 && builds) read_w(bh, wb, w);
+        bf16x8 av[2][SW];
+#pragma unroll
+        for (int hl = 0; hl < 2; ++hl)
+#pragma unroll
+            for (int i = 0; i < SW; ++i) av[hl][i] = as_bf16x8(sm.AF[hf][0][hl][sb + i][lane]);
+#pragma unroll
+        for (int k = 0; k < HS; ++k) {
+            const int js = HS * hf + k;
+            bf16x8 bfr[TW];
+#pragma unroll
+            for (int j = 0; j < TW; ++j) bfr[j] = br[js % R][j];
+            if (js + R < NS) load_b(c, js + R);
+            else load_b(cn, js + R - NS);
+            bf16x8 an[2][SW];
+            if (k + 1 < HS) {
+#pragma unroll
+                for (int hl = 0; hl < 2; ++hl)
+#pragma unroll
+                    for (int i = 0; i < SW; ++i)
+                        an[hl][i] = as_bf16x8(sm.AF[hf][k + 1][hl][sb + i][lane]);
+            }
+            if (bh >= 0 && builds) {
+#pragma unroll
+                for (int s = 0; s < SPB; ++s)
+                    if (s % HS == k) build_set(bh, s, w);
+            }
+            // all head products, then all remainder products: no MFMA waits
+            // on the one just issued
+#pragma unroll
+            for (int hl = 0; hl < 2; ++hl)
+#pragma unroll
+                for (int i = 0; i < SW; ++i)
+#pragma unroll
+                    for (int j = 0; j < TW; ++j)
+                        acc[i][j] = mfma16x16x32(av[hl][i], bfr[j], acc[i][j]);
+            if (k + 1 < HS) {
+#pragma unroll
+                for (int hl = 0; hl < 2; ++hl)
+#pragma unroll
+                    for (int i = 0; i < SW; ++i) av[hl][i] = an[hl][i];
+            }
+            // schedule: the next slab's LDS reads and the B loads first, then
+            // each MFMA followed by three VALU instructions of the build
+            __builtin_amdgcn_sched_group_barrier(0x100, 2 * SW, 0);   // DS read
+            __builtin_amdgcn_sched_group_barrier(0x020, TW, 0);       // VMEM read
+#pragma unroll
+            for (int u = 0; u < 2 * SW * TW; ++u) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);    // MFMA
+                __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);    // VALU
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+    auto store_hprev = [&](int32_t c) {
+        uint16_t *hp = a.hprev + (bhi * a.nc + c) * (int64_t)(P * N) + ncol;
 #pragma unroll
         for (int i = 0; i < SW; ++i)
 #pragma unroll
@@ -271,90 +374,53 @@ __global__ __launch_bounds__(256, 2) void state_fwd_kernel(FwdArgs a, uint32_t n
                 for (int j = 0; j < TW; ++j) v[j] = acc[i][j][e];
                 store_bf<TW>(hp + prow(i, e) * N, v);
             }
-        // 2. per-token weights
-        const float glast = glv;
-        if (tid < L) sm.w[tid] = dtv * fast_exp2(glast - gv);
-        __syncthreads();   // w visible; every wavefront is done reading AF of chunk c-1
-        // 3. x*w fragments of this wavefront's slabs, head + remainder
+    };
+
+    // Prologue: weights of chunk 0, its first half built, x of its second
+    // half and of chunk 1's first half in flight, G and dt of chunk 1.
+    const int32_t c1 = min(1, a.nc - 1);
+    if (builds) {
+        load_x(0, 0);
+        load_x(0, 1);
+    }
+    load_g(0);
 #pragma unroll
-        for (int k = 0; k < SPW; ++k) {
-            const int js = W + 4 * k;
-            if (js < NS) {
-                const int jw = 32 * js + 8 * q;
-                const float4 w0 = *reinterpret_cast<const float4 *>(&sm.w[jw]);
-                const float4 w1 = *reinterpret_cast<const float4 *>(&sm.w[jw + 4]);
-                const float w[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
-#pragma unroll
-                for (int s = 0; s < SPB; ++s) {
-                    uint4 vh, vl;
-                    uint32_t *wh = reinterpret_cast<uint32_t *>(&vh);
-                    uint32_t *wl = reinterpret_cast<uint32_t *>(&vl);
-#pragma unroll
-                    for (int rr = 0; rr < 4; ++rr) {
-                        const uint32_t a0 = word_of(xr[k][2 * rr], s);
-                        const uint32_t a1 = word_of(xr[k][2 * rr + 1], s);
-                        const float e0 = ((s & 1) ? bf16_hi(a0) : bf16_lo(a0)) * w[2 * rr];
-                        const float e1 = ((s & 1) ? bf16_hi(a1) : bf16_lo(a1)) * w[2 * rr + 1];
-                        const uint32_t hw = pack_bf16x2(e0, e1);
-                        wh[rr] = hw;
-                        wl[rr] = pack_bf16x2(e0 - bf16_lo(hw), e1 - bf16_hi(hw));
-                    }
-                    sm.AF[js][0][s][lane] = vh;
-                    sm.AF[js][1][s][lane] = vl;
-                }
-            }
-        }
-        // the next chunk's operands are loaded unconditionally (the last chunk
-        // reloads itself), so no branch lets the compiler move the loads
+    for (int js = 0; js < R; ++js) load_b(0, js);
+    float glc = glv;                 // last G of the chunk being multiplied
+    if (tid < L) sm.w[0][tid] = dtv * fast_exp2(glc - gv);
+    load_g(c1);
+    __syncthreads();
+    if (builds) {
+        build(0, 0);
+        load_x(c1, 0);
+    }
+
+    // Steps of half a chunk.  In each, every wavefront builds the next half's
+    // x*w fragments into one buffer while it multiplies the current half from
+    // the other (the VALU work of one overlaps the MFMAs of the other), after
+    // one barrier that publishes the half just built and frees the one just
+    // multiplied.
+    for (int32_t c = 0; c < a.nc; ++c) {
         const int32_t cn = min(c + 1, a.nc - 1);
-        load_x(cn);   // in flight during the MFMAs
-        __builtin_amdgcn_sched_barrier(0);
-        __syncthreads();   // AF visible
-        // 4. h <- exp2(G_last) h + (x w)^T B
-        const float dec = fast_exp2(glast);
+        const int32_t cnn = min(c + 2, a.nc - 1);
+        // ---- first half of chunk c (fragments in AF[0]) ----
+        __syncthreads();
+        store_hprev(c);              // the state entering chunk c
+        const float dec = fast_exp2(glc);
 #pragma unroll
         for (int i = 0; i < SW; ++i)
 #pragma unroll
             for (int j = 0; j < TW; ++j) acc[i][j] *= dec;
-        // The x*w fragments of a slab are read from LDS one slab ahead of
-        // their MFMAs, and B runs R slabs ahead through the ring (the slabs
-        // after the chunk's last come from chunk cn), so neither an LDS nor a
-        // global load is waited on right after issue.
-        bf16x8 av[2][SW];
-#pragma unroll
-        for (int hl = 0; hl < 2; ++hl)
-#pragma unroll
-            for (int i = 0; i < SW; ++i) av[hl][i] = as_bf16x8(sm.AF[0][hl][sb + i][lane]);
-#pragma unroll
-        for (int js = 0; js < NS; ++js) {
-            bf16x8 bfr[TW];
-#pragma unroll
-            for (int j = 0; j < TW; ++j) bfr[j] = br[js % R][j];
-            if (js + R < NS) load_b(c, js + R);
-            else load_b(cn, js + R - NS);
-            bf16x8 an[2][SW];
-            if (js + 1 < NS) {
-#pragma unroll
-                for (int hl = 0; hl < 2; ++hl)
-#pragma unroll
-                    for (int i = 0; i < SW; ++i) an[hl][i] = as_bf16x8(sm.AF[js + 1][hl][sb + i][lane]);
-            }
-            __builtin_amdgcn_sched_barrier(0);   // keep those reads a slab ahead
-            // all head products, then all remainder products: no MFMA waits
-            // on the one just issued
-#pragma unroll
-            for (int hl = 0; hl < 2; ++hl)
-#pragma unroll
-                for (int i = 0; i < SW; ++i)
-#pragma unroll
-                    for (int j = 0; j < TW; ++j) acc[i][j] = mfma16x16x32(av[hl][i], bfr[j], acc[i][j]);
-            if (js + 1 < NS) {
-#pragma unroll
-                for (int hl = 0; hl < 2; ++hl)
-#pragma unroll
-                    for (int i = 0; i < SW; ++i) av[hl][i] = an[hl][i];
-            }
-        }
+        const float gln = glv;       // weights of chunk c + 1, then its G and dt in flight
+        if (tid < L) sm.w[(c + 1) & 1][tid] = dtv * fast_exp2(gln - gv);
+        load_g(cnn);
+        mfma_half(0, c, cn, 1, c & 1);   // and build the second half of chunk c
+        if (builds) load_x(cn, 1);
+        // ---- second half of chunk c (fragments in AF[1]) ----
+        __syncthreads();
+        mfma_half(1, c, cn, 0, (c + 1) & 1);   // and build the first half of chunk c + 1
+        if (builds) load_x(cnn, 0);
+        glc = gln;
     }
     if (a.fin) {
 #pragma unroll
