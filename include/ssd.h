@@ -123,12 +123,12 @@ ssd_status ssd_chunked_fwd_workspace_layout(const ssd_dims *dims, int64_t chunk_
  * workspace): chunk_cumsum, chunk_state, state_passing, chunk_scan in this
  * order give y, final_state and every intermediate.  ssd_chunked_fwd runs
  * chunk_cumsum, then either chunk_state and state_passing or the one-pass
- * ssd_state_fwd stage below, then chunk_scan.  It takes the one-pass stage
- * for bf16 io when batch * nheads >= 384 (enough independent chains to fill
- * the GPU while each walks its chunks in order); fp32 io always runs the
- * four stages.  The environment variable SSD_STATE_FWD_ROWS, read at each
- * call, overrides the choice: 0 selects the two stages, 4, 2 or 1 the
- * one-pass stage with that many of the four 16-row sets per workgroup.
+ * ssd_state_fwd stage below, then chunk_scan.  bf16 io takes the one-pass
+ * stage (with all 64 state rows of a head per workgroup when batch * nheads
+ * >= 384, two of the four 16-row sets when >= 48, else one); fp32 io runs
+ * the four stages.  The environment variable SSD_STATE_FWD_ROWS, read at
+ * each call, overrides the choice: 0 selects the two stages, 4, 2 or 1 the
+ * one-pass stage with that many 16-row sets per workgroup.
  *
  * chunk_cumsum: reads dt, A; writes G and DT.  One wavefront-level prefix
  *   sum per (b, h, chunk) ("Accelerating Mamba-2 ...", section "Kernel 1").

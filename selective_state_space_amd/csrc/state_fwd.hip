@@ -463,18 +463,22 @@ hipError_t launch_fwd_l(const Shape &s, const FwdArgs &a, int spb, hipStream_t s
 }  // namespace
 
 int state_fwd_rows_per_block(const Shape &s) {
-    // all 64 rows per workgroup (the x*w operand built once per head and
-    // chunk); the 2- and 1-row-set splits exist for few, long chains
-    (void)s;
-    return 4;
+    // Row sets (of 16 state rows) per workgroup.  All four while Bt*H chains
+    // alone give most of the 512 resident slots (two workgroups per CU);
+    // fewer chains are split over 2 or 4 workgroups each, which also fit
+    // three per CU, so that enough chains run at once.
+    const int64_t bh = s.Bt * s.H;
+    if (bh >= 384) return 4;
+    if (bh >= 48) return 2;
+    return 1;
 }
 
 bool state_fwd_preferred(const Shape &s) {
-    // The chunks of a chain run one after another, so the one-pass form only
-    // pays when Bt*H chains keep the GPU busy (two 4-wavefront workgroups per
-    // CU, 512 on 256 CUs); with fewer chains, or very long ones, the
-    // chunk-parallel chunk_state + state_passing pair is faster.
-    return s.Bt * s.H >= 384;
+    // Measured on MI355X at the 370M, 2.7B and long-context shapes, the
+    // one-pass form beats chunk_state + state_passing at each (it never
+    // writes or reads the fp32 chunk states) once the row split keeps the
+    // chains' sequential chunk steps overlapped.
+    return state_fwd_supported(s);
 }
 
 bool state_fwd_supported(const Shape &s) {

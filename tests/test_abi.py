@@ -145,7 +145,7 @@ def test_path_query(monkeypatch):
     q = lambda d: lib().ssd_chunked_fwd_path(ctypes.byref(d), 256, ctypes.byref(out))
     monkeypatch.delenv("SSD_STATE_FWD_ROWS", raising=False)
     assert q(dims(Bt=8, T=4096, H=80, G=1)) == 0 and out.value == 1      # 640 chains
-    assert q(dims(Bt=4, T=2048, H=32, G=1)) == 0 and out.value == 0      # 128 chains
+    assert q(dims(Bt=4, T=2048, H=32, G=1)) == 0 and out.value == 1      # 128 chains
     assert q(dims(Bt=8, T=4096, H=80, G=1, io=ssd.SSD_F32)) == 0 and out.value == 0
     monkeypatch.setenv("SSD_STATE_FWD_ROWS", "0")
     assert q(dims(Bt=8, T=4096, H=80, G=1)) == 0 and out.value == 0

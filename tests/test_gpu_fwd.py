@@ -233,10 +233,11 @@ def _check_sampled(w, inp, y, fin, npairs=12):
     assert_close(fg, fr, w.io_dtype, "%s final" % w.name)
 
 
-@pytest.mark.parametrize("idx,rows", [(1, ""), (2, ""), (2, "0"), (3, "")])
+@pytest.mark.parametrize("idx,rows", [(1, ""), (1, "0"), (2, ""), (2, "0"), (3, "")])
 def test_full_size_workload(idx, rows, monkeypatch):
-    # rows "" = the path the shape selects (two-stage state for 1 and 3,
-    # one-pass for 2); "0" = the two-stage state path for 2 as well
+    # rows "" = the path the shape selects (the one-pass state stage, with
+    # two row sets per workgroup for 1 and 3 and all four for 2); "0" = the
+    # two-stage state path
     monkeypatch.setenv("SSD_STATE_FWD_ROWS", rows)
     w = gen.WORKLOADS[idx]
     log("workload", w.name, w.description, "rows", rows or "auto")
