@@ -70,11 +70,16 @@ def algorithmic(w, io_bytes: int):
         flops=2 * units * P * N)
     tri = L * (L + 1) // 2
     tok_y = Bt * T * H * P * 4           # y is written fp32
-    # one pass: x, B, G and DT in, h_prev out, init/final state; S never exists
-    out["state_fwd"] = dict(
+    # one pass: x, B (as MFMA fragments), G and DT in, h_prev out, init/final
+    # state; S never exists.  The stage also runs b_fragments (B re-laid out:
+    # read once, written once), counted in the stage's bytes.
+    out["b_fragments"] = dict(bytes=2 * tok_bc, flops=0)
+    out["state_fwd_kernel"] = dict(
         bytes=tok_x + tok_bc + gdt + units * P * N * io_bytes
         + (state if w.init_state else 0) + state,
         flops=2 * P * N * L * units + 2 * units * P * N)
+    out["state_fwd"] = dict(bytes=out["state_fwd_kernel"]["bytes"] + out["b_fragments"]["bytes"],
+                            flops=out["state_fwd_kernel"]["flops"])
     out["chunk_scan"] = dict(
         bytes=tok_x + tok_y + 2 * tok_bc + units * P * N * io_bytes + gdt,
         flops=units * (2 * L * P * N + 2 * tri * P) + (Bt * G * nc) * 2 * tri * N)

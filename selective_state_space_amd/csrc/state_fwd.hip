@@ -241,8 +241,13 @@ __global__ __launch_bounds__(256, 2) void state_fwd_kernel(FwdArgs a, uint32_t n
     // row offset sits in the VGPR offset (the range check covers it); the
     // stride goes through an empty asm per call so that the offsets are
     // formed at each load rather than hoisted out of the chunk loop.
+    // A chunk index past the last gives a resource of zero range: the loads
+    // return zeros without touching memory (the pipeline's look-ahead past
+    // the end costs no traffic and needs no branch).
     auto load_x = [&](int32_t c, int hf) {
-        const int32_t nv = nvalid_of(c);
+        const bool real = c < a.nc;
+        if (!real) c = a.nc - 1;
+        const int32_t nv = real ? nvalid_of(c) : 0;
         int32_t rs = XR * 2;
         asm volatile("" : "+s"(rs));
         const auto rx = make_rsrc(a.x + ((b * a.T + (int64_t)c * L) * a.H + h) * P + s0,
@@ -253,15 +258,17 @@ __global__ __launch_bounds__(256, 2) void state_fwd_kernel(FwdArgs a, uint32_t n
         for (int r = 0; r < 8; ++r)
             xr[hf][r] = load_bf<SPB, kStream>(rx, lo + (uint32_t)((32 * js + r) * rs));
     };
-    auto load_g = [&](int32_t c) {
-        const int64_t o = (bhi * a.nc + c) * L;
+    auto load_g = [&](int32_t c) {   // plain loads: the index is clamped
+        const int64_t o = (bhi * a.nc + min(c, a.nc - 1)) * L;
         gv = a.Gws[o + min(tid, L - 1)];
         dtv = a.DTws[o + min(tid, L - 1)];
         glv = a.Gws[o + L - 1];
     };
     auto load_b = [&](int32_t c, int js) {
+        const bool real = c < a.nc;
+        if (!real) c = a.nc - 1;
         const auto rb = make_rsrc(a.BF + (((b * a.nc + c) * a.G + g) * NS) * (NT * 64),
-                                  (uint32_t)(NS * NT * 64 * 16));
+                                  real ? (uint32_t)(NS * NT * 64 * 16) : 0u);
 #pragma unroll
         for (int j = 0; j < TW; ++j) {
             const auto v = __builtin_amdgcn_raw_buffer_load_b128(
@@ -378,7 +385,7 @@ __global__ __launch_bounds__(256, 2) void state_fwd_kernel(FwdArgs a, uint32_t n
 
     // Prologue: weights of chunk 0, its first half built, x of its second
     // half and of chunk 1's first half in flight, G and dt of chunk 1.
-    const int32_t c1 = min(1, a.nc - 1);
+    const int32_t c1 = 1;
     if (builds) {
         load_x(0, 0);
         load_x(0, 1);
@@ -401,8 +408,7 @@ __global__ __launch_bounds__(256, 2) void state_fwd_kernel(FwdArgs a, uint32_t n
     // one barrier that publishes the half just built and frees the one just
     // multiplied.
     for (int32_t c = 0; c < a.nc; ++c) {
-        const int32_t cn = min(c + 1, a.nc - 1);
-        const int32_t cnn = min(c + 2, a.nc - 1);
+        const int32_t cn = c + 1, cnn = c + 2;   // may run past the end (zero-range loads)
         // ---- first half of chunk c (fragments in AF[0]) ----
         __syncthreads();
         store_hprev(c);              // the state entering chunk c
