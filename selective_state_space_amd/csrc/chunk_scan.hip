@@ -495,11 +495,13 @@ __global__ __launch_bounds__(256) void chunk_scan_f32_kernel(
 }
 
 // Heads per workgroup: enough heads share one set of C B^T tiles to amortise
-// them, while the grid keeps about 512 workgroups (two per CU) in flight.
+// them, while the grid is one round of resident workgroups: about 256 (one
+// per CU) at L = 256, whose 128 KB of LDS allows one per CU, else 512.
 inline int32_t heads_per_block(const Shape &s) {
     const int64_t hpg = s.H / s.G;
     const int64_t groups = s.Bt * s.nc * s.G;
-    int64_t nh = (groups * hpg + 511) / 512;
+    const int64_t slots = s.L == 256 ? 256 : 512;
+    int64_t nh = (groups * hpg + slots - 1) / slots;
     if (nh < 1) nh = 1;
     if (nh > hpg) nh = hpg;
     return (int32_t)nh;
