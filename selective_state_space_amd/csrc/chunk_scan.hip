@@ -111,7 +111,7 @@ struct HeadRegs {
     static constexpr int HPL = (NK * 4 + NW - 1) / NW;
     uint2 xr[XSW][8];
     uint4 hv[HPL];
-    float g, gl, dt;
+    float g, gl, dt, dh;   // G, G at the end of the token's 16-block, dt; D of the head
 };
 
 template <int L, int N, bool RAGGED>
@@ -142,12 +142,15 @@ __device__ __forceinline__ void head_load(HeadRegs<L, N> &r, const ScanArgs<L, N
                       ? *reinterpret_cast<const uint4 *>(hp + (4 * m + s) * N + 32 * kn + 8 * q)
                       : make_uint4(0u, 0u, 0u, 0u);
     }
-    if (tid < L) {
-        const float *Gp = a.Gws + bhc * L;
-        r.g = Gp[tid];
-        r.gl = Gp[tid | 15];
-        r.dt = a.DTws[bhc * L + tid];
-    }
+    // Unconditional (threads past L load token L-1 again): a load under a
+    // branch, or one used right after issue, makes the compiler wait with
+    // vmcnt(0), which would drain this prefetch as well.
+    const int tk = tid < L ? tid : L - 1;
+    const float *Gp = a.Gws + bhc * L;
+    r.g = Gp[tk];
+    r.gl = Gp[tk | 15];
+    r.dt = a.DTws[bhc * L + tk];
+    r.dh = a.D[h];
 }
 
 template <int L, int N>
@@ -244,12 +247,17 @@ __device__ __forceinline__ void chunk_scan_group(ScanSmem<L, N> &sm, const ScanA
     }
     __syncthreads();   // BF is dead; the head buffer takes its place
     head_store<L, N>(sm.hd, pre, W, lane);
+    float dh = pre.dh;   // D of the head being computed (pre is refilled ahead)
     __syncthreads();
 
     for (int hh = 0; hh < nh; ++hh) {
         const int h = h0 + hh;
         auto &hd = sm.hd;
-        if (hh + 1 < nh) head_load<L, N, RAGGED>(pre, a, b, h + 1, c, nvalid, W, lane);
+        // the next head's operands, unconditionally (the last head reloads
+        // itself) and pinned here: under a branch the compiler sinks these
+        // loads down to their use and nothing is left in flight
+        head_load<L, N, RAGGED>(pre, a, b, min(h + 1, h0 + nh - 1), c, nvalid, W, lane);
+        __builtin_amdgcn_sched_barrier(0);
 
         // ---- inter: acc = C h_prev^T, rows scaled by exp2(G_i) ----
         // acc[k][s][e] = y[i = 16 I_k + 4q + e][p = 4m + s]
@@ -338,7 +346,7 @@ __device__ __forceinline__ void chunk_scan_group(ScanSmem<L, N> &sm, const ScanA
 
         __builtin_amdgcn_sched_barrier(0);
         // ---- y = acc + D x (x from this lane's own fragments), fp32 ----
-        const float Dh = a.D[h];
+        const float Dh = dh;
         float *yb = a.y + ((b * a.T + t0) * a.H + h) * P;
         const int32_t XR = a.H * P;
 #pragma unroll
@@ -371,6 +379,7 @@ __device__ __forceinline__ void chunk_scan_group(ScanSmem<L, N> &sm, const ScanA
         if (hh + 1 < nh) {
             __syncthreads();   // every wavefront is done with this head's buffer
             head_store<L, N>(sm.hd, pre, W, lane);
+            dh = pre.dh;
             __syncthreads();
         }
     }
