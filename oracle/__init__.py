@@ -74,6 +74,12 @@ def _load():
         lib.ssd_oracle_decode.argtypes = [dp, fp, fp, fp, fp, fp, fp, i64, i64, i64, i64, i64,
                                           dp, i64, dp, ip]
         lib.ssd_oracle_decode.restype = ctypes.c_int
+        lib.ssd_oracle_fwd_gated.argtypes = [fp, fp, fp, fp, fp, fp, fp, ip, fp, dp, i64, i64,
+                                             i64, i64, i64, i64, dp, i64, dp, dp, ip]
+        lib.ssd_oracle_fwd_gated.restype = ctypes.c_int
+        lib.ssd_oracle_decode_gated.argtypes = [dp, fp, fp, fp, fp, fp, fp, fp, ip, fp, i64, i64,
+                                                i64, i64, i64, dp, i64, dp, ip]
+        lib.ssd_oracle_decode_gated.restype = ctypes.c_int
         lib.ssd_oracle_host_threads.argtypes = []
         lib.ssd_oracle_host_threads.restype = ctypes.c_int
         _lib = lib
@@ -94,7 +100,8 @@ def _ptr(a):
 
 
 def token_fwd(x, dt, A, B, C, D, init_state=None, pairs: Optional[Sequence[int]] = None,
-              want_y: bool = True, nthreads: int = 0):
+              want_y: bool = True, nthreads: int = 0, dt_bias=None, dt_softplus: bool = False,
+              z=None):
     """Token-by-token float64 forward.
 
     x [Bt,T,H,P], dt [Bt,T,H], A [H], B/C [Bt,T,G,N], D [H], init_state
@@ -102,6 +109,11 @@ def token_fwd(x, dt, A, B, C, D, init_state=None, pairs: Optional[Sequence[int]]
     (None = all, in order).  Returns (y [npairs,T,P] or None, final
     [npairs,P,N], threads_used).  With pairs=None the results reshape to
     [Bt,H,T,P] and [Bt,H,P,N].
+
+    The optional layer interface ("Optimizing Nemotron v3 Super in
+    TensorRT-LLM", sections 6.1 and 6.3): ``dt_bias`` [H] is added to dt, then
+    ``dt_softplus`` applies log(1 + e^dt) where dt <= 20; ``z`` [Bt,T,H,P]
+    gates the output, y * silu(z), after the D term.
     """
     x, dt, A, B, C, D = map(_f32, (x, dt, A, B, C, D))
     Bt, T, H, P = x.shape
@@ -116,19 +128,25 @@ def token_fwd(x, dt, A, B, C, D, init_state=None, pairs: Optional[Sequence[int]]
         init = np.ascontiguousarray(init if pr is None else init[pr])
     y = np.empty((npairs, T, P), np.float64) if want_y else None
     fin = np.empty((npairs, P, N), np.float64)
-    rc = _load().ssd_oracle_fwd(_ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
-                                _ptr(init), Bt, T, H, P, N, G, _ptr(pr), npairs, _ptr(y),
-                                _ptr(fin), nthreads)
+    bias = None if dt_bias is None else _f32(dt_bias)
+    zz = None if z is None else _f32(z)
+    assert bias is None or bias.shape == (H,)
+    assert zz is None or zz.shape == x.shape
+    rc = _load().ssd_oracle_fwd_gated(_ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
+                                      _ptr(bias), int(bool(dt_softplus)), _ptr(zz), _ptr(init),
+                                      Bt, T, H, P, N, G, _ptr(pr), npairs, _ptr(y), _ptr(fin),
+                                      nthreads)
     if rc < 0:
         raise ValueError("ssd_oracle_fwd rejected its arguments (%d)" % rc)
     return y, fin, rc
 
 
 def token_decode(state, x_t, dt_t, B_t, C_t, A, D, pairs: Optional[Sequence[int]] = None,
-                 nthreads: int = 0):
+                 nthreads: int = 0, dt_bias=None, dt_softplus: bool = False, z_t=None):
     """One float64 decode step, updating ``state`` [npairs,P,N] (float64) in place.
 
     x_t [Bt,H,P], dt_t [Bt,H], B_t/C_t [Bt,G,N].  Returns y_t [npairs,P].
+    dt_bias, dt_softplus and the gate z_t [Bt,H,P] as in token_fwd.
     """
     x_t, dt_t, B_t, C_t, A, D = map(_f32, (x_t, dt_t, B_t, C_t, A, D))
     Bt, H, P = x_t.shape
@@ -138,9 +156,13 @@ def token_decode(state, x_t, dt_t, B_t, C_t, A, D, pairs: Optional[Sequence[int]
     npairs = Bt * H if pr is None else len(pr)
     assert state.shape == (npairs, P, N)
     y = np.empty((npairs, P), np.float64)
-    rc = _load().ssd_oracle_decode(_ptr(state), _ptr(x_t), _ptr(dt_t), _ptr(B_t), _ptr(C_t),
-                                   _ptr(A), _ptr(D), Bt, H, P, N, G, _ptr(pr), npairs, _ptr(y),
-                                   nthreads)
+    bias = None if dt_bias is None else _f32(dt_bias)
+    zz = None if z_t is None else _f32(z_t)
+    assert zz is None or zz.shape == x_t.shape
+    rc = _load().ssd_oracle_decode_gated(_ptr(state), _ptr(x_t), _ptr(dt_t), _ptr(B_t),
+                                         _ptr(C_t), _ptr(A), _ptr(D), _ptr(bias),
+                                         int(bool(dt_softplus)), _ptr(zz), Bt, H, P, N, G,
+                                         _ptr(pr), npairs, _ptr(y), nthreads)
     if rc < 0:
         raise ValueError("ssd_oracle_decode rejected its arguments (%d)" % rc)
     return y

@@ -15,7 +15,12 @@
  *     y_t = h_t C_t + D_h * x_t                                      (P)
  *
  * The output uses the updated state h_t (the diagonal of the causal mask is
- * included).  Head h reads B and C of group h / (H / G).  The state of head h
+ * included).  Optionally (the layer interface around the scan, "Optimizing
+ * Nemotron v3 Super in TensorRT-LLM", sections 6.1 and 6.3): the step is
+ * preprocessed per token, dt <- dt + dt_bias_h and then, if requested,
+ * dt <- softplus(dt) = log(1 + e^dt) for dt <= 20 (left as is above 20); and
+ * the output is gated, y_t <- y_t * silu(z_t) with silu(z) = z / (1 + e^-z),
+ * after the D term.  The gate does not touch the state.  Head h reads B and C of group h / (H / G).  The state of head h
  * is stored [P][N] (N contiguous).  The chunked SSD form the GPU path uses is
  * an algebraic rearrangement of exactly this recurrence, so the recurrence is
  * the reference.
@@ -38,6 +43,9 @@
 
 typedef struct {
     const float *x, *dt, *A, *B, *C, *D;
+    const float *dt_bias;   /* [H] or NULL */
+    int softplus;           /* nonzero: softplus on dt (+ bias), identity above 20 */
+    const float *z;         /* [Bt,T,H,P] gate or NULL */
     const double *init;     /* [npairs][P][N] or NULL */
     double *y;              /* [npairs][T][P] or NULL */
     double *fin;            /* [npairs][P][N] or NULL */
@@ -64,7 +72,9 @@ static void run_row(const fwd_job *j, int64_t unit, double *s)
 
     for (int64_t t = 0; t < T; ++t) {
         const int64_t bt = b * T + t;
-        const double dt = (double)j->dt[bt * H + h];
+        double dt = (double)j->dt[bt * H + h];
+        if (j->dt_bias) dt += (double)j->dt_bias[h];
+        if (j->softplus && dt <= 20.0) dt = log1p(exp(dt));
         const double xv = (double)j->x[(bt * H + h) * P + p];
         const float *Bv = j->B + (bt * G + g) * N;
         const float *Cv = j->C + (bt * G + g) * N;
@@ -76,7 +86,12 @@ static void run_row(const fwd_job *j, int64_t unit, double *s)
             s[n] = v;
             acc += (double)Cv[n] * v;
         }
-        if (j->y) j->y[(pi * T + t) * P + p] = acc + D * xv;
+        double yv = acc + D * xv;
+        if (j->z) {
+            const double zv = (double)j->z[(bt * H + h) * P + p];
+            yv *= zv / (1.0 + exp(-zv));
+        }
+        if (j->y) j->y[(pi * T + t) * P + p] = yv;
     }
     if (j->fin)
         for (int64_t n = 0; n < N; ++n) j->fin[(pi * P + p) * N + n] = s[n];
@@ -113,14 +128,15 @@ int ssd_oracle_host_threads(void)
  * NULL = all Bt*H pairs in order).  x [Bt,T,H,P], dt [Bt,T,H], A [H],
  * B and C [Bt,T,G,N], D [H]; init [npairs,P,N] (NULL = zeros); outputs
  * y [npairs,T,P] and fin [npairs,P,N] (either may be NULL).  init may alias
- * fin.  Returns the number of threads used, or a negative value on a bad
- * argument.
+ * fin.  dt_bias [H] (NULL = none), softplus (0/1) and the gate z [Bt,T,H,P]
+ * (NULL = none) are the optional layer interface described above.  Returns
+ * the number of threads used, or a negative value on a bad argument.
  */
-int ssd_oracle_fwd(const float *x, const float *dt, const float *A, const float *B,
-                   const float *C, const float *D, const double *init,
-                   int64_t Bt, int64_t T, int64_t H, int64_t P, int64_t N, int64_t G,
-                   const int64_t *pairs, int64_t npairs, double *y, double *fin,
-                   int nthreads)
+int ssd_oracle_fwd_gated(const float *x, const float *dt, const float *A, const float *B,
+                         const float *C, const float *D, const float *dt_bias, int softplus,
+                         const float *z, const double *init, int64_t Bt, int64_t T, int64_t H,
+                         int64_t P, int64_t N, int64_t G, const int64_t *pairs, int64_t npairs,
+                         double *y, double *fin, int nthreads)
 {
     if (!x || !dt || !A || !B || !C || !D) return -1;
     if (Bt < 1 || T < 0 || H < 1 || P < 1 || N < 1 || G < 1 || H % G) return -2;
@@ -128,8 +144,8 @@ int ssd_oracle_fwd(const float *x, const float *dt, const float *A, const float 
     for (int64_t i = 0; pairs && i < npairs; ++i)
         if (pairs[i] < 0 || pairs[i] >= Bt * H) return -3;
 
-    fwd_job j = {x, dt, A, B, C, D, init, y, fin, Bt, T, H, P, N, G, pairs, npairs,
-                 npairs * P, 0};
+    fwd_job j = {x, dt, A, B, C, D, dt_bias, softplus, z, init, y, fin, Bt, T, H, P, N, G,
+                 pairs, npairs, npairs * P, 0};
     if (nthreads <= 0) nthreads = ssd_oracle_host_threads();
     if (nthreads > j.nunits) nthreads = (int)(j.nunits > 0 ? j.nunits : 1);
 
@@ -146,6 +162,17 @@ int ssd_oracle_fwd(const float *x, const float *dt, const float *A, const float 
     return started + 1;
 }
 
+/* The plain recurrence: no dt preprocessing, no gate. */
+int ssd_oracle_fwd(const float *x, const float *dt, const float *A, const float *B,
+                   const float *C, const float *D, const double *init,
+                   int64_t Bt, int64_t T, int64_t H, int64_t P, int64_t N, int64_t G,
+                   const int64_t *pairs, int64_t npairs, double *y, double *fin,
+                   int nthreads)
+{
+    return ssd_oracle_fwd_gated(x, dt, A, B, C, D, NULL, 0, NULL, init, Bt, T, H, P, N, G,
+                                pairs, npairs, y, fin, nthreads);
+}
+
 /*
  * One recurrent decode step ("Optimizing Nemotron v3 Super in TensorRT-LLM",
  * section 6.1): the forward body for a single token, with the state read from
@@ -160,4 +187,16 @@ int ssd_oracle_decode(double *state, const float *x_t, const float *dt_t, const 
     if (!state) return -1;
     return ssd_oracle_fwd(x_t, dt_t, A, B_t, C_t, D, state, Bt, 1, H, P, N, G, pairs, npairs,
                           y_t, state, nthreads);
+}
+
+/* The decode step with the optional dt preprocessing and gate z_t [Bt,H,P]. */
+int ssd_oracle_decode_gated(double *state, const float *x_t, const float *dt_t,
+                            const float *B_t, const float *C_t, const float *A, const float *D,
+                            const float *dt_bias, int softplus, const float *z_t, int64_t Bt,
+                            int64_t H, int64_t P, int64_t N, int64_t G, const int64_t *pairs,
+                            int64_t npairs, double *y_t, int nthreads)
+{
+    if (!state) return -1;
+    return ssd_oracle_fwd_gated(x_t, dt_t, A, B_t, C_t, D, dt_bias, softplus, z_t, state, Bt, 1,
+                                H, P, N, G, pairs, npairs, y_t, state, nthreads);
 }
