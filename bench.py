@@ -214,6 +214,64 @@ def run_decode(w, steps: int, warmup: int):
     return float(np.median(t)), float(np.mean(t))
 
 
+def run_layer_interface(w, wd, steps: int, warmup: int):
+    """The forward and decode step with every layer option on (dt_bias,
+    softplus, the z gate).  The raw steps are the inverse softplus of the
+    workload's dt with a zero bias, so the recurrence sees the same steps as
+    the plain run; z is standard normal in x's dtype."""
+    import torch
+    from selective_state_space_amd import inputs as gen
+    from selective_state_space_amd import ssd
+
+    dev = torch.device("cuda:0")
+
+    def up(a, dt=torch.float32):
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dt).to(dev)
+
+    def inv_softplus(d):
+        d = np.asarray(d, np.float64)
+        return np.log(np.expm1(d)).astype(np.float32)
+
+    def timed(fn, n, k0):
+        for _ in range(k0):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(n):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
+
+    bf = torch.bfloat16 if w.io_dtype == gen.BF16 else torch.float32
+    inp = gen.make_fwd(w, 0)
+    rng = np.random.default_rng(3)
+    z = up(rng.standard_normal(inp.x.shape, dtype=np.float32), bf)
+    a = ssd.FwdArgs(up(inp.x, bf), up(inv_softplus(inp.dt)), up(inp.A), up(inp.B, bf),
+                    up(inp.C, bf), up(inp.D), w.chunk_size,
+                    None if inp.init_state is None else up(inp.init_state),
+                    dt_bias=torch.zeros(w.nheads, device=dev), dt_softplus=True, z=z)
+    del inp
+    fwd_ms = timed(lambda: ssd.ssd_chunked_fwd(a), steps, warmup)
+    del a, z
+    torch.cuda.empty_cache()
+
+    prm = gen.decode_params(wd, 0)
+    s = gen.make_decode_step(wd, 0, prm, 0)
+    state = torch.zeros((wd.batch, wd.nheads, wd.headdim, wd.dstate), device=dev)
+    y = torch.empty((wd.batch, wd.nheads, wd.headdim), dtype=torch.float32, device=dev)
+    zt = up(rng.standard_normal(s.x_t.shape, dtype=np.float32), torch.bfloat16)
+    args = (up(s.x_t, torch.bfloat16), up(inv_softplus(s.dt_t)), up(s.B_t, torch.bfloat16),
+            up(s.C_t, torch.bfloat16), up(prm.A), up(prm.D))
+    bias = torch.zeros(wd.nheads, device=dev)
+    dec_ms = timed(lambda: ssd.ssd_decode_step(state, *args, y_t=y, dt_bias=bias,
+                                               dt_softplus=True, z_t=zt), 50, 5)
+    del state
+    torch.cuda.empty_cache()
+    return fwd_ms, dec_ms
+
+
 def run_copy_reference(nbytes: int = 1 << 30, reps: int = 10):
     """HBM bandwidth of torch's device copy (read + write), for context."""
     import torch
@@ -344,6 +402,18 @@ def main():
                       tokens_per_s=round(wd.batch / (med * 1e-3), 1),
                       alg_bytes_per_step=int(byt), steps_timed=args.decode_steps)
         log("decode: %.1f us/step, %.0f GB/s" % (med * 1e3, decode["GBps"]))
+    layer = None
+    if not args.no_decode:
+        wd = gen.WORKLOADS[4]
+        fms, dms_ = run_layer_interface(w, wd, max(10, args.steps // 2), 10)
+        zb = w.batch * w.seqlen * w.nheads * w.headdim * io_bytes
+        layer = dict(options="dt_bias + softplus + z gate",
+                     forward_us=round(fms * 1e3, 2), forward_tokens_per_s=round(tokens / (fms * 1e-3), 1),
+                     forward_over_plain=round(fms / step_ms, 4), z_bytes=int(zb),
+                     decode_workload=wd.name, decode_us_per_step=round(dms_ * 1e3, 2),
+                     decode_over_plain=(round(dms_ / med, 4) if decode else None))
+        log("layer interface: forward %.1f us (%.3fx plain), decode %.1f us/step"
+            % (fms * 1e3, fms / step_ms, dms_ * 1e3))
     copy_gbps = run_copy_reference()
     log("device copy reference: %.0f GB/s" % copy_gbps)
 
@@ -384,6 +454,7 @@ def main():
                                               / BF16_PEAK_TFLOPS, 4),
         "kernels": kernels,
         "decode": decode,
+        "layer_interface": layer,
         "hbm_copy_reference_GBps": round(copy_gbps, 1),
         "wall_s_timed": round(wall, 4),
         "git": sha,

@@ -178,6 +178,35 @@ ssd_status ssd_state_fwd(const void *x, const void *B, const float *init_state,
 ssd_status ssd_chunked_fwd_path(const ssd_dims *dims, int64_t chunk_size, int *uses_state_fwd);
 
 /*
+ * The layer interface around the scan ("Optimizing Nemotron v3 Super in
+ * TensorRT-LLM", section 6.1 "The SSU Math" and section 6.3): optional
+ * preprocessing of the step and an optional output gate.  Pass NULL for
+ * none of them (the plain ssd_chunked_fwd / ssd_decode_step).
+ *   dt_bias      float32 [H], added to dt before anything else; NULL = none.
+ *   dt_softplus  nonzero: dt <- log(1 + e^dt) where dt <= 20, unchanged
+ *                above 20 (after the bias).  Tokens past T stay at dt = 0.
+ *   reserved     must be 0 (else SSD_ERR_UNSUPPORTED).
+ *   z            gate in x's dtype and layout ([Bt, T, H, P] for the
+ *                forward, [Bt, H, P] for decode): y <- y * silu(z) with
+ *                silu(z) = z / (1 + e^-z), after the D term.  The state and
+ *                final_state are not gated.  NULL = no gate.
+ * Pointers are caller-owned device memory, 16-byte aligned (SSD_ERR_ALIGN).
+ */
+typedef struct {
+    const float *dt_bias;
+    int32_t dt_softplus;
+    int32_t reserved;
+    const void *z;
+} ssd_layer_opts;
+
+/* ssd_chunked_fwd with the options above (opts may be NULL). */
+ssd_status ssd_chunked_fwd_opts(const void *x, const float *dt, const float *A, const void *B,
+                                const void *C, const float *D, int64_t chunk_size,
+                                const float *init_state, void *y, float *final_state,
+                                const ssd_layer_opts *opts, const ssd_dims *dims,
+                                void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * One recurrent decode step ("Optimizing Nemotron v3 Super in TensorRT-LLM",
  * section 6.1; "mamba-metal: running Mamba on Apple Silicon", section on
  * O(L) incremental decoding): for every (b, h),
@@ -194,6 +223,12 @@ ssd_status ssd_chunked_fwd_path(const ssd_dims *dims, int64_t chunk_size, int *u
 ssd_status ssd_decode_step(float *state, const void *x_t, const float *dt_t, const void *B_t,
                            const void *C_t, const float *A, const float *D, void *y_t,
                            const ssd_dims *dims, void *stream);
+
+/* ssd_decode_step with the options above (opts may be NULL; z is [Bt, H, P]). */
+ssd_status ssd_decode_step_opts(float *state, const void *x_t, const float *dt_t,
+                                const void *B_t, const void *C_t, const float *A, const float *D,
+                                void *y_t, const ssd_layer_opts *opts, const ssd_dims *dims,
+                                void *stream);
 
 /* Static text for a status code. */
 const char *ssd_status_string(ssd_status status);

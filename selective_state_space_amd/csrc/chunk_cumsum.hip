@@ -12,6 +12,11 @@
 // float32 [Bt, H, nc, L] (tokens contiguous).  Positions past T get dt = 0,
 // so a ragged last chunk carries its last valid G to the end of the chunk.
 //
+// Optionally the step is preprocessed first, as the layer interface of
+// "Optimizing Nemotron v3 Super in TensorRT-LLM" (sections 6.1, 6.3) does:
+// dt <- dt + dt_bias_h, then dt <- log(1 + e^dt) where dt <= 20.  DT then
+// holds the effective step, so the later stages need no change.
+//
 // One workgroup of 256 threads per (b, chunk, block of 32 heads).  dt rows of
 // 32 heads (128 bytes) are read with 16-byte loads, transposed through LDS, and
 // each wavefront then scans 8 heads: a lane sums L/64 tokens serially, a wave-wide
@@ -30,7 +35,8 @@ constexpr int kHeadsPerBlock = 32;
 template <int L>
 __global__ __launch_bounds__(256) void chunk_cumsum_kernel(
     const float *__restrict__ dt, const float *__restrict__ A, float *__restrict__ Gws,
-    float *__restrict__ DTws, int64_t T, int32_t H, int32_t nc, int32_t nhb, uint32_t nblk) {
+    float *__restrict__ DTws, const float *__restrict__ dt_bias, int32_t softplus, int64_t T,
+    int32_t H, int32_t nc, int32_t nhb, uint32_t nblk) {
     constexpr int V = L / 64;  // tokens per lane
     __shared__ float tile[kHeadsPerBlock][L + 1];
 
@@ -76,11 +82,18 @@ __global__ __launch_bounds__(256) void chunk_cumsum_kernel(
         const int h = h0 + hh;
         if (h >= H) break;  // wave-uniform
         const float a2 = A[h] * kLog2e;
+        const float bias = dt_bias ? dt_bias[h] : 0.f;
         float d[V], g[V];
         float run = 0.f;
 #pragma unroll
         for (int v = 0; v < V; ++v) {
             d[v] = tile[hh][lane * V + v];
+            if (dt_bias || softplus) {   // kernel-uniform
+                const bool real = (int64_t)c * L + lane * V + v < T;   // padding stays 0
+                float e = d[v] + bias;
+                if (softplus && e <= 20.f) e = log1pf(expf(e));
+                d[v] = real ? e : 0.f;
+            }
             run += a2 * d[v];
             g[v] = run;
         }
@@ -110,23 +123,26 @@ __global__ __launch_bounds__(256) void chunk_cumsum_kernel(
 }  // namespace
 
 hipError_t launch_chunk_cumsum(const Shape &s, const float *dt, const float *A, float *Gws,
-                               float *DTws, hipStream_t st) {
+                               float *DTws, const float *dt_bias, int softplus, hipStream_t st) {
     if (s.Bt == 0 || s.nc == 0) return hipSuccess;
     const int32_t nhb = (int32_t)((s.H + kHeadsPerBlock - 1) / kHeadsPerBlock);
     const uint64_t nblk = (uint64_t)s.Bt * s.nc * nhb;
     const dim3 grid((uint32_t)nblk), block(256);
     switch (s.L) {
     case 64:
-        hipLaunchKernelGGL(chunk_cumsum_kernel<64>, grid, block, 0, st, dt, A, Gws, DTws, s.T,
-                           (int32_t)s.H, (int32_t)s.nc, nhb, (uint32_t)nblk);
+        hipLaunchKernelGGL(chunk_cumsum_kernel<64>, grid, block, 0, st, dt, A, Gws, DTws, dt_bias,
+                           (int32_t)softplus, s.T, (int32_t)s.H, (int32_t)s.nc, nhb,
+                           (uint32_t)nblk);
         break;
     case 128:
-        hipLaunchKernelGGL(chunk_cumsum_kernel<128>, grid, block, 0, st, dt, A, Gws, DTws, s.T,
-                           (int32_t)s.H, (int32_t)s.nc, nhb, (uint32_t)nblk);
+        hipLaunchKernelGGL(chunk_cumsum_kernel<128>, grid, block, 0, st, dt, A, Gws, DTws, dt_bias,
+                           (int32_t)softplus, s.T, (int32_t)s.H, (int32_t)s.nc, nhb,
+                           (uint32_t)nblk);
         break;
     case 256:
-        hipLaunchKernelGGL(chunk_cumsum_kernel<256>, grid, block, 0, st, dt, A, Gws, DTws, s.T,
-                           (int32_t)s.H, (int32_t)s.nc, nhb, (uint32_t)nblk);
+        hipLaunchKernelGGL(chunk_cumsum_kernel<256>, grid, block, 0, st, dt, A, Gws, DTws, dt_bias,
+                           (int32_t)softplus, s.T, (int32_t)s.H, (int32_t)s.nc, nhb,
+                           (uint32_t)nblk);
         break;
     default:
         return hipErrorInvalidValue;

@@ -96,6 +96,7 @@ struct ScanSmem {
 template <int L, int N>
 struct ScanArgs {
     const uint16_t *x, *Bm, *Cm, *hprev;
+    const uint16_t *z;   // output gate (GATE instantiations only)
     const float *D, *Gws, *DTws;
     float *y;
     int64_t T;
@@ -190,7 +191,7 @@ __device__ __forceinline__ void head_store(typename ScanSmem<L, N>::Head &hd,
     }
 }
 
-template <int L, int N, bool RAGGED, int W>
+template <int L, int N, bool RAGGED, bool GATE, int W>
 __device__ __forceinline__ void chunk_scan_group(ScanSmem<L, N> &sm, const ScanArgs<L, N> &a,
                                                  int64_t b, int32_t c, int32_t g, int32_t h0,
                                                  int32_t nh, int32_t nvalid) {
@@ -286,10 +287,29 @@ __device__ __forceinline__ void chunk_scan_group(ScanSmem<L, N> &sm, const ScanA
                 for (int e = 0; e < 4; ++e) acc[k][s][e] *= sc[e];
         }
 
+        // the gate of this lane's outputs (rows 16 I + 4q + e, columns 4m..4m+3),
+        // loaded two slabs before the end of the intra products and used in
+        // the epilogue: issued any earlier, its registers push the products
+        // into spills
+        constexpr int kZLead = 2;
+        uint2 zr[RBW][4];
+        auto load_z = [&]() {
+            const uint16_t *zb = a.z + ((b * a.T + t0) * a.H + h) * P + 4 * m;
+#pragma unroll
+            for (int k = 0; k < RBW; ++k)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int il = 16 * RB::at(k) + 4 * q + e;
+                    const int ic = RAGGED ? min(il, nvalid - 1) : il;   // unconditional
+                    zr[k][e] = load_nt(zb + (int64_t)ic * a.H * P);
+                }
+        };
         __builtin_amdgcn_sched_barrier(0);
         // ---- intra: the cached tiles drained with this head's decay ----
 #pragma unroll
         for (int js = 0; js < NS; ++js) {
+            if constexpr (GATE)
+                if (js == (NS > kZLead ? NS - kZLead : 0)) load_z();
             bf16x8 xf[4];
 #pragma unroll
             for (int s = 0; s < 4; ++s) xf[s] = as_bf16x8(hd.XF[js][s][lane]);
@@ -370,9 +390,16 @@ __device__ __forceinline__ void chunk_scan_group(ScanSmem<L, N> &sm, const ScanA
                         const uint32_t wd = (e < 2) ? xw[s].x : xw[s].y;
                         xv[s] = (e & 1) ? bf16_hi(wd) : bf16_lo(wd);
                     }
-                    store_nt(yb + il * XR + 4 * m,
-                             make_float4(acc[k][0][e] + Dh * xv[0], acc[k][1][e] + Dh * xv[1],
-                                         acc[k][2][e] + Dh * xv[2], acc[k][3][e] + Dh * xv[3]));
+                    float o[4];
+#pragma unroll
+                    for (int s = 0; s < 4; ++s) o[s] = acc[k][s][e] + Dh * xv[s];
+                    if constexpr (GATE) {   // y * silu(z)
+                        const float zf[4] = {bf16_lo(zr[k][e].x), bf16_hi(zr[k][e].x),
+                                             bf16_lo(zr[k][e].y), bf16_hi(zr[k][e].y)};
+#pragma unroll
+                        for (int s = 0; s < 4; ++s) o[s] *= fast_silu(zf[s]);
+                    }
+                    store_nt(yb + il * XR + 4 * m, make_float4(o[0], o[1], o[2], o[3]));
                 }
             }
         }
@@ -385,33 +412,33 @@ __device__ __forceinline__ void chunk_scan_group(ScanSmem<L, N> &sm, const ScanA
     }
 }
 
-template <int L, int N, bool RAGGED>
+template <int L, int N, bool RAGGED, bool GATE>
 __device__ __forceinline__ void chunk_scan_dispatch(ScanSmem<L, N> &sm, const ScanArgs<L, N> &a,
                                                     int64_t b, int32_t c, int32_t g, int32_t h0,
                                                     int32_t nh, int32_t nvalid) {
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     if constexpr (ScanWaves<L>::NW == 8) {
         switch (w) {
-        case 0: chunk_scan_group<L, N, RAGGED, 0>(sm, a, b, c, g, h0, nh, nvalid); break;
-        case 1: chunk_scan_group<L, N, RAGGED, 1>(sm, a, b, c, g, h0, nh, nvalid); break;
-        case 2: chunk_scan_group<L, N, RAGGED, 2>(sm, a, b, c, g, h0, nh, nvalid); break;
-        case 3: chunk_scan_group<L, N, RAGGED, 3>(sm, a, b, c, g, h0, nh, nvalid); break;
-        case 4: chunk_scan_group<L, N, RAGGED, 4>(sm, a, b, c, g, h0, nh, nvalid); break;
-        case 5: chunk_scan_group<L, N, RAGGED, 5>(sm, a, b, c, g, h0, nh, nvalid); break;
-        case 6: chunk_scan_group<L, N, RAGGED, 6>(sm, a, b, c, g, h0, nh, nvalid); break;
-        default: chunk_scan_group<L, N, RAGGED, 7>(sm, a, b, c, g, h0, nh, nvalid); break;
+        case 0: chunk_scan_group<L, N, RAGGED, GATE, 0>(sm, a, b, c, g, h0, nh, nvalid); break;
+        case 1: chunk_scan_group<L, N, RAGGED, GATE, 1>(sm, a, b, c, g, h0, nh, nvalid); break;
+        case 2: chunk_scan_group<L, N, RAGGED, GATE, 2>(sm, a, b, c, g, h0, nh, nvalid); break;
+        case 3: chunk_scan_group<L, N, RAGGED, GATE, 3>(sm, a, b, c, g, h0, nh, nvalid); break;
+        case 4: chunk_scan_group<L, N, RAGGED, GATE, 4>(sm, a, b, c, g, h0, nh, nvalid); break;
+        case 5: chunk_scan_group<L, N, RAGGED, GATE, 5>(sm, a, b, c, g, h0, nh, nvalid); break;
+        case 6: chunk_scan_group<L, N, RAGGED, GATE, 6>(sm, a, b, c, g, h0, nh, nvalid); break;
+        default: chunk_scan_group<L, N, RAGGED, GATE, 7>(sm, a, b, c, g, h0, nh, nvalid); break;
         }
     } else {
         switch (w) {
-        case 0: chunk_scan_group<L, N, RAGGED, 0>(sm, a, b, c, g, h0, nh, nvalid); break;
-        case 1: chunk_scan_group<L, N, RAGGED, 1>(sm, a, b, c, g, h0, nh, nvalid); break;
-        case 2: chunk_scan_group<L, N, RAGGED, 2>(sm, a, b, c, g, h0, nh, nvalid); break;
-        default: chunk_scan_group<L, N, RAGGED, 3>(sm, a, b, c, g, h0, nh, nvalid); break;
+        case 0: chunk_scan_group<L, N, RAGGED, GATE, 0>(sm, a, b, c, g, h0, nh, nvalid); break;
+        case 1: chunk_scan_group<L, N, RAGGED, GATE, 1>(sm, a, b, c, g, h0, nh, nvalid); break;
+        case 2: chunk_scan_group<L, N, RAGGED, GATE, 2>(sm, a, b, c, g, h0, nh, nvalid); break;
+        default: chunk_scan_group<L, N, RAGGED, GATE, 3>(sm, a, b, c, g, h0, nh, nvalid); break;
         }
     }
 }
 
-template <int L, int N>
+template <int L, int N, bool GATE>
 __global__ __launch_bounds__(64 * ScanWaves<L>::NW, 1) void chunk_scan_bf16_kernel(
     ScanArgs<L, N> a, uint32_t nblk) {
     __shared__ ScanSmem<L, N> sm;
@@ -427,17 +454,17 @@ __global__ __launch_bounds__(64 * ScanWaves<L>::NW, 1) void chunk_scan_bf16_kern
     const int64_t rem = a.T - (int64_t)c * L;
     const int32_t nvalid = rem < L ? (int32_t)rem : L;
     if (nvalid == L)
-        chunk_scan_dispatch<L, N, false>(sm, a, b, c, g, h0, nh, nvalid);
+        chunk_scan_dispatch<L, N, false, GATE>(sm, a, b, c, g, h0, nh, nvalid);
     else
-        chunk_scan_dispatch<L, N, true>(sm, a, b, c, g, h0, nh, nvalid);
+        chunk_scan_dispatch<L, N, true, GATE>(sm, a, b, c, g, h0, nh, nvalid);
 }
 
 template <int L, int N>
 __global__ __launch_bounds__(256) void chunk_scan_f32_kernel(
     const float *__restrict__ x, const float *__restrict__ Bm, const float *__restrict__ Cm,
     const float *__restrict__ D, const float *__restrict__ Gws, const float *__restrict__ DTws,
-    const float *__restrict__ hprev, float *__restrict__ y, int64_t T, int32_t H, int32_t G,
-    int32_t nc, uint32_t nblk) {
+    const float *__restrict__ hprev, float *__restrict__ y, const float *__restrict__ z,
+    int64_t T, int32_t H, int32_t G, int32_t nc, uint32_t nblk) {
     constexpr int P = 64;
     constexpr int RT = 16;  // rows per tile
     __shared__ float hs[P][N + 1];
@@ -498,7 +525,9 @@ __global__ __launch_bounds__(256) void chunk_scan_f32_kernel(
                 acc += cb[ii][j] * x[((b * T + tj) * H + h) * P + p];
             }
             const int64_t off = ((b * T + tok) * H + h) * P + p;
-            y[off] = acc + Dh * x[off];
+            float out = acc + Dh * x[off];
+            if (z) out *= fast_silu(z[off]);   // y * silu(z)
+            y[off] = out;
         }
     }
 }
@@ -519,10 +548,11 @@ inline int32_t heads_per_block(const Shape &s) {
 template <int L, int N>
 hipError_t launch_scan(const Shape &s, const void *x, const void *B, const void *C,
                        const float *D, const float *Gws, const float *DTws, const void *hprev,
-                       void *y, hipStream_t st) {
+                       void *y, const void *z, hipStream_t st) {
     if (s.bf16) {
         ScanArgs<L, N> a;
         a.x = (const uint16_t *)x;
+        a.z = (const uint16_t *)z;
         a.Bm = (const uint16_t *)B;
         a.Cm = (const uint16_t *)C;
         a.hprev = (const uint16_t *)hprev;
@@ -538,14 +568,18 @@ hipError_t launch_scan(const Shape &s, const void *x, const void *B, const void 
         a.NH = heads_per_block(s);
         a.nhb = (a.hpg + a.NH - 1) / a.NH;
         const uint64_t nblk = (uint64_t)s.Bt * s.nc * s.G * a.nhb;
-        hipLaunchKernelGGL((chunk_scan_bf16_kernel<L, N>), dim3((uint32_t)nblk),
-                           dim3(64 * ScanWaves<L>::NW), 0, st, a, (uint32_t)nblk);
+        if (z)
+            hipLaunchKernelGGL((chunk_scan_bf16_kernel<L, N, true>), dim3((uint32_t)nblk),
+                               dim3(64 * ScanWaves<L>::NW), 0, st, a, (uint32_t)nblk);
+        else
+            hipLaunchKernelGGL((chunk_scan_bf16_kernel<L, N, false>), dim3((uint32_t)nblk),
+                               dim3(64 * ScanWaves<L>::NW), 0, st, a, (uint32_t)nblk);
     } else {
         const uint64_t nblk = (uint64_t)s.Bt * s.nc * s.H;
         hipLaunchKernelGGL((chunk_scan_f32_kernel<L, N>), dim3((uint32_t)nblk), dim3(256), 0, st,
                            (const float *)x, (const float *)B, (const float *)C, D, Gws, DTws,
-                           (const float *)hprev, (float *)y, s.T, (int32_t)s.H, (int32_t)s.G,
-                           (int32_t)s.nc, (uint32_t)nblk);
+                           (const float *)hprev, (float *)y, (const float *)z, s.T,
+                           (int32_t)s.H, (int32_t)s.G, (int32_t)s.nc, (uint32_t)nblk);
     }
     return hipGetLastError();
 }
@@ -553,9 +587,9 @@ hipError_t launch_scan(const Shape &s, const void *x, const void *B, const void 
 template <int L>
 hipError_t launch_scan_n(const Shape &s, const void *x, const void *B, const void *C,
                          const float *D, const float *Gws, const float *DTws, const void *hprev,
-                         void *y, hipStream_t st) {
-    if (s.N == 64) return launch_scan<L, 64>(s, x, B, C, D, Gws, DTws, hprev, y, st);
-    if (s.N == 128) return launch_scan<L, 128>(s, x, B, C, D, Gws, DTws, hprev, y, st);
+                         void *y, const void *z, hipStream_t st) {
+    if (s.N == 64) return launch_scan<L, 64>(s, x, B, C, D, Gws, DTws, hprev, y, z, st);
+    if (s.N == 128) return launch_scan<L, 128>(s, x, B, C, D, Gws, DTws, hprev, y, z, st);
     return hipErrorInvalidValue;
 }
 
@@ -563,12 +597,12 @@ hipError_t launch_scan_n(const Shape &s, const void *x, const void *B, const voi
 
 hipError_t launch_chunk_scan(const Shape &s, const void *x, const void *B, const void *C,
                              const float *D, const float *Gws, const float *DTws,
-                             const void *hprev, void *y, hipStream_t st) {
+                             const void *hprev, void *y, const void *z, hipStream_t st) {
     if (s.Bt == 0 || s.nc == 0) return hipSuccess;
     switch (s.L) {
-    case 64: return launch_scan_n<64>(s, x, B, C, D, Gws, DTws, hprev, y, st);
-    case 128: return launch_scan_n<128>(s, x, B, C, D, Gws, DTws, hprev, y, st);
-    case 256: return launch_scan_n<256>(s, x, B, C, D, Gws, DTws, hprev, y, st);
+    case 64: return launch_scan_n<64>(s, x, B, C, D, Gws, DTws, hprev, y, z, st);
+    case 128: return launch_scan_n<128>(s, x, B, C, D, Gws, DTws, hprev, y, z, st);
+    case 256: return launch_scan_n<256>(s, x, B, C, D, Gws, DTws, hprev, y, z, st);
     default: return hipErrorInvalidValue;
     }
 }

@@ -20,6 +20,10 @@
 // wavefront: no LDS, no atomics.  B_t and C_t of the head's group (N values)
 // are read once per lane as 4-element vectors.  y is written fp32 (for bf16
 // inputs too: a bf16 y would carry a rounding of up to 2^-8 |y|).
+//
+// Optionally (sections 6.1 and 6.3 of the same page): dt <- dt + dt_bias_h,
+// then dt <- log(1 + e^dt) where dt <= 20; and y <- y * silu(z) after the D
+// term (GATE: z is loaded with x, up front, like every other operand).
 
 #include "ssd_device.h"
 #include "ssd_launch.h"
@@ -42,11 +46,12 @@ __device__ __forceinline__ float4 load4<uint16_t>(const uint16_t *p) {
 __device__ __forceinline__ float load1(const float *p) { return *p; }
 __device__ __forceinline__ float load1(const uint16_t *p) { return bf16_to_f32(*p); }
 
-template <int N, typename Tio>
+template <int N, typename Tio, bool GATE>
 __global__ __launch_bounds__(256) void decode_step_kernel(
     float *__restrict__ state, const Tio *__restrict__ x, const float *__restrict__ dt,
     const Tio *__restrict__ B, const Tio *__restrict__ C, const float *__restrict__ A,
-    const float *__restrict__ D, float *__restrict__ y, int32_t H, int32_t G) {
+    const float *__restrict__ D, float *__restrict__ y, const float *__restrict__ dt_bias,
+    int32_t softplus, const Tio *__restrict__ z, int32_t H, int32_t G) {
     constexpr int P = 64;
     constexpr int LPR = N / 4;         // lanes per state row
     constexpr int RPI = 64 / LPR;      // rows per wavefront iteration
@@ -59,7 +64,9 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
     const int lane = threadIdx.x & 63;
     const int sub = lane % LPR, rw = lane / LPR;
 
-    const float dtv = dt[bh];
+    float dtv = dt[bh];
+    if (dt_bias) dtv += dt_bias[h];
+    if (softplus && dtv <= 20.f) dtv = log1pf(expf(dtv));
     const float dA = fast_exp2(A[h] * dtv * kLog2e);
     const float Dh = D[h];
     const float4 Bv = load4(B + (b * G + g) * N + 4 * sub);
@@ -67,12 +74,13 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
 
     float *st = state + bh * (int64_t)(P * N);
     float4 sv[ITER];
-    float xv[ITER];
+    float xv[ITER], zv[ITER];
 #pragma unroll
     for (int k = 0; k < ITER; ++k) {
         const int p = 16 * wave + RPI * k + rw;
         sv[k] = load_nt(st + p * N + 4 * sub);
         xv[k] = load1(x + bh * P + p);
+        if constexpr (GATE) zv[k] = load1(z + bh * P + p);
     }
 #pragma unroll
     for (int k = 0; k < ITER; ++k) {
@@ -87,33 +95,50 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
         float part = ns.x * Cv.x + ns.y * Cv.y + ns.z * Cv.z + ns.w * Cv.w;
 #pragma unroll
         for (int off = LPR / 2; off > 0; off >>= 1) part += __shfl_xor(part, off, 64);
-        if (sub == 0) y[bh * P + p] = part + Dh * xv[k];
+        float out = part + Dh * xv[k];
+        if constexpr (GATE) out *= fast_silu(zv[k]);
+        if (sub == 0) y[bh * P + p] = out;
     }
+}
+
+template <int N, typename Tio>
+hipError_t launch_dec_t(const Shape &s, float *state, const void *x, const float *dt,
+                        const void *B, const void *C, const float *A, const float *D, void *y,
+                        const float *dt_bias, int softplus, const void *z, hipStream_t st) {
+    const uint64_t nblk = (uint64_t)s.Bt * s.H;
+    if (z)
+        hipLaunchKernelGGL((decode_step_kernel<N, Tio, true>), dim3((uint32_t)nblk), dim3(256), 0,
+                           st, state, (const Tio *)x, dt, (const Tio *)B, (const Tio *)C, A, D,
+                           (float *)y, dt_bias, (int32_t)softplus, (const Tio *)z, (int32_t)s.H,
+                           (int32_t)s.G);
+    else
+        hipLaunchKernelGGL((decode_step_kernel<N, Tio, false>), dim3((uint32_t)nblk), dim3(256),
+                           0, st, state, (const Tio *)x, dt, (const Tio *)B, (const Tio *)C, A,
+                           D, (float *)y, dt_bias, (int32_t)softplus, (const Tio *)nullptr,
+                           (int32_t)s.H, (int32_t)s.G);
+    return hipGetLastError();
 }
 
 template <int N>
 hipError_t launch_dec(const Shape &s, float *state, const void *x, const float *dt, const void *B,
-                      const void *C, const float *A, const float *D, void *y, hipStream_t st) {
-    const uint64_t nblk = (uint64_t)s.Bt * s.H;
+                      const void *C, const float *A, const float *D, void *y,
+                      const float *dt_bias, int softplus, const void *z, hipStream_t st) {
     if (s.bf16)
-        hipLaunchKernelGGL((decode_step_kernel<N, uint16_t>), dim3((uint32_t)nblk), dim3(256), 0,
-                           st, state, (const uint16_t *)x, dt, (const uint16_t *)B,
-                           (const uint16_t *)C, A, D, (float *)y, (int32_t)s.H, (int32_t)s.G);
-    else
-        hipLaunchKernelGGL((decode_step_kernel<N, float>), dim3((uint32_t)nblk), dim3(256), 0, st,
-                           state, (const float *)x, dt, (const float *)B, (const float *)C, A, D,
-                           (float *)y, (int32_t)s.H, (int32_t)s.G);
-    return hipGetLastError();
+        return launch_dec_t<N, uint16_t>(s, state, x, dt, B, C, A, D, y, dt_bias, softplus, z,
+                                         st);
+    return launch_dec_t<N, float>(s, state, x, dt, B, C, A, D, y, dt_bias, softplus, z, st);
 }
 
 }  // namespace
 
 hipError_t launch_decode_step(const Shape &s, float *state, const void *x, const float *dt,
                               const void *B, const void *C, const float *A, const float *D,
-                              void *y, hipStream_t st) {
+                              void *y, const float *dt_bias, int softplus, const void *z,
+                              hipStream_t st) {
     if (s.Bt == 0) return hipSuccess;
-    if (s.N == 64) return launch_dec<64>(s, state, x, dt, B, C, A, D, y, st);
-    if (s.N == 128) return launch_dec<128>(s, state, x, dt, B, C, A, D, y, st);
+    if (s.N == 64) return launch_dec<64>(s, state, x, dt, B, C, A, D, y, dt_bias, softplus, z, st);
+    if (s.N == 128)
+        return launch_dec<128>(s, state, x, dt, B, C, A, D, y, dt_bias, softplus, z, st);
     return hipErrorInvalidValue;
 }
 

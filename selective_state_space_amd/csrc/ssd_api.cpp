@@ -152,6 +152,15 @@ ssd_status check_ws(const ssd::Shape &s, void *ws, size_t bytes, Ws *w) {
         if (misaligned(p)) return fail(SSD_ERR_ALIGN, "%s is not 16-byte aligned", #p); \
     } while (0)
 
+// The optional layer interface: reserved must be 0; pointers 16-byte aligned.
+ssd_status check_opts(const ssd_layer_opts *o) {
+    if (!o) return SSD_OK;
+    if (o->reserved != 0) return fail(SSD_ERR_UNSUPPORTED, "ssd_layer_opts.reserved must be 0");
+    if (misaligned(o->dt_bias)) return fail(SSD_ERR_ALIGN, "dt_bias is not 16-byte aligned");
+    if (misaligned(o->z)) return fail(SSD_ERR_ALIGN, "z is not 16-byte aligned");
+    return SSD_OK;
+}
+
 ssd_status hip_result(hipError_t e, const char *what, hipStream_t st) {
     if (e == hipSuccess && debug_sync()) {
         e = hipStreamSynchronize(st);
@@ -163,8 +172,10 @@ ssd_status hip_result(hipError_t e, const char *what, hipStream_t st) {
 
 // Stage runners on validated arguments.
 ssd_status run_cumsum(const ssd::Shape &s, const float *dt, const float *A, const Ws &w,
-                      hipStream_t st) {
-    return hip_result(ssd::launch_chunk_cumsum(s, dt, A, w.G, w.DT, st), "chunk_cumsum", st);
+                      hipStream_t st, const ssd_layer_opts *o = nullptr) {
+    return hip_result(ssd::launch_chunk_cumsum(s, dt, A, w.G, w.DT, o ? o->dt_bias : nullptr,
+                                               o ? o->dt_softplus : 0, st),
+                      "chunk_cumsum", st);
 }
 ssd_status run_state(const ssd::Shape &s, const void *x, const void *B, const Ws &w,
                      hipStream_t st) {
@@ -199,8 +210,9 @@ ssd_status run_state_fwd(const ssd::Shape &s, const void *x, const void *B, cons
                       "state_fwd", st);
 }
 ssd_status run_scan(const ssd::Shape &s, const void *x, const void *B, const void *C,
-                    const float *D, void *y, const Ws &w, hipStream_t st) {
-    return hip_result(ssd::launch_chunk_scan(s, x, B, C, D, w.G, w.DT, w.hprev, y, st),
+                    const float *D, void *y, const Ws &w, hipStream_t st,
+                    const void *z = nullptr) {
+    return hip_result(ssd::launch_chunk_scan(s, x, B, C, D, w.G, w.DT, w.hprev, y, z, st),
                       "chunk_scan", st);
 }
 
@@ -321,14 +333,15 @@ ssd_status ssd_chunked_fwd_path(const ssd_dims *dims, int64_t chunk_size, int *u
     return ok();
 }
 
-ssd_status ssd_chunked_fwd(const void *x, const float *dt, const float *A, const void *B,
-                           const void *C, const float *D, int64_t chunk_size,
-                           const float *init_state, void *y, float *final_state,
-                           const ssd_dims *dims, void *workspace, size_t workspace_bytes,
-                           void *stream) {
+ssd_status ssd_chunked_fwd_opts(const void *x, const float *dt, const float *A, const void *B,
+                                const void *C, const float *D, int64_t chunk_size,
+                                const float *init_state, void *y, float *final_state,
+                                const ssd_layer_opts *opts, const ssd_dims *dims,
+                                void *workspace, size_t workspace_bytes, void *stream) {
     ssd::Shape s;
     ssd_status r = check_dims(dims, chunk_size, true, &s);
     if (r != SSD_OK) return r;
+    if ((r = check_opts(opts)) != SSD_OK) return r;
     if (s.Bt > 0 && s.T > 0) {
         REQUIRE_PTR(x);
         REQUIRE_PTR(dt);
@@ -352,23 +365,34 @@ ssd_status ssd_chunked_fwd(const void *x, const float *dt, const float *A, const
     if ((r = check_ws(s, workspace, workspace_bytes, &w)) != SSD_OK) return r;
     if (s.Bt == 0) return ok();
     hipStream_t st = static_cast<hipStream_t>(stream);
-    if ((r = run_cumsum(s, dt, A, w, st)) != SSD_OK) return r;
+    if ((r = run_cumsum(s, dt, A, w, st, opts)) != SSD_OK) return r;
     if (use_state_fwd(s)) {
         if ((r = run_state_fwd(s, x, B, init_state, final_state, w, st)) != SSD_OK) return r;
     } else {
         if ((r = run_state(s, x, B, w, st)) != SSD_OK) return r;
         if ((r = run_passing(s, init_state, final_state, w, st)) != SSD_OK) return r;
     }
-    if ((r = run_scan(s, x, B, C, D, y, w, st)) != SSD_OK) return r;
+    if ((r = run_scan(s, x, B, C, D, y, w, st, opts ? opts->z : nullptr)) != SSD_OK) return r;
     return ok();
 }
 
-ssd_status ssd_decode_step(float *state, const void *x_t, const float *dt_t, const void *B_t,
-                           const void *C_t, const float *A, const float *D, void *y_t,
-                           const ssd_dims *dims, void *stream) {
+ssd_status ssd_chunked_fwd(const void *x, const float *dt, const float *A, const void *B,
+                           const void *C, const float *D, int64_t chunk_size,
+                           const float *init_state, void *y, float *final_state,
+                           const ssd_dims *dims, void *workspace, size_t workspace_bytes,
+                           void *stream) {
+    return ssd_chunked_fwd_opts(x, dt, A, B, C, D, chunk_size, init_state, y, final_state,
+                                nullptr, dims, workspace, workspace_bytes, stream);
+}
+
+ssd_status ssd_decode_step_opts(float *state, const void *x_t, const float *dt_t,
+                                const void *B_t, const void *C_t, const float *A, const float *D,
+                                void *y_t, const ssd_layer_opts *opts, const ssd_dims *dims,
+                                void *stream) {
     ssd::Shape s;
     ssd_status r = check_dims(dims, 0, false, &s);
     if (r != SSD_OK) return r;
+    if ((r = check_opts(opts)) != SSD_OK) return r;
     REQUIRE_PTR(state);
     REQUIRE_PTR(x_t);
     REQUIRE_PTR(dt_t);
@@ -379,10 +403,19 @@ ssd_status ssd_decode_step(float *state, const void *x_t, const float *dt_t, con
     REQUIRE_PTR(y_t);
     if (s.Bt == 0) return ok();
     hipStream_t st = static_cast<hipStream_t>(stream);
-    r = hip_result(ssd::launch_decode_step(s, state, x_t, dt_t, B_t, C_t, A, D, y_t, st),
+    r = hip_result(ssd::launch_decode_step(s, state, x_t, dt_t, B_t, C_t, A, D, y_t,
+                                           opts ? opts->dt_bias : nullptr,
+                                           opts ? opts->dt_softplus : 0, opts ? opts->z : nullptr,
+                                           st),
                    "decode_step", st);
     if (r != SSD_OK) return r;
     return ok();
+}
+
+ssd_status ssd_decode_step(float *state, const void *x_t, const float *dt_t, const void *B_t,
+                           const void *C_t, const float *A, const float *D, void *y_t,
+                           const ssd_dims *dims, void *stream) {
+    return ssd_decode_step_opts(state, x_t, dt_t, B_t, C_t, A, D, y_t, nullptr, dims, stream);
 }
 
 const char *ssd_status_string(ssd_status status) {

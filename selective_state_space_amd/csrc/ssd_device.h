@@ -61,6 +61,13 @@ __device__ __forceinline__ void store_nt(uint16_t *p, uint2 v) {
 // 2^x on the transcendental unit (v_exp_f32).
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// silu(z) = z / (1 + e^-z) on the transcendental unit: e^-z as 2^(-z log2 e),
+// then v_rcp_f32.  Both limits come out right: z -> -inf gives 1/inf = 0 and
+// z -> +inf gives z * 1.
+__device__ __forceinline__ float fast_silu(float z) {
+    return z * __builtin_amdgcn_rcpf(1.f + fast_exp2(-1.4426950408889634f * z));
+}
+
 // Workgroups are dispatched round-robin over the 8 XCDs (id % 8).  Map the
 // hardware id to a logical id so that consecutive logical ids share an XCD
 // (and its L2): logical [x*per, (x+1)*per) runs on XCD x.  Ids past the last

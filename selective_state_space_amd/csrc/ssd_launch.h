@@ -12,15 +12,17 @@ struct Shape {
     bool bf16;                          // io dtype: bf16 (else float32)
 };
 
+// dt_bias (NULL = none) and softplus: the optional dt preprocessing.
 hipError_t launch_chunk_cumsum(const Shape &s, const float *dt, const float *A, float *Gws,
-                               float *DTws, hipStream_t st);
+                               float *DTws, const float *dt_bias, int softplus, hipStream_t st);
 hipError_t launch_chunk_state(const Shape &s, const void *x, const void *B, const float *Gws,
                               const float *DTws, float *S, hipStream_t st);
 hipError_t launch_state_passing(const Shape &s, const float *S, const float *Gws,
                                 const float *init, void *hprev, float *fin, hipStream_t st);
+// z: output gate (x's dtype and layout), y <- y * silu(z); NULL = none.
 hipError_t launch_chunk_scan(const Shape &s, const void *x, const void *B, const void *C,
                              const float *D, const float *Gws, const float *DTws,
-                             const void *hprev, void *y, hipStream_t st);
+                             const void *hprev, void *y, const void *z, hipStream_t st);
 // chunk_state + state_passing in one pass (bf16 io).  rows_per_block = 4, 2
 // or 1 row sets of the head per workgroup, 0 = chosen from the shape.
 bool state_fwd_supported(const Shape &s);
@@ -32,6 +34,7 @@ hipError_t launch_state_fwd(const Shape &s, const void *x, const void *B, const 
                             void *bfrag, int rows_per_block, hipStream_t st);
 hipError_t launch_decode_step(const Shape &s, float *state, const void *x, const float *dt,
                               const void *B, const void *C, const float *A, const float *D,
-                              void *y, hipStream_t st);
+                              void *y, const float *dt_bias, int softplus, const void *z,
+                              hipStream_t st);
 
 }  // namespace ssd

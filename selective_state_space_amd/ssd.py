@@ -50,6 +50,12 @@ class Dims(ctypes.Structure):
                 ("io_dtype", ctypes.c_int32)]
 
 
+class LayerOpts(ctypes.Structure):
+    """ssd_layer_opts: dt_bias [H] f32 (or NULL), dt_softplus, reserved = 0, z (or NULL)."""
+    _fields_ = [("dt_bias", ctypes.c_void_p), ("dt_softplus", ctypes.c_int32),
+                ("reserved", ctypes.c_int32), ("z", ctypes.c_void_p)]
+
+
 _lib = None
 
 
@@ -73,6 +79,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "ssd_state_passing": ([vp, vp, i64, dp, vp, sz, vp], st),
         "ssd_chunk_scan": ([vp, vp, vp, vp, vp, i64, dp, vp, sz, vp], st),
         "ssd_state_fwd": ([vp, vp, vp, vp, i64, dp, vp, sz, vp], st),
+        "ssd_chunked_fwd_opts": ([vp, vp, vp, vp, vp, vp, i64, vp, vp, vp,
+                                  ctypes.POINTER(LayerOpts), dp, vp, sz, vp], st),
+        "ssd_decode_step_opts": ([vp, vp, vp, vp, vp, vp, vp, vp, ctypes.POINTER(LayerOpts), dp,
+                                  vp], st),
         "ssd_chunked_fwd_path": ([dp, i64, ctypes.POINTER(ctypes.c_int)], st),
         "ssd_decode_step": ([vp, vp, vp, vp, vp, vp, vp, vp, dp, vp], st),
         "ssd_status_string": ([st], ctypes.c_char_p),
@@ -150,7 +160,8 @@ class FwdArgs:
     """Checked, contiguous arguments of one chunked forward (shared by the stage calls)."""
 
     def __init__(self, x, dt, A, B, C, D, chunk_size, init_state=None, y=None,
-                 final_state=None, want_final=True, workspace=None):
+                 final_state=None, want_final=True, workspace=None, dt_bias=None,
+                 dt_softplus=False, z=None):
         if x.dim() != 4 or B.dim() != 4:
             raise ValueError("x must be [Bt,T,H,P] and B, C [Bt,T,G,N]")
         dev = x.device
@@ -176,6 +187,10 @@ class FwdArgs:
         else:
             self.final = None
         self.L = int(chunk_size)
+        self.dt_bias = None if dt_bias is None else _need(dt_bias, "dt_bias", torch.float32,
+                                                          (H,), dev)
+        self.z = None if z is None else _need(z, "z", io, (Bt, T, H, P), dev)
+        self.dt_softplus = bool(dt_softplus)
         self.dims = fwd_dims(self.x, self.B)
         need = ssd_chunked_fwd_workspace_size(self.dims, self.L)
         if workspace is None:
@@ -184,9 +199,15 @@ class FwdArgs:
         self.device = dev
 
 
+def _layer_opts(dt_bias, dt_softplus, z):
+    if dt_bias is None and not dt_softplus and z is None:
+        return None
+    return LayerOpts(_ptr(dt_bias), int(bool(dt_softplus)), 0, _ptr(z))
+
+
 def ssd_chunked_fwd(x, dt=None, A=None, B=None, C=None, D=None, chunk_size=None,
                     init_state=None, y=None, final_state=None, want_final: bool = True,
-                    workspace=None):
+                    workspace=None, dt_bias=None, dt_softplus: bool = False, z=None):
     """Chunked forward.  Returns (y, final_state or None).
 
     x [Bt,T,H,P] (float32 or bfloat16), dt [Bt,T,H] f32, A/D [H] f32,
@@ -195,6 +216,8 @@ def ssd_chunked_fwd(x, dt=None, A=None, B=None, C=None, D=None, chunk_size=None,
     ``final_state`` and ``workspace`` may be passed in to avoid allocation;
     ``final_state`` may be the same tensor as ``init_state``.  ``x`` may
     instead be a prepared FwdArgs (then the other arguments are ignored).
+    ``dt_bias`` [H] f32, ``dt_softplus`` and the gate ``z`` (x's shape and
+    dtype) are the optional layer interface (ssd_layer_opts).
     """
     if isinstance(x, FwdArgs):
         a = x
@@ -202,12 +225,21 @@ def ssd_chunked_fwd(x, dt=None, A=None, B=None, C=None, D=None, chunk_size=None,
         if any(v is None for v in (dt, A, B, C, D, chunk_size)):
             raise ValueError("ssd_chunked_fwd needs x, dt, A, B, C, D and chunk_size")
         a = FwdArgs(x, dt, A, B, C, D, chunk_size, init_state, y, final_state, want_final,
-                    workspace)
+                    workspace, dt_bias, dt_softplus, z)
     lib = load_library()
-    st = lib.ssd_chunked_fwd(_ptr(a.x), _ptr(a.dt), _ptr(a.A), _ptr(a.B), _ptr(a.C), _ptr(a.D),
-                             a.L, _ptr(a.init), _ptr(a.y), _ptr(a.final), ctypes.byref(a.dims),
-                             _ptr(a.ws), a.ws.numel(), _stream(a.device))
-    _check("ssd_chunked_fwd", st)
+    opts = _layer_opts(a.dt_bias, a.dt_softplus, a.z)
+    if opts is None:
+        st = lib.ssd_chunked_fwd(_ptr(a.x), _ptr(a.dt), _ptr(a.A), _ptr(a.B), _ptr(a.C),
+                                 _ptr(a.D), a.L, _ptr(a.init), _ptr(a.y), _ptr(a.final),
+                                 ctypes.byref(a.dims), _ptr(a.ws), a.ws.numel(),
+                                 _stream(a.device))
+        _check("ssd_chunked_fwd", st)
+    else:
+        st = lib.ssd_chunked_fwd_opts(_ptr(a.x), _ptr(a.dt), _ptr(a.A), _ptr(a.B), _ptr(a.C),
+                                      _ptr(a.D), a.L, _ptr(a.init), _ptr(a.y), _ptr(a.final),
+                                      ctypes.byref(opts), ctypes.byref(a.dims), _ptr(a.ws),
+                                      a.ws.numel(), _stream(a.device))
+        _check("ssd_chunked_fwd_opts", st)
     return a.y, a.final
 
 
@@ -274,8 +306,13 @@ def workspace_views(a: FwdArgs):
     }
 
 
-def ssd_decode_step(state, x_t, dt_t, B_t, C_t, A, D, y_t=None):
-    """One decode step; ``state`` [Bt,H,P,N] f32 is updated in place.  Returns y_t [Bt,H,P] f32."""
+def ssd_decode_step(state, x_t, dt_t, B_t, C_t, A, D, y_t=None, dt_bias=None,
+                    dt_softplus: bool = False, z_t=None):
+    """One decode step; ``state`` [Bt,H,P,N] f32 is updated in place.  Returns y_t [Bt,H,P] f32.
+
+    ``dt_bias`` [H], ``dt_softplus`` and the gate ``z_t`` [Bt,H,P] (x_t's dtype)
+    are the optional layer interface (ssd_layer_opts).
+    """
     dev = state.device
     if dev.type != "cuda":
         raise ValueError("tensors must live on a GPU device, got %s" % dev)
@@ -293,8 +330,19 @@ def ssd_decode_step(state, x_t, dt_t, B_t, C_t, A, D, y_t=None):
     y_t = (torch.empty((Bt, H, P), dtype=torch.float32, device=dev) if y_t is None
            else _need(y_t, "y_t", torch.float32, (Bt, H, P), dev))
     dims = Dims(Bt, 1, H, P, N, G, _io_code(io))
+    if dt_bias is not None:
+        dt_bias = _need(dt_bias, "dt_bias", torch.float32, (H,), dev)
+    if z_t is not None:
+        z_t = _need(z_t, "z_t", io, (Bt, H, P), dev)
     lib = load_library()
-    _check("ssd_decode_step", lib.ssd_decode_step(_ptr(state), _ptr(x_t), _ptr(dt_t), _ptr(B_t),
-                                                  _ptr(C_t), _ptr(A), _ptr(D), _ptr(y_t),
-                                                  ctypes.byref(dims), _stream(dev)))
+    opts = _layer_opts(dt_bias, dt_softplus, z_t)
+    if opts is None:
+        _check("ssd_decode_step", lib.ssd_decode_step(_ptr(state), _ptr(x_t), _ptr(dt_t),
+                                                      _ptr(B_t), _ptr(C_t), _ptr(A), _ptr(D),
+                                                      _ptr(y_t), ctypes.byref(dims),
+                                                      _stream(dev)))
+    else:
+        _check("ssd_decode_step_opts", lib.ssd_decode_step_opts(
+            _ptr(state), _ptr(x_t), _ptr(dt_t), _ptr(B_t), _ptr(C_t), _ptr(A), _ptr(D),
+            _ptr(y_t), ctypes.byref(opts), ctypes.byref(dims), _stream(dev)))
     return y_t

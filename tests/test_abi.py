@@ -205,3 +205,21 @@ def test_empty_sequence_allows_null_token_tensors():
                 fin=P_MIS) == -4
     # with tokens present the same NULLs are errors
     assert _fwd(dims(), x=None) == -1
+
+
+def test_layer_opts_are_validated():
+    L = lib()
+    d = dims()
+    bad = ssd.LayerOpts(None, 1, 7, None)          # reserved must be 0
+    assert L.ssd_chunked_fwd_opts(P16, P16, P16, P16, P16, P16, 256, None, P16, None,
+                                  ctypes.byref(bad), ctypes.byref(d), P16, 1 << 40, None) == -3
+    assert "reserved" in L.ssd_last_error_detail().decode()
+    mis = ssd.LayerOpts(None, 0, 0, P_MIS)
+    assert L.ssd_chunked_fwd_opts(P16, P16, P16, P16, P16, P16, 256, None, P16, None,
+                                  ctypes.byref(mis), ctypes.byref(d), P16, 1 << 40, None) == -4
+    misb = ssd.LayerOpts(P_MIS, 0, 0, None)
+    assert L.ssd_decode_step_opts(P16, P16, P16, P16, P16, P16, P16, P16, ctypes.byref(misb),
+                                  ctypes.byref(d), None) == -4
+    # NULL options fall through to the usual validation (short workspace)
+    assert L.ssd_chunked_fwd_opts(P16, P16, P16, P16, P16, P16, 256, None, P16, None, None,
+                                  ctypes.byref(d), P16, 10, None) == -5
