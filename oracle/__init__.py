@@ -168,6 +168,53 @@ def token_decode(state, x_t, dt_t, B_t, C_t, A, D, pairs: Optional[Sequence[int]
     return y
 
 
+def token_decode_multi(state, x, dt, B, C, A, D, parent=None, update_state: bool = True,
+                       pairs: Optional[Sequence[int]] = None, nthreads: int = 0, dt_bias=None,
+                       dt_softplus: bool = False, z=None):
+    """K decode steps per sequence in float64, with the state after every step.
+
+    Multi-token state update with per-step snapshots ("Optimizing Nemotron v3
+    Super in TensorRT-LLM", sections 10.3 and 10.4): for each sequence b the
+    K tokens x[b, k] are taken in order; step k starts from the state that
+    step p(k) produced, where p(k) = parent[b, k] when parent is given,
+    k >= 1 and 0 <= parent[b, k] < k (a draft tree), and p(k) = k - 1
+    otherwise; step 0 starts from ``state``.  The snapshot of step k is the
+    state after step k.  With ``update_state`` the final running state (that
+    of step K - 1) replaces ``state``; without it ``state`` is left as it was
+    (the verification pass that must not overwrite the main state).
+
+    state [npairs,P,N] float64, x [Bt,K,H,P], dt [Bt,K,H], B/C [Bt,K,G,N],
+    parent [Bt,K] integers or None; z [Bt,K,H,P] as in token_fwd.
+    Returns (y [npairs,K,P], snapshots [npairs,K,P,N]).
+    """
+    x, dt, B, C = map(_f32, (x, dt, B, C))
+    Bt, K, H, P = x.shape
+    N = B.shape[3]
+    assert state.dtype == np.float64 and state.flags.c_contiguous
+    pr = np.arange(Bt * H) if pairs is None else np.asarray(pairs, dtype=np.int64)
+    npairs = len(pr)
+    assert state.shape == (npairs, P, N)
+    zz = None if z is None else _f32(z)
+    par = None if parent is None else np.asarray(parent, dtype=np.int64).reshape(Bt, K)
+    y = np.empty((npairs, K, P), np.float64)
+    snaps = np.empty((npairs, K, P, N), np.float64)
+    run = state.copy()
+    row = pr // H            # the sequence of each pair
+    for k in range(K):
+        if par is not None and k >= 1:
+            pk = par[row, k]
+            take = (pk >= 0) & (pk < k)
+            for i in np.nonzero(take)[0]:
+                run[i] = snaps[i, pk[i]]
+        y[:, k] = token_decode(run, x[:, k], dt[:, k], B[:, k], C[:, k], A, D, pairs=pr,
+                               nthreads=nthreads, dt_bias=dt_bias, dt_softplus=dt_softplus,
+                               z_t=None if zz is None else zz[:, k])
+        snaps[:, k] = run
+    if update_state:
+        state[...] = run
+    return y, snaps
+
+
 def chunked_reference(x, dt, A, B, C, D, chunk_size: int, init_state=None):
     """The chunked SSD form in float64 NumPy, with its intermediates.
 
