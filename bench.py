@@ -214,6 +214,55 @@ def run_decode(w, steps: int, warmup: int):
     return float(np.median(t)), float(np.mean(t))
 
 
+def multi_bytes(w, snapshots: bool, update: bool, io_bytes=2):
+    """Algorithmic HBM bytes of one multi-token decode call."""
+    Bt, K, H, P, N, G = w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.ngroups
+    st = Bt * H * P * N * 4
+    tok = Bt * K * (H * P * io_bytes + H * 4 + 2 * G * N * io_bytes + H * P * 4)
+    return st * (1 + (K if snapshots else 0) + (1 if update else 0)) + tok
+
+
+def run_decode_multi(w, steps: int, warmup: int):
+    """The multi-token decode workload in its two modes: speculative
+    verification (a snapshot after every token, main state not updated) and
+    plain multi-token steps (no snapshots, state updated).  Returns the mean
+    per-call milliseconds of each."""
+    import torch
+    from selective_state_space_amd import inputs as gen
+    from selective_state_space_amd import ssd
+
+    dev = torch.device("cuda:0")
+    prm = gen.decode_params(w, 0)
+    m = gen.make_decode_multi(w, prm, 0)
+    bf = torch.bfloat16
+
+    def up(a, dt=torch.float32):
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dt).to(dev)
+
+    args = (up(m.x, bf), up(m.dt), up(m.B, bf), up(m.C, bf), up(prm.A), up(prm.D))
+    state = torch.zeros((w.batch, w.nheads, w.headdim, w.dstate), device=dev)
+    y = torch.empty((w.batch, w.seqlen, w.nheads, w.headdim), device=dev)
+    snaps = torch.empty((w.batch, w.seqlen, w.nheads, w.headdim, w.dstate), device=dev)
+    out = {}
+    for mode, kw in (("verify", dict(snapshots=snaps, update_state=False)),
+                     ("plain", dict(snapshots=None, update_state=True))):
+        def call():
+            ssd.ssd_decode_multi(state, *args, y=y, **kw)
+        for _ in range(warmup):
+            call()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            call()
+        e1.record()
+        torch.cuda.synchronize()
+        out[mode] = e0.elapsed_time(e1) / steps
+    del state, snaps, y
+    torch.cuda.empty_cache()
+    return out
+
+
 def run_layer_interface(w, wd, steps: int, warmup: int):
     """The forward and decode step with every layer option on (dt_bias,
     softplus, the z gate).  The raw steps are the inverse softplus of the
@@ -402,6 +451,20 @@ def main():
                       tokens_per_s=round(wd.batch / (med * 1e-3), 1),
                       alg_bytes_per_step=int(byt), steps_timed=args.decode_steps)
         log("decode: %.1f us/step, %.0f GB/s" % (med * 1e3, decode["GBps"]))
+    multi = None
+    if not args.no_decode:
+        wm = gen.BY_NAME["mtp_verify_b256_k4"]
+        ms = run_decode_multi(wm, 20, 5)
+        multi = {"workload": wm.name, "tokens_per_call": wm.batch * wm.seqlen}
+        for mode, snap, upd in (("verify", True, False), ("plain", False, True)):
+            byt = multi_bytes(wm, snap, upd)
+            multi[mode] = dict(us_per_call=round(ms[mode] * 1e3, 2),
+                               tokens_per_s=round(wm.batch * wm.seqlen / (ms[mode] * 1e-3), 1),
+                               GBps=round(byt / (ms[mode] * 1e-3) / 1e9, 1),
+                               hbm_frac=round(byt / (ms[mode] * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+                               alg_bytes_per_call=int(byt), snapshots=snap, state_update=upd)
+            log("multi-token decode (%s): %.1f us/call, %.0f GB/s"
+                % (mode, ms[mode] * 1e3, multi[mode]["GBps"]))
     layer = None
     if not args.no_decode:
         wd = gen.WORKLOADS[4]
@@ -454,6 +517,7 @@ def main():
                                               / BF16_PEAK_TFLOPS, 4),
         "kernels": kernels,
         "decode": decode,
+        "decode_multi": multi,
         "layer_interface": layer,
         "hbm_copy_reference_GBps": round(copy_gbps, 1),
         "wall_s_timed": round(wall, 4),

@@ -230,6 +230,47 @@ ssd_status ssd_decode_step_opts(float *state, const void *x_t, const float *dt_t
                                 void *y_t, const ssd_layer_opts *opts, const ssd_dims *dims,
                                 void *stream);
 
+/*
+ * Several decode steps per sequence in one launch: the multi-token state
+ * update of speculative decoding ("Optimizing Nemotron v3 Super in
+ * TensorRT-LLM", sections 10.3 and 10.4).  K = dims->seqlen tokens per
+ * sequence (0 <= K <= 65536; K = 0 does nothing).  For every (b, h), step
+ * k = 0 .. K-1 is the decode step of ssd_decode_step on token k, starting from
+ *   - the state passed in, for k = 0;
+ *   - the snapshot of step parent[b, k], when parent is given and
+ *     0 <= parent[b, k] < k (a draft tree);
+ *   - the state after step k - 1, otherwise (any other parent value
+ *     included: negative, k itself or a later step).
+ *
+ *   state      [Bt, H, P, N]     float32   in; out unless NO_STATE_UPDATE
+ *   x          [Bt, K, H, P]     io dtype  in
+ *   dt         [Bt, K, H]        float32   in
+ *   B, C       [Bt, K, G, N]     io dtype  in
+ *   A, D       [H]               float32   in
+ *   y          [Bt, K, H, P]     float32   out: y of every step
+ *   snapshots  [Bt, K, H, P, N]  float32   out, or NULL: the state after each
+ *                                          step (the buffer a later accept
+ *                                          step copies from)
+ *   parent     [Bt, K]           int32     in, or NULL (needs snapshots:
+ *                                          SSD_ERR_NULL otherwise)
+ *   flags      0, or SSD_DECODE_NO_STATE_UPDATE: the state is only read (the
+ *              verification pass that must not overwrite the main state);
+ *              other bits SSD_ERR_UNSUPPORTED
+ *   opts       as for ssd_decode_step_opts, with z [Bt, K, H, P]; may be NULL
+ *
+ * Without the flag the state ends as the state after step K - 1 (in a tree:
+ * that step's own path).  Pointers as for ssd_decode_step (caller-owned device
+ * memory, 16-byte aligned, snapshots and parent included); snapshots, y and
+ * state must not overlap.  With no tokens (K = 0 or batch 0) the token
+ * tensors may be NULL and the state is left as it is.  With K = 1, no parent and no snapshots this is
+ * ssd_decode_step(_opts).
+ */
+#define SSD_DECODE_NO_STATE_UPDATE 1u
+ssd_status ssd_decode_multi(float *state, const void *x, const float *dt, const void *B,
+                            const void *C, const float *A, const float *D, void *y,
+                            float *snapshots, const int32_t *parent, uint32_t flags,
+                            const ssd_layer_opts *opts, const ssd_dims *dims, void *stream);
+
 /* Static text for a status code. */
 const char *ssd_status_string(ssd_status status);
 

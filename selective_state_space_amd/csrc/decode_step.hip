@@ -101,6 +101,144 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
     }
 }
 
+// ---------------------------------------------------------------------------
+// decode_multi: K tokens per sequence in one launch ("Optimizing Nemotron v3
+// Super in TensorRT-LLM", sections 10.3 and 10.4: the multi-token state update
+// of speculative decoding).  Same work split as decode_step -- one workgroup
+// per (b, h), the lane's slice of the state in registers -- but the state
+// stays in registers across the K steps, so it is read once and written at
+// most once per call instead of once per token.  SNAP writes the state after
+// every step (the per-step snapshots, [Bt, K, H, P, N]); TREE restarts step k
+// from the snapshot of step parent[b, k] when that is an earlier step (a
+// draft tree; other values continue from step k - 1).  The snapshot is read
+// back by the same lanes that wrote it, so no synchronisation is needed.
+// Without update the state is only read (the verification pass).
+template <int N, typename Tio, bool GATE>
+struct TokenIn {
+    static constexpr int ITER = 16 / (64 / (N / 4));
+    float dtv;
+    float4 Bv, Cv;
+    float xv[ITER], zv[ITER];
+};
+
+template <int N, typename Tio, bool GATE, bool SNAP, bool TREE>
+__global__ __launch_bounds__(256) void decode_multi_kernel(
+    float *__restrict__ state, const Tio *__restrict__ x, const float *__restrict__ dt,
+    const Tio *__restrict__ B, const Tio *__restrict__ C, const float *__restrict__ A,
+    const float *__restrict__ D, float *__restrict__ y, const float *__restrict__ dt_bias,
+    int32_t softplus, const Tio *__restrict__ z, float *__restrict__ snaps,
+    const int32_t *__restrict__ parent, int32_t update, int32_t H, int32_t G, int32_t K) {
+    constexpr int P = 64;
+    constexpr int LPR = N / 4;         // lanes per state row
+    constexpr int RPI = 64 / LPR;      // rows per wavefront iteration
+    constexpr int ITER = 16 / RPI;     // rows per lane
+    const int64_t bh = blockIdx.x;
+    const int64_t b = bh / H;
+    const int32_t h = (int32_t)(bh % H);
+    const int32_t g = h / (H / G);
+    const int wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int sub = lane % LPR, rw = lane / LPR;
+    const float a2 = A[h] * kLog2e, Dh = D[h];
+    const float bias = dt_bias ? dt_bias[h] : 0.f;
+    int rowoff[ITER];                  // this lane's rows p, as offsets into a [P][N] state
+#pragma unroll
+    for (int i = 0; i < ITER; ++i) rowoff[i] = (16 * wave + RPI * i + rw) * N + 4 * sub;
+
+    // the small per-token operands of step k (B, C of the head's group)
+    auto load_tok = [&](int k, TokenIn<N, Tio, GATE> &in) {
+        const int64_t tk = b * K + k;
+        const int64_t th = tk * H + h;
+        in.dtv = dt[th];
+        in.Bv = load4(B + (tk * G + g) * N + 4 * sub);
+        in.Cv = load4(C + (tk * G + g) * N + 4 * sub);
+#pragma unroll
+        for (int i = 0; i < ITER; ++i) {
+            const int p = 16 * wave + RPI * i + rw;
+            in.xv[i] = load1(x + th * P + p);
+            if constexpr (GATE) in.zv[i] = load1(z + th * P + p);
+        }
+    };
+
+    const float *st_in = state + bh * (int64_t)(P * N);
+    float4 sv[ITER];
+#pragma unroll
+    for (int i = 0; i < ITER; ++i) sv[i] = load_nt(st_in + rowoff[i]);
+    TokenIn<N, Tio, GATE> cur, nxt;
+    load_tok(0, cur);
+    for (int k = 0; k < K; ++k) {
+        const int64_t th = (b * K + k) * H + h;
+        load_tok(min(k + 1, K - 1), nxt);   // the next step's operands, in flight now
+        if constexpr (TREE) {
+            const int par = k > 0 ? parent[b * K + k] : -1;   // uniform over the workgroup
+            if (par >= 0 && par < k) {
+                const float *sp = snaps + ((b * K + par) * H + h) * (int64_t)(P * N);
+#pragma unroll
+                for (int i = 0; i < ITER; ++i)
+                    sv[i] = *reinterpret_cast<const float4 *>(sp + rowoff[i]);
+            }
+        }
+        float dtv = cur.dtv + bias;
+        if (softplus && dtv <= 20.f) dtv = log1pf(expf(dtv));
+        const float dA = fast_exp2(a2 * dtv);
+        float *sn = SNAP ? snaps + th * (int64_t)(P * N) : nullptr;
+#pragma unroll
+        for (int i = 0; i < ITER; ++i) {
+            const float u = dtv * cur.xv[i];
+            sv[i].x = dA * sv[i].x + u * cur.Bv.x;
+            sv[i].y = dA * sv[i].y + u * cur.Bv.y;
+            sv[i].z = dA * sv[i].z + u * cur.Bv.z;
+            sv[i].w = dA * sv[i].w + u * cur.Bv.w;
+            if constexpr (SNAP) store_nt(sn + rowoff[i], sv[i]);
+            float part = sv[i].x * cur.Cv.x + sv[i].y * cur.Cv.y + sv[i].z * cur.Cv.z +
+                         sv[i].w * cur.Cv.w;
+#pragma unroll
+            for (int off = LPR / 2; off > 0; off >>= 1) part += __shfl_xor(part, off, 64);
+            float out = part + Dh * cur.xv[i];
+            if constexpr (GATE) out *= fast_silu(cur.zv[i]);
+            if (sub == 0) y[th * P + 16 * wave + RPI * i + rw] = out;
+        }
+        cur = nxt;
+    }
+    if (update && K > 0) {
+        float *st_out = state + bh * (int64_t)(P * N);
+#pragma unroll
+        for (int i = 0; i < ITER; ++i) store_nt(st_out + rowoff[i], sv[i]);
+    }
+}
+
+template <int N, typename Tio, bool GATE>
+hipError_t launch_multi_g(const Shape &s, const MultiArgs &m, hipStream_t st) {
+    const uint32_t nblk = (uint32_t)((uint64_t)s.Bt * s.H);
+    const Tio *z = (const Tio *)m.z;
+#define SSD_MULTI_LAUNCH(SNAP, TREE)                                                          \
+    hipLaunchKernelGGL((decode_multi_kernel<N, Tio, GATE, SNAP, TREE>), dim3(nblk), dim3(256), \
+                       0, st, m.state, (const Tio *)m.x, m.dt, (const Tio *)m.B,              \
+                       (const Tio *)m.C, m.A, m.D, m.y, m.dt_bias, (int32_t)m.softplus, z,     \
+                       m.snaps, m.parent, (int32_t)m.update, (int32_t)s.H, (int32_t)s.G,      \
+                       (int32_t)s.T)
+    if (m.parent)
+        SSD_MULTI_LAUNCH(true, true);
+    else if (m.snaps)
+        SSD_MULTI_LAUNCH(true, false);
+    else
+        SSD_MULTI_LAUNCH(false, false);
+#undef SSD_MULTI_LAUNCH
+    return hipGetLastError();
+}
+
+template <int N, typename Tio>
+hipError_t launch_multi_t(const Shape &s, const MultiArgs &m, hipStream_t st) {
+    if (m.z) return launch_multi_g<N, Tio, true>(s, m, st);
+    return launch_multi_g<N, Tio, false>(s, m, st);
+}
+
+template <int N>
+hipError_t launch_multi_n(const Shape &s, const MultiArgs &m, hipStream_t st) {
+    if (s.bf16) return launch_multi_t<N, uint16_t>(s, m, st);
+    return launch_multi_t<N, float>(s, m, st);
+}
+
 template <int N, typename Tio>
 hipError_t launch_dec_t(const Shape &s, float *state, const void *x, const float *dt,
                         const void *B, const void *C, const float *A, const float *D, void *y,
@@ -130,6 +268,13 @@ hipError_t launch_dec(const Shape &s, float *state, const void *x, const float *
 }
 
 }  // namespace
+
+hipError_t launch_decode_multi(const Shape &s, const MultiArgs &m, hipStream_t st) {
+    if (s.Bt == 0 || s.T == 0) return hipSuccess;
+    if (s.N == 64) return launch_multi_n<64>(s, m, st);
+    if (s.N == 128) return launch_multi_n<128>(s, m, st);
+    return hipErrorInvalidValue;
+}
 
 hipError_t launch_decode_step(const Shape &s, float *state, const void *x, const float *dt,
                               const void *B, const void *C, const float *A, const float *D,

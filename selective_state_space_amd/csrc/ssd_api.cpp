@@ -47,6 +47,7 @@ bool debug_sync() {
 
 constexpr int64_t kMaxDim = int64_t(1) << 30;
 constexpr uint64_t kMaxGrid = (uint64_t(1) << 31) - 1;
+constexpr int64_t kMaxTokensPerStep = int64_t(1) << 16;   // ssd_decode_multi's K
 
 bool misaligned(const void *p) { return p && (reinterpret_cast<uintptr_t>(p) & 15u); }
 
@@ -416,6 +417,59 @@ ssd_status ssd_decode_step(float *state, const void *x_t, const float *dt_t, con
                            const void *C_t, const float *A, const float *D, void *y_t,
                            const ssd_dims *dims, void *stream) {
     return ssd_decode_step_opts(state, x_t, dt_t, B_t, C_t, A, D, y_t, nullptr, dims, stream);
+}
+
+ssd_status ssd_decode_multi(float *state, const void *x, const float *dt, const void *B,
+                            const void *C, const float *A, const float *D, void *y,
+                            float *snapshots, const int32_t *parent, uint32_t flags,
+                            const ssd_layer_opts *opts, const ssd_dims *dims, void *stream) {
+    ssd::Shape s;
+    ssd_status r = check_dims(dims, 0, false, &s);
+    if (r != SSD_OK) return r;
+    if (dims->seqlen < 0 || dims->seqlen > kMaxTokensPerStep)
+        return fail(SSD_ERR_SHAPE, "seqlen = %lld tokens per sequence out of range [0, %lld]",
+                    (long long)dims->seqlen, (long long)kMaxTokensPerStep);
+    s.T = dims->seqlen;
+    if ((double)s.Bt * (double)s.T * (double)s.H * 64.0 * (double)s.N * 4.0 > 0x1p50)
+        return fail(SSD_ERR_SHAPE, "batch * seqlen * nheads too large for 64-bit offsets");
+    if (flags & ~(uint32_t)SSD_DECODE_NO_STATE_UPDATE)
+        return fail(SSD_ERR_UNSUPPORTED, "flags = 0x%x; only SSD_DECODE_NO_STATE_UPDATE is defined",
+                    (unsigned)flags);
+    if ((r = check_opts(opts)) != SSD_OK) return r;
+    if (s.Bt > 0)
+        REQUIRE_PTR(state);
+    else
+        OPTIONAL_PTR(state);
+    if (s.Bt > 0 && s.T > 0) {
+        REQUIRE_PTR(x);
+        REQUIRE_PTR(dt);
+        REQUIRE_PTR(B);
+        REQUIRE_PTR(C);
+        REQUIRE_PTR(A);
+        REQUIRE_PTR(D);
+        REQUIRE_PTR(y);
+    } else {  // no tokens: the token tensors are empty and may be NULL
+        OPTIONAL_PTR(x);
+        OPTIONAL_PTR(dt);
+        OPTIONAL_PTR(B);
+        OPTIONAL_PTR(C);
+        OPTIONAL_PTR(A);
+        OPTIONAL_PTR(D);
+        OPTIONAL_PTR(y);
+    }
+    if (misaligned(snapshots)) return fail(SSD_ERR_ALIGN, "snapshots is not 16-byte aligned");
+    if (misaligned(parent)) return fail(SSD_ERR_ALIGN, "parent is not 16-byte aligned");
+    if (parent && !snapshots)
+        return fail(SSD_ERR_NULL, "parent needs the snapshots buffer (steps restart from it)");
+    if (s.Bt == 0 || s.T == 0) return ok();
+    ssd::MultiArgs m{state, x, dt, B, C, A, D, static_cast<float *>(y),
+                     opts ? opts->dt_bias : nullptr, opts ? opts->dt_softplus : 0,
+                     opts ? opts->z : nullptr, snapshots, parent,
+                     (flags & SSD_DECODE_NO_STATE_UPDATE) ? 0 : 1};
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    r = hip_result(ssd::launch_decode_multi(s, m, st), "decode_multi", st);
+    if (r != SSD_OK) return r;
+    return ok();
 }
 
 const char *ssd_status_string(ssd_status status) {

@@ -32,6 +32,23 @@ size_t state_fwd_bfrag_bytes(const Shape &s);
 hipError_t launch_state_fwd(const Shape &s, const void *x, const void *B, const float *Gws,
                             const float *DTws, const float *init, void *hprev, float *fin,
                             void *bfrag, int rows_per_block, hipStream_t st);
+// K = s.T tokens per sequence; snaps / parent NULL = none; update = 0 leaves
+// the state unwritten.
+struct MultiArgs {
+    float *state;
+    const void *x;
+    const float *dt;
+    const void *B, *C;
+    const float *A, *D;
+    float *y;
+    const float *dt_bias;
+    int softplus;
+    const void *z;
+    float *snaps;
+    const int32_t *parent;
+    int update;
+};
+hipError_t launch_decode_multi(const Shape &s, const MultiArgs &m, hipStream_t st);
 hipError_t launch_decode_step(const Shape &s, float *state, const void *x, const float *dt,
                               const void *B, const void *C, const float *A, const float *D,
                               void *y, const float *dt_bias, int softplus, const void *z,

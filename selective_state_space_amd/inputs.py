@@ -4,7 +4,7 @@ This module only draws random numbers and rounds them; it holds none of the
 scan's arithmetic. Both the GPU path's tests/bench and the CPU oracle take
 their inputs from here, so the two sides always see identical values.
 
-Recipe (the shapes and value distributions of the five workloads):
+Recipe (the shapes and value distributions of the six workloads):
 
 * ``A_h = -exp(U(ln 1, ln 16))`` per head (a negative decay rate, so that
   ``a_t = A dt_t <= 0``; "Accelerating Mamba-2 with High-Performance Forward
@@ -26,7 +26,8 @@ Recipe (the shapes and value distributions of the five workloads):
   and h0 (ids 1..5) are drawn in blocks of 2^22 elements, block k from
   ``default_rng([seed, id, k])``, so blocks can be drawn in parallel threads
   and the values do not depend on the thread count.  Decode step s uses the
-  ids 1000 + 8 s + (1, 2, 3, 4) for its x, z, B, C.
+  ids 1000 + 8 s + (1, 2, 3, 4) for its x, z, B, C; call c of a multi-token
+  decode with K tokens per sequence takes decode steps cK .. cK + K - 1.
 """
 
 from __future__ import annotations
@@ -73,7 +74,7 @@ class Workload:
         return dataclasses.replace(self, **kw)
 
 
-# The five workloads.  Index 0 is the tiny fp32 case, 1-3 forward layers, 4 decode.
+# Index 0 is the tiny fp32 case, 1-3 forward layers, 4 decode, 5 multi-token decode.
 WORKLOADS = [
     Workload("tiny_fp32", 1, 256, 4, 64, 64, 1, 64, F32,
              description="tiny SSD forward, fp32 throughout"),
@@ -86,6 +87,10 @@ WORKLOADS = [
              description="long-context hybrid-model layer, 128 heads, 8 groups, T=65536"),
     Workload("decode_b256", 256, 1, 128, 64, 128, 8, 256, BF16, kind="decode", steps=512,
              description="recurrent decode, batch 256, 128 heads, 8 groups, 512 steps"),
+    Workload("mtp_verify_b256_k4", 256, 4, 128, 64, 128, 8, 256, BF16, kind="decode_multi",
+             description="multi-token decode of speculative verification: 256 sequences x 4 "
+                         "tokens (seqlen = tokens per sequence), decode_b256's heads, a snapshot "
+                         "of the state after every token, main state not updated"),
 ]
 
 BY_NAME = {w.name: w for w in WORKLOADS}
@@ -237,6 +242,23 @@ def make_decode_step(w: Workload, step: int, prm: Params, seed: int = 0) -> Deco
     B = _normal((seed, base + 3), (Bt, G, N), s, bf16=bf)
     C = _normal((seed, base + 4), (Bt, G, N), s, bf16=bf)
     return DecodeInputs(x, dt, B, C)
+
+
+@dataclasses.dataclass
+class MultiInputs:
+    x: np.ndarray    # [Bt, K, H, P]
+    dt: np.ndarray   # [Bt, K, H]
+    B: np.ndarray    # [Bt, K, G, N]
+    C: np.ndarray    # [Bt, K, G, N]
+
+
+def make_decode_multi(w: Workload, prm: Params, call: int = 0, seed: int = 0) -> MultiInputs:
+    """Inputs of one multi-token decode call: K = w.seqlen tokens per sequence,
+    token k being decode step call * K + k of the same stream."""
+    K = w.seqlen
+    steps = [make_decode_step(w, call * K + k, prm, seed) for k in range(K)]
+    return MultiInputs(*(np.stack([getattr(s, f) for s in steps], axis=1)
+                         for f in ("x_t", "dt_t", "B_t", "C_t")))
 
 
 def make_small(Bt: int, T: int, H: int, P: int, N: int, G: int, io_dtype: str = F32,

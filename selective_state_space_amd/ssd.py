@@ -85,6 +85,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                   vp], st),
         "ssd_chunked_fwd_path": ([dp, i64, ctypes.POINTER(ctypes.c_int)], st),
         "ssd_decode_step": ([vp, vp, vp, vp, vp, vp, vp, vp, dp, vp], st),
+        "ssd_decode_multi": ([vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_uint32,
+                              ctypes.POINTER(LayerOpts), dp, vp], st),
         "ssd_status_string": ([st], ctypes.c_char_p),
         "ssd_last_error_detail": ([], ctypes.c_char_p),
         "ssd_version": ([], ctypes.c_int),
@@ -139,6 +141,13 @@ def _need(t: torch.Tensor, name: str, dtype: torch.dtype, shape, device) -> torc
     return t.contiguous()
 
 
+def _need_out(t: torch.Tensor, name: str, dtype: torch.dtype, shape, device) -> torch.Tensor:
+    """An output the library writes into: a contiguous copy would lose the result."""
+    if isinstance(t, torch.Tensor) and not t.is_contiguous():
+        raise ValueError("%s must be contiguous (the library writes into it)" % name)
+    return _need(t, name, dtype, shape, device)
+
+
 def fwd_dims(x: torch.Tensor, B: torch.Tensor) -> Dims:
     Bt, T, H, P = x.shape
     G, N = B.shape[2], B.shape[3]
@@ -179,9 +188,9 @@ class FwdArgs:
         self.init = None if init_state is None else _need(init_state, "init_state", torch.float32,
                                                          (Bt, H, P, N), dev)
         self.y = (torch.empty((Bt, T, H, P), dtype=torch.float32, device=dev) if y is None
-                  else _need(y, "y", torch.float32, (Bt, T, H, P), dev))
+                  else _need_out(y, "y", torch.float32, (Bt, T, H, P), dev))
         if final_state is not None:
-            self.final = _need(final_state, "final_state", torch.float32, (Bt, H, P, N), dev)
+            self.final = _need_out(final_state, "final_state", torch.float32, (Bt, H, P, N), dev)
         elif want_final:
             self.final = torch.empty((Bt, H, P, N), dtype=torch.float32, device=dev)
         else:
@@ -328,7 +337,7 @@ def ssd_decode_step(state, x_t, dt_t, B_t, C_t, A, D, y_t=None, dt_bias=None,
     A = _need(A, "A", torch.float32, (H,), dev)
     D = _need(D, "D", torch.float32, (H,), dev)
     y_t = (torch.empty((Bt, H, P), dtype=torch.float32, device=dev) if y_t is None
-           else _need(y_t, "y_t", torch.float32, (Bt, H, P), dev))
+           else _need_out(y_t, "y_t", torch.float32, (Bt, H, P), dev))
     dims = Dims(Bt, 1, H, P, N, G, _io_code(io))
     if dt_bias is not None:
         dt_bias = _need(dt_bias, "dt_bias", torch.float32, (H,), dev)
@@ -346,3 +355,55 @@ def ssd_decode_step(state, x_t, dt_t, B_t, C_t, A, D, y_t=None, dt_bias=None,
             _ptr(state), _ptr(x_t), _ptr(dt_t), _ptr(B_t), _ptr(C_t), _ptr(A), _ptr(D),
             _ptr(y_t), ctypes.byref(opts), ctypes.byref(dims), _stream(dev)))
     return y_t
+
+
+DECODE_NO_STATE_UPDATE = 1   # SSD_DECODE_NO_STATE_UPDATE
+
+
+def ssd_decode_multi(state, x, dt, B, C, A, D, y=None, snapshots=None, parent=None,
+                     update_state: bool = True, dt_bias=None, dt_softplus: bool = False, z=None):
+    """K decode steps per sequence (speculative decoding); returns (y, snapshots).
+
+    state [Bt,H,P,N] f32 (updated in place unless ``update_state`` is False),
+    x [Bt,K,H,P], dt [Bt,K,H] f32, B/C [Bt,K,G,N] (x's dtype), A/D [H] f32.
+    ``snapshots``: None (not written), True (allocated here) or a float32
+    [Bt,K,H,P,N] tensor that receives the state after every step.  ``parent``
+    [Bt,K] int32: step k restarts from the snapshot of step parent[b,k] when
+    0 <= parent[b,k] < k (needs snapshots).  y [Bt,K,H,P] f32.
+    """
+    dev = state.device
+    if dev.type != "cuda":
+        raise ValueError("tensors must live on a GPU device, got %s" % dev)
+    if not state.is_contiguous() or state.dtype != torch.float32 or state.dim() != 4:
+        raise ValueError("state must be a contiguous float32 [Bt,H,P,N] tensor")
+    Bt, H, P, N = state.shape
+    if x.dim() != 4 or B.dim() != 4:
+        raise ValueError("x must be [Bt,K,H,P] and B, C [Bt,K,G,N]")
+    io = x.dtype
+    K, G = x.shape[1], B.shape[2]
+    x = _need(x, "x", io, (Bt, K, H, P), dev)
+    dt = _need(dt, "dt", torch.float32, (Bt, K, H), dev)
+    B = _need(B, "B", io, (Bt, K, G, N), dev)
+    C = _need(C, "C", io, (Bt, K, G, N), dev)
+    A = _need(A, "A", torch.float32, (H,), dev)
+    D = _need(D, "D", torch.float32, (H,), dev)
+    y = (torch.empty((Bt, K, H, P), dtype=torch.float32, device=dev) if y is None
+         else _need_out(y, "y", torch.float32, (Bt, K, H, P), dev))
+    if snapshots is True:
+        snapshots = torch.empty((Bt, K, H, P, N), dtype=torch.float32, device=dev)
+    elif snapshots is not None:
+        snapshots = _need_out(snapshots, "snapshots", torch.float32, (Bt, K, H, P, N), dev)
+    if parent is not None:
+        parent = _need(parent, "parent", torch.int32, (Bt, K), dev)
+    if dt_bias is not None:
+        dt_bias = _need(dt_bias, "dt_bias", torch.float32, (H,), dev)
+    if z is not None:
+        z = _need(z, "z", io, (Bt, K, H, P), dev)
+    opts = _layer_opts(dt_bias, dt_softplus, z)
+    dims = Dims(Bt, K, H, P, N, G, _io_code(io))
+    flags = 0 if update_state else DECODE_NO_STATE_UPDATE
+    _check("ssd_decode_multi", load_library().ssd_decode_multi(
+        _ptr(state), _ptr(x), _ptr(dt), _ptr(B), _ptr(C), _ptr(A), _ptr(D), _ptr(y),
+        _ptr(snapshots), _ptr(parent), flags, None if opts is None else ctypes.byref(opts),
+        ctypes.byref(dims), _stream(dev)))
+    return y, snapshots

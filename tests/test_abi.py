@@ -223,3 +223,35 @@ def test_layer_opts_are_validated():
     # NULL options fall through to the usual validation (short workspace)
     assert L.ssd_chunked_fwd_opts(P16, P16, P16, P16, P16, P16, 256, None, P16, None, None,
                                   ctypes.byref(d), P16, 10, None) == -5
+
+
+def multi(d, snaps=P16, parent=None, flags=0, opts=None, y=P16, state=P16):
+    return lib().ssd_decode_multi(state, P16, P16, P16, P16, P16, P16, y, snaps, parent, flags,
+                                  opts, ctypes.byref(d), None)
+
+
+def test_decode_multi_is_validated():
+    L = lib()
+    d = dims(T=4)
+    assert multi(d, flags=2) == -3
+    assert "flags" in L.ssd_last_error_detail().decode()
+    assert multi(d, snaps=None, parent=P16) == -1
+    assert "parent" in L.ssd_last_error_detail().decode()
+    assert multi(d, snaps=P_MIS) == -4
+    assert multi(d, parent=P_MIS) == -4
+    assert multi(d, y=None) == -1
+    assert multi(d, state=P_MIS) == -4
+    assert multi(dims(T=-1)) == -2
+    assert multi(dims(T=(1 << 16) + 1)) == -2
+    assert multi(dims(Bt=1 << 30, T=1 << 16, H=1 << 10, G=1)) == -2
+    assert multi(dims(N=96, T=4)) == -3
+    bad = ssd.LayerOpts(None, 0, 1, None)
+    assert multi(d, opts=ctypes.byref(bad)) == -3
+    # nothing to do: no HIP call is made, so these succeed without a GPU
+    assert multi(dims(T=0)) == 0
+    assert multi(dims(Bt=0, T=4)) == 0
+    assert multi(dims(T=0), snaps=None, flags=1) == 0
+    assert lib().ssd_decode_multi(P16, None, None, None, None, None, None, None, None, None, 0,
+                                  None, ctypes.byref(dims(T=0)), None) == 0
+    assert lib().ssd_decode_multi(None, None, None, None, None, None, None, None, None, None, 0,
+                                  None, ctypes.byref(dims(T=0)), None) == -1   # state
