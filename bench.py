@@ -263,6 +263,52 @@ def run_decode_multi(w, steps: int, warmup: int):
     return out
 
 
+def lowp_bytes(w, fmt: str, io_bytes=2):
+    """Algorithmic HBM bytes of one decode step on a 16-bit state."""
+    Bt, H, P, N, G = w.batch, w.nheads, w.headdim, w.dstate, w.ngroups
+    st = Bt * H * P * N * 2 * 2 + (Bt * H * P * 4 * 2 if fmt == "int16" else 0)
+    return st + Bt * (H * P * io_bytes + H * 4 + 2 * G * N * io_bytes + H * P * 4)
+
+
+def run_decode_lowp(w, steps: int, warmup: int):
+    """The decode step on decode_b256 with the state stored at 16 bits:
+    median per-step milliseconds for each format."""
+    import torch
+    from selective_state_space_amd import inputs as gen
+    from selective_state_space_amd import ssd
+
+    dev = torch.device("cuda:0")
+    prm = gen.decode_params(w, 0)
+    s = gen.make_decode_step(w, 0, prm, 0)
+
+    def up(a, dt=torch.float32):
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dt).to(dev)
+
+    args = (up(s.x_t, torch.bfloat16), up(s.dt_t), up(s.B_t, torch.bfloat16),
+            up(s.C_t, torch.bfloat16), up(prm.A), up(prm.D))
+    y = torch.empty((w.batch, w.nheads, w.headdim), dtype=torch.float32, device=dev)
+    out = {}
+    for name, fmt, stoch in (("f16", "f16", False), ("f16_stochastic", "f16", True),
+                             ("bf16", "bf16", False), ("int16", "int16", False)):
+        state = torch.zeros((w.batch, w.nheads, w.headdim, w.dstate),
+                            dtype=ssd.STATE_DTYPES[fmt][1], device=dev)
+        scale = (torch.zeros((w.batch, w.nheads, w.headdim), device=dev) if fmt == "int16"
+                 else None)
+        for k in range(warmup):
+            ssd.ssd_decode_step_lp(state, *args, fmt, scale=scale, philox_rounds=10 * stoch, seed=k, y_t=y)
+        torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+        ev[0].record()
+        for k in range(steps):
+            ssd.ssd_decode_step_lp(state, *args, fmt, scale=scale, philox_rounds=10 * stoch, seed=k, y_t=y)
+            ev[k + 1].record()
+        torch.cuda.synchronize()
+        out[name] = float(np.median([ev[k].elapsed_time(ev[k + 1]) for k in range(steps)]))
+        del state, scale
+    torch.cuda.empty_cache()
+    return out
+
+
 def run_layer_interface(w, wd, steps: int, warmup: int):
     """The forward and decode step with every layer option on (dt_bias,
     softplus, the z gate).  The raw steps are the inverse softplus of the
@@ -465,6 +511,18 @@ def main():
                                alg_bytes_per_call=int(byt), snapshots=snap, state_update=upd)
             log("multi-token decode (%s): %.1f us/call, %.0f GB/s"
                 % (mode, ms[mode] * 1e3, multi[mode]["GBps"]))
+    lowp = None
+    if not args.no_decode:
+        wd = gen.WORKLOADS[4]
+        ms = run_decode_lowp(wd, 30, 5)
+        lowp = {"workload": wd.name}
+        for name, v in ms.items():
+            byt = lowp_bytes(wd, "int16" if name == "int16" else "f16")
+            lowp[name] = dict(us_per_step=round(v * 1e3, 2),
+                              GBps=round(byt / (v * 1e-3) / 1e9, 1),
+                              hbm_frac=round(byt / (v * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+                              alg_bytes_per_step=int(byt))
+            log("decode, %s state: %.1f us/step, %.0f GB/s" % (name, v * 1e3, lowp[name]["GBps"]))
     layer = None
     if not args.no_decode:
         wd = gen.WORKLOADS[4]
@@ -518,6 +576,7 @@ def main():
         "kernels": kernels,
         "decode": decode,
         "decode_multi": multi,
+        "decode_lowp_state": lowp,
         "layer_interface": layer,
         "hbm_copy_reference_GBps": round(copy_gbps, 1),
         "wall_s_timed": round(wall, 4),

@@ -271,6 +271,55 @@ ssd_status ssd_decode_multi(float *state, const void *x, const float *dt, const 
                             float *snapshots, const int32_t *parent, uint32_t flags,
                             const ssd_layer_opts *opts, const ssd_dims *dims, void *stream);
 
+/*
+ * The decode state kept at 16 bits per element ("Optimizing Nemotron v3
+ * Super in TensorRT-LLM", section 6.5, and the state types of section 6.6):
+ *   SSD_STATE_F16    fp16; round to nearest even, or, with philox_rounds in
+ *                    1..10, stochastic rounding: |x| + (r / 2^13) ulp16(|x|)
+ *                    rounded toward zero and saturated at 65504, r the low 13
+ *                    bits of a word of Philox-4x32 with that many rounds (10
+ *                    is the generator's standard; Salmon et al., SC'11): one block
+ *                    per 4 consecutive elements of a row, counter = flat index
+ *                    (b, h, p, n) of the first (low word, high word, 0, 0),
+ *                    key = seed (low word, high word); element n takes word
+ *                    n mod 4.  Vary the seed from call to call.
+ *   SSD_STATE_BF16   bf16, round to nearest even.
+ *   SSD_STATE_INT16  int16 codes plus one fp32 decode scale per row (b, h, p)
+ *                    in `scale` [Bt, H, P]: the stored value is code * scale;
+ *                    after the update, encode = 32767 / max|row| and scale =
+ *                    1 / encode (fp32 divisions), code = round-half-even(x *
+ *                    encode); an all-zero row stores codes 0 and scale 0.
+ *   SSD_STATE_F32    the fp32 state of ssd_decode_step.
+ * philox_rounds must be 0 except for SSD_STATE_F16; scale is required for
+ * SSD_STATE_INT16 and must be NULL otherwise (SSD_ERR_UNSUPPORTED / _NULL).
+ */
+typedef enum {
+    SSD_STATE_F32 = 0,
+    SSD_STATE_F16 = 1,
+    SSD_STATE_BF16 = 2,
+    SSD_STATE_INT16 = 3
+} ssd_state_dtype;
+
+typedef struct {
+    int32_t dtype;        /* ssd_state_dtype */
+    int32_t philox_rounds; /* SSD_STATE_F16 only: 0 = nearest, 1..10 = stochastic */
+    uint64_t seed;        /* Philox key for stochastic rounding */
+    float *scale;         /* SSD_STATE_INT16: [Bt, H, P] decode scales, in/out */
+} ssd_state_format;
+
+/*
+ * ssd_decode_step on a state stored as *fmt says: the stored state is decoded
+ * to fp32, updated and y computed exactly as in ssd_decode_step (y from the
+ * updated fp32 state), and the new state stored back in the same format, in
+ * place.  state is [Bt, H, P, N] of 16-bit elements (fp32 for
+ * SSD_STATE_F32).  Other arguments, options and errors as for
+ * ssd_decode_step_opts.
+ */
+ssd_status ssd_decode_step_lp(void *state, const ssd_state_format *fmt, const void *x_t,
+                              const float *dt_t, const void *B_t, const void *C_t, const float *A,
+                              const float *D, void *y_t, const ssd_layer_opts *opts,
+                              const ssd_dims *dims, void *stream);
+
 /* Static text for a status code. */
 const char *ssd_status_string(ssd_status status);
 

@@ -9,7 +9,8 @@
   beside them;
 * fp16, rounded to nearest or stochastically, with the random bits taken
   from a Philox-4x32 counter-based generator (13 bits per element: the bits
-  fp32 carries below fp16's last place);
+  fp32 carries below fp16's last place) whose round count is a parameter of
+  the kernels (zero rounds meaning no stochastic rounding);
 * and, as the same section's dispatch table lists, bf16 (round to nearest).
 
 The update itself is the plain fp64 decode step of the oracle (section 6.1)
@@ -22,7 +23,8 @@ Philox-4x32 follows its published definition (J. K. Salmon, M. A. Moraes,
 R. O. Dror, D. E. Shaw, "Parallel Random Numbers: As Easy as 1, 2, 3", SC'11,
 section 5): per round, two 32x32 -> 64-bit products of counter words with
 the multipliers 0xD2511F53 and 0xCD9E8D57, a swap-and-xor with the key, and a
-Weyl increment of the key by (0x9E3779B9, 0xBB67AE85); 10 rounds.
+Weyl increment of the key by (0x9E3779B9, 0xBB67AE85); 10 rounds is the
+generator's standard count.
 
 Readings (listed with the others in the design notes): the abs-max is over
 the N values of a row; codes round half to even and are clipped to
@@ -66,7 +68,7 @@ def philox4x32(counter, key, rounds: int = 10):
     return np.stack(c, axis=-1).astype(np.uint32)
 
 
-def state_random_bits(nelem: int, seed: int, start: int = 0):
+def state_random_bits(nelem: int, seed: int, start: int = 0, rounds: int = 10):
     """13 random bits for the state elements of flat indices start ..
     start + nelem - 1 (start a multiple of 4), from one Philox block per 4
     consecutive elements."""
@@ -75,7 +77,7 @@ def state_random_bits(nelem: int, seed: int, start: int = 0):
     ctr = np.stack([first & np.uint64(MASK32), first >> np.uint64(32),
                     np.zeros_like(first), np.zeros_like(first)], axis=-1)
     key = np.array([seed & MASK32, (seed >> 32) & MASK32], dtype=np.uint64)
-    words = philox4x32(ctr, key)                       # [nelem/4, 4]
+    words = philox4x32(ctr, key, rounds)               # [nelem/4, 4]
     return (words.reshape(-1)[:nelem] & np.uint32(0x1FFF)).astype(np.int64)
 
 
@@ -143,20 +145,22 @@ def dequantize_rows_int16(codes, dec):
             ).astype(np.float32)
 
 
-def encode_state(v, fmt: str, seed: int = 0, stochastic: bool = False, N: Optional[int] = None):
+def encode_state(v, fmt: str, seed: int = 0, philox_rounds: int = 0, start: int = 0):
     """fp64 state [..., N] -> (stored values as float64, int16 scales or None).
     For INT16 the stored values are the decoded fp32 values of the codes and
-    the second result is (codes, decode scales)."""
+    the second result is (codes, decode scales).  ``start`` is the flat index
+    of v's first element in the whole state (the Philox counter); fp16 is
+    rounded stochastically when philox_rounds > 0."""
     v32 = np.asarray(v, dtype=np.float64).astype(np.float32)
     if fmt == F32:
         return v32.astype(np.float64), None
     if fmt == BF16:
         return round_bf16_nearest(v32), None
     if fmt == F16:
-        if not stochastic:
+        if philox_rounds <= 0:
             return round_f16_nearest(v32), None
         flat = v32.reshape(-1)
-        r = state_random_bits(flat.size, seed)
+        r = state_random_bits(flat.size, seed, start, philox_rounds)
         return round_f16_stochastic(flat, r).reshape(v32.shape), None
     if fmt == INT16:
         codes, dec = quantize_rows_int16(v32)
@@ -165,20 +169,32 @@ def encode_state(v, fmt: str, seed: int = 0, stochastic: bool = False, N: Option
 
 
 def decode_step_lowp(state, x_t, dt_t, B_t, C_t, A, D, fmt: str, seed: int = 0,
-                     stochastic: bool = False, dt_bias=None, dt_softplus: bool = False,
-                     z_t=None):
+                     philox_rounds: int = 0, dt_bias=None, dt_softplus: bool = False,
+                     z_t=None, pairs: Optional[Sequence[int]] = None):
     """One decode step on a state stored in ``fmt``.
 
-    ``state`` [Bt,H,P,N] float64 holds the values the stored state decodes to
-    (for INT16: codes times decode scales, one fp32 product).  The step is
-    the oracle's fp64 decode step on those values; the new state is then
-    encoded as the format stores it (Philox key = ``seed`` when stochastic).
-    Returns (y [Bt,H,P] from the unrounded new state, new stored values
-    [Bt,H,P,N] float64, (codes, scales) for INT16 else None)."""
+    ``state`` [Bt,H,P,N] (or [npairs,P,N] for the (b, h) pairs b*H+h listed
+    in ``pairs``) float64 holds the values the stored state decodes to (for
+    INT16: codes times decode scales, one fp32 product).  The step is the
+    oracle's fp64 decode step on those values; the new state is then encoded
+    as the format stores it (fp16 stochastically when ``philox_rounds`` > 0,
+    Philox key = ``seed``, counters
+    from each element's flat index in the whole [Bt,H,P,N] state).
+    Returns (y [Bt,H,P] or [npairs,P] from the unrounded new state, new
+    stored values shaped like ``state``, (codes, scales) for INT16 else None)."""
     from . import token_decode
-    Bt, H, P, N = state.shape
-    run = np.ascontiguousarray(state, dtype=np.float64).reshape(Bt * H, P, N).copy()
-    y = token_decode(run, x_t, dt_t, B_t, C_t, A, D, dt_bias=dt_bias,
+    P, N = state.shape[-2], state.shape[-1]
+    run = np.ascontiguousarray(state, dtype=np.float64).reshape(-1, P, N).copy()
+    y = token_decode(run, x_t, dt_t, B_t, C_t, A, D, pairs=pairs, dt_bias=dt_bias,
                      dt_softplus=dt_softplus, z_t=z_t)
-    stored, extra = encode_state(run.reshape(Bt, H, P, N), fmt, seed, stochastic)
-    return y.reshape(Bt, H, P), stored, extra
+    idx = range(run.shape[0]) if pairs is None else pairs
+    stored = np.empty_like(run)
+    codes = np.empty(run.shape, np.int16) if fmt == INT16 else None
+    scales = np.empty(run.shape[:2], np.float32) if fmt == INT16 else None
+    for i, pr in enumerate(idx):
+        stored[i], extra = encode_state(run[i], fmt, seed, philox_rounds, start=int(pr) * P * N)
+        if extra is not None:
+            codes[i], scales[i] = extra
+    shape = state.shape
+    return (y.reshape(shape[:-1]), stored.reshape(shape),
+            None if codes is None else (codes.reshape(shape), scales.reshape(shape[:-1])))

@@ -23,7 +23,7 @@ ARCH = "gfx950"
 
 SOURCES = ["chunk_cumsum.hip", "chunk_state.hip", "state_passing.hip", "state_fwd.hip",
            "chunk_scan.hip",
-           "decode_step.hip", "ssd_api.cpp"]
+           "decode_step.hip", "decode_lowp.hip", "ssd_api.cpp"]
 
 # -packed-fp32-ops: keep the compiler from emitting packed fp32 VALU ops.
 FLAGS = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=" + ARCH, "-Wall",

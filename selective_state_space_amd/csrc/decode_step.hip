@@ -32,20 +32,6 @@ namespace ssd {
 
 namespace {
 
-template <typename Tio>
-__device__ __forceinline__ float4 load4(const Tio *p);
-template <>
-__device__ __forceinline__ float4 load4<float>(const float *p) {
-    return *reinterpret_cast<const float4 *>(p);
-}
-template <>
-__device__ __forceinline__ float4 load4<uint16_t>(const uint16_t *p) {
-    const uint2 v = *reinterpret_cast<const uint2 *>(p);
-    return make_float4(bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y));
-}
-__device__ __forceinline__ float load1(const float *p) { return *p; }
-__device__ __forceinline__ float load1(const uint16_t *p) { return bf16_to_f32(*p); }
-
 template <int N, typename Tio, bool GATE>
 __global__ __launch_bounds__(256) void decode_step_kernel(
     float *__restrict__ state, const Tio *__restrict__ x, const float *__restrict__ dt,

@@ -472,6 +472,52 @@ ssd_status ssd_decode_multi(float *state, const void *x, const float *dt, const 
     return ok();
 }
 
+ssd_status ssd_decode_step_lp(void *state, const ssd_state_format *fmt, const void *x_t,
+                              const float *dt_t, const void *B_t, const void *C_t, const float *A,
+                              const float *D, void *y_t, const ssd_layer_opts *opts,
+                              const ssd_dims *dims, void *stream) {
+    if (!fmt) return fail(SSD_ERR_NULL, "fmt is NULL");
+    const int32_t f = fmt->dtype;
+    if (f != SSD_STATE_F32 && f != SSD_STATE_F16 && f != SSD_STATE_BF16 && f != SSD_STATE_INT16)
+        return fail(SSD_ERR_UNSUPPORTED, "state dtype = %d; only SSD_STATE_F32/F16/BF16/INT16",
+                    (int)f);
+    if (fmt->philox_rounds != 0 &&
+        (fmt->philox_rounds < 1 || fmt->philox_rounds > 10 || f != SSD_STATE_F16))
+        return fail(SSD_ERR_UNSUPPORTED,
+                    "philox_rounds = %d; 1..10 (stochastic rounding) for SSD_STATE_F16 only",
+                    (int)fmt->philox_rounds);
+    if (f == SSD_STATE_INT16 && !fmt->scale)
+        return fail(SSD_ERR_NULL, "fmt->scale is NULL (SSD_STATE_INT16 needs its row scales)");
+    if (f != SSD_STATE_INT16 && fmt->scale)
+        return fail(SSD_ERR_UNSUPPORTED, "fmt->scale is only used by SSD_STATE_INT16");
+    if (misaligned(fmt->scale)) return fail(SSD_ERR_ALIGN, "fmt->scale is not 16-byte aligned");
+    if (f == SSD_STATE_F32)
+        return ssd_decode_step_opts(static_cast<float *>(state), x_t, dt_t, B_t, C_t, A, D, y_t,
+                                    opts, dims, stream);
+    ssd::Shape s;
+    ssd_status r = check_dims(dims, 0, false, &s);
+    if (r != SSD_OK) return r;
+    if ((r = check_opts(opts)) != SSD_OK) return r;
+    REQUIRE_PTR(state);
+    REQUIRE_PTR(x_t);
+    REQUIRE_PTR(dt_t);
+    REQUIRE_PTR(B_t);
+    REQUIRE_PTR(C_t);
+    REQUIRE_PTR(A);
+    REQUIRE_PTR(D);
+    REQUIRE_PTR(y_t);
+    if (s.Bt == 0) return ok();
+    const int lf = f == SSD_STATE_F16 ? ssd::LOWP_F16
+                                      : (f == SSD_STATE_BF16 ? ssd::LOWP_BF16 : ssd::LOWP_INT16);
+    ssd::LowpArgs a{state, fmt->scale, lf, (int)fmt->philox_rounds, fmt->seed, x_t, dt_t, B_t, C_t,
+                    A, D, static_cast<float *>(y_t), opts ? opts->dt_bias : nullptr,
+                    opts ? opts->dt_softplus : 0, opts ? opts->z : nullptr};
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    r = hip_result(ssd::launch_decode_lowp(s, a, st), "decode_lowp", st);
+    if (r != SSD_OK) return r;
+    return ok();
+}
+
 const char *ssd_status_string(ssd_status status) {
     switch (status) {
     case SSD_OK: return "SSD_OK";

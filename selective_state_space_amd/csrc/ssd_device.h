@@ -61,6 +61,21 @@ __device__ __forceinline__ void store_nt(uint16_t *p, uint2 v) {
 // 2^x on the transcendental unit (v_exp_f32).
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// 4 (or 1) io-dtype values as fp32: float, or bf16 carried as uint16_t.
+template <typename Tio>
+__device__ __forceinline__ float4 load4(const Tio *p);
+template <>
+__device__ __forceinline__ float4 load4<float>(const float *p) {
+    return *reinterpret_cast<const float4 *>(p);
+}
+template <>
+__device__ __forceinline__ float4 load4<uint16_t>(const uint16_t *p) {
+    const uint2 v = *reinterpret_cast<const uint2 *>(p);
+    return make_float4(bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y));
+}
+__device__ __forceinline__ float load1(const float *p) { return *p; }
+__device__ __forceinline__ float load1(const uint16_t *p) { return bf16_to_f32(*p); }
+
 // silu(z) = z / (1 + e^-z) on the transcendental unit: e^-z as 2^(-z log2 e),
 // then v_rcp_f32.  Both limits come out right: z -> -inf gives 1/inf = 0 and
 // z -> +inf gives z * 1.

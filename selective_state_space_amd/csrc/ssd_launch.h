@@ -49,6 +49,25 @@ struct MultiArgs {
     int update;
 };
 hipError_t launch_decode_multi(const Shape &s, const MultiArgs &m, hipStream_t st);
+// The decode step on a 16-bit state (fp16 nearest or stochastic, bf16, or
+// int16 codes with per-row decode scales in `scale`).
+enum LowpFormat { LOWP_F16 = 1, LOWP_BF16 = 2, LOWP_INT16 = 3 };
+struct LowpArgs {
+    void *state;
+    float *scale;
+    int format;
+    int philox_rounds;   // fp16: > 0 = stochastic rounding with that many rounds
+    uint64_t seed;
+    const void *x;
+    const float *dt;
+    const void *B, *C;
+    const float *A, *D;
+    float *y;
+    const float *dt_bias;
+    int softplus;
+    const void *z;
+};
+hipError_t launch_decode_lowp(const Shape &s, const LowpArgs &a, hipStream_t st);
 hipError_t launch_decode_step(const Shape &s, float *state, const void *x, const float *dt,
                               const void *B, const void *C, const float *A, const float *D,
                               void *y, const float *dt_bias, int softplus, const void *z,

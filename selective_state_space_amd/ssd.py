@@ -50,6 +50,16 @@ class Dims(ctypes.Structure):
                 ("io_dtype", ctypes.c_int32)]
 
 
+class StateFormat(ctypes.Structure):
+    """ssd_state_format."""
+    _fields_ = [("dtype", ctypes.c_int32), ("philox_rounds", ctypes.c_int32),
+                ("seed", ctypes.c_uint64), ("scale", ctypes.c_void_p)]
+
+
+STATE_DTYPES = {"f32": (0, torch.float32), "f16": (1, torch.float16), "bf16": (2, torch.bfloat16),
+                "int16": (3, torch.int16)}
+
+
 class LayerOpts(ctypes.Structure):
     """ssd_layer_opts: dt_bias [H] f32 (or NULL), dt_softplus, reserved = 0, z (or NULL)."""
     _fields_ = [("dt_bias", ctypes.c_void_p), ("dt_softplus", ctypes.c_int32),
@@ -87,6 +97,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "ssd_decode_step": ([vp, vp, vp, vp, vp, vp, vp, vp, dp, vp], st),
         "ssd_decode_multi": ([vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_uint32,
                               ctypes.POINTER(LayerOpts), dp, vp], st),
+        "ssd_decode_step_lp": ([vp, ctypes.POINTER(StateFormat), vp, vp, vp, vp, vp, vp, vp,
+                                ctypes.POINTER(LayerOpts), dp, vp], st),
         "ssd_status_string": ([st], ctypes.c_char_p),
         "ssd_last_error_detail": ([], ctypes.c_char_p),
         "ssd_version": ([], ctypes.c_int),
@@ -407,3 +419,48 @@ def ssd_decode_multi(state, x, dt, B, C, A, D, y=None, snapshots=None, parent=No
         _ptr(snapshots), _ptr(parent), flags, None if opts is None else ctypes.byref(opts),
         ctypes.byref(dims), _stream(dev)))
     return y, snapshots
+
+
+def ssd_decode_step_lp(state, x_t, dt_t, B_t, C_t, A, D, fmt: str, scale=None,
+                       philox_rounds: int = 0, seed: int = 0, y_t=None, dt_bias=None,
+                       dt_softplus: bool = False, z_t=None):
+    """One decode step on a 16-bit state (``fmt`` "f16", "bf16" or "int16"; "f32"
+    is the plain step), updated in place.  state [Bt,H,P,N] of fp16 / bf16 /
+    int16; ``scale`` [Bt,H,P] f32 decode scales (int16 only, updated in place);
+    ``philox_rounds`` > 0 (10 is standard) and ``seed`` select fp16
+    stochastic rounding.  Returns y_t
+    [Bt,H,P] f32."""
+    if fmt not in STATE_DTYPES:
+        raise ValueError("fmt must be one of %s" % sorted(STATE_DTYPES))
+    code, sdt = STATE_DTYPES[fmt]
+    dev = state.device
+    if dev.type != "cuda":
+        raise ValueError("tensors must live on a GPU device, got %s" % dev)
+    if not state.is_contiguous() or state.dtype != sdt or state.dim() != 4:
+        raise ValueError("state must be a contiguous %s [Bt,H,P,N] tensor" % sdt)
+    Bt, H, P, N = state.shape
+    io = x_t.dtype
+    G = B_t.shape[1]
+    x_t = _need(x_t, "x_t", io, (Bt, H, P), dev)
+    dt_t = _need(dt_t, "dt_t", torch.float32, (Bt, H), dev)
+    B_t = _need(B_t, "B_t", io, (Bt, G, N), dev)
+    C_t = _need(C_t, "C_t", io, (Bt, G, N), dev)
+    A = _need(A, "A", torch.float32, (H,), dev)
+    D = _need(D, "D", torch.float32, (H,), dev)
+    y_t = (torch.empty((Bt, H, P), dtype=torch.float32, device=dev) if y_t is None
+           else _need_out(y_t, "y_t", torch.float32, (Bt, H, P), dev))
+    if scale is not None:
+        scale = _need_out(scale, "scale", torch.float32, (Bt, H, P), dev)
+    if dt_bias is not None:
+        dt_bias = _need(dt_bias, "dt_bias", torch.float32, (H,), dev)
+    if z_t is not None:
+        z_t = _need(z_t, "z_t", io, (Bt, H, P), dev)
+    f = StateFormat(code, int(philox_rounds), int(seed) & 0xFFFFFFFFFFFFFFFF,
+                    None if scale is None else scale.data_ptr())
+    opts = _layer_opts(dt_bias, dt_softplus, z_t)
+    dims = Dims(Bt, 1, H, P, N, G, _io_code(io))
+    _check("ssd_decode_step_lp", load_library().ssd_decode_step_lp(
+        _ptr(state), ctypes.byref(f), _ptr(x_t), _ptr(dt_t), _ptr(B_t), _ptr(C_t), _ptr(A),
+        _ptr(D), _ptr(y_t), None if opts is None else ctypes.byref(opts), ctypes.byref(dims),
+        _stream(dev)))
+    return y_t

@@ -255,3 +255,29 @@ def test_decode_multi_is_validated():
                                   None, ctypes.byref(dims(T=0)), None) == 0
     assert lib().ssd_decode_multi(None, None, None, None, None, None, None, None, None, None, 0,
                                   None, ctypes.byref(dims(T=0)), None) == -1   # state
+
+
+def lp(fmt, d=None, state=P16, y=P16):
+    d = d or dims(T=1)
+    f = None if fmt is None else ctypes.byref(fmt)
+    return lib().ssd_decode_step_lp(state, f, P16, P16, P16, P16, P16, P16, y, None,
+                                    ctypes.byref(d), None)
+
+
+def test_decode_step_lp_is_validated():
+    L = lib()
+    SF = ssd.StateFormat
+    assert lp(None) == -1
+    assert lp(SF(7, 0, 0, None)) == -3
+    assert lp(SF(2, 10, 0, None)) == -3                     # stochastic bf16
+    assert lp(SF(1, 11, 0, None)) == -3                     # 0..10 rounds
+    assert lp(SF(1, -1, 0, None)) == -3
+    assert lp(SF(3, 0, 0, None)) == -1                      # int16 without scales
+    assert "scale" in L.ssd_last_error_detail().decode()
+    assert lp(SF(1, 0, 0, 0x1000)) == -3                    # scales on an fp16 state
+    assert lp(SF(3, 0, 0, 0x1004)) == -4
+    assert lp(SF(3, 0, 0, 0x1000), state=P_MIS) == -4
+    assert lp(SF(1, 1, 5, None), y=None) == -1
+    assert lp(SF(1, 1, 5, None), d=dims(N=96)) == -3
+    assert lp(SF(0, 0, 0, None), state=None) == -1          # fp32: the plain step's checks
+    assert lp(SF(3, 0, 0, 0x1000), d=dims(Bt=0)) == 0       # empty batch: no HIP call

@@ -130,7 +130,7 @@ def test_encode_formats():
     np.testing.assert_array_equal(s32, v.astype(np.float32))
     s16, _ = sf.encode_state(v, sf.F16)
     np.testing.assert_array_equal(s16, v.astype(np.float32).astype(np.float16))
-    sr, _ = sf.encode_state(v, sf.F16, seed=7, stochastic=True)
+    sr, _ = sf.encode_state(v, sf.F16, seed=7, philox_rounds=10)
     assert np.all(np.abs(sr - v) <= sf._ulp16(np.abs(v)) * (1 + 1e-9))
     si, (codes, dec) = sf.encode_state(v, sf.INT16)
     np.testing.assert_array_equal(si, codes.astype(np.float32) * dec[..., None])
@@ -148,3 +148,21 @@ def test_lowp_step_f32_is_the_plain_step():
     yr = oracle.token_decode(ref, x, dt, B, C, A, D)
     np.testing.assert_array_equal(y.reshape(-1, P), yr)
     np.testing.assert_array_equal(new.reshape(ref.shape), ref.astype(np.float32))
+
+
+@pytest.mark.parametrize("fmt,stoch", [(sf.F16, True), (sf.INT16, False), (sf.BF16, False)])
+def test_lowp_step_pair_subset_equals_full(fmt, stoch):
+    rng = np.random.default_rng(4)
+    Bt, H, P, N, G = 3, 4, 8, 16, 2
+    st, _ = sf.encode_state(rng.normal(0, 0.3, (Bt, H, P, N)), fmt)
+    x = rng.normal(0, 1, (Bt, H, P)); dt = rng.uniform(0.01, 0.2, (Bt, H))
+    B = rng.normal(0, 0.3, (Bt, G, N)); C = rng.normal(0, 0.3, (Bt, G, N))
+    A = -rng.uniform(0.5, 4, H); D = rng.normal(0, 1, H)
+    y, new, ex = sf.decode_step_lowp(st, x, dt, B, C, A, D, fmt, seed=99, philox_rounds=10 * stoch)
+    pr = [11, 0, 5]
+    ys, news, exs = sf.decode_step_lowp(st.reshape(-1, P, N)[pr], x, dt, B, C, A, D, fmt,
+                                        seed=99, philox_rounds=10 * stoch, pairs=pr)
+    np.testing.assert_array_equal(ys, y.reshape(-1, P)[pr])
+    np.testing.assert_array_equal(news, new.reshape(-1, P, N)[pr])
+    if ex is not None:
+        np.testing.assert_array_equal(exs[0], ex[0].reshape(-1, P, N)[pr])
