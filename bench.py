@@ -118,6 +118,103 @@ def measured_traffic(kernel: str, workload: str):
     return int(k["hbm_bytes_per_launch"])
 
 
+PROFILE_CMD = "python3 bench.py --steps 10 --warmup 3 --no-cpu-baseline --no-decode"
+
+
+def profile_kind(name: str):
+    """The algorithmic-bytes entry of a forward kernel's (demangled) name; None
+    for every other kernel (the gated chunk_scan included)."""
+    if "chunk_scan_bf16_kernel" in name:
+        args = name[name.index("<") + 1:name.index(">")].split(",")
+        return "chunk_scan" if args[-1].strip() == "false" else None
+    for k in ("chunk_cumsum", "chunk_state", "state_passing", "b_fragments", "state_fwd"):
+        if k + "_kernel" in name:
+            return "state_fwd_kernel" if k == "state_fwd" else k
+    return None
+
+
+def summarize_rocprof(pdir: str, workload: str):
+    """Writes profiles/kernel_trace_<workload>.md and profiles/traffic_<workload>.{md,json}
+    from a rocprofv3 output directory holding trace/ (kernel trace of the
+    default bench run), fetch/ and write/ (one counter each over PROFILE_CMD)
+    and copyf/ and copyw/ (the same counters over --copy-reference-only)."""
+    import collections
+    import csv
+    import re
+    from selective_state_space_amd import inputs as gen
+
+    def short(n):
+        n = n.replace("ssd::(anonymous namespace)::", "").replace("void ", "")
+        return re.sub(r"\(.*", "", n).replace("unsigned short", "bf16")
+
+    rows = list(csv.DictReader(open(os.path.join(pdir, "trace", "trace_kernel_stats.csv"))))
+    out = ["# Kernel trace: %s forward, decode legs and copy reference" % workload, "",
+           "Command (from the repo root, on one MI355X):", "",
+           "    rocprofv3 --kernel-trace --stats -f csv -d <dir> -o trace -- python3 bench.py", "",
+           "| kernel | calls | avg us | min us | max us | % of GPU time |",
+           "|---|---|---|---|---|---|"]
+    for r in rows:
+        out.append("| %s | %s | %.1f | %.1f | %.1f | %s |" % (
+            short(r["Name"]), r["Calls"], float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3,
+            float(r["MaxNs"]) / 1e3, r["Percentage"]))
+    with open(os.path.join(ROOT, "profiles", "kernel_trace_%s.md" % workload), "w") as fh:
+        fh.write("\n".join(out) + "\n")
+
+    def counters(sub):
+        agg = collections.defaultdict(list)
+        for r in csv.DictReader(open(os.path.join(pdir, sub, sub + "_counter_collection.csv"))):
+            agg[r["Kernel_Name"]].append(float(r["Counter_Value"]))
+        return agg
+
+    fetch, write = counters("fetch"), counters("write")
+    copy_kib = (1 << 30) / 1024
+    cf = [v for k, vs in counters("copyf").items() if "copyBuffer" in k for v in vs if v > 1e5]
+    cw = [v for k, vs in counters("copyw").items() if "copyBuffer" in k for v in vs if v > 1e5]
+    f_fetch, f_write = copy_kib / (sum(cf) / len(cf)), copy_kib / (sum(cw) / len(cw))
+    w = gen.BY_NAME[workload]
+    alg = algorithmic(w, 2 if w.io_dtype == gen.BF16 else 4)
+    res = {"workload": workload,
+           "command": "rocprofv3 --pmc FETCH_SIZE (then WRITE_SIZE) -f csv -- " + PROFILE_CMD,
+           "copy_calibration": {"bytes_read": 1 << 30, "bytes_written": 1 << 30,
+                                "FETCH_SIZE_KiB": sum(cf) / len(cf),
+                                "WRITE_SIZE_KiB": sum(cw) / len(cw),
+                                "fetch_scale": f_fetch, "write_scale": f_write},
+           "kernels": {}}
+    md = ["# HBM traffic per launch: %s" % workload, "",
+          "Two counter passes of the same bench command (one counter each), from the repo root:",
+          "", "    rocprofv3 --pmc FETCH_SIZE -f csv -d <dir> -o fetch -- " + PROFILE_CMD,
+          "    rocprofv3 --pmc WRITE_SIZE -f csv -d <dir> -o write -- " + PROFILE_CMD, "",
+          "Calibration runs the same two counters over a plain 1 GiB device copy:", "",
+          "    rocprofv3 --pmc FETCH_SIZE -f csv -d <dir> -o copyf -- python3 bench.py "
+          "--copy-reference-only",
+          "    rocprofv3 --pmc WRITE_SIZE -f csv -d <dir> -o copyw -- python3 bench.py "
+          "--copy-reference-only", "",
+          "The copy (torch `copy_`, the `__amd_rocclr_copyBuffer` kernel) reads %.0f KiB by "
+          "FETCH_SIZE and writes %.0f KiB by WRITE_SIZE, so the scale factors are fetch x%.3f and "
+          "write x%.3f (1 GiB = 1048576 KiB).  `python3 bench.py --summarize-rocprof <dir>` "
+          "wrote this file." % (sum(cf) / len(cf), sum(cw) / len(cw), f_fetch, f_write), "",
+          "| kernel | FETCH_SIZE KiB | WRITE_SIZE KiB | HBM bytes (scaled) | algorithmic bytes "
+          "| ratio |", "|---|---|---|---|---|---|"]
+    for name in fetch:
+        k = profile_kind(name)
+        if k is None or name not in write:
+            continue
+        fk = sum(fetch[name]) / len(fetch[name])
+        wk = sum(write[name]) / len(write[name])
+        hbm = fk * 1024 * f_fetch + wk * 1024 * f_write
+        a = alg[k]["bytes"]
+        src = {"state_fwd_kernel": "state_fwd", "b_fragments": "state_fwd"}.get(k, k)
+        res["kernels"][k] = {"fetch_kib": fk, "write_kib": wk, "hbm_bytes_per_launch": int(hbm),
+                             "alg_bytes": a, "source_sha": kernel_source_sha(src)}
+        md.append("| %s | %.0f | %.0f | %.4g | %.4g | %.3f |" % (k, fk, wk, hbm, a, hbm / a))
+    with open(os.path.join(ROOT, "profiles", "traffic_%s.md" % workload), "w") as fh:
+        fh.write("\n".join(md) + "\n")
+    with open(TRAFFIC_FILE, "w") as fh:
+        json.dump(res, fh, indent=1)
+    print("\n".join(out))
+    print("\n".join(md))
+
+
 # ---- the GPU legs ----------------------------------------------------------------------
 
 def run_forward(w, steps: int, warmup: int):
@@ -431,13 +528,19 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=50)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--summarize-rocprof", metavar="DIR",
+                    help="write the profiles/ summaries from a rocprofv3 output directory "
+                         "(host only, no GPU)")
     ap.add_argument("--copy-reference-only", action="store_true",
                     help="only the 1 GiB device copy (calibrates HBM byte counters)")
     args = ap.parse_args()
 
+    if args.summarize_rocprof:
+        summarize_rocprof(args.summarize_rocprof, args.workload)
+        return
     if args.gpus != 1:
-        print("bench.py measures one GPU only: this build targets a single MI355X "
-              "(no multi-GPU path); run with --gpus 1", file=sys.stderr)
+        print("bench.py measures one GPU only (a single MI355X; there is no multi-GPU "
+              "path): run with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
     import torch

@@ -359,7 +359,7 @@ __global__ __launch_bounds__(256, 2) void state_fwd_kernel(FwdArgs a, uint32_t n
                     for (int i = 0; i < SW; ++i) av[hl][i] = an[hl][i];
             }
             // schedule: the next slab's LDS reads and the B loads first, then
-            // each MFMA followed by three VALU instructions of the build
+            // each MFMA followed by three VALU instructions of the fragment build
             __builtin_amdgcn_sched_group_barrier(0x100, 2 * SW, 0);   // DS read
             __builtin_amdgcn_sched_group_barrier(0x020, TW, 0);       // VMEM read
 #pragma unroll
