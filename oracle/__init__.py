@@ -80,6 +80,9 @@ def _load():
         lib.ssd_oracle_decode_gated.argtypes = [dp, fp, fp, fp, fp, fp, fp, fp, ip, fp, i64, i64,
                                                 i64, i64, i64, dp, i64, dp, ip]
         lib.ssd_oracle_decode_gated.restype = ctypes.c_int
+        lib.ssd_oracle_bwd.argtypes = [fp, fp, fp, fp, fp, fp, dp, fp, fp, i64, i64, i64, i64,
+                                       i64, i64, dp, dp, dp, dp, dp, dp, dp, ip]
+        lib.ssd_oracle_bwd.restype = ctypes.c_int
         lib.ssd_oracle_host_threads.argtypes = []
         lib.ssd_oracle_host_threads.restype = ctypes.c_int
         _lib = lib
@@ -213,6 +216,35 @@ def token_decode_multi(state, x, dt, B, C, A, D, parent=None, update_state: bool
     if update_state:
         state[...] = run
     return y, snaps
+
+
+def token_bwd(x, dt, A, B, C, D, dy, init_state=None, dfinal=None, nthreads: int = 0):
+    """Float64 gradients of L = sum(dy * y) + sum(dfinal * final_state) for the
+    plain forward (no layer options): the exact adjoint of the recurrence,
+    token by token ("Mamba-3 ... kernels", section "Backward", for the order a
+    chunked backward takes: a reverse scan of the state adjoint).
+
+    Shapes as token_fwd, dy [Bt,T,H,P], dfinal [Bt,H,P,N] or None.  Returns a
+    dict with dx [Bt,T,H,P], ddt [Bt,T,H], dB and dC [Bt,T,G,N] (summed over
+    the heads of each group), dA and dD [H] (summed over batch and tokens)
+    and dinit [Bt,H,P,N].
+    """
+    x, dt, A, B, C, D, dy = map(_f32, (x, dt, A, B, C, D, dy))
+    Bt, T, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    assert dy.shape == x.shape and dt.shape == (Bt, T, H) and B.shape == C.shape
+    init = None if init_state is None else np.ascontiguousarray(init_state, np.float64)
+    dfin = None if dfinal is None else _f32(dfinal)
+    out = dict(dx=np.empty((Bt, T, H, P)), ddt=np.empty((Bt, T, H)), dB=np.empty((Bt, T, G, N)),
+               dC=np.empty((Bt, T, G, N)), dA=np.empty(H), dD=np.empty(H),
+               dinit=np.empty((Bt, H, P, N)))
+    rc = _load().ssd_oracle_bwd(_ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
+                                _ptr(init), _ptr(dy), _ptr(dfin), Bt, T, H, P, N, G,
+                                *(_ptr(out[k]) for k in ("dx", "ddt", "dB", "dC", "dA", "dD",
+                                                        "dinit")), nthreads)
+    if rc < 0:
+        raise ValueError("ssd_oracle_bwd rejected its arguments (%d)" % rc)
+    return out
 
 
 def chunked_reference(x, dt, A, B, C, D, chunk_size: int, init_state=None):

@@ -200,3 +200,159 @@ int ssd_oracle_decode_gated(double *state, const float *x_t, const float *dt_t,
     return ssd_oracle_fwd_gated(x_t, dt_t, A, B_t, C_t, D, dt_bias, softplus, z_t, state, Bt, 1,
                                 H, P, N, G, pairs, npairs, y_t, state, nthreads);
 }
+
+/*
+ * The backward of the plain forward: the exact adjoint of the recurrence,
+ * token by token in float64.  With g_t = dL/dh_t (P x N), starting from
+ * g = dL/d(final state) and walking t = T .. 1:
+ *
+ *     g_t    = (g from later tokens) + dy_t (outer) C_t
+ *     dC_t  += h_t^T dy_t                 (summed over the heads of the group)
+ *     dx_t   = D dy_t + dt_t g_t B_t
+ *     dB_t  += dt_t g_t^T x_t             (summed over the heads of the group)
+ *     ddt_t  = x_t^T g_t B_t + A a_t <g_t, h_{t-1}>,   a_t = exp(A dt_t)
+ *     dA    += dt_t a_t <g_t, h_{t-1}>     (summed over batch and tokens)
+ *     dD    += dy_t . x_t                  (summed over batch and tokens)
+ *     g_{t-1} = a_t g_t,   and finally dL/d(init state) = g_0.
+ *
+ * This is the chain rule applied to the recurrence of the header comment
+ * ("Mamba-3 ... kernels", section "Backward", gives the chunked order of the
+ * same adjoint: a reverse scan of the state adjoint between chunk-parallel
+ * passes).  Rows p of a head do not interact, so each row's forward states
+ * are stored (T + 1 vectors of N) and walked back.  The unit of work is one
+ * (b, g): all rows of all heads of group g in batch row b, in head and row
+ * order, so the sums over heads and rows are taken in a fixed order; dA and
+ * dD are summed over b in order at the end.
+ */
+typedef struct {
+    const float *x, *dt, *A, *B, *C, *D, *dy, *dfin;
+    const double *init;      /* [Bt*H][P][N] or NULL */
+    double *dx, *ddt, *dB, *dC, *dinit, *dA_part, *dD_part;   /* part: [Bt*H] */
+    int64_t Bt, T, H, P, N, G;
+    int64_t next;
+} bwd_job;
+
+static void bwd_unit(const bwd_job *j, int64_t unit, double *S, double *gr)
+{
+    const int64_t b = unit / j->G, g = unit % j->G;
+    const int64_t T = j->T, H = j->H, P = j->P, N = j->N, G = j->G, hpg = H / G;
+    for (int64_t h = g * hpg; h < (g + 1) * hpg; ++h) {
+        const int64_t bh = b * H + h;
+        const double A = (double)j->A[h], D = (double)j->D[h];
+        double dA = 0.0, dD = 0.0;
+        for (int64_t p = 0; p < P; ++p) {
+            /* forward: S[t] = state row after t tokens */
+            for (int64_t n = 0; n < N; ++n)
+                S[n] = j->init ? j->init[(bh * P + p) * N + n] : 0.0;
+            for (int64_t t = 0; t < T; ++t) {
+                const int64_t bt = b * T + t;
+                const double dt = (double)j->dt[bt * H + h];
+                const double a = exp(A * dt), u = dt * (double)j->x[(bt * H + h) * P + p];
+                const float *Bv = j->B + (bt * G + g) * N;
+                for (int64_t n = 0; n < N; ++n)
+                    S[(t + 1) * N + n] = a * S[t * N + n] + u * (double)Bv[n];
+            }
+            /* backward */
+            for (int64_t n = 0; n < N; ++n)
+                gr[n] = j->dfin ? (double)j->dfin[(bh * P + p) * N + n] : 0.0;
+            for (int64_t t = T - 1; t >= 0; --t) {
+                const int64_t bt = b * T + t;
+                const double dt = (double)j->dt[bt * H + h];
+                const double a = exp(A * dt);
+                const double xv = (double)j->x[(bt * H + h) * P + p];
+                const double dyv = (double)j->dy[(bt * H + h) * P + p];
+                const float *Bv = j->B + (bt * G + g) * N;
+                const float *Cv = j->C + (bt * G + g) * N;
+                double *dBt = j->dB + (bt * G + g) * N;
+                double *dCt = j->dC + (bt * G + g) * N;
+                double gB = 0.0, sh = 0.0;
+                for (int64_t n = 0; n < N; ++n) {
+                    gr[n] += dyv * (double)Cv[n];
+                    dCt[n] += S[(t + 1) * N + n] * dyv;
+                    gB += gr[n] * (double)Bv[n];
+                    dBt[n] += dt * xv * gr[n];
+                    sh += gr[n] * S[t * N + n];
+                }
+                j->dx[(bt * H + h) * P + p] = D * dyv + dt * gB;
+                j->ddt[bt * H + h] += xv * gB + A * a * sh;
+                dA += dt * a * sh;
+                dD += dyv * xv;
+                for (int64_t n = 0; n < N; ++n) gr[n] *= a;
+            }
+            if (j->dinit)
+                for (int64_t n = 0; n < N; ++n) j->dinit[(bh * P + p) * N + n] = gr[n];
+        }
+        j->dA_part[bh] = dA;
+        j->dD_part[bh] = dD;
+    }
+}
+
+static void *bwd_worker(void *arg)
+{
+    bwd_job *j = (bwd_job *)arg;
+    double *S = (double *)malloc(sizeof(double) * (size_t)((j->T + 1) * j->N));
+    double *gr = (double *)malloc(sizeof(double) * (size_t)j->N);
+    if (S && gr) {
+        for (;;) {
+            int64_t u = __atomic_fetch_add(&j->next, 1, __ATOMIC_RELAXED);
+            if (u >= j->Bt * j->G) break;
+            bwd_unit(j, u, S, gr);
+        }
+    }
+    free(S);
+    free(gr);
+    return NULL;
+}
+
+/*
+ * Gradients of L = sum(dy . y) + sum(dfin . final) for the plain forward.
+ * Inputs as ssd_oracle_fwd plus dy [Bt,T,H,P] and dfin [Bt,H,P,N] (NULL = 0);
+ * init [Bt*H,P,N] float64 or NULL.  Outputs (float64, all written): dx
+ * [Bt,T,H,P], ddt [Bt,T,H], dB and dC [Bt,T,G,N], dA and dD [H], and dinit
+ * [Bt,H,P,N] (may be NULL).  Returns the number of threads used, or a
+ * negative value on a bad argument or allocation failure.
+ */
+int ssd_oracle_bwd(const float *x, const float *dt, const float *A, const float *B,
+                   const float *C, const float *D, const double *init, const float *dy,
+                   const float *dfin, int64_t Bt, int64_t T, int64_t H, int64_t P, int64_t N,
+                   int64_t G, double *dx, double *ddt, double *dB, double *dC, double *dA,
+                   double *dD, double *dinit, int nthreads)
+{
+    if (!x || !dt || !A || !B || !C || !D || !dy || !dx || !ddt || !dB || !dC || !dA || !dD)
+        return -1;
+    if (Bt < 1 || T < 0 || H < 1 || P < 1 || N < 1 || G < 1 || H % G) return -2;
+    double *part = (double *)calloc((size_t)(2 * Bt * H), sizeof(double));
+    if (!part) return -4;
+    memset(ddt, 0, sizeof(double) * (size_t)(Bt * T * H));
+    memset(dB, 0, sizeof(double) * (size_t)(Bt * T * G * N));
+    memset(dC, 0, sizeof(double) * (size_t)(Bt * T * G * N));
+    bwd_job j = {x, dt, A, B, C, D, dy, dfin, init, dx, ddt, dB, dC, dinit, part,
+                 part + Bt * H, Bt, T, H, P, N, G, 0};
+    if (nthreads <= 0) nthreads = ssd_oracle_host_threads();
+    if (nthreads > Bt * G) nthreads = (int)(Bt * G);
+    pthread_t *th = (pthread_t *)malloc(sizeof(pthread_t) * (size_t)nthreads);
+    if (!th) {
+        free(part);
+        return -4;
+    }
+    int started = 0;
+    for (int i = 1; i < nthreads; ++i) {
+        if (pthread_create(&th[i], NULL, bwd_worker, &j) != 0) break;
+        ++started;
+    }
+    bwd_worker(&j);
+    for (int i = 1; i <= started; ++i) pthread_join(th[i], NULL);
+    free(th);
+    for (int64_t h = 0; h < H; ++h) {
+        double a = 0.0, d = 0.0;
+        for (int64_t b = 0; b < Bt; ++b) {
+            a += part[b * H + h];
+            d += part[Bt * H + b * H + h];
+        }
+        dA[h] = a;
+        dD[h] = d;
+    }
+    free(part);
+    return started + 1;
+}
+
