@@ -406,6 +406,45 @@ def run_decode_lowp(w, steps: int, warmup: int):
     return out
 
 
+def run_backward(w, steps: int, warmup: int):
+    """ssd_chunked_bwd on the forward workload (dy ~ N(0,1), dfinal ~ N(0,1));
+    mean milliseconds per call over ``steps`` calls."""
+    import torch
+    from selective_state_space_amd import inputs as gen
+    from selective_state_space_amd import ssd
+
+    dev = torch.device("cuda:0")
+    inp = gen.make_fwd(w, 0)
+    bf = torch.bfloat16 if w.io_dtype == gen.BF16 else torch.float32
+
+    def up(a, dt=torch.float32):
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dt).to(dev)
+
+    rng = np.random.default_rng(9)
+    args = (up(inp.x, bf), up(inp.dt), up(inp.A), up(inp.B, bf), up(inp.C, bf), up(inp.D),
+            w.chunk_size, up(rng.standard_normal(inp.x.shape, dtype=np.float32)),
+            None if inp.init_state is None else up(inp.init_state),
+            up(rng.standard_normal((w.batch, w.nheads, w.headdim, w.dstate), dtype=np.float32)))
+    del inp
+    a = ssd.FwdArgs(*args[:7], init_state=args[8])
+    ws = torch.empty(ssd.ssd_chunked_bwd_workspace_size(a.dims, w.chunk_size), dtype=torch.uint8,
+                     device=dev)
+    del a
+    for _ in range(warmup):
+        ssd.ssd_chunked_bwd(*args, workspace=ws)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        ssd.ssd_chunked_bwd(*args, workspace=ws)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    del args, ws
+    torch.cuda.empty_cache()
+    return ms
+
+
 def run_layer_interface(w, wd, steps: int, warmup: int):
     """The forward and decode step with every layer option on (dt_bias,
     softplus, the z gate).  The raw steps are the inverse softplus of the
@@ -626,6 +665,13 @@ def main():
                               hbm_frac=round(byt / (v * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
                               alg_bytes_per_step=int(byt))
             log("decode, %s state: %.1f us/step, %.0f GB/s" % (name, v * 1e3, lowp[name]["GBps"]))
+    bwd = None
+    if not args.no_decode:
+        bms = run_backward(w, 10, 3)
+        bwd = dict(us_per_call=round(bms * 1e3, 2), tokens_per_s=round(tokens / (bms * 1e-3), 1),
+                   over_forward=round(bms / step_ms, 3),
+                   gradients="dx, ddt, dA, dB, dC, dD, dinit (fp32)")
+        log("backward: %.1f us/call (%.2fx the forward)" % (bms * 1e3, bms / step_ms))
     layer = None
     if not args.no_decode:
         wd = gen.WORKLOADS[4]
@@ -678,6 +724,7 @@ def main():
                                               / BF16_PEAK_TFLOPS, 4),
         "kernels": kernels,
         "decode": decode,
+        "backward": bwd,
         "decode_multi": multi,
         "decode_lowp_state": lowp,
         "layer_interface": layer,

@@ -320,6 +320,37 @@ ssd_status ssd_decode_step_lp(void *state, const ssd_state_format *fmt, const vo
                               const float *D, void *y_t, const ssd_layer_opts *opts,
                               const ssd_dims *dims, void *stream);
 
+/*
+ * The backward of ssd_chunked_fwd (no layer options): gradients of
+ * L = sum(dy . y) + sum(dfinal . final_state).  "Mamba-3 ... kernels",
+ * section "Backward": the forward's chunk states are recomputed on the
+ * workspace, the state adjoint is scanned in reverse over the chunks between
+ * two chunk-parallel passes, and there are no floating-point atomics: every
+ * output element has one owner and every sum over heads or batch rows is
+ * taken in a fixed order, so reruns are bitwise identical.  Gradients are
+ * float32 whatever the io dtype.
+ *
+ *   x, dt, A, B, C, D, chunk_size, init_state, dims   as for ssd_chunked_fwd
+ *   dy      [Bt, T, H, P]   float32  in   gradient of y
+ *   dfinal  [Bt, H, P, N]   float32  in   gradient of the final state, or NULL (0)
+ *   dx      [Bt, T, H, P]   float32  out
+ *   ddt     [Bt, T, H]      float32  out
+ *   dA, dD  [H]             float32  out  (summed over batch and tokens)
+ *   dB, dC  [Bt, T, G, N]   float32  out  (summed over the heads of a group)
+ *   dinit   [Bt, H, P, N]   float32  out  gradient of init_state, or NULL (not
+ *                                         written); defined for init_state = NULL too
+ * workspace: ssd_chunked_bwd_workspace_size(dims, chunk_size) bytes, 16-byte
+ * aligned.  With no tokens the token tensors may be NULL; dA and dD are then
+ * zero and dinit = dfinal.  Errors as for ssd_chunked_fwd.
+ */
+size_t ssd_chunked_bwd_workspace_size(const ssd_dims *dims, int64_t chunk_size);
+ssd_status ssd_chunked_bwd(const void *x, const float *dt, const float *A, const void *B,
+                           const void *C, const float *D, int64_t chunk_size,
+                           const float *init_state, const float *dy, const float *dfinal,
+                           float *dx, float *ddt, float *dA, float *dB, float *dC, float *dD,
+                           float *dinit, const ssd_dims *dims, void *workspace,
+                           size_t workspace_bytes, void *stream);
+
 /* Static text for a status code. */
 const char *ssd_status_string(ssd_status status);
 

@@ -1,0 +1,580 @@
+// The backward of the chunked forward: gradients of L = sum(dy . y) +
+// sum(dfinal . final) with respect to x, dt, A, B, C, D and the initial state.
+//
+// "Mamba-3 ... kernels", section "Backward": two chunk-parallel passes around a
+// reverse scan of the state adjoint, with the chunk intermediates recomputed
+// rather than stored, and no floating-point atomics (every output element has
+// one owner; sums over heads and batch rows are taken in a fixed order).
+// The arithmetic is the chain rule of the recurrence of "Accelerating Mamba-2
+// with High-Performance Forward Pass Kernels in NVIDIA CUDA Tile", section
+// "Mamba-2 architecture", in the chunked form of the same section.  Per
+// (b, h), chunk c, chunk-local log-decay G (log2 units here) and the adjoint
+// ghat_c of the state leaving chunk c (ghat of the last chunk = dfinal):
+//
+//   dSp_c   = sum_k exp(G_k) dy_k (outer) C_k                    (bwd_dstate)
+//   ghat_{c-1} = dSp_c + exp(G_last) ghat_c; dinit = ghat_{-1}    (bwd_passing)
+//   CB(k,j) = C_k . B_j                                           (bwd_cb)
+//   U_i = sum_{k>=i} exp(G_k-G_i) CB(k,i) dy_k + exp(G_last-G_i) ghat_c B_i
+//        (the state adjoint g_i times B_i);  dx_i = D dy_i + dt_i U_i
+//   Y_i = exp(G_i) h_prev C_i + sum_{j<=i} exp(G_i-G_j) CB(i,j) dt_j x_j
+//   r_i = dy_i . Y_i - dt_i x_i . U_i                              (bwd_dx)
+//   M(k,j) = sum_h [k>=j] exp(G_k-G_j) dt_j (dy_k . x_j)
+//   dC_k = sum_j M(k,j) B_j + sum_h exp(G_k) h_prev^T dy_k
+//   dB_j = sum_k M(k,j) C_k + sum_h dt_j exp(G_last-G_j) ghat_c^T x_j (bwd_dbdc)
+//   s_t  = <dfinal, final> + sum_{t'>=t} r_t'  (over the whole sequence)
+//   ddt_t = x_t . U_t + A s_t;  dA = sum dt_t s_t;  dD = sum dy_t . x_t
+//                                                   (bwd_scalars, bwd_heads)
+// The identity behind s_t: with g_t the state adjoint, <g_t, exp(A dt_t)
+// h_{t-1}> = dy_t . (h_t C_t) - dt_t x_t . (g_t B_t) + <g_{t+1}, exp(A dt_{t+1}) h_t>,
+// so the decay part of the step gradient is a reverse running sum of per-token
+// scalars and never needs a per-token state.
+//
+// These kernels are fp32 SIMT: each stage stages operand tiles into LDS and
+// every thread accumulates a small register tile.  h_prev is read in fp32
+// (recomputed by chunk_state + state_passing with an fp32 output): the decay
+// gradients sum per-token products with it over the whole sequence, and
+// bf16's rounding of it would not average out there.
+
+#include "ssd_device.h"
+#include "ssd_launch.h"
+
+namespace ssd {
+
+namespace {
+
+constexpr int P = 64;
+constexpr int KT = 32;        // K-tile of the staged products
+constexpr int LD = 68;        // LDS row pitch in floats (16-byte aligned, 2-way at worst)
+
+template <typename T>
+__device__ __forceinline__ float ld1(const T *p);
+template <>
+__device__ __forceinline__ float ld1<float>(const float *p) { return *p; }
+template <>
+__device__ __forceinline__ float ld1<uint16_t>(const uint16_t *p) { return bf16_to_f32(*p); }
+
+// acc[TM][TN] += sum_{k < KT} As[k][m0 + i] * Bs[k][n0 + j]
+template <int TM, int TN>
+__device__ __forceinline__ void mm_acc(float (&acc)[TM][TN], const float *As, int lda,
+                                       const float *Bs, int ldb, int m0, int n0) {
+#pragma unroll 4
+    for (int k = 0; k < KT; ++k) {
+        float a[TM], b[TN];
+#pragma unroll
+        for (int i = 0; i < TM; i += 4) {
+            const float4 v = *reinterpret_cast<const float4 *>(As + k * lda + m0 + i);
+            a[i] = v.x; a[i + 1] = v.y; a[i + 2] = v.z; a[i + 3] = v.w;
+        }
+#pragma unroll
+        for (int j = 0; j < TN; j += 4) {
+            const float4 v = *reinterpret_cast<const float4 *>(Bs + k * ldb + n0 + j);
+            b[j] = v.x; b[j + 1] = v.y; b[j + 2] = v.z; b[j + 3] = v.w;
+        }
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j) acc[i][j] = fmaf(a[i], b[j], acc[i][j]);
+    }
+}
+
+// ---- bwd_dstate: dSp[b,h,c] = sum_k exp2(G_k) dy_k (outer) C_k, [P][N] ------
+template <int L, int N, typename Tio>
+__global__ __launch_bounds__(256) void bwd_dstate_kernel(const float *__restrict__ dy,
+                                                         const Tio *__restrict__ C,
+                                                         const float *__restrict__ Gws,
+                                                         float *__restrict__ dS, int64_t T,
+                                                         int32_t H, int32_t G, int32_t nc) {
+    constexpr int TN = N / 16;
+    __shared__ __align__(16) float As[KT * LD];
+    __shared__ __align__(16) float Bs[KT * (N + 4)];
+    const int64_t unit = blockIdx.x;              // (b*H + h)*nc + c
+    const int32_t c = (int32_t)(unit % nc);
+    const int64_t bh = unit / nc;
+    const int64_t b = bh / H;
+    const int32_t h = (int32_t)(bh % H), g = h / (H / G);
+    const int tid = threadIdx.x;
+    const int p0 = 4 * (tid >> 4), n0 = TN * (tid & 15);
+    const float *Gc = Gws + unit * L;
+    float acc[4][TN] = {};
+    for (int k0 = 0; k0 < L; k0 += KT) {
+        __syncthreads();
+        for (int e = tid; e < KT * P; e += 256) {          // dy rows, scaled
+            const int kk = e / P, p = e % P;
+            const int64_t t = (int64_t)c * L + k0 + kk;
+            As[kk * LD + p] = t < T ? dy[((b * T + t) * H + h) * P + p] * fast_exp2(Gc[k0 + kk]) : 0.f;
+        }
+        for (int e = tid; e < KT * N; e += 256) {
+            const int kk = e / N, n = e % N;
+            const int64_t t = (int64_t)c * L + k0 + kk;
+            Bs[kk * (N + 4) + n] = t < T ? ld1(C + ((b * T + t) * G + g) * N + n) : 0.f;
+        }
+        __syncthreads();
+        mm_acc<4, TN>(acc, As, LD, Bs, N + 4, p0, n0);
+    }
+    float *o = dS + unit * (int64_t)(P * N);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; j += 4)
+            *reinterpret_cast<float4 *>(o + (p0 + i) * N + n0 + j) =
+                make_float4(acc[i][j], acc[i][j + 1], acc[i][j + 2], acc[i][j + 3]);
+}
+
+// ---- bwd_passing: reverse scan of the state adjoint, in place over dSp ------
+// The slot of chunk c ends holding ghat_c (the adjoint of the state leaving c).
+template <int L, int N>
+__global__ __launch_bounds__(256) void bwd_passing_kernel(float *__restrict__ dS,
+                                                          const float *__restrict__ Gws,
+                                                          const float *__restrict__ dfin,
+                                                          const float *__restrict__ fin,
+                                                          float *__restrict__ dinit,
+                                                          double *__restrict__ bnd, int32_t nc) {
+    constexpr int E = P * N / 256;                 // elements per thread
+    __shared__ double red[256];
+    const int64_t bh = blockIdx.x;
+    const int tid = threadIdx.x;
+    const int64_t off = bh * (int64_t)(P * N) + (int64_t)tid * E;
+    float gh[E];
+    double dot = 0.0;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+        gh[e] = dfin ? dfin[off + e] : 0.f;
+        if (dfin) dot += (double)gh[e] * (double)fin[off + e];
+    }
+    for (int c = nc - 1; c >= 0; --c) {
+        float *slot = dS + (bh * nc + c) * (int64_t)(P * N) + (int64_t)tid * E;
+        const float a = fast_exp2(Gws[(bh * nc + c) * L + (L - 1)]);
+#pragma unroll
+        for (int e = 0; e < E; e += 4) {
+            const float4 v = *reinterpret_cast<const float4 *>(slot + e);
+            *reinterpret_cast<float4 *>(slot + e) =
+                make_float4(gh[e], gh[e + 1], gh[e + 2], gh[e + 3]);
+            gh[e] = fmaf(a, gh[e], v.x);
+            gh[e + 1] = fmaf(a, gh[e + 1], v.y);
+            gh[e + 2] = fmaf(a, gh[e + 2], v.z);
+            gh[e + 3] = fmaf(a, gh[e + 3], v.w);
+        }
+    }
+    if (dinit)
+#pragma unroll
+        for (int e = 0; e < E; ++e) dinit[off + e] = gh[e];
+    red[tid] = dot;
+    __syncthreads();
+    for (int s = 128; s > 0; s >>= 1) {
+        if (tid < s) red[tid] += red[tid + s];
+        __syncthreads();
+    }
+    if (tid == 0) bnd[bh] = red[0];
+}
+
+// ---- bwd_cb: CB(k, j) = C_k . B_j for the 64x64 blocks on or below the diagonal
+template <int L, int N, typename Tio>
+__global__ __launch_bounds__(256) void bwd_cb_kernel(const Tio *__restrict__ B,
+                                                     const Tio *__restrict__ C,
+                                                     float *__restrict__ CB, int64_t T,
+                                                     int32_t G, int32_t nc) {
+    constexpr int NB = L / 64, NTRI = NB * (NB + 1) / 2;
+    __shared__ __align__(16) float As[KT * LD];
+    __shared__ __align__(16) float Bs[KT * LD];
+    const int64_t blk = blockIdx.x;
+    int tri = (int)(blk % NTRI);
+    const int64_t bcg = blk / NTRI;                // (b*nc + c)*G + g
+    const int32_t g = (int32_t)(bcg % G);
+    const int64_t bc = bcg / G;
+    const int32_t c = (int32_t)(bc % nc);
+    const int64_t b = bc / nc;
+    int kb = 0;
+    while (tri > kb) { tri -= kb + 1; ++kb; }
+    const int jb = tri;                             // jb <= kb
+    const int tid = threadIdx.x;
+    const int m0 = 4 * (tid >> 4), n0 = 4 * (tid & 15);
+    float acc[4][4] = {};
+    for (int q0 = 0; q0 < N; q0 += KT) {
+        __syncthreads();
+        for (int e = tid; e < KT * 64; e += 256) {
+            const int r = e / KT, q = e % KT;       // token row r, state index q
+            const int64_t tk = (int64_t)c * L + 64 * kb + r, tj = (int64_t)c * L + 64 * jb + r;
+            As[q * LD + r] = tk < T ? ld1(C + ((b * T + tk) * G + g) * N + q0 + q) : 0.f;
+            Bs[q * LD + r] = tj < T ? ld1(B + ((b * T + tj) * G + g) * N + q0 + q) : 0.f;
+        }
+        __syncthreads();
+        mm_acc<4, 4>(acc, As, LD, Bs, LD, m0, n0);
+    }
+    float *o = CB + bcg * (int64_t)(L * L) + (int64_t)(64 * kb + m0) * L + 64 * jb + n0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        *reinterpret_cast<float4 *>(o + i * L) =
+            make_float4(acc[i][0], acc[i][1], acc[i][2], acc[i][3]);
+}
+
+// ---- bwd_dx: dx and the per-token scalars of one (b, c, h, 64-row block) ----
+template <int L, int N, typename Tio, typename Thp>
+__global__ __launch_bounds__(256) void bwd_dx_kernel(
+    const Tio *__restrict__ x, const Tio *__restrict__ B, const Tio *__restrict__ C,
+    const float *__restrict__ D, const float *__restrict__ dy, const float *__restrict__ Gws,
+    const float *__restrict__ DTws, const float *__restrict__ CB, const float *__restrict__ gh,
+    const Thp *__restrict__ hprev, float *__restrict__ dx, float *__restrict__ tok, int64_t T,
+    int32_t H, int32_t G, int32_t nc) {
+    __shared__ __align__(16) float As[KT * LD];
+    __shared__ __align__(16) float Bs[KT * LD];
+    const int64_t blk = blockIdx.x;
+    const int ib = (int)(blk % (L / 64));
+    const int64_t unit = blk / (L / 64);            // (b*H + h)*nc + c
+    const int32_t c = (int32_t)(unit % nc);
+    const int64_t bh = unit / nc;
+    const int64_t b = bh / H;
+    const int32_t h = (int32_t)(bh % H), g = h / (H / G);
+    const int64_t bcg = ((b * nc) + c) * G + g;
+    const int i0 = 64 * ib;
+    const int tid = threadIdx.x;
+    const int m0 = 4 * (tid >> 4), n0 = 4 * (tid & 15);
+    const float *Gc = Gws + unit * L, *DTc = DTws + unit * L;
+    const float *CBc = CB + bcg * (int64_t)(L * L);
+    const int64_t tc = (int64_t)c * L;
+    const float glast = Gc[L - 1];
+    float U[4][4] = {}, Y[4][4] = {};
+
+    // U intra: sum_{k >= i} exp2(G_k - G_i) CB(k, i) dy_k
+    for (int k0 = i0; k0 < L; k0 += KT) {
+        __syncthreads();
+        for (int e = tid; e < KT * 64; e += 256) {
+            const int kk = e / 64, ii = e % 64;
+            const int k = k0 + kk, i = i0 + ii;
+            As[kk * LD + ii] = k >= i ? fast_exp2(Gc[k] - Gc[i]) * CBc[(int64_t)k * L + i] : 0.f;
+            const int64_t t = tc + k;
+            Bs[kk * LD + ii] = t < T ? dy[((b * T + t) * H + h) * P + ii] : 0.f;
+        }
+        __syncthreads();
+        mm_acc<4, 4>(U, As, LD, Bs, LD, m0, n0);
+    }
+    // U inter: exp2(G_last - G_i) ghat_c B_i;  Y inter: exp2(G_i) h_prev C_i
+    const float *ghc = gh + unit * (int64_t)(P * N);
+    const Thp *hpc = hprev + unit * (int64_t)(P * N);
+    for (int q0 = 0; q0 < N; q0 += KT) {
+        __syncthreads();
+        for (int e = tid; e < KT * 64; e += 256) {
+            const int ii = e / KT, q = e % KT;
+            const int64_t t = tc + i0 + ii;
+            const float f = fast_exp2(glast - Gc[i0 + ii]);
+            As[q * LD + ii] = t < T ? f * ld1(B + ((b * T + t) * G + g) * N + q0 + q) : 0.f;
+            Bs[q * LD + ii] = ghc[ii * N + q0 + q];    // ii plays p here
+        }
+        __syncthreads();
+        mm_acc<4, 4>(U, As, LD, Bs, LD, m0, n0);
+        __syncthreads();
+        for (int e = tid; e < KT * 64; e += 256) {
+            const int ii = e / KT, q = e % KT;
+            const int64_t t = tc + i0 + ii;
+            const float f = fast_exp2(Gc[i0 + ii]);
+            As[q * LD + ii] = t < T ? f * ld1(C + ((b * T + t) * G + g) * N + q0 + q) : 0.f;
+            Bs[q * LD + ii] = ld1(hpc + ii * N + q0 + q);
+        }
+        __syncthreads();
+        mm_acc<4, 4>(Y, As, LD, Bs, LD, m0, n0);
+    }
+    // Y intra: sum_{j <= i} exp2(G_i - G_j) CB(i, j) dt_j x_j
+    for (int j0 = 0; j0 < i0 + 64; j0 += KT) {
+        __syncthreads();
+        for (int e = tid; e < KT * 64; e += 256) {
+            const int ii = e / KT, jj = e % KT;
+            const int i = i0 + ii, j = j0 + jj;
+            As[jj * LD + ii] =
+                j <= i ? fast_exp2(Gc[i] - Gc[j]) * CBc[(int64_t)i * L + j] * DTc[j] : 0.f;
+        }
+        for (int e = tid; e < KT * 64; e += 256) {
+            const int jj = e / 64, p = e % 64;
+            const int64_t t = tc + j0 + jj;
+            Bs[jj * LD + p] = t < T ? ld1(x + ((b * T + t) * H + h) * P + p) : 0.f;
+        }
+        __syncthreads();
+        mm_acc<4, 4>(Y, As, LD, Bs, LD, m0, n0);
+    }
+    // epilogue: dx, and x.U, dy.Y, dy.x summed over p (16 lanes share a row)
+    const float Dh = D[h];
+    float *tokc = tok + unit * (int64_t)L;
+    const int64_t ntok = (int64_t)gridDim.x / (L / 64) * L;   // one plane of token scalars
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const int i = i0 + m0 + e;
+        const int64_t t = tc + i;
+        const bool real = t < T;
+        const int64_t tt = real ? t : 0;
+        const float dti = DTc[i];
+        float xu = 0.f, dyy = 0.f, dyx = 0.f;
+        float dv[4];
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            const int p = n0 + s;
+            const float dyv = real ? dy[((b * T + tt) * H + h) * P + p] : 0.f;
+            const float xv = real ? ld1(x + ((b * T + tt) * H + h) * P + p) : 0.f;
+            dv[s] = Dh * dyv + dti * U[e][s];
+            xu = fmaf(xv, U[e][s], xu);
+            dyy = fmaf(dyv, Y[e][s], dyy);
+            dyx = fmaf(dyv, xv, dyx);
+        }
+        if (real)
+            *reinterpret_cast<float4 *>(dx + ((b * T + t) * H + h) * P + n0) =
+                make_float4(dv[0], dv[1], dv[2], dv[3]);
+#pragma unroll
+        for (int o = 1; o < 16; o <<= 1) {
+            xu += __shfl_xor(xu, o, 64);
+            dyy += __shfl_xor(dyy, o, 64);
+            dyx += __shfl_xor(dyx, o, 64);
+        }
+        if ((tid & 15) == 0) {
+            tokc[i] = xu;                            // x . U  (plane 0)
+            tokc[ntok + i] = dyy - dti * xu;         // r      (plane 1)
+            tokc[2 * ntok + i] = dyx;                // dy . x (plane 2)
+        }
+    }
+}
+
+// ---- bwd_dbdc: dC (orientation 0) or dB (orientation 1) for one 64-row block
+template <int L, int N, typename Tio, typename Thp>
+__global__ __launch_bounds__(256) void bwd_dbdc_kernel(
+    const Tio *__restrict__ x, const Tio *__restrict__ B, const Tio *__restrict__ C,
+    const float *__restrict__ dy, const float *__restrict__ Gws, const float *__restrict__ DTws,
+    const float *__restrict__ gh, const Thp *__restrict__ hprev, float *__restrict__ dB,
+    float *__restrict__ dC, int64_t T, int32_t H, int32_t G, int32_t nc) {
+    constexpr int NB = L / 64, TN = N / 16;
+    __shared__ __align__(16) float As[KT * LD];
+    __shared__ __align__(16) float Bs[KT * (N + 4)];
+    const int64_t blk = blockIdx.x;
+    const int orient = (int)(blk & 1);
+    const int rb = (int)((blk >> 1) % NB);
+    const int64_t bcg = (blk >> 1) / NB;            // (b*nc + c)*G + g
+    const int32_t g = (int32_t)(bcg % G);
+    const int64_t bc = bcg / G;
+    const int32_t c = (int32_t)(bc % nc);
+    const int64_t b = bc / nc;
+    const int hpg = H / G;
+    const int r0 = 64 * rb;
+    const int tid = threadIdx.x;
+    const int m0 = 4 * (tid >> 4), cj = 4 * (tid & 15), q0n = TN * (tid & 15);
+    const int64_t tc = (int64_t)c * L;
+    // M(row, col) over the columns of 64-wide blocks; orientation 0: rows k of
+    // this block, columns j <= k; orientation 1: rows j of this block, columns k >= j
+    float M[NB][4][4] = {};
+    float acc2[4][TN] = {};                         // the inter-chunk term, [row][n]
+    for (int hh = 0; hh < hpg; ++hh) {
+        const int32_t h = g * hpg + hh;
+        const int64_t unit = ((b * H) + h) * nc + c;
+        const float *Gc = Gws + unit * L, *DTc = DTws + unit * L;
+        const float glast = Gc[L - 1];
+#pragma unroll
+        for (int ob = 0; ob < NB; ++ob) {
+            if (orient == 0 ? ob > rb : ob < rb) continue;
+            // dYX block: orientation 0 -> dy_rows . x_cols, 1 -> x_rows . dy_cols (K = P)
+            float a4[4][4] = {};
+            for (int p0 = 0; p0 < P; p0 += KT) {
+                __syncthreads();
+                for (int e = tid; e < KT * 64; e += 256) {
+                    const int r = e / KT, q = e % KT;
+                    const int64_t tr = tc + r0 + r, to = tc + 64 * ob + r;
+                    const int64_t ir = ((b * T + (tr < T ? tr : 0)) * H + h) * P + p0 + q;
+                    const int64_t io = ((b * T + (to < T ? to : 0)) * H + h) * P + p0 + q;
+                    const float rv = tr < T ? (orient == 0 ? dy[ir] : ld1(x + ir)) : 0.f;
+                    const float ov = to < T ? (orient == 0 ? ld1(x + io) : dy[io]) : 0.f;
+                    As[q * LD + r] = rv;
+                    Bs[q * LD + r] = ov;
+                }
+                __syncthreads();
+                mm_acc<4, 4>(a4, As, LD, Bs, LD, m0, cj);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int rr = r0 + m0 + i, oo = 64 * ob + cj + j;
+                    const int k = orient == 0 ? rr : oo, jx = orient == 0 ? oo : rr;
+                    M[ob][i][j] += k >= jx ? fast_exp2(Gc[k] - Gc[jx]) * DTc[jx] * a4[i][j] : 0.f;
+                }
+        }
+        // inter: orientation 0: exp2(G_k) h_prev^T dy_k; 1: dt_j exp2(G_last - G_j) ghat^T x_j
+        const float *ghc = gh + unit * (int64_t)(P * N);
+        const Thp *hpc = hprev + unit * (int64_t)(P * N);
+        for (int p0 = 0; p0 < P; p0 += KT) {
+            __syncthreads();
+            for (int e = tid; e < KT * 64; e += 256) {
+                const int r = e / KT, q = e % KT;
+                const int rr = r0 + r;
+                const int64_t t = tc + rr;
+                const int64_t ix = ((b * T + (t < T ? t : 0)) * H + h) * P + p0 + q;
+                float v = 0.f;
+                if (t < T)
+                    v = orient == 0 ? dy[ix] * fast_exp2(Gc[rr])
+                                    : ld1(x + ix) * DTc[rr] * fast_exp2(glast - Gc[rr]);
+                As[q * LD + r] = v;
+            }
+            for (int e = tid; e < KT * N; e += 256) {
+                const int q = e / N, n = e % N;
+                Bs[q * (N + 4) + n] = orient == 0 ? ld1(hpc + (p0 + q) * N + n)
+                                                  : ghc[(p0 + q) * N + n];
+            }
+            __syncthreads();
+            mm_acc<4, TN>(acc2, As, LD, Bs, N + 4, m0, q0n);
+        }
+    }
+    // out(row, n) += sum_col M(row, col) V_col[n], V = B (orientation 0) or C (1)
+    for (int ob = 0; ob < NB; ++ob) {
+        if (orient == 0 ? ob > rb : ob < rb) continue;
+        for (int h0 = 0; h0 < 64; h0 += KT) {
+            __syncthreads();
+            // this thread's M columns cj..cj+3 that fall in [h0, h0+KT)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int col = cj + j;
+                if (col >= h0 && col < h0 + KT)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) As[(col - h0) * LD + m0 + i] = M[ob][i][j];
+            }
+            for (int e = tid; e < KT * N; e += 256) {
+                const int q = e / N, n = e % N;
+                const int64_t t = tc + 64 * ob + h0 + q;
+                const Tio *V = orient == 0 ? B : C;
+                Bs[q * (N + 4) + n] = t < T ? ld1(V + ((b * T + t) * G + g) * N + n) : 0.f;
+            }
+            __syncthreads();
+            mm_acc<4, TN>(acc2, As, LD, Bs, N + 4, m0, q0n);
+        }
+    }
+    float *out = orient == 0 ? dC : dB;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int64_t t = tc + r0 + m0 + i;
+        if (t < T)
+#pragma unroll
+            for (int j = 0; j < TN; j += 4)
+                *reinterpret_cast<float4 *>(out + ((b * T + t) * G + g) * N + q0n + j) =
+                    make_float4(acc2[i][j], acc2[i][j + 1], acc2[i][j + 2], acc2[i][j + 3]);
+    }
+}
+
+// ---- bwd_scalars: s_t = bnd + sum_{t' >= t} r_t' per (b, h); ddt, dA/dD parts
+// The running sums are kept in fp64: s_t sums thousands of terms of both signs
+// to a small value, and dA sums dt_t s_t over the sequence again.
+template <int L>
+__global__ __launch_bounds__(256) void bwd_scalars_kernel(
+    const float *__restrict__ tok, const float *__restrict__ DTws, const float *__restrict__ A,
+    const double *__restrict__ bnd, float *__restrict__ ddt, double *__restrict__ part,
+    int64_t T, int32_t H, int32_t nc, int64_t ntok, int64_t nbh) {
+    __shared__ double seg[256];
+    __shared__ double red[2][256];
+    const int64_t bh = blockIdx.x;
+    const int64_t b = bh / H;
+    const int32_t h = (int32_t)(bh % H);
+    const int tid = threadIdx.x;
+    const int64_t per = (T + 255) / 256;
+    const int64_t t0 = (int64_t)tid * per, t1 = t0 + per < T ? t0 + per : T;
+    const float *xu = tok + bh * nc * L, *r = tok + ntok + bh * nc * L,
+                *dyx = tok + 2 * ntok + bh * nc * L, *DT = DTws + bh * nc * L;
+    double sum = 0.0;
+    for (int64_t t = t0; t < t1; ++t) sum += (double)r[t];
+    seg[tid] = sum;
+    __syncthreads();
+    // exclusive suffix sum over the segments, in a fixed order
+    if (tid == 0) {
+        double acc = bnd[bh];
+        for (int i = 255; i >= 0; --i) {
+            const double v = seg[i];
+            seg[i] = acc;
+            acc += v;
+        }
+    }
+    __syncthreads();
+    const double Ah = (double)A[h];
+    double s = seg[tid], da = 0.0, dd = 0.0;
+    for (int64_t t = t1 - 1; t >= t0; --t) {
+        s += (double)r[t];
+        ddt[(b * T + t) * H + h] = (float)((double)xu[t] + Ah * s);
+        da += (double)DT[t] * s;
+        dd += (double)dyx[t];
+    }
+    red[0][tid] = da;
+    red[1][tid] = dd;
+    __syncthreads();
+    for (int st = 128; st > 0; st >>= 1) {
+        if (tid < st) {
+            red[0][tid] += red[0][tid + st];
+            red[1][tid] += red[1][tid + st];
+        }
+        __syncthreads();
+    }
+    if (tid == 0) {
+        part[bh] = red[0][0];
+        part[nbh + bh] = red[1][0];
+    }
+}
+
+// dA[h], dD[h]: the per-(b, h) parts summed over b in order
+__global__ void bwd_heads_kernel(const double *__restrict__ part, float *__restrict__ dA,
+                                 float *__restrict__ dD, int64_t Bt, int32_t H) {
+    const int h = blockIdx.x * blockDim.x + threadIdx.x;
+    if (h >= H) return;
+    double a = 0.0, d = 0.0;
+    for (int64_t b = 0; b < Bt; ++b) {
+        a += part[b * H + h];
+        d += part[Bt * H + b * H + h];
+    }
+    dA[h] = (float)a;
+    dD[h] = (float)d;
+}
+
+template <int L, int N, typename Tio, typename Thp>
+hipError_t launch_bwd_t(const Shape &s, const BwdArgs &a, hipStream_t st) {
+    const int64_t units = s.Bt * s.H * s.nc;
+    const int64_t T = s.T;
+    const int32_t H = (int32_t)s.H, G = (int32_t)s.G, nc = (int32_t)s.nc;
+    const Tio *x = (const Tio *)a.x, *B = (const Tio *)a.B, *C = (const Tio *)a.C;
+    if (units > 0) {
+        hipLaunchKernelGGL((bwd_dstate_kernel<L, N, Tio>), dim3((uint32_t)units), dim3(256), 0, st,
+                           a.dy, C, a.G, a.S, T, H, G, nc);
+    }
+    hipLaunchKernelGGL((bwd_passing_kernel<L, N>), dim3((uint32_t)(s.Bt * s.H)), dim3(256), 0, st,
+                       a.S, a.G, a.dfinal, a.fin, a.dinit, a.part + 2 * s.Bt * s.H, nc);
+    if (units > 0) {
+        constexpr int NTRI = (L / 64) * (L / 64 + 1) / 2;
+        const uint64_t ncb = (uint64_t)s.Bt * s.nc * s.G;
+        hipLaunchKernelGGL((bwd_cb_kernel<L, N, Tio>), dim3((uint32_t)(ncb * NTRI)), dim3(256), 0,
+                           st, B, C, a.CB, T, G, nc);
+        hipLaunchKernelGGL((bwd_dx_kernel<L, N, Tio, Thp>), dim3((uint32_t)(units * (L / 64))),
+                           dim3(256), 0, st, x, B, C, a.D, a.dy, a.G, a.DT, a.CB, a.S,
+                           (const Thp *)a.hprev, a.dx, a.tok, T, H, G, nc);
+        hipLaunchKernelGGL((bwd_dbdc_kernel<L, N, Tio, Thp>), dim3((uint32_t)(ncb * (L / 64) * 2)),
+                           dim3(256), 0, st, x, B, C, a.dy, a.G, a.DT, a.S, (const Thp *)a.hprev,
+                           a.dB, a.dC, T, H, G, nc);
+    }
+    hipLaunchKernelGGL((bwd_scalars_kernel<L>), dim3((uint32_t)(s.Bt * s.H)), dim3(256), 0, st,
+                       a.tok, a.DT, a.A, a.part + 2 * s.Bt * s.H, a.ddt, a.part, T, H, nc,
+                       (int64_t)units * L, (int64_t)(s.Bt * s.H));
+    hipLaunchKernelGGL(bwd_heads_kernel, dim3((uint32_t)((s.H + 63) / 64)), dim3(64), 0, st, a.part,
+                       a.dA, a.dD, (int64_t)s.Bt, H);
+    return hipGetLastError();
+}
+
+template <int L, int N>
+hipError_t launch_bwd_ln(const Shape &s, const BwdArgs &a, hipStream_t st) {
+    if (s.bf16) return launch_bwd_t<L, N, uint16_t, float>(s, a, st);
+    return launch_bwd_t<L, N, float, float>(s, a, st);
+}
+
+template <int L>
+hipError_t launch_bwd_l(const Shape &s, const BwdArgs &a, hipStream_t st) {
+    if (s.N == 64) return launch_bwd_ln<L, 64>(s, a, st);
+    if (s.N == 128) return launch_bwd_ln<L, 128>(s, a, st);
+    return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+size_t bwd_cb_bytes(const Shape &s) { return (size_t)s.Bt * s.nc * s.G * s.L * s.L * 4; }
+
+hipError_t launch_chunked_bwd(const Shape &s, const BwdArgs &a, hipStream_t st) {
+    if (s.Bt == 0) return hipSuccess;
+    if (s.L == 64) return launch_bwd_l<64>(s, a, st);
+    if (s.L == 128) return launch_bwd_l<128>(s, a, st);
+    if (s.L == 256) return launch_bwd_l<256>(s, a, st);
+    return hipErrorInvalidValue;
+}
+
+}  // namespace ssd

@@ -518,6 +518,105 @@ ssd_status ssd_decode_step_lp(void *state, const ssd_state_format *fmt, const vo
     return ok();
 }
 
+// Backward workspace: the forward's regions, then the final state, C B^T per
+// (b, chunk, group), three planes of per-token scalars, 3 * Bt*H fp64 partials and,
+// for bf16 io, h_prev again in fp32 (the forward keeps it in bf16 for its
+// MFMA; the decay gradient sums per-token products of it over the whole
+// sequence, where bf16's rounding would not cancel).
+struct BwdLayout {
+    Layout fwd;
+    size_t fin, cb, tok, part, hp32, total;
+};
+
+BwdLayout bwd_layout_of(const ssd::Shape &s) {
+    BwdLayout l;
+    l.fwd = layout_of(s);
+    const size_t bh = (size_t)s.Bt * s.H;
+    l.fin = align256(l.fwd.total);
+    l.cb = align256(l.fin + bh * s.P * s.N * sizeof(float));
+    l.tok = align256(l.cb + ssd::bwd_cb_bytes(s));
+    l.part = align256(l.tok + 3 * bh * s.nc * s.L * sizeof(float));
+    l.hp32 = align256(l.part + 3 * bh * sizeof(double));
+    const size_t hp = s.bf16 ? bh * s.nc * s.P * s.N * sizeof(float) : 0;
+    l.total = bh ? align256(l.hp32 + hp) : 0;
+    return l;
+}
+
+size_t ssd_chunked_bwd_workspace_size(const ssd_dims *dims, int64_t chunk_size) {
+    ssd::Shape s;
+    if (check_dims(dims, chunk_size, true, &s) != SSD_OK) return 0;
+    return bwd_layout_of(s).total;
+}
+
+ssd_status ssd_chunked_bwd(const void *x, const float *dt, const float *A, const void *B,
+                           const void *C, const float *D, int64_t chunk_size,
+                           const float *init_state, const float *dy, const float *dfinal,
+                           float *dx, float *ddt, float *dA, float *dB, float *dC, float *dD,
+                           float *dinit, const ssd_dims *dims, void *workspace,
+                           size_t workspace_bytes, void *stream) {
+    ssd::Shape s;
+    ssd_status r = check_dims(dims, chunk_size, true, &s);
+    if (r != SSD_OK) return r;
+    if (s.Bt > 0 && s.T > 0) {
+        REQUIRE_PTR(x);
+        REQUIRE_PTR(dt);
+        REQUIRE_PTR(B);
+        REQUIRE_PTR(C);
+        REQUIRE_PTR(dy);
+        REQUIRE_PTR(dx);
+        REQUIRE_PTR(ddt);
+        REQUIRE_PTR(dB);
+        REQUIRE_PTR(dC);
+    } else {  // no tokens: the token tensors are empty and may be NULL
+        OPTIONAL_PTR(x);
+        OPTIONAL_PTR(dt);
+        OPTIONAL_PTR(B);
+        OPTIONAL_PTR(C);
+        OPTIONAL_PTR(dy);
+        OPTIONAL_PTR(dx);
+        OPTIONAL_PTR(ddt);
+        OPTIONAL_PTR(dB);
+        OPTIONAL_PTR(dC);
+    }
+    REQUIRE_PTR(A);
+    REQUIRE_PTR(D);
+    REQUIRE_PTR(dA);
+    REQUIRE_PTR(dD);
+    OPTIONAL_PTR(init_state);
+    OPTIONAL_PTR(dfinal);
+    OPTIONAL_PTR(dinit);
+    const BwdLayout l = bwd_layout_of(s);
+    if (l.total && !workspace)
+        return fail(SSD_ERR_NULL, "workspace is NULL (%zu bytes needed)", l.total);
+    if (misaligned(workspace)) return fail(SSD_ERR_ALIGN, "workspace is not 16-byte aligned");
+    if (workspace_bytes < l.total)
+        return fail(SSD_ERR_WORKSPACE, "workspace_bytes = %zu < %zu required", workspace_bytes,
+                    l.total);
+    if (s.Bt == 0) return ok();
+    Ws w;
+    if ((r = check_ws(s, workspace, workspace_bytes, &w)) != SSD_OK) return r;
+    char *base = static_cast<char *>(workspace);
+    float *fin = reinterpret_cast<float *>(base + l.fin);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    // the forward's chunk quantities again: G, DT, S, then h_prev in fp32 and
+    // the final state (state_passing writes fp32 h_prev for fp32 io)
+    void *hp32 = s.bf16 ? static_cast<void *>(base + l.hp32) : w.hprev;
+    ssd::Shape s32 = s;
+    s32.bf16 = false;
+    if ((r = run_cumsum(s, dt, A, w, st, nullptr)) != SSD_OK) return r;
+    if ((r = run_state(s, x, B, w, st)) != SSD_OK) return r;
+    r = hip_result(ssd::launch_state_passing(s32, w.S, w.G, init_state, hp32, fin, st),
+                   "state_passing", st);
+    if (r != SSD_OK) return r;
+    ssd::BwdArgs a{x, B, C, A, D, dy, dfinal, fin, dinit, dx, ddt, dA, dB, dC, dD, w.G, w.DT,
+                   w.S, hp32, reinterpret_cast<float *>(base + l.cb),
+                   reinterpret_cast<float *>(base + l.tok),
+                   reinterpret_cast<double *>(base + l.part)};
+    r = hip_result(ssd::launch_chunked_bwd(s, a, st), "chunked_bwd", st);
+    if (r != SSD_OK) return r;
+    return ok();
+}
+
 const char *ssd_status_string(ssd_status status) {
     switch (status) {
     case SSD_OK: return "SSD_OK";

@@ -68,6 +68,23 @@ struct LowpArgs {
     const void *z;
 };
 hipError_t launch_decode_lowp(const Shape &s, const LowpArgs &a, hipStream_t st);
+
+// The backward of the chunked forward.  G, DT, hprev and fin come from the
+// forward stages run again on the same workspace; S (the forward's S region,
+// dead by then) receives the chunk adjoints; CB, tok (3 planes of
+// Bt*H*nc*L floats) and part (3 * Bt*H doubles) are backward scratch.
+struct BwdArgs {
+    const void *x, *B, *C;
+    const float *A, *D, *dy, *dfinal, *fin;
+    float *dinit, *dx, *ddt, *dA, *dB, *dC, *dD;
+    const float *G, *DT;
+    float *S;
+    const void *hprev;
+    float *CB, *tok;
+    double *part;
+};
+size_t bwd_cb_bytes(const Shape &s);
+hipError_t launch_chunked_bwd(const Shape &s, const BwdArgs &a, hipStream_t st);
 hipError_t launch_decode_step(const Shape &s, float *state, const void *x, const float *dt,
                               const void *B, const void *C, const float *A, const float *D,
                               void *y, const float *dt_bias, int softplus, const void *z,

@@ -97,6 +97,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "ssd_decode_step": ([vp, vp, vp, vp, vp, vp, vp, vp, dp, vp], st),
         "ssd_decode_multi": ([vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_uint32,
                               ctypes.POINTER(LayerOpts), dp, vp], st),
+        "ssd_chunked_bwd_workspace_size": ([dp, i64], sz),
+        "ssd_chunked_bwd": ([vp, vp, vp, vp, vp, vp, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                             vp, dp, vp, sz, vp], st),
         "ssd_decode_step_lp": ([vp, ctypes.POINTER(StateFormat), vp, vp, vp, vp, vp, vp, vp,
                                 ctypes.POINTER(LayerOpts), dp, vp], st),
         "ssd_status_string": ([st], ctypes.c_char_p),
@@ -464,3 +467,37 @@ def ssd_decode_step_lp(state, x_t, dt_t, B_t, C_t, A, D, fmt: str, scale=None,
         _ptr(D), _ptr(y_t), None if opts is None else ctypes.byref(opts), ctypes.byref(dims),
         _stream(dev)))
     return y_t
+
+
+def ssd_chunked_bwd_workspace_size(dims: Dims, chunk_size: int) -> int:
+    return int(load_library().ssd_chunked_bwd_workspace_size(ctypes.byref(dims), chunk_size))
+
+
+def ssd_chunked_bwd(x, dt, A, B, C, D, chunk_size, dy, init_state=None, dfinal=None,
+                    want_dinit: bool = True, workspace=None):
+    """Backward of ssd_chunked_fwd (no layer options).  Returns a dict of float32
+    gradients: dx [Bt,T,H,P], ddt [Bt,T,H], dA [H], dB and dC [Bt,T,G,N], dD [H],
+    dinit [Bt,H,P,N] (None unless ``want_dinit``).  dy [Bt,T,H,P] f32; dfinal
+    [Bt,H,P,N] f32 or None."""
+    a = FwdArgs(x, dt, A, B, C, D, chunk_size, init_state, want_final=False,
+                workspace=torch.empty(256, dtype=torch.uint8, device=x.device))
+    Bt, T, H, P = a.x.shape
+    G, N = a.B.shape[2], a.B.shape[3]
+    dev = a.device
+    dy = _need(dy, "dy", torch.float32, (Bt, T, H, P), dev)
+    if dfinal is not None:
+        dfinal = _need(dfinal, "dfinal", torch.float32, (Bt, H, P, N), dev)
+    need = ssd_chunked_bwd_workspace_size(a.dims, a.L)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    f32 = dict(dtype=torch.float32, device=dev)
+    out = dict(dx=torch.empty((Bt, T, H, P), **f32), ddt=torch.empty((Bt, T, H), **f32),
+               dA=torch.empty((H,), **f32), dB=torch.empty((Bt, T, G, N), **f32),
+               dC=torch.empty((Bt, T, G, N), **f32), dD=torch.empty((H,), **f32),
+               dinit=torch.empty((Bt, H, P, N), **f32) if want_dinit else None)
+    _check("ssd_chunked_bwd", load_library().ssd_chunked_bwd(
+        _ptr(a.x), _ptr(a.dt), _ptr(a.A), _ptr(a.B), _ptr(a.C), _ptr(a.D), a.L, _ptr(a.init),
+        _ptr(dy), _ptr(dfinal), _ptr(out["dx"]), _ptr(out["ddt"]), _ptr(out["dA"]),
+        _ptr(out["dB"]), _ptr(out["dC"]), _ptr(out["dD"]), _ptr(out["dinit"]),
+        ctypes.byref(a.dims), _ptr(workspace), workspace.numel(), _stream(dev)))
+    return out

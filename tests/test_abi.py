@@ -281,3 +281,30 @@ def test_decode_step_lp_is_validated():
     assert lp(SF(1, 1, 5, None), d=dims(N=96)) == -3
     assert lp(SF(0, 0, 0, None), state=None) == -1          # fp32: the plain step's checks
     assert lp(SF(3, 0, 0, 0x1000), d=dims(Bt=0)) == 0       # empty batch: no HIP call
+
+
+def test_chunked_bwd_workspace_and_validation():
+    L = lib()
+    d = dims(8, 4096, 80, 64, 128, 1)
+    fwd = ssd.ssd_chunked_fwd_workspace_size(d, 256)
+    bwd = ssd.ssd_chunked_bwd_workspace_size(d, 256)
+    nc, bh = 16, 8 * 80
+    assert bwd >= fwd + bh * 64 * 128 * 4 + 8 * nc * 256 * 256 * 4 + 3 * bh * nc * 256 * 4
+    assert bwd % 256 == 0
+    assert ssd.ssd_chunked_bwd_workspace_size(dims(N=96), 256) == 0
+    args = [P16] * 6 + [256] + [None, P16, None] + [P16] * 6 + [None]
+    call = lambda a, dd=dims(), ws=P16, wsb=1 << 40: L.ssd_chunked_bwd(
+        *a, ctypes.byref(dd), ws, wsb, None)
+    bad = list(args); bad[8] = None                      # dy
+    assert call(bad) == -1
+    bad = list(args); bad[12] = None                     # dA
+    assert call(bad) == -1
+    bad = list(args); bad[16] = P_MIS                    # dinit
+    assert call(bad) == -4
+    assert call(args, wsb=10) == -5
+    assert call(args, ws=None) == -1
+    assert call(args, dd=dims(N=96)) == -3
+    assert L.ssd_chunked_bwd(*args[:6], 100, *args[7:], ctypes.byref(dims()), P16, 1 << 40,
+                             None) == -3
+    # empty batch: no HIP call is made
+    assert call(args, dd=dims(Bt=0)) == 0

@@ -1,0 +1,112 @@
+"""GPU parity of the backward (ssd_chunked_bwd) through the C ABI against the
+fp64 oracle's exact adjoint ("Mamba-3 ... kernels", section "Backward", for
+the chunked order the GPU takes)."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from selective_state_space_amd import inputs as gen
+from selective_state_space_amd import ssd
+
+from _gpu import assert_close, dev_tensor, host, log, upload_fwd
+
+pytestmark = pytest.mark.gpu
+
+NAMES = ("dx", "ddt", "dA", "dB", "dC", "dD", "dinit")
+
+
+def run_both(inp, io, L, dy, dfin, want_dinit=True):
+    t = upload_fwd(inp, io)
+    g = ssd.ssd_chunked_bwd(t["x"], t["dt"], t["A"], t["B"], t["C"], t["D"], L, dev_tensor(dy),
+                            t["init_state"], None if dfin is None else dev_tensor(dfin),
+                            want_dinit=want_dinit)
+    torch.cuda.synchronize()
+    ref = oracle.token_bwd(inp.x, inp.dt, inp.A, inp.B, inp.C, inp.D, dy, inp.init_state, dfin)
+    return g, ref
+
+
+def compare(g, ref, io, names=NAMES):
+    for k in names:
+        if g.get(k) is not None:
+            assert_close(host(g[k]), ref[k], io, k)
+
+
+def grads_inputs(inp, seed, dfinal=True):
+    rng = np.random.default_rng(seed)
+    dy = rng.normal(0, 1, inp.x.shape).astype(np.float32)
+    Bt, T, H, P = inp.x.shape
+    N = inp.B.shape[3]
+    dfin = rng.normal(0, 1, (Bt, H, P, N)).astype(np.float32) if dfinal else None
+    return dy, dfin
+
+
+@pytest.mark.parametrize("io", [gen.F32, gen.BF16])
+@pytest.mark.parametrize("L", [64, 128, 256])
+@pytest.mark.parametrize("N", [64, 128])
+def test_backward_against_oracle(io, L, N):
+    log("bwd", io, "L", L, "N", N)
+    inp = gen.make_small(2, 2 * L + 29, 4, 64, N, 2, io, init_state=True, seed=L + N)
+    dy, dfin = grads_inputs(inp, 1)
+    g, ref = run_both(inp, io, L, dy, dfin)
+    compare(g, ref, io)
+
+
+@pytest.mark.parametrize("G", [1, 2, 8])
+def test_group_counts(G):
+    """dB and dC sum over the heads of a group: 8, 4 and 1 heads per group."""
+    log("bwd groups", G)
+    inp = gen.make_small(2, 300, 8, 64, 128, G, gen.BF16, init_state=True, seed=4)
+    dy, dfin = grads_inputs(inp, 2)
+    g, ref = run_both(inp, gen.BF16, 128, dy, dfin)
+    compare(g, ref, gen.BF16)
+
+
+def test_without_init_and_dfinal():
+    inp = gen.make_small(1, 200, 4, 64, 64, 1, gen.F32, init_state=False, seed=6)
+    dy, _ = grads_inputs(inp, 3, dfinal=False)
+    g, ref = run_both(inp, gen.F32, 64, dy, None)
+    compare(g, ref, gen.F32)
+    g2, _ = run_both(inp, gen.F32, 64, dy, None, want_dinit=False)
+    assert g2["dinit"] is None
+    for k in NAMES[:-1]:
+        assert torch.equal(g[k], g2[k]), k
+
+
+def test_reruns_are_bitwise_identical():
+    inp = gen.make_small(2, 333, 8, 64, 128, 2, gen.BF16, init_state=True, seed=8)
+    dy, dfin = grads_inputs(inp, 4)
+    t = upload_fwd(inp, gen.BF16)
+    args = (t["x"], t["dt"], t["A"], t["B"], t["C"], t["D"], 128, dev_tensor(dy), t["init_state"],
+            dev_tensor(dfin))
+    a = ssd.ssd_chunked_bwd(*args)
+    b = ssd.ssd_chunked_bwd(*args)
+    torch.cuda.synchronize()
+    for k in NAMES:
+        assert torch.equal(a[k], b[k]), k
+
+
+def test_no_tokens():
+    Bt, H, P, N = 2, 4, 64, 64
+    x = torch.empty((Bt, 0, H, P), device="cuda")
+    Bm = torch.empty((Bt, 0, 1, N), device="cuda")
+    dt = torch.empty((Bt, 0, H), device="cuda")
+    A = -torch.ones(H, device="cuda")
+    D = torch.ones(H, device="cuda")
+    dfin = torch.randn(Bt, H, P, N, device="cuda")
+    g = ssd.ssd_chunked_bwd(x, dt, A, Bm, Bm, D, 64, torch.empty((Bt, 0, H, P), device="cuda"),
+                            torch.randn(Bt, H, P, N, device="cuda"), dfin)
+    torch.cuda.synchronize()
+    assert torch.equal(g["dinit"], dfin)
+    assert torch.count_nonzero(g["dA"]) == 0 and torch.count_nonzero(g["dD"]) == 0
+
+
+def test_backward_full_size():
+    """The 2.7B-shaped layer: every gradient against the oracle."""
+    w = gen.WORKLOADS[2]
+    log("bwd full size", w.name)
+    inp = gen.make_fwd(w, 0)
+    dy, dfin = grads_inputs(inp, 5)
+    g, ref = run_both(inp, w.io_dtype, w.chunk_size, dy, dfin)
+    compare(g, ref, w.io_dtype)
