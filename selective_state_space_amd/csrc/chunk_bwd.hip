@@ -450,6 +450,254 @@ __global__ __launch_bounds__(256) void bwd_dbdc_kernel(
     }
 }
 
+// ---- bwd_dbdc_mfma: the same dB / dC on bf16 MFMA (bf16 io) ----------------
+// One 64-row block of one (b, c, g) per workgroup; wavefront w owns the 16-row
+// strip 16w..16w+15.  ORIENT 0 computes dC (rows k: the strip's dy rows times
+// the x rows of the chunk, inter term dy h_prev^T, final M B); ORIENT 1
+// computes dB (rows j: x rows times dy rows, inter term x ghat^T, final M^T C).
+// Per head the column-side rows (x or dy) and the inter operand (h_prev or
+// ghat, transposed to [n][p]) are staged in LDS; the strip's own rows are the
+// A operands, straight from global memory.  v_mfma_f32_16x16x32_bf16 layouts:
+// A lane l holds row l%16, k 8(l/16)..+7; B lane l holds column l%16, the same
+// k; D lane l holds rows 4(l/16)+e, column l%16.  M stays in the accumulators
+// over the heads (fp32) and goes through LDS for the final product.
+// Precision: dB and dC are small differences of large terms near the end of a
+// sequence (where dfinal enters), so every fp32 operand is carried as a bf16
+// head plus a bf16 remainder (x, B and C are bf16 already): products of two
+// split operands take three MFMAs (hi.hi + hi.lo + lo.hi), of one split
+// operand two, which leaves about 2^-16 of relative error instead of 2^-9.
+constexpr int SP = P + 8;     // LDS row pitch (bf16) of the staged [row][p] tiles
+
+__device__ __forceinline__ uint4 pack8(const float (&v)[8]) {
+    return make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
+                      pack_bf16x2(v[6], v[7]));
+}
+// v = hi + lo with hi = bf16(v), lo = bf16(v - hi)
+__device__ __forceinline__ void split8(const float (&v)[8], uint4 &hi, uint4 &lo) {
+    hi = pack8(v);
+    const uint32_t hw[4] = {hi.x, hi.y, hi.z, hi.w};
+    float r[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        r[2 * i] = v[2 * i] - bf16_lo(hw[i]);
+        r[2 * i + 1] = v[2 * i + 1] - bf16_hi(hw[i]);
+    }
+    lo = pack8(r);
+}
+__device__ __forceinline__ void split1(float v, uint16_t &hi, uint16_t &lo) {
+    const uint32_t h = pack_bf16x2(v, 0.f) & 0xffffu;
+    hi = (uint16_t)h;
+    lo = (uint16_t)(pack_bf16x2(v - __uint_as_float(h << 16), 0.f) & 0xffffu);
+}
+
+template <int L, int N, int ORIENT>
+__global__ __launch_bounds__(256) void bwd_dbdc_mfma_kernel(
+    const uint16_t *__restrict__ x, const uint16_t *__restrict__ B,
+    const uint16_t *__restrict__ C, const float *__restrict__ dy, const float *__restrict__ Gws,
+    const float *__restrict__ DTws, const float *__restrict__ gh, const float *__restrict__ hprev,
+    float *__restrict__ out, int64_t T, int32_t H, int32_t G, int32_t nc) {
+    constexpr int NT = L / 16, NN = N / 16;
+    constexpr int NCS = ORIENT == 1 ? 2 : 1;          // dy rows need a remainder copy
+    __shared__ __align__(16) uint16_t Cs[NCS][L * SP];  // column-side rows [row][p]; final: M
+    __shared__ __align__(16) uint16_t Ib[2][N * SP];    // inter operand [n][p]; final: V^T
+    __shared__ float Gs[L], DTs[L];
+    const int64_t blk = blockIdx.x;
+    const int rb = (int)(blk % (L / 64));
+    const int64_t bcg = blk / (L / 64);               // (b*nc + c)*G + g
+    const int32_t g = (int32_t)(bcg % G);
+    const int64_t bc = bcg / G;
+    const int32_t c = (int32_t)(bc % nc);
+    const int64_t b = bc / nc;
+    const int hpg = H / G;
+    const int r0 = 64 * rb;
+    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+    const int m = lane & 15, q = lane >> 4;
+    const int64_t tc = (int64_t)c * L;
+    // column range: ORIENT 0 -> [0, r0 + 64), ORIENT 1 -> [r0, L)
+    const int c_lo = ORIENT == 0 ? 0 : r0, c_hi = ORIENT == 0 ? r0 + 64 : L;
+    const int arow = r0 + 16 * w + m;                 // this lane's A-operand row
+    const int64_t ta = tc + arow;
+    f32x4 Macc[NT];
+    f32x4 dacc[NN];
+#pragma unroll
+    for (int i = 0; i < NT; ++i) Macc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < NN; ++i) dacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    for (int hh = 0; hh < hpg; ++hh) {
+        const int32_t h = g * hpg + hh;
+        const int64_t unit = ((b * H) + h) * nc + c;
+        __syncthreads();
+        // stage the column-side rows of the range (x exact, or dy as hi + lo)
+        for (int e = tid; e < (c_hi - c_lo) * (P / 8); e += 256) {
+            const int r = c_lo + e / (P / 8), p8 = 8 * (e % (P / 8));
+            const int64_t t = tc + r;
+            const int64_t o = ((b * T + (t < T ? t : 0)) * H + h) * P + p8;
+            if constexpr (ORIENT == 0) {
+                const uint4 v = t < T ? *reinterpret_cast<const uint4 *>(x + o)
+                                      : make_uint4(0u, 0u, 0u, 0u);
+                *reinterpret_cast<uint4 *>(&Cs[0][r * SP + p8]) = v;
+            } else {
+                float f[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+                if (t < T) {
+                    const float4 u0 = *reinterpret_cast<const float4 *>(dy + o);
+                    const float4 u1 = *reinterpret_cast<const float4 *>(dy + o + 4);
+                    f[0] = u0.x; f[1] = u0.y; f[2] = u0.z; f[3] = u0.w;
+                    f[4] = u1.x; f[5] = u1.y; f[6] = u1.z; f[7] = u1.w;
+                }
+                uint4 hi, lo;
+                split8(f, hi, lo);
+                *reinterpret_cast<uint4 *>(&Cs[0][r * SP + p8]) = hi;
+                *reinterpret_cast<uint4 *>(&Cs[NCS - 1][r * SP + p8]) = lo;
+            }
+        }
+        // the inter operand, transposed to [n][p], as hi + lo
+        const float *src = (ORIENT == 0 ? hprev : gh) + unit * (int64_t)(P * N);
+        for (int e = tid; e < P * N / 4; e += 256) {
+            const int p = e / (N / 4), n4 = 4 * (e % (N / 4));
+            const float4 v = *reinterpret_cast<const float4 *>(src + p * N + n4);
+            const float vv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) split1(vv[i], Ib[0][(n4 + i) * SP + p], Ib[1][(n4 + i) * SP + p]);
+        }
+        for (int e = tid; e < L; e += 256) {
+            Gs[e] = Gws[unit * L + e];
+            DTs[e] = DTws[unit * L + e];
+        }
+        __syncthreads();
+        // A operands: the strip's own rows (plain, and scaled for the inter term)
+        const float ga = Gs[arow], glast = Gs[L - 1];
+        const float sc = ORIENT == 0 ? fast_exp2(ga) : DTs[arow] * fast_exp2(glast - ga);
+        bf16x8 aS[2], aSl[2], aI[2], aIl[2];
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+            float f[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+            if (ta < T) {
+                const int64_t o = ((b * T + ta) * H + h) * P + 32 * st + 8 * q;
+                if constexpr (ORIENT == 0) {
+                    const float4 u0 = *reinterpret_cast<const float4 *>(dy + o);
+                    const float4 u1 = *reinterpret_cast<const float4 *>(dy + o + 4);
+                    f[0] = u0.x; f[1] = u0.y; f[2] = u0.z; f[3] = u0.w;
+                    f[4] = u1.x; f[5] = u1.y; f[6] = u1.z; f[7] = u1.w;
+                } else {
+                    const uint4 u = *reinterpret_cast<const uint4 *>(x + o);
+                    f[0] = bf16_lo(u.x); f[1] = bf16_hi(u.x); f[2] = bf16_lo(u.y); f[3] = bf16_hi(u.y);
+                    f[4] = bf16_lo(u.z); f[5] = bf16_hi(u.z); f[6] = bf16_lo(u.w); f[7] = bf16_hi(u.w);
+                }
+            }
+            uint4 hi, lo;
+            split8(f, hi, lo);                        // lo = 0 for x (bf16 already)
+            aS[st] = as_bf16x8(hi);
+            aSl[st] = as_bf16x8(lo);
+            float fs[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) fs[i] = f[i] * sc;
+            split8(fs, hi, lo);
+            aI[st] = as_bf16x8(hi);
+            aIl[st] = as_bf16x8(lo);
+        }
+        // S tiles of the column range, decayed and masked into M
+#pragma unroll
+        for (int jt = 0; jt < NT; ++jt) {
+            if (16 * jt < c_lo || 16 * jt >= c_hi) continue;
+            f32x4 s = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int st = 0; st < 2; ++st) {
+                const int off = (16 * jt + m) * SP + 32 * st + 8 * q;
+                const bf16x8 bh = as_bf16x8(*reinterpret_cast<const uint4 *>(&Cs[0][off]));
+                s = mfma16x16x32(aS[st], bh, s);
+                if constexpr (ORIENT == 0) {
+                    s = mfma16x16x32(aSl[st], bh, s);         // dy remainder . x
+                } else {
+                    const bf16x8 bl = as_bf16x8(*reinterpret_cast<const uint4 *>(&Cs[1][off]));
+                    s = mfma16x16x32(aS[st], bl, s);          // x . dy remainder
+                }
+            }
+            const int col = 16 * jt + m;
+            const float gc = Gs[col], dc = DTs[col];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int row = r0 + 16 * w + 4 * q + e;
+                const float gr = Gs[row];
+                float v;
+                if constexpr (ORIENT == 0)
+                    v = row >= col ? fast_exp2(gr - gc) * dc * s[e] : 0.f;
+                else
+                    v = col >= row ? fast_exp2(gc - gr) * DTs[row] * s[e] : 0.f;
+                Macc[jt][e] += v;
+            }
+        }
+        // inter term: (scaled strip rows) x (h_prev or ghat), K = P, three products
+#pragma unroll
+        for (int nt = 0; nt < NN; ++nt)
+#pragma unroll
+            for (int st = 0; st < 2; ++st) {
+                const int off = (16 * nt + m) * SP + 32 * st + 8 * q;
+                const bf16x8 bh = as_bf16x8(*reinterpret_cast<const uint4 *>(&Ib[0][off]));
+                const bf16x8 bl = as_bf16x8(*reinterpret_cast<const uint4 *>(&Ib[1][off]));
+                dacc[nt] = mfma16x16x32(aI[st], bh, dacc[nt]);
+                dacc[nt] = mfma16x16x32(aI[st], bl, dacc[nt]);
+                dacc[nt] = mfma16x16x32(aIl[st], bh, dacc[nt]);
+            }
+    }
+    // final: out(row, n) += sum_col M(row, col) V_col[n], V = B (dC) or C (dB);
+    // M goes through LDS as hi (rows 0..63 of Cs[0]) + lo (rows 0..63 of Ib[1])
+    const uint16_t *V = ORIENT == 0 ? B : C;
+    for (int cc = c_lo / 64; cc < c_hi / 64; ++cc) {
+        __syncthreads();
+#pragma unroll
+        for (int jt = 0; jt < NT; ++jt) {
+            if (jt / 4 != cc) continue;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                uint16_t hi, lo;
+                split1(Macc[jt][e], hi, lo);
+                const int r = 16 * w + 4 * q + e, cl = 16 * (jt % 4) + m;
+                Cs[0][r * SP + cl] = hi;
+                Ib[1][r * SP + cl] = lo;
+            }
+        }
+        // V rows of the chunk, transposed to [n][token]
+        for (int e = tid; e < 64 * N / 8; e += 256) {
+            const int r = e / (N / 8), n8 = 8 * (e % (N / 8));
+            const int64_t t = tc + 64 * cc + r;
+            uint4 v = make_uint4(0u, 0u, 0u, 0u);
+            if (t < T) v = *reinterpret_cast<const uint4 *>(V + ((b * T + t) * G + g) * N + n8);
+            const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                Ib[0][(n8 + 2 * i) * SP + r] = (uint16_t)(wv[i] & 0xffffu);
+                Ib[0][(n8 + 2 * i + 1) * SP + r] = (uint16_t)(wv[i] >> 16);
+            }
+        }
+        __syncthreads();
+        bf16x8 aM[2], aMl[2];
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+            aM[st] = as_bf16x8(*reinterpret_cast<const uint4 *>(&Cs[0][(16 * w + m) * SP + 32 * st + 8 * q]));
+            aMl[st] = as_bf16x8(
+                *reinterpret_cast<const uint4 *>(&Ib[1][(16 * w + m) * SP + 32 * st + 8 * q]));
+        }
+#pragma unroll
+        for (int nt = 0; nt < NN; ++nt)
+#pragma unroll
+            for (int st = 0; st < 2; ++st) {
+                const bf16x8 bv = as_bf16x8(
+                    *reinterpret_cast<const uint4 *>(&Ib[0][(16 * nt + m) * SP + 32 * st + 8 * q]));
+                dacc[nt] = mfma16x16x32(aM[st], bv, dacc[nt]);
+                dacc[nt] = mfma16x16x32(aMl[st], bv, dacc[nt]);
+            }
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const int64_t t = tc + r0 + 16 * w + 4 * q + e;
+        if (t < T)
+#pragma unroll
+            for (int nt = 0; nt < NN; ++nt)
+                out[((b * T + t) * G + g) * N + 16 * nt + m] = dacc[nt][e];
+    }
+}
+
 // ---- bwd_scalars: s_t = bnd + sum_{t' >= t} r_t' per (b, h); ddt, dA/dD parts
 // The running sums are kept in fp64: s_t sums thousands of terms of both signs
 // to a small value, and dA sums dt_t s_t over the sequence again.
@@ -540,9 +788,17 @@ hipError_t launch_bwd_t(const Shape &s, const BwdArgs &a, hipStream_t st) {
         hipLaunchKernelGGL((bwd_dx_kernel<L, N, Tio, Thp>), dim3((uint32_t)(units * (L / 64))),
                            dim3(256), 0, st, x, B, C, a.D, a.dy, a.G, a.DT, a.CB, a.S,
                            (const Thp *)a.hprev, a.dx, a.tok, T, H, G, nc);
-        hipLaunchKernelGGL((bwd_dbdc_kernel<L, N, Tio, Thp>), dim3((uint32_t)(ncb * (L / 64) * 2)),
-                           dim3(256), 0, st, x, B, C, a.dy, a.G, a.DT, a.S, (const Thp *)a.hprev,
-                           a.dB, a.dC, T, H, G, nc);
+        if constexpr (sizeof(Tio) == 2) {
+            const uint32_t nb = (uint32_t)(ncb * (L / 64));
+            hipLaunchKernelGGL((bwd_dbdc_mfma_kernel<L, N, 0>), dim3(nb), dim3(256), 0, st, x, B,
+                               C, a.dy, a.G, a.DT, a.S, (const float *)a.hprev, a.dC, T, H, G, nc);
+            hipLaunchKernelGGL((bwd_dbdc_mfma_kernel<L, N, 1>), dim3(nb), dim3(256), 0, st, x, B,
+                               C, a.dy, a.G, a.DT, a.S, (const float *)a.hprev, a.dB, T, H, G, nc);
+        } else {
+            hipLaunchKernelGGL((bwd_dbdc_kernel<L, N, Tio, Thp>),
+                               dim3((uint32_t)(ncb * (L / 64) * 2)), dim3(256), 0, st, x, B, C,
+                               a.dy, a.G, a.DT, a.S, (const Thp *)a.hprev, a.dB, a.dC, T, H, G, nc);
+        }
     }
     hipLaunchKernelGGL((bwd_scalars_kernel<L>), dim3((uint32_t)(s.Bt * s.H)), dim3(256), 0, st,
                        a.tok, a.DT, a.A, a.part + 2 * s.Bt * s.H, a.ddt, a.part, T, H, nc,
