@@ -322,7 +322,7 @@ ssd_status ssd_decode_step_lp(void *state, const ssd_state_format *fmt, const vo
 
 /*
  * The backward of ssd_chunked_fwd (no layer options): gradients of
- * L = sum(dy . y) + sum(dfinal . final_state).  "Mamba-3 ... kernels",
+ * L = sum(dy . y) + sum(dfinal . final_state).  The "mamba3" kernel card,
  * section "Backward": the forward's chunk states are recomputed on the
  * workspace, the state adjoint is scanned in reverse over the chunks between
  * two chunk-parallel passes, and there are no floating-point atomics: every

@@ -221,7 +221,7 @@ def token_decode_multi(state, x, dt, B, C, A, D, parent=None, update_state: bool
 def token_bwd(x, dt, A, B, C, D, dy, init_state=None, dfinal=None, nthreads: int = 0):
     """Float64 gradients of L = sum(dy * y) + sum(dfinal * final_state) for the
     plain forward (no layer options): the exact adjoint of the recurrence,
-    token by token ("Mamba-3 ... kernels", section "Backward", for the order a
+    token by token (the "mamba3" kernel card, section "Backward", for the order a
     chunked backward takes: a reverse scan of the state adjoint).
 
     Shapes as token_fwd, dy [Bt,T,H,P], dfinal [Bt,H,P,N] or None.  Returns a

@@ -216,7 +216,7 @@ int ssd_oracle_decode_gated(double *state, const float *x_t, const float *dt_t,
  *     g_{t-1} = a_t g_t,   and finally dL/d(init state) = g_0.
  *
  * This is the chain rule applied to the recurrence of the header comment
- * ("Mamba-3 ... kernels", section "Backward", gives the chunked order of the
+ * (the "mamba3" kernel card, section "Backward", gives the chunked order of the
  * same adjoint: a reverse scan of the state adjoint between chunk-parallel
  * passes).  Rows p of a head do not interact, so each row's forward states
  * are stored (T + 1 vectors of N) and walked back.  The unit of work is one

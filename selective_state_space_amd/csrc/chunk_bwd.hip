@@ -1,7 +1,7 @@
 // The backward of the chunked forward: gradients of L = sum(dy . y) +
 // sum(dfinal . final) with respect to x, dt, A, B, C, D and the initial state.
 //
-// "Mamba-3 ... kernels", section "Backward": two chunk-parallel passes around a
+// the "mamba3" kernel card, section "Backward": two chunk-parallel passes around a
 // reverse scan of the state adjoint, with the chunk intermediates recomputed
 // rather than stored, and no floating-point atomics (every output element has
 // one owner; sums over heads and batch rows are taken in a fixed order).

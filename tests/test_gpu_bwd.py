@@ -1,5 +1,5 @@
 """GPU parity of the backward (ssd_chunked_bwd) through the C ABI against the
-fp64 oracle's exact adjoint ("Mamba-3 ... kernels", section "Backward", for
+fp64 oracle's exact adjoint (the "mamba3" kernel card, section "Backward", for
 the chunked order the GPU takes)."""
 
 import numpy as np

@@ -1,5 +1,5 @@
 """Pins of the oracle's backward: the exact adjoint of the recurrence
-("Mamba-3 ... kernels", section "Backward", for the chunked order; the values
+(the "mamba3" kernel card, section "Backward", for the chunked order; the values
 are those of the chain rule on the token recurrence).
 
 Each gradient is checked against central differences of the forward oracle
