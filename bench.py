@@ -94,11 +94,12 @@ def decode_bytes(w, io_bytes=2):
 
 
 def kernel_source_sha(kernel: str) -> str:
-    """Hash of the sources a kernel is built from (its .hip file and the shared headers)."""
+    """Hash of the device code a kernel is built from (its .hip file and the
+    shared device header; the host-side launch declarations do not enter)."""
     import hashlib
     csrc = os.path.join(ROOT, "selective_state_space_amd", "csrc")
     h = hashlib.sha256()
-    for f in (kernel + ".hip", "ssd_device.h", "ssd_launch.h"):
+    for f in (kernel + ".hip", "ssd_device.h"):
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
