@@ -87,11 +87,15 @@ __global__ __launch_bounds__(256) void bwd_dstate_kernel(const float *__restrict
     constexpr int TN = N / 16;
     __shared__ __align__(16) float As[KT * LD];
     __shared__ __align__(16) float Bs[KT * (N + 4)];
-    const int64_t unit = blockIdx.x;              // (b*H + h)*nc + c
-    const int32_t c = (int32_t)(unit % nc);
-    const int64_t bh = unit / nc;
-    const int64_t b = bh / H;
-    const int32_t h = (int32_t)(bh % H), g = h / (H / G);
+    // logical order (b, c, g, head) with the head fastest, consecutive ids on
+    // one XCD: the heads of a group share the chunk's C rows in that L2
+    const int64_t blk = xcd_remap(blockIdx.x, gridDim.x);
+    const int hpg = H / G;
+    const int32_t h = (int32_t)((blk / hpg) % G) * hpg + (int32_t)(blk % hpg);
+    const int32_t g = h / hpg;
+    const int32_t c = (int32_t)((blk / H) % nc);
+    const int64_t b = blk / H / nc;
+    const int64_t unit = (b * H + h) * nc + c;
     const int tid = threadIdx.x;
     const int p0 = 4 * (tid >> 4), n0 = TN * (tid & 15);
     const float *Gc = Gws + unit * L;
@@ -171,7 +175,8 @@ __global__ __launch_bounds__(256) void bwd_passing_kernel(float *__restrict__ dS
 template <int L, int N, typename Tio>
 __global__ __launch_bounds__(256) void bwd_cb_kernel(const Tio *__restrict__ B,
                                                      const Tio *__restrict__ C,
-                                                     float *__restrict__ CB, int64_t T,
+                                                     float *__restrict__ CB,
+                                                     float *__restrict__ CBT, int64_t T,
                                                      int32_t G, int32_t nc) {
     constexpr int NB = L / 64, NTRI = NB * (NB + 1) / 2;
     __shared__ __align__(16) float As[KT * LD];
@@ -205,6 +210,13 @@ __global__ __launch_bounds__(256) void bwd_cb_kernel(const Tio *__restrict__ B,
     for (int i = 0; i < 4; ++i)
         *reinterpret_cast<float4 *>(o + i * L) =
             make_float4(acc[i][0], acc[i][1], acc[i][2], acc[i][3]);
+    if (CBT) {   // CBT[j][k] = CB[k][j]
+        float *ot = CBT + bcg * (int64_t)(L * L) + (int64_t)(64 * jb + n0) * L + 64 * kb + m0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            *reinterpret_cast<float4 *>(ot + j * L) =
+                make_float4(acc[0][j], acc[1][j], acc[2][j], acc[3][j]);
+    }
 }
 
 // ---- bwd_dx: dx and the per-token scalars of one (b, c, h, 64-row block) ----
@@ -489,6 +501,34 @@ __device__ __forceinline__ void split1(float v, uint16_t &hi, uint16_t &lo) {
     hi = (uint16_t)h;
     lo = (uint16_t)(pack_bf16x2(v - __uint_as_float(h << 16), 0.f) & 0xffffu);
 }
+// three bf16 terms: v = s0 + s1 + s2 up to about 2^-27 of v
+__device__ __forceinline__ void split8x3(const float (&v)[8], uint4 &s0, uint4 &s1, uint4 &s2) {
+    float r[8];
+    s0 = pack8(v);
+    const uint32_t a[4] = {s0.x, s0.y, s0.z, s0.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        r[2 * i] = v[2 * i] - bf16_lo(a[i]);
+        r[2 * i + 1] = v[2 * i + 1] - bf16_hi(a[i]);
+    }
+    s1 = pack8(r);
+    const uint32_t bq[4] = {s1.x, s1.y, s1.z, s1.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        r[2 * i] -= bf16_lo(bq[i]);
+        r[2 * i + 1] -= bf16_hi(bq[i]);
+    }
+    s2 = pack8(r);
+}
+__device__ __forceinline__ void split1x3(float v, uint16_t &s0, uint16_t &s1, uint16_t &s2) {
+    const uint32_t a = pack_bf16x2(v, 0.f) & 0xffffu;
+    const float r1 = v - __uint_as_float(a << 16);
+    const uint32_t bq = pack_bf16x2(r1, 0.f) & 0xffffu;
+    const float r2 = r1 - __uint_as_float(bq << 16);
+    s0 = (uint16_t)a;
+    s1 = (uint16_t)bq;
+    s2 = (uint16_t)(pack_bf16x2(r2, 0.f) & 0xffffu);
+}
 
 template <int L, int N, int ORIENT>
 __global__ __launch_bounds__(256) void bwd_dbdc_mfma_kernel(
@@ -501,7 +541,7 @@ __global__ __launch_bounds__(256) void bwd_dbdc_mfma_kernel(
     __shared__ __align__(16) uint16_t Cs[NCS][L * SP];  // column-side rows [row][p]; final: M
     __shared__ __align__(16) uint16_t Ib[2][N * SP];    // inter operand [n][p]; final: V^T
     __shared__ float Gs[L], DTs[L];
-    const int64_t blk = blockIdx.x;
+    const int64_t blk = xcd_remap(blockIdx.x, gridDim.x);   // row blocks of a group on one XCD
     const int rb = (int)(blk % (L / 64));
     const int64_t bcg = blk / (L / 64);               // (b*nc + c)*G + g
     const int32_t g = (int32_t)(bcg % G);
@@ -698,6 +738,233 @@ __global__ __launch_bounds__(256) void bwd_dbdc_mfma_kernel(
     }
 }
 
+// ---- bwd_dx_mfma: bwd_dx on bf16 MFMA with hi/lo-split operands (bf16 io) ----
+// One 64-row block of one (b, c, h) per workgroup, wavefront w owning rows
+// i0 + 16w .. +15; MFMA layouts as for bwd_dbdc_mfma.  Products (K in brackets):
+//   U_intra(i, p) = sum_{k >= i} W(k, i) dy_k[p]    [k]  A = W from CB^T rows, B = dy^T (LDS)
+//   Y_intra(i, p) = sum_{j <= i} V(i, j) x_j[p]     [j]  A = V from CB rows,   B = x^T  (LDS)
+//   U_inter(i, p) = sum_n B_i[n] ghat[p][n]         [n]  A = B rows, B = ghat (LDS [p][n])
+//   Y_inter(i, p) = sum_n C_i[n] h_prev[p][n]       [n]  A = C rows, B = h_prev (LDS)
+// with W(k, i) = exp2(G_k - G_i) CB(k, i) and V(i, j) = exp2(G_i - G_j) CB(i, j) dt_j;
+// the inter products are scaled per row afterwards (exp2(G_last - G_i), exp2(G_i)).
+// These feed ddt and the decay sums, which add thousands of per-token terms
+// with weights growing along the sequence, so every fp32 operand is carried as
+// three bf16 terms (about 2^-27 of it; two terms, 2^-18, left the full-size dA
+// at 0.7 of its bar): W x dy takes the six products of order up to 2^-16,
+// V x x and the inter products (x, B, C are bf16) three each.
+#ifndef BWD_INTRA3
+#define BWD_INTRA3 1
+#endif
+template <int L, int N>
+__global__ __launch_bounds__(256) void bwd_dx_mfma_kernel(
+    const uint16_t *__restrict__ x, const uint16_t *__restrict__ B, const uint16_t *__restrict__ C,
+    const float *__restrict__ D, const float *__restrict__ dy, const float *__restrict__ Gws,
+    const float *__restrict__ DTws, const float *__restrict__ CB, const float *__restrict__ CBT,
+    const float *__restrict__ gh, const float *__restrict__ hprev, float *__restrict__ dx,
+    float *__restrict__ tok, int64_t T, int32_t H, int32_t G, int32_t nc, int64_t ntok) {
+    constexpr int NB = L / 64, NP = P / 16, PN = N + 8;
+    // phase-shared LDS: the intra phases use T0/T1/T3 (dy^T in three terms) and
+    // T2 (x^T) as [p][64 tokens] tiles, the inter phases Ih/Im/Il as [p][N]
+    constexpr int NLDS = 3 * P * PN > 4 * P * SP ? 3 * P * PN : 4 * P * SP;
+    __shared__ __align__(16) uint16_t lds[NLDS];
+    __shared__ float Gs[L], DTs[L];
+    uint16_t *const T0 = lds, *const T1 = lds + P * SP, *const T3 = lds + 2 * P * SP,
+             *const T2 = lds + 3 * P * SP;
+    uint16_t *const Ih = lds, *const Im = lds + P * PN, *const Il = lds + 2 * P * PN;
+    // logical block order (b, c, g, row block, head) with the head fastest and
+    // consecutive ids on one XCD: the heads of a group reuse the same C B^T
+    // rows from that XCD's L2
+    const int64_t blk = xcd_remap(blockIdx.x, gridDim.x);
+    const int hpg = H / G;
+    const int32_t hh = (int32_t)(blk % hpg);
+    const int ib = (int)((blk / hpg) % NB);
+    const int64_t bcg = blk / hpg / NB;               // (b*nc + c)*G + g
+    const int32_t g = (int32_t)(bcg % G);
+    const int64_t bc = bcg / G;
+    const int32_t c = (int32_t)(bc % nc);
+    const int64_t b = bc / nc;
+    const int32_t h = g * hpg + hh;
+    const int64_t bh = b * H + h;
+    const int64_t unit = bh * nc + c;                 // (b*H + h)*nc + c
+    const int i0 = 64 * ib;
+    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+    const int m = lane & 15, q = lane >> 4;
+    const int64_t tc = (int64_t)c * L;
+    const int arow = i0 + 16 * w + m;                 // A-operand row of this lane
+    const float *CBr = CB + bcg * (int64_t)(L * L) + (int64_t)arow * L;
+    const float *CBTr = CBT + bcg * (int64_t)(L * L) + (int64_t)arow * L;
+    for (int e = tid; e < L; e += 256) {
+        Gs[e] = Gws[unit * L + e];
+        DTs[e] = DTws[unit * L + e];
+    }
+    f32x4 U[NP], Y[NP], Ui[NP], Yi[NP];
+#pragma unroll
+    for (int i = 0; i < NP; ++i) {
+        U[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+        Y[i] = U[i];
+        Ui[i] = U[i];
+        Yi[i] = U[i];
+    }
+    __syncthreads();
+    const float gi = Gs[arow];
+
+    // ---- U intra over token chunks kc >= ib
+    for (int kc = ib; kc < NB; ++kc) {
+        __syncthreads();
+        for (int e = tid; e < 64 * (P / 4); e += 256) {       // dy rows -> dy^T hi / lo
+            const int r = e / (P / 4), p4 = 4 * (e % (P / 4));
+            const int64_t t = tc + 64 * kc + r;
+            float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (t < T) v = *reinterpret_cast<const float4 *>(dy + ((b * T + t) * H + h) * P + p4);
+            const float vv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                split1x3(vv[i], T0[(p4 + i) * SP + r], T1[(p4 + i) * SP + r], T3[(p4 + i) * SP + r]);
+        }
+        __syncthreads();
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+            const int k0 = 64 * kc + 32 * st + 8 * q;         // this lane's 8 k's
+            const float4 c0 = *reinterpret_cast<const float4 *>(CBTr + k0);
+            const float4 c1 = *reinterpret_cast<const float4 *>(CBTr + k0 + 4);
+            const float cv[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+            float wv[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int k = k0 + i;
+                wv[i] = k >= arow ? fast_exp2(Gs[k] - gi) * cv[i] : 0.f;
+            }
+            uint4 a0, a1, a2;
+            split8x3(wv, a0, a1, a2);
+#pragma unroll
+            for (int pt = 0; pt < NP; ++pt) {
+                const int off = (16 * pt + m) * SP + 32 * st + 8 * q;
+                const bf16x8 b0 = as_bf16x8(*reinterpret_cast<const uint4 *>(T0 + off));
+                const bf16x8 b1 = as_bf16x8(*reinterpret_cast<const uint4 *>(T1 + off));
+                const bf16x8 b2 = as_bf16x8(*reinterpret_cast<const uint4 *>(T3 + off));
+                // the products of order 2^-16 and above, smallest first
+                if (BWD_INTRA3) {
+                U[pt] = mfma16x16x32(as_bf16x8(a2), b0, U[pt]);
+                U[pt] = mfma16x16x32(as_bf16x8(a0), b2, U[pt]);
+                U[pt] = mfma16x16x32(as_bf16x8(a1), b1, U[pt]);
+                }
+                U[pt] = mfma16x16x32(as_bf16x8(a1), b0, U[pt]);
+                U[pt] = mfma16x16x32(as_bf16x8(a0), b1, U[pt]);
+                U[pt] = mfma16x16x32(as_bf16x8(a0), b0, U[pt]);
+            }
+        }
+    }
+    // ---- Y intra over token chunks jc <= ib
+    for (int jc = 0; jc <= ib; ++jc) {
+        __syncthreads();
+        for (int e = tid; e < 64 * (P / 8); e += 256) {       // x rows -> x^T (exact)
+            const int r = e / (P / 8), p8 = 8 * (e % (P / 8));
+            const int64_t t = tc + 64 * jc + r;
+            uint4 v = make_uint4(0u, 0u, 0u, 0u);
+            if (t < T) v = *reinterpret_cast<const uint4 *>(x + ((b * T + t) * H + h) * P + p8);
+            const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                T2[(p8 + 2 * i) * SP + r] = (uint16_t)(wv[i] & 0xffffu);
+                T2[(p8 + 2 * i + 1) * SP + r] = (uint16_t)(wv[i] >> 16);
+            }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+            const int j0 = 64 * jc + 32 * st + 8 * q;
+            const float4 c0 = *reinterpret_cast<const float4 *>(CBr + j0);
+            const float4 c1 = *reinterpret_cast<const float4 *>(CBr + j0 + 4);
+            const float cv[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+            float vv[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int j = j0 + i;
+                vv[i] = j <= arow ? fast_exp2(gi - Gs[j]) * cv[i] * DTs[j] : 0.f;
+            }
+            uint4 a0, a1, a2;
+            split8x3(vv, a0, a1, a2);
+#pragma unroll
+            for (int pt = 0; pt < NP; ++pt) {
+                const int off = (16 * pt + m) * SP + 32 * st + 8 * q;
+                const bf16x8 bx = as_bf16x8(*reinterpret_cast<const uint4 *>(T2 + off));
+                if (BWD_INTRA3) Y[pt] = mfma16x16x32(as_bf16x8(a2), bx, Y[pt]);
+                Y[pt] = mfma16x16x32(as_bf16x8(a1), bx, Y[pt]);
+                Y[pt] = mfma16x16x32(as_bf16x8(a0), bx, Y[pt]);
+            }
+        }
+    }
+    // ---- inter products: U_inter with (B rows, ghat), then Y_inter with (C rows, h_prev)
+    const int64_t ta = tc + arow;
+#pragma unroll
+    for (int ph = 0; ph < 2; ++ph) {
+        const float *src = (ph == 0 ? gh : hprev) + unit * (int64_t)(P * N);
+        __syncthreads();
+        for (int e = tid; e < P * N / 4; e += 256) {          // [p][n] hi / lo
+            const int p = e / (N / 4), n4 = 4 * (e % (N / 4));
+            const float4 v = *reinterpret_cast<const float4 *>(src + p * N + n4);
+            const float vv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                split1x3(vv[i], Ih[p * PN + n4 + i], Im[p * PN + n4 + i], Il[p * PN + n4 + i]);
+        }
+        __syncthreads();
+        const uint16_t *rows = (ph == 0 ? B : C) + ((b * T + (ta < T ? ta : 0)) * G + g) * N;
+#pragma unroll
+        for (int ks = 0; ks < N / 32; ++ks) {
+            uint4 av = make_uint4(0u, 0u, 0u, 0u);
+            if (ta < T) av = *reinterpret_cast<const uint4 *>(rows + 32 * ks + 8 * q);
+#pragma unroll
+            for (int pt = 0; pt < NP; ++pt) {
+                const int off = (16 * pt + m) * PN + 32 * ks + 8 * q;
+                const bf16x8 b0 = as_bf16x8(*reinterpret_cast<const uint4 *>(Ih + off));
+                const bf16x8 b1 = as_bf16x8(*reinterpret_cast<const uint4 *>(Im + off));
+                const bf16x8 b2 = as_bf16x8(*reinterpret_cast<const uint4 *>(Il + off));
+                f32x4 &acc = ph == 0 ? Ui[pt] : Yi[pt];
+                acc = mfma16x16x32(as_bf16x8(av), b2, acc);
+                acc = mfma16x16x32(as_bf16x8(av), b1, acc);
+                acc = mfma16x16x32(as_bf16x8(av), b0, acc);
+            }
+        }
+    }
+    // ---- epilogue: rows i = i0 + 16w + 4q + e, columns p = 16 pt + m
+    const float Dh = D[h], glast = Gs[L - 1];
+    float *tokc = tok + unit * (int64_t)L;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const int i = i0 + 16 * w + 4 * q + e;
+        const int64_t t = tc + i;
+        const bool real = t < T;
+        const int64_t tt = real ? t : 0;
+        const float su = fast_exp2(glast - Gs[i]), sy = fast_exp2(Gs[i]), dti = DTs[i];
+        float xu = 0.f, dyy = 0.f, dyx = 0.f;
+#pragma unroll
+        for (int pt = 0; pt < NP; ++pt) {
+            const int p = 16 * pt + m;
+            const int64_t o = ((b * T + tt) * H + h) * P + p;
+            const float dyv = real ? dy[o] : 0.f;
+            const float xv = real ? bf16_to_f32(x[o]) : 0.f;
+            const float u = U[pt][e] + su * Ui[pt][e];
+            const float yv = Y[pt][e] + sy * Yi[pt][e];
+            if (real) dx[o] = Dh * dyv + dti * u;
+            xu = fmaf(xv, u, xu);
+            dyy = fmaf(dyv, yv, dyy);
+            dyx = fmaf(dyv, xv, dyx);
+        }
+#pragma unroll
+        for (int o = 1; o < 16; o <<= 1) {
+            xu += __shfl_xor(xu, o, 64);
+            dyy += __shfl_xor(dyy, o, 64);
+            dyx += __shfl_xor(dyx, o, 64);
+        }
+        if (m == 0) {
+            tokc[i] = xu;
+            tokc[ntok + i] = dyy - dti * xu;
+            tokc[2 * ntok + i] = dyx;
+        }
+    }
+}
+
 // ---- bwd_scalars: s_t = bnd + sum_{t' >= t} r_t' per (b, h); ddt, dA/dD parts
 // The running sums are kept in fp64: s_t sums thousands of terms of both signs
 // to a small value, and dA sums dt_t s_t over the sequence again.
@@ -784,10 +1051,16 @@ hipError_t launch_bwd_t(const Shape &s, const BwdArgs &a, hipStream_t st) {
         constexpr int NTRI = (L / 64) * (L / 64 + 1) / 2;
         const uint64_t ncb = (uint64_t)s.Bt * s.nc * s.G;
         hipLaunchKernelGGL((bwd_cb_kernel<L, N, Tio>), dim3((uint32_t)(ncb * NTRI)), dim3(256), 0,
-                           st, B, C, a.CB, T, G, nc);
-        hipLaunchKernelGGL((bwd_dx_kernel<L, N, Tio, Thp>), dim3((uint32_t)(units * (L / 64))),
-                           dim3(256), 0, st, x, B, C, a.D, a.dy, a.G, a.DT, a.CB, a.S,
-                           (const Thp *)a.hprev, a.dx, a.tok, T, H, G, nc);
+                           st, B, C, a.CB, a.CBT, T, G, nc);
+        if constexpr (sizeof(Tio) == 2)
+            hipLaunchKernelGGL((bwd_dx_mfma_kernel<L, N>), dim3((uint32_t)(units * (L / 64))),
+                               dim3(256), 0, st, x, B, C, a.D, a.dy, a.G, a.DT, a.CB, a.CBT, a.S,
+                               (const float *)a.hprev, a.dx, a.tok, T, H, G, nc,
+                               (int64_t)units * L);
+        else
+            hipLaunchKernelGGL((bwd_dx_kernel<L, N, Tio, Thp>), dim3((uint32_t)(units * (L / 64))),
+                               dim3(256), 0, st, x, B, C, a.D, a.dy, a.G, a.DT, a.CB, a.S,
+                               (const Thp *)a.hprev, a.dx, a.tok, T, H, G, nc);
         if constexpr (sizeof(Tio) == 2) {
             const uint32_t nb = (uint32_t)(ncb * (L / 64));
             hipLaunchKernelGGL((bwd_dbdc_mfma_kernel<L, N, 0>), dim3(nb), dim3(256), 0, st, x, B,

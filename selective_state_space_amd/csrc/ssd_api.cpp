@@ -519,13 +519,13 @@ ssd_status ssd_decode_step_lp(void *state, const ssd_state_format *fmt, const vo
 }
 
 // Backward workspace: the forward's regions, then the final state, C B^T per
-// (b, chunk, group), three planes of per-token scalars, 3 * Bt*H fp64 partials and,
+// (b, chunk, group) (and its transpose for bf16 io), three planes of per-token scalars, 3 * Bt*H fp64 partials and,
 // for bf16 io, h_prev again in fp32 (the forward keeps it in bf16 for its
 // MFMA; the decay gradient sums per-token products of it over the whole
 // sequence, where bf16's rounding would not cancel).
 struct BwdLayout {
     Layout fwd;
-    size_t fin, cb, tok, part, hp32, total;
+    size_t fin, cb, cbt, tok, part, hp32, total;
 };
 
 BwdLayout bwd_layout_of(const ssd::Shape &s) {
@@ -534,7 +534,8 @@ BwdLayout bwd_layout_of(const ssd::Shape &s) {
     const size_t bh = (size_t)s.Bt * s.H;
     l.fin = align256(l.fwd.total);
     l.cb = align256(l.fin + bh * s.P * s.N * sizeof(float));
-    l.tok = align256(l.cb + ssd::bwd_cb_bytes(s));
+    l.cbt = align256(l.cb + ssd::bwd_cb_bytes(s));
+    l.tok = align256(l.cbt + (s.bf16 ? ssd::bwd_cb_bytes(s) : 0));
     l.part = align256(l.tok + 3 * bh * s.nc * s.L * sizeof(float));
     l.hp32 = align256(l.part + 3 * bh * sizeof(double));
     const size_t hp = s.bf16 ? bh * s.nc * s.P * s.N * sizeof(float) : 0;
@@ -610,6 +611,7 @@ ssd_status ssd_chunked_bwd(const void *x, const float *dt, const float *A, const
     if (r != SSD_OK) return r;
     ssd::BwdArgs a{x, B, C, A, D, dy, dfinal, fin, dinit, dx, ddt, dA, dB, dC, dD, w.G, w.DT,
                    w.S, hp32, reinterpret_cast<float *>(base + l.cb),
+                   s.bf16 ? reinterpret_cast<float *>(base + l.cbt) : nullptr,
                    reinterpret_cast<float *>(base + l.tok),
                    reinterpret_cast<double *>(base + l.part)};
     r = hip_result(ssd::launch_chunked_bwd(s, a, st), "chunked_bwd", st);

@@ -71,7 +71,7 @@ hipError_t launch_decode_lowp(const Shape &s, const LowpArgs &a, hipStream_t st)
 
 // The backward of the chunked forward.  G, DT, hprev and fin come from the
 // forward stages run again on the same workspace; S (the forward's S region,
-// dead by then) receives the chunk adjoints; CB, tok (3 planes of
+// dead by then) receives the chunk adjoints; CB (and CBT), tok (3 planes of
 // Bt*H*nc*L floats) and part (3 * Bt*H doubles) are backward scratch.
 struct BwdArgs {
     const void *x, *B, *C;
@@ -80,7 +80,7 @@ struct BwdArgs {
     const float *G, *DT;
     float *S;
     const void *hprev;
-    float *CB, *tok;
+    float *CB, *CBT, *tok;   // CBT: CB transposed, bf16 io only (NULL otherwise)
     double *part;
 };
 size_t bwd_cb_bytes(const Shape &s);
