@@ -48,9 +48,10 @@ def log(*a):
 def algorithmic(w, io_bytes: int):
     """Bytes and useful flops each stage must move/compute for workload w.
 
-    Per (b, h, chunk) unit, L tokens, P = 64, N: see DESIGN.md ("Algorithmic
-    bytes and flops").  B and C are per group and chunk, so their bytes are
-    shared by the heads_per_group heads of a group.
+    Per (b, h, chunk) unit, L tokens, P = 64, N: the bytes each stage must
+    read and write once and the flops of its useful products (causal pairs
+    only).  B and C are per group and chunk, so their bytes are shared by the
+    heads_per_group heads of a group.
     """
     Bt, T, H, P, N, G, L = w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.ngroups, w.chunk_size
     nc = -(-T // L)

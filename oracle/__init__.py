@@ -7,7 +7,7 @@ Three independent CPU computations of the same layer, all float64:
 
 * :func:`token_fwd` / :func:`token_decode` -- the plain token-by-token
   recurrence, in C (``ssd_oracle.c``, POSIX threads).  This is the oracle the
-  GPU path is judged against.
+  GPU path is compared with.
 * :func:`chunked_reference` -- the chunked (SSD) form in NumPy, written out
   from its equations: chunk-local cumulative log-decay G, per-chunk states,
   the state pass between chunks, and the chunk output with the decayed,
@@ -28,7 +28,7 @@ TensorRT-LLM"):
 * the three-stage decomposition (cumulative sum per chunk, state carried from
   chunk to chunk, chunk output): [T] sections "Kernel 1" to "Kernel 3".
 
-Readings where the pages are silent or disagree (all listed in the design doc):
+Readings where the pages are silent or disagree:
 the output uses the updated state h_t; the state is stored [P][N]; head h
 uses group h // (H/G); positions past the end of a ragged last chunk carry
 dt = 0; a missing initial state means zeros.

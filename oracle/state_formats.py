@@ -26,7 +26,7 @@ the multipliers 0xD2511F53 and 0xCD9E8D57, a swap-and-xor with the key, and a
 Weyl increment of the key by (0x9E3779B9, 0xBB67AE85); 10 rounds is the
 generator's standard count.
 
-Readings (listed with the others in the design notes): the abs-max is over
+Readings where the page is silent: the abs-max is over
 the N values of a row; codes round half to even and are clipped to
 [-32767, 32767]; an all-zero row stores codes 0 and decode scale 0; one
 Philox block serves 4 consecutive elements of a row, its counter being the
