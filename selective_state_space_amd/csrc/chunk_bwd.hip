@@ -738,9 +738,11 @@ __global__ __launch_bounds__(256) void bwd_dbdc_mfma_kernel(
     }
 }
 
-// ---- bwd_dx_mfma: bwd_dx on bf16 MFMA with hi/lo-split operands (bf16 io) ----
-// One 64-row block of one (b, c, h) per workgroup, wavefront w owning rows
-// i0 + 16w .. +15; MFMA layouts as for bwd_dbdc_mfma.  Products (K in brackets):
+// ---- bwd_dx_mfma: bwd_dx on bf16 MFMA with split operands (bf16 io) ------
+// One (b, c, h) per workgroup of L/16 wavefronts, wavefront w owning rows
+// 16w .. 16w+15, so each head's operands are staged once and the causal work
+// per wavefront is the same (U takes k >= i, Y takes j <= i); MFMA layouts
+// as for bwd_dbdc_mfma.  Products (K in brackets):
 //   U_intra(i, p) = sum_{k >= i} W(k, i) dy_k[p]    [k]  A = W from CB^T rows, B = dy^T (LDS)
 //   Y_intra(i, p) = sum_{j <= i} V(i, j) x_j[p]     [j]  A = V from CB rows,   B = x^T  (LDS)
 //   U_inter(i, p) = sum_n B_i[n] ghat[p][n]         [n]  A = B rows, B = ghat (LDS [p][n])
@@ -756,13 +758,14 @@ __global__ __launch_bounds__(256) void bwd_dbdc_mfma_kernel(
 #define BWD_INTRA3 1
 #endif
 template <int L, int N>
-__global__ __launch_bounds__(256) void bwd_dx_mfma_kernel(
+__global__ __launch_bounds__(4 * L) void bwd_dx_mfma_kernel(
     const uint16_t *__restrict__ x, const uint16_t *__restrict__ B, const uint16_t *__restrict__ C,
     const float *__restrict__ D, const float *__restrict__ dy, const float *__restrict__ Gws,
     const float *__restrict__ DTws, const float *__restrict__ CB, const float *__restrict__ CBT,
     const float *__restrict__ gh, const float *__restrict__ hprev, float *__restrict__ dx,
     float *__restrict__ tok, int64_t T, int32_t H, int32_t G, int32_t nc, int64_t ntok) {
     constexpr int NB = L / 64, NP = P / 16, PN = N + 8;
+    constexpr int NTH = 4 * L;                        // L/16 wavefronts: one 16-row strip each
     // phase-shared LDS: the intra phases use T0/T1/T3 (dy^T in three terms) and
     // T2 (x^T) as [p][64 tokens] tiles, the inter phases Ih/Im/Il as [p][N]
     constexpr int NLDS = 3 * P * PN > 4 * P * SP ? 3 * P * PN : 4 * P * SP;
@@ -771,14 +774,13 @@ __global__ __launch_bounds__(256) void bwd_dx_mfma_kernel(
     uint16_t *const T0 = lds, *const T1 = lds + P * SP, *const T3 = lds + 2 * P * SP,
              *const T2 = lds + 3 * P * SP;
     uint16_t *const Ih = lds, *const Im = lds + P * PN, *const Il = lds + 2 * P * PN;
-    // logical block order (b, c, g, row block, head) with the head fastest and
+    // logical block order (b, c, g, head) with the head fastest and
     // consecutive ids on one XCD: the heads of a group reuse the same C B^T
     // rows from that XCD's L2
     const int64_t blk = xcd_remap(blockIdx.x, gridDim.x);
     const int hpg = H / G;
     const int32_t hh = (int32_t)(blk % hpg);
-    const int ib = (int)((blk / hpg) % NB);
-    const int64_t bcg = blk / hpg / NB;               // (b*nc + c)*G + g
+    const int64_t bcg = blk / hpg;                    // (b*nc + c)*G + g
     const int32_t g = (int32_t)(bcg % G);
     const int64_t bc = bcg / G;
     const int32_t c = (int32_t)(bc % nc);
@@ -786,14 +788,14 @@ __global__ __launch_bounds__(256) void bwd_dx_mfma_kernel(
     const int32_t h = g * hpg + hh;
     const int64_t bh = b * H + h;
     const int64_t unit = bh * nc + c;                 // (b*H + h)*nc + c
-    const int i0 = 64 * ib;
+    const int i0 = 0;                                 // the workgroup covers the chunk
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
     const int m = lane & 15, q = lane >> 4;
     const int64_t tc = (int64_t)c * L;
     const int arow = i0 + 16 * w + m;                 // A-operand row of this lane
     const float *CBr = CB + bcg * (int64_t)(L * L) + (int64_t)arow * L;
     const float *CBTr = CBT + bcg * (int64_t)(L * L) + (int64_t)arow * L;
-    for (int e = tid; e < L; e += 256) {
+    for (int e = tid; e < L; e += NTH) {
         Gs[e] = Gws[unit * L + e];
         DTs[e] = DTws[unit * L + e];
     }
@@ -808,10 +810,11 @@ __global__ __launch_bounds__(256) void bwd_dx_mfma_kernel(
     __syncthreads();
     const float gi = Gs[arow];
 
-    // ---- U intra over token chunks kc >= ib
-    for (int kc = ib; kc < NB; ++kc) {
+    // ---- U intra over the token chunks; strip w takes part from the chunk
+    // holding its rows on (k >= i)
+    for (int kc = 0; kc < NB; ++kc) {
         __syncthreads();
-        for (int e = tid; e < 64 * (P / 4); e += 256) {       // dy rows -> dy^T hi / lo
+        for (int e = tid; e < 64 * (P / 4); e += NTH) {       // dy rows -> dy^T hi / lo
             const int r = e / (P / 4), p4 = 4 * (e % (P / 4));
             const int64_t t = tc + 64 * kc + r;
             float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -822,6 +825,7 @@ __global__ __launch_bounds__(256) void bwd_dx_mfma_kernel(
                 split1x3(vv[i], T0[(p4 + i) * SP + r], T1[(p4 + i) * SP + r], T3[(p4 + i) * SP + r]);
         }
         __syncthreads();
+        if (16 * w <= 64 * kc + 63)
 #pragma unroll
         for (int st = 0; st < 2; ++st) {
             const int k0 = 64 * kc + 32 * st + 8 * q;         // this lane's 8 k's
@@ -854,10 +858,10 @@ __global__ __launch_bounds__(256) void bwd_dx_mfma_kernel(
             }
         }
     }
-    // ---- Y intra over token chunks jc <= ib
-    for (int jc = 0; jc <= ib; ++jc) {
+    // ---- Y intra over the token chunks up to the one holding strip w's rows
+    for (int jc = 0; jc < NB; ++jc) {
         __syncthreads();
-        for (int e = tid; e < 64 * (P / 8); e += 256) {       // x rows -> x^T (exact)
+        for (int e = tid; e < 64 * (P / 8); e += NTH) {       // x rows -> x^T (exact)
             const int r = e / (P / 8), p8 = 8 * (e % (P / 8));
             const int64_t t = tc + 64 * jc + r;
             uint4 v = make_uint4(0u, 0u, 0u, 0u);
@@ -870,6 +874,7 @@ __global__ __launch_bounds__(256) void bwd_dx_mfma_kernel(
             }
         }
         __syncthreads();
+        if (16 * w + 15 >= 64 * jc)
 #pragma unroll
         for (int st = 0; st < 2; ++st) {
             const int j0 = 64 * jc + 32 * st + 8 * q;
@@ -900,7 +905,7 @@ __global__ __launch_bounds__(256) void bwd_dx_mfma_kernel(
     for (int ph = 0; ph < 2; ++ph) {
         const float *src = (ph == 0 ? gh : hprev) + unit * (int64_t)(P * N);
         __syncthreads();
-        for (int e = tid; e < P * N / 4; e += 256) {          // [p][n] hi / lo
+        for (int e = tid; e < P * N / 4; e += NTH) {          // [p][n] hi / lo
             const int p = e / (N / 4), n4 = 4 * (e % (N / 4));
             const float4 v = *reinterpret_cast<const float4 *>(src + p * N + n4);
             const float vv[4] = {v.x, v.y, v.z, v.w};
@@ -1053,8 +1058,8 @@ hipError_t launch_bwd_t(const Shape &s, const BwdArgs &a, hipStream_t st) {
         hipLaunchKernelGGL((bwd_cb_kernel<L, N, Tio>), dim3((uint32_t)(ncb * NTRI)), dim3(256), 0,
                            st, B, C, a.CB, a.CBT, T, G, nc);
         if constexpr (sizeof(Tio) == 2)
-            hipLaunchKernelGGL((bwd_dx_mfma_kernel<L, N>), dim3((uint32_t)(units * (L / 64))),
-                               dim3(256), 0, st, x, B, C, a.D, a.dy, a.G, a.DT, a.CB, a.CBT, a.S,
+            hipLaunchKernelGGL((bwd_dx_mfma_kernel<L, N>), dim3((uint32_t)units),
+                               dim3(4 * L), 0, st, x, B, C, a.D, a.dy, a.G, a.DT, a.CB, a.CBT, a.S,
                                (const float *)a.hprev, a.dx, a.tok, T, H, G, nc,
                                (int64_t)units * L);
         else
