@@ -529,6 +529,23 @@ __device__ __forceinline__ void split1x3(float v, uint16_t &s0, uint16_t &s1, ui
     s1 = (uint16_t)bq;
     s2 = (uint16_t)(pack_bf16x2(r2, 0.f) & 0xffffu);
 }
+// the two 16-bit halves of a word: lo = the element of the even index
+__device__ __forceinline__ uint32_t pair16(uint32_t lo, uint32_t hi) { return (lo & 0xffffu) | (hi << 16); }
+__device__ __forceinline__ void split2x3(float a, float b, uint32_t &s0, uint32_t &s1, uint32_t &s2) {
+    uint16_t a0, a1, a2, b0, b1, b2;
+    split1x3(a, a0, a1, a2);
+    split1x3(b, b0, b1, b2);
+    s0 = pair16(a0, b0);
+    s1 = pair16(a1, b1);
+    s2 = pair16(a2, b2);
+}
+__device__ __forceinline__ void split2(float a, float b, uint32_t &hi, uint32_t &lo) {
+    uint16_t ah, al, bh, bl;
+    split1(a, ah, al);
+    split1(b, bh, bl);
+    hi = pair16(ah, bh);
+    lo = pair16(al, bl);
+}
 
 template <int L, int N, int ORIENT>
 __global__ __launch_bounds__(256) void bwd_dbdc_mfma_kernel(
@@ -591,14 +608,21 @@ __global__ __launch_bounds__(256) void bwd_dbdc_mfma_kernel(
                 *reinterpret_cast<uint4 *>(&Cs[NCS - 1][r * SP + p8]) = lo;
             }
         }
-        // the inter operand, transposed to [n][p], as hi + lo
+        // the inter operand, transposed to [n][p], as hi + lo: a lane takes rows
+        // p, p+1 and writes 32-bit pairs, consecutive lanes consecutive pairs
         const float *src = (ORIENT == 0 ? hprev : gh) + unit * (int64_t)(P * N);
-        for (int e = tid; e < P * N / 4; e += 256) {
-            const int p = e / (N / 4), n4 = 4 * (e % (N / 4));
-            const float4 v = *reinterpret_cast<const float4 *>(src + p * N + n4);
-            const float vv[4] = {v.x, v.y, v.z, v.w};
+        for (int e = tid; e < P * N / 8; e += 256) {
+            const int p = 2 * (e % (P / 2)), n4 = 4 * (e / (P / 2));
+            const float4 v0 = *reinterpret_cast<const float4 *>(src + p * N + n4);
+            const float4 v1 = *reinterpret_cast<const float4 *>(src + (p + 1) * N + n4);
+            const float a0[4] = {v0.x, v0.y, v0.z, v0.w}, a1[4] = {v1.x, v1.y, v1.z, v1.w};
 #pragma unroll
-            for (int i = 0; i < 4; ++i) split1(vv[i], Ib[0][(n4 + i) * SP + p], Ib[1][(n4 + i) * SP + p]);
+            for (int i = 0; i < 4; ++i) {
+                uint32_t hi, lo;
+                split2(a0[i], a1[i], hi, lo);
+                *reinterpret_cast<uint32_t *>(&Ib[0][(n4 + i) * SP + p]) = hi;
+                *reinterpret_cast<uint32_t *>(&Ib[1][(n4 + i) * SP + p]) = lo;
+            }
         }
         for (int e = tid; e < L; e += 256) {
             Gs[e] = Gws[unit * L + e];
@@ -697,17 +721,19 @@ __global__ __launch_bounds__(256) void bwd_dbdc_mfma_kernel(
                 Ib[1][r * SP + cl] = lo;
             }
         }
-        // V rows of the chunk, transposed to [n][token]
-        for (int e = tid; e < 64 * N / 8; e += 256) {
-            const int r = e / (N / 8), n8 = 8 * (e % (N / 8));
+        // V rows of the chunk, transposed to [n][token]: a lane takes tokens r, r+1
+        for (int e = tid; e < 64 * N / 16; e += 256) {
+            const int r = 2 * (e % 32), n8 = 8 * (e / 32);
             const int64_t t = tc + 64 * cc + r;
-            uint4 v = make_uint4(0u, 0u, 0u, 0u);
-            if (t < T) v = *reinterpret_cast<const uint4 *>(V + ((b * T + t) * G + g) * N + n8);
-            const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
+            uint4 v0 = make_uint4(0u, 0u, 0u, 0u), v1 = v0;
+            if (t < T) v0 = *reinterpret_cast<const uint4 *>(V + ((b * T + t) * G + g) * N + n8);
+            if (t + 1 < T) v1 = *reinterpret_cast<const uint4 *>(V + ((b * T + t + 1) * G + g) * N + n8);
+            const uint32_t w0[4] = {v0.x, v0.y, v0.z, v0.w}, w1[4] = {v1.x, v1.y, v1.z, v1.w};
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                Ib[0][(n8 + 2 * i) * SP + r] = (uint16_t)(wv[i] & 0xffffu);
-                Ib[0][(n8 + 2 * i + 1) * SP + r] = (uint16_t)(wv[i] >> 16);
+                *reinterpret_cast<uint32_t *>(&Ib[0][(n8 + 2 * i) * SP + r]) = pair16(w0[i], w1[i]);
+                *reinterpret_cast<uint32_t *>(&Ib[0][(n8 + 2 * i + 1) * SP + r]) =
+                    pair16(w0[i] >> 16, w1[i] >> 16);
             }
         }
         __syncthreads();
@@ -814,15 +840,23 @@ __global__ __launch_bounds__(4 * L) void bwd_dx_mfma_kernel(
     // holding its rows on (k >= i)
     for (int kc = 0; kc < NB; ++kc) {
         __syncthreads();
-        for (int e = tid; e < 64 * (P / 4); e += NTH) {       // dy rows -> dy^T hi / lo
-            const int r = e / (P / 4), p4 = 4 * (e % (P / 4));
+        for (int e = tid; e < 64 * (P / 8); e += NTH) {       // dy rows -> dy^T, 3 terms
+            const int r = 2 * (e % 32), p4 = 4 * (e / 32);    // tokens r, r+1
             const int64_t t = tc + 64 * kc + r;
-            float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-            if (t < T) v = *reinterpret_cast<const float4 *>(dy + ((b * T + t) * H + h) * P + p4);
-            const float vv[4] = {v.x, v.y, v.z, v.w};
+            float4 v0 = make_float4(0.f, 0.f, 0.f, 0.f), v1 = v0;
+            if (t < T) v0 = *reinterpret_cast<const float4 *>(dy + ((b * T + t) * H + h) * P + p4);
+            if (t + 1 < T)
+                v1 = *reinterpret_cast<const float4 *>(dy + ((b * T + t + 1) * H + h) * P + p4);
+            const float a0[4] = {v0.x, v0.y, v0.z, v0.w}, a1[4] = {v1.x, v1.y, v1.z, v1.w};
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                split1x3(vv[i], T0[(p4 + i) * SP + r], T1[(p4 + i) * SP + r], T3[(p4 + i) * SP + r]);
+            for (int i = 0; i < 4; ++i) {
+                uint32_t s0, s1, s2;
+                split2x3(a0[i], a1[i], s0, s1, s2);
+                const int o = (p4 + i) * SP + r;
+                *reinterpret_cast<uint32_t *>(T0 + o) = s0;
+                *reinterpret_cast<uint32_t *>(T1 + o) = s1;
+                *reinterpret_cast<uint32_t *>(T3 + o) = s2;
+            }
         }
         __syncthreads();
         if (16 * w <= 64 * kc + 63)
@@ -861,16 +895,19 @@ __global__ __launch_bounds__(4 * L) void bwd_dx_mfma_kernel(
     // ---- Y intra over the token chunks up to the one holding strip w's rows
     for (int jc = 0; jc < NB; ++jc) {
         __syncthreads();
-        for (int e = tid; e < 64 * (P / 8); e += NTH) {       // x rows -> x^T (exact)
-            const int r = e / (P / 8), p8 = 8 * (e % (P / 8));
+        for (int e = tid; e < 64 * (P / 16); e += NTH) {      // x rows -> x^T (exact)
+            const int r = 2 * (e % 32), p8 = 8 * (e / 32);    // tokens r, r+1
             const int64_t t = tc + 64 * jc + r;
-            uint4 v = make_uint4(0u, 0u, 0u, 0u);
-            if (t < T) v = *reinterpret_cast<const uint4 *>(x + ((b * T + t) * H + h) * P + p8);
-            const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
+            uint4 v0 = make_uint4(0u, 0u, 0u, 0u), v1 = v0;
+            if (t < T) v0 = *reinterpret_cast<const uint4 *>(x + ((b * T + t) * H + h) * P + p8);
+            if (t + 1 < T)
+                v1 = *reinterpret_cast<const uint4 *>(x + ((b * T + t + 1) * H + h) * P + p8);
+            const uint32_t w0[4] = {v0.x, v0.y, v0.z, v0.w}, w1[4] = {v1.x, v1.y, v1.z, v1.w};
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                T2[(p8 + 2 * i) * SP + r] = (uint16_t)(wv[i] & 0xffffu);
-                T2[(p8 + 2 * i + 1) * SP + r] = (uint16_t)(wv[i] >> 16);
+                *reinterpret_cast<uint32_t *>(T2 + (p8 + 2 * i) * SP + r) = pair16(w0[i], w1[i]);
+                *reinterpret_cast<uint32_t *>(T2 + (p8 + 2 * i + 1) * SP + r) =
+                    pair16(w0[i] >> 16, w1[i] >> 16);
             }
         }
         __syncthreads();
@@ -905,13 +942,16 @@ __global__ __launch_bounds__(4 * L) void bwd_dx_mfma_kernel(
     for (int ph = 0; ph < 2; ++ph) {
         const float *src = (ph == 0 ? gh : hprev) + unit * (int64_t)(P * N);
         __syncthreads();
-        for (int e = tid; e < P * N / 4; e += NTH) {          // [p][n] hi / lo
+        for (int e = tid; e < P * N / 4; e += NTH) {          // [p][n], 3 terms
             const int p = e / (N / 4), n4 = 4 * (e % (N / 4));
             const float4 v = *reinterpret_cast<const float4 *>(src + p * N + n4);
-            const float vv[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                split1x3(vv[i], Ih[p * PN + n4 + i], Im[p * PN + n4 + i], Il[p * PN + n4 + i]);
+            uint32_t s0a, s1a, s2a, s0b, s1b, s2b;
+            split2x3(v.x, v.y, s0a, s1a, s2a);
+            split2x3(v.z, v.w, s0b, s1b, s2b);
+            const int o = p * PN + n4;
+            *reinterpret_cast<uint2 *>(Ih + o) = make_uint2(s0a, s0b);
+            *reinterpret_cast<uint2 *>(Im + o) = make_uint2(s1a, s1b);
+            *reinterpret_cast<uint2 *>(Il + o) = make_uint2(s2a, s2b);
         }
         __syncthreads();
         const uint16_t *rows = (ph == 0 ? B : C) + ((b * T + (ta < T ? ta : 0)) * G + g) * N;
