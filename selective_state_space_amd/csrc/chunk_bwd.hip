@@ -547,31 +547,34 @@ __device__ __forceinline__ void split2(float a, float b, uint32_t &hi, uint32_t 
     lo = pair16(al, bl);
 }
 
-template <int L, int N, int ORIENT>
-__global__ __launch_bounds__(256) void bwd_dbdc_mfma_kernel(
+template <int L, int N, int ORIENT, int WPB>
+__global__ __launch_bounds__(64 * WPB) void bwd_dbdc_mfma_kernel(
     const uint16_t *__restrict__ x, const uint16_t *__restrict__ B,
     const uint16_t *__restrict__ C, const float *__restrict__ dy, const float *__restrict__ Gws,
     const float *__restrict__ DTws, const float *__restrict__ gh, const float *__restrict__ hprev,
     float *__restrict__ out, int64_t T, int32_t H, int32_t G, int32_t nc) {
     constexpr int NT = L / 16, NN = N / 16;
+    constexpr int RB = 16 * WPB;                      // rows per workgroup (one strip per wavefront)
+    constexpr int NTH = 64 * WPB;
     constexpr int NCS = ORIENT == 1 ? 2 : 1;          // dy rows need a remainder copy
+    constexpr int NIB = N > RB ? N : RB;              // Ib rows: n, or the M remainder's rows
     __shared__ __align__(16) uint16_t Cs[NCS][L * SP];  // column-side rows [row][p]; final: M
-    __shared__ __align__(16) uint16_t Ib[2][N * SP];    // inter operand [n][p]; final: V^T
+    __shared__ __align__(16) uint16_t Ib[2][NIB * SP];  // inter operand [n][p]; final: V^T
     __shared__ float Gs[L], DTs[L];
     const int64_t blk = xcd_remap(blockIdx.x, gridDim.x);   // row blocks of a group on one XCD
-    const int rb = (int)(blk % (L / 64));
-    const int64_t bcg = blk / (L / 64);               // (b*nc + c)*G + g
+    const int rb = (int)(blk % (L / RB));
+    const int64_t bcg = blk / (L / RB);               // (b*nc + c)*G + g
     const int32_t g = (int32_t)(bcg % G);
     const int64_t bc = bcg / G;
     const int32_t c = (int32_t)(bc % nc);
     const int64_t b = bc / nc;
     const int hpg = H / G;
-    const int r0 = 64 * rb;
+    const int r0 = RB * rb;
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
     const int m = lane & 15, q = lane >> 4;
     const int64_t tc = (int64_t)c * L;
-    // column range: ORIENT 0 -> [0, r0 + 64), ORIENT 1 -> [r0, L)
-    const int c_lo = ORIENT == 0 ? 0 : r0, c_hi = ORIENT == 0 ? r0 + 64 : L;
+    // column range: ORIENT 0 -> [0, r0 + RB), ORIENT 1 -> [r0, L)
+    const int c_lo = ORIENT == 0 ? 0 : r0, c_hi = ORIENT == 0 ? r0 + RB : L;
     const int arow = r0 + 16 * w + m;                 // this lane's A-operand row
     const int64_t ta = tc + arow;
     f32x4 Macc[NT];
@@ -586,7 +589,7 @@ __global__ __launch_bounds__(256) void bwd_dbdc_mfma_kernel(
         const int64_t unit = ((b * H) + h) * nc + c;
         __syncthreads();
         // stage the column-side rows of the range (x exact, or dy as hi + lo)
-        for (int e = tid; e < (c_hi - c_lo) * (P / 8); e += 256) {
+        for (int e = tid; e < (c_hi - c_lo) * (P / 8); e += NTH) {
             const int r = c_lo + e / (P / 8), p8 = 8 * (e % (P / 8));
             const int64_t t = tc + r;
             const int64_t o = ((b * T + (t < T ? t : 0)) * H + h) * P + p8;
@@ -611,7 +614,7 @@ __global__ __launch_bounds__(256) void bwd_dbdc_mfma_kernel(
         // the inter operand, transposed to [n][p], as hi + lo: a lane takes rows
         // p, p+1 and writes 32-bit pairs, consecutive lanes consecutive pairs
         const float *src = (ORIENT == 0 ? hprev : gh) + unit * (int64_t)(P * N);
-        for (int e = tid; e < P * N / 8; e += 256) {
+        for (int e = tid; e < P * N / 8; e += NTH) {
             const int p = 2 * (e % (P / 2)), n4 = 4 * (e / (P / 2));
             const float4 v0 = *reinterpret_cast<const float4 *>(src + p * N + n4);
             const float4 v1 = *reinterpret_cast<const float4 *>(src + (p + 1) * N + n4);
@@ -624,7 +627,7 @@ __global__ __launch_bounds__(256) void bwd_dbdc_mfma_kernel(
                 *reinterpret_cast<uint32_t *>(&Ib[1][(n4 + i) * SP + p]) = lo;
             }
         }
-        for (int e = tid; e < L; e += 256) {
+        for (int e = tid; e < L; e += NTH) {
             Gs[e] = Gws[unit * L + e];
             DTs[e] = DTws[unit * L + e];
         }
@@ -722,7 +725,7 @@ __global__ __launch_bounds__(256) void bwd_dbdc_mfma_kernel(
             }
         }
         // V rows of the chunk, transposed to [n][token]: a lane takes tokens r, r+1
-        for (int e = tid; e < 64 * N / 16; e += 256) {
+        for (int e = tid; e < 64 * N / 16; e += NTH) {
             const int r = 2 * (e % 32), n8 = 8 * (e / 32);
             const int64_t t = tc + 64 * cc + r;
             uint4 v0 = make_uint4(0u, 0u, 0u, 0u), v1 = v0;
@@ -1107,11 +1110,14 @@ hipError_t launch_bwd_t(const Shape &s, const BwdArgs &a, hipStream_t st) {
                                dim3(256), 0, st, x, B, C, a.D, a.dy, a.G, a.DT, a.CB, a.S,
                                (const Thp *)a.hprev, a.dx, a.tok, T, H, G, nc);
         if constexpr (sizeof(Tio) == 2) {
-            const uint32_t nb = (uint32_t)(ncb * (L / 64));
-            hipLaunchKernelGGL((bwd_dbdc_mfma_kernel<L, N, 0>), dim3(nb), dim3(256), 0, st, x, B,
-                               C, a.dy, a.G, a.DT, a.S, (const float *)a.hprev, a.dC, T, H, G, nc);
-            hipLaunchKernelGGL((bwd_dbdc_mfma_kernel<L, N, 1>), dim3(nb), dim3(256), 0, st, x, B,
-                               C, a.dy, a.G, a.DT, a.S, (const float *)a.hprev, a.dB, T, H, G, nc);
+            constexpr int WPB = L >= 128 ? 8 : 4;
+            const uint32_t nb = (uint32_t)(ncb * (L / (16 * WPB)));
+            hipLaunchKernelGGL((bwd_dbdc_mfma_kernel<L, N, 0, WPB>), dim3(nb), dim3(64 * WPB), 0,
+                               st, x, B, C, a.dy, a.G, a.DT, a.S, (const float *)a.hprev, a.dC, T,
+                               H, G, nc);
+            hipLaunchKernelGGL((bwd_dbdc_mfma_kernel<L, N, 1, WPB>), dim3(nb), dim3(64 * WPB), 0,
+                               st, x, B, C, a.dy, a.G, a.DT, a.S, (const float *)a.hprev, a.dB, T,
+                               H, G, nc);
         } else {
             hipLaunchKernelGGL((bwd_dbdc_kernel<L, N, Tio, Thp>),
                                dim3((uint32_t)(ncb * (L / 64) * 2)), dim3(256), 0, st, x, B, C,
