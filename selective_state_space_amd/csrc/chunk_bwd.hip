@@ -1013,6 +1013,97 @@ __global__ __launch_bounds__(4 * L) void bwd_dx_mfma_kernel(
     }
 }
 
+// ---- bwd_dstate_mfma: bwd_dstate on bf16 MFMA (bf16 io) ---------------------
+// dSp[p][n] = sum_k exp2(G_k) dy_k[p] C_k[n] for one (b, h, c) per workgroup;
+// wavefront w owns rows p = 16w..16w+15 and all N columns.  Both operands
+// have K = token, so each 64-token chunk is staged transposed into LDS with
+// 32-bit pair writes: (exp2(G) dy)^T in three bf16 terms (the adjoint it
+// feeds reaches dx, ddt and dA) and C^T (bf16 already).  Three MFMAs per
+// step; layouts as for bwd_dbdc_mfma.
+template <int L, int N>
+__global__ __launch_bounds__(256) void bwd_dstate_mfma_kernel(const float *__restrict__ dy,
+                                                              const uint16_t *__restrict__ C,
+                                                              const float *__restrict__ Gws,
+                                                              float *__restrict__ dS, int64_t T,
+                                                              int32_t H, int32_t G, int32_t nc) {
+    constexpr int NN = N / 16;
+    __shared__ __align__(16) uint16_t Dt[3][P * SP];   // (exp2(G) dy)^T, three terms [p][token]
+    __shared__ __align__(16) uint16_t Ct[N * SP];      // C^T [n][token]
+    __shared__ float Gs[L];
+    const int64_t blk = xcd_remap(blockIdx.x, gridDim.x);
+    const int hpg = H / G;
+    const int32_t h = (int32_t)((blk / hpg) % G) * hpg + (int32_t)(blk % hpg);
+    const int32_t g = h / hpg;
+    const int32_t c = (int32_t)((blk / H) % nc);
+    const int64_t b = blk / H / nc;
+    const int64_t unit = (b * H + h) * nc + c;
+    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+    const int m = lane & 15, q = lane >> 4;
+    const int64_t tc = (int64_t)c * L;
+    for (int e = tid; e < L; e += 256) Gs[e] = Gws[unit * L + e];
+    f32x4 acc[NN];
+#pragma unroll
+    for (int i = 0; i < NN; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int kc = 0; kc < L / 64; ++kc) {
+        __syncthreads();
+        for (int e = tid; e < 64 * (P / 8); e += 256) {       // tokens r, r+1; p4..p4+3
+            const int r = 2 * (e % 32), p4 = 4 * (e / 32);
+            const int64_t t = tc + 64 * kc + r;
+            float4 v0 = make_float4(0.f, 0.f, 0.f, 0.f), v1 = v0;
+            if (t < T) v0 = *reinterpret_cast<const float4 *>(dy + ((b * T + t) * H + h) * P + p4);
+            if (t + 1 < T)
+                v1 = *reinterpret_cast<const float4 *>(dy + ((b * T + t + 1) * H + h) * P + p4);
+            const float s0 = fast_exp2(Gs[64 * kc + r]), s1 = fast_exp2(Gs[64 * kc + r + 1]);
+            const float a0[4] = {v0.x * s0, v0.y * s0, v0.z * s0, v0.w * s0};
+            const float a1[4] = {v1.x * s1, v1.y * s1, v1.z * s1, v1.w * s1};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                uint32_t w0, w1, w2;
+                split2x3(a0[i], a1[i], w0, w1, w2);
+                const int o = (p4 + i) * SP + r;
+                *reinterpret_cast<uint32_t *>(&Dt[0][o]) = w0;
+                *reinterpret_cast<uint32_t *>(&Dt[1][o]) = w1;
+                *reinterpret_cast<uint32_t *>(&Dt[2][o]) = w2;
+            }
+        }
+        for (int e = tid; e < 64 * (N / 16); e += 256) {      // tokens r, r+1; n8..n8+7
+            const int r = 2 * (e % 32), n8 = 8 * (e / 32);
+            const int64_t t = tc + 64 * kc + r;
+            uint4 v0 = make_uint4(0u, 0u, 0u, 0u), v1 = v0;
+            if (t < T) v0 = *reinterpret_cast<const uint4 *>(C + ((b * T + t) * G + g) * N + n8);
+            if (t + 1 < T) v1 = *reinterpret_cast<const uint4 *>(C + ((b * T + t + 1) * G + g) * N + n8);
+            const uint32_t w0[4] = {v0.x, v0.y, v0.z, v0.w}, w1[4] = {v1.x, v1.y, v1.z, v1.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                *reinterpret_cast<uint32_t *>(&Ct[(n8 + 2 * i) * SP + r]) = pair16(w0[i], w1[i]);
+                *reinterpret_cast<uint32_t *>(&Ct[(n8 + 2 * i + 1) * SP + r]) =
+                    pair16(w0[i] >> 16, w1[i] >> 16);
+            }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+            const int ao = (16 * w + m) * SP + 32 * st + 8 * q;
+            const bf16x8 a0 = as_bf16x8(*reinterpret_cast<const uint4 *>(&Dt[0][ao]));
+            const bf16x8 a1 = as_bf16x8(*reinterpret_cast<const uint4 *>(&Dt[1][ao]));
+            const bf16x8 a2 = as_bf16x8(*reinterpret_cast<const uint4 *>(&Dt[2][ao]));
+#pragma unroll
+            for (int nt = 0; nt < NN; ++nt) {
+                const bf16x8 bv = as_bf16x8(
+                    *reinterpret_cast<const uint4 *>(&Ct[(16 * nt + m) * SP + 32 * st + 8 * q]));
+                acc[nt] = mfma16x16x32(a2, bv, acc[nt]);
+                acc[nt] = mfma16x16x32(a1, bv, acc[nt]);
+                acc[nt] = mfma16x16x32(a0, bv, acc[nt]);
+            }
+        }
+    }
+    float *o = dS + unit * (int64_t)(P * N);
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+#pragma unroll
+        for (int nt = 0; nt < NN; ++nt) o[(16 * w + 4 * q + e) * N + 16 * nt + m] = acc[nt][e];
+}
+
 // ---- bwd_scalars: s_t = bnd + sum_{t' >= t} r_t' per (b, h); ddt, dA/dD parts
 // The running sums are kept in fp64: s_t sums thousands of terms of both signs
 // to a small value, and dA sums dt_t s_t over the sequence again.
@@ -1090,8 +1181,12 @@ hipError_t launch_bwd_t(const Shape &s, const BwdArgs &a, hipStream_t st) {
     const int32_t H = (int32_t)s.H, G = (int32_t)s.G, nc = (int32_t)s.nc;
     const Tio *x = (const Tio *)a.x, *B = (const Tio *)a.B, *C = (const Tio *)a.C;
     if (units > 0) {
-        hipLaunchKernelGGL((bwd_dstate_kernel<L, N, Tio>), dim3((uint32_t)units), dim3(256), 0, st,
-                           a.dy, C, a.G, a.S, T, H, G, nc);
+        if constexpr (sizeof(Tio) == 2)
+            hipLaunchKernelGGL((bwd_dstate_mfma_kernel<L, N>), dim3((uint32_t)units), dim3(256), 0,
+                               st, a.dy, C, a.G, a.S, T, H, G, nc);
+        else
+            hipLaunchKernelGGL((bwd_dstate_kernel<L, N, Tio>), dim3((uint32_t)units), dim3(256), 0,
+                               st, a.dy, C, a.G, a.S, T, H, G, nc);
     }
     hipLaunchKernelGGL((bwd_passing_kernel<L, N>), dim3((uint32_t)(s.Bt * s.H)), dim3(256), 0, st,
                        a.S, a.G, a.dfinal, a.fin, a.dinit, a.part + 2 * s.Bt * s.H, nc);
