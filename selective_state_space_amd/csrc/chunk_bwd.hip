@@ -795,8 +795,17 @@ __global__ __launch_bounds__(4 * L) void bwd_dx_mfma_kernel(
     float *__restrict__ tok, int64_t T, int32_t H, int32_t G, int32_t nc, int64_t ntok) {
     constexpr int NB = L / 64, NP = P / 16, PN = N + 8;
     constexpr int NTH = 4 * L;                        // L/16 wavefronts: one 16-row strip each
-    // phase-shared LDS: the intra phases use T0/T1/T3 (dy^T in three terms) and
-    // T2 (x^T) as [p][64 tokens] tiles, the inter phases Ih/Im/Il as [p][N]
+    // phases: U over token chunk 0..NB-1, Y over chunk 0..NB-1, the ghat and
+    // the h_prev inter products.  Each phase's global operands are loaded into
+    // registers while the previous phase computes (one workgroup fills a CU).
+    constexpr int NPH = 2 * NB + 2;
+    constexpr int N_DY = 64 * (P / 8), N_X = 64 * (P / 16), N_I = P * N / 4;   // staging items
+    constexpr int IT_DY = (N_DY + NTH - 1) / NTH, IT_X = (N_X + NTH - 1) / NTH,
+                  IT_I = (N_I + NTH - 1) / NTH;
+    constexpr int NSR0 = 2 * IT_DY > 2 * IT_X ? 2 * IT_DY : 2 * IT_X;
+    constexpr int NSR = NSR0 > IT_I ? NSR0 : IT_I;
+    // phase-shared LDS: the U phases use T0/T1/T3 (dy^T in three terms), the Y
+    // phases T2 (x^T), as [p][64 tokens] tiles; the inter phases Ih/Im/Il [p][N]
     constexpr int NLDS = 3 * P * PN > 4 * P * SP ? 3 * P * PN : 4 * P * SP;
     __shared__ __align__(16) uint16_t lds[NLDS];
     __shared__ float Gs[L], DTs[L];
@@ -817,11 +826,11 @@ __global__ __launch_bounds__(4 * L) void bwd_dx_mfma_kernel(
     const int32_t h = g * hpg + hh;
     const int64_t bh = b * H + h;
     const int64_t unit = bh * nc + c;                 // (b*H + h)*nc + c
-    const int i0 = 0;                                 // the workgroup covers the chunk
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
     const int m = lane & 15, q = lane >> 4;
     const int64_t tc = (int64_t)c * L;
-    const int arow = i0 + 16 * w + m;                 // A-operand row of this lane
+    const int arow = 16 * w + m;                      // A-operand row of this lane
+    const int64_t ta = tc + arow;
     const float *CBr = CB + bcg * (int64_t)(L * L) + (int64_t)arow * L;
     const float *CBTr = CBT + bcg * (int64_t)(L * L) + (int64_t)arow * L;
     for (int e = tid; e < L; e += NTH) {
@@ -833,154 +842,228 @@ __global__ __launch_bounds__(4 * L) void bwd_dx_mfma_kernel(
     for (int i = 0; i < NP; ++i) {
         U[i] = f32x4{0.f, 0.f, 0.f, 0.f};
         Y[i] = U[i];
-        Ui[i] = U[i];
-        Yi[i] = U[i];
     }
+    uint4 sr[NSR];            // staging registers of the next phase
+    float4 ca[4];             // this lane's C B^T values of the next phase (two k-steps)
+    uint4 ra[N / 32];         // this lane's B or C row of the next inter phase
+
+    auto load_phase = [&](int ph) {
+        if (ph < 2 * NB) {
+            const bool isU = ph < NB;
+            const int ck = isU ? ph : ph - NB;
+#pragma unroll
+            for (int j = 0; j < NSR / 2; ++j) {
+                const int e = tid + j * NTH;
+                sr[2 * j] = make_uint4(0u, 0u, 0u, 0u);
+                sr[2 * j + 1] = sr[2 * j];
+                if (e < (isU ? N_DY : N_X)) {
+                    const int r = 2 * (e % 32);
+                    const int pc = isU ? 4 * (e / 32) : 8 * (e / 32);
+                    const int64_t t = tc + 64 * ck + r;
+                    if (isU) {
+                        if (t < T)
+                            sr[2 * j] = *reinterpret_cast<const uint4 *>(dy + ((b * T + t) * H + h) * P + pc);
+                        if (t + 1 < T)
+                            sr[2 * j + 1] =
+                                *reinterpret_cast<const uint4 *>(dy + ((b * T + t + 1) * H + h) * P + pc);
+                    } else {
+                        if (t < T)
+                            sr[2 * j] = *reinterpret_cast<const uint4 *>(x + ((b * T + t) * H + h) * P + pc);
+                        if (t + 1 < T)
+                            sr[2 * j + 1] =
+                                *reinterpret_cast<const uint4 *>(x + ((b * T + t + 1) * H + h) * P + pc);
+                    }
+                }
+            }
+            const float *rowp = isU ? CBTr : CBr;
+#pragma unroll
+            for (int st = 0; st < 2; ++st) {
+                const int k0 = 64 * ck + 32 * st + 8 * q;
+                ca[2 * st] = *reinterpret_cast<const float4 *>(rowp + k0);
+                ca[2 * st + 1] = *reinterpret_cast<const float4 *>(rowp + k0 + 4);
+            }
+        } else {
+            const float *src = (ph == 2 * NB ? gh : hprev) + unit * (int64_t)(P * N);
+#pragma unroll
+            for (int j = 0; j < NSR; ++j) {
+                const int e = tid + j * NTH;
+                sr[j] = make_uint4(0u, 0u, 0u, 0u);
+                if (j < IT_I && e < N_I) {
+                    const int pp = e / (N / 4), n4 = 4 * (e % (N / 4));
+                    sr[j] = *reinterpret_cast<const uint4 *>(src + pp * N + n4);
+                }
+            }
+            const uint16_t *rows = (ph == 2 * NB ? B : C) + ((b * T + (ta < T ? ta : 0)) * G + g) * N;
+#pragma unroll
+            for (int ks = 0; ks < N / 32; ++ks)
+                ra[ks] = ta < T ? *reinterpret_cast<const uint4 *>(rows + 32 * ks + 8 * q)
+                                : make_uint4(0u, 0u, 0u, 0u);
+        }
+    };
+    auto store_phase = [&](int ph) {
+        if (ph < NB) {                                 // dy^T, three terms
+#pragma unroll
+            for (int j = 0; j < NSR / 2; ++j) {
+                const int e = tid + j * NTH;
+                if (e < N_DY) {
+                    const int r = 2 * (e % 32), p4 = 4 * (e / 32);
+                    const uint4 u0 = sr[2 * j], u1 = sr[2 * j + 1];
+                    const float a0[4] = {__uint_as_float(u0.x), __uint_as_float(u0.y),
+                                         __uint_as_float(u0.z), __uint_as_float(u0.w)};
+                    const float a1[4] = {__uint_as_float(u1.x), __uint_as_float(u1.y),
+                                         __uint_as_float(u1.z), __uint_as_float(u1.w)};
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        uint32_t s0, s1, s2;
+                        split2x3(a0[i], a1[i], s0, s1, s2);
+                        const int o = (p4 + i) * SP + r;
+                        *reinterpret_cast<uint32_t *>(T0 + o) = s0;
+                        *reinterpret_cast<uint32_t *>(T1 + o) = s1;
+                        *reinterpret_cast<uint32_t *>(T3 + o) = s2;
+                    }
+                }
+            }
+        } else if (ph < 2 * NB) {                      // x^T (exact)
+#pragma unroll
+            for (int j = 0; j < NSR / 2; ++j) {
+                const int e = tid + j * NTH;
+                if (e < N_X) {
+                    const int r = 2 * (e % 32), p8 = 8 * (e / 32);
+                    const uint32_t w0[4] = {sr[2 * j].x, sr[2 * j].y, sr[2 * j].z, sr[2 * j].w};
+                    const uint32_t w1[4] = {sr[2 * j + 1].x, sr[2 * j + 1].y, sr[2 * j + 1].z,
+                                            sr[2 * j + 1].w};
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        *reinterpret_cast<uint32_t *>(T2 + (p8 + 2 * i) * SP + r) = pair16(w0[i], w1[i]);
+                        *reinterpret_cast<uint32_t *>(T2 + (p8 + 2 * i + 1) * SP + r) =
+                            pair16(w0[i] >> 16, w1[i] >> 16);
+                    }
+                }
+            }
+        } else {                                       // [p][n], three terms
+#pragma unroll
+            for (int j = 0; j < NSR; ++j) {
+                const int e = tid + j * NTH;
+                if (j < IT_I && e < N_I) {
+                    const int pp = e / (N / 4), n4 = 4 * (e % (N / 4));
+                    uint32_t s0a, s1a, s2a, s0b, s1b, s2b;
+                    split2x3(__uint_as_float(sr[j].x), __uint_as_float(sr[j].y), s0a, s1a, s2a);
+                    split2x3(__uint_as_float(sr[j].z), __uint_as_float(sr[j].w), s0b, s1b, s2b);
+                    const int o = pp * PN + n4;
+                    *reinterpret_cast<uint2 *>(Ih + o) = make_uint2(s0a, s0b);
+                    *reinterpret_cast<uint2 *>(Im + o) = make_uint2(s1a, s1b);
+                    *reinterpret_cast<uint2 *>(Il + o) = make_uint2(s2a, s2b);
+                }
+            }
+        }
+    };
+
     __syncthreads();
     const float gi = Gs[arow];
-
-    // ---- U intra over the token chunks; strip w takes part from the chunk
-    // holding its rows on (k >= i)
-    for (int kc = 0; kc < NB; ++kc) {
-        __syncthreads();
-        for (int e = tid; e < 64 * (P / 8); e += NTH) {       // dy rows -> dy^T, 3 terms
-            const int r = 2 * (e % 32), p4 = 4 * (e / 32);    // tokens r, r+1
-            const int64_t t = tc + 64 * kc + r;
-            float4 v0 = make_float4(0.f, 0.f, 0.f, 0.f), v1 = v0;
-            if (t < T) v0 = *reinterpret_cast<const float4 *>(dy + ((b * T + t) * H + h) * P + p4);
-            if (t + 1 < T)
-                v1 = *reinterpret_cast<const float4 *>(dy + ((b * T + t + 1) * H + h) * P + p4);
-            const float a0[4] = {v0.x, v0.y, v0.z, v0.w}, a1[4] = {v1.x, v1.y, v1.z, v1.w};
+    load_phase(0);
+    // unrolled: each phase's code is specialised, so only its registers are live
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                uint32_t s0, s1, s2;
-                split2x3(a0[i], a1[i], s0, s1, s2);
-                const int o = (p4 + i) * SP + r;
-                *reinterpret_cast<uint32_t *>(T0 + o) = s0;
-                *reinterpret_cast<uint32_t *>(T1 + o) = s1;
-                *reinterpret_cast<uint32_t *>(T3 + o) = s2;
+    for (int ph = 0; ph < NPH; ++ph) {
+        if (ph == 2 * NB)
+#pragma unroll
+            for (int i = 0; i < NP; ++i) {
+                Ui[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+                Yi[i] = Ui[i];
             }
-        }
+        __syncthreads();                               // the previous phase is done with the LDS
+        store_phase(ph);
+        // this phase's A operands, before the registers take the next phase's loads
+        const float4 cur[4] = {ca[0], ca[1], ca[2], ca[3]};
+        uint4 rcur[N / 32];
+#pragma unroll
+        for (int ks = 0; ks < N / 32; ++ks) rcur[ks] = ra[ks];
+        if (ph + 1 < NPH) load_phase(ph + 1);
         __syncthreads();
-        if (16 * w <= 64 * kc + 63)
+        if (ph < NB) {                                 // U: k >= i
+            const int kc = ph;
+            if (16 * w <= 64 * kc + 63)
 #pragma unroll
-        for (int st = 0; st < 2; ++st) {
-            const int k0 = 64 * kc + 32 * st + 8 * q;         // this lane's 8 k's
-            const float4 c0 = *reinterpret_cast<const float4 *>(CBTr + k0);
-            const float4 c1 = *reinterpret_cast<const float4 *>(CBTr + k0 + 4);
-            const float cv[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
-            float wv[8];
+                for (int st = 0; st < 2; ++st) {
+                    const int k0 = 64 * kc + 32 * st + 8 * q;
+                    const float cv[8] = {cur[2 * st].x, cur[2 * st].y, cur[2 * st].z, cur[2 * st].w,
+                                         cur[2 * st + 1].x, cur[2 * st + 1].y, cur[2 * st + 1].z,
+                                         cur[2 * st + 1].w};
+                    float wv[8];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const int k = k0 + i;
-                wv[i] = k >= arow ? fast_exp2(Gs[k] - gi) * cv[i] : 0.f;
-            }
-            uint4 a0, a1, a2;
-            split8x3(wv, a0, a1, a2);
+                    for (int i = 0; i < 8; ++i) {
+                        const int k = k0 + i;
+                        wv[i] = k >= arow ? fast_exp2(Gs[k] - gi) * cv[i] : 0.f;
+                    }
+                    uint4 a0, a1, a2;
+                    split8x3(wv, a0, a1, a2);
 #pragma unroll
-            for (int pt = 0; pt < NP; ++pt) {
-                const int off = (16 * pt + m) * SP + 32 * st + 8 * q;
-                const bf16x8 b0 = as_bf16x8(*reinterpret_cast<const uint4 *>(T0 + off));
-                const bf16x8 b1 = as_bf16x8(*reinterpret_cast<const uint4 *>(T1 + off));
-                const bf16x8 b2 = as_bf16x8(*reinterpret_cast<const uint4 *>(T3 + off));
-                // the products of order 2^-16 and above, smallest first
-                if (BWD_INTRA3) {
-                U[pt] = mfma16x16x32(as_bf16x8(a2), b0, U[pt]);
-                U[pt] = mfma16x16x32(as_bf16x8(a0), b2, U[pt]);
-                U[pt] = mfma16x16x32(as_bf16x8(a1), b1, U[pt]);
+                    for (int pt = 0; pt < NP; ++pt) {
+                        const int off = (16 * pt + m) * SP + 32 * st + 8 * q;
+                        const bf16x8 b0 = as_bf16x8(*reinterpret_cast<const uint4 *>(T0 + off));
+                        const bf16x8 b1 = as_bf16x8(*reinterpret_cast<const uint4 *>(T1 + off));
+                        const bf16x8 b2 = as_bf16x8(*reinterpret_cast<const uint4 *>(T3 + off));
+                        // the products of order 2^-16 and above, smallest first
+                        U[pt] = mfma16x16x32(as_bf16x8(a2), b0, U[pt]);
+                        U[pt] = mfma16x16x32(as_bf16x8(a0), b2, U[pt]);
+                        U[pt] = mfma16x16x32(as_bf16x8(a1), b1, U[pt]);
+                        U[pt] = mfma16x16x32(as_bf16x8(a1), b0, U[pt]);
+                        U[pt] = mfma16x16x32(as_bf16x8(a0), b1, U[pt]);
+                        U[pt] = mfma16x16x32(as_bf16x8(a0), b0, U[pt]);
+                    }
                 }
-                U[pt] = mfma16x16x32(as_bf16x8(a1), b0, U[pt]);
-                U[pt] = mfma16x16x32(as_bf16x8(a0), b1, U[pt]);
-                U[pt] = mfma16x16x32(as_bf16x8(a0), b0, U[pt]);
-            }
+        } else if (ph < 2 * NB) {                      // Y: j <= i
+            const int jc = ph - NB;
+            if (16 * w + 15 >= 64 * jc)
+#pragma unroll
+                for (int st = 0; st < 2; ++st) {
+                    const int j0 = 64 * jc + 32 * st + 8 * q;
+                    const float cv[8] = {cur[2 * st].x, cur[2 * st].y, cur[2 * st].z, cur[2 * st].w,
+                                         cur[2 * st + 1].x, cur[2 * st + 1].y, cur[2 * st + 1].z,
+                                         cur[2 * st + 1].w};
+                    float vv[8];
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) {
+                        const int j = j0 + i;
+                        vv[i] = j <= arow ? fast_exp2(gi - Gs[j]) * cv[i] * DTs[j] : 0.f;
+                    }
+                    uint4 a0, a1, a2;
+                    split8x3(vv, a0, a1, a2);
+#pragma unroll
+                    for (int pt = 0; pt < NP; ++pt) {
+                        const int off = (16 * pt + m) * SP + 32 * st + 8 * q;
+                        const bf16x8 bx = as_bf16x8(*reinterpret_cast<const uint4 *>(T2 + off));
+                        Y[pt] = mfma16x16x32(as_bf16x8(a2), bx, Y[pt]);
+                        Y[pt] = mfma16x16x32(as_bf16x8(a1), bx, Y[pt]);
+                        Y[pt] = mfma16x16x32(as_bf16x8(a0), bx, Y[pt]);
+                    }
+                }
+        } else {                                       // inter: (B or C rows) x (ghat or h_prev)
+            const bool first = ph == 2 * NB;
+#pragma unroll
+            for (int ks = 0; ks < N / 32; ++ks)
+#pragma unroll
+                for (int pt = 0; pt < NP; ++pt) {
+                    const int off = (16 * pt + m) * PN + 32 * ks + 8 * q;
+                    const bf16x8 b0 = as_bf16x8(*reinterpret_cast<const uint4 *>(Ih + off));
+                    const bf16x8 b1 = as_bf16x8(*reinterpret_cast<const uint4 *>(Im + off));
+                    const bf16x8 b2 = as_bf16x8(*reinterpret_cast<const uint4 *>(Il + off));
+                    f32x4 acc = first ? Ui[pt] : Yi[pt];
+                    acc = mfma16x16x32(as_bf16x8(rcur[ks]), b2, acc);
+                    acc = mfma16x16x32(as_bf16x8(rcur[ks]), b1, acc);
+                    acc = mfma16x16x32(as_bf16x8(rcur[ks]), b0, acc);
+                    if (first)
+                        Ui[pt] = acc;
+                    else
+                        Yi[pt] = acc;
+                }
         }
     }
-    // ---- Y intra over the token chunks up to the one holding strip w's rows
-    for (int jc = 0; jc < NB; ++jc) {
-        __syncthreads();
-        for (int e = tid; e < 64 * (P / 16); e += NTH) {      // x rows -> x^T (exact)
-            const int r = 2 * (e % 32), p8 = 8 * (e / 32);    // tokens r, r+1
-            const int64_t t = tc + 64 * jc + r;
-            uint4 v0 = make_uint4(0u, 0u, 0u, 0u), v1 = v0;
-            if (t < T) v0 = *reinterpret_cast<const uint4 *>(x + ((b * T + t) * H + h) * P + p8);
-            if (t + 1 < T)
-                v1 = *reinterpret_cast<const uint4 *>(x + ((b * T + t + 1) * H + h) * P + p8);
-            const uint32_t w0[4] = {v0.x, v0.y, v0.z, v0.w}, w1[4] = {v1.x, v1.y, v1.z, v1.w};
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                *reinterpret_cast<uint32_t *>(T2 + (p8 + 2 * i) * SP + r) = pair16(w0[i], w1[i]);
-                *reinterpret_cast<uint32_t *>(T2 + (p8 + 2 * i + 1) * SP + r) =
-                    pair16(w0[i] >> 16, w1[i] >> 16);
-            }
-        }
-        __syncthreads();
-        if (16 * w + 15 >= 64 * jc)
-#pragma unroll
-        for (int st = 0; st < 2; ++st) {
-            const int j0 = 64 * jc + 32 * st + 8 * q;
-            const float4 c0 = *reinterpret_cast<const float4 *>(CBr + j0);
-            const float4 c1 = *reinterpret_cast<const float4 *>(CBr + j0 + 4);
-            const float cv[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
-            float vv[8];
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const int j = j0 + i;
-                vv[i] = j <= arow ? fast_exp2(gi - Gs[j]) * cv[i] * DTs[j] : 0.f;
-            }
-            uint4 a0, a1, a2;
-            split8x3(vv, a0, a1, a2);
-#pragma unroll
-            for (int pt = 0; pt < NP; ++pt) {
-                const int off = (16 * pt + m) * SP + 32 * st + 8 * q;
-                const bf16x8 bx = as_bf16x8(*reinterpret_cast<const uint4 *>(T2 + off));
-                if (BWD_INTRA3) Y[pt] = mfma16x16x32(as_bf16x8(a2), bx, Y[pt]);
-                Y[pt] = mfma16x16x32(as_bf16x8(a1), bx, Y[pt]);
-                Y[pt] = mfma16x16x32(as_bf16x8(a0), bx, Y[pt]);
-            }
-        }
-    }
-    // ---- inter products: U_inter with (B rows, ghat), then Y_inter with (C rows, h_prev)
-    const int64_t ta = tc + arow;
-#pragma unroll
-    for (int ph = 0; ph < 2; ++ph) {
-        const float *src = (ph == 0 ? gh : hprev) + unit * (int64_t)(P * N);
-        __syncthreads();
-        for (int e = tid; e < P * N / 4; e += NTH) {          // [p][n], 3 terms
-            const int p = e / (N / 4), n4 = 4 * (e % (N / 4));
-            const float4 v = *reinterpret_cast<const float4 *>(src + p * N + n4);
-            uint32_t s0a, s1a, s2a, s0b, s1b, s2b;
-            split2x3(v.x, v.y, s0a, s1a, s2a);
-            split2x3(v.z, v.w, s0b, s1b, s2b);
-            const int o = p * PN + n4;
-            *reinterpret_cast<uint2 *>(Ih + o) = make_uint2(s0a, s0b);
-            *reinterpret_cast<uint2 *>(Im + o) = make_uint2(s1a, s1b);
-            *reinterpret_cast<uint2 *>(Il + o) = make_uint2(s2a, s2b);
-        }
-        __syncthreads();
-        const uint16_t *rows = (ph == 0 ? B : C) + ((b * T + (ta < T ? ta : 0)) * G + g) * N;
-#pragma unroll
-        for (int ks = 0; ks < N / 32; ++ks) {
-            uint4 av = make_uint4(0u, 0u, 0u, 0u);
-            if (ta < T) av = *reinterpret_cast<const uint4 *>(rows + 32 * ks + 8 * q);
-#pragma unroll
-            for (int pt = 0; pt < NP; ++pt) {
-                const int off = (16 * pt + m) * PN + 32 * ks + 8 * q;
-                const bf16x8 b0 = as_bf16x8(*reinterpret_cast<const uint4 *>(Ih + off));
-                const bf16x8 b1 = as_bf16x8(*reinterpret_cast<const uint4 *>(Im + off));
-                const bf16x8 b2 = as_bf16x8(*reinterpret_cast<const uint4 *>(Il + off));
-                f32x4 &acc = ph == 0 ? Ui[pt] : Yi[pt];
-                acc = mfma16x16x32(as_bf16x8(av), b2, acc);
-                acc = mfma16x16x32(as_bf16x8(av), b1, acc);
-                acc = mfma16x16x32(as_bf16x8(av), b0, acc);
-            }
-        }
-    }
-    // ---- epilogue: rows i = i0 + 16w + 4q + e, columns p = 16 pt + m
+    // ---- epilogue: rows i = 16w + 4q + e, columns p = 16 pt + m
     const float Dh = D[h], glast = Gs[L - 1];
     float *tokc = tok + unit * (int64_t)L;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-        const int i = i0 + 16 * w + 4 * q + e;
+        const int i = 16 * w + 4 * q + e;
         const int64_t t = tc + i;
         const bool real = t < T;
         const int64_t tt = real ? t : 0;
