@@ -635,6 +635,15 @@ __global__ __launch_bounds__(64 * WPB) void bwd_dbdc_mfma_kernel(
         // A operands: the strip's own rows (plain, and scaled for the inter term)
         const float ga = Gs[arow], glast = Gs[L - 1];
         const float sc = ORIENT == 0 ? fast_exp2(ga) : DTs[arow] * fast_exp2(glast - ga);
+        // row factors of the off-diagonal decay, against the strip's edge row:
+        // the first row (ORIENT 0, columns before it) or the last (ORIENT 1)
+        const float gedge = Gs[r0 + 16 * w + (ORIENT == 0 ? 0 : 15)];
+        float rowf[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int row = r0 + 16 * w + 4 * q + e;
+            rowf[e] = ORIENT == 0 ? fast_exp2(Gs[row] - gedge) : fast_exp2(gedge - Gs[row]) * DTs[row];
+        }
         bf16x8 aS[2], aSl[2], aI[2], aIl[2];
 #pragma unroll
         for (int st = 0; st < 2; ++st) {
@@ -667,6 +676,8 @@ __global__ __launch_bounds__(64 * WPB) void bwd_dbdc_mfma_kernel(
 #pragma unroll
         for (int jt = 0; jt < NT; ++jt) {
             if (16 * jt < c_lo || 16 * jt >= c_hi) continue;
+            // tiles wholly on the masked side of this strip's rows add nothing
+            if (ORIENT == 0 ? 16 * jt > r0 + 16 * w : 16 * jt < r0 + 16 * w) continue;
             f32x4 s = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int st = 0; st < 2; ++st) {
@@ -682,16 +693,27 @@ __global__ __launch_bounds__(64 * WPB) void bwd_dbdc_mfma_kernel(
             }
             const int col = 16 * jt + m;
             const float gc = Gs[col], dc = DTs[col];
+            if (16 * jt == r0 + 16 * w) {
+                // the diagonal tile: the exact pairwise decay, masked
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int row = r0 + 16 * w + 4 * q + e;
-                const float gr = Gs[row];
-                float v;
-                if constexpr (ORIENT == 0)
-                    v = row >= col ? fast_exp2(gr - gc) * dc * s[e] : 0.f;
-                else
-                    v = col >= row ? fast_exp2(gc - gr) * DTs[row] * s[e] : 0.f;
-                Macc[jt][e] += v;
+                for (int e = 0; e < 4; ++e) {
+                    const int row = r0 + 16 * w + 4 * q + e;
+                    const float gr = Gs[row];
+                    float v;
+                    if constexpr (ORIENT == 0)
+                        v = row >= col ? fast_exp2(gr - gc) * dc * s[e] : 0.f;
+                    else
+                        v = col >= row ? fast_exp2(gc - gr) * DTs[row] * s[e] : 0.f;
+                    Macc[jt][e] += v;
+                }
+            } else if (ORIENT == 0 ? 16 * jt < r0 + 16 * w : 16 * jt > r0 + 16 * w) {
+                // off the diagonal on the causal side every pair counts, and the
+                // decay splits at the strip's edge row into a row factor and a
+                // column factor, both at most 1: one exp2 per tile instead of four
+                // (tiles on the other side are entirely masked)
+                const float cf = ORIENT == 0 ? fast_exp2(gedge - gc) * dc : fast_exp2(gc - gedge);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) Macc[jt][e] += rowf[e] * (cf * s[e]);
             }
         }
         // inter term: (scaled strip rows) x (h_prev or ghat), K = P, three products
