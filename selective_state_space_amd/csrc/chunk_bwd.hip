@@ -77,6 +77,76 @@ __device__ __forceinline__ void mm_acc(float (&acc)[TM][TN], const float *As, in
     }
 }
 
+// ---- bf16 operand helpers shared by the MFMA kernels below -----------------
+constexpr int SP = P + 8;     // LDS row pitch (bf16) of the staged [row][p] tiles
+
+__device__ __forceinline__ uint4 pack8(const float (&v)[8]) {
+    return make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
+                      pack_bf16x2(v[6], v[7]));
+}
+// v = hi + lo with hi = bf16(v), lo = bf16(v - hi)
+__device__ __forceinline__ void split8(const float (&v)[8], uint4 &hi, uint4 &lo) {
+    hi = pack8(v);
+    const uint32_t hw[4] = {hi.x, hi.y, hi.z, hi.w};
+    float r[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        r[2 * i] = v[2 * i] - bf16_lo(hw[i]);
+        r[2 * i + 1] = v[2 * i + 1] - bf16_hi(hw[i]);
+    }
+    lo = pack8(r);
+}
+__device__ __forceinline__ void split1(float v, uint16_t &hi, uint16_t &lo) {
+    const uint32_t h = pack_bf16x2(v, 0.f) & 0xffffu;
+    hi = (uint16_t)h;
+    lo = (uint16_t)(pack_bf16x2(v - __uint_as_float(h << 16), 0.f) & 0xffffu);
+}
+// three bf16 terms: v = s0 + s1 + s2 up to about 2^-27 of v
+__device__ __forceinline__ void split8x3(const float (&v)[8], uint4 &s0, uint4 &s1, uint4 &s2) {
+    float r[8];
+    s0 = pack8(v);
+    const uint32_t a[4] = {s0.x, s0.y, s0.z, s0.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        r[2 * i] = v[2 * i] - bf16_lo(a[i]);
+        r[2 * i + 1] = v[2 * i + 1] - bf16_hi(a[i]);
+    }
+    s1 = pack8(r);
+    const uint32_t bq[4] = {s1.x, s1.y, s1.z, s1.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        r[2 * i] -= bf16_lo(bq[i]);
+        r[2 * i + 1] -= bf16_hi(bq[i]);
+    }
+    s2 = pack8(r);
+}
+__device__ __forceinline__ void split1x3(float v, uint16_t &s0, uint16_t &s1, uint16_t &s2) {
+    const uint32_t a = pack_bf16x2(v, 0.f) & 0xffffu;
+    const float r1 = v - __uint_as_float(a << 16);
+    const uint32_t bq = pack_bf16x2(r1, 0.f) & 0xffffu;
+    const float r2 = r1 - __uint_as_float(bq << 16);
+    s0 = (uint16_t)a;
+    s1 = (uint16_t)bq;
+    s2 = (uint16_t)(pack_bf16x2(r2, 0.f) & 0xffffu);
+}
+// the two 16-bit halves of a word: lo = the element of the even index
+__device__ __forceinline__ uint32_t pair16(uint32_t lo, uint32_t hi) { return (lo & 0xffffu) | (hi << 16); }
+__device__ __forceinline__ void split2x3(float a, float b, uint32_t &s0, uint32_t &s1, uint32_t &s2) {
+    uint16_t a0, a1, a2, b0, b1, b2;
+    split1x3(a, a0, a1, a2);
+    split1x3(b, b0, b1, b2);
+    s0 = pair16(a0, b0);
+    s1 = pair16(a1, b1);
+    s2 = pair16(a2, b2);
+}
+__device__ __forceinline__ void split2(float a, float b, uint32_t &hi, uint32_t &lo) {
+    uint16_t ah, al, bh, bl;
+    split1(a, ah, al);
+    split1(b, bh, bl);
+    hi = pair16(ah, bh);
+    lo = pair16(al, bl);
+}
+
 // ---- bwd_dstate: dSp[b,h,c] = sum_k exp2(G_k) dy_k (outer) C_k, [P][N] ------
 template <int L, int N, typename Tio>
 __global__ __launch_bounds__(256) void bwd_dstate_kernel(const float *__restrict__ dy,
@@ -176,7 +246,9 @@ template <int L, int N, typename Tio>
 __global__ __launch_bounds__(256) void bwd_cb_kernel(const Tio *__restrict__ B,
                                                      const Tio *__restrict__ C,
                                                      float *__restrict__ CB,
-                                                     float *__restrict__ CBT, int64_t T,
+                                                     float *__restrict__ CBT,
+                                                     uint16_t *__restrict__ CB3,
+                                                     uint16_t *__restrict__ CBT3, int64_t T,
                                                      int32_t G, int32_t nc) {
     constexpr int NB = L / 64, NTRI = NB * (NB + 1) / 2;
     __shared__ __align__(16) float As[KT * LD];
@@ -216,6 +288,30 @@ __global__ __launch_bounds__(256) void bwd_cb_kernel(const Tio *__restrict__ B,
         for (int j = 0; j < 4; ++j)
             *reinterpret_cast<float4 *>(ot + j * L) =
                 make_float4(acc[0][j], acc[1][j], acc[2][j], acc[3][j]);
+    }
+    if (CB3) {   // both as three bf16 terms, [term][bcg][row][col]
+        const int64_t plane = (int64_t)gridDim.x / NTRI * L * L;   // Bt*nc*G*L*L
+        const int64_t base = bcg * (int64_t)(L * L);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            uint32_t s0a, s1a, s2a, s0b, s1b, s2b;
+            split2x3(acc[i][0], acc[i][1], s0a, s1a, s2a);
+            split2x3(acc[i][2], acc[i][3], s0b, s1b, s2b);
+            const int64_t o = base + (int64_t)(64 * kb + m0 + i) * L + 64 * jb + n0;
+            *reinterpret_cast<uint2 *>(CB3 + o) = make_uint2(s0a, s0b);
+            *reinterpret_cast<uint2 *>(CB3 + plane + o) = make_uint2(s1a, s1b);
+            *reinterpret_cast<uint2 *>(CB3 + 2 * plane + o) = make_uint2(s2a, s2b);
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            uint32_t s0a, s1a, s2a, s0b, s1b, s2b;
+            split2x3(acc[0][j], acc[1][j], s0a, s1a, s2a);
+            split2x3(acc[2][j], acc[3][j], s0b, s1b, s2b);
+            const int64_t o = base + (int64_t)(64 * jb + n0 + j) * L + 64 * kb + m0;
+            *reinterpret_cast<uint2 *>(CBT3 + o) = make_uint2(s0a, s0b);
+            *reinterpret_cast<uint2 *>(CBT3 + plane + o) = make_uint2(s1a, s1b);
+            *reinterpret_cast<uint2 *>(CBT3 + 2 * plane + o) = make_uint2(s2a, s2b);
+        }
     }
 }
 
@@ -478,74 +574,6 @@ __global__ __launch_bounds__(256) void bwd_dbdc_kernel(
 // head plus a bf16 remainder (x, B and C are bf16 already): products of two
 // split operands take three MFMAs (hi.hi + hi.lo + lo.hi), of one split
 // operand two, which leaves about 2^-16 of relative error instead of 2^-9.
-constexpr int SP = P + 8;     // LDS row pitch (bf16) of the staged [row][p] tiles
-
-__device__ __forceinline__ uint4 pack8(const float (&v)[8]) {
-    return make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
-                      pack_bf16x2(v[6], v[7]));
-}
-// v = hi + lo with hi = bf16(v), lo = bf16(v - hi)
-__device__ __forceinline__ void split8(const float (&v)[8], uint4 &hi, uint4 &lo) {
-    hi = pack8(v);
-    const uint32_t hw[4] = {hi.x, hi.y, hi.z, hi.w};
-    float r[8];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        r[2 * i] = v[2 * i] - bf16_lo(hw[i]);
-        r[2 * i + 1] = v[2 * i + 1] - bf16_hi(hw[i]);
-    }
-    lo = pack8(r);
-}
-__device__ __forceinline__ void split1(float v, uint16_t &hi, uint16_t &lo) {
-    const uint32_t h = pack_bf16x2(v, 0.f) & 0xffffu;
-    hi = (uint16_t)h;
-    lo = (uint16_t)(pack_bf16x2(v - __uint_as_float(h << 16), 0.f) & 0xffffu);
-}
-// three bf16 terms: v = s0 + s1 + s2 up to about 2^-27 of v
-__device__ __forceinline__ void split8x3(const float (&v)[8], uint4 &s0, uint4 &s1, uint4 &s2) {
-    float r[8];
-    s0 = pack8(v);
-    const uint32_t a[4] = {s0.x, s0.y, s0.z, s0.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        r[2 * i] = v[2 * i] - bf16_lo(a[i]);
-        r[2 * i + 1] = v[2 * i + 1] - bf16_hi(a[i]);
-    }
-    s1 = pack8(r);
-    const uint32_t bq[4] = {s1.x, s1.y, s1.z, s1.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        r[2 * i] -= bf16_lo(bq[i]);
-        r[2 * i + 1] -= bf16_hi(bq[i]);
-    }
-    s2 = pack8(r);
-}
-__device__ __forceinline__ void split1x3(float v, uint16_t &s0, uint16_t &s1, uint16_t &s2) {
-    const uint32_t a = pack_bf16x2(v, 0.f) & 0xffffu;
-    const float r1 = v - __uint_as_float(a << 16);
-    const uint32_t bq = pack_bf16x2(r1, 0.f) & 0xffffu;
-    const float r2 = r1 - __uint_as_float(bq << 16);
-    s0 = (uint16_t)a;
-    s1 = (uint16_t)bq;
-    s2 = (uint16_t)(pack_bf16x2(r2, 0.f) & 0xffffu);
-}
-// the two 16-bit halves of a word: lo = the element of the even index
-__device__ __forceinline__ uint32_t pair16(uint32_t lo, uint32_t hi) { return (lo & 0xffffu) | (hi << 16); }
-__device__ __forceinline__ void split2x3(float a, float b, uint32_t &s0, uint32_t &s1, uint32_t &s2) {
-    uint16_t a0, a1, a2, b0, b1, b2;
-    split1x3(a, a0, a1, a2);
-    split1x3(b, b0, b1, b2);
-    s0 = pair16(a0, b0);
-    s1 = pair16(a1, b1);
-    s2 = pair16(a2, b2);
-}
-__device__ __forceinline__ void split2(float a, float b, uint32_t &hi, uint32_t &lo) {
-    uint16_t ah, al, bh, bl;
-    split1(a, ah, al);
-    split1(b, bh, bl);
-    hi = pair16(ah, bh);
-    lo = pair16(al, bl);
-}
 
 template <int L, int N, int ORIENT, int WPB>
 __global__ __launch_bounds__(64 * WPB) void bwd_dbdc_mfma_kernel(
@@ -794,45 +822,52 @@ __global__ __launch_bounds__(64 * WPB) void bwd_dbdc_mfma_kernel(
 // 16w .. 16w+15, so each head's operands are staged once and the causal work
 // per wavefront is the same (U takes k >= i, Y takes j <= i); MFMA layouts
 // as for bwd_dbdc_mfma.  Products (K in brackets):
-//   U_intra(i, p) = sum_{k >= i} W(k, i) dy_k[p]    [k]  A = W from CB^T rows, B = dy^T (LDS)
-//   Y_intra(i, p) = sum_{j <= i} V(i, j) x_j[p]     [j]  A = V from CB rows,   B = x^T  (LDS)
-//   U_inter(i, p) = sum_n B_i[n] ghat[p][n]         [n]  A = B rows, B = ghat (LDS [p][n])
-//   Y_inter(i, p) = sum_n C_i[n] h_prev[p][n]       [n]  A = C rows, B = h_prev (LDS)
-// with W(k, i) = exp2(G_k - G_i) CB(k, i) and V(i, j) = exp2(G_i - G_j) CB(i, j) dt_j;
-// the inter products are scaled per row afterwards (exp2(G_last - G_i), exp2(G_i)).
-// These feed ddt and the decay sums, which add thousands of per-token terms
-// with weights growing along the sequence, so every fp32 operand is carried as
-// three bf16 terms (about 2^-27 of it; two terms, 2^-18, left the full-size dA
-// at 0.7 of its bar): W x dy takes the six products of order up to 2^-16,
-// V x x and the inter products (x, B, C are bf16) three each.
-#ifndef BWD_INTRA3
-#define BWD_INTRA3 1
-#endif
+//   U_intra(i, p) = sum_{k >= i} W(k, i) dy_k[p]    [k]  W(k, i) = exp2(G_k - G_i) CB(k, i)
+//   Y_intra(i, p) = sum_{j <= i} V(i, j) x_j[p]     [j]  V(i, j) = exp2(G_i - G_j) CB(i, j) dt_j
+//   U_inter(i, p) = sum_n B_i[n] ghat[p][n]         [n]
+//   Y_inter(i, p) = sum_n C_i[n] h_prev[p][n]       [n]
+// the inter products scaled per row afterwards (exp2(G_last - G_i), exp2(G_i)).
+// K runs in 32-token steps.  A step wholly on the causal side of a strip
+// splits the decay at the step's edge token e (the first for U, the last for
+// Y) into a token factor and a row factor, both at most 1:
+//   exp2(G_k - G_i) = exp2(G_k - G_e) exp2(G_e - G_i),
+// so its A operand is C B^T itself (head-independent, split into three bf16
+// terms once per group), its B operand the staged dy or dt x scaled by the
+// token factor, and the row factor scales the step's product.  The step that
+// holds the strip's rows takes the exact pairwise decay per element.  These
+// sums feed ddt and the decay gradients, so every fp32 operand is carried as
+// three bf16 terms (two terms left the full-size dA at 0.7 of its bar) and a
+// product takes the six MFMAs of order 2^-16 and above.
 template <int L, int N>
 __global__ __launch_bounds__(4 * L) void bwd_dx_mfma_kernel(
     const uint16_t *__restrict__ x, const uint16_t *__restrict__ B, const uint16_t *__restrict__ C,
     const float *__restrict__ D, const float *__restrict__ dy, const float *__restrict__ Gws,
     const float *__restrict__ DTws, const float *__restrict__ CB, const float *__restrict__ CBT,
+    const uint16_t *__restrict__ CB3, const uint16_t *__restrict__ CBT3, int64_t plane,
     const float *__restrict__ gh, const float *__restrict__ hprev, float *__restrict__ dx,
     float *__restrict__ tok, int64_t T, int32_t H, int32_t G, int32_t nc, int64_t ntok) {
     constexpr int NB = L / 64, NP = P / 16, PN = N + 8;
     constexpr int NTH = 4 * L;                        // L/16 wavefronts: one 16-row strip each
-    // phases: U over token chunk 0..NB-1, Y over chunk 0..NB-1, the ghat and
-    // the h_prev inter products.  Each phase's global operands are loaded into
-    // registers while the previous phase computes (one workgroup fills a CU).
-    constexpr int NPH = 2 * NB + 2;
-    constexpr int N_DY = 64 * (P / 8), N_X = 64 * (P / 16), N_I = P * N / 4;   // staging items
-    constexpr int IT_DY = (N_DY + NTH - 1) / NTH, IT_X = (N_X + NTH - 1) / NTH,
-                  IT_I = (N_I + NTH - 1) / NTH;
-    constexpr int NSR0 = 2 * IT_DY > 2 * IT_X ? 2 * IT_DY : 2 * IT_X;
-    constexpr int NSR = NSR0 > IT_I ? NSR0 : IT_I;
-    // phase-shared LDS: the U phases use T0/T1/T3 (dy^T in three terms), the Y
-    // phases T2 (x^T), as [p][64 tokens] tiles; the inter phases Ih/Im/Il [p][N]
-    constexpr int NLDS = 3 * P * PN > 4 * P * SP ? 3 * P * PN : 4 * P * SP;
+    // phases: U and Y over token chunk 0..NB-1 (chunk ck holds steps 2ck and
+    // 2ck+1; U takes the steps at or after a strip's own, Y those at or
+    // before it, so every wavefront has two or three steps in each phase),
+    // then the ghat and the h_prev inter products.  Each phase's staged
+    // operands are loaded into registers while the previous phase computes
+    // (one workgroup fills a CU).
+    constexpr int NPH = NB + 2;
+    // staging items of a chunk phase: (token pair, 4 p) of dy, then
+    // (token pair, 8 p) of x; of an inter phase: 4 consecutive [p][n] values
+    constexpr int N_DY = 64 * (P / 8), N_X = 64 * (P / 16), N_S = N_DY + N_X, N_I = P * N / 4;
+    constexpr int IT_S = (N_S + NTH - 1) / NTH, IT_I = (N_I + NTH - 1) / NTH;
+    constexpr int NSR = 2 * IT_S > IT_I ? 2 * IT_S : IT_I;
+    // phase-shared LDS, [p][64 tokens] tiles: tiles 0..2 hold dy in three
+    // terms, 3..5 dy times its token factor, 6 x, 7..9 dt x times its token
+    // factor; the inter phases use Ih/Im/Il [p][N]
+    constexpr int TY = 6;                             // first Y tile
+    constexpr int NLDS = 3 * P * PN > 10 * P * SP ? 3 * P * PN : 10 * P * SP;
     __shared__ __align__(16) uint16_t lds[NLDS];
     __shared__ float Gs[L], DTs[L];
-    uint16_t *const T0 = lds, *const T1 = lds + P * SP, *const T3 = lds + 2 * P * SP,
-             *const T2 = lds + 3 * P * SP;
+    uint16_t *const Tu = lds;
     uint16_t *const Ih = lds, *const Im = lds + P * PN, *const Il = lds + 2 * P * PN;
     // logical block order (b, c, g, head) with the head fastest and
     // consecutive ids on one XCD: the heads of a group reuse the same C B^T
@@ -852,9 +887,9 @@ __global__ __launch_bounds__(4 * L) void bwd_dx_mfma_kernel(
     const int m = lane & 15, q = lane >> 4;
     const int64_t tc = (int64_t)c * L;
     const int arow = 16 * w + m;                      // A-operand row of this lane
+    const int sdiag = w >> 1;                         // the 32-token step holding the strip
     const int64_t ta = tc + arow;
-    const float *CBr = CB + bcg * (int64_t)(L * L) + (int64_t)arow * L;
-    const float *CBTr = CBT + bcg * (int64_t)(L * L) + (int64_t)arow * L;
+    const int64_t rowoff = bcg * (int64_t)(L * L) + (int64_t)arow * L;
     for (int e = tid; e < L; e += NTH) {
         Gs[e] = Gws[unit * L + e];
         DTs[e] = DTws[unit * L + e];
@@ -866,46 +901,36 @@ __global__ __launch_bounds__(4 * L) void bwd_dx_mfma_kernel(
         Y[i] = U[i];
     }
     uint4 sr[NSR];            // staging registers of the next phase
-    float4 ca[4];             // this lane's C B^T values of the next phase (two k-steps)
     uint4 ra[N / 32];         // this lane's B or C row of the next inter phase
 
     auto load_phase = [&](int ph) {
-        if (ph < 2 * NB) {
-            const bool isU = ph < NB;
-            const int ck = isU ? ph : ph - NB;
+        if (ph < NB) {
 #pragma unroll
-            for (int j = 0; j < NSR / 2; ++j) {
+            for (int j = 0; j < IT_S; ++j) {
                 const int e = tid + j * NTH;
                 sr[2 * j] = make_uint4(0u, 0u, 0u, 0u);
                 sr[2 * j + 1] = sr[2 * j];
-                if (e < (isU ? N_DY : N_X)) {
-                    const int r = 2 * (e % 32);
-                    const int pc = isU ? 4 * (e / 32) : 8 * (e / 32);
-                    const int64_t t = tc + 64 * ck + r;
-                    if (isU) {
-                        if (t < T)
-                            sr[2 * j] = *reinterpret_cast<const uint4 *>(dy + ((b * T + t) * H + h) * P + pc);
-                        if (t + 1 < T)
-                            sr[2 * j + 1] =
-                                *reinterpret_cast<const uint4 *>(dy + ((b * T + t + 1) * H + h) * P + pc);
-                    } else {
-                        if (t < T)
-                            sr[2 * j] = *reinterpret_cast<const uint4 *>(x + ((b * T + t) * H + h) * P + pc);
-                        if (t + 1 < T)
-                            sr[2 * j + 1] =
-                                *reinterpret_cast<const uint4 *>(x + ((b * T + t + 1) * H + h) * P + pc);
-                    }
+                if (e < N_DY) {
+                    const int r = 2 * (e % 32), pc = 4 * (e / 32);
+                    const int64_t t = tc + 64 * ph + r;
+                    if (t < T)
+                        sr[2 * j] = *reinterpret_cast<const uint4 *>(dy + ((b * T + t) * H + h) * P + pc);
+                    if (t + 1 < T)
+                        sr[2 * j + 1] =
+                            *reinterpret_cast<const uint4 *>(dy + ((b * T + t + 1) * H + h) * P + pc);
+                } else if (e < N_S) {
+                    const int ex = e - N_DY;
+                    const int r = 2 * (ex % 32), pc = 8 * (ex / 32);
+                    const int64_t t = tc + 64 * ph + r;
+                    if (t < T)
+                        sr[2 * j] = *reinterpret_cast<const uint4 *>(x + ((b * T + t) * H + h) * P + pc);
+                    if (t + 1 < T)
+                        sr[2 * j + 1] =
+                            *reinterpret_cast<const uint4 *>(x + ((b * T + t + 1) * H + h) * P + pc);
                 }
             }
-            const float *rowp = isU ? CBTr : CBr;
-#pragma unroll
-            for (int st = 0; st < 2; ++st) {
-                const int k0 = 64 * ck + 32 * st + 8 * q;
-                ca[2 * st] = *reinterpret_cast<const float4 *>(rowp + k0);
-                ca[2 * st + 1] = *reinterpret_cast<const float4 *>(rowp + k0 + 4);
-            }
         } else {
-            const float *src = (ph == 2 * NB ? gh : hprev) + unit * (int64_t)(P * N);
+            const float *src = (ph == NB ? gh : hprev) + unit * (int64_t)(P * N);
 #pragma unroll
             for (int j = 0; j < NSR; ++j) {
                 const int e = tid + j * NTH;
@@ -915,7 +940,7 @@ __global__ __launch_bounds__(4 * L) void bwd_dx_mfma_kernel(
                     sr[j] = *reinterpret_cast<const uint4 *>(src + pp * N + n4);
                 }
             }
-            const uint16_t *rows = (ph == 2 * NB ? B : C) + ((b * T + (ta < T ? ta : 0)) * G + g) * N;
+            const uint16_t *rows = (ph == NB ? B : C) + ((b * T + (ta < T ? ta : 0)) * G + g) * N;
 #pragma unroll
             for (int ks = 0; ks < N / 32; ++ks)
                 ra[ks] = ta < T ? *reinterpret_cast<const uint4 *>(rows + 32 * ks + 8 * q)
@@ -923,12 +948,15 @@ __global__ __launch_bounds__(4 * L) void bwd_dx_mfma_kernel(
         }
     };
     auto store_phase = [&](int ph) {
-        if (ph < NB) {                                 // dy^T, three terms
+        if (ph < NB) {
 #pragma unroll
-            for (int j = 0; j < NSR / 2; ++j) {
+            for (int j = 0; j < IT_S; ++j) {
                 const int e = tid + j * NTH;
-                if (e < N_DY) {
+                if (e < N_DY) {                        // dy, and dy times its token factor
                     const int r = 2 * (e % 32), p4 = 4 * (e / 32);
+                    const int k = 64 * ph + r;         // tokens k, k+1 (one 32-token step)
+                    const float ge = Gs[k & ~31];
+                    const float f0 = fast_exp2(Gs[k] - ge), f1 = fast_exp2(Gs[k + 1] - ge);
                     const uint4 u0 = sr[2 * j], u1 = sr[2 * j + 1];
                     const float a0[4] = {__uint_as_float(u0.x), __uint_as_float(u0.y),
                                          __uint_as_float(u0.z), __uint_as_float(u0.w)};
@@ -937,28 +965,41 @@ __global__ __launch_bounds__(4 * L) void bwd_dx_mfma_kernel(
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
                         uint32_t s0, s1, s2;
-                        split2x3(a0[i], a1[i], s0, s1, s2);
                         const int o = (p4 + i) * SP + r;
-                        *reinterpret_cast<uint32_t *>(T0 + o) = s0;
-                        *reinterpret_cast<uint32_t *>(T1 + o) = s1;
-                        *reinterpret_cast<uint32_t *>(T3 + o) = s2;
+                        split2x3(a0[i], a1[i], s0, s1, s2);
+                        *reinterpret_cast<uint32_t *>(Tu + o) = s0;
+                        *reinterpret_cast<uint32_t *>(Tu + P * SP + o) = s1;
+                        *reinterpret_cast<uint32_t *>(Tu + 2 * P * SP + o) = s2;
+                        split2x3(a0[i] * f0, a1[i] * f1, s0, s1, s2);
+                        *reinterpret_cast<uint32_t *>(Tu + 3 * P * SP + o) = s0;
+                        *reinterpret_cast<uint32_t *>(Tu + 4 * P * SP + o) = s1;
+                        *reinterpret_cast<uint32_t *>(Tu + 5 * P * SP + o) = s2;
                     }
-                }
-            }
-        } else if (ph < 2 * NB) {                      // x^T (exact)
-#pragma unroll
-            for (int j = 0; j < NSR / 2; ++j) {
-                const int e = tid + j * NTH;
-                if (e < N_X) {
-                    const int r = 2 * (e % 32), p8 = 8 * (e / 32);
+                } else if (e < N_S) {                  // x (exact), and dt x times its token factor
+                    const int ex = e - N_DY;
+                    const int r = 2 * (ex % 32), p8 = 8 * (ex / 32);
+                    const int jt = 64 * ph + r;
+                    const float ge = Gs[jt | 31];
+                    const float f0 = fast_exp2(ge - Gs[jt]) * DTs[jt];
+                    const float f1 = fast_exp2(ge - Gs[jt + 1]) * DTs[jt + 1];
                     const uint32_t w0[4] = {sr[2 * j].x, sr[2 * j].y, sr[2 * j].z, sr[2 * j].w};
                     const uint32_t w1[4] = {sr[2 * j + 1].x, sr[2 * j + 1].y, sr[2 * j + 1].z,
                                             sr[2 * j + 1].w};
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
-                        *reinterpret_cast<uint32_t *>(T2 + (p8 + 2 * i) * SP + r) = pair16(w0[i], w1[i]);
-                        *reinterpret_cast<uint32_t *>(T2 + (p8 + 2 * i + 1) * SP + r) =
-                            pair16(w0[i] >> 16, w1[i] >> 16);
+#pragma unroll
+                        for (int hf = 0; hf < 2; ++hf) {
+                            const int o = (p8 + 2 * i + hf) * SP + r;
+                            const uint32_t b0 = hf ? w0[i] >> 16 : w0[i] & 0xffffu;
+                            const uint32_t b1 = hf ? w1[i] >> 16 : w1[i] & 0xffffu;
+                            *reinterpret_cast<uint32_t *>(Tu + TY * P * SP + o) = pair16(b0, b1);
+                            uint32_t s0, s1, s2;
+                            split2x3(__uint_as_float(b0 << 16) * f0, __uint_as_float(b1 << 16) * f1, s0,
+                                     s1, s2);
+                            *reinterpret_cast<uint32_t *>(Tu + (TY + 1) * P * SP + o) = s0;
+                            *reinterpret_cast<uint32_t *>(Tu + (TY + 2) * P * SP + o) = s1;
+                            *reinterpret_cast<uint32_t *>(Tu + (TY + 3) * P * SP + o) = s2;
+                        }
                     }
                 }
             }
@@ -979,14 +1020,91 @@ __global__ __launch_bounds__(4 * L) void bwd_dx_mfma_kernel(
             }
         }
     };
+    // six products of two three-term operands, smallest first
+    auto mfma6 = [](const bf16x8 (&a)[3], const bf16x8 (&bb)[3], f32x4 acc) {
+        acc = mfma16x16x32(a[2], bb[0], acc);
+        acc = mfma16x16x32(a[0], bb[2], acc);
+        acc = mfma16x16x32(a[1], bb[1], acc);
+        acc = mfma16x16x32(a[1], bb[0], acc);
+        acc = mfma16x16x32(a[0], bb[1], acc);
+        return mfma16x16x32(a[0], bb[0], acc);
+    };
+    // one 32-token step s of U (isU) or Y whose staged tokens sit at toff
+    auto step = [&](const bool isU, const int s, const int toff, const float g_i) {
+        const int k0 = 32 * s + 8 * q;                 // this lane's 8 tokens of it
+        if (s == sdiag) {
+            // the exact pairwise decay, masked, from fp32 C B^T
+            const float *rowp = (isU ? CBT : CB) + rowoff + k0;
+            const float4 c0 = *reinterpret_cast<const float4 *>(rowp);
+            const float4 c1 = *reinterpret_cast<const float4 *>(rowp + 4);
+            const float cv[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+            float av[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int k = k0 + i;
+                av[i] = isU ? (k >= arow ? fast_exp2(Gs[k] - g_i) * cv[i] : 0.f)
+                            : (k <= arow ? fast_exp2(g_i - Gs[k]) * cv[i] * DTs[k] : 0.f);
+            }
+            uint4 a0, a1, a2;
+            split8x3(av, a0, a1, a2);
+            const bf16x8 a[3] = {as_bf16x8(a0), as_bf16x8(a1), as_bf16x8(a2)};
+#pragma unroll
+            for (int pt = 0; pt < NP; ++pt) {
+                const int off = (16 * pt + m) * SP + toff;
+                if (isU) {
+                    const bf16x8 bb[3] = {as_bf16x8(*reinterpret_cast<const uint4 *>(Tu + off)),
+                                          as_bf16x8(*reinterpret_cast<const uint4 *>(Tu + P * SP + off)),
+                                          as_bf16x8(*reinterpret_cast<const uint4 *>(Tu + 2 * P * SP + off))};
+                    U[pt] = mfma6(a, bb, U[pt]);
+                } else {
+                    const bf16x8 bx = as_bf16x8(*reinterpret_cast<const uint4 *>(Tu + TY * P * SP + off));
+                    Y[pt] = mfma16x16x32(a[2], bx, Y[pt]);
+                    Y[pt] = mfma16x16x32(a[1], bx, Y[pt]);
+                    Y[pt] = mfma16x16x32(a[0], bx, Y[pt]);
+                }
+            }
+        } else if (isU ? s > sdiag : s < sdiag) {
+            // wholly causal: C B^T in three terms times the scaled operand
+            const uint16_t *rowp = (isU ? CBT3 : CB3) + rowoff + k0;
+            const bf16x8 a[3] = {as_bf16x8(*reinterpret_cast<const uint4 *>(rowp)),
+                                 as_bf16x8(*reinterpret_cast<const uint4 *>(rowp + plane)),
+                                 as_bf16x8(*reinterpret_cast<const uint4 *>(rowp + 2 * plane))};
+            const int tb = isU ? 3 : TY + 1;           // first tile of the scaled operand
+            f32x4 part[NP];
+#pragma unroll
+            for (int pt = 0; pt < NP; ++pt) {
+                const int off = (16 * pt + m) * SP + toff;
+                const bf16x8 bb[3] = {
+                    as_bf16x8(*reinterpret_cast<const uint4 *>(Tu + tb * P * SP + off)),
+                    as_bf16x8(*reinterpret_cast<const uint4 *>(Tu + (tb + 1) * P * SP + off)),
+                    as_bf16x8(*reinterpret_cast<const uint4 *>(Tu + (tb + 2) * P * SP + off))};
+                part[pt] = mfma6(a, bb, f32x4{0.f, 0.f, 0.f, 0.f});
+            }
+            // the row factor: exp2(G_e - G_i) for U (e the step's first
+            // token), exp2(G_i - G_e) for Y (e its last)
+            const float ge = Gs[isU ? 32 * s : 32 * s + 31];
+#pragma unroll
+            for (int e4 = 0; e4 < 4; ++e4) {
+                const float gr = Gs[16 * w + 4 * q + e4];
+                const float rf = isU ? fast_exp2(ge - gr) : fast_exp2(gr - ge);
+#pragma unroll
+                for (int pt = 0; pt < NP; ++pt) {
+                    if (isU)
+                        U[pt][e4] = fmaf(rf, part[pt][e4], U[pt][e4]);
+                    else
+                        Y[pt][e4] = fmaf(rf, part[pt][e4], Y[pt][e4]);
+                }
+            }
+        }
+    };
 
     __syncthreads();
-    const float gi = Gs[arow];
+    const float g_i = Gs[arow];
     load_phase(0);
     // unrolled: each phase's code is specialised, so only its registers are live
 #pragma unroll
     for (int ph = 0; ph < NPH; ++ph) {
-        if (ph == 2 * NB)
+        if (ph == NB)
 #pragma unroll
             for (int i = 0; i < NP; ++i) {
                 Ui[i] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -994,73 +1112,18 @@ __global__ __launch_bounds__(4 * L) void bwd_dx_mfma_kernel(
             }
         __syncthreads();                               // the previous phase is done with the LDS
         store_phase(ph);
-        // this phase's A operands, before the registers take the next phase's loads
-        const float4 cur[4] = {ca[0], ca[1], ca[2], ca[3]};
         uint4 rcur[N / 32];
 #pragma unroll
         for (int ks = 0; ks < N / 32; ++ks) rcur[ks] = ra[ks];
         if (ph + 1 < NPH) load_phase(ph + 1);
         __syncthreads();
-        if (ph < NB) {                                 // U: k >= i
-            const int kc = ph;
-            if (16 * w <= 64 * kc + 63)
+        if (ph < NB) {
 #pragma unroll
-                for (int st = 0; st < 2; ++st) {
-                    const int k0 = 64 * kc + 32 * st + 8 * q;
-                    const float cv[8] = {cur[2 * st].x, cur[2 * st].y, cur[2 * st].z, cur[2 * st].w,
-                                         cur[2 * st + 1].x, cur[2 * st + 1].y, cur[2 * st + 1].z,
-                                         cur[2 * st + 1].w};
-                    float wv[8];
+            for (int st = 0; st < 2; ++st) step(true, 2 * ph + st, 32 * st + 8 * q, g_i);
 #pragma unroll
-                    for (int i = 0; i < 8; ++i) {
-                        const int k = k0 + i;
-                        wv[i] = k >= arow ? fast_exp2(Gs[k] - gi) * cv[i] : 0.f;
-                    }
-                    uint4 a0, a1, a2;
-                    split8x3(wv, a0, a1, a2);
-#pragma unroll
-                    for (int pt = 0; pt < NP; ++pt) {
-                        const int off = (16 * pt + m) * SP + 32 * st + 8 * q;
-                        const bf16x8 b0 = as_bf16x8(*reinterpret_cast<const uint4 *>(T0 + off));
-                        const bf16x8 b1 = as_bf16x8(*reinterpret_cast<const uint4 *>(T1 + off));
-                        const bf16x8 b2 = as_bf16x8(*reinterpret_cast<const uint4 *>(T3 + off));
-                        // the products of order 2^-16 and above, smallest first
-                        U[pt] = mfma16x16x32(as_bf16x8(a2), b0, U[pt]);
-                        U[pt] = mfma16x16x32(as_bf16x8(a0), b2, U[pt]);
-                        U[pt] = mfma16x16x32(as_bf16x8(a1), b1, U[pt]);
-                        U[pt] = mfma16x16x32(as_bf16x8(a1), b0, U[pt]);
-                        U[pt] = mfma16x16x32(as_bf16x8(a0), b1, U[pt]);
-                        U[pt] = mfma16x16x32(as_bf16x8(a0), b0, U[pt]);
-                    }
-                }
-        } else if (ph < 2 * NB) {                      // Y: j <= i
-            const int jc = ph - NB;
-            if (16 * w + 15 >= 64 * jc)
-#pragma unroll
-                for (int st = 0; st < 2; ++st) {
-                    const int j0 = 64 * jc + 32 * st + 8 * q;
-                    const float cv[8] = {cur[2 * st].x, cur[2 * st].y, cur[2 * st].z, cur[2 * st].w,
-                                         cur[2 * st + 1].x, cur[2 * st + 1].y, cur[2 * st + 1].z,
-                                         cur[2 * st + 1].w};
-                    float vv[8];
-#pragma unroll
-                    for (int i = 0; i < 8; ++i) {
-                        const int j = j0 + i;
-                        vv[i] = j <= arow ? fast_exp2(gi - Gs[j]) * cv[i] * DTs[j] : 0.f;
-                    }
-                    uint4 a0, a1, a2;
-                    split8x3(vv, a0, a1, a2);
-#pragma unroll
-                    for (int pt = 0; pt < NP; ++pt) {
-                        const int off = (16 * pt + m) * SP + 32 * st + 8 * q;
-                        const bf16x8 bx = as_bf16x8(*reinterpret_cast<const uint4 *>(T2 + off));
-                        Y[pt] = mfma16x16x32(as_bf16x8(a2), bx, Y[pt]);
-                        Y[pt] = mfma16x16x32(as_bf16x8(a1), bx, Y[pt]);
-                        Y[pt] = mfma16x16x32(as_bf16x8(a0), bx, Y[pt]);
-                    }
-                }
+            for (int st = 0; st < 2; ++st) step(false, 2 * ph + st, 32 * st + 8 * q, g_i);
         } else {                                       // inter: (B or C rows) x (ghat or h_prev)
-            const bool first = ph == 2 * NB;
+            const bool first = ph == NB;
 #pragma unroll
             for (int ks = 0; ks < N / 32; ++ks)
 #pragma unroll
@@ -1299,10 +1362,11 @@ hipError_t launch_bwd_t(const Shape &s, const BwdArgs &a, hipStream_t st) {
         constexpr int NTRI = (L / 64) * (L / 64 + 1) / 2;
         const uint64_t ncb = (uint64_t)s.Bt * s.nc * s.G;
         hipLaunchKernelGGL((bwd_cb_kernel<L, N, Tio>), dim3((uint32_t)(ncb * NTRI)), dim3(256), 0,
-                           st, B, C, a.CB, a.CBT, T, G, nc);
+                           st, B, C, a.CB, a.CBT, a.CB3, a.CBT3, T, G, nc);
         if constexpr (sizeof(Tio) == 2)
             hipLaunchKernelGGL((bwd_dx_mfma_kernel<L, N>), dim3((uint32_t)units),
-                               dim3(4 * L), 0, st, x, B, C, a.D, a.dy, a.G, a.DT, a.CB, a.CBT, a.S,
+                               dim3(4 * L), 0, st, x, B, C, a.D, a.dy, a.G, a.DT, a.CB, a.CBT,
+                               a.CB3, a.CBT3, (int64_t)(ncb * L * L), a.S,
                                (const float *)a.hprev, a.dx, a.tok, T, H, G, nc,
                                (int64_t)units * L);
         else

@@ -519,13 +519,14 @@ ssd_status ssd_decode_step_lp(void *state, const ssd_state_format *fmt, const vo
 }
 
 // Backward workspace: the forward's regions, then the final state, C B^T per
-// (b, chunk, group) (and its transpose for bf16 io), three planes of per-token scalars, 3 * Bt*H fp64 partials and,
+// (b, chunk, group) (and, for bf16 io, its transpose and both as three bf16
+// terms), three planes of per-token scalars, 3 * Bt*H fp64 partials and,
 // for bf16 io, h_prev again in fp32 (the forward keeps it in bf16 for its
 // MFMA; the decay gradient sums per-token products of it over the whole
 // sequence, where bf16's rounding would not cancel).
 struct BwdLayout {
     Layout fwd;
-    size_t fin, cb, cbt, tok, part, hp32, total;
+    size_t fin, cb, cbt, cb3, cbt3, tok, part, hp32, total;
 };
 
 BwdLayout bwd_layout_of(const ssd::Shape &s) {
@@ -535,7 +536,9 @@ BwdLayout bwd_layout_of(const ssd::Shape &s) {
     l.fin = align256(l.fwd.total);
     l.cb = align256(l.fin + bh * s.P * s.N * sizeof(float));
     l.cbt = align256(l.cb + ssd::bwd_cb_bytes(s));
-    l.tok = align256(l.cbt + (s.bf16 ? ssd::bwd_cb_bytes(s) : 0));
+    l.cb3 = align256(l.cbt + (s.bf16 ? ssd::bwd_cb_bytes(s) : 0));
+    l.cbt3 = align256(l.cb3 + (s.bf16 ? ssd::bwd_cb_bytes(s) * 3 / 2 : 0));
+    l.tok = align256(l.cbt3 + (s.bf16 ? ssd::bwd_cb_bytes(s) * 3 / 2 : 0));
     l.part = align256(l.tok + 3 * bh * s.nc * s.L * sizeof(float));
     l.hp32 = align256(l.part + 3 * bh * sizeof(double));
     const size_t hp = s.bf16 ? bh * s.nc * s.P * s.N * sizeof(float) : 0;
@@ -613,6 +616,8 @@ ssd_status ssd_chunked_bwd(const void *x, const float *dt, const float *A, const
                    w.S, hp32, reinterpret_cast<float *>(base + l.cb),
                    s.bf16 ? reinterpret_cast<float *>(base + l.cbt) : nullptr,
                    reinterpret_cast<float *>(base + l.tok),
+                   s.bf16 ? reinterpret_cast<uint16_t *>(base + l.cb3) : nullptr,
+                   s.bf16 ? reinterpret_cast<uint16_t *>(base + l.cbt3) : nullptr,
                    reinterpret_cast<double *>(base + l.part)};
     r = hip_result(ssd::launch_chunked_bwd(s, a, st), "chunked_bwd", st);
     if (r != SSD_OK) return r;

@@ -81,6 +81,7 @@ struct BwdArgs {
     float *S;
     const void *hprev;
     float *CB, *CBT, *tok;   // CBT: CB transposed, bf16 io only (NULL otherwise)
+    uint16_t *CB3, *CBT3;    // CB and CBT as three bf16 terms each, bf16 io only
     double *part;
 };
 size_t bwd_cb_bytes(const Shape &s);
