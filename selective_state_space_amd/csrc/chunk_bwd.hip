@@ -131,20 +131,16 @@ __device__ __forceinline__ void split1x3(float v, uint16_t &s0, uint16_t &s1, ui
 }
 // the two 16-bit halves of a word: lo = the element of the even index
 __device__ __forceinline__ uint32_t pair16(uint32_t lo, uint32_t hi) { return (lo & 0xffffu) | (hi << 16); }
+// split1x3 / split1 of two values at once, one paired conversion per term
 __device__ __forceinline__ void split2x3(float a, float b, uint32_t &s0, uint32_t &s1, uint32_t &s2) {
-    uint16_t a0, a1, a2, b0, b1, b2;
-    split1x3(a, a0, a1, a2);
-    split1x3(b, b0, b1, b2);
-    s0 = pair16(a0, b0);
-    s1 = pair16(a1, b1);
-    s2 = pair16(a2, b2);
+    s0 = pack_bf16x2(a, b);
+    const float ra = a - bf16_lo(s0), rb = b - bf16_hi(s0);
+    s1 = pack_bf16x2(ra, rb);
+    s2 = pack_bf16x2(ra - bf16_lo(s1), rb - bf16_hi(s1));
 }
 __device__ __forceinline__ void split2(float a, float b, uint32_t &hi, uint32_t &lo) {
-    uint16_t ah, al, bh, bl;
-    split1(a, ah, al);
-    split1(b, bh, bl);
-    hi = pair16(ah, bh);
-    lo = pair16(al, bl);
+    hi = pack_bf16x2(a, b);
+    lo = pack_bf16x2(a - bf16_lo(hi), b - bf16_hi(hi));
 }
 
 // ---- bwd_dstate: dSp[b,h,c] = sum_k exp2(G_k) dy_k (outer) C_k, [P][N] ------
