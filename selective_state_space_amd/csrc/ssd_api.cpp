@@ -207,7 +207,7 @@ ssd_status run_state_fwd(const ssd::Shape &s, const void *x, const void *B, cons
                          float *fin, const Ws &w, hipStream_t st) {
     const int r = state_fwd_rows();
     return hip_result(ssd::launch_state_fwd(s, x, B, w.G, w.DT, init, w.hprev, fin, w.S,
-                                            r > 0 ? r : 0, st),
+                                            r > 0 ? r : 0, false, st),
                       "state_fwd", st);
 }
 ssd_status run_scan(const ssd::Shape &s, const void *x, const void *B, const void *C,
@@ -602,15 +602,24 @@ ssd_status ssd_chunked_bwd(const void *x, const float *dt, const float *A, const
     char *base = static_cast<char *>(workspace);
     float *fin = reinterpret_cast<float *>(base + l.fin);
     hipStream_t st = static_cast<hipStream_t>(stream);
-    // the forward's chunk quantities again: G, DT, S, then h_prev in fp32 and
-    // the final state (state_passing writes fp32 h_prev for fp32 io)
+    // the forward's chunk quantities again: G, DT, then h_prev in fp32 and the
+    // final state, by the one-pass state stage where the forward would take
+    // it, else by S (chunk_state) and state_passing, which writes fp32 h_prev
+    // for fp32 io
     void *hp32 = s.bf16 ? static_cast<void *>(base + l.hp32) : w.hprev;
-    ssd::Shape s32 = s;
-    s32.bf16 = false;
     if ((r = run_cumsum(s, dt, A, w, st, nullptr)) != SSD_OK) return r;
-    if ((r = run_state(s, x, B, w, st)) != SSD_OK) return r;
-    r = hip_result(ssd::launch_state_passing(s32, w.S, w.G, init_state, hp32, fin, st),
-                   "state_passing", st);
+    if (use_state_fwd(s)) {
+        const int rows = state_fwd_rows();
+        r = hip_result(ssd::launch_state_fwd(s, x, B, w.G, w.DT, init_state, hp32, fin, w.S,
+                                             rows > 0 ? rows : 0, true, st),
+                       "state_fwd", st);
+    } else {
+        ssd::Shape s32 = s;
+        s32.bf16 = false;
+        if ((r = run_state(s, x, B, w, st)) != SSD_OK) return r;
+        r = hip_result(ssd::launch_state_passing(s32, w.S, w.G, init_state, hp32, fin, st),
+                       "state_passing", st);
+    }
     if (r != SSD_OK) return r;
     ssd::BwdArgs a{x, B, C, A, D, dy, dfinal, fin, dinit, dx, ddt, dA, dB, dC, dD, w.G, w.DT,
                    w.S, hp32, reinterpret_cast<float *>(base + l.cb),

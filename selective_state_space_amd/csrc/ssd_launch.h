@@ -31,7 +31,7 @@ bool state_fwd_preferred(const Shape &s);   // shape heuristic of the fused call
 size_t state_fwd_bfrag_bytes(const Shape &s);
 hipError_t launch_state_fwd(const Shape &s, const void *x, const void *B, const float *Gws,
                             const float *DTws, const float *init, void *hprev, float *fin,
-                            void *bfrag, int rows_per_block, hipStream_t st);
+                            void *bfrag, int rows_per_block, bool hprev_f32, hipStream_t st);
 // K = s.T tokens per sequence; snaps / parent NULL = none; update = 0 leaves
 // the state unwritten.
 struct MultiArgs {

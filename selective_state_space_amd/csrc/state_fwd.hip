@@ -69,7 +69,7 @@ struct FwdArgs {
     const uint16_t *x;
     const uint4 *BF;   // B in MFMA fragment order, from b_fragments_kernel
     const float *Gws, *DTws, *init;
-    uint16_t *hprev;
+    void *hprev;       // bf16, or fp32 when the kernel's HP32 is set
     float *fin;
     int64_t T;
     int32_t H, G, nc, hpg;
@@ -160,7 +160,7 @@ __global__ __launch_bounds__(256) void b_fragments_kernel(const uint16_t *__rest
     }
 }
 
-template <int L, int N, int SPB>
+template <int L, int N, int SPB, bool HP32>
 __global__ __launch_bounds__(256, 2) void state_fwd_kernel(FwdArgs a, uint32_t nblk) {
     using Cfg = FwdCfg<L, N, SPB>;
     constexpr int P = 64, NS = Cfg::NS, HS = Cfg::HS, SW = Cfg::SW, TW = Cfg::TW;
@@ -371,7 +371,7 @@ __global__ __launch_bounds__(256, 2) void state_fwd_kernel(FwdArgs a, uint32_t n
         }
     };
     auto store_hprev = [&](int32_t c) {
-        uint16_t *hp = a.hprev + (bhi * a.nc + c) * (int64_t)(P * N) + ncol;
+        const int64_t o = (bhi * a.nc + c) * (int64_t)(P * N) + ncol;
 #pragma unroll
         for (int i = 0; i < SW; ++i)
 #pragma unroll
@@ -379,7 +379,10 @@ __global__ __launch_bounds__(256, 2) void state_fwd_kernel(FwdArgs a, uint32_t n
                 float v[TW];
 #pragma unroll
                 for (int j = 0; j < TW; ++j) v[j] = acc[i][j][e];
-                store_bf<TW>(hp + prow(i, e) * N, v);
+                if constexpr (HP32)
+                    store_f<TW>(static_cast<float *>(a.hprev) + o + prow(i, e) * N, v);
+                else
+                    store_bf<TW>(static_cast<uint16_t *>(a.hprev) + o + prow(i, e) * N, v);
             }
     };
 
@@ -442,27 +445,31 @@ __global__ __launch_bounds__(256, 2) void state_fwd_kernel(FwdArgs a, uint32_t n
 }
 
 template <int L, int N, int SPB>
-hipError_t launch_fwd(const Shape &s, const FwdArgs &a, hipStream_t st) {
+hipError_t launch_fwd(const Shape &s, const FwdArgs &a, bool hp32, hipStream_t st) {
     const uint64_t nblk = (uint64_t)s.Bt * s.H * (4 / SPB);
-    hipLaunchKernelGGL((state_fwd_kernel<L, N, SPB>), dim3((uint32_t)nblk), dim3(256), 0, st, a,
-                       (uint32_t)nblk);
+    if (hp32)
+        hipLaunchKernelGGL((state_fwd_kernel<L, N, SPB, true>), dim3((uint32_t)nblk), dim3(256), 0,
+                           st, a, (uint32_t)nblk);
+    else
+        hipLaunchKernelGGL((state_fwd_kernel<L, N, SPB, false>), dim3((uint32_t)nblk), dim3(256),
+                           0, st, a, (uint32_t)nblk);
     return hipGetLastError();
 }
 
 template <int L, int N>
-hipError_t launch_fwd_n(const Shape &s, const FwdArgs &a, int spb, hipStream_t st) {
+hipError_t launch_fwd_n(const Shape &s, const FwdArgs &a, int spb, bool hp32, hipStream_t st) {
     switch (spb) {
-    case 4: return launch_fwd<L, N, 4>(s, a, st);
-    case 2: return launch_fwd<L, N, 2>(s, a, st);
-    case 1: return launch_fwd<L, N, 1>(s, a, st);
+    case 4: return launch_fwd<L, N, 4>(s, a, hp32, st);
+    case 2: return launch_fwd<L, N, 2>(s, a, hp32, st);
+    case 1: return launch_fwd<L, N, 1>(s, a, hp32, st);
     default: return hipErrorInvalidValue;
     }
 }
 
 template <int L>
-hipError_t launch_fwd_l(const Shape &s, const FwdArgs &a, int spb, hipStream_t st) {
-    if (s.N == 64) return launch_fwd_n<L, 64>(s, a, spb, st);
-    if (s.N == 128) return launch_fwd_n<L, 128>(s, a, spb, st);
+hipError_t launch_fwd_l(const Shape &s, const FwdArgs &a, int spb, bool hp32, hipStream_t st) {
+    if (s.N == 64) return launch_fwd_n<L, 64>(s, a, spb, hp32, st);
+    if (s.N == 128) return launch_fwd_n<L, 128>(s, a, spb, hp32, st);
     return hipErrorInvalidValue;
 }
 
@@ -500,7 +507,7 @@ size_t state_fwd_bfrag_bytes(const Shape &s) {
 
 hipError_t launch_state_fwd(const Shape &s, const void *x, const void *B, const float *Gws,
                             const float *DTws, const float *init, void *hprev, float *fin,
-                            void *bfrag, int spb, hipStream_t st) {
+                            void *bfrag, int spb, bool hprev_f32, hipStream_t st) {
     if (!state_fwd_supported(s)) return hipErrorInvalidValue;
     if (s.Bt == 0 || s.H == 0) return hipSuccess;
     if (s.nc == 0 && !fin) return hipSuccess;
@@ -528,7 +535,7 @@ hipError_t launch_state_fwd(const Shape &s, const void *x, const void *B, const 
     a.Gws = Gws;
     a.DTws = DTws;
     a.init = init;
-    a.hprev = (uint16_t *)hprev;
+    a.hprev = hprev;
     a.fin = fin;
     a.T = s.T;
     a.H = (int32_t)s.H;
@@ -537,9 +544,9 @@ hipError_t launch_state_fwd(const Shape &s, const void *x, const void *B, const 
     a.hpg = (int32_t)(s.H / s.G);
     if (spb <= 0) spb = state_fwd_rows_per_block(s);
     switch (s.L) {
-    case 64: return launch_fwd_l<64>(s, a, spb, st);
-    case 128: return launch_fwd_l<128>(s, a, spb, st);
-    case 256: return launch_fwd_l<256>(s, a, spb, st);
+    case 64: return launch_fwd_l<64>(s, a, spb, hprev_f32, st);
+    case 128: return launch_fwd_l<128>(s, a, spb, hprev_f32, st);
+    case 256: return launch_fwd_l<256>(s, a, spb, hprev_f32, st);
     default: return hipErrorInvalidValue;
     }
 }
