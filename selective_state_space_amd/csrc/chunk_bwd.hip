@@ -1344,7 +1344,7 @@ hipError_t launch_bwd_t(const Shape &s, const BwdArgs &a, hipStream_t st) {
     const int64_t T = s.T;
     const int32_t H = (int32_t)s.H, G = (int32_t)s.G, nc = (int32_t)s.nc;
     const Tio *x = (const Tio *)a.x, *B = (const Tio *)a.B, *C = (const Tio *)a.C;
-    if (units > 0) {
+    if (units > 0 && !a.ghat_ready) {
         if constexpr (sizeof(Tio) == 2)
             hipLaunchKernelGGL((bwd_dstate_mfma_kernel<L, N>), dim3((uint32_t)units), dim3(256), 0,
                                st, a.dy, C, a.G, a.S, T, H, G, nc);
@@ -1352,8 +1352,11 @@ hipError_t launch_bwd_t(const Shape &s, const BwdArgs &a, hipStream_t st) {
             hipLaunchKernelGGL((bwd_dstate_kernel<L, N, Tio>), dim3((uint32_t)units), dim3(256), 0,
                                st, a.dy, C, a.G, a.S, T, H, G, nc);
     }
+    // with ghat already in S only the boundary dot <dfinal, final> remains
+    // (no chunk steps, dinit untouched)
     hipLaunchKernelGGL((bwd_passing_kernel<L, N>), dim3((uint32_t)(s.Bt * s.H)), dim3(256), 0, st,
-                       a.S, a.G, a.dfinal, a.fin, a.dinit, a.part + 2 * s.Bt * s.H, nc);
+                       a.S, a.G, a.dfinal, a.fin, a.ghat_ready ? nullptr : a.dinit,
+                       a.part + 2 * s.Bt * s.H, a.ghat_ready ? 0 : nc);
     if (units > 0) {
         constexpr int NTRI = (L / 64) * (L / 64 + 1) / 2;
         const uint64_t ncb = (uint64_t)s.Bt * s.nc * s.G;

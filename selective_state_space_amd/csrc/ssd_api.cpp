@@ -197,6 +197,14 @@ int state_fwd_rows() {
     const int v = atoi(e);
     return (v == 0 || v == 1 || v == 2 || v == 4) ? v : -1;
 }
+// SSD_STATE_ADJ_ROWS: 4, 2 or 1 forces that row split of the backward's
+// one-pass adjoint scan (tests cover every path); otherwise the shape picks.
+int state_adj_rows() {
+    const char *e = getenv("SSD_STATE_ADJ_ROWS");
+    if (!e || !e[0]) return 0;
+    const int v = atoi(e);
+    return (v == 1 || v == 2 || v == 4) ? v : 0;
+}
 bool use_state_fwd(const ssd::Shape &s) {
     if (!ssd::state_fwd_supported(s)) return false;
     const int r = state_fwd_rows();
@@ -526,7 +534,7 @@ ssd_status ssd_decode_step_lp(void *state, const ssd_state_format *fmt, const vo
 // sequence, where bf16's rounding would not cancel).
 struct BwdLayout {
     Layout fwd;
-    size_t fin, cb, cbt, cb3, cbt3, tok, part, hp32, total;
+    size_t fin, cb, cbt, cb3, cbt3, cfr, tok, part, hp32, total;
 };
 
 BwdLayout bwd_layout_of(const ssd::Shape &s) {
@@ -538,7 +546,8 @@ BwdLayout bwd_layout_of(const ssd::Shape &s) {
     l.cbt = align256(l.cb + ssd::bwd_cb_bytes(s));
     l.cb3 = align256(l.cbt + (s.bf16 ? ssd::bwd_cb_bytes(s) : 0));
     l.cbt3 = align256(l.cb3 + (s.bf16 ? ssd::bwd_cb_bytes(s) * 3 / 2 : 0));
-    l.tok = align256(l.cbt3 + (s.bf16 ? ssd::bwd_cb_bytes(s) * 3 / 2 : 0));
+    l.cfr = align256(l.cbt3 + (s.bf16 ? ssd::bwd_cb_bytes(s) * 3 / 2 : 0));
+    l.tok = align256(l.cfr + (ssd::state_adj_supported(s) ? ssd::state_fwd_bfrag_bytes(s) : 0));
     l.part = align256(l.tok + 3 * bh * s.nc * s.L * sizeof(float));
     l.hp32 = align256(l.part + 3 * bh * sizeof(double));
     const size_t hp = s.bf16 ? bh * s.nc * s.P * s.N * sizeof(float) : 0;
@@ -627,7 +636,18 @@ ssd_status ssd_chunked_bwd(const void *x, const float *dt, const float *A, const
                    reinterpret_cast<float *>(base + l.tok),
                    s.bf16 ? reinterpret_cast<uint16_t *>(base + l.cb3) : nullptr,
                    s.bf16 ? reinterpret_cast<uint16_t *>(base + l.cbt3) : nullptr,
-                   reinterpret_cast<double *>(base + l.part)};
+                   reinterpret_cast<double *>(base + l.part), false};
+    // the state adjoint: the one-pass reverse scan where the forward takes the
+    // one-pass form, else per-chunk sums and a separate reverse scan
+    if (use_state_fwd(s) && ssd::state_adj_supported(s)) {
+        r = hip_result(ssd::launch_state_adj(s, static_cast<const float *>(dy), C, w.G,
+                                             static_cast<const float *>(dfinal), w.S,
+                                             static_cast<float *>(dinit), base + l.cfr,
+                                             state_adj_rows(), st),
+                       "state_adj", st);
+        if (r != SSD_OK) return r;
+        a.ghat_ready = true;
+    }
     r = hip_result(ssd::launch_chunked_bwd(s, a, st), "chunked_bwd", st);
     if (r != SSD_OK) return r;
     return ok();

@@ -32,6 +32,14 @@ size_t state_fwd_bfrag_bytes(const Shape &s);
 hipError_t launch_state_fwd(const Shape &s, const void *x, const void *B, const float *Gws,
                             const float *DTws, const float *init, void *hprev, float *fin,
                             void *bfrag, int rows_per_block, bool hprev_f32, hipStream_t st);
+// The backward's adjoint scan in the same one-pass form, chunks last to
+// first: ghat[c] (fp32, the adjoint of the state leaving chunk c) and dinit
+// (NULL = not written) from dy (fp32), C (bf16) and dfinal (NULL = zero);
+// cfrag: scratch of state_fwd_bfrag_bytes(s) bytes (C in fragment order).
+bool state_adj_supported(const Shape &s);
+hipError_t launch_state_adj(const Shape &s, const float *dy, const void *C, const float *Gws,
+                            const float *dfinal, float *ghat, float *dinit, void *cfrag,
+                            int rows_per_block, hipStream_t st);
 // K = s.T tokens per sequence; snaps / parent NULL = none; update = 0 leaves
 // the state unwritten.
 struct MultiArgs {
@@ -83,6 +91,7 @@ struct BwdArgs {
     float *CB, *CBT, *tok;   // CBT: CB transposed, bf16 io only (NULL otherwise)
     uint16_t *CB3, *CBT3;    // CB and CBT as three bf16 terms each, bf16 io only
     double *part;
+    bool ghat_ready;         // S already holds ghat and dinit is written (launch_state_adj)
 };
 size_t bwd_cb_bytes(const Shape &s);
 hipError_t launch_chunked_bwd(const Shape &s, const BwdArgs &a, hipStream_t st);

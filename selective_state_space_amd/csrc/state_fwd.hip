@@ -59,14 +59,14 @@ struct FwdCfg {
 
 // Two half-chunk buffers of x*w fragments (the half being multiplied and the
 // half being built) and the per-token weights of two chunks.
-template <int L, int SPB>
+template <int L, int SPB, int NTERM>
 struct FwdSmem {
-    uint4 AF[2][L / 64][2][SPB][64];  // half, slab of the half, head/remainder, row set s, lane
+    uint4 AF[2][L / 64][NTERM][SPB][64];  // half, slab of the half, bf16 term, row set s, lane
     float w[2][L];                    // by chunk parity
 };
 
 struct FwdArgs {
-    const uint16_t *x;
+    const void *x;     // x (bf16), or dy (fp32) for the adjoint
     const uint4 *BF;   // B in MFMA fragment order, from b_fragments_kernel
     const float *Gws, *DTws, *init;
     void *hprev;       // bf16, or fp32 when the kernel's HP32 is set
@@ -93,6 +93,38 @@ __device__ __forceinline__ uint2 load_bf(__amdgpu_buffer_rsrc_t r, uint32_t off)
 }
 // the word of element j of piece v
 __device__ __forceinline__ uint32_t word_of(uint2 v, int j) { return (j < 2) ? v.x : v.y; }
+
+// the three modes of state_fwd_kernel: the forward with bf16 or fp32 h_prev,
+// and the adjoint scan of the backward
+constexpr int kModeBf16 = 0, kModeF32 = 1, kModeAdjoint = 2;
+
+// a lane's piece of SPB consecutive elements of one token row: SPB bf16 fit
+// in two words; SPB fp32 take four words when SPB = 4
+template <bool WIDE> struct XPiece { using type = uint2; };
+template <> struct XPiece<true> { using type = uint4; };
+
+// K consecutive fp32 (K = 4, 2, 1) by a buffer load, as in load_bf
+template <int K, int AUX = 0>
+__device__ __forceinline__ auto load_f32p(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    if constexpr (K == 4) {
+        const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, AUX);
+        return make_uint4(v[0], v[1], v[2], v[3]);
+    } else if constexpr (K == 2) {
+        const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, AUX);
+        return make_uint2(v[0], v[1]);
+    } else {
+        return make_uint2(__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, AUX), 0u);
+    }
+}
+// element j of a piece, as a float: bf16 pieces (two to a word) or fp32
+__device__ __forceinline__ float elem_of(uint2 v, int j, bool f32) {
+    if (f32) return __uint_as_float(j == 0 ? v.x : v.y);
+    const uint32_t w = word_of(v, j);
+    return (j & 1) ? bf16_hi(w) : bf16_lo(w);
+}
+__device__ __forceinline__ float elem_of(uint4 v, int j, bool) {
+    return __uint_as_float(j == 0 ? v.x : j == 1 ? v.y : j == 2 ? v.z : v.w);
+}
 
 // K consecutive floats of a state row
 template <int K>
@@ -160,14 +192,20 @@ __global__ __launch_bounds__(256) void b_fragments_kernel(const uint16_t *__rest
     }
 }
 
-template <int L, int N, int SPB, bool HP32>
+template <int L, int N, int SPB, int MODE>
 __global__ __launch_bounds__(256, 2) void state_fwd_kernel(FwdArgs a, uint32_t nblk) {
     using Cfg = FwdCfg<L, N, SPB>;
     constexpr int P = 64, NS = Cfg::NS, HS = Cfg::HS, SW = Cfg::SW, TW = Cfg::TW;
     constexpr int PSPLIT = 4 / SPB;
     constexpr int NT = N / 16;
     constexpr int R = NS < 4 ? NS : 4;   // B ring depth (slabs in flight)
-    __shared__ FwdSmem<L, SPB> sm;
+    constexpr bool ADJ = MODE == kModeAdjoint, HP32 = MODE != kModeBf16;
+    constexpr int NTERM = ADJ ? 3 : 2;   // bf16 terms of the x*w (dy*w) operand
+    constexpr int ES = ADJ ? 4 : 2;      // bytes per element of x (dy)
+    using XP = typename XPiece<ADJ && SPB == 4>::type;
+    __shared__ FwdSmem<L, SPB, NTERM> sm;
+    // the chunk a step works on: in order, or last to first for the adjoint
+    auto phys = [&](int32_t c) { return ADJ ? a.nc - 1 - c : c; };
 
     const uint32_t lid = xcd_remap(blockIdx.x, nblk);
     const int32_t ps = lid % PSPLIT;
@@ -229,7 +267,7 @@ __global__ __launch_bounds__(256, 2) void state_fwd_kernel(FwdArgs a, uint32_t n
     //           bytes a lane each, from b_fragments_kernel);
     //   gv, dtv, glv  G and dt of token tid and the last G of the chunk after
     //           the one being multiplied.
-    uint2 xr[2][8];
+    XP xr[2][8];
     bf16x8 br[R][TW];
     float gv = 0.f, dtv = 0.f, glv = 0.f;
     auto nvalid_of = [&](int32_t c) {
@@ -246,27 +284,32 @@ __global__ __launch_bounds__(256, 2) void state_fwd_kernel(FwdArgs a, uint32_t n
     // the end costs no traffic and needs no branch).
     auto load_x = [&](int32_t c, int hf) {
         const bool real = c < a.nc;
-        if (!real) c = a.nc - 1;
+        c = real ? phys(c) : a.nc - 1;
         const int32_t nv = real ? nvalid_of(c) : 0;
-        int32_t rs = XR * 2;
+        int32_t rs = XR * ES;
         asm volatile("" : "+s"(rs));
-        const auto rx = make_rsrc(a.x + ((b * a.T + (int64_t)c * L) * a.H + h) * P + s0,
+        const auto rx = make_rsrc(static_cast<const char *>(a.x) +
+                                      (((b * a.T + (int64_t)c * L) * a.H + h) * P + s0) * ES,
                                   (uint32_t)(nv * rs));
-        const uint32_t lo = (uint32_t)(8 * q * rs + 8 * m);
+        const uint32_t lo = (uint32_t)(8 * q * rs + 4 * ES * m);
         const int js = HS * hf + W;
 #pragma unroll
-        for (int r = 0; r < 8; ++r)
-            xr[hf][r] = load_bf<SPB, kStream>(rx, lo + (uint32_t)((32 * js + r) * rs));
+        for (int r = 0; r < 8; ++r) {
+            if constexpr (ADJ)
+                xr[hf][r] = load_f32p<SPB, kStream>(rx, lo + (uint32_t)((32 * js + r) * rs));
+            else
+                xr[hf][r] = load_bf<SPB, kStream>(rx, lo + (uint32_t)((32 * js + r) * rs));
+        }
     };
     auto load_g = [&](int32_t c) {   // plain loads: the index is clamped
-        const int64_t o = (bhi * a.nc + min(c, a.nc - 1)) * L;
+        const int64_t o = (bhi * a.nc + phys(min(c, a.nc - 1))) * L;
         gv = a.Gws[o + min(tid, L - 1)];
         dtv = a.DTws[o + min(tid, L - 1)];
         glv = a.Gws[o + L - 1];
     };
     auto load_b = [&](int32_t c, int js) {
         const bool real = c < a.nc;
-        if (!real) c = a.nc - 1;
+        c = real ? phys(c) : a.nc - 1;
         const auto rb = make_rsrc(a.BF + (((b * a.nc + c) * a.G + g) * NS) * (NT * 64),
                                   real ? (uint32_t)(NS * NT * 64 * 16) : 0u);
 #pragma unroll
@@ -276,24 +319,25 @@ __global__ __launch_bounds__(256, 2) void state_fwd_kernel(FwdArgs a, uint32_t n
             br[js % R][j] = __builtin_bit_cast(bf16x8, v);
         }
     };
-    // x*w fragments (head + remainder) of row set s of this wavefront's slab
-    // of half hf, with weights w (8 tokens), into AF[hf]
+    // x*w fragments of row set s of this wavefront's slab of half hf, with
+    // weights w (8 tokens), into AF[hf]: a bf16 head plus a bf16 remainder
+    // (the adjoint's dy*w: three bf16 terms)
     auto build_set = [&](int hf, int s, const float *w) {
-        uint4 vh, vl;
-        uint32_t *wh = reinterpret_cast<uint32_t *>(&vh);
-        uint32_t *wl = reinterpret_cast<uint32_t *>(&vl);
+        uint4 v[NTERM];
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
-            const uint32_t a0 = word_of(xr[hf][2 * rr], s);
-            const uint32_t a1 = word_of(xr[hf][2 * rr + 1], s);
-            const float e0 = ((s & 1) ? bf16_hi(a0) : bf16_lo(a0)) * w[2 * rr];
-            const float e1 = ((s & 1) ? bf16_hi(a1) : bf16_lo(a1)) * w[2 * rr + 1];
-            const uint32_t hw = pack_bf16x2(e0, e1);
-            wh[rr] = hw;
-            wl[rr] = pack_bf16x2(e0 - bf16_lo(hw), e1 - bf16_hi(hw));
+            float e0 = elem_of(xr[hf][2 * rr], s, ADJ) * w[2 * rr];
+            float e1 = elem_of(xr[hf][2 * rr + 1], s, ADJ) * w[2 * rr + 1];
+#pragma unroll
+            for (int tm = 0; tm < NTERM; ++tm) {
+                const uint32_t hw = pack_bf16x2(e0, e1);
+                reinterpret_cast<uint32_t *>(&v[tm])[rr] = hw;
+                e0 -= bf16_lo(hw);
+                e1 -= bf16_hi(hw);
+            }
         }
-        sm.AF[hf][W][0][s][lane] = vh;
-        sm.AF[hf][W][1][s][lane] = vl;
+#pragma unroll
+        for (int tm = 0; tm < NTERM; ++tm) sm.AF[hf][W][tm][s][lane] = v[tm];
     };
     auto read_w = [&](int hf, int wb, float *w) {
         const int jw = 32 * (HS * hf + W) + 8 * q;
@@ -317,9 +361,9 @@ __global__ __launch_bounds__(256, 2) void state_fwd_kernel(FwdArgs a, uint32_t n
     auto mfma_half = [&](int hf, int32_t c, int32_t cn, int bh, int wb) {
         float w[8];
         if (bh >= 0 && builds) read_w(bh, wb, w);
-        bf16x8 av[2][SW];
+        bf16x8 av[NTERM][SW];
 #pragma unroll
-        for (int hl = 0; hl < 2; ++hl)
+        for (int hl = 0; hl < NTERM; ++hl)
 #pragma unroll
             for (int i = 0; i < SW; ++i) av[hl][i] = as_bf16x8(sm.AF[hf][0][hl][sb + i][lane]);
 #pragma unroll
@@ -330,10 +374,10 @@ __global__ __launch_bounds__(256, 2) void state_fwd_kernel(FwdArgs a, uint32_t n
             for (int j = 0; j < TW; ++j) bfr[j] = br[js % R][j];
             if (js + R < NS) load_b(c, js + R);
             else load_b(cn, js + R - NS);
-            bf16x8 an[2][SW];
+            bf16x8 an[NTERM][SW];
             if (k + 1 < HS) {
 #pragma unroll
-                for (int hl = 0; hl < 2; ++hl)
+                for (int hl = 0; hl < NTERM; ++hl)
 #pragma unroll
                     for (int i = 0; i < SW; ++i)
                         an[hl][i] = as_bf16x8(sm.AF[hf][k + 1][hl][sb + i][lane]);
@@ -346,7 +390,7 @@ __global__ __launch_bounds__(256, 2) void state_fwd_kernel(FwdArgs a, uint32_t n
             // all head products, then all remainder products: no MFMA waits
             // on the one just issued
 #pragma unroll
-            for (int hl = 0; hl < 2; ++hl)
+            for (int hl = 0; hl < NTERM; ++hl)
 #pragma unroll
                 for (int i = 0; i < SW; ++i)
 #pragma unroll
@@ -354,16 +398,16 @@ __global__ __launch_bounds__(256, 2) void state_fwd_kernel(FwdArgs a, uint32_t n
                         acc[i][j] = mfma16x16x32(av[hl][i], bfr[j], acc[i][j]);
             if (k + 1 < HS) {
 #pragma unroll
-                for (int hl = 0; hl < 2; ++hl)
+                for (int hl = 0; hl < NTERM; ++hl)
 #pragma unroll
                     for (int i = 0; i < SW; ++i) av[hl][i] = an[hl][i];
             }
             // schedule: the next slab's LDS reads and the B loads first, then
             // each MFMA followed by three VALU instructions of the fragment build
-            __builtin_amdgcn_sched_group_barrier(0x100, 2 * SW, 0);   // DS read
+            __builtin_amdgcn_sched_group_barrier(0x100, NTERM * SW, 0);   // DS read
             __builtin_amdgcn_sched_group_barrier(0x020, TW, 0);       // VMEM read
 #pragma unroll
-            for (int u = 0; u < 2 * SW * TW; ++u) {
+            for (int u = 0; u < NTERM * SW * TW; ++u) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);    // MFMA
                 __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);    // VALU
             }
@@ -371,7 +415,7 @@ __global__ __launch_bounds__(256, 2) void state_fwd_kernel(FwdArgs a, uint32_t n
         }
     };
     auto store_hprev = [&](int32_t c) {
-        const int64_t o = (bhi * a.nc + c) * (int64_t)(P * N) + ncol;
+        const int64_t o = (bhi * a.nc + phys(c)) * (int64_t)(P * N) + ncol;
 #pragma unroll
         for (int i = 0; i < SW; ++i)
 #pragma unroll
@@ -397,7 +441,7 @@ __global__ __launch_bounds__(256, 2) void state_fwd_kernel(FwdArgs a, uint32_t n
 #pragma unroll
     for (int js = 0; js < R; ++js) load_b(0, js);
     float glc = glv;                 // last G of the chunk being multiplied
-    if (tid < L) sm.w[0][tid] = dtv * fast_exp2(glc - gv);
+    if (tid < L) sm.w[0][tid] = ADJ ? fast_exp2(gv) : dtv * fast_exp2(glc - gv);
     load_g(c1);
     __syncthreads();
     if (builds) {
@@ -421,7 +465,7 @@ __global__ __launch_bounds__(256, 2) void state_fwd_kernel(FwdArgs a, uint32_t n
 #pragma unroll
             for (int j = 0; j < TW; ++j) acc[i][j] *= dec;
         const float gln = glv;       // weights of chunk c + 1, then its G and dt in flight
-        if (tid < L) sm.w[(c + 1) & 1][tid] = dtv * fast_exp2(gln - gv);
+        if (tid < L) sm.w[(c + 1) & 1][tid] = ADJ ? fast_exp2(gv) : dtv * fast_exp2(gln - gv);
         load_g(cnn);
         mfma_half(0, c, cn, 1, c & 1);   // and build the second half of chunk c
         if (builds) load_x(cn, 1);
@@ -445,31 +489,34 @@ __global__ __launch_bounds__(256, 2) void state_fwd_kernel(FwdArgs a, uint32_t n
 }
 
 template <int L, int N, int SPB>
-hipError_t launch_fwd(const Shape &s, const FwdArgs &a, bool hp32, hipStream_t st) {
+hipError_t launch_fwd(const Shape &s, const FwdArgs &a, int mode, hipStream_t st) {
     const uint64_t nblk = (uint64_t)s.Bt * s.H * (4 / SPB);
-    if (hp32)
-        hipLaunchKernelGGL((state_fwd_kernel<L, N, SPB, true>), dim3((uint32_t)nblk), dim3(256), 0,
-                           st, a, (uint32_t)nblk);
-    else
-        hipLaunchKernelGGL((state_fwd_kernel<L, N, SPB, false>), dim3((uint32_t)nblk), dim3(256),
+    if (mode == kModeAdjoint)
+        hipLaunchKernelGGL((state_fwd_kernel<L, N, SPB, kModeAdjoint>), dim3((uint32_t)nblk),
+                           dim3(256), 0, st, a, (uint32_t)nblk);
+    else if (mode == kModeF32)
+        hipLaunchKernelGGL((state_fwd_kernel<L, N, SPB, kModeF32>), dim3((uint32_t)nblk), dim3(256),
                            0, st, a, (uint32_t)nblk);
+    else
+        hipLaunchKernelGGL((state_fwd_kernel<L, N, SPB, kModeBf16>), dim3((uint32_t)nblk),
+                           dim3(256), 0, st, a, (uint32_t)nblk);
     return hipGetLastError();
 }
 
 template <int L, int N>
-hipError_t launch_fwd_n(const Shape &s, const FwdArgs &a, int spb, bool hp32, hipStream_t st) {
+hipError_t launch_fwd_n(const Shape &s, const FwdArgs &a, int spb, int mode, hipStream_t st) {
     switch (spb) {
-    case 4: return launch_fwd<L, N, 4>(s, a, hp32, st);
-    case 2: return launch_fwd<L, N, 2>(s, a, hp32, st);
-    case 1: return launch_fwd<L, N, 1>(s, a, hp32, st);
+    case 4: return launch_fwd<L, N, 4>(s, a, mode, st);
+    case 2: return launch_fwd<L, N, 2>(s, a, mode, st);
+    case 1: return launch_fwd<L, N, 1>(s, a, mode, st);
     default: return hipErrorInvalidValue;
     }
 }
 
 template <int L>
-hipError_t launch_fwd_l(const Shape &s, const FwdArgs &a, int spb, bool hp32, hipStream_t st) {
-    if (s.N == 64) return launch_fwd_n<L, 64>(s, a, spb, hp32, st);
-    if (s.N == 128) return launch_fwd_n<L, 128>(s, a, spb, hp32, st);
+hipError_t launch_fwd_l(const Shape &s, const FwdArgs &a, int spb, int mode, hipStream_t st) {
+    if (s.N == 64) return launch_fwd_n<L, 64>(s, a, spb, mode, st);
+    if (s.N == 128) return launch_fwd_n<L, 128>(s, a, spb, mode, st);
     return hipErrorInvalidValue;
 }
 
@@ -505,17 +552,19 @@ size_t state_fwd_bfrag_bytes(const Shape &s) {
     return (size_t)s.Bt * s.nc * s.G * s.L * s.N * 2;
 }
 
-hipError_t launch_state_fwd(const Shape &s, const void *x, const void *B, const float *Gws,
-                            const float *DTws, const float *init, void *hprev, float *fin,
-                            void *bfrag, int spb, bool hprev_f32, hipStream_t st) {
-    if (!state_fwd_supported(s)) return hipErrorInvalidValue;
+// the one-pass scan of either direction: x (or dy) and V = B (or C) in, the
+// state before each chunk step (h_prev, or the adjoint ghat) and the last
+// state (final, or dinit) out
+static hipError_t launch_pass(const Shape &s, const void *x, const void *V, const float *Gws,
+                              const float *DTws, const float *init, void *out, float *fin,
+                              void *vfrag, int spb, int mode, hipStream_t st) {
     if (s.Bt == 0 || s.H == 0) return hipSuccess;
     if (s.nc == 0 && !fin) return hipSuccess;
     if (s.nc > 0) {
         const uint64_t nfb = (uint64_t)s.Bt * s.nc * s.G * (s.L / 32);
         auto lb = [&](auto kern) {
-            hipLaunchKernelGGL(kern, dim3((uint32_t)nfb), dim3(256), 0, st, (const uint16_t *)B,
-                               (uint4 *)bfrag, s.T, (int32_t)s.G, (int32_t)s.nc);
+            hipLaunchKernelGGL(kern, dim3((uint32_t)nfb), dim3(256), 0, st, (const uint16_t *)V,
+                               (uint4 *)vfrag, s.T, (int32_t)s.G, (int32_t)s.nc);
         };
         if (s.N == 64) {
             if (s.L == 64) lb(b_fragments_kernel<64, 64>);
@@ -530,25 +579,53 @@ hipError_t launch_state_fwd(const Shape &s, const void *x, const void *B, const 
         if (e != hipSuccess) return e;
     }
     FwdArgs a;
-    a.x = (const uint16_t *)x;
-    a.BF = (const uint4 *)bfrag;
+    a.x = x;
+    a.BF = (const uint4 *)vfrag;
     a.Gws = Gws;
     a.DTws = DTws;
     a.init = init;
-    a.hprev = hprev;
+    a.hprev = out;
     a.fin = fin;
     a.T = s.T;
     a.H = (int32_t)s.H;
     a.G = (int32_t)s.G;
     a.nc = (int32_t)s.nc;
     a.hpg = (int32_t)(s.H / s.G);
-    if (spb <= 0) spb = state_fwd_rows_per_block(s);
     switch (s.L) {
-    case 64: return launch_fwd_l<64>(s, a, spb, hprev_f32, st);
-    case 128: return launch_fwd_l<128>(s, a, spb, hprev_f32, st);
-    case 256: return launch_fwd_l<256>(s, a, spb, hprev_f32, st);
+    case 64: return launch_fwd_l<64>(s, a, spb, mode, st);
+    case 128: return launch_fwd_l<128>(s, a, spb, mode, st);
+    case 256: return launch_fwd_l<256>(s, a, spb, mode, st);
     default: return hipErrorInvalidValue;
     }
+}
+
+hipError_t launch_state_fwd(const Shape &s, const void *x, const void *B, const float *Gws,
+                            const float *DTws, const float *init, void *hprev, float *fin,
+                            void *bfrag, int spb, bool hprev_f32, hipStream_t st) {
+    if (!state_fwd_supported(s)) return hipErrorInvalidValue;
+    if (spb <= 0) spb = state_fwd_rows_per_block(s);
+    return launch_pass(s, x, B, Gws, DTws, init, hprev, fin, bfrag, spb,
+                       hprev_f32 ? kModeF32 : kModeBf16, st);
+}
+
+bool state_adj_supported(const Shape &s) {
+    // as the forward, with fp32 dy rows
+    const int64_t lim = (int64_t(1) << 31) - 1;
+    return state_fwd_supported(s) && s.L * s.H * s.P * 4 <= lim;
+}
+
+int state_adj_rows_per_block(const Shape &s) {
+    // three bf16 terms of dy*w take 1.5x the forward's LDS per row set: two
+    // row sets keep three workgroups resident per CU
+    return s.Bt * s.H >= 48 ? 2 : 1;
+}
+
+hipError_t launch_state_adj(const Shape &s, const float *dy, const void *C, const float *Gws,
+                            const float *dfinal, float *ghat, float *dinit, void *cfrag, int spb,
+                            hipStream_t st) {
+    if (!state_adj_supported(s)) return hipErrorInvalidValue;
+    if (spb <= 0) spb = state_adj_rows_per_block(s);
+    return launch_pass(s, dy, C, Gws, Gws, dfinal, ghat, dinit, cfrag, spb, kModeAdjoint, st);
 }
 
 }  // namespace ssd

@@ -53,6 +53,22 @@ def test_backward_against_oracle(io, L, N):
     compare(g, ref, io)
 
 
+@pytest.mark.parametrize("fwd_rows,adj_rows", [("0", ""), ("4", "1"), ("2", "2"), ("1", "4")])
+@pytest.mark.parametrize("L", [64, 256])
+def test_state_stage_paths(monkeypatch, fwd_rows, adj_rows, L):
+    """Every form of the recomputed forward states and of the state adjoint:
+    chunk_state + state_passing with per-chunk adjoint sums and a separate
+    reverse scan (rows 0), and the one-pass scans in both directions at each
+    row split; the ragged last chunk and dfinal enter each."""
+    monkeypatch.setenv("SSD_STATE_FWD_ROWS", fwd_rows)
+    monkeypatch.setenv("SSD_STATE_ADJ_ROWS", adj_rows)
+    log("bwd state paths", fwd_rows, adj_rows, "L", L)
+    inp = gen.make_small(2, 3 * L + 17, 8, 64, 128, 2, gen.BF16, init_state=True, seed=L + 3)
+    dy, dfin = grads_inputs(inp, 5)
+    g, ref = run_both(inp, gen.BF16, L, dy, dfin)
+    compare(g, ref, gen.BF16)
+
+
 @pytest.mark.parametrize("G", [1, 2, 8])
 def test_group_counts(G):
     """dB and dC sum over the heads of a group: 8, 4 and 1 heads per group."""
@@ -87,10 +103,11 @@ def test_reruns_are_bitwise_identical():
         assert torch.equal(a[k], b[k]), k
 
 
-def test_no_tokens():
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_no_tokens(dtype):
     Bt, H, P, N = 2, 4, 64, 64
-    x = torch.empty((Bt, 0, H, P), device="cuda")
-    Bm = torch.empty((Bt, 0, 1, N), device="cuda")
+    x = torch.empty((Bt, 0, H, P), device="cuda", dtype=dtype)
+    Bm = torch.empty((Bt, 0, 1, N), device="cuda", dtype=dtype)
     dt = torch.empty((Bt, 0, H), device="cuda")
     A = -torch.ones(H, device="cuda")
     D = torch.ones(H, device="cuda")
