@@ -237,6 +237,43 @@ __global__ __launch_bounds__(256) void bwd_passing_kernel(float *__restrict__ dS
     if (tid == 0) bnd[bh] = red[0];
 }
 
+// ---- bwd_bnd: bnd[bh] = <dfinal, final> of one (b, h) in fp64, coalesced
+// 16-byte loads (the one-pass adjoint scan leaves only this of bwd_passing)
+template <int N>
+__global__ __launch_bounds__(256) void bwd_bnd_kernel(const float *__restrict__ dfin,
+                                                      const float *__restrict__ fin,
+                                                      double *__restrict__ bnd) {
+    constexpr int E4 = P * N / 4 / 256;            // float4 per thread
+    __shared__ double red[256];
+    const int64_t bh = blockIdx.x;
+    const int tid = threadIdx.x;
+    const float4 *d4 = reinterpret_cast<const float4 *>(dfin + bh * (int64_t)(P * N));
+    const float4 *f4 = reinterpret_cast<const float4 *>(fin + bh * (int64_t)(P * N));
+    float4 dv[E4], fv[E4];
+#pragma unroll
+    for (int e = 0; e < E4; ++e) {
+        dv[e] = d4[e * 256 + tid];
+        fv[e] = f4[e * 256 + tid];
+    }
+    double dot = 0.0;
+#pragma unroll
+    for (int e = 0; e < E4; ++e)
+        dot += (double)dv[e].x * fv[e].x + (double)dv[e].y * fv[e].y + (double)dv[e].z * fv[e].z +
+               (double)dv[e].w * fv[e].w;
+    red[tid] = dot;
+    __syncthreads();
+    for (int s = 128; s > 0; s >>= 1) {
+        if (tid < s) red[tid] += red[tid + s];
+        __syncthreads();
+    }
+    if (tid == 0) bnd[bh] = red[0];
+}
+
+__global__ __launch_bounds__(256) void fill_f64_kernel(double *__restrict__ p, int64_t n) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i < n) p[i] = 0.0;
+}
+
 // ---- bwd_cb: CB(k, j) = C_k . B_j for the 64x64 blocks on or below the diagonal
 template <int L, int N, typename Tio>
 __global__ __launch_bounds__(256) void bwd_cb_kernel(const Tio *__restrict__ B,
@@ -1353,10 +1390,16 @@ hipError_t launch_bwd_t(const Shape &s, const BwdArgs &a, hipStream_t st) {
                                st, a.dy, C, a.G, a.S, T, H, G, nc);
     }
     // with ghat already in S only the boundary dot <dfinal, final> remains
-    // (no chunk steps, dinit untouched)
-    hipLaunchKernelGGL((bwd_passing_kernel<L, N>), dim3((uint32_t)(s.Bt * s.H)), dim3(256), 0, st,
-                       a.S, a.G, a.dfinal, a.fin, a.ghat_ready ? nullptr : a.dinit,
-                       a.part + 2 * s.Bt * s.H, a.ghat_ready ? 0 : nc);
+    double *bnd = a.part + 2 * s.Bt * s.H;
+    if (!a.ghat_ready)
+        hipLaunchKernelGGL((bwd_passing_kernel<L, N>), dim3((uint32_t)(s.Bt * s.H)), dim3(256), 0,
+                           st, a.S, a.G, a.dfinal, a.fin, a.dinit, bnd, nc);
+    else if (a.dfinal)
+        hipLaunchKernelGGL((bwd_bnd_kernel<N>), dim3((uint32_t)(s.Bt * s.H)), dim3(256), 0, st,
+                           a.dfinal, a.fin, bnd);
+    else
+        hipLaunchKernelGGL((fill_f64_kernel), dim3((uint32_t)((s.Bt * s.H + 255) / 256)), dim3(256),
+                           0, st, bnd, (int64_t)(s.Bt * s.H));
     if (units > 0) {
         constexpr int NTRI = (L / 64) * (L / 64 + 1) / 2;
         const uint64_t ncb = (uint64_t)s.Bt * s.nc * s.G;

@@ -79,12 +79,14 @@ def test_group_counts(G):
     compare(g, ref, gen.BF16)
 
 
-def test_without_init_and_dfinal():
-    inp = gen.make_small(1, 200, 4, 64, 64, 1, gen.F32, init_state=False, seed=6)
+@pytest.mark.parametrize("io", [gen.F32, gen.BF16])
+def test_without_init_and_dfinal(io):
+    log("bwd no init, no dfinal", io)
+    inp = gen.make_small(1, 200, 4, 64, 64, 1, io, init_state=False, seed=6)
     dy, _ = grads_inputs(inp, 3, dfinal=False)
-    g, ref = run_both(inp, gen.F32, 64, dy, None)
-    compare(g, ref, gen.F32)
-    g2, _ = run_both(inp, gen.F32, 64, dy, None, want_dinit=False)
+    g, ref = run_both(inp, io, 64, dy, None)
+    compare(g, ref, io)
+    g2, _ = run_both(inp, io, 64, dy, None, want_dinit=False)
     assert g2["dinit"] is None
     for k in NAMES[:-1]:
         assert torch.equal(g[k], g2[k]), k
