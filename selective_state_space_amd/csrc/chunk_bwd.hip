@@ -608,19 +608,18 @@ __global__ __launch_bounds__(256) void bwd_dbdc_kernel(
 // split operands take three MFMAs (hi.hi + hi.lo + lo.hi), of one split
 // operand two, which leaves about 2^-16 of relative error instead of 2^-9.
 
-template <int L, int N, int ORIENT, int WPB>
-__global__ __launch_bounds__(64 * WPB) void bwd_dbdc_mfma_kernel(
-    const uint16_t *__restrict__ x, const uint16_t *__restrict__ B,
-    const uint16_t *__restrict__ C, const float *__restrict__ dy, const float *__restrict__ Gws,
-    const float *__restrict__ DTws, const float *__restrict__ gh, const float *__restrict__ hprev,
-    float *__restrict__ out, int64_t T, int32_t H, int32_t G, int32_t nc) {
+template <int L, int N, int WPB>
+__global__ __launch_bounds__(64 * WPB) void bwd_dc_mfma_kernel(
+    const uint16_t *__restrict__ x, const uint16_t *__restrict__ B, const float *__restrict__ dy,
+    const float *__restrict__ Gws, const float *__restrict__ DTws,
+    const float *__restrict__ hprev, float *__restrict__ out, float *__restrict__ MT, int64_t T,
+    int32_t H, int32_t G, int32_t nc) {
     constexpr int NT = L / 16, NN = N / 16;
     constexpr int RB = 16 * WPB;                      // rows per workgroup (one strip per wavefront)
     constexpr int NTH = 64 * WPB;
-    constexpr int NCS = ORIENT == 1 ? 2 : 1;          // dy rows need a remainder copy
     constexpr int NIB = N > RB ? N : RB;              // Ib rows: n, or the M remainder's rows
-    __shared__ __align__(16) uint16_t Cs[NCS][L * SP];  // column-side rows [row][p]; final: M
-    __shared__ __align__(16) uint16_t Ib[2][NIB * SP];  // inter operand [n][p]; final: V^T
+    __shared__ __align__(16) uint16_t Cs[L * SP];     // x rows [row][p]; final: M
+    __shared__ __align__(16) uint16_t Ib[2][NIB * SP];  // h_prev^T [n][p]; final: B^T
     __shared__ float Gs[L], DTs[L];
     const int64_t blk = xcd_remap(blockIdx.x, gridDim.x);   // row blocks of a group on one XCD
     const int rb = (int)(blk % (L / RB));
@@ -634,8 +633,7 @@ __global__ __launch_bounds__(64 * WPB) void bwd_dbdc_mfma_kernel(
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
     const int m = lane & 15, q = lane >> 4;
     const int64_t tc = (int64_t)c * L;
-    // column range: ORIENT 0 -> [0, r0 + RB), ORIENT 1 -> [r0, L)
-    const int c_lo = ORIENT == 0 ? 0 : r0, c_hi = ORIENT == 0 ? r0 + RB : L;
+    const int c_hi = r0 + RB;                         // columns [0, c_hi): on or below the diagonal
     const int arow = r0 + 16 * w + m;                 // this lane's A-operand row
     const int64_t ta = tc + arow;
     f32x4 Macc[NT];
@@ -645,85 +643,93 @@ __global__ __launch_bounds__(64 * WPB) void bwd_dbdc_mfma_kernel(
 #pragma unroll
     for (int i = 0; i < NN; ++i) dacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+    // staging items per thread: x rows (8 p each), h_prev (two p rows x 4 n each)
+    static_assert(NTH >= L, "one G and DT value per thread");
+    constexpr int NCI = (L * (P / 8) + NTH - 1) / NTH;
+    constexpr int NII = (P * N / 8 + NTH - 1) / NTH;
+    const int ncols = c_hi * (P / 8);
     for (int hh = 0; hh < hpg; ++hh) {
         const int32_t h = g * hpg + hh;
         const int64_t unit = ((b * H) + h) * nc + c;
         __syncthreads();
-        // stage the column-side rows of the range (x exact, or dy as hi + lo)
-        for (int e = tid; e < (c_hi - c_lo) * (P / 8); e += NTH) {
-            const int r = c_lo + e / (P / 8), p8 = 8 * (e % (P / 8));
-            const int64_t t = tc + r;
-            const int64_t o = ((b * T + (t < T ? t : 0)) * H + h) * P + p8;
-            if constexpr (ORIENT == 0) {
-                const uint4 v = t < T ? *reinterpret_cast<const uint4 *>(x + o)
-                                      : make_uint4(0u, 0u, 0u, 0u);
-                *reinterpret_cast<uint4 *>(&Cs[0][r * SP + p8]) = v;
-            } else {
-                float f[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-                if (t < T) {
-                    const float4 u0 = *reinterpret_cast<const float4 *>(dy + o);
-                    const float4 u1 = *reinterpret_cast<const float4 *>(dy + o + 4);
-                    f[0] = u0.x; f[1] = u0.y; f[2] = u0.z; f[3] = u0.w;
-                    f[4] = u1.x; f[5] = u1.y; f[6] = u1.z; f[7] = u1.w;
-                }
-                uint4 hi, lo;
-                split8(f, hi, lo);
-                *reinterpret_cast<uint4 *>(&Cs[0][r * SP + p8]) = hi;
-                *reinterpret_cast<uint4 *>(&Cs[NCS - 1][r * SP + p8]) = lo;
-            }
-        }
-        // the inter operand, transposed to [n][p], as hi + lo: a lane takes rows
-        // p, p+1 and writes 32-bit pairs, consecutive lanes consecutive pairs
-        const float *src = (ORIENT == 0 ? hprev : gh) + unit * (int64_t)(P * N);
-        for (int e = tid; e < P * N / 8; e += NTH) {
-            const int p = 2 * (e % (P / 2)), n4 = 4 * (e / (P / 2));
-            const float4 v0 = *reinterpret_cast<const float4 *>(src + p * N + n4);
-            const float4 v1 = *reinterpret_cast<const float4 *>(src + (p + 1) * N + n4);
-            const float a0[4] = {v0.x, v0.y, v0.z, v0.w}, a1[4] = {v1.x, v1.y, v1.z, v1.w};
+        // every global load of this head is issued before any is used (one
+        // memory latency per head): the x rows, h_prev, G and DT, and the
+        // strip's own dy rows
+        uint4 cx[NCI];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                uint32_t hi, lo;
-                split2(a0[i], a1[i], hi, lo);
-                *reinterpret_cast<uint32_t *>(&Ib[0][(n4 + i) * SP + p]) = hi;
-                *reinterpret_cast<uint32_t *>(&Ib[1][(n4 + i) * SP + p]) = lo;
+        for (int j = 0; j < NCI; ++j) {
+            const int e = tid + j * NTH;
+            const int r = e / (P / 8), p8 = 8 * (e % (P / 8));
+            const int64_t t = tc + r;
+            const bool ok = e < ncols && t < T;
+            const int64_t o = ((b * T + (ok ? t : 0)) * H + h) * P + p8;
+            cx[j] = ok ? *reinterpret_cast<const uint4 *>(x + o) : make_uint4(0u, 0u, 0u, 0u);
+        }
+        const float *src = hprev + unit * (int64_t)(P * N);
+        float4 iv[NII][2];
+#pragma unroll
+        for (int j = 0; j < NII; ++j) {
+            const int e = tid + j * NTH;
+            const int p = 2 * (e % (P / 2)), n4 = 4 * (e / (P / 2));
+            const bool ok = e < P * N / 8;
+            iv[j][0] = ok ? *reinterpret_cast<const float4 *>(src + p * N + n4) : make_float4(0.f, 0.f, 0.f, 0.f);
+            iv[j][1] = ok ? *reinterpret_cast<const float4 *>(src + (p + 1) * N + n4)
+                          : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+        float gl = 0.f, dl = 0.f;
+        if (tid < L) {
+            gl = Gws[unit * L + tid];
+            dl = DTws[unit * L + tid];
+        }
+        float4 ar[2][2];                              // the strip's own dy rows
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+            const int64_t o = ((b * T + (ta < T ? ta : 0)) * H + h) * P + 32 * st + 8 * q;
+            ar[st][0] = ta < T ? *reinterpret_cast<const float4 *>(dy + o) : make_float4(0.f, 0.f, 0.f, 0.f);
+            ar[st][1] = ta < T ? *reinterpret_cast<const float4 *>(dy + o + 4) : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+#pragma unroll
+        for (int j = 0; j < NCI; ++j) {
+            const int e = tid + j * NTH;
+            if (e < ncols) *reinterpret_cast<uint4 *>(&Cs[(e / (P / 8)) * SP + 8 * (e % (P / 8))]) = cx[j];
+        }
+        // h_prev transposed to [n][p], as hi + lo: a lane takes rows p, p+1 and
+        // writes 32-bit pairs, consecutive lanes consecutive pairs
+#pragma unroll
+        for (int j = 0; j < NII; ++j) {
+            const int e = tid + j * NTH;
+            if (e < P * N / 8) {
+                const int p = 2 * (e % (P / 2)), n4 = 4 * (e / (P / 2));
+                const float a0[4] = {iv[j][0].x, iv[j][0].y, iv[j][0].z, iv[j][0].w};
+                const float a1[4] = {iv[j][1].x, iv[j][1].y, iv[j][1].z, iv[j][1].w};
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    uint32_t hi, lo;
+                    split2(a0[i], a1[i], hi, lo);
+                    *reinterpret_cast<uint32_t *>(&Ib[0][(n4 + i) * SP + p]) = hi;
+                    *reinterpret_cast<uint32_t *>(&Ib[1][(n4 + i) * SP + p]) = lo;
+                }
             }
         }
-        for (int e = tid; e < L; e += NTH) {
-            Gs[e] = Gws[unit * L + e];
-            DTs[e] = DTws[unit * L + e];
+        if (tid < L) {
+            Gs[tid] = gl;
+            DTs[tid] = dl;
         }
         __syncthreads();
-        // A operands: the strip's own rows (plain, and scaled for the inter term)
-        const float ga = Gs[arow], glast = Gs[L - 1];
-        const float sc = ORIENT == 0 ? fast_exp2(ga) : DTs[arow] * fast_exp2(glast - ga);
-        // row factors of the off-diagonal decay, against the strip's edge row:
-        // the first row (ORIENT 0, columns before it) or the last (ORIENT 1)
-        const float gedge = Gs[r0 + 16 * w + (ORIENT == 0 ? 0 : 15)];
+        // A operands: the strip's dy rows (plain, and times exp2(G) for the inter term)
+        const float sc = fast_exp2(Gs[arow]);
+        // row factors of the off-diagonal decay, against the strip's first row
+        const float gedge = Gs[r0 + 16 * w];
         float rowf[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int row = r0 + 16 * w + 4 * q + e;
-            rowf[e] = ORIENT == 0 ? fast_exp2(Gs[row] - gedge) : fast_exp2(gedge - Gs[row]) * DTs[row];
-        }
+        for (int e = 0; e < 4; ++e) rowf[e] = fast_exp2(Gs[r0 + 16 * w + 4 * q + e] - gedge);
         bf16x8 aS[2], aSl[2], aI[2], aIl[2];
 #pragma unroll
         for (int st = 0; st < 2; ++st) {
-            float f[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-            if (ta < T) {
-                const int64_t o = ((b * T + ta) * H + h) * P + 32 * st + 8 * q;
-                if constexpr (ORIENT == 0) {
-                    const float4 u0 = *reinterpret_cast<const float4 *>(dy + o);
-                    const float4 u1 = *reinterpret_cast<const float4 *>(dy + o + 4);
-                    f[0] = u0.x; f[1] = u0.y; f[2] = u0.z; f[3] = u0.w;
-                    f[4] = u1.x; f[5] = u1.y; f[6] = u1.z; f[7] = u1.w;
-                } else {
-                    const uint4 u = *reinterpret_cast<const uint4 *>(x + o);
-                    f[0] = bf16_lo(u.x); f[1] = bf16_hi(u.x); f[2] = bf16_lo(u.y); f[3] = bf16_hi(u.y);
-                    f[4] = bf16_lo(u.z); f[5] = bf16_hi(u.z); f[6] = bf16_lo(u.w); f[7] = bf16_hi(u.w);
-                }
-            }
+            const float f[8] = {ar[st][0].x, ar[st][0].y, ar[st][0].z, ar[st][0].w,
+                                ar[st][1].x, ar[st][1].y, ar[st][1].z, ar[st][1].w};
             uint4 hi, lo;
-            split8(f, hi, lo);                        // lo = 0 for x (bf16 already)
+            split8(f, hi, lo);
             aS[st] = as_bf16x8(hi);
             aSl[st] = as_bf16x8(lo);
             float fs[8];
@@ -733,24 +739,17 @@ __global__ __launch_bounds__(64 * WPB) void bwd_dbdc_mfma_kernel(
             aI[st] = as_bf16x8(hi);
             aIl[st] = as_bf16x8(lo);
         }
-        // S tiles of the column range, decayed and masked into M
+        // S tiles on or below the diagonal, decayed and masked into M
 #pragma unroll
         for (int jt = 0; jt < NT; ++jt) {
-            if (16 * jt < c_lo || 16 * jt >= c_hi) continue;
-            // tiles wholly on the masked side of this strip's rows add nothing
-            if (ORIENT == 0 ? 16 * jt > r0 + 16 * w : 16 * jt < r0 + 16 * w) continue;
+            if (16 * jt > r0 + 16 * w) continue;      // wholly masked
             f32x4 s = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int st = 0; st < 2; ++st) {
                 const int off = (16 * jt + m) * SP + 32 * st + 8 * q;
-                const bf16x8 bh = as_bf16x8(*reinterpret_cast<const uint4 *>(&Cs[0][off]));
+                const bf16x8 bh = as_bf16x8(*reinterpret_cast<const uint4 *>(&Cs[off]));
                 s = mfma16x16x32(aS[st], bh, s);
-                if constexpr (ORIENT == 0) {
-                    s = mfma16x16x32(aSl[st], bh, s);         // dy remainder . x
-                } else {
-                    const bf16x8 bl = as_bf16x8(*reinterpret_cast<const uint4 *>(&Cs[1][off]));
-                    s = mfma16x16x32(aS[st], bl, s);          // x . dy remainder
-                }
+                s = mfma16x16x32(aSl[st], bh, s);     // dy remainder . x
             }
             const int col = 16 * jt + m;
             const float gc = Gs[col], dc = DTs[col];
@@ -759,25 +758,18 @@ __global__ __launch_bounds__(64 * WPB) void bwd_dbdc_mfma_kernel(
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int row = r0 + 16 * w + 4 * q + e;
-                    const float gr = Gs[row];
-                    float v;
-                    if constexpr (ORIENT == 0)
-                        v = row >= col ? fast_exp2(gr - gc) * dc * s[e] : 0.f;
-                    else
-                        v = col >= row ? fast_exp2(gc - gr) * DTs[row] * s[e] : 0.f;
-                    Macc[jt][e] += v;
+                    Macc[jt][e] += row >= col ? fast_exp2(Gs[row] - gc) * dc * s[e] : 0.f;
                 }
-            } else if (ORIENT == 0 ? 16 * jt < r0 + 16 * w : 16 * jt > r0 + 16 * w) {
-                // off the diagonal on the causal side every pair counts, and the
-                // decay splits at the strip's edge row into a row factor and a
-                // column factor, both at most 1: one exp2 per tile instead of four
-                // (tiles on the other side are entirely masked)
-                const float cf = ORIENT == 0 ? fast_exp2(gedge - gc) * dc : fast_exp2(gc - gedge);
+            } else {
+                // below the diagonal every pair counts, and the decay splits at
+                // the strip's first row into a row factor and a column factor,
+                // both at most 1: one exp2 per tile instead of four
+                const float cf = fast_exp2(gedge - gc) * dc;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) Macc[jt][e] += rowf[e] * (cf * s[e]);
             }
         }
-        // inter term: (scaled strip rows) x (h_prev or ghat), K = P, three products
+        // inter term: (exp2(G) dy rows) x h_prev, K = P, three products
 #pragma unroll
         for (int nt = 0; nt < NN; ++nt)
 #pragma unroll
@@ -790,10 +782,19 @@ __global__ __launch_bounds__(64 * WPB) void bwd_dbdc_mfma_kernel(
                 dacc[nt] = mfma16x16x32(aIl[st], bh, dacc[nt]);
             }
     }
-    // final: out(row, n) += sum_col M(row, col) V_col[n], V = B (dC) or C (dB);
-    // M goes through LDS as hi (rows 0..63 of Cs[0]) + lo (rows 0..63 of Ib[1])
-    const uint16_t *V = ORIENT == 0 ? B : C;
-    for (int cc = c_lo / 64; cc < c_hi / 64; ++cc) {
+    // M of the strip's rows, all L columns (zero where masked), transposed
+    // into MT[col][row] for the dB pass: lane (m, q) holds rows 4q..4q+3 of
+    // column 16 jt + m
+    {
+        float *mt = MT + bcg * (int64_t)(L * L) + r0 + 16 * w + 4 * q;
+#pragma unroll
+        for (int jt = 0; jt < NT; ++jt)
+            *reinterpret_cast<float4 *>(mt + (int64_t)(16 * jt + m) * L) =
+                make_float4(Macc[jt][0], Macc[jt][1], Macc[jt][2], Macc[jt][3]);
+    }
+    // final: dC(row, n) += sum_col M(row, col) B_col[n];
+    // M goes through LDS as hi (rows 0..RB-1 of Cs) + lo (rows 0..RB-1 of Ib[1])
+    for (int cc = 0; cc < c_hi / 64; ++cc) {
         __syncthreads();
 #pragma unroll
         for (int jt = 0; jt < NT; ++jt) {
@@ -803,17 +804,17 @@ __global__ __launch_bounds__(64 * WPB) void bwd_dbdc_mfma_kernel(
                 uint16_t hi, lo;
                 split1(Macc[jt][e], hi, lo);
                 const int r = 16 * w + 4 * q + e, cl = 16 * (jt % 4) + m;
-                Cs[0][r * SP + cl] = hi;
+                Cs[r * SP + cl] = hi;
                 Ib[1][r * SP + cl] = lo;
             }
         }
-        // V rows of the chunk, transposed to [n][token]: a lane takes tokens r, r+1
+        // B rows of the chunk, transposed to [n][token]: a lane takes tokens r, r+1
         for (int e = tid; e < 64 * N / 16; e += NTH) {
             const int r = 2 * (e % 32), n8 = 8 * (e / 32);
             const int64_t t = tc + 64 * cc + r;
             uint4 v0 = make_uint4(0u, 0u, 0u, 0u), v1 = v0;
-            if (t < T) v0 = *reinterpret_cast<const uint4 *>(V + ((b * T + t) * G + g) * N + n8);
-            if (t + 1 < T) v1 = *reinterpret_cast<const uint4 *>(V + ((b * T + t + 1) * G + g) * N + n8);
+            if (t < T) v0 = *reinterpret_cast<const uint4 *>(B + ((b * T + t) * G + g) * N + n8);
+            if (t + 1 < T) v1 = *reinterpret_cast<const uint4 *>(B + ((b * T + t + 1) * G + g) * N + n8);
             const uint32_t w0[4] = {v0.x, v0.y, v0.z, v0.w}, w1[4] = {v1.x, v1.y, v1.z, v1.w};
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -826,9 +827,166 @@ __global__ __launch_bounds__(64 * WPB) void bwd_dbdc_mfma_kernel(
         bf16x8 aM[2], aMl[2];
 #pragma unroll
         for (int st = 0; st < 2; ++st) {
-            aM[st] = as_bf16x8(*reinterpret_cast<const uint4 *>(&Cs[0][(16 * w + m) * SP + 32 * st + 8 * q]));
+            aM[st] = as_bf16x8(*reinterpret_cast<const uint4 *>(&Cs[(16 * w + m) * SP + 32 * st + 8 * q]));
             aMl[st] = as_bf16x8(
                 *reinterpret_cast<const uint4 *>(&Ib[1][(16 * w + m) * SP + 32 * st + 8 * q]));
+        }
+#pragma unroll
+        for (int nt = 0; nt < NN; ++nt)
+#pragma unroll
+            for (int st = 0; st < 2; ++st) {
+                const bf16x8 bv = as_bf16x8(
+                    *reinterpret_cast<const uint4 *>(&Ib[0][(16 * nt + m) * SP + 32 * st + 8 * q]));
+                dacc[nt] = mfma16x16x32(aM[st], bv, dacc[nt]);
+                dacc[nt] = mfma16x16x32(aMl[st], bv, dacc[nt]);
+            }
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const int64_t t = tc + r0 + 16 * w + 4 * q + e;
+        if (t < T)
+#pragma unroll
+            for (int nt = 0; nt < NN; ++nt)
+                out[((b * T + t) * G + g) * N + 16 * nt + m] = dacc[nt][e];
+    }
+}
+
+// ---- bwd_db_mfma: dB rows j of one (b, chunk, group) from the M that
+// bwd_dc_mfma stored (transposed, fp32):
+//   dB(j, n) = sum_{k >= j} M(k, j) C_k[n] + sum_h dt_j exp2(G_last - G_j) x_j . ghat_h[:, n]
+// Per head only ghat (staged transposed as hi + lo) and the strip's x rows
+// (A operands from global memory) are read; M^T rows come from global memory
+// as hi + lo A operands for the final product with C (staged transposed).
+template <int L, int N, int WPB>
+__global__ __launch_bounds__(64 * WPB) void bwd_db_mfma_kernel(
+    const uint16_t *__restrict__ x, const uint16_t *__restrict__ C, const float *__restrict__ Gws,
+    const float *__restrict__ DTws, const float *__restrict__ gh, const float *__restrict__ MT,
+    float *__restrict__ out, int64_t T, int32_t H, int32_t G, int32_t nc) {
+    constexpr int NN = N / 16;
+    constexpr int RB = 16 * WPB;
+    constexpr int NTH = 64 * WPB;
+    __shared__ __align__(16) uint16_t Ib[2][N * SP];  // ghat^T [n][p] hi + lo; final: C^T
+    const int64_t blk = xcd_remap(blockIdx.x, gridDim.x);
+    const int rb = (int)(blk % (L / RB));
+    const int64_t bcg = blk / (L / RB);               // (b*nc + c)*G + g
+    const int32_t g = (int32_t)(bcg % G);
+    const int64_t bc = bcg / G;
+    const int32_t c = (int32_t)(bc % nc);
+    const int64_t b = bc / nc;
+    const int hpg = H / G;
+    const int r0 = RB * rb;
+    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+    const int m = lane & 15, q = lane >> 4;
+    const int64_t tc = (int64_t)c * L;
+    const int arow = r0 + 16 * w + m;                 // this lane's A-operand row
+    const int64_t ta = tc + arow;
+    f32x4 dacc[NN];
+#pragma unroll
+    for (int i = 0; i < NN; ++i) dacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    constexpr int NII = (P * N / 8 + NTH - 1) / NTH;
+    for (int hh = 0; hh < hpg; ++hh) {
+        const int32_t h = g * hpg + hh;
+        const int64_t unit = ((b * H) + h) * nc + c;
+        __syncthreads();
+        // all of this head's loads first: ghat, the strip row's G, DT and x
+        const float *src = gh + unit * (int64_t)(P * N);
+        float4 iv[NII][2];
+#pragma unroll
+        for (int j = 0; j < NII; ++j) {
+            const int e = tid + j * NTH;
+            const int p = 2 * (e % (P / 2)), n4 = 4 * (e / (P / 2));
+            const bool ok = e < P * N / 8;
+            iv[j][0] = ok ? *reinterpret_cast<const float4 *>(src + p * N + n4) : make_float4(0.f, 0.f, 0.f, 0.f);
+            iv[j][1] = ok ? *reinterpret_cast<const float4 *>(src + (p + 1) * N + n4)
+                          : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+        const float ga = Gws[unit * L + arow], glast = Gws[unit * L + L - 1];
+        const float da = DTws[unit * L + arow];
+        uint4 ar[2];
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+            const int64_t o = ((b * T + (ta < T ? ta : 0)) * H + h) * P + 32 * st + 8 * q;
+            ar[st] = ta < T ? *reinterpret_cast<const uint4 *>(x + o) : make_uint4(0u, 0u, 0u, 0u);
+        }
+#pragma unroll
+        for (int j = 0; j < NII; ++j) {
+            const int e = tid + j * NTH;
+            if (e < P * N / 8) {
+                const int p = 2 * (e % (P / 2)), n4 = 4 * (e / (P / 2));
+                const float a0[4] = {iv[j][0].x, iv[j][0].y, iv[j][0].z, iv[j][0].w};
+                const float a1[4] = {iv[j][1].x, iv[j][1].y, iv[j][1].z, iv[j][1].w};
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    uint32_t hi, lo;
+                    split2(a0[i], a1[i], hi, lo);
+                    *reinterpret_cast<uint32_t *>(&Ib[0][(n4 + i) * SP + p]) = hi;
+                    *reinterpret_cast<uint32_t *>(&Ib[1][(n4 + i) * SP + p]) = lo;
+                }
+            }
+        }
+        __syncthreads();
+        // A operand: the strip's x rows times dt exp2(G_last - G), hi + lo
+        const float sc = da * fast_exp2(glast - ga);
+        bf16x8 aI[2], aIl[2];
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+            const uint4 u = ar[st];
+            const float fs[8] = {bf16_lo(u.x) * sc, bf16_hi(u.x) * sc, bf16_lo(u.y) * sc,
+                                 bf16_hi(u.y) * sc, bf16_lo(u.z) * sc, bf16_hi(u.z) * sc,
+                                 bf16_lo(u.w) * sc, bf16_hi(u.w) * sc};
+            uint4 hi, lo;
+            split8(fs, hi, lo);
+            aI[st] = as_bf16x8(hi);
+            aIl[st] = as_bf16x8(lo);
+        }
+#pragma unroll
+        for (int nt = 0; nt < NN; ++nt)
+#pragma unroll
+            for (int st = 0; st < 2; ++st) {
+                const int off = (16 * nt + m) * SP + 32 * st + 8 * q;
+                const bf16x8 bh = as_bf16x8(*reinterpret_cast<const uint4 *>(&Ib[0][off]));
+                const bf16x8 bl = as_bf16x8(*reinterpret_cast<const uint4 *>(&Ib[1][off]));
+                dacc[nt] = mfma16x16x32(aI[st], bh, dacc[nt]);
+                dacc[nt] = mfma16x16x32(aI[st], bl, dacc[nt]);
+                dacc[nt] = mfma16x16x32(aIl[st], bh, dacc[nt]);
+            }
+    }
+    // final: dB(j, n) += sum_k M^T(j, k) C_k[n] over k >= r0 (M is zero above
+    // its diagonal), 64 tokens k at a time
+    const float *mrow = MT + bcg * (int64_t)(L * L) + (int64_t)arow * L;
+    for (int cc = r0 / 64; cc < L / 64; ++cc) {
+        float4 mv[2][2];
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+            mv[st][0] = *reinterpret_cast<const float4 *>(mrow + 64 * cc + 32 * st + 8 * q);
+            mv[st][1] = *reinterpret_cast<const float4 *>(mrow + 64 * cc + 32 * st + 8 * q + 4);
+        }
+        __syncthreads();
+        // C rows of the chunk, transposed to [n][token]: a lane takes tokens r, r+1
+        for (int e = tid; e < 64 * N / 16; e += NTH) {
+            const int r = 2 * (e % 32), n8 = 8 * (e / 32);
+            const int64_t t = tc + 64 * cc + r;
+            uint4 v0 = make_uint4(0u, 0u, 0u, 0u), v1 = v0;
+            if (t < T) v0 = *reinterpret_cast<const uint4 *>(C + ((b * T + t) * G + g) * N + n8);
+            if (t + 1 < T) v1 = *reinterpret_cast<const uint4 *>(C + ((b * T + t + 1) * G + g) * N + n8);
+            const uint32_t w0[4] = {v0.x, v0.y, v0.z, v0.w}, w1[4] = {v1.x, v1.y, v1.z, v1.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                *reinterpret_cast<uint32_t *>(&Ib[0][(n8 + 2 * i) * SP + r]) = pair16(w0[i], w1[i]);
+                *reinterpret_cast<uint32_t *>(&Ib[0][(n8 + 2 * i + 1) * SP + r]) =
+                    pair16(w0[i] >> 16, w1[i] >> 16);
+            }
+        }
+        __syncthreads();
+        bf16x8 aM[2], aMl[2];
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+            const float f[8] = {mv[st][0].x, mv[st][0].y, mv[st][0].z, mv[st][0].w,
+                                mv[st][1].x, mv[st][1].y, mv[st][1].z, mv[st][1].w};
+            uint4 hi, lo;
+            split8(f, hi, lo);
+            aM[st] = as_bf16x8(hi);
+            aMl[st] = as_bf16x8(lo);
         }
 #pragma unroll
         for (int nt = 0; nt < NN; ++nt)
@@ -1418,12 +1576,11 @@ hipError_t launch_bwd_t(const Shape &s, const BwdArgs &a, hipStream_t st) {
         if constexpr (sizeof(Tio) == 2) {
             constexpr int WPB = L >= 128 ? 8 : 4;
             const uint32_t nb = (uint32_t)(ncb * (L / (16 * WPB)));
-            hipLaunchKernelGGL((bwd_dbdc_mfma_kernel<L, N, 0, WPB>), dim3(nb), dim3(64 * WPB), 0,
-                               st, x, B, C, a.dy, a.G, a.DT, a.S, (const float *)a.hprev, a.dC, T,
-                               H, G, nc);
-            hipLaunchKernelGGL((bwd_dbdc_mfma_kernel<L, N, 1, WPB>), dim3(nb), dim3(64 * WPB), 0,
-                               st, x, B, C, a.dy, a.G, a.DT, a.S, (const float *)a.hprev, a.dB, T,
-                               H, G, nc);
+            hipLaunchKernelGGL((bwd_dc_mfma_kernel<L, N, WPB>), dim3(nb), dim3(64 * WPB), 0, st, x,
+                               B, a.dy, a.G, a.DT, (const float *)a.hprev, a.dC, a.MT, T, H, G,
+                               nc);
+            hipLaunchKernelGGL((bwd_db_mfma_kernel<L, N, WPB>), dim3(nb), dim3(64 * WPB), 0, st, x,
+                               C, a.G, a.DT, a.S, a.MT, a.dB, T, H, G, nc);
         } else {
             hipLaunchKernelGGL((bwd_dbdc_kernel<L, N, Tio, Thp>),
                                dim3((uint32_t)(ncb * (L / 64) * 2)), dim3(256), 0, st, x, B, C,

@@ -534,7 +534,7 @@ ssd_status ssd_decode_step_lp(void *state, const ssd_state_format *fmt, const vo
 // sequence, where bf16's rounding would not cancel).
 struct BwdLayout {
     Layout fwd;
-    size_t fin, cb, cbt, cb3, cbt3, cfr, tok, part, hp32, total;
+    size_t fin, cb, cbt, cb3, cbt3, mt, cfr, tok, part, hp32, total;
 };
 
 BwdLayout bwd_layout_of(const ssd::Shape &s) {
@@ -546,7 +546,8 @@ BwdLayout bwd_layout_of(const ssd::Shape &s) {
     l.cbt = align256(l.cb + ssd::bwd_cb_bytes(s));
     l.cb3 = align256(l.cbt + (s.bf16 ? ssd::bwd_cb_bytes(s) : 0));
     l.cbt3 = align256(l.cb3 + (s.bf16 ? ssd::bwd_cb_bytes(s) * 3 / 2 : 0));
-    l.cfr = align256(l.cbt3 + (s.bf16 ? ssd::bwd_cb_bytes(s) * 3 / 2 : 0));
+    l.mt = align256(l.cbt3 + (s.bf16 ? ssd::bwd_cb_bytes(s) * 3 / 2 : 0));
+    l.cfr = align256(l.mt + (s.bf16 ? ssd::bwd_cb_bytes(s) : 0));
     l.tok = align256(l.cfr + (ssd::state_adj_supported(s) ? ssd::state_fwd_bfrag_bytes(s) : 0));
     l.part = align256(l.tok + 3 * bh * s.nc * s.L * sizeof(float));
     l.hp32 = align256(l.part + 3 * bh * sizeof(double));
@@ -636,6 +637,7 @@ ssd_status ssd_chunked_bwd(const void *x, const float *dt, const float *A, const
                    reinterpret_cast<float *>(base + l.tok),
                    s.bf16 ? reinterpret_cast<uint16_t *>(base + l.cb3) : nullptr,
                    s.bf16 ? reinterpret_cast<uint16_t *>(base + l.cbt3) : nullptr,
+                   s.bf16 ? reinterpret_cast<float *>(base + l.mt) : nullptr,
                    reinterpret_cast<double *>(base + l.part), false};
     // the state adjoint: the one-pass reverse scan where the forward takes the
     // one-pass form, else per-chunk sums and a separate reverse scan

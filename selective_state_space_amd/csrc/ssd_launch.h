@@ -90,6 +90,7 @@ struct BwdArgs {
     const void *hprev;
     float *CB, *CBT, *tok;   // CBT: CB transposed, bf16 io only (NULL otherwise)
     uint16_t *CB3, *CBT3;    // CB and CBT as three bf16 terms each, bf16 io only
+    float *MT;               // the dB/dC matrix M, transposed, bf16 io only
     double *part;
     bool ghat_ready;         // S already holds ghat and dinit is written (launch_state_adj)
 };
