@@ -1289,6 +1289,24 @@ __global__ __launch_bounds__(4 * L) void bwd_dx_mfma_kernel(
         }
     };
 
+    // the epilogue's dy (rows i = 16w + 4q + e, columns p = 16 pt + m),
+    // loaded during the last phase where the registers allow (at N = 64 the
+    // allocator spills with them live; there the epilogue loads them itself)
+    constexpr bool kEpiPrefetch = N >= 128;
+    float edy[4][NP];
+    auto load_epilogue = [&]() {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int64_t t = tc + 16 * w + 4 * q + e;
+            const bool real = t < T;
+#pragma unroll
+            for (int pt = 0; pt < NP; ++pt) {
+                const int64_t o = ((b * T + (real ? t : 0)) * H + h) * P + 16 * pt + m;
+                edy[e][pt] = real ? dy[o] : 0.f;
+            }
+        }
+    };
+
     __syncthreads();
     const float g_i = Gs[arow];
     load_phase(0);
@@ -1307,6 +1325,7 @@ __global__ __launch_bounds__(4 * L) void bwd_dx_mfma_kernel(
 #pragma unroll
         for (int ks = 0; ks < N / 32; ++ks) rcur[ks] = ra[ks];
         if (ph + 1 < NPH) load_phase(ph + 1);
+        else if constexpr (kEpiPrefetch) load_epilogue();
         __syncthreads();
         if (ph < NB) {
 #pragma unroll
@@ -1349,7 +1368,7 @@ __global__ __launch_bounds__(4 * L) void bwd_dx_mfma_kernel(
         for (int pt = 0; pt < NP; ++pt) {
             const int p = 16 * pt + m;
             const int64_t o = ((b * T + tt) * H + h) * P + p;
-            const float dyv = real ? dy[o] : 0.f;
+            const float dyv = kEpiPrefetch ? edy[e][pt] : (real ? dy[o] : 0.f);
             const float xv = real ? bf16_to_f32(x[o]) : 0.f;
             const float u = U[pt][e] + su * Ui[pt][e];
             const float yv = Y[pt][e] + sy * Yi[pt][e];
