@@ -1490,7 +1490,8 @@ __global__ __launch_bounds__(256) void bwd_scalars_kernel(
     const float *__restrict__ tok, const float *__restrict__ DTws, const float *__restrict__ A,
     const double *__restrict__ bnd, float *__restrict__ ddt, double *__restrict__ part,
     int64_t T, int32_t H, int32_t nc, int64_t ntok, int64_t nbh) {
-    __shared__ double seg[256];
+    constexpr int KB = 16;                         // tokens per load batch
+    __shared__ double seg[2][256];
     __shared__ double red[2][256];
     const int64_t bh = blockIdx.x;
     const int64_t b = bh / H;
@@ -1500,27 +1501,48 @@ __global__ __launch_bounds__(256) void bwd_scalars_kernel(
     const int64_t t0 = (int64_t)tid * per, t1 = t0 + per < T ? t0 + per : T;
     const float *xu = tok + bh * nc * L, *r = tok + ntok + bh * nc * L,
                 *dyx = tok + 2 * ntok + bh * nc * L, *DT = DTws + bh * nc * L;
+    // this thread's segment [t0, t1) in batches of KB tokens whose loads are
+    // all issued before any is used
     double sum = 0.0;
-    for (int64_t t = t0; t < t1; ++t) sum += (double)r[t];
-    seg[tid] = sum;
-    __syncthreads();
-    // exclusive suffix sum over the segments, in a fixed order
-    if (tid == 0) {
-        double acc = bnd[bh];
-        for (int i = 255; i >= 0; --i) {
-            const double v = seg[i];
-            seg[i] = acc;
-            acc += v;
-        }
+    for (int64_t bs = t0; bs < t1; bs += KB) {
+        float rv[KB];
+#pragma unroll
+        for (int i = 0; i < KB; ++i) rv[i] = bs + i < t1 ? r[bs + i] : 0.f;
+#pragma unroll
+        for (int i = 0; i < KB; ++i) sum += (double)rv[i];
     }
+    // exclusive suffix sums over the segments (fixed order: a Hillis-Steele
+    // scan), starting from the boundary term
+    seg[0][tid] = sum;
     __syncthreads();
+    int cur = 0;
+    for (int d = 1; d < 256; d <<= 1) {
+        const double v = seg[cur][tid] + (tid + d < 256 ? seg[cur][tid + d] : 0.0);
+        seg[cur ^ 1][tid] = v;
+        cur ^= 1;
+        __syncthreads();
+    }
     const double Ah = (double)A[h];
-    double s = seg[tid], da = 0.0, dd = 0.0;
-    for (int64_t t = t1 - 1; t >= t0; --t) {
-        s += (double)r[t];
-        ddt[(b * T + t) * H + h] = (float)((double)xu[t] + Ah * s);
-        da += (double)DT[t] * s;
-        dd += (double)dyx[t];
+    double s = bnd[bh] + (tid + 1 < 256 ? seg[cur][tid + 1] : 0.0), da = 0.0, dd = 0.0;
+    for (int64_t be = t1; be > t0; be -= KB) {
+        const int64_t bs = be - KB;
+        float rv[KB], xv[KB], dv[KB], yv[KB];
+#pragma unroll
+        for (int i = 0; i < KB; ++i) {
+            const bool ok = bs + i >= t0;
+            rv[i] = ok ? r[bs + i] : 0.f;
+            xv[i] = ok ? xu[bs + i] : 0.f;
+            dv[i] = ok ? DT[bs + i] : 0.f;
+            yv[i] = ok ? dyx[bs + i] : 0.f;
+        }
+#pragma unroll
+        for (int i = KB - 1; i >= 0; --i) {
+            if (bs + i < t0) break;
+            s += (double)rv[i];
+            ddt[(b * T + bs + i) * H + h] = (float)((double)xv[i] + Ah * s);
+            da += (double)dv[i] * s;
+            dd += (double)yv[i];
+        }
     }
     red[0][tid] = da;
     red[1][tid] = dd;
