@@ -129,9 +129,14 @@ def profile_kind(name: str):
     if "chunk_scan_bf16_kernel" in name:
         args = name[name.index("<") + 1:name.index(">")].split(",")
         return "chunk_scan" if args[-1].strip() == "false" else None
-    for k in ("chunk_cumsum", "chunk_state", "state_passing", "b_fragments", "state_fwd"):
+    if "state_fwd_kernel" in name:
+        # the forward's mode (bf16 h_prev) only: the backward runs the same
+        # kernel with fp32 h_prev (mode 1) and as its adjoint scan (mode 2)
+        args = name[name.index("<") + 1:name.index(">")].split(",")
+        return "state_fwd_kernel" if args[-1].strip() == "0" else None
+    for k in ("chunk_cumsum", "chunk_state", "state_passing", "b_fragments"):
         if k + "_kernel" in name:
-            return "state_fwd_kernel" if k == "state_fwd" else k
+            return k
     return None
 
 
