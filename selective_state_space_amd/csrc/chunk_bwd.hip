@@ -648,14 +648,13 @@ __global__ __launch_bounds__(64 * WPB) void bwd_dc_mfma_kernel(
     constexpr int NCI = (L * (P / 8) + NTH - 1) / NTH;
     constexpr int NII = (P * N / 8 + NTH - 1) / NTH;
     const int ncols = c_hi * (P / 8);
-    for (int hh = 0; hh < hpg; ++hh) {
+    // the x rows and h_prev of head hh + 1 load into registers while head hh
+    // computes; G, DT and the strip's dy rows load at the head's start
+    uint4 cx[NCI];
+    float4 iv[NII][2];
+    auto load_head = [&](int hh) {
         const int32_t h = g * hpg + hh;
         const int64_t unit = ((b * H) + h) * nc + c;
-        __syncthreads();
-        // every global load of this head is issued before any is used (one
-        // memory latency per head): the x rows, h_prev, G and DT, and the
-        // strip's own dy rows
-        uint4 cx[NCI];
 #pragma unroll
         for (int j = 0; j < NCI; ++j) {
             const int e = tid + j * NTH;
@@ -666,7 +665,6 @@ __global__ __launch_bounds__(64 * WPB) void bwd_dc_mfma_kernel(
             cx[j] = ok ? *reinterpret_cast<const uint4 *>(x + o) : make_uint4(0u, 0u, 0u, 0u);
         }
         const float *src = hprev + unit * (int64_t)(P * N);
-        float4 iv[NII][2];
 #pragma unroll
         for (int j = 0; j < NII; ++j) {
             const int e = tid + j * NTH;
@@ -676,6 +674,12 @@ __global__ __launch_bounds__(64 * WPB) void bwd_dc_mfma_kernel(
             iv[j][1] = ok ? *reinterpret_cast<const float4 *>(src + (p + 1) * N + n4)
                           : make_float4(0.f, 0.f, 0.f, 0.f);
         }
+    };
+    load_head(0);
+    for (int hh = 0; hh < hpg; ++hh) {
+        const int32_t h = g * hpg + hh;
+        const int64_t unit = ((b * H) + h) * nc + c;
+        __syncthreads();
         float gl = 0.f, dl = 0.f;
         if (tid < L) {
             gl = Gws[unit * L + tid];
@@ -711,6 +715,7 @@ __global__ __launch_bounds__(64 * WPB) void bwd_dc_mfma_kernel(
                 }
             }
         }
+        if (hh + 1 < hpg) load_head(hh + 1);
         if (tid < L) {
             Gs[tid] = gl;
             DTs[tid] = dl;
@@ -884,13 +889,15 @@ __global__ __launch_bounds__(64 * WPB) void bwd_db_mfma_kernel(
 #pragma unroll
     for (int i = 0; i < NN; ++i) dacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
     constexpr int NII = (P * N / 8 + NTH - 1) / NTH;
-    for (int hh = 0; hh < hpg; ++hh) {
+    // one head ahead: ghat, the strip row's G, DT and x of head hh + 1 load
+    // into registers while head hh computes
+    float4 iv[NII][2];
+    float ga = 0.f, glast = 0.f, da = 0.f;
+    uint4 ar[2];
+    auto load_head = [&](int hh) {
         const int32_t h = g * hpg + hh;
         const int64_t unit = ((b * H) + h) * nc + c;
-        __syncthreads();
-        // all of this head's loads first: ghat, the strip row's G, DT and x
         const float *src = gh + unit * (int64_t)(P * N);
-        float4 iv[NII][2];
 #pragma unroll
         for (int j = 0; j < NII; ++j) {
             const int e = tid + j * NTH;
@@ -900,14 +907,18 @@ __global__ __launch_bounds__(64 * WPB) void bwd_db_mfma_kernel(
             iv[j][1] = ok ? *reinterpret_cast<const float4 *>(src + (p + 1) * N + n4)
                           : make_float4(0.f, 0.f, 0.f, 0.f);
         }
-        const float ga = Gws[unit * L + arow], glast = Gws[unit * L + L - 1];
-        const float da = DTws[unit * L + arow];
-        uint4 ar[2];
+        ga = Gws[unit * L + arow];
+        glast = Gws[unit * L + L - 1];
+        da = DTws[unit * L + arow];
 #pragma unroll
         for (int st = 0; st < 2; ++st) {
             const int64_t o = ((b * T + (ta < T ? ta : 0)) * H + h) * P + 32 * st + 8 * q;
             ar[st] = ta < T ? *reinterpret_cast<const uint4 *>(x + o) : make_uint4(0u, 0u, 0u, 0u);
         }
+    };
+    load_head(0);
+    for (int hh = 0; hh < hpg; ++hh) {
+        __syncthreads();
 #pragma unroll
         for (int j = 0; j < NII; ++j) {
             const int e = tid + j * NTH;
@@ -924,7 +935,6 @@ __global__ __launch_bounds__(64 * WPB) void bwd_db_mfma_kernel(
                 }
             }
         }
-        __syncthreads();
         // A operand: the strip's x rows times dt exp2(G_last - G), hi + lo
         const float sc = da * fast_exp2(glast - ga);
         bf16x8 aI[2], aIl[2];
@@ -939,6 +949,8 @@ __global__ __launch_bounds__(64 * WPB) void bwd_db_mfma_kernel(
             aI[st] = as_bf16x8(hi);
             aIl[st] = as_bf16x8(lo);
         }
+        if (hh + 1 < hpg) load_head(hh + 1);
+        __syncthreads();
 #pragma unroll
         for (int nt = 0; nt < NN; ++nt)
 #pragma unroll
