@@ -20,7 +20,8 @@
 //   r_i = dy_i . Y_i - dt_i x_i . U_i                              (bwd_dx)
 //   M(k,j) = sum_h [k>=j] exp(G_k-G_j) dt_j (dy_k . x_j)
 //   dC_k = sum_j M(k,j) B_j + sum_h exp(G_k) h_prev^T dy_k
-//   dB_j = sum_k M(k,j) C_k + sum_h dt_j exp(G_last-G_j) ghat_c^T x_j (bwd_dbdc)
+//   dB_j = sum_k M(k,j) C_k + sum_h dt_j exp(G_last-G_j) ghat_c^T x_j
+//                                     (bwd_dbdc; bwd_dc_mfma and bwd_db_mfma)
 //   s_t  = <dfinal, final> + sum_{t'>=t} r_t'  (over the whole sequence)
 //   ddt_t = x_t . U_t + A s_t;  dA = sum dt_t s_t;  dD = sum dy_t . x_t
 //                                                   (bwd_scalars, bwd_heads)
@@ -29,11 +30,15 @@
 // so the decay part of the step gradient is a reverse running sum of per-token
 // scalars and never needs a per-token state.
 //
-// These kernels are fp32 SIMT: each stage stages operand tiles into LDS and
-// every thread accumulates a small register tile.  h_prev is read in fp32
-// (recomputed by chunk_state + state_passing with an fp32 output): the decay
-// gradients sum per-token products with it over the whole sequence, and
-// bf16's rounding of it would not average out there.
+// bf16 io runs bwd_dx, dC and dB on bf16 MFMA with fp32 operands split into
+// two or three bf16 terms; fp32 io runs fp32 SIMT versions that stage operand
+// tiles into LDS and accumulate small register tiles per thread.  h_prev is
+// read in fp32 (recomputed with fp32 stores, by the one-pass state kernel or
+// by chunk_state + state_passing): the decay gradients sum per-token products
+// with it over the whole sequence, and bf16's rounding of it would not average
+// out there.  Where the forward takes the one-pass form, the same kernel also
+// runs the state adjoint scan (dSp and the reverse scan in one pass, chunks
+// last to first); bwd_dstate and bwd_passing serve the other shapes.
 
 #include "ssd_device.h"
 #include "ssd_launch.h"
@@ -591,17 +596,17 @@ __global__ __launch_bounds__(256) void bwd_dbdc_kernel(
     }
 }
 
-// ---- bwd_dbdc_mfma: the same dB / dC on bf16 MFMA (bf16 io) ----------------
-// One 64-row block of one (b, c, g) per workgroup; wavefront w owns the 16-row
-// strip 16w..16w+15.  ORIENT 0 computes dC (rows k: the strip's dy rows times
-// the x rows of the chunk, inter term dy h_prev^T, final M B); ORIENT 1
-// computes dB (rows j: x rows times dy rows, inter term x ghat^T, final M^T C).
-// Per head the column-side rows (x or dy) and the inter operand (h_prev or
-// ghat, transposed to [n][p]) are staged in LDS; the strip's own rows are the
-// A operands, straight from global memory.  v_mfma_f32_16x16x32_bf16 layouts:
+// ---- bwd_dc_mfma: dC on bf16 MFMA (bf16 io), and M for bwd_db_mfma ---------
+// One block of 16*WPB rows k of one (b, c, g) per workgroup; wavefront w owns
+// the 16-row strip r0+16w..+15: per head, the strip's dy rows times the x
+// rows of the chunk (decayed and masked into M), and the inter term
+// exp2(G) dy h_prev^T; after the heads, M B.  Per head the x rows and h_prev
+// (transposed to [n][p]) are staged in LDS; the strip's own rows are the A
+// operands, straight from global memory.  v_mfma_f32_16x16x32_bf16 layouts:
 // A lane l holds row l%16, k 8(l/16)..+7; B lane l holds column l%16, the same
 // k; D lane l holds rows 4(l/16)+e, column l%16.  M stays in the accumulators
-// over the heads (fp32) and goes through LDS for the final product.
+// over the heads (fp32), is stored transposed for dB = M^T C, and goes
+// through LDS for the final product.
 // Precision: dB and dC are small differences of large terms near the end of a
 // sequence (where dfinal enters), so every fp32 operand is carried as a bf16
 // head plus a bf16 remainder (x, B and C are bf16 already): products of two
