@@ -41,6 +41,16 @@
 // x and B are read with buffer loads whose range is the chunk's valid rows:
 // a ragged last chunk reads zeros past T (its dt is 0 there as well).
 // Every exponent G_last - G_j and G_last is <= 0.
+//
+// The backward runs the same kernel in two more modes.  kModeF32 stores h_prev
+// in fp32.  kModeAdjoint is the reverse scan of the state adjoint (the
+// "mamba3" kernel card, section "Backward"): chunks last to first,
+//     ghat[c] = g;   g <- exp2(G_last,c) g + sum_k (dy_k exp2(G_k)) C_k^T;
+//     dinit = g,
+// with dy (fp32) in place of x -- its weighted values carried as three bf16
+// terms, the adjoint feeding dA through long sums -- C fragments in place of
+// B, dfinal as the initial state, and ghat stored in fp32.  Every exponent is
+// again <= 0.
 
 #include "ssd_device.h"
 #include "ssd_launch.h"
