@@ -83,7 +83,9 @@ __device__ __forceinline__ void mm_acc(float (&acc)[TM][TN], const float *As, in
 }
 
 // ---- bf16 operand helpers shared by the MFMA kernels below -----------------
-constexpr int SP = P + 8;     // LDS row pitch (bf16) of the staged [row][p] tiles
+constexpr int SP = P + 16;    // LDS row pitch (bf16) of the staged [row][p] tiles: 40
+                              // words (a 36-word pitch left the 16-byte MFMA operand
+                              // reads with bank conflicts, measured)
 
 __device__ __forceinline__ uint4 pack8(const float (&v)[8]) {
     return make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
@@ -1054,7 +1056,10 @@ __global__ __launch_bounds__(4 * L) void bwd_dx_mfma_kernel(
     const uint16_t *__restrict__ CB3, const uint16_t *__restrict__ CBT3, int64_t plane,
     const float *__restrict__ gh, const float *__restrict__ hprev, float *__restrict__ dx,
     float *__restrict__ tok, int64_t T, int32_t H, int32_t G, int32_t nc, int64_t ntok) {
-    constexpr int NB = L / 64, NP = P / 16, PN = N + 8;
+    constexpr int NB = L / 64, NP = P / 16, PN = N + 16;   // PN: 72- or 40-word rows, conflict-free
+    // the chunk tiles keep a 36-word pitch: their read conflicts cost no measurable time
+    // here, and the conflict-free 40-word pitch makes the allocator spill
+    constexpr int SPX = P + 8;
     constexpr int NTH = 4 * L;                        // L/16 wavefronts: one 16-row strip each
     // phases: U and Y over token chunk 0..NB-1 (chunk ck holds steps 2ck and
     // 2ck+1; U takes the steps at or after a strip's own, Y those at or
@@ -1072,7 +1077,7 @@ __global__ __launch_bounds__(4 * L) void bwd_dx_mfma_kernel(
     // terms, 3..5 dy times its token factor, 6 x, 7..9 dt x times its token
     // factor; the inter phases use Ih/Im/Il [p][N]
     constexpr int TY = 6;                             // first Y tile
-    constexpr int NLDS = 3 * P * PN > 10 * P * SP ? 3 * P * PN : 10 * P * SP;
+    constexpr int NLDS = 3 * P * PN > 10 * P * SPX ? 3 * P * PN : 10 * P * SPX;
     __shared__ __align__(16) uint16_t lds[NLDS];
     __shared__ float Gs[L], DTs[L];
     uint16_t *const Tu = lds;
@@ -1173,15 +1178,15 @@ __global__ __launch_bounds__(4 * L) void bwd_dx_mfma_kernel(
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
                         uint32_t s0, s1, s2;
-                        const int o = (p4 + i) * SP + r;
+                        const int o = (p4 + i) * SPX + r;
                         split2x3(a0[i], a1[i], s0, s1, s2);
                         *reinterpret_cast<uint32_t *>(Tu + o) = s0;
-                        *reinterpret_cast<uint32_t *>(Tu + P * SP + o) = s1;
-                        *reinterpret_cast<uint32_t *>(Tu + 2 * P * SP + o) = s2;
+                        *reinterpret_cast<uint32_t *>(Tu + P * SPX + o) = s1;
+                        *reinterpret_cast<uint32_t *>(Tu + 2 * P * SPX + o) = s2;
                         split2x3(a0[i] * f0, a1[i] * f1, s0, s1, s2);
-                        *reinterpret_cast<uint32_t *>(Tu + 3 * P * SP + o) = s0;
-                        *reinterpret_cast<uint32_t *>(Tu + 4 * P * SP + o) = s1;
-                        *reinterpret_cast<uint32_t *>(Tu + 5 * P * SP + o) = s2;
+                        *reinterpret_cast<uint32_t *>(Tu + 3 * P * SPX + o) = s0;
+                        *reinterpret_cast<uint32_t *>(Tu + 4 * P * SPX + o) = s1;
+                        *reinterpret_cast<uint32_t *>(Tu + 5 * P * SPX + o) = s2;
                     }
                 } else if (e < N_S) {                  // x (exact), and dt x times its token factor
                     const int ex = e - N_DY;
@@ -1197,16 +1202,16 @@ __global__ __launch_bounds__(4 * L) void bwd_dx_mfma_kernel(
                     for (int i = 0; i < 4; ++i) {
 #pragma unroll
                         for (int hf = 0; hf < 2; ++hf) {
-                            const int o = (p8 + 2 * i + hf) * SP + r;
+                            const int o = (p8 + 2 * i + hf) * SPX + r;
                             const uint32_t b0 = hf ? w0[i] >> 16 : w0[i] & 0xffffu;
                             const uint32_t b1 = hf ? w1[i] >> 16 : w1[i] & 0xffffu;
-                            *reinterpret_cast<uint32_t *>(Tu + TY * P * SP + o) = pair16(b0, b1);
+                            *reinterpret_cast<uint32_t *>(Tu + TY * P * SPX + o) = pair16(b0, b1);
                             uint32_t s0, s1, s2;
                             split2x3(__uint_as_float(b0 << 16) * f0, __uint_as_float(b1 << 16) * f1, s0,
                                      s1, s2);
-                            *reinterpret_cast<uint32_t *>(Tu + (TY + 1) * P * SP + o) = s0;
-                            *reinterpret_cast<uint32_t *>(Tu + (TY + 2) * P * SP + o) = s1;
-                            *reinterpret_cast<uint32_t *>(Tu + (TY + 3) * P * SP + o) = s2;
+                            *reinterpret_cast<uint32_t *>(Tu + (TY + 1) * P * SPX + o) = s0;
+                            *reinterpret_cast<uint32_t *>(Tu + (TY + 2) * P * SPX + o) = s1;
+                            *reinterpret_cast<uint32_t *>(Tu + (TY + 3) * P * SPX + o) = s2;
                         }
                     }
                 }
@@ -1258,14 +1263,14 @@ __global__ __launch_bounds__(4 * L) void bwd_dx_mfma_kernel(
             const bf16x8 a[3] = {as_bf16x8(a0), as_bf16x8(a1), as_bf16x8(a2)};
 #pragma unroll
             for (int pt = 0; pt < NP; ++pt) {
-                const int off = (16 * pt + m) * SP + toff;
+                const int off = (16 * pt + m) * SPX + toff;
                 if (isU) {
                     const bf16x8 bb[3] = {as_bf16x8(*reinterpret_cast<const uint4 *>(Tu + off)),
-                                          as_bf16x8(*reinterpret_cast<const uint4 *>(Tu + P * SP + off)),
-                                          as_bf16x8(*reinterpret_cast<const uint4 *>(Tu + 2 * P * SP + off))};
+                                          as_bf16x8(*reinterpret_cast<const uint4 *>(Tu + P * SPX + off)),
+                                          as_bf16x8(*reinterpret_cast<const uint4 *>(Tu + 2 * P * SPX + off))};
                     U[pt] = mfma6(a, bb, U[pt]);
                 } else {
-                    const bf16x8 bx = as_bf16x8(*reinterpret_cast<const uint4 *>(Tu + TY * P * SP + off));
+                    const bf16x8 bx = as_bf16x8(*reinterpret_cast<const uint4 *>(Tu + TY * P * SPX + off));
                     Y[pt] = mfma16x16x32(a[2], bx, Y[pt]);
                     Y[pt] = mfma16x16x32(a[1], bx, Y[pt]);
                     Y[pt] = mfma16x16x32(a[0], bx, Y[pt]);
@@ -1281,11 +1286,11 @@ __global__ __launch_bounds__(4 * L) void bwd_dx_mfma_kernel(
             f32x4 part[NP];
 #pragma unroll
             for (int pt = 0; pt < NP; ++pt) {
-                const int off = (16 * pt + m) * SP + toff;
+                const int off = (16 * pt + m) * SPX + toff;
                 const bf16x8 bb[3] = {
-                    as_bf16x8(*reinterpret_cast<const uint4 *>(Tu + tb * P * SP + off)),
-                    as_bf16x8(*reinterpret_cast<const uint4 *>(Tu + (tb + 1) * P * SP + off)),
-                    as_bf16x8(*reinterpret_cast<const uint4 *>(Tu + (tb + 2) * P * SP + off))};
+                    as_bf16x8(*reinterpret_cast<const uint4 *>(Tu + tb * P * SPX + off)),
+                    as_bf16x8(*reinterpret_cast<const uint4 *>(Tu + (tb + 1) * P * SPX + off)),
+                    as_bf16x8(*reinterpret_cast<const uint4 *>(Tu + (tb + 2) * P * SPX + off))};
                 part[pt] = mfma6(a, bb, f32x4{0.f, 0.f, 0.f, 0.f});
             }
             // the row factor: exp2(G_e - G_i) for U (e the step's first
