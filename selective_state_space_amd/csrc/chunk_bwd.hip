@@ -655,13 +655,25 @@ __global__ __launch_bounds__(64 * WPB) void bwd_dc_mfma_kernel(
     constexpr int NCI = (L * (P / 8) + NTH - 1) / NTH;
     constexpr int NII = (P * N / 8 + NTH - 1) / NTH;
     const int ncols = c_hi * (P / 8);
-    // the x rows and h_prev of head hh + 1 load into registers while head hh
-    // computes; G, DT and the strip's dy rows load at the head's start
+    // every operand of head hh + 1 (x rows, h_prev, G, DT and the strip's dy
+    // rows) loads into registers while head hh computes
     uint4 cx[NCI];
     float4 iv[NII][2];
+    float gl = 0.f, dl = 0.f;
+    float4 ar[2][2];                                  // the strip's own dy rows
     auto load_head = [&](int hh) {
         const int32_t h = g * hpg + hh;
         const int64_t unit = ((b * H) + h) * nc + c;
+        if (tid < L) {
+            gl = Gws[unit * L + tid];
+            dl = DTws[unit * L + tid];
+        }
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+            const int64_t o = ((b * T + (ta < T ? ta : 0)) * H + h) * P + 32 * st + 8 * q;
+            ar[st][0] = ta < T ? *reinterpret_cast<const float4 *>(dy + o) : make_float4(0.f, 0.f, 0.f, 0.f);
+            ar[st][1] = ta < T ? *reinterpret_cast<const float4 *>(dy + o + 4) : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
 #pragma unroll
         for (int j = 0; j < NCI; ++j) {
             const int e = tid + j * NTH;
@@ -684,21 +696,7 @@ __global__ __launch_bounds__(64 * WPB) void bwd_dc_mfma_kernel(
     };
     load_head(0);
     for (int hh = 0; hh < hpg; ++hh) {
-        const int32_t h = g * hpg + hh;
-        const int64_t unit = ((b * H) + h) * nc + c;
         __syncthreads();
-        float gl = 0.f, dl = 0.f;
-        if (tid < L) {
-            gl = Gws[unit * L + tid];
-            dl = DTws[unit * L + tid];
-        }
-        float4 ar[2][2];                              // the strip's own dy rows
-#pragma unroll
-        for (int st = 0; st < 2; ++st) {
-            const int64_t o = ((b * T + (ta < T ? ta : 0)) * H + h) * P + 32 * st + 8 * q;
-            ar[st][0] = ta < T ? *reinterpret_cast<const float4 *>(dy + o) : make_float4(0.f, 0.f, 0.f, 0.f);
-            ar[st][1] = ta < T ? *reinterpret_cast<const float4 *>(dy + o + 4) : make_float4(0.f, 0.f, 0.f, 0.f);
-        }
 #pragma unroll
         for (int j = 0; j < NCI; ++j) {
             const int e = tid + j * NTH;
@@ -722,7 +720,6 @@ __global__ __launch_bounds__(64 * WPB) void bwd_dc_mfma_kernel(
                 }
             }
         }
-        if (hh + 1 < hpg) load_head(hh + 1);
         if (tid < L) {
             Gs[tid] = gl;
             DTs[tid] = dl;
@@ -751,6 +748,7 @@ __global__ __launch_bounds__(64 * WPB) void bwd_dc_mfma_kernel(
             aI[st] = as_bf16x8(hi);
             aIl[st] = as_bf16x8(lo);
         }
+        if (hh + 1 < hpg) load_head(hh + 1);   // gl, dl and ar are consumed
         // S tiles on or below the diagonal, decayed and masked into M
 #pragma unroll
         for (int jt = 0; jt < NT; ++jt) {
