@@ -121,9 +121,11 @@ def test_no_tokens(dtype):
     assert torch.count_nonzero(g["dA"]) == 0 and torch.count_nonzero(g["dD"]) == 0
 
 
-def test_backward_full_size():
-    """The 2.7B-shaped layer: every gradient against the oracle."""
-    w = gen.WORKLOADS[2]
+@pytest.mark.parametrize("wi", [0, 1, 2])
+def test_backward_full_size(wi):
+    """The tiny fp32, 370M-shaped and 2.7B-shaped layers at their full sizes:
+    every gradient against the oracle."""
+    w = gen.WORKLOADS[wi]
     log("bwd full size", w.name)
     inp = gen.make_fwd(w, 0)
     dy, dfin = grads_inputs(inp, 5)
