@@ -154,11 +154,10 @@ __global__ __launch_bounds__(256) void decode_lowp_kernel(
 #pragma unroll
         for (int e = 0; e < 4; ++e) s[e] = dA * s[e] + u * bb[e];
         float part = s[0] * Cv.x + s[1] * Cv.y + s[2] * Cv.z + s[3] * Cv.w;
-#pragma unroll
-        for (int off = LPR / 2; off > 0; off >>= 1) part += __shfl_xor(part, off, 64);
+        part = group_sum<LPR>(part);   // the row's sum, in its last lane
         float out = part + Dh * xv[k];
         if constexpr (GATE) out *= fast_silu(zv[k]);
-        if (sub == 0) y[bh * P + p] = out;
+        if (sub == LPR - 1) y[bh * P + p] = out;
 
         uint32_t o[4];
         if constexpr (FMT == FMT_BF16) {

@@ -79,11 +79,10 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
         ns.w = dA * sv[k].w + u * Bv.w;
         store_nt(st + p * N + 4 * sub, ns);
         float part = ns.x * Cv.x + ns.y * Cv.y + ns.z * Cv.z + ns.w * Cv.w;
-#pragma unroll
-        for (int off = LPR / 2; off > 0; off >>= 1) part += __shfl_xor(part, off, 64);
+        part = group_sum<LPR>(part);   // the row's sum, in its last lane
         float out = part + Dh * xv[k];
         if constexpr (GATE) out *= fast_silu(zv[k]);
-        if (sub == 0) y[bh * P + p] = out;
+        if (sub == LPR - 1) y[bh * P + p] = out;
     }
 }
 
@@ -178,11 +177,10 @@ __global__ __launch_bounds__(256) void decode_multi_kernel(
             if constexpr (SNAP) store_nt(sn + rowoff[i], sv[i]);
             float part = sv[i].x * cur.Cv.x + sv[i].y * cur.Cv.y + sv[i].z * cur.Cv.z +
                          sv[i].w * cur.Cv.w;
-#pragma unroll
-            for (int off = LPR / 2; off > 0; off >>= 1) part += __shfl_xor(part, off, 64);
+            part = group_sum<LPR>(part);   // the row's sum, in its last lane
             float out = part + Dh * cur.xv[i];
             if constexpr (GATE) out *= fast_silu(cur.zv[i]);
-            if (sub == 0) y[th * P + 16 * wave + RPI * i + rw] = out;
+            if (sub == LPR - 1) y[th * P + 16 * wave + RPI * i + rw] = out;
         }
         cur = nxt;
     }

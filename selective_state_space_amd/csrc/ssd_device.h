@@ -124,4 +124,26 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, ui
                                              0x00020000);
 }
 
+// Sum over each group of LPR = 16 or 32 consecutive lanes by DPP moves (VALU
+// operand modifiers, no LDS crossbar round trip): butterflies inside quads,
+// then the half-row and row mirrors leave every lane of a 16-lane row with the
+// row's sum; for 32-lane groups, row_bcast:15 adds row 0's (row 2's) sum into
+// row 1 (row 3).  The group's sum is valid in its last lane, LPR - 1 (for
+// LPR = 16, in every lane).
+template <int CTRL, int ROW_MASK = 0xf>
+__device__ __forceinline__ float dpp_mov(float v) {
+    return __int_as_float(
+        __builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROW_MASK, 0xf, false));
+}
+template <int LPR>
+__device__ __forceinline__ float group_sum(float v) {
+    static_assert(LPR == 16 || LPR == 32, "16- or 32-lane groups");
+    v += dpp_mov<0xB1>(v);    // quad_perm [1,0,3,2]
+    v += dpp_mov<0x4E>(v);    // quad_perm [2,3,0,1]
+    v += dpp_mov<0x141>(v);   // row_half_mirror
+    v += dpp_mov<0x140>(v);   // row_mirror
+    if constexpr (LPR == 32) v += dpp_mov<0x142, 0xa>(v);   // row_bcast:15 into rows 1, 3
+    return v;
+}
+
 }  // namespace ssd
