@@ -1397,12 +1397,9 @@ __global__ __launch_bounds__(4 * L) void bwd_dx_mfma_kernel(
             dyy = fmaf(dyv, yv, dyy);
             dyx = fmaf(dyv, xv, dyx);
         }
-#pragma unroll
-        for (int o = 1; o < 16; o <<= 1) {
-            xu += __shfl_xor(xu, o, 64);
-            dyy += __shfl_xor(dyy, o, 64);
-            dyx += __shfl_xor(dyx, o, 64);
-        }
+        xu = group_sum<16>(xu);                       // over the 16 lanes of one q
+        dyy = group_sum<16>(dyy);
+        dyx = group_sum<16>(dyx);
         if (m == 0) {
             tokc[i] = xu;
             tokc[ntok + i] = dyy - dti * xu;

@@ -174,8 +174,7 @@ __global__ __launch_bounds__(256) void decode_lowp_kernel(
             for (int e = 0; e < 4; ++e) o[e] = f32_to_half_sr(s[e], rb[k][e] & 0x1FFFu);
         } else {   // FMT_INT16
             float m = fmaxf(fmaxf(fabsf(s[0]), fabsf(s[1])), fmaxf(fabsf(s[2]), fabsf(s[3])));
-#pragma unroll
-            for (int off = LPR / 2; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+            m = group_max<LPR>(m);
             const bool zero = m == 0.f;
             const float enc = 32767.f / (zero ? 1.f : m);
 #pragma unroll

@@ -145,5 +145,17 @@ __device__ __forceinline__ float group_sum(float v) {
     if constexpr (LPR == 32) v += dpp_mov<0x142, 0xa>(v);   // row_bcast:15 into rows 1, 3
     return v;
 }
+// The maximum over each group of LPR = 16 or 32 lanes, in every lane of it:
+// the same DPP steps within 16-lane rows, then one swap of neighbouring rows.
+template <int LPR>
+__device__ __forceinline__ float group_max(float v) {
+    static_assert(LPR == 16 || LPR == 32, "16- or 32-lane groups");
+    v = fmaxf(v, dpp_mov<0xB1>(v));
+    v = fmaxf(v, dpp_mov<0x4E>(v));
+    v = fmaxf(v, dpp_mov<0x141>(v));
+    v = fmaxf(v, dpp_mov<0x140>(v));
+    if constexpr (LPR == 32) v = fmaxf(v, __shfl_xor(v, 16, 64));
+    return v;
+}
 
 }  // namespace ssd
