@@ -625,9 +625,10 @@ bool state_adj_supported(const Shape &s) {
 }
 
 int state_adj_rows_per_block(const Shape &s) {
-    // three bf16 terms of dy*w take 1.5x the forward's LDS per row set: two
-    // row sets keep three workgroups resident per CU
-    return s.Bt * s.H >= 48 ? 2 : 1;
+    // the forward's rule: measured at the 2.7B shape, four row sets per
+    // workgroup (one resident per CU: three bf16 terms take 1.5x the forward's
+    // LDS) beat two (2.97 vs 3.03 ms for the whole backward) and one (3.26 ms)
+    return state_fwd_rows_per_block(s);
 }
 
 hipError_t launch_state_adj(const Shape &s, const float *dy, const void *C, const float *Gws,
