@@ -94,6 +94,17 @@ def decode_bytes(w, io_bytes=2):
             + 2 * Bt * G * N * io_bytes)
 
 
+def bwd_bytes(w, io_bytes=2):
+    """What the backward must move at least: x, B, C (io dtype), dy, dt, the
+    initial state and dfinal (fp32) in; dx, ddt, dB, dC and dinit (fp32) out."""
+    Bt, T, H, P, N, G = w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.ngroups
+    tok = Bt * T
+    ins = tok * H * P * (io_bytes + 4) + 2 * tok * G * N * io_bytes + tok * H * 4
+    outs = tok * H * P * 4 + tok * H * 4 + 2 * tok * G * N * 4
+    states = 3 * Bt * H * P * N * 4
+    return ins + outs + states
+
+
 def kernel_source_sha(kernel: str) -> str:
     """Hash of the device code a kernel is built from (its .hip file and the
     shared device header; the host-side launch declarations do not enter)."""
@@ -675,8 +686,11 @@ def main():
     bwd = None
     if not args.no_decode:
         bms = run_backward(w, 10, 3)
+        bb = bwd_bytes(w, io_bytes)
         bwd = dict(us_per_call=round(bms * 1e3, 2), tokens_per_s=round(tokens / (bms * 1e-3), 1),
                    over_forward=round(bms / step_ms, 3),
+                   must_move_bytes=int(bb), GBps=round(bb / (bms * 1e-3) / 1e9, 1),
+                   hbm_frac=round(bb / (bms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
                    gradients="dx, ddt, dA, dB, dC, dD, dinit (fp32)")
         log("backward: %.1f us/call (%.2fx the forward)" % (bms * 1e3, bms / step_ms))
     layer = None
