@@ -286,7 +286,6 @@ template <int L, int N, typename Tio>
 __global__ __launch_bounds__(256) void bwd_cb_kernel(const Tio *__restrict__ B,
                                                      const Tio *__restrict__ C,
                                                      float *__restrict__ CB,
-                                                     float *__restrict__ CBT,
                                                      uint16_t *__restrict__ CB3,
                                                      uint16_t *__restrict__ CBT3, int64_t T,
                                                      int32_t G, int32_t nc) {
@@ -317,17 +316,12 @@ __global__ __launch_bounds__(256) void bwd_cb_kernel(const Tio *__restrict__ B,
         __syncthreads();
         mm_acc<4, 4>(acc, As, LD, Bs, LD, m0, n0);
     }
-    float *o = CB + bcg * (int64_t)(L * L) + (int64_t)(64 * kb + m0) * L + 64 * jb + n0;
+    if (CB) {    // fp32 (fp32 io)
+        float *o = CB + bcg * (int64_t)(L * L) + (int64_t)(64 * kb + m0) * L + 64 * jb + n0;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-        *reinterpret_cast<float4 *>(o + i * L) =
-            make_float4(acc[i][0], acc[i][1], acc[i][2], acc[i][3]);
-    if (CBT) {   // CBT[j][k] = CB[k][j]
-        float *ot = CBT + bcg * (int64_t)(L * L) + (int64_t)(64 * jb + n0) * L + 64 * kb + m0;
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-            *reinterpret_cast<float4 *>(ot + j * L) =
-                make_float4(acc[0][j], acc[1][j], acc[2][j], acc[3][j]);
+        for (int i = 0; i < 4; ++i)
+            *reinterpret_cast<float4 *>(o + i * L) =
+                make_float4(acc[i][0], acc[i][1], acc[i][2], acc[i][3]);
     }
     if (CB3) {   // both as three bf16 terms, [term][bcg][row][col]
         const int64_t plane = (int64_t)gridDim.x / NTRI * L * L;   // Bt*nc*G*L*L
@@ -1050,8 +1044,7 @@ template <int L, int N>
 __global__ __launch_bounds__(4 * L) void bwd_dx_mfma_kernel(
     const uint16_t *__restrict__ x, const uint16_t *__restrict__ B, const uint16_t *__restrict__ C,
     const float *__restrict__ D, const float *__restrict__ dy, const float *__restrict__ Gws,
-    const float *__restrict__ DTws, const float *__restrict__ CB, const float *__restrict__ CBT,
-    const uint16_t *__restrict__ CB3, const uint16_t *__restrict__ CBT3, int64_t plane,
+    const float *__restrict__ DTws, const uint16_t *__restrict__ CB3, const uint16_t *__restrict__ CBT3, int64_t plane,
     const float *__restrict__ gh, const float *__restrict__ hprev, float *__restrict__ dx,
     float *__restrict__ tok, int64_t T, int32_t H, int32_t G, int32_t nc, int64_t ntok) {
     constexpr int NB = L / 64, NP = P / 16, PN = N + 16;   // PN: 72- or 40-word rows, conflict-free
@@ -1244,11 +1237,20 @@ __global__ __launch_bounds__(4 * L) void bwd_dx_mfma_kernel(
     auto step = [&](const bool isU, const int s, const int toff, const float g_i) {
         const int k0 = 32 * s + 8 * q;                 // this lane's 8 tokens of it
         if (s == sdiag) {
-            // the exact pairwise decay, masked, from fp32 C B^T
-            const float *rowp = (isU ? CBT : CB) + rowoff + k0;
-            const float4 c0 = *reinterpret_cast<const float4 *>(rowp);
-            const float4 c1 = *reinterpret_cast<const float4 *>(rowp + 4);
-            const float cv[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+            // the exact pairwise decay, masked, on C B^T rebuilt in fp32 from
+            // its three bf16 terms (their sum is the fp32 value exactly)
+            const uint16_t *rowp = (isU ? CBT3 : CB3) + rowoff + k0;
+            const uint4 t0 = *reinterpret_cast<const uint4 *>(rowp);
+            const uint4 t1 = *reinterpret_cast<const uint4 *>(rowp + plane);
+            const uint4 t2 = *reinterpret_cast<const uint4 *>(rowp + 2 * plane);
+            const uint32_t w0[4] = {t0.x, t0.y, t0.z, t0.w}, w1[4] = {t1.x, t1.y, t1.z, t1.w},
+                           w2[4] = {t2.x, t2.y, t2.z, t2.w};
+            float cv[8];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                cv[2 * i] = (bf16_lo(w0[i]) + bf16_lo(w1[i])) + bf16_lo(w2[i]);
+                cv[2 * i + 1] = (bf16_hi(w0[i]) + bf16_hi(w1[i])) + bf16_hi(w2[i]);
+            }
             float av[8];
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
@@ -1620,11 +1622,11 @@ hipError_t launch_bwd_t(const Shape &s, const BwdArgs &a, hipStream_t st) {
         constexpr int NTRI = (L / 64) * (L / 64 + 1) / 2;
         const uint64_t ncb = (uint64_t)s.Bt * s.nc * s.G;
         hipLaunchKernelGGL((bwd_cb_kernel<L, N, Tio>), dim3((uint32_t)(ncb * NTRI)), dim3(256), 0,
-                           st, B, C, a.CB, a.CBT, a.CB3, a.CBT3, T, G, nc);
+                           st, B, C, a.CB, a.CB3, a.CBT3, T, G, nc);
         if constexpr (sizeof(Tio) == 2)
             hipLaunchKernelGGL((bwd_dx_mfma_kernel<L, N>), dim3((uint32_t)units),
-                               dim3(4 * L), 0, st, x, B, C, a.D, a.dy, a.G, a.DT, a.CB, a.CBT,
-                               a.CB3, a.CBT3, (int64_t)(ncb * L * L), a.S,
+                               dim3(4 * L), 0, st, x, B, C, a.D, a.dy, a.G, a.DT, a.CB3,
+                               a.CBT3, (int64_t)(ncb * L * L), a.S,
                                (const float *)a.hprev, a.dx, a.tok, T, H, G, nc,
                                (int64_t)units * L);
         else

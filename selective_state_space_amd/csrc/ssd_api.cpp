@@ -527,14 +527,15 @@ ssd_status ssd_decode_step_lp(void *state, const ssd_state_format *fmt, const vo
 }
 
 // Backward workspace: the forward's regions, then the final state, C B^T per
-// (b, chunk, group) (and, for bf16 io, its transpose and both as three bf16
-// terms), three planes of per-token scalars, 3 * Bt*H fp64 partials and,
+// (b, chunk, group) (fp32 for fp32 io; for bf16 io it and its transpose as
+// three bf16 terms each, the dB/dC matrix M and the C fragments of the
+// adjoint scan), three planes of per-token scalars, 3 * Bt*H fp64 partials and,
 // for bf16 io, h_prev again in fp32 (the forward keeps it in bf16 for its
 // MFMA; the decay gradient sums per-token products of it over the whole
 // sequence, where bf16's rounding would not cancel).
 struct BwdLayout {
     Layout fwd;
-    size_t fin, cb, cbt, cb3, cbt3, mt, cfr, tok, part, hp32, total;
+    size_t fin, cb, cb3, cbt3, mt, cfr, tok, part, hp32, total;
 };
 
 BwdLayout bwd_layout_of(const ssd::Shape &s) {
@@ -543,8 +544,7 @@ BwdLayout bwd_layout_of(const ssd::Shape &s) {
     const size_t bh = (size_t)s.Bt * s.H;
     l.fin = align256(l.fwd.total);
     l.cb = align256(l.fin + bh * s.P * s.N * sizeof(float));
-    l.cbt = align256(l.cb + ssd::bwd_cb_bytes(s));
-    l.cb3 = align256(l.cbt + (s.bf16 ? ssd::bwd_cb_bytes(s) : 0));
+    l.cb3 = align256(l.cb + (s.bf16 ? 0 : ssd::bwd_cb_bytes(s)));
     l.cbt3 = align256(l.cb3 + (s.bf16 ? ssd::bwd_cb_bytes(s) * 3 / 2 : 0));
     l.mt = align256(l.cbt3 + (s.bf16 ? ssd::bwd_cb_bytes(s) * 3 / 2 : 0));
     l.cfr = align256(l.mt + (s.bf16 ? ssd::bwd_cb_bytes(s) : 0));
@@ -632,8 +632,7 @@ ssd_status ssd_chunked_bwd(const void *x, const float *dt, const float *A, const
     }
     if (r != SSD_OK) return r;
     ssd::BwdArgs a{x, B, C, A, D, dy, dfinal, fin, dinit, dx, ddt, dA, dB, dC, dD, w.G, w.DT,
-                   w.S, hp32, reinterpret_cast<float *>(base + l.cb),
-                   s.bf16 ? reinterpret_cast<float *>(base + l.cbt) : nullptr,
+                   w.S, hp32, s.bf16 ? nullptr : reinterpret_cast<float *>(base + l.cb),
                    reinterpret_cast<float *>(base + l.tok),
                    s.bf16 ? reinterpret_cast<uint16_t *>(base + l.cb3) : nullptr,
                    s.bf16 ? reinterpret_cast<uint16_t *>(base + l.cbt3) : nullptr,

@@ -79,8 +79,9 @@ hipError_t launch_decode_lowp(const Shape &s, const LowpArgs &a, hipStream_t st)
 
 // The backward of the chunked forward.  G, DT, hprev and fin come from the
 // forward stages run again on the same workspace; S (the forward's S region,
-// dead by then) receives the chunk adjoints; CB (and CBT), tok (3 planes of
-// Bt*H*nc*L floats) and part (3 * Bt*H doubles) are backward scratch.
+// dead by then) receives the chunk adjoints; CB (fp32 io) or CB3/CBT3 (bf16
+// io), MT, tok (3 planes of Bt*H*nc*L floats) and part (3 * Bt*H doubles) are
+// backward scratch.
 struct BwdArgs {
     const void *x, *B, *C;
     const float *A, *D, *dy, *dfinal, *fin;
@@ -88,8 +89,8 @@ struct BwdArgs {
     const float *G, *DT;
     float *S;
     const void *hprev;
-    float *CB, *CBT, *tok;   // CBT: CB transposed, bf16 io only (NULL otherwise)
-    uint16_t *CB3, *CBT3;    // CB and CBT as three bf16 terms each, bf16 io only
+    float *CB, *tok;         // CB: C B^T in fp32, fp32 io only (NULL otherwise)
+    uint16_t *CB3, *CBT3;    // C B^T and its transpose as three bf16 terms each, bf16 io only
     float *MT;               // the dB/dC matrix M, transposed, bf16 io only
     double *part;
     bool ghat_ready;         // S already holds ghat and dinit is written (launch_state_adj)
