@@ -1509,59 +1509,53 @@ __global__ __launch_bounds__(256) void bwd_scalars_kernel(
     const float *__restrict__ tok, const float *__restrict__ DTws, const float *__restrict__ A,
     const double *__restrict__ bnd, float *__restrict__ ddt, double *__restrict__ part,
     int64_t T, int32_t H, int32_t nc, int64_t ntok, int64_t nbh) {
-    constexpr int KB = 16;                         // tokens per load batch
-    __shared__ double seg[2][256];
+    // tiles of 1024 tokens from the last to the first; a thread takes 4
+    // consecutive tokens of a tile (one 16-byte load per plane, coalesced), the
+    // tile's 256 segment sums are suffix-scanned in parallel, and the running
+    // carry holds the boundary term plus everything after the tile
+    constexpr int TT = 1024;
+    __shared__ double sc[2][256];
     __shared__ double red[2][256];
     const int64_t bh = blockIdx.x;
     const int64_t b = bh / H;
     const int32_t h = (int32_t)(bh % H);
     const int tid = threadIdx.x;
-    const int64_t per = (T + 255) / 256;
-    const int64_t t0 = (int64_t)tid * per, t1 = t0 + per < T ? t0 + per : T;
-    const float *xu = tok + bh * nc * L, *r = tok + ntok + bh * nc * L,
-                *dyx = tok + 2 * ntok + bh * nc * L, *DT = DTws + bh * nc * L;
-    // this thread's segment [t0, t1) in batches of KB tokens whose loads are
-    // all issued before any is used
-    double sum = 0.0;
-    for (int64_t bs = t0; bs < t1; bs += KB) {
-        float rv[KB];
-#pragma unroll
-        for (int i = 0; i < KB; ++i) rv[i] = bs + i < t1 ? r[bs + i] : 0.f;
-#pragma unroll
-        for (int i = 0; i < KB; ++i) sum += (double)rv[i];
-    }
-    // exclusive suffix sums over the segments (fixed order: a Hillis-Steele
-    // scan), starting from the boundary term
-    seg[0][tid] = sum;
-    __syncthreads();
-    int cur = 0;
-    for (int d = 1; d < 256; d <<= 1) {
-        const double v = seg[cur][tid] + (tid + d < 256 ? seg[cur][tid + d] : 0.0);
-        seg[cur ^ 1][tid] = v;
-        cur ^= 1;
-        __syncthreads();
-    }
+    const int64_t Tp = (int64_t)nc * L;             // padded tokens: r, x.U, dy.x, dt are 0
+    const float *xu = tok + bh * Tp, *r = tok + ntok + bh * Tp, *dyx = tok + 2 * ntok + bh * Tp,
+                *DT = DTws + bh * Tp;
     const double Ah = (double)A[h];
-    double s = bnd[bh] + (tid + 1 < 256 ? seg[cur][tid + 1] : 0.0), da = 0.0, dd = 0.0;
-    for (int64_t be = t1; be > t0; be -= KB) {
-        const int64_t bs = be - KB;
-        float rv[KB], xv[KB], dv[KB], yv[KB];
-#pragma unroll
-        for (int i = 0; i < KB; ++i) {
-            const bool ok = bs + i >= t0;
-            rv[i] = ok ? r[bs + i] : 0.f;
-            xv[i] = ok ? xu[bs + i] : 0.f;
-            dv[i] = ok ? DT[bs + i] : 0.f;
-            yv[i] = ok ? dyx[bs + i] : 0.f;
+    double carry = bnd[bh], da = 0.0, dd = 0.0;
+    for (int64_t tl = (Tp + TT - 1) / TT - 1; tl >= 0; --tl) {
+        const int64_t t0 = tl * TT + 4 * tid;
+        float4 rv = make_float4(0.f, 0.f, 0.f, 0.f), xv = rv, dv = rv, yv = rv;
+        if (t0 < Tp) {                               // Tp is a multiple of 64
+            rv = *reinterpret_cast<const float4 *>(r + t0);
+            xv = *reinterpret_cast<const float4 *>(xu + t0);
+            dv = *reinterpret_cast<const float4 *>(DT + t0);
+            yv = *reinterpret_cast<const float4 *>(dyx + t0);
         }
-#pragma unroll
-        for (int i = KB - 1; i >= 0; --i) {
-            if (bs + i < t0) break;
-            s += (double)rv[i];
-            ddt[(b * T + bs + i) * H + h] = (float)((double)xv[i] + Ah * s);
-            da += (double)dv[i] * s;
-            dd += (double)yv[i];
+        const double rr[4] = {rv.x, rv.y, rv.z, rv.w}, xx[4] = {xv.x, xv.y, xv.z, xv.w},
+                     dtt[4] = {dv.x, dv.y, dv.z, dv.w}, yy[4] = {yv.x, yv.y, yv.z, yv.w};
+        sc[0][tid] = ((rr[0] + rr[1]) + rr[2]) + rr[3];
+        __syncthreads();
+        int cur = 0;
+        for (int d = 1; d < 256; d <<= 1) {         // inclusive suffix sums (Hillis-Steele)
+            const double v = sc[cur][tid] + (tid + d < 256 ? sc[cur][tid + d] : 0.0);
+            sc[cur ^ 1][tid] = v;
+            cur ^= 1;
+            __syncthreads();
         }
+        double s = carry + (tid + 1 < 256 ? sc[cur][tid + 1] : 0.0);
+        const double total = sc[cur][0];
+#pragma unroll
+        for (int i = 3; i >= 0; --i) {
+            s += rr[i];
+            if (t0 + i < T) ddt[(b * T + t0 + i) * H + h] = (float)(xx[i] + Ah * s);
+            da += dtt[i] * s;
+            dd += yy[i];
+        }
+        carry += total;
+        __syncthreads();                             // sc is rewritten by the next tile
     }
     red[0][tid] = da;
     red[1][tid] = dd;
