@@ -285,9 +285,7 @@ __global__ __launch_bounds__(256) void fill_f64_kernel(double *__restrict__ p, i
 template <int L, int N, typename Tio>
 __global__ __launch_bounds__(256) void bwd_cb_kernel(const Tio *__restrict__ B,
                                                      const Tio *__restrict__ C,
-                                                     float *__restrict__ CB,
-                                                     uint16_t *__restrict__ CB3,
-                                                     uint16_t *__restrict__ CBT3, int64_t T,
+                                                     float *__restrict__ CB, int64_t T,
                                                      int32_t G, int32_t nc) {
     constexpr int NB = L / 64, NTRI = NB * (NB + 1) / 2;
     __shared__ __align__(16) float As[KT * LD];
@@ -316,36 +314,77 @@ __global__ __launch_bounds__(256) void bwd_cb_kernel(const Tio *__restrict__ B,
         __syncthreads();
         mm_acc<4, 4>(acc, As, LD, Bs, LD, m0, n0);
     }
-    if (CB) {    // fp32 (fp32 io)
-        float *o = CB + bcg * (int64_t)(L * L) + (int64_t)(64 * kb + m0) * L + 64 * jb + n0;
+    float *o = CB + bcg * (int64_t)(L * L) + (int64_t)(64 * kb + m0) * L + 64 * jb + n0;
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            *reinterpret_cast<float4 *>(o + i * L) =
-                make_float4(acc[i][0], acc[i][1], acc[i][2], acc[i][3]);
-    }
-    if (CB3) {   // both as three bf16 terms, [term][bcg][row][col]
-        const int64_t plane = (int64_t)gridDim.x / NTRI * L * L;   // Bt*nc*G*L*L
-        const int64_t base = bcg * (int64_t)(L * L);
+    for (int i = 0; i < 4; ++i)
+        *reinterpret_cast<float4 *>(o + i * L) =
+            make_float4(acc[i][0], acc[i][1], acc[i][2], acc[i][3]);
+}
+
+// ---- bwd_cb_mfma (bf16 io): C B^T and its transpose as three bf16 terms each,
+// [term][bcg][row][col], for the 64x64 blocks on or below the diagonal (the
+// diagonal blocks whole).  B and C are exact bf16, so the MFMA's fp32 sums are
+// the fp32 products' sums.  Wavefront w takes rows k = 64 kb + 16 w .. +15
+// against the four 16-column tiles of block jb; each tile is formed both ways
+// (C B^T and B C^T), so that each layout leaves the D registers as 4
+// consecutive elements of one row per lane (8-byte stores per term).
+template <int L, int N>
+__global__ __launch_bounds__(256) void bwd_cb_mfma_kernel(const uint16_t *__restrict__ B,
+                                                          const uint16_t *__restrict__ C,
+                                                          uint16_t *__restrict__ CB3,
+                                                          uint16_t *__restrict__ CBT3, int64_t T,
+                                                          int32_t G, int32_t nc) {
+    constexpr int NB = L / 64, NTRI = NB * (NB + 1) / 2, NK = N / 32;
+    const int64_t blk = blockIdx.x;
+    int tri = (int)(blk % NTRI);
+    const int64_t bcg = blk / NTRI;                // (b*nc + c)*G + g
+    const int32_t g = (int32_t)(bcg % G);
+    const int64_t bc = bcg / G;
+    const int32_t c = (int32_t)(bc % nc);
+    const int64_t b = bc / nc;
+    int kb = 0;
+    while (tri > kb) { tri -= kb + 1; ++kb; }
+    const int jb = tri;                             // jb <= kb
+    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int m = lane & 15, q = lane >> 4;
+    const int64_t tc = (int64_t)c * L;
+    const int k0 = 64 * kb + 16 * w;
+    const int64_t tk = tc + k0 + m;
+    bf16x8 ca[NK];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            uint32_t s0a, s1a, s2a, s0b, s1b, s2b;
-            split2x3(acc[i][0], acc[i][1], s0a, s1a, s2a);
-            split2x3(acc[i][2], acc[i][3], s0b, s1b, s2b);
-            const int64_t o = base + (int64_t)(64 * kb + m0 + i) * L + 64 * jb + n0;
-            *reinterpret_cast<uint2 *>(CB3 + o) = make_uint2(s0a, s0b);
-            *reinterpret_cast<uint2 *>(CB3 + plane + o) = make_uint2(s1a, s1b);
-            *reinterpret_cast<uint2 *>(CB3 + 2 * plane + o) = make_uint2(s2a, s2b);
+    for (int ks = 0; ks < NK; ++ks)
+        ca[ks] = as_bf16x8(tk < T ? *reinterpret_cast<const uint4 *>(C + ((b * T + tk) * G + g) * N + 32 * ks + 8 * q)
+                                  : make_uint4(0u, 0u, 0u, 0u));
+    const int64_t plane = (int64_t)gridDim.x / NTRI * L * L;   // Bt*nc*G*L*L
+    const int64_t base = bcg * (int64_t)(L * L);
+#pragma unroll
+    for (int jt = 0; jt < 4; ++jt) {
+        const int j0 = 64 * jb + 16 * jt;
+        const int64_t tj = tc + j0 + m;
+        f32x4 d = f32x4{0.f, 0.f, 0.f, 0.f}, dtr = d;
+#pragma unroll
+        for (int ks = 0; ks < NK; ++ks) {
+            const bf16x8 bv = as_bf16x8(
+                tj < T ? *reinterpret_cast<const uint4 *>(B + ((b * T + tj) * G + g) * N + 32 * ks + 8 * q)
+                       : make_uint4(0u, 0u, 0u, 0u));
+            d = mfma16x16x32(ca[ks], bv, d);       // rows k, column j
+            dtr = mfma16x16x32(bv, ca[ks], dtr);   // rows j, column k
         }
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            uint32_t s0a, s1a, s2a, s0b, s1b, s2b;
-            split2x3(acc[0][j], acc[1][j], s0a, s1a, s2a);
-            split2x3(acc[2][j], acc[3][j], s0b, s1b, s2b);
-            const int64_t o = base + (int64_t)(64 * jb + n0 + j) * L + 64 * kb + m0;
-            *reinterpret_cast<uint2 *>(CBT3 + o) = make_uint2(s0a, s0b);
-            *reinterpret_cast<uint2 *>(CBT3 + plane + o) = make_uint2(s1a, s1b);
-            *reinterpret_cast<uint2 *>(CBT3 + 2 * plane + o) = make_uint2(s2a, s2b);
-        }
+        uint32_t s0a, s1a, s2a, s0b, s1b, s2b;
+        // CBT3[j = j0 + m][k = k0 + 4q .. +3]
+        split2x3(d[0], d[1], s0a, s1a, s2a);
+        split2x3(d[2], d[3], s0b, s1b, s2b);
+        int64_t o = base + (int64_t)(j0 + m) * L + k0 + 4 * q;
+        *reinterpret_cast<uint2 *>(CBT3 + o) = make_uint2(s0a, s0b);
+        *reinterpret_cast<uint2 *>(CBT3 + plane + o) = make_uint2(s1a, s1b);
+        *reinterpret_cast<uint2 *>(CBT3 + 2 * plane + o) = make_uint2(s2a, s2b);
+        // CB3[k = k0 + m][j = j0 + 4q .. +3]
+        split2x3(dtr[0], dtr[1], s0a, s1a, s2a);
+        split2x3(dtr[2], dtr[3], s0b, s1b, s2b);
+        o = base + (int64_t)(k0 + m) * L + j0 + 4 * q;
+        *reinterpret_cast<uint2 *>(CB3 + o) = make_uint2(s0a, s0b);
+        *reinterpret_cast<uint2 *>(CB3 + plane + o) = make_uint2(s1a, s1b);
+        *reinterpret_cast<uint2 *>(CB3 + 2 * plane + o) = make_uint2(s2a, s2b);
     }
 }
 
@@ -1615,8 +1654,12 @@ hipError_t launch_bwd_t(const Shape &s, const BwdArgs &a, hipStream_t st) {
     if (units > 0) {
         constexpr int NTRI = (L / 64) * (L / 64 + 1) / 2;
         const uint64_t ncb = (uint64_t)s.Bt * s.nc * s.G;
-        hipLaunchKernelGGL((bwd_cb_kernel<L, N, Tio>), dim3((uint32_t)(ncb * NTRI)), dim3(256), 0,
-                           st, B, C, a.CB, a.CB3, a.CBT3, T, G, nc);
+        if constexpr (sizeof(Tio) == 2)
+            hipLaunchKernelGGL((bwd_cb_mfma_kernel<L, N>), dim3((uint32_t)(ncb * NTRI)), dim3(256),
+                               0, st, B, C, a.CB3, a.CBT3, T, G, nc);
+        else
+            hipLaunchKernelGGL((bwd_cb_kernel<L, N, Tio>), dim3((uint32_t)(ncb * NTRI)), dim3(256),
+                               0, st, B, C, a.CB, T, G, nc);
         if constexpr (sizeof(Tio) == 2)
             hipLaunchKernelGGL((bwd_dx_mfma_kernel<L, N>), dim3((uint32_t)units),
                                dim3(4 * L), 0, st, x, B, C, a.D, a.dy, a.G, a.DT, a.CB3,
