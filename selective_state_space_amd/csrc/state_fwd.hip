@@ -47,10 +47,10 @@
 // "mamba3" kernel card, section "Backward"): chunks last to first,
 //     ghat[c] = g;   g <- exp2(G_last,c) g + sum_k (dy_k exp2(G_k)) C_k^T;
 //     dinit = g,
-// with dy (fp32) in place of x -- its weighted values carried as three bf16
-// terms, the adjoint feeding dA through long sums -- C fragments in place of
-// B, dfinal as the initial state, and ghat stored in fp32.  Every exponent is
-// again <= 0.
+// with dy (fp32) in place of x -- its weighted values carried, like x*w, as a
+// bf16 head and remainder (a third term left the full-size dA where it was) --
+// C fragments in place of B, dfinal as the initial state, and ghat stored in
+// fp32.  Every exponent is again <= 0.
 
 #include "ssd_device.h"
 #include "ssd_launch.h"
@@ -210,7 +210,7 @@ __global__ __launch_bounds__(256, 2) void state_fwd_kernel(FwdArgs a, uint32_t n
     constexpr int NT = N / 16;
     constexpr int R = NS < 4 ? NS : 4;   // B ring depth (slabs in flight)
     constexpr bool ADJ = MODE == kModeAdjoint, HP32 = MODE != kModeBf16;
-    constexpr int NTERM = ADJ ? 3 : 2;   // bf16 terms of the x*w (dy*w) operand
+    constexpr int NTERM = 2;             // bf16 terms of the x*w (dy*w) operand
     constexpr int ES = ADJ ? 4 : 2;      // bytes per element of x (dy)
     using XP = typename XPiece<ADJ && SPB == 4>::type;
     __shared__ FwdSmem<L, SPB, NTERM> sm;
