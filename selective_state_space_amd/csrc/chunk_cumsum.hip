@@ -20,7 +20,7 @@
 // One workgroup of 256 threads per (b, chunk, block of 32 heads).  dt rows of
 // 32 heads (128 bytes) are read with 16-byte loads, transposed through LDS, and
 // each wavefront then scans 8 heads: a lane sums L/64 tokens serially, a wave-wide
-// log-depth scan (6 shuffle steps) combines the lane totals, and each lane
+// log-depth scan (six DPP steps) combines the lane totals, and each lane
 // adds its exclusive prefix back.
 
 #include "ssd_device.h"
@@ -98,12 +98,7 @@ __global__ __launch_bounds__(256) void chunk_cumsum_kernel(
             g[v] = run;
         }
         // inclusive scan of the lane totals across the wavefront
-        float incl = run;
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-            const float o = __shfl_up(incl, off, 64);
-            if (lane >= off) incl += o;
-        }
+        const float incl = wave_inclusive_sum(run);
         const float excl = incl - run;
         const int64_t base = (((int64_t)b * H + h) * nc + c) * L + lane * V;
         if constexpr (V == 4) {

@@ -145,6 +145,19 @@ __device__ __forceinline__ float group_sum(float v) {
     if constexpr (LPR == 32) v += dpp_mov<0x142, 0xa>(v);   // row_bcast:15 into rows 1, 3
     return v;
 }
+// Inclusive prefix sum over the 64 lanes of a wavefront by DPP moves: shifts
+// by 1, 2, 4 and 8 lanes inside each 16-lane row (lanes shifted in read 0),
+// then row_bcast:15 carries each even row's total into the row after it and
+// row_bcast:31 the first half's total into the second half.
+__device__ __forceinline__ float wave_inclusive_sum(float v) {
+    v += dpp_mov<0x111>(v);         // row_shr:1
+    v += dpp_mov<0x112>(v);         // row_shr:2
+    v += dpp_mov<0x114>(v);         // row_shr:4
+    v += dpp_mov<0x118>(v);         // row_shr:8
+    v += dpp_mov<0x142, 0xa>(v);    // row_bcast:15 into rows 1, 3
+    v += dpp_mov<0x143, 0xc>(v);    // row_bcast:31 into rows 2, 3
+    return v;
+}
 // The maximum over each group of LPR = 16 or 32 lanes, in every lane of it:
 // the same DPP steps within 16-lane rows, then one swap of neighbouring rows.
 template <int LPR>
