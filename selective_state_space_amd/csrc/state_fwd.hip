@@ -208,8 +208,9 @@ __global__ __launch_bounds__(256, 2) void state_fwd_kernel(FwdArgs a, uint32_t n
     constexpr int P = 64, NS = Cfg::NS, HS = Cfg::HS, SW = Cfg::SW, TW = Cfg::TW;
     constexpr int PSPLIT = 4 / SPB;
     constexpr int NT = N / 16;
-    constexpr int R = NS < 4 ? NS : 4;   // B ring depth (slabs in flight)
     constexpr bool ADJ = MODE == kModeAdjoint, HP32 = MODE != kModeBf16;
+    constexpr int RD = ADJ ? 2 : 4;
+    constexpr int R = NS < RD ? NS : RD;   // B ring depth (slabs in flight)
     constexpr int NTERM = 2;             // bf16 terms of the x*w (dy*w) operand
     constexpr int ES = ADJ ? 4 : 2;      // bytes per element of x (dy)
     using XP = typename XPiece<ADJ && SPB == 4>::type;
