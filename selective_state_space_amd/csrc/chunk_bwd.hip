@@ -1062,7 +1062,7 @@ __global__ __launch_bounds__(64 * WPB) void bwd_db_mfma_kernel(
 // One (b, c, h) per workgroup of L/16 wavefronts, wavefront w owning rows
 // 16w .. 16w+15, so each head's operands are staged once and the causal work
 // per wavefront is the same (U takes k >= i, Y takes j <= i); MFMA layouts
-// as for bwd_dbdc_mfma.  Products (K in brackets):
+// as for bwd_dc_mfma.  Products (K in brackets):
 //   U_intra(i, p) = sum_{k >= i} W(k, i) dy_k[p]    [k]  W(k, i) = exp2(G_k - G_i) CB(k, i)
 //   Y_intra(i, p) = sum_{j <= i} V(i, j) x_j[p]     [j]  V(i, j) = exp2(G_i - G_j) CB(i, j) dt_j
 //   U_inter(i, p) = sum_n B_i[n] ghat[p][n]         [n]
@@ -1455,7 +1455,7 @@ __global__ __launch_bounds__(4 * L) void bwd_dx_mfma_kernel(
 // have K = token, so each 64-token chunk is staged transposed into LDS with
 // 32-bit pair writes: (exp2(G) dy)^T in three bf16 terms (the adjoint it
 // feeds reaches dx, ddt and dA) and C^T (bf16 already).  Three MFMAs per
-// step; layouts as for bwd_dbdc_mfma.
+// step; layouts as for bwd_dc_mfma.
 template <int L, int N>
 __global__ __launch_bounds__(256) void bwd_dstate_mfma_kernel(const float *__restrict__ dy,
                                                               const uint16_t *__restrict__ C,
