@@ -17,9 +17,9 @@
 // dt <- dt + dt_bias_h, then dt <- log(1 + e^dt) where dt <= 20.  DT then
 // holds the effective step, so the later stages need no change.
 //
-// One workgroup of 256 threads per (b, chunk, block of 32 heads).  dt rows of
-// 32 heads (128 bytes) are read with 16-byte loads, transposed through LDS, and
-// each wavefront then scans 8 heads: a lane sums L/64 tokens serially, a wave-wide
+// One workgroup of 256 threads per (b, chunk, block of 16 heads).  dt rows of
+// 16 heads (64 bytes) are read with 16-byte loads, transposed through LDS, and
+// each wavefront then scans 4 heads: a lane sums L/64 tokens serially, a wave-wide
 // log-depth scan (six DPP steps) combines the lane totals, and each lane
 // adds its exclusive prefix back.
 
@@ -30,7 +30,7 @@ namespace ssd {
 
 namespace {
 
-constexpr int kHeadsPerBlock = 32;
+constexpr int kHeadsPerBlock = 16;
 
 template <int L>
 __global__ __launch_bounds__(256) void chunk_cumsum_kernel(
@@ -47,14 +47,15 @@ __global__ __launch_bounds__(256) void chunk_cumsum_kernel(
     const int32_t h0 = hb * kHeadsPerBlock;
     const int tid = threadIdx.x;
 
-    // coalesced load of dt[b, c*L + t, h0 .. h0+31]: 8 threads cover one
-    // 128-byte token row with 16-byte loads (when rows are 16-byte aligned)
+    // coalesced load of dt[b, c*L + t, h0 .. h0+KH-1]: KH/4 threads cover one
+    // token row with 16-byte loads (when rows are 16-byte aligned)
     {
-        const int c4 = (tid & 7) * 4;
+        constexpr int TPR = kHeadsPerBlock / 4, RPP = 256 / TPR;   // threads per row, rows per pass
+        const int c4 = (tid % TPR) * 4;
         const bool vec = (H & 3) == 0;
 #pragma unroll
-        for (int k = 0; k < L / 32; ++k) {
-            const int t = (tid >> 3) + 32 * k;
+        for (int k = 0; k < L / RPP; ++k) {
+            const int t = tid / TPR + RPP * k;
             const int64_t tg = (int64_t)c * L + t;
             float v[4] = {0.f, 0.f, 0.f, 0.f};
             if (tg < T) {
