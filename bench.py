@@ -233,6 +233,65 @@ def summarize_rocprof(pdir: str, workload: str):
     print("\n".join(md))
 
 
+COUNTER_PASSES = (
+    "SQ_WAVES SQ_WAVE_CYCLES SQ_BUSY_CYCLES SQ_WAIT_ANY SQ_WAIT_INST_ANY SQ_ACTIVE_INST_VALU "
+    "SQ_ACTIVE_INST_LDS SQ_ACTIVE_INST_MISC",
+    "SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_VALU SQ_INSTS_MFMA SQ_INSTS_LDS SQ_INSTS_VMEM_RD "
+    "SQ_INSTS_VMEM_WR SQ_LDS_BANK_CONFLICT SQ_WAIT_INST_LDS",
+)
+
+
+def summarize_counters(pdir: str, workload: str):
+    """Writes profiles/counters_<workload>.md from rocprofv3 SQ-counter passes:
+    <pdir>/{fwd,bwd}{1,2}/c_counter_collection.csv, the passes of COUNTER_PASSES
+    over the forward (PROFILE_CMD) and over --backward-only."""
+    import collections
+    import csv
+    import re
+    cmds = {"fwd": PROFILE_CMD, "bwd": "python3 bench.py --backward-only"}
+    keep = re.compile(r"chunk_scan_bf16_kernel<256, 128, false>|state_fwd_kernel<256, 128, 4, [012]>|"
+                      r"chunk_cumsum|bwd_\w+_kernel")
+    out = ["# SQ counters per kernel: %s" % workload, "",
+           "Two counter passes (rocprofv3 takes at most 8 SQ counters per pass) for each of",
+           "the forward and the backward, from the repo root on one MI355X:", ""]
+    for leg in ("fwd", "bwd"):
+        for i, pas in enumerate(COUNTER_PASSES, 1):
+            out.append("    rocprofv3 --pmc %s -f csv -d <dir>/%s%d -o c -- %s" % (pas, leg, i, cmds[leg]))
+    out += ["", "Means over the launches of each kernel (the counters sum over the chip;",
+            "WAVE_CYCLES and the WAIT/ACTIVE counters are in the same units, so their",
+            "ratios are the shares of wave time).  `python3 bench.py --summarize-counters",
+            "<dir>` wrote this file.", ""]
+    for leg in ("fwd", "bwd"):
+        vals = collections.defaultdict(dict)
+        for i in (1, 2):
+            per = collections.defaultdict(float)
+            for r in csv.DictReader(open(os.path.join(pdir, "%s%d" % (leg, i), "c_counter_collection.csv"))):
+                per[(r["Kernel_Name"], r["Dispatch_Id"], r["Counter_Name"])] += float(r["Counter_Value"])
+            agg = collections.defaultdict(list)
+            for (k, d, c), v in per.items():
+                agg[(k, c)].append(v)
+            for (k, c), vs in agg.items():
+                vals[k][c] = sum(vs) / len(vs)
+        out += ["## %s" % ("forward" if leg == "fwd" else "backward"), "",
+                "| kernel | wave cycles | wait (memory, barrier) | wait (dependency) | VALU issue | "
+                "MFMA busy / SIMD | LDS conflict cycles |", "|---|---|---|---|---|---|---|"]
+        for k in sorted(vals):
+            m = keep.search(k)
+            if not m:
+                continue
+            v = vals[k]
+            wc = v.get("SQ_WAVE_CYCLES", 0.0) or 1.0
+            name = re.sub(r"\(.*", "", k.replace("ssd::(anonymous namespace)::", "").replace("void ", ""))
+            out.append("| %s | %.3g | %.0f%% | %.0f%% | %.0f%% | %.3g | %.3g |" % (
+                name.replace("unsigned short", "bf16"), wc, 100 * v.get("SQ_WAIT_ANY", 0) / wc,
+                100 * v.get("SQ_WAIT_INST_ANY", 0) / wc, 100 * v.get("SQ_ACTIVE_INST_VALU", 0) / wc,
+                v.get("SQ_VALU_MFMA_BUSY_CYCLES", 0) / 1024, v.get("SQ_LDS_BANK_CONFLICT", 0)))
+        out.append("")
+    with open(os.path.join(ROOT, "profiles", "counters_%s.md" % workload), "w") as fh:
+        fh.write("\n".join(out) + "\n")
+    print("\n".join(out))
+
+
 # ---- the GPU legs ----------------------------------------------------------------------
 
 def run_forward(w, steps: int, warmup: int):
@@ -593,12 +652,19 @@ def main():
     ap.add_argument("--summarize-rocprof", metavar="DIR",
                     help="write the profiles/ summaries from a rocprofv3 output directory "
                          "(host only, no GPU)")
+    ap.add_argument("--summarize-counters", metavar="DIR",
+                    help="write profiles/counters_<workload>.md from SQ-counter passes (host only)")
+    ap.add_argument("--backward-only", action="store_true",
+                    help="only the backward leg (for profiling): prints its mean time per call")
     ap.add_argument("--copy-reference-only", action="store_true",
                     help="only the 1 GiB device copy (calibrates HBM byte counters)")
     args = ap.parse_args()
 
     if args.summarize_rocprof:
         summarize_rocprof(args.summarize_rocprof, args.workload)
+        return
+    if args.summarize_counters:
+        summarize_counters(args.summarize_counters, args.workload)
         return
     if args.gpus != 1:
         print("bench.py measures one GPU only (a single MI355X; there is no multi-GPU "
@@ -619,6 +685,11 @@ def main():
     ssd.load_library()   # fails loudly if libssd.so is missing
 
     w = gen.BY_NAME[args.workload]
+    if args.backward_only:
+        bms = run_backward(w, 10, 3)
+        print(json.dumps({"workload": w.name, "backward_us_per_call": round(bms * 1e3, 2)}),
+              flush=True)
+        return
     io_bytes = 2 if w.io_dtype == gen.BF16 else 4
     log("workload %s: %s" % (w.name, w.description))
 
