@@ -69,6 +69,17 @@ def test_state_stage_paths(monkeypatch, fwd_rows, adj_rows, L):
     compare(g, ref, gen.BF16)
 
 
+def test_long_context_layout():
+    """The long-context layer's head layout (128 heads in 8 groups of 16, N 128,
+    chunk 256, bf16, one sequence) over its first 4096 tokens: every gradient,
+    dB and dC summed over 16 heads per group."""
+    log("bwd long-context layout, 4096 tokens")
+    inp = gen.make_small(1, 4096, 128, 64, 128, 8, gen.BF16, init_state=False, seed=12)
+    dy, dfin = grads_inputs(inp, 7)
+    g, ref = run_both(inp, gen.BF16, 256, dy, dfin)
+    compare(g, ref, gen.BF16)
+
+
 @pytest.mark.parametrize("G", [1, 2, 8])
 def test_group_counts(G):
     """dB and dC sum over the heads of a group: 8, 4 and 1 heads per group."""
