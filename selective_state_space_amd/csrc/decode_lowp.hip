@@ -75,11 +75,11 @@ __device__ __forceinline__ uint32_t f32_to_half_sr(float x, uint32_t r) {
     // added random bits is the round away from zero
     const uint32_t ut = (ua + r) & ~0x1FFFu;
     const uint32_t hn = ut >= 0x47800000u ? 0x7BFFu : (ut >> 13) - (112u << 10);
-    // below, fp16 is subnormal: whole units of 2^-24 plus a fraction
-    const float A = __uint_as_float(ua) * 0x1p24f;   // exact, < 1024
-    const float n = floorf(A);
-    const float f8 = (A - n) * 8192.f;               // exact
-    const uint32_t hs = (uint32_t)n + (f8 >= (float)(8192u - r) ? 1u : 0u);
+    // below, fp16 is subnormal: with |x| 2^24 = n + f (n whole, 0 <= f < 1) the
+    // result is n units of 2^-24, or n + 1 where f 2^13 >= 2^13 - r, that is
+    // floor((floor(|x| 2^37) + r) / 2^13) (|x| 2^37 < 2^23 is exact in fp32 and
+    // the conversion truncates; a carry into 2^10 units is the smallest normal)
+    const uint32_t hs = ((uint32_t)(__uint_as_float(ua) * 0x1p37f) + r) >> 13;
     return (ua >= 0x38800000u ? hn : hs) | sgn;
 }
 
