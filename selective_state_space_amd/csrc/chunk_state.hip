@@ -194,7 +194,9 @@ __device__ __forceinline__ void chunk_state_group(StateSmem<L, N> &sm, const Sta
                 }
         }
         // D layout: lane holds rows M = 4q + e of column m: p = 4M + s,
-        // n = 64 (nt / 4) + 4m + nt % 4; the TPW n-tiles are adjacent columns
+        // n = 64 (nt / 4) + 4m + nt % 4; the TPW n-tiles are adjacent columns.
+        // Plain stores: state_passing reads S next, and what it finds in the
+        // memory-side cache is not read from HBM again.
         const int64_t bhc = ((int64_t)b * a.H + h) * a.nc + c;
         float *Sp = a.S + bhc * (int64_t)(P * N) + 64 * (nt0 >> 2) + 4 * m + (nt0 & 3);
 #pragma unroll
@@ -203,10 +205,10 @@ __device__ __forceinline__ void chunk_state_group(StateSmem<L, N> &sm, const Sta
             for (int e = 0; e < 4; ++e) {
                 const int p = 4 * (4 * q + e) + 2 * sp + i;
                 if constexpr (TPW == 4)
-                    store_nt(Sp + p * N,
-                             make_float4(acc[i][0][e], acc[i][1][e], acc[i][2][e], acc[i][3][e]));
+                    *reinterpret_cast<float4 *>(Sp + p * N) =
+                        make_float4(acc[i][0][e], acc[i][1][e], acc[i][2][e], acc[i][3][e]);
                 else
-                    store_nt(Sp + p * N, make_float2(acc[i][0][e], acc[i][1][e]));
+                    *reinterpret_cast<float2 *>(Sp + p * N) = make_float2(acc[i][0][e], acc[i][1][e]);
             }
         if (hh + 1 < nh) w_store((hh + 1) & 1, pre);
         __syncthreads();   // AF is rewritten for the next head

@@ -155,9 +155,12 @@ __device__ __forceinline__ void store_f(float *p, const float *v) {
     else if constexpr (K == 2) *reinterpret_cast<float2 *>(p) = make_float2(v[0], v[1]);
     else *p = v[0];
 }
+// Plain (not streaming) stores: chunk_scan reads h_prev right after this
+// kernel, and lines left in the memory-side cache spare it that re-read from
+// HBM (measured: the 2.7B forward takes 5% less time than with streaming stores).
 template <int K>
 __device__ __forceinline__ void store_bf(uint16_t *p, const float *v) {
-    if constexpr (K == 4) store_nt(p, make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])));
+    if constexpr (K == 4) *reinterpret_cast<uint2 *>(p) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
     else if constexpr (K == 2) *reinterpret_cast<uint32_t *>(p) = pack_bf16x2(v[0], v[1]);
     else *p = (uint16_t)f32_to_bf16_bits(v[0]);
 }

@@ -61,14 +61,16 @@ __global__ __launch_bounds__(256) void state_passing_kernel(
                     sbuf[k] = load_nt(Sb + (int64_t)(c + kPF) * PN);
                     gbuf[k] = Gl[(int64_t)(c + kPF) * L];
                 }
+                // plain stores: chunk_scan reads h_prev next, and what it
+                // finds in the memory-side cache is not read from HBM again
                 const int64_t off = (bh * (int64_t)nc + c) * PN + e;
                 if constexpr (BF16) {
                     uint2 v;
                     v.x = pack_bf16x2(h.x, h.y);
                     v.y = pack_bf16x2(h.z, h.w);
-                    store_nt(static_cast<uint16_t *>(hprev) + off, v);
+                    *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(hprev) + off) = v;
                 } else {
-                    store_nt(static_cast<float *>(hprev) + off, h);
+                    *reinterpret_cast<float4 *>(static_cast<float *>(hprev) + off) = h;
                 }
                 h.x = dec * h.x + s.x;
                 h.y = dec * h.y + s.y;
