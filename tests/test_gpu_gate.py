@@ -55,7 +55,7 @@ def gated_case(io, Bt, T, H, N, G, L, seed, bias=True, softplus=True, gate=True,
 
 
 @pytest.mark.parametrize("io", [gen.F32, gen.BF16])
-@pytest.mark.parametrize("L,N", [(64, 64), (256, 128)])
+@pytest.mark.parametrize("L,N", [(64, 64), (128, 128), (256, 128)])
 @pytest.mark.parametrize("rows", ["", "0"])
 def test_gated_forward(io, L, N, rows, monkeypatch):
     """rows "" lets the library pick the state path; "0" forces the two-stage one."""
@@ -69,6 +69,18 @@ def test_gated_forward(io, L, N, rows, monkeypatch):
                               n_big=2 if io == gen.F32 else 0)
     assert_close(y, yr, io, "y (gated)")
     assert_close(f, fr, io, "final")
+
+
+@pytest.mark.parametrize("L,N,H", [(128, 64, 256), (256, 128, 128)])
+def test_gated_forward_heads_per_workgroup(L, N, H):
+    """Enough heads per group that each chunk_scan workgroup takes two of them
+    in turn (the gate's LDS buffer is refilled for the second), with a ragged
+    last chunk."""
+    T = 2 * L + 29
+    log("gated forward, two heads per workgroup: L", L, "N", N, "H", H)
+    y, yr, f, fr = gated_case(gen.BF16, 1, T, H, N, 1, L, seed=7 * L + N)
+    assert_close(y, yr, gen.BF16, "y (gated)")
+    assert_close(f, fr, gen.BF16, "final")
 
 
 @pytest.mark.parametrize("opt", ["bias", "softplus", "gate"])
