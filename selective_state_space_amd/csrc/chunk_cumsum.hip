@@ -23,6 +23,7 @@
 // log-depth scan (six DPP steps) combines the lane totals, and each lane
 // adds its exclusive prefix back.
 
+#include "b_fragments.h"
 #include "ssd_device.h"
 #include "ssd_launch.h"
 
@@ -32,15 +33,15 @@ namespace {
 
 constexpr int kHeadsPerBlock = 16;
 
+// One workgroup's share: logical id lid -> (b, chunk, block of heads).
 template <int L>
-__global__ __launch_bounds__(256) void chunk_cumsum_kernel(
+__device__ __forceinline__ void cumsum_block(
     const float *__restrict__ dt, const float *__restrict__ A, float *__restrict__ Gws,
     float *__restrict__ DTws, const float *__restrict__ dt_bias, int32_t softplus, int64_t T,
-    int32_t H, int32_t nc, int32_t nhb, uint32_t nblk) {
+    int32_t H, int32_t nc, int32_t nhb, uint32_t lid) {
     constexpr int V = L / 64;  // tokens per lane
     __shared__ float tile[kHeadsPerBlock][L + 1];
 
-    const uint32_t lid = xcd_remap(blockIdx.x, nblk);
     const int32_t hb = lid % nhb;
     const int32_t c = (lid / nhb) % nc;
     const int64_t b = lid / ((uint32_t)nhb * nc);
@@ -116,13 +117,67 @@ __global__ __launch_bounds__(256) void chunk_cumsum_kernel(
     }
 }
 
+template <int L>
+__global__ __launch_bounds__(256) void chunk_cumsum_kernel(
+    const float *__restrict__ dt, const float *__restrict__ A, float *__restrict__ Gws,
+    float *__restrict__ DTws, const float *__restrict__ dt_bias, int32_t softplus, int64_t T,
+    int32_t H, int32_t nc, int32_t nhb, uint32_t nblk) {
+    cumsum_block<L>(dt, A, Gws, DTws, dt_bias, softplus, T, H, nc, nhb,
+                    xcd_remap(blockIdx.x, nblk));
+}
+
+// The cumsum and the state stage's B fragments in one launch: both are small
+// and independent, so one grid holds both sets of workgroups at once (the
+// first ncum do the cumsum) and the forward pays one kernel boundary less.
+template <int L, int N>
+__global__ __launch_bounds__(256) void cumsum_bfrag_kernel(
+    const float *__restrict__ dt, const float *__restrict__ A, float *__restrict__ Gws,
+    float *__restrict__ DTws, const float *__restrict__ dt_bias, int32_t softplus, int64_t T,
+    int32_t H, int32_t nc, int32_t nhb, uint32_t ncum, const uint16_t *__restrict__ B,
+    uint4 *__restrict__ BF, int32_t G) {
+    if (blockIdx.x < ncum)   // workgroup-uniform
+        cumsum_block<L>(dt, A, Gws, DTws, dt_bias, softplus, T, H, nc, nhb,
+                        xcd_remap(blockIdx.x, ncum));
+    else
+        b_fragments_block<L, N>(B, BF, T, G, nc, (int64_t)(blockIdx.x - ncum));
+}
+
+template <int L>
+hipError_t launch_cumsum_bfrag(const Shape &s, const float *dt, const float *A, float *Gws,
+                               float *DTws, const float *dt_bias, int softplus, int32_t nhb,
+                               uint32_t ncum, const void *B, void *bfrag, hipStream_t st) {
+    const uint64_t nfb = (uint64_t)s.Bt * s.nc * s.G * (L / 32);
+    const dim3 grid((uint32_t)(ncum + nfb)), block(256);
+    auto go = [&](auto kern) {
+        hipLaunchKernelGGL(kern, grid, block, 0, st, dt, A, Gws, DTws, dt_bias,
+                           (int32_t)softplus, s.T, (int32_t)s.H, (int32_t)s.nc, nhb, ncum,
+                           (const uint16_t *)B, (uint4 *)bfrag, (int32_t)s.G);
+    };
+    if (s.N == 64) go(cumsum_bfrag_kernel<L, 64>);
+    else if (s.N == 128) go(cumsum_bfrag_kernel<L, 128>);
+    else return hipErrorInvalidValue;
+    return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_chunk_cumsum(const Shape &s, const float *dt, const float *A, float *Gws,
-                               float *DTws, const float *dt_bias, int softplus, hipStream_t st) {
+                               float *DTws, const float *dt_bias, int softplus, hipStream_t st,
+                               const void *B, void *bfrag) {
     if (s.Bt == 0 || s.nc == 0) return hipSuccess;
     const int32_t nhb = (int32_t)((s.H + kHeadsPerBlock - 1) / kHeadsPerBlock);
     const uint64_t nblk = (uint64_t)s.Bt * s.nc * nhb;
+    if (bfrag) {
+        switch (s.L) {
+        case 64: return launch_cumsum_bfrag<64>(s, dt, A, Gws, DTws, dt_bias, softplus, nhb,
+                                                (uint32_t)nblk, B, bfrag, st);
+        case 128: return launch_cumsum_bfrag<128>(s, dt, A, Gws, DTws, dt_bias, softplus, nhb,
+                                                  (uint32_t)nblk, B, bfrag, st);
+        case 256: return launch_cumsum_bfrag<256>(s, dt, A, Gws, DTws, dt_bias, softplus, nhb,
+                                                  (uint32_t)nblk, B, bfrag, st);
+        default: return hipErrorInvalidValue;
+        }
+    }
     const dim3 grid((uint32_t)nblk), block(256);
     switch (s.L) {
     case 64:

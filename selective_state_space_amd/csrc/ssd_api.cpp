@@ -172,10 +172,13 @@ ssd_status hip_result(hipError_t e, const char *what, hipStream_t st) {
 }
 
 // Stage runners on validated arguments.
+// B non-NULL: also lay B out in w.S for the one-pass state stage (bf16 only).
 ssd_status run_cumsum(const ssd::Shape &s, const float *dt, const float *A, const Ws &w,
-                      hipStream_t st, const ssd_layer_opts *o = nullptr) {
+                      hipStream_t st, const ssd_layer_opts *o = nullptr,
+                      const void *B = nullptr) {
     return hip_result(ssd::launch_chunk_cumsum(s, dt, A, w.G, w.DT, o ? o->dt_bias : nullptr,
-                                               o ? o->dt_softplus : 0, st),
+                                               o ? o->dt_softplus : 0, st, B,
+                                               B ? static_cast<void *>(w.S) : nullptr),
                       "chunk_cumsum", st);
 }
 ssd_status run_state(const ssd::Shape &s, const void *x, const void *B, const Ws &w,
@@ -211,11 +214,12 @@ bool use_state_fwd(const ssd::Shape &s) {
     if (r >= 0) return r > 0;
     return ssd::state_fwd_preferred(s);
 }
+// bfrag_ready: run_cumsum was given B, so w.S already holds its fragments.
 ssd_status run_state_fwd(const ssd::Shape &s, const void *x, const void *B, const float *init,
-                         float *fin, const Ws &w, hipStream_t st) {
+                         float *fin, const Ws &w, hipStream_t st, bool bfrag_ready = false) {
     const int r = state_fwd_rows();
     return hip_result(ssd::launch_state_fwd(s, x, B, w.G, w.DT, init, w.hprev, fin, w.S,
-                                            r > 0 ? r : 0, false, st),
+                                            r > 0 ? r : 0, false, st, bfrag_ready),
                       "state_fwd", st);
 }
 ssd_status run_scan(const ssd::Shape &s, const void *x, const void *B, const void *C,
@@ -374,9 +378,12 @@ ssd_status ssd_chunked_fwd_opts(const void *x, const float *dt, const float *A, 
     if ((r = check_ws(s, workspace, workspace_bytes, &w)) != SSD_OK) return r;
     if (s.Bt == 0) return ok();
     hipStream_t st = static_cast<hipStream_t>(stream);
-    if ((r = run_cumsum(s, dt, A, w, st, opts)) != SSD_OK) return r;
-    if (use_state_fwd(s)) {
-        if ((r = run_state_fwd(s, x, B, init_state, final_state, w, st)) != SSD_OK) return r;
+    const bool one_pass = use_state_fwd(s);
+    // the one-pass state stage's B fragments are built in the cumsum's launch
+    if ((r = run_cumsum(s, dt, A, w, st, opts, one_pass ? B : nullptr)) != SSD_OK) return r;
+    if (one_pass) {
+        if ((r = run_state_fwd(s, x, B, init_state, final_state, w, st, true)) != SSD_OK)
+            return r;
     } else {
         if ((r = run_state(s, x, B, w, st)) != SSD_OK) return r;
         if ((r = run_passing(s, init_state, final_state, w, st)) != SSD_OK) return r;

@@ -12,9 +12,12 @@ struct Shape {
     bool bf16;                          // io dtype: bf16 (else float32)
 };
 
-// dt_bias (NULL = none) and softplus: the optional dt preprocessing.
+// dt_bias (NULL = none) and softplus: the optional dt preprocessing.  With
+// bfrag non-NULL (bf16 B), the same launch also lays B out for launch_state_fwd
+// (state_fwd_bfrag_bytes(s) bytes), which is then called with bfrag_ready.
 hipError_t launch_chunk_cumsum(const Shape &s, const float *dt, const float *A, float *Gws,
-                               float *DTws, const float *dt_bias, int softplus, hipStream_t st);
+                               float *DTws, const float *dt_bias, int softplus, hipStream_t st,
+                               const void *B = nullptr, void *bfrag = nullptr);
 hipError_t launch_chunk_state(const Shape &s, const void *x, const void *B, const float *Gws,
                               const float *DTws, float *S, hipStream_t st);
 hipError_t launch_state_passing(const Shape &s, const float *S, const float *Gws,
@@ -31,7 +34,8 @@ bool state_fwd_preferred(const Shape &s);   // shape heuristic of the fused call
 size_t state_fwd_bfrag_bytes(const Shape &s);
 hipError_t launch_state_fwd(const Shape &s, const void *x, const void *B, const float *Gws,
                             const float *DTws, const float *init, void *hprev, float *fin,
-                            void *bfrag, int rows_per_block, bool hprev_f32, hipStream_t st);
+                            void *bfrag, int rows_per_block, bool hprev_f32, hipStream_t st,
+                            bool bfrag_ready = false);
 // The backward's adjoint scan in the same one-pass form, chunks last to
 // first: ghat[c] (fp32, the adjoint of the state leaving chunk c) and dinit
 // (NULL = not written) from dy (fp32), C (bf16) and dfinal (NULL = zero);

@@ -52,6 +52,7 @@
 // C fragments in place of B, dfinal as the initial state, and ghat stored in
 // fp32.  Every exponent is again <= 0.
 
+#include "b_fragments.h"
 #include "ssd_device.h"
 #include "ssd_launch.h"
 
@@ -165,44 +166,12 @@ __device__ __forceinline__ void store_bf(uint16_t *p, const float *v) {
     else *p = (uint16_t)f32_to_bf16_bits(v[0]);
 }
 
-// B of one (b, chunk, group) laid out as the MFMA B operand of the state
-// product: fragment (slab js, n-tile nt) is 64 lanes x 16 bytes, lane
-// (m, q) holding B[32 js + 8 q + e][n] for e = 0..7 and
-// n = 64 (nt / 4) + 4 m + nt % 4.  Tokens past T are zero.  One workgroup per
-// (b, chunk, group, slab) stages the 32 x N slab in LDS with coalesced 16-byte
-// row loads and writes the N/16 fragments with 16-byte stores.
+// One workgroup per (b, chunk, group, slab): see b_fragments_block.
 template <int L, int N>
 __global__ __launch_bounds__(256) void b_fragments_kernel(const uint16_t *__restrict__ B,
                                                           uint4 *__restrict__ BF, int64_t T,
                                                           int32_t G, int32_t nc) {
-    constexpr int NS = L / 32, NT = N / 16, RW = N / 8;   // 16-byte pieces per row
-    __shared__ uint16_t tile[32][N + 8];
-    const int64_t blk = blockIdx.x;                    // ((b * nc + c) * G + g) * NS + js
-    const int js = (int)(blk % NS);
-    const int64_t bcg = blk / NS;
-    const int32_t g = (int32_t)(bcg % G);
-    const int64_t bc = bcg / G;
-    const int32_t c = (int32_t)(bc % nc);
-    const int64_t b = bc / nc;
-    const int tid = threadIdx.x;
-    for (int k = tid; k < 32 * RW; k += 256) {
-        const int r = k / RW, pc = k % RW;
-        const int64_t tok = (int64_t)c * L + 32 * js + r;
-        uint4 v = make_uint4(0u, 0u, 0u, 0u);
-        if (tok < T) v = *reinterpret_cast<const uint4 *>(B + ((b * T + tok) * G + g) * N + 8 * pc);
-        *reinterpret_cast<uint4 *>(&tile[r][8 * pc]) = v;
-    }
-    __syncthreads();
-    for (int k = tid; k < NT * 64; k += 256) {
-        const int nt = k / 64, l = k % 64, m = l & 15, q = l >> 4;
-        const int n = 64 * (nt >> 2) + 4 * m + (nt & 3);
-        uint4 v;
-        uint32_t *vw = reinterpret_cast<uint32_t *>(&v);
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr)
-            vw[rr] = (uint32_t)tile[8 * q + 2 * rr][n] | ((uint32_t)tile[8 * q + 2 * rr + 1][n] << 16);
-        BF[blk * (NT * 64) + k] = v;
-    }
+    b_fragments_block<L, N>(B, BF, T, G, nc, blockIdx.x);
 }
 
 template <int L, int N, int SPB, int MODE>
@@ -571,10 +540,11 @@ size_t state_fwd_bfrag_bytes(const Shape &s) {
 // state (final, or dinit) out
 static hipError_t launch_pass(const Shape &s, const void *x, const void *V, const float *Gws,
                               const float *DTws, const float *init, void *out, float *fin,
-                              void *vfrag, int spb, int mode, hipStream_t st) {
+                              void *vfrag, int spb, int mode, hipStream_t st,
+                              bool vfrag_ready = false) {
     if (s.Bt == 0 || s.H == 0) return hipSuccess;
     if (s.nc == 0 && !fin) return hipSuccess;
-    if (s.nc > 0) {
+    if (s.nc > 0 && !vfrag_ready) {
         const uint64_t nfb = (uint64_t)s.Bt * s.nc * s.G * (s.L / 32);
         auto lb = [&](auto kern) {
             hipLaunchKernelGGL(kern, dim3((uint32_t)nfb), dim3(256), 0, st, (const uint16_t *)V,
@@ -615,11 +585,12 @@ static hipError_t launch_pass(const Shape &s, const void *x, const void *V, cons
 
 hipError_t launch_state_fwd(const Shape &s, const void *x, const void *B, const float *Gws,
                             const float *DTws, const float *init, void *hprev, float *fin,
-                            void *bfrag, int spb, bool hprev_f32, hipStream_t st) {
+                            void *bfrag, int spb, bool hprev_f32, hipStream_t st,
+                            bool bfrag_ready) {
     if (!state_fwd_supported(s)) return hipErrorInvalidValue;
     if (spb <= 0) spb = state_fwd_rows_per_block(s);
     return launch_pass(s, x, B, Gws, DTws, init, hprev, fin, bfrag, spb,
-                       hprev_f32 ? kModeF32 : kModeBf16, st);
+                       hprev_f32 ? kModeF32 : kModeBf16, st, bfrag_ready);
 }
 
 bool state_adj_supported(const Shape &s) {
