@@ -75,6 +75,9 @@ def algorithmic(w, io_bytes: int):
     # state; S never exists.  The stage also runs b_fragments (B re-laid out:
     # read once, written once), counted in the stage's bytes.
     out["b_fragments"] = dict(bytes=2 * tok_bc, flops=0)
+    # ssd_chunked_fwd builds the fragments in the cumsum's launch
+    out["cumsum_bfrag"] = dict(bytes=out["chunk_cumsum"]["bytes"] + out["b_fragments"]["bytes"],
+                               flops=out["chunk_cumsum"]["flops"])
     out["state_fwd_kernel"] = dict(
         bytes=tok_x + tok_bc + gdt + units * P * N * io_bytes
         + (state if w.init_state else 0) + state,
@@ -111,7 +114,9 @@ def kernel_source_sha(kernel: str) -> str:
     import hashlib
     csrc = os.path.join(ROOT, "selective_state_space_amd", "csrc")
     h = hashlib.sha256()
-    for f in (kernel + ".hip", "ssd_device.h"):
+    files = {"b_fragments": ("state_fwd.hip", "b_fragments.h"),
+             "cumsum_bfrag": ("chunk_cumsum.hip", "b_fragments.h")}.get(kernel, (kernel + ".hip",))
+    for f in files + ("ssd_device.h",):
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -145,7 +150,7 @@ def profile_kind(name: str):
         # kernel with fp32 h_prev (mode 1) and as its adjoint scan (mode 2)
         args = name[name.index("<") + 1:name.index(">")].split(",")
         return "state_fwd_kernel" if args[-1].strip() == "0" else None
-    for k in ("chunk_cumsum", "chunk_state", "state_passing", "b_fragments"):
+    for k in ("chunk_cumsum", "chunk_state", "state_passing", "b_fragments", "cumsum_bfrag"):
         if k + "_kernel" in name:
             return k
     return None
@@ -221,7 +226,7 @@ def summarize_rocprof(pdir: str, workload: str):
         wk = sum(write[name]) / len(write[name])
         hbm = fk * 1024 * f_fetch + wk * 1024 * f_write
         a = alg[k]["bytes"]
-        src = {"state_fwd_kernel": "state_fwd", "b_fragments": "state_fwd"}.get(k, k)
+        src = {"state_fwd_kernel": "state_fwd"}.get(k, k)
         res["kernels"][k] = {"fetch_kib": fk, "write_kib": wk, "hbm_bytes_per_launch": int(hbm),
                              "alg_bytes": a, "source_sha": kernel_source_sha(src)}
         md.append("| %s | %.0f | %.0f | %.4g | %.4g | %.3f |" % (k, fk, wk, hbm, a, hbm / a))
@@ -250,7 +255,7 @@ def summarize_counters(pdir: str, workload: str):
     import re
     cmds = {"fwd": PROFILE_CMD, "bwd": "python3 bench.py --backward-only"}
     keep = re.compile(r"chunk_scan_bf16_kernel<256, 128, false>|state_fwd_kernel<256, 128, 4, [012]>|"
-                      r"chunk_cumsum|bwd_\w+_kernel")
+                      r"chunk_cumsum|cumsum_bfrag|bwd_\w+_kernel")
     out = ["# SQ counters per kernel: %s" % workload, "",
            "Two counter passes (rocprofv3 takes at most 8 SQ counters per pass) for each of",
            "the forward and the backward, from the repo root on one MI355X:", ""]
