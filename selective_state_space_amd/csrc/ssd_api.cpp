@@ -624,11 +624,14 @@ ssd_status ssd_chunked_bwd(const void *x, const float *dt, const float *A, const
     // it, else by S (chunk_state) and state_passing, which writes fp32 h_prev
     // for fp32 io
     void *hp32 = s.bf16 ? static_cast<void *>(base + l.hp32) : w.hprev;
-    if ((r = run_cumsum(s, dt, A, w, st, nullptr)) != SSD_OK) return r;
-    if (use_state_fwd(s)) {
+    // as in the forward, the one-pass recompute's B fragments come from the
+    // cumsum's launch
+    const bool one_pass = use_state_fwd(s);
+    if ((r = run_cumsum(s, dt, A, w, st, nullptr, one_pass ? B : nullptr)) != SSD_OK) return r;
+    if (one_pass) {
         const int rows = state_fwd_rows();
         r = hip_result(ssd::launch_state_fwd(s, x, B, w.G, w.DT, init_state, hp32, fin, w.S,
-                                             rows > 0 ? rows : 0, true, st),
+                                             rows > 0 ? rows : 0, true, st, true),
                        "state_fwd", st);
     } else {
         ssd::Shape s32 = s;
