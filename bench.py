@@ -777,7 +777,7 @@ def main():
     layer = None
     if not args.no_decode:
         wd = gen.WORKLOADS[4]
-        fms, dms_ = run_layer_interface(w, wd, max(10, args.steps // 2), 10)
+        fms, dms_ = run_layer_interface(w, wd, args.steps, args.warmup)
         zb = w.batch * w.seqlen * w.nheads * w.headdim * io_bytes
         layer = dict(options="dt_bias + softplus + z gate",
                      forward_us=round(fms * 1e3, 2), forward_tokens_per_s=round(tokens / (fms * 1e-3), 1),
