@@ -691,7 +691,7 @@ def main():
 
     w = gen.BY_NAME[args.workload]
     if args.backward_only:
-        bms = run_backward(w, 10, 3)
+        bms = run_backward(w, 10, 10)
         print(json.dumps({"workload": w.name, "backward_us_per_call": round(bms * 1e3, 2)}),
               flush=True)
         return
@@ -766,7 +766,7 @@ def main():
             log("decode, %s state: %.1f us/step, %.0f GB/s" % (name, v * 1e3, lowp[name]["GBps"]))
     bwd = None
     if not args.no_decode:
-        bms = run_backward(w, 10, 3)
+        bms = run_backward(w, 10, 10)
         bb = bwd_bytes(w, io_bytes)
         bwd = dict(us_per_call=round(bms * 1e3, 2), tokens_per_s=round(tokens / (bms * 1e-3), 1),
                    over_forward=round(bms / step_ms, 3),
