@@ -316,7 +316,7 @@ def run_forward(w, steps: int, warmup: int):
                     up(inp.D), w.chunk_size,
                     None if inp.init_state is None else up(inp.init_state))
     log("inputs generated and resident in HBM (%.1f s)" % (time.time() - t0))
-    one_pass = ssd.uses_state_fwd(a.dims, w.chunk_size)
+    one_pass = ssd.fwd_path(a.dims, w.chunk_size) == ssd.PATH_STATE_FWD
 
     # the boundary call, K steps between two synchronizations
     def step():

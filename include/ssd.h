@@ -56,10 +56,12 @@ typedef enum {
     SSD_ERR_HIP = -6           /* a HIP launch reported an error */
 } ssd_status;
 
-/* Element type of the inputs x, B, C (and x_t, B_t, C_t).  dt, A, D, every
- * state and the outputs y and y_t are always float32: stored in bf16, y would
- * carry its own rounding of up to 2^-8 |y|, which alone exceeds 2e-2 rms(y)
- * wherever |y| > 5 rms(y) -- and the D x skip term makes such outputs common. */
+/* Element type of the inputs x, B, C (and x_t, B_t, C_t).  dt, A, D and every
+ * state are always float32.  The outputs y and y_t are float32 by default:
+ * stored in bf16, y carries its own rounding of up to 2^-8 |y|, which alone
+ * exceeds 2e-2 rms(y) wherever |y| > 5 rms(y) -- and the D x skip term makes
+ * such outputs common.  ssd_layer_opts.y_io_dtype stores them in the io dtype
+ * instead (the pages' interfaces return y in x's dtype). */
 typedef enum { SSD_F32 = 0, SSD_BF16 = 1 } ssd_dtype;
 
 typedef struct {
@@ -82,7 +84,7 @@ typedef struct {
  *   B, C        [Bt, T, G, N]  io dtype      in
  *   chunk_size  L in {64, 128, 256}
  *   init_state  [Bt, H, P, N]  float32       in   NULL = zeros
- *   y           [Bt, T, H, P]  float32       out
+ *   y           [Bt, T, H, P]  float32       out  (io dtype with opts->y_io_dtype)
  *   final_state [Bt, H, P, N]  float32       out  NULL = not written
  *   workspace   ssd_chunked_fwd_workspace_size() bytes of device memory
  *
@@ -109,9 +111,12 @@ size_t ssd_chunked_fwd_workspace_size(const ssd_dims *dims, int64_t chunk_size);
  * intermediates.  With nc = ceil(T / L):
  *   offsets[0]  G       float32 [Bt, H, nc, L]   log2(e) * chunk-local cumsum of A dt
  *   offsets[1]  DT      float32 [Bt, H, nc, L]   dt transposed, 0 past T
- *   offsets[2]  S       float32 [Bt, H, nc, P, N] per-chunk states
+ *   offsets[2]  S       float32 [Bt, H, nc, P, N] per-chunk states (four-stage
+ *               path); on the other paths it holds B re-laid out in MFMA
+ *               fragment order instead (contents unspecified)
  *   offsets[3]  h_prev  io dtype [Bt, H, nc, P, N] state entering each chunk
- *               (bf16 for bf16 inputs: it is an MFMA operand of chunk_scan)
+ *               (bf16 for bf16 inputs: it is an MFMA operand of chunk_scan);
+ *               unspecified after a call on the fused path
  * Each region starts on a 256-byte boundary.
  */
 ssd_status ssd_chunked_fwd_workspace_layout(const ssd_dims *dims, int64_t chunk_size,
@@ -121,14 +126,10 @@ ssd_status ssd_chunked_fwd_workspace_layout(const ssd_dims *dims, int64_t chunk_
  * The four stages of the chunked forward, callable one at a time (same
  * arguments and workspace; each reads what the previous stage left in the
  * workspace): chunk_cumsum, chunk_state, state_passing, chunk_scan in this
- * order give y, final_state and every intermediate.  ssd_chunked_fwd runs
- * chunk_cumsum, then either chunk_state and state_passing or the one-pass
- * ssd_state_fwd stage below, then chunk_scan.  bf16 io takes the one-pass
- * stage (with all 64 state rows of a head per workgroup when batch * nheads
- * >= 384, two of the four 16-row sets when >= 48, else one); fp32 io runs
- * the four stages.  The environment variable SSD_STATE_FWD_ROWS, read at
- * each call, overrides the choice: 0 selects the two stages, 4, 2 or 1 the
- * one-pass stage with that many 16-row sets per workgroup.
+ * order give y, final_state and every intermediate.  ssd_chunked_fwd takes
+ * one of three paths (ssd_chunked_fwd_path says which): the four stages
+ * (fp32 io), chunk_cumsum + the one-pass ssd_state_fwd stage + chunk_scan,
+ * or the fused pass described at ssd_fwd_path (bf16 io, the default).
  *
  * chunk_cumsum: reads dt, A; writes G and DT.  One wavefront-level prefix
  *   sum per (b, h, chunk) ("Accelerating Mamba-2 ...", section "Kernel 1").
@@ -157,9 +158,10 @@ ssd_status ssd_chunk_scan(const void *x, const void *B, const void *C, const flo
  * the accumulator of the per-chunk product, stored before each chunk's
  * update).  Reads x, B, G, DT (left by ssd_chunk_cumsum) and init_state
  * (NULL = zeros); writes h_prev and final_state (NULL = not written).  The S
- * region is neither read nor written.  init_state may equal final_state.
- * h_prev and final_state agree with those of ssd_chunk_state followed by
- * ssd_state_passing up to fp32 summation order, not bit for bit.
+ * region receives B in MFMA fragment order (no chunk state is formed).
+ * init_state may equal final_state.  h_prev and final_state agree with those
+ * of ssd_chunk_state followed by ssd_state_passing up to fp32 summation
+ * order, not bit for bit.
  * bf16 io only: SSD_ERR_UNSUPPORTED for SSD_F32, and for shapes whose
  * per-chunk row span does not fit 32-bit offsets (chunk_size * nheads * 64 * 2
  * or chunk_size * ngroups * dstate * 2 bytes above 2^31 - 1), where
@@ -170,12 +172,40 @@ ssd_status ssd_state_fwd(const void *x, const void *B, const float *init_state,
                          void *workspace, size_t workspace_bytes, void *stream);
 
 /*
- * Which state path ssd_chunked_fwd would take for these dims and chunk size
- * under the current environment: *uses_state_fwd = 1 for the one-pass
- * ssd_state_fwd stage (the workspace's S region is then left untouched),
- * 0 for ssd_chunk_state + ssd_state_passing.  Host only; no HIP call.
+ * The paths of the chunked forward:
+ *   SSD_PATH_FOUR_STAGE  chunk_cumsum, chunk_state, state_passing, chunk_scan
+ *                        (the per-chunk states S and h_prev go through HBM);
+ *   SSD_PATH_STATE_FWD   chunk_cumsum, the one-pass ssd_state_fwd stage
+ *                        (h_prev through HBM, S never formed), chunk_scan;
+ *   SSD_PATH_FUSED       chunk_cumsum with the per-chunk C B^T tiles, then one
+ *                        pass per (b, h) that carries the state through the
+ *                        chunks in registers and writes y as it goes (neither
+ *                        S nor h_prev exists; x is read once).  bf16 io.
+ * All three give y and final_state within the same tolerances; they are
+ * not bitwise equal to one another (fp32 summation order).
  */
-ssd_status ssd_chunked_fwd_path(const ssd_dims *dims, int64_t chunk_size, int *uses_state_fwd);
+typedef enum {
+    SSD_PATH_FOUR_STAGE = 0,
+    SSD_PATH_STATE_FWD = 1,
+    SSD_PATH_FUSED = 2
+} ssd_fwd_path;
+
+/* The path ssd_chunked_fwd takes for these dims and chunk size (*path, an
+ * ssd_fwd_path), under the current override.  Host only; no HIP call. */
+ssd_status ssd_chunked_fwd_path(const ssd_dims *dims, int64_t chunk_size, int *path);
+
+/*
+ * TEST HOOK, for the parity tests that cover every path: makes later calls
+ * in this process take forward path fwd_path (-1 = chosen by the shape; a
+ * path the shape does not support is ignored) and, for the one-pass state
+ * stage and the backward's one-pass adjoint scan, state_rows / adj_rows sets
+ * of 16 state rows per workgroup (4, 2 or 1; 0 = chosen by the shape).  With
+ * fwd_path = SSD_PATH_FOUR_STAGE the backward recomputes its states with the
+ * four-stage kernels too.  Process-wide and not synchronized with calls on
+ * other threads.  (-1, 0, 0) restores the default.  SSD_ERR_UNSUPPORTED for
+ * other values.
+ */
+ssd_status ssd_set_path_override(int32_t fwd_path, int32_t state_rows, int32_t adj_rows);
 
 /*
  * The layer interface around the scan ("Optimizing Nemotron v3 Super in
@@ -185,7 +215,9 @@ ssd_status ssd_chunked_fwd_path(const ssd_dims *dims, int64_t chunk_size, int *u
  *   dt_bias      float32 [H], added to dt before anything else; NULL = none.
  *   dt_softplus  nonzero: dt <- log(1 + e^dt) where dt <= 20, unchanged
  *                above 20 (after the bias).  Tokens past T stay at dt = 0.
- *   reserved     must be 0 (else SSD_ERR_UNSUPPORTED).
+ *   y_io_dtype   0: y (y_t) float32;  1: y (y_t) in the io dtype (bf16 for
+ *                bf16 io, rounded to nearest even from the fp32 result; for
+ *                fp32 io the same as 0).  Other values SSD_ERR_UNSUPPORTED.
  *   z            gate in x's dtype and layout ([Bt, T, H, P] for the
  *                forward, [Bt, H, P] for decode): y <- y * silu(z) with
  *                silu(z) = z / (1 + e^-z), after the D term.  The state and
@@ -195,7 +227,7 @@ ssd_status ssd_chunked_fwd_path(const ssd_dims *dims, int64_t chunk_size, int *u
 typedef struct {
     const float *dt_bias;
     int32_t dt_softplus;
-    int32_t reserved;
+    int32_t y_io_dtype;
     const void *z;
 } ssd_layer_opts;
 
@@ -217,7 +249,7 @@ ssd_status ssd_chunked_fwd_opts(const void *x, const float *dt, const float *A, 
  *   dt_t   [Bt, H]        float32   in
  *   B_t, C_t [Bt, G, N]   io dtype  in
  *   A, D   [H]            float32   in
- *   y_t    [Bt, H, P]     float32   out
+ *   y_t    [Bt, H, P]     float32   out  (io dtype with opts->y_io_dtype)
  * dims->seqlen is ignored.
  */
 ssd_status ssd_decode_step(float *state, const void *x_t, const float *dt_t, const void *B_t,
@@ -247,7 +279,8 @@ ssd_status ssd_decode_step_opts(float *state, const void *x_t, const float *dt_t
  *   dt         [Bt, K, H]        float32   in
  *   B, C       [Bt, K, G, N]     io dtype  in
  *   A, D       [H]               float32   in
- *   y          [Bt, K, H, P]     float32   out: y of every step
+ *   y          [Bt, K, H, P]     float32   out: y of every step (io dtype
+ *                                          with opts->y_io_dtype)
  *   snapshots  [Bt, K, H, P, N]  float32   out, or NULL: the state after each
  *                                          step (the buffer a later accept
  *                                          step copies from)

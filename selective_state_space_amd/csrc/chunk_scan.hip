@@ -34,7 +34,8 @@
 //      exponents <= 0, so a tile needs one exp2 per lane (V_j = exp2(G_a - G_j)
 //      dt_j is staged per token).  Diagonal tiles use the exact pairwise
 //      exponent with a causal select.  Tiles above the diagonal do not exist.
-//   3. y = acc + D x (x from the lane's own fragment), written fp32.
+//   3. y = acc + D x (x from the lane's own fragment), written fp32 (or bf16
+//      when the caller asks for y in the io dtype).
 //
 // fp32 path (VALU): one workgroup per (b, h, chunk), 16-row tiles: the
 // decayed, masked C B^T rows are built in LDS, then each thread forms y for
@@ -98,9 +99,9 @@ struct ScanArgs {
     const uint16_t *x, *Bm, *Cm, *hprev;
     const uint16_t *z;   // output gate (GATE instantiations only)
     const float *D, *Gws, *DTws;
-    float *y;
+    void *y;             // float32, or bf16 when ybf
     int64_t T;
-    int32_t H, G, nc, hpg, NH, nhb;
+    int32_t H, G, nc, hpg, NH, nhb, ybf;
 };
 
 // Everything one head of the workgroup needs, loaded into registers (issued
@@ -365,9 +366,9 @@ __device__ __forceinline__ void chunk_scan_group(ScanSmem<L, N> &sm, const ScanA
         }
 
         __builtin_amdgcn_sched_barrier(0);
-        // ---- y = acc + D x (x from this lane's own fragments), fp32 ----
+        // ---- y = acc + D x (x from this lane's own fragments), fp32 or bf16 ----
         const float Dh = dh;
-        float *yb = a.y + ((b * a.T + t0) * a.H + h) * P;
+        const int64_t yb = ((b * a.T + t0) * a.H + h) * P;   // element offset of row 0
         const int32_t XR = a.H * P;
 #pragma unroll
         for (int k = 0; k < RBW; ++k) {
@@ -399,7 +400,8 @@ __device__ __forceinline__ void chunk_scan_group(ScanSmem<L, N> &sm, const ScanA
 #pragma unroll
                         for (int s = 0; s < 4; ++s) o[s] *= fast_silu(zf[s]);
                     }
-                    store_nt(yb + il * XR + 4 * m, make_float4(o[0], o[1], o[2], o[3]));
+                    store_y4(a.y, yb + il * XR + 4 * m, make_float4(o[0], o[1], o[2], o[3]),
+                             a.ybf != 0);
                 }
             }
         }
@@ -559,7 +561,8 @@ hipError_t launch_scan(const Shape &s, const void *x, const void *B, const void 
         a.D = D;
         a.Gws = Gws;
         a.DTws = DTws;
-        a.y = (float *)y;
+        a.y = y;
+        a.ybf = s.ybf16 ? 1 : 0;
         a.T = s.T;
         a.H = (int32_t)s.H;
         a.G = (int32_t)s.G;

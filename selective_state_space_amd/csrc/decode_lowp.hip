@@ -87,9 +87,9 @@ template <int N, typename Tio, bool GATE, int FMT>
 __global__ __launch_bounds__(256) void decode_lowp_kernel(
     uint16_t *__restrict__ state, float *__restrict__ scale, const Tio *__restrict__ x,
     const float *__restrict__ dt, const Tio *__restrict__ B, const Tio *__restrict__ C,
-    const float *__restrict__ A, const float *__restrict__ D, float *__restrict__ y,
+    const float *__restrict__ A, const float *__restrict__ D, void *__restrict__ y,
     const float *__restrict__ dt_bias, int32_t softplus, const Tio *__restrict__ z,
-    uint32_t seed_lo, uint32_t seed_hi, int32_t rounds, int32_t H, int32_t G) {
+    uint32_t seed_lo, uint32_t seed_hi, int32_t rounds, int32_t H, int32_t G, int32_t ybf) {
     constexpr int P = 64;
     constexpr int LPR = N / 4;         // lanes per state row
     constexpr int RPI = 64 / LPR;      // rows per wavefront iteration
@@ -157,7 +157,7 @@ __global__ __launch_bounds__(256) void decode_lowp_kernel(
         part = group_sum<LPR>(part);   // the row's sum, in its last lane
         float out = part + Dh * xv[k];
         if constexpr (GATE) out *= fast_silu(zv[k]);
-        if (sub == LPR - 1) y[bh * P + p] = out;
+        if (sub == LPR - 1) store_y1(y, bh * P + p, out, ybf != 0);
 
         uint32_t o[4];
         if constexpr (FMT == FMT_BF16) {
@@ -197,7 +197,7 @@ hipError_t launch_lowp_g(const Shape &s, const LowpArgs &a, hipStream_t st) {
                        (uint16_t *)a.state, a.scale, (const Tio *)a.x, a.dt, (const Tio *)a.B,    \
                        (const Tio *)a.C, a.A, a.D, a.y, a.dt_bias, (int32_t)a.softplus,           \
                        (const Tio *)a.z, slo, shi, (int32_t)a.philox_rounds, (int32_t)s.H, \
-                       (int32_t)s.G)
+                       (int32_t)s.G, (int32_t)s.ybf16)
     switch (a.format) {
     case LOWP_F16:
         if (a.philox_rounds > 0)

@@ -19,7 +19,8 @@
 // sum over the N/4 lanes of a row, formed with xor shuffles inside the
 // wavefront: no LDS, no atomics.  B_t and C_t of the head's group (N values)
 // are read once per lane as 4-element vectors.  y is written fp32 (for bf16
-// inputs too: a bf16 y would carry a rounding of up to 2^-8 |y|).
+// inputs too: a bf16 y would carry a rounding of up to 2^-8 |y|), or in bf16
+// when the caller asks for y in the io dtype.
 //
 // Optionally (sections 6.1 and 6.3 of the same page): dt <- dt + dt_bias_h,
 // then dt <- log(1 + e^dt) where dt <= 20; and y <- y * silu(z) after the D
@@ -36,8 +37,8 @@ template <int N, typename Tio, bool GATE>
 __global__ __launch_bounds__(256) void decode_step_kernel(
     float *__restrict__ state, const Tio *__restrict__ x, const float *__restrict__ dt,
     const Tio *__restrict__ B, const Tio *__restrict__ C, const float *__restrict__ A,
-    const float *__restrict__ D, float *__restrict__ y, const float *__restrict__ dt_bias,
-    int32_t softplus, const Tio *__restrict__ z, int32_t H, int32_t G) {
+    const float *__restrict__ D, void *__restrict__ y, const float *__restrict__ dt_bias,
+    int32_t softplus, const Tio *__restrict__ z, int32_t H, int32_t G, int32_t ybf) {
     constexpr int P = 64;
     constexpr int LPR = N / 4;         // lanes per state row
     constexpr int RPI = 64 / LPR;      // rows per wavefront iteration
@@ -82,7 +83,7 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
         part = group_sum<LPR>(part);   // the row's sum, in its last lane
         float out = part + Dh * xv[k];
         if constexpr (GATE) out *= fast_silu(zv[k]);
-        if (sub == LPR - 1) y[bh * P + p] = out;
+        if (sub == LPR - 1) store_y1(y, bh * P + p, out, ybf != 0);
     }
 }
 
@@ -110,9 +111,10 @@ template <int N, typename Tio, bool GATE, bool SNAP, bool TREE>
 __global__ __launch_bounds__(256) void decode_multi_kernel(
     float *__restrict__ state, const Tio *__restrict__ x, const float *__restrict__ dt,
     const Tio *__restrict__ B, const Tio *__restrict__ C, const float *__restrict__ A,
-    const float *__restrict__ D, float *__restrict__ y, const float *__restrict__ dt_bias,
+    const float *__restrict__ D, void *__restrict__ y, const float *__restrict__ dt_bias,
     int32_t softplus, const Tio *__restrict__ z, float *__restrict__ snaps,
-    const int32_t *__restrict__ parent, int32_t update, int32_t H, int32_t G, int32_t K) {
+    const int32_t *__restrict__ parent, int32_t update, int32_t H, int32_t G, int32_t K,
+    int32_t ybf) {
     constexpr int P = 64;
     constexpr int LPR = N / 4;         // lanes per state row
     constexpr int RPI = 64 / LPR;      // rows per wavefront iteration
@@ -180,7 +182,7 @@ __global__ __launch_bounds__(256) void decode_multi_kernel(
             part = group_sum<LPR>(part);   // the row's sum, in its last lane
             float out = part + Dh * cur.xv[i];
             if constexpr (GATE) out *= fast_silu(cur.zv[i]);
-            if (sub == LPR - 1) y[th * P + 16 * wave + RPI * i + rw] = out;
+            if (sub == LPR - 1) store_y1(y, th * P + 16 * wave + RPI * i + rw, out, ybf != 0);
         }
         cur = nxt;
     }
@@ -200,7 +202,7 @@ hipError_t launch_multi_g(const Shape &s, const MultiArgs &m, hipStream_t st) {
                        0, st, m.state, (const Tio *)m.x, m.dt, (const Tio *)m.B,              \
                        (const Tio *)m.C, m.A, m.D, m.y, m.dt_bias, (int32_t)m.softplus, z,     \
                        m.snaps, m.parent, (int32_t)m.update, (int32_t)s.H, (int32_t)s.G,      \
-                       (int32_t)s.T)
+                       (int32_t)s.T, (int32_t)s.ybf16)
     if (m.parent)
         SSD_MULTI_LAUNCH(true, true);
     else if (m.snaps)
@@ -231,13 +233,13 @@ hipError_t launch_dec_t(const Shape &s, float *state, const void *x, const float
     if (z)
         hipLaunchKernelGGL((decode_step_kernel<N, Tio, true>), dim3((uint32_t)nblk), dim3(256), 0,
                            st, state, (const Tio *)x, dt, (const Tio *)B, (const Tio *)C, A, D,
-                           (float *)y, dt_bias, (int32_t)softplus, (const Tio *)z, (int32_t)s.H,
-                           (int32_t)s.G);
+                           y, dt_bias, (int32_t)softplus, (const Tio *)z, (int32_t)s.H,
+                           (int32_t)s.G, (int32_t)s.ybf16);
     else
         hipLaunchKernelGGL((decode_step_kernel<N, Tio, false>), dim3((uint32_t)nblk), dim3(256),
                            0, st, state, (const Tio *)x, dt, (const Tio *)B, (const Tio *)C, A,
-                           D, (float *)y, dt_bias, (int32_t)softplus, (const Tio *)nullptr,
-                           (int32_t)s.H, (int32_t)s.G);
+                           D, y, dt_bias, (int32_t)softplus, (const Tio *)nullptr,
+                           (int32_t)s.H, (int32_t)s.G, (int32_t)s.ybf16);
     return hipGetLastError();
 }
 

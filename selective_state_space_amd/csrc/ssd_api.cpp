@@ -94,6 +94,7 @@ ssd_status check_dims(const ssd_dims *d, int64_t L, bool need_seq, ssd::Shape *s
     s->L = L > 0 ? L : 64;
     s->nc = need_seq ? (s->T + s->L - 1) / s->L : 0;
     s->bf16 = d->io_dtype == SSD_BF16;
+    s->ybf16 = false;
     if (s->nc > kMaxDim) return fail(SSD_ERR_SHAPE, "too many chunks (%lld)", (long long)s->nc);
     const uint64_t grid_chunks = (uint64_t)s->Bt * (uint64_t)s->nc * (uint64_t)s->H;
     const uint64_t grid_heads = (uint64_t)s->Bt * (uint64_t)s->H * 8u;
@@ -153,12 +154,17 @@ ssd_status check_ws(const ssd::Shape &s, void *ws, size_t bytes, Ws *w) {
         if (misaligned(p)) return fail(SSD_ERR_ALIGN, "%s is not 16-byte aligned", #p); \
     } while (0)
 
-// The optional layer interface: reserved must be 0; pointers 16-byte aligned.
-ssd_status check_opts(const ssd_layer_opts *o) {
+// The optional layer interface: pointers 16-byte aligned.  Also records in
+// the shape whether y is stored in the io dtype (bf16 io only: for fp32 io
+// the io dtype is float32 already).
+ssd_status check_opts(const ssd_layer_opts *o, ssd::Shape *s) {
     if (!o) return SSD_OK;
-    if (o->reserved != 0) return fail(SSD_ERR_UNSUPPORTED, "ssd_layer_opts.reserved must be 0");
+    if (o->y_io_dtype != 0 && o->y_io_dtype != 1)
+        return fail(SSD_ERR_UNSUPPORTED, "ssd_layer_opts.y_io_dtype = %d; 0 or 1",
+                    (int)o->y_io_dtype);
     if (misaligned(o->dt_bias)) return fail(SSD_ERR_ALIGN, "dt_bias is not 16-byte aligned");
     if (misaligned(o->z)) return fail(SSD_ERR_ALIGN, "z is not 16-byte aligned");
+    s->ybf16 = s->bf16 && o->y_io_dtype != 0;
     return SSD_OK;
 }
 
@@ -190,36 +196,44 @@ ssd_status run_passing(const ssd::Shape &s, const float *init, float *fin, const
     return hip_result(ssd::launch_state_passing(s, w.S, w.G, init, w.hprev, fin, st),
                       "state_passing", st);
 }
-// SSD_STATE_FWD_ROWS (read at each call; tests use it to cover every path):
-// 4, 2 or 1 forces the one-pass state stage with that row split, also in
-// ssd_chunked_fwd; 0 makes ssd_chunked_fwd use chunk_state + state_passing;
-// unset or empty leaves both choices to the shape.
-int state_fwd_rows() {
-    const char *e = getenv("SSD_STATE_FWD_ROWS");
-    if (!e || !e[0]) return -1;
-    const int v = atoi(e);
-    return (v == 0 || v == 1 || v == 2 || v == 4) ? v : -1;
+// Path override for tests (ssd_set_path_override): -1 / 0 = chosen by the
+// shape.  Set between calls, read by every call; never from the environment.
+struct PathOverride {
+    int fwd_path = -1;     // an ssd_fwd_path, or -1
+    int state_rows = 0;    // 4, 2, 1, or 0
+    int adj_rows = 0;      // 4, 2, 1, or 0
+};
+PathOverride g_override;
+
+int state_fwd_rows() { return g_override.state_rows; }
+int state_adj_rows() { return g_override.adj_rows; }
+
+// The forward path a call takes: the override where the shape supports it,
+// else the shape's own choice (the one-pass state stage for bf16 io, the
+// four stages for fp32 io).
+int fwd_path(const ssd::Shape &s) {
+    const bool one_pass_ok = ssd::state_fwd_supported(s);
+    switch (g_override.fwd_path) {
+    case SSD_PATH_FOUR_STAGE: return SSD_PATH_FOUR_STAGE;
+    case SSD_PATH_STATE_FWD:
+        if (one_pass_ok) return SSD_PATH_STATE_FWD;
+        break;
+    default: break;
+    }
+    if (one_pass_ok && ssd::state_fwd_preferred(s)) return SSD_PATH_STATE_FWD;
+    return SSD_PATH_FOUR_STAGE;
 }
-// SSD_STATE_ADJ_ROWS: 4, 2 or 1 forces that row split of the backward's
-// one-pass adjoint scan (tests cover every path); otherwise the shape picks.
-int state_adj_rows() {
-    const char *e = getenv("SSD_STATE_ADJ_ROWS");
-    if (!e || !e[0]) return 0;
-    const int v = atoi(e);
-    return (v == 1 || v == 2 || v == 4) ? v : 0;
-}
-bool use_state_fwd(const ssd::Shape &s) {
-    if (!ssd::state_fwd_supported(s)) return false;
-    const int r = state_fwd_rows();
-    if (r >= 0) return r > 0;
-    return ssd::state_fwd_preferred(s);
+bool use_state_fwd(const ssd::Shape &s) { return fwd_path(s) == SSD_PATH_STATE_FWD; }
+// The backward recomputes the forward's states with the one-pass stage
+// wherever it is supported, unless the override asks for the four stages.
+bool bwd_one_pass(const ssd::Shape &s) {
+    return ssd::state_fwd_supported(s) && g_override.fwd_path != SSD_PATH_FOUR_STAGE;
 }
 // bfrag_ready: run_cumsum was given B, so w.S already holds its fragments.
 ssd_status run_state_fwd(const ssd::Shape &s, const void *x, const void *B, const float *init,
                          float *fin, const Ws &w, hipStream_t st, bool bfrag_ready = false) {
-    const int r = state_fwd_rows();
     return hip_result(ssd::launch_state_fwd(s, x, B, w.G, w.DT, init, w.hprev, fin, w.S,
-                                            r > 0 ? r : 0, false, st, bfrag_ready),
+                                            state_fwd_rows(), false, st, bfrag_ready),
                       "state_fwd", st);
 }
 ssd_status run_scan(const ssd::Shape &s, const void *x, const void *B, const void *C,
@@ -337,12 +351,26 @@ ssd_status ssd_state_fwd(const void *x, const void *B, const float *init_state,
     return ok();
 }
 
-ssd_status ssd_chunked_fwd_path(const ssd_dims *dims, int64_t chunk_size, int *uses_state_fwd) {
-    if (!uses_state_fwd) return fail(SSD_ERR_NULL, "uses_state_fwd is NULL");
+ssd_status ssd_chunked_fwd_path(const ssd_dims *dims, int64_t chunk_size, int *path) {
+    if (!path) return fail(SSD_ERR_NULL, "path is NULL");
     ssd::Shape s;
     const ssd_status r = check_dims(dims, chunk_size, true, &s);
     if (r != SSD_OK) return r;
-    *uses_state_fwd = use_state_fwd(s) ? 1 : 0;
+    *path = fwd_path(s);
+    return ok();
+}
+
+ssd_status ssd_set_path_override(int32_t fwd, int32_t state_rows, int32_t adj_rows) {
+    if (fwd < -1 || fwd > SSD_PATH_FUSED)
+        return fail(SSD_ERR_UNSUPPORTED, "fwd_path = %d; -1 or an ssd_fwd_path", (int)fwd);
+    auto rows_ok = [](int32_t r) { return r == 0 || r == 1 || r == 2 || r == 4; };
+    if (!rows_ok(state_rows))
+        return fail(SSD_ERR_UNSUPPORTED, "state_rows = %d; 0, 1, 2 or 4", (int)state_rows);
+    if (!rows_ok(adj_rows))
+        return fail(SSD_ERR_UNSUPPORTED, "adj_rows = %d; 0, 1, 2 or 4", (int)adj_rows);
+    g_override.fwd_path = fwd;
+    g_override.state_rows = state_rows;
+    g_override.adj_rows = adj_rows;
     return ok();
 }
 
@@ -354,7 +382,7 @@ ssd_status ssd_chunked_fwd_opts(const void *x, const float *dt, const float *A, 
     ssd::Shape s;
     ssd_status r = check_dims(dims, chunk_size, true, &s);
     if (r != SSD_OK) return r;
-    if ((r = check_opts(opts)) != SSD_OK) return r;
+    if ((r = check_opts(opts, &s)) != SSD_OK) return r;
     if (s.Bt > 0 && s.T > 0) {
         REQUIRE_PTR(x);
         REQUIRE_PTR(dt);
@@ -408,7 +436,7 @@ ssd_status ssd_decode_step_opts(float *state, const void *x_t, const float *dt_t
     ssd::Shape s;
     ssd_status r = check_dims(dims, 0, false, &s);
     if (r != SSD_OK) return r;
-    if ((r = check_opts(opts)) != SSD_OK) return r;
+    if ((r = check_opts(opts, &s)) != SSD_OK) return r;
     REQUIRE_PTR(state);
     REQUIRE_PTR(x_t);
     REQUIRE_PTR(dt_t);
@@ -450,7 +478,7 @@ ssd_status ssd_decode_multi(float *state, const void *x, const float *dt, const 
     if (flags & ~(uint32_t)SSD_DECODE_NO_STATE_UPDATE)
         return fail(SSD_ERR_UNSUPPORTED, "flags = 0x%x; only SSD_DECODE_NO_STATE_UPDATE is defined",
                     (unsigned)flags);
-    if ((r = check_opts(opts)) != SSD_OK) return r;
+    if ((r = check_opts(opts, &s)) != SSD_OK) return r;
     if (s.Bt > 0)
         REQUIRE_PTR(state);
     else
@@ -512,7 +540,7 @@ ssd_status ssd_decode_step_lp(void *state, const ssd_state_format *fmt, const vo
     ssd::Shape s;
     ssd_status r = check_dims(dims, 0, false, &s);
     if (r != SSD_OK) return r;
-    if ((r = check_opts(opts)) != SSD_OK) return r;
+    if ((r = check_opts(opts, &s)) != SSD_OK) return r;
     REQUIRE_PTR(state);
     REQUIRE_PTR(x_t);
     REQUIRE_PTR(dt_t);
@@ -626,12 +654,11 @@ ssd_status ssd_chunked_bwd(const void *x, const float *dt, const float *A, const
     void *hp32 = s.bf16 ? static_cast<void *>(base + l.hp32) : w.hprev;
     // as in the forward, the one-pass recompute's B fragments come from the
     // cumsum's launch
-    const bool one_pass = use_state_fwd(s);
+    const bool one_pass = bwd_one_pass(s);
     if ((r = run_cumsum(s, dt, A, w, st, nullptr, one_pass ? B : nullptr)) != SSD_OK) return r;
     if (one_pass) {
-        const int rows = state_fwd_rows();
         r = hip_result(ssd::launch_state_fwd(s, x, B, w.G, w.DT, init_state, hp32, fin, w.S,
-                                             rows > 0 ? rows : 0, true, st, true),
+                                             state_fwd_rows(), true, st, true),
                        "state_fwd", st);
     } else {
         ssd::Shape s32 = s;
@@ -650,7 +677,7 @@ ssd_status ssd_chunked_bwd(const void *x, const float *dt, const float *A, const
                    reinterpret_cast<double *>(base + l.part), false};
     // the state adjoint: the one-pass reverse scan where the forward takes the
     // one-pass form, else per-chunk sums and a separate reverse scan
-    if (use_state_fwd(s) && ssd::state_adj_supported(s)) {
+    if (one_pass && ssd::state_adj_supported(s)) {
         r = hip_result(ssd::launch_state_adj(s, static_cast<const float *>(dy), C, w.G,
                                              static_cast<const float *>(dfinal), w.S,
                                              static_cast<float *>(dinit), base + l.cfr,

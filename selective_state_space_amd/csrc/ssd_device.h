@@ -58,6 +58,23 @@ __device__ __forceinline__ void store_nt(uint16_t *p, uint2 v) {
     __builtin_nontemporal_store(w, reinterpret_cast<u32x2 *>(p));
 }
 
+// Output stores: y in float32, or in bf16 (round to nearest even) when the
+// caller asked for y in the io dtype.  ybf is uniform over the launch.
+__device__ __forceinline__ void store_y1(void *y, int64_t i, float v, bool ybf) {
+    if (ybf)
+        static_cast<uint16_t *>(y)[i] = (uint16_t)f32_to_bf16_bits(v);
+    else
+        static_cast<float *>(y)[i] = v;
+}
+// four consecutive outputs from element i (16- or 8-byte aligned), streaming
+__device__ __forceinline__ void store_y4(void *y, int64_t i, float4 v, bool ybf) {
+    if (ybf)
+        store_nt(static_cast<uint16_t *>(y) + i, make_uint2(pack_bf16x2(v.x, v.y),
+                                                            pack_bf16x2(v.z, v.w)));
+    else
+        store_nt(static_cast<float *>(y) + i, v);
+}
+
 // 2^x on the transcendental unit (v_exp_f32).
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 

@@ -10,6 +10,7 @@ namespace ssd {
 struct Shape {
     int64_t Bt, T, H, P, N, G, L, nc;  // nc = ceil(T / L)
     bool bf16;                          // io dtype: bf16 (else float32)
+    bool ybf16;                         // y (y_t) stored as bf16 (bf16 io only), else float32
 };
 
 // dt_bias (NULL = none) and softplus: the optional dt preprocessing.  With
@@ -52,7 +53,7 @@ struct MultiArgs {
     const float *dt;
     const void *B, *C;
     const float *A, *D;
-    float *y;
+    void *y;
     const float *dt_bias;
     int softplus;
     const void *z;
@@ -74,7 +75,7 @@ struct LowpArgs {
     const float *dt;
     const void *B, *C;
     const float *A, *D;
-    float *y;
+    void *y;
     const float *dt_bias;
     int softplus;
     const void *z;

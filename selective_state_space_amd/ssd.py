@@ -61,9 +61,9 @@ STATE_DTYPES = {"f32": (0, torch.float32), "f16": (1, torch.float16), "bf16": (2
 
 
 class LayerOpts(ctypes.Structure):
-    """ssd_layer_opts: dt_bias [H] f32 (or NULL), dt_softplus, reserved = 0, z (or NULL)."""
+    """ssd_layer_opts: dt_bias [H] f32 (or NULL), dt_softplus, y_io_dtype, z (or NULL)."""
     _fields_ = [("dt_bias", ctypes.c_void_p), ("dt_softplus", ctypes.c_int32),
-                ("reserved", ctypes.c_int32), ("z", ctypes.c_void_p)]
+                ("y_io_dtype", ctypes.c_int32), ("z", ctypes.c_void_p)]
 
 
 _lib = None
@@ -94,6 +94,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "ssd_decode_step_opts": ([vp, vp, vp, vp, vp, vp, vp, vp, ctypes.POINTER(LayerOpts), dp,
                                   vp], st),
         "ssd_chunked_fwd_path": ([dp, i64, ctypes.POINTER(ctypes.c_int)], st),
+        "ssd_set_path_override": ([ctypes.c_int32, ctypes.c_int32, ctypes.c_int32], st),
         "ssd_decode_step": ([vp, vp, vp, vp, vp, vp, vp, vp, dp, vp], st),
         "ssd_decode_multi": ([vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_uint32,
                               ctypes.POINTER(LayerOpts), dp, vp], st),
@@ -185,7 +186,7 @@ class FwdArgs:
 
     def __init__(self, x, dt, A, B, C, D, chunk_size, init_state=None, y=None,
                  final_state=None, want_final=True, workspace=None, dt_bias=None,
-                 dt_softplus=False, z=None):
+                 dt_softplus=False, z=None, y_io_dtype=False):
         if x.dim() != 4 or B.dim() != 4:
             raise ValueError("x must be [Bt,T,H,P] and B, C [Bt,T,G,N]")
         dev = x.device
@@ -202,8 +203,10 @@ class FwdArgs:
         self.D = _need(D, "D", torch.float32, (H,), dev)
         self.init = None if init_state is None else _need(init_state, "init_state", torch.float32,
                                                          (Bt, H, P, N), dev)
-        self.y = (torch.empty((Bt, T, H, P), dtype=torch.float32, device=dev) if y is None
-                  else _need_out(y, "y", torch.float32, (Bt, T, H, P), dev))
+        self.y_io_dtype = bool(y_io_dtype)
+        ydt = io if self.y_io_dtype else torch.float32
+        self.y = (torch.empty((Bt, T, H, P), dtype=ydt, device=dev) if y is None
+                  else _need_out(y, "y", ydt, (Bt, T, H, P), dev))
         if final_state is not None:
             self.final = _need_out(final_state, "final_state", torch.float32, (Bt, H, P, N), dev)
         elif want_final:
@@ -223,15 +226,16 @@ class FwdArgs:
         self.device = dev
 
 
-def _layer_opts(dt_bias, dt_softplus, z):
-    if dt_bias is None and not dt_softplus and z is None:
+def _layer_opts(dt_bias, dt_softplus, z, y_io_dtype=False):
+    if dt_bias is None and not dt_softplus and z is None and not y_io_dtype:
         return None
-    return LayerOpts(_ptr(dt_bias), int(bool(dt_softplus)), 0, _ptr(z))
+    return LayerOpts(_ptr(dt_bias), int(bool(dt_softplus)), int(bool(y_io_dtype)), _ptr(z))
 
 
 def ssd_chunked_fwd(x, dt=None, A=None, B=None, C=None, D=None, chunk_size=None,
                     init_state=None, y=None, final_state=None, want_final: bool = True,
-                    workspace=None, dt_bias=None, dt_softplus: bool = False, z=None):
+                    workspace=None, dt_bias=None, dt_softplus: bool = False, z=None,
+                    y_io_dtype: bool = False):
     """Chunked forward.  Returns (y, final_state or None).
 
     x [Bt,T,H,P] (float32 or bfloat16), dt [Bt,T,H] f32, A/D [H] f32,
@@ -241,7 +245,8 @@ def ssd_chunked_fwd(x, dt=None, A=None, B=None, C=None, D=None, chunk_size=None,
     ``final_state`` may be the same tensor as ``init_state``.  ``x`` may
     instead be a prepared FwdArgs (then the other arguments are ignored).
     ``dt_bias`` [H] f32, ``dt_softplus`` and the gate ``z`` (x's shape and
-    dtype) are the optional layer interface (ssd_layer_opts).
+    dtype) are the optional layer interface (ssd_layer_opts); ``y_io_dtype``
+    stores y in x's dtype instead of float32.
     """
     if isinstance(x, FwdArgs):
         a = x
@@ -249,9 +254,9 @@ def ssd_chunked_fwd(x, dt=None, A=None, B=None, C=None, D=None, chunk_size=None,
         if any(v is None for v in (dt, A, B, C, D, chunk_size)):
             raise ValueError("ssd_chunked_fwd needs x, dt, A, B, C, D and chunk_size")
         a = FwdArgs(x, dt, A, B, C, D, chunk_size, init_state, y, final_state, want_final,
-                    workspace, dt_bias, dt_softplus, z)
+                    workspace, dt_bias, dt_softplus, z, y_io_dtype)
     lib = load_library()
-    opts = _layer_opts(a.dt_bias, a.dt_softplus, a.z)
+    opts = _layer_opts(a.dt_bias, a.dt_softplus, a.z, a.y_io_dtype)
     if opts is None:
         st = lib.ssd_chunked_fwd(_ptr(a.x), _ptr(a.dt), _ptr(a.A), _ptr(a.B), _ptr(a.C),
                                  _ptr(a.D), a.L, _ptr(a.init), _ptr(a.y), _ptr(a.final),
@@ -295,12 +300,22 @@ def ssd_state_fwd(a: FwdArgs):
                                               a.ws.numel(), _stream(a.device)))
 
 
-def uses_state_fwd(dims: Dims, chunk_size: int) -> bool:
-    """True if ssd_chunked_fwd takes the one-pass state stage for this shape."""
+PATH_FOUR_STAGE, PATH_STATE_FWD, PATH_FUSED = 0, 1, 2   # ssd_fwd_path
+
+
+def fwd_path(dims: Dims, chunk_size: int) -> int:
+    """The ssd_fwd_path ssd_chunked_fwd takes for this shape."""
     out = ctypes.c_int(-1)
     _check("ssd_chunked_fwd_path", load_library().ssd_chunked_fwd_path(
         ctypes.byref(dims), chunk_size, ctypes.byref(out)))
-    return out.value == 1
+    return out.value
+
+
+def set_path_override(fwd: int = -1, state_rows: int = 0, adj_rows: int = 0):
+    """Test hook (ssd_set_path_override): force a forward path and row splits
+    for later calls in this process; (-1, 0, 0) restores the default."""
+    _check("ssd_set_path_override",
+           load_library().ssd_set_path_override(int(fwd), int(state_rows), int(adj_rows)))
 
 
 def ssd_chunk_scan(a: FwdArgs):
@@ -331,11 +346,12 @@ def workspace_views(a: FwdArgs):
 
 
 def ssd_decode_step(state, x_t, dt_t, B_t, C_t, A, D, y_t=None, dt_bias=None,
-                    dt_softplus: bool = False, z_t=None):
+                    dt_softplus: bool = False, z_t=None, y_io_dtype: bool = False):
     """One decode step; ``state`` [Bt,H,P,N] f32 is updated in place.  Returns y_t [Bt,H,P] f32.
 
     ``dt_bias`` [H], ``dt_softplus`` and the gate ``z_t`` [Bt,H,P] (x_t's dtype)
-    are the optional layer interface (ssd_layer_opts).
+    are the optional layer interface (ssd_layer_opts); ``y_io_dtype`` stores
+    y_t in x_t's dtype instead of float32.
     """
     dev = state.device
     if dev.type != "cuda":
@@ -351,15 +367,16 @@ def ssd_decode_step(state, x_t, dt_t, B_t, C_t, A, D, y_t=None, dt_bias=None,
     C_t = _need(C_t, "C_t", io, (Bt, G, N), dev)
     A = _need(A, "A", torch.float32, (H,), dev)
     D = _need(D, "D", torch.float32, (H,), dev)
-    y_t = (torch.empty((Bt, H, P), dtype=torch.float32, device=dev) if y_t is None
-           else _need_out(y_t, "y_t", torch.float32, (Bt, H, P), dev))
+    ydt = io if y_io_dtype else torch.float32
+    y_t = (torch.empty((Bt, H, P), dtype=ydt, device=dev) if y_t is None
+           else _need_out(y_t, "y_t", ydt, (Bt, H, P), dev))
     dims = Dims(Bt, 1, H, P, N, G, _io_code(io))
     if dt_bias is not None:
         dt_bias = _need(dt_bias, "dt_bias", torch.float32, (H,), dev)
     if z_t is not None:
         z_t = _need(z_t, "z_t", io, (Bt, H, P), dev)
     lib = load_library()
-    opts = _layer_opts(dt_bias, dt_softplus, z_t)
+    opts = _layer_opts(dt_bias, dt_softplus, z_t, y_io_dtype)
     if opts is None:
         _check("ssd_decode_step", lib.ssd_decode_step(_ptr(state), _ptr(x_t), _ptr(dt_t),
                                                       _ptr(B_t), _ptr(C_t), _ptr(A), _ptr(D),
@@ -376,7 +393,8 @@ DECODE_NO_STATE_UPDATE = 1   # SSD_DECODE_NO_STATE_UPDATE
 
 
 def ssd_decode_multi(state, x, dt, B, C, A, D, y=None, snapshots=None, parent=None,
-                     update_state: bool = True, dt_bias=None, dt_softplus: bool = False, z=None):
+                     update_state: bool = True, dt_bias=None, dt_softplus: bool = False, z=None,
+                     y_io_dtype: bool = False):
     """K decode steps per sequence (speculative decoding); returns (y, snapshots).
 
     state [Bt,H,P,N] f32 (updated in place unless ``update_state`` is False),
@@ -402,8 +420,9 @@ def ssd_decode_multi(state, x, dt, B, C, A, D, y=None, snapshots=None, parent=No
     C = _need(C, "C", io, (Bt, K, G, N), dev)
     A = _need(A, "A", torch.float32, (H,), dev)
     D = _need(D, "D", torch.float32, (H,), dev)
-    y = (torch.empty((Bt, K, H, P), dtype=torch.float32, device=dev) if y is None
-         else _need_out(y, "y", torch.float32, (Bt, K, H, P), dev))
+    ydt = io if y_io_dtype else torch.float32
+    y = (torch.empty((Bt, K, H, P), dtype=ydt, device=dev) if y is None
+         else _need_out(y, "y", ydt, (Bt, K, H, P), dev))
     if snapshots is True:
         snapshots = torch.empty((Bt, K, H, P, N), dtype=torch.float32, device=dev)
     elif snapshots is not None:
@@ -414,7 +433,7 @@ def ssd_decode_multi(state, x, dt, B, C, A, D, y=None, snapshots=None, parent=No
         dt_bias = _need(dt_bias, "dt_bias", torch.float32, (H,), dev)
     if z is not None:
         z = _need(z, "z", io, (Bt, K, H, P), dev)
-    opts = _layer_opts(dt_bias, dt_softplus, z)
+    opts = _layer_opts(dt_bias, dt_softplus, z, y_io_dtype)
     dims = Dims(Bt, K, H, P, N, G, _io_code(io))
     flags = 0 if update_state else DECODE_NO_STATE_UPDATE
     _check("ssd_decode_multi", load_library().ssd_decode_multi(
@@ -426,7 +445,7 @@ def ssd_decode_multi(state, x, dt, B, C, A, D, y=None, snapshots=None, parent=No
 
 def ssd_decode_step_lp(state, x_t, dt_t, B_t, C_t, A, D, fmt: str, scale=None,
                        philox_rounds: int = 0, seed: int = 0, y_t=None, dt_bias=None,
-                       dt_softplus: bool = False, z_t=None):
+                       dt_softplus: bool = False, z_t=None, y_io_dtype: bool = False):
     """One decode step on a 16-bit state (``fmt`` "f16", "bf16" or "int16"; "f32"
     is the plain step), updated in place.  state [Bt,H,P,N] of fp16 / bf16 /
     int16; ``scale`` [Bt,H,P] f32 decode scales (int16 only, updated in place);
@@ -450,8 +469,9 @@ def ssd_decode_step_lp(state, x_t, dt_t, B_t, C_t, A, D, fmt: str, scale=None,
     C_t = _need(C_t, "C_t", io, (Bt, G, N), dev)
     A = _need(A, "A", torch.float32, (H,), dev)
     D = _need(D, "D", torch.float32, (H,), dev)
-    y_t = (torch.empty((Bt, H, P), dtype=torch.float32, device=dev) if y_t is None
-           else _need_out(y_t, "y_t", torch.float32, (Bt, H, P), dev))
+    ydt = io if y_io_dtype else torch.float32
+    y_t = (torch.empty((Bt, H, P), dtype=ydt, device=dev) if y_t is None
+           else _need_out(y_t, "y_t", ydt, (Bt, H, P), dev))
     if scale is not None:
         scale = _need_out(scale, "scale", torch.float32, (Bt, H, P), dev)
     if dt_bias is not None:
@@ -460,7 +480,7 @@ def ssd_decode_step_lp(state, x_t, dt_t, B_t, C_t, A, D, fmt: str, scale=None,
         z_t = _need(z_t, "z_t", io, (Bt, H, P), dev)
     f = StateFormat(code, int(philox_rounds), int(seed) & 0xFFFFFFFFFFFFFFFF,
                     None if scale is None else scale.data_ptr())
-    opts = _layer_opts(dt_bias, dt_softplus, z_t)
+    opts = _layer_opts(dt_bias, dt_softplus, z_t, y_io_dtype)
     dims = Dims(Bt, 1, H, P, N, G, _io_code(io))
     _check("ssd_decode_step_lp", load_library().ssd_decode_step_lp(
         _ptr(state), ctypes.byref(f), _ptr(x_t), _ptr(dt_t), _ptr(B_t), _ptr(C_t), _ptr(A),

@@ -140,17 +140,28 @@ def test_stage_calls_validate_too():
     assert L.ssd_state_fwd(P16, P16, None, None, 256, ctypes.byref(d), P16, 10, None) == -5
 
 
-def test_path_query(monkeypatch):
+def test_path_query_and_override():
     out = ctypes.c_int(-1)
     q = lambda d: lib().ssd_chunked_fwd_path(ctypes.byref(d), 256, ctypes.byref(out))
-    monkeypatch.delenv("SSD_STATE_FWD_ROWS", raising=False)
-    assert q(dims(Bt=8, T=4096, H=80, G=1)) == 0 and out.value == 1      # 640 chains
-    assert q(dims(Bt=4, T=2048, H=32, G=1)) == 0 and out.value == 1      # 128 chains
-    assert q(dims(Bt=8, T=4096, H=80, G=1, io=ssd.SSD_F32)) == 0 and out.value == 0
-    monkeypatch.setenv("SSD_STATE_FWD_ROWS", "0")
-    assert q(dims(Bt=8, T=4096, H=80, G=1)) == 0 and out.value == 0
-    monkeypatch.setenv("SSD_STATE_FWD_ROWS", "2")
-    assert q(dims(Bt=1, T=4096, H=8, G=1)) == 0 and out.value == 1
+    default = ssd.PATH_STATE_FWD
+    try:
+        assert lib().ssd_set_path_override(-1, 0, 0) == 0
+        assert q(dims(Bt=8, T=4096, H=80, G=1)) == 0 and out.value == default
+        assert q(dims(Bt=4, T=2048, H=32, G=1)) == 0 and out.value == default
+        assert q(dims(Bt=8, T=4096, H=80, G=1, io=ssd.SSD_F32)) == 0 and out.value == 0
+        ssd.set_path_override(ssd.PATH_FOUR_STAGE)
+        assert q(dims(Bt=8, T=4096, H=80, G=1)) == 0 and out.value == 0
+        ssd.set_path_override(ssd.PATH_STATE_FWD, 2)
+        assert q(dims(Bt=1, T=4096, H=8, G=1)) == 0 and out.value == ssd.PATH_STATE_FWD
+        # an override the shape does not support is ignored (fp32 io: four stages only)
+        assert q(dims(io=ssd.SSD_F32)) == 0 and out.value == 0
+        # bad values are rejected and leave the override as it was
+        assert lib().ssd_set_path_override(3, 0, 0) == -3
+        assert lib().ssd_set_path_override(-1, 3, 0) == -3
+        assert lib().ssd_set_path_override(-1, 0, 8) == -3
+        assert q(dims(Bt=1, T=4096, H=8, G=1)) == 0 and out.value == ssd.PATH_STATE_FWD
+    finally:
+        ssd.set_path_override(-1, 0, 0)
     assert lib().ssd_chunked_fwd_path(ctypes.byref(dims()), 256, None) == -1
     assert q(dims(P=32)) == -3
 
@@ -210,10 +221,16 @@ def test_empty_sequence_allows_null_token_tensors():
 def test_layer_opts_are_validated():
     L = lib()
     d = dims()
-    bad = ssd.LayerOpts(None, 1, 7, None)          # reserved must be 0
+    bad = ssd.LayerOpts(None, 1, 7, None)          # y_io_dtype is 0 or 1
     assert L.ssd_chunked_fwd_opts(P16, P16, P16, P16, P16, P16, 256, None, P16, None,
                                   ctypes.byref(bad), ctypes.byref(d), P16, 1 << 40, None) == -3
-    assert "reserved" in L.ssd_last_error_detail().decode()
+    assert "y_io_dtype" in L.ssd_last_error_detail().decode()
+    assert L.ssd_decode_step_opts(P16, P16, P16, P16, P16, P16, P16, P16, ctypes.byref(bad),
+                                  ctypes.byref(d), None) == -3
+    # y in the io dtype passes validation (short workspace is the error here)
+    yio = ssd.LayerOpts(None, 0, 1, None)
+    assert L.ssd_chunked_fwd_opts(P16, P16, P16, P16, P16, P16, 256, None, P16, None,
+                                  ctypes.byref(yio), ctypes.byref(d), P16, 10, None) == -5
     mis = ssd.LayerOpts(None, 0, 0, P_MIS)
     assert L.ssd_chunked_fwd_opts(P16, P16, P16, P16, P16, P16, 256, None, P16, None,
                                   ctypes.byref(mis), ctypes.byref(d), P16, 1 << 40, None) == -4
@@ -245,7 +262,7 @@ def test_decode_multi_is_validated():
     assert multi(dims(T=(1 << 16) + 1)) == -2
     assert multi(dims(Bt=1 << 30, T=1 << 16, H=1 << 10, G=1)) == -2
     assert multi(dims(N=96, T=4)) == -3
-    bad = ssd.LayerOpts(None, 0, 1, None)
+    bad = ssd.LayerOpts(None, 0, 2, None)        # y_io_dtype is 0 or 1
     assert multi(d, opts=ctypes.byref(bad)) == -3
     # nothing to do: no HIP call is made, so these succeed without a GPU
     assert multi(dims(T=0)) == 0

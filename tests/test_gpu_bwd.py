@@ -55,13 +55,12 @@ def test_backward_against_oracle(io, L, N):
 
 @pytest.mark.parametrize("fwd_rows,adj_rows", [("0", ""), ("4", "1"), ("2", "2"), ("1", "4")])
 @pytest.mark.parametrize("L", [64, 256])
-def test_state_stage_paths(monkeypatch, fwd_rows, adj_rows, L):
+def test_state_stage_paths(force_path, fwd_rows, adj_rows, L):
     """Every form of the recomputed forward states and of the state adjoint:
     chunk_state + state_passing with per-chunk adjoint sums and a separate
     reverse scan (rows 0), and the one-pass scans in both directions at each
     row split; the ragged last chunk and dfinal enter each."""
-    monkeypatch.setenv("SSD_STATE_FWD_ROWS", fwd_rows)
-    monkeypatch.setenv("SSD_STATE_ADJ_ROWS", adj_rows)
+    force_path(fwd_rows, adj_rows)
     log("bwd state paths", fwd_rows, adj_rows, "L", L)
     inp = gen.make_small(2, 3 * L + 17, 8, 64, 128, 2, gen.BF16, init_state=True, seed=L + 3)
     dy, dfin = grads_inputs(inp, 5)

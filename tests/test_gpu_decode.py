@@ -8,7 +8,7 @@ import oracle
 from selective_state_space_amd import inputs as gen
 from selective_state_space_amd import ssd
 
-from _gpu import assert_close, dev_tensor, host, log, upload_fwd
+from _gpu import assert_close, dev_tensor, host, log, row_pairs, upload_fwd
 
 pytestmark = pytest.mark.gpu
 
@@ -84,8 +84,8 @@ def test_decode_full_size_512_steps():
     prm = gen.decode_params(w, 0)
     state = torch.zeros((Bt, H, P, N), device="cuda")
     A, D = dev_tensor(prm.A), dev_tensor(prm.D)
-    rng = np.random.default_rng(0)
-    pairs = sorted({0, Bt * H - 1} | {int(v) for v in rng.integers(Bt * H, size=10)})
+    pairs = row_pairs(Bt, H, 16)   # every head of 16 batch rows: 2048 of 32768 pairs
+    log("  %d (b, h) pairs" % len(pairs))
     ref = np.zeros((len(pairs), P, N))
     ys, yrs = [], []
     for k in range(w.steps):
@@ -101,5 +101,36 @@ def test_decode_full_size_512_steps():
             log("  step", k)
     torch.cuda.synchronize()
     assert_close(np.stack(ys), np.stack(yrs), w.io_dtype, "decode y, 512 steps")
+    del ys, yrs
     fg = host(state).reshape(Bt * H, P, N)[pairs]
     assert_close(fg, ref, w.io_dtype, "decode state after 512 steps")
+
+
+def test_y_in_io_dtype_is_the_rounded_float32_output():
+    # y_t stored in bf16 (ssd_layer_opts.y_io_dtype): the fp32 output of the
+    # same step rounded to nearest even, for the plain step, the multi-token
+    # call and a 16-bit state
+    io = gen.BF16
+    w = gen.Workload("dec", 3, 1, 8, 64, 128, 2, 64, io, kind="decode")
+    prm = gen.decode_params(w, 5)
+    s = gen.make_decode_step(w, 0, prm, 5)
+    bf = torch.bfloat16
+    args = (dev_tensor(s.x_t, bf), dev_tensor(s.dt_t), dev_tensor(s.B_t, bf),
+            dev_tensor(s.C_t, bf), dev_tensor(prm.A), dev_tensor(prm.D))
+    st0 = torch.randn(3, 8, 64, 128, device="cuda")
+    a, b = st0.clone(), st0.clone()
+    y32 = ssd.ssd_decode_step(a, *args)
+    y16 = ssd.ssd_decode_step(b, *args, y_io_dtype=True)
+    torch.cuda.synchronize()
+    assert y16.dtype == bf and torch.equal(y16, y32.to(bf)) and torch.equal(a, b)
+    xk, dk, Bk, Ck = (t.unsqueeze(1).repeat(1, 3, *([1] * (t.dim() - 1))) for t in args[:4])
+    a, b = st0.clone(), st0.clone()
+    m32, _ = ssd.ssd_decode_multi(a, xk, dk, Bk, Ck, args[4], args[5])
+    m16, _ = ssd.ssd_decode_multi(b, xk, dk, Bk, Ck, args[4], args[5], y_io_dtype=True)
+    torch.cuda.synchronize()
+    assert m16.dtype == bf and torch.equal(m16, m32.to(bf)) and torch.equal(a, b)
+    a, b = st0.to(bf), st0.to(bf)
+    l32 = ssd.ssd_decode_step_lp(a, *args, "bf16")
+    l16 = ssd.ssd_decode_step_lp(b, *args, "bf16", y_io_dtype=True)
+    torch.cuda.synchronize()
+    assert l16.dtype == bf and torch.equal(l16, l32.to(bf)) and torch.equal(a, b)

@@ -8,7 +8,7 @@ import oracle
 from selective_state_space_amd import inputs as gen
 from selective_state_space_amd import ssd
 
-from _gpu import assert_close, host, log, upload_fwd
+from _gpu import assert_close, compare_all_pairs, host, log, upload_fwd
 
 pytestmark = pytest.mark.gpu
 
@@ -89,10 +89,10 @@ def test_intermediates_against_chunked_reference(io):
 
 
 @pytest.mark.parametrize("io,path", [(gen.F32, "auto"), (gen.BF16, "0"), (gen.BF16, "4")])
-def test_fused_call_equals_stage_calls_bitwise(io, path, monkeypatch):
+def test_fused_call_equals_stage_calls_bitwise(io, path, force_path):
     # ssd_chunked_fwd is cumsum, state + passing or the one-pass state stage, scan
     if path != "auto":
-        monkeypatch.setenv("SSD_STATE_FWD_ROWS", path)
+        force_path(path)
     inp = gen.make_small(2, 300, 8, 64, 128, 2, io, init_state=True, seed=37)
     t = upload_fwd(inp, io)
     y1, f1 = ssd.ssd_chunked_fwd(t["x"], t["dt"], t["A"], t["B"], t["C"], t["D"], 128,
@@ -106,9 +106,9 @@ def test_fused_call_equals_stage_calls_bitwise(io, path, monkeypatch):
 
 
 @pytest.mark.parametrize("rows", ["0", "4", "2", "1"])
-def test_both_state_paths_against_oracle(rows, monkeypatch):
+def test_both_state_paths_against_oracle(rows, force_path):
     # the same forward through the two stages and through each one-pass split
-    monkeypatch.setenv("SSD_STATE_FWD_ROWS", rows)
+    force_path(rows)
     inp = gen.make_small(2, 3 * 128 + 21, 4, 64, 128, 2, gen.BF16, init_state=True, seed=83)
     y, fin = run_fwd(inp, gen.BF16, 128)
     yr, fr = oracle_full(inp)
@@ -128,8 +128,8 @@ def test_reruns_are_bitwise_identical(io):
 
 
 @pytest.mark.parametrize("rows", ["0", "4"])
-def test_init_state_may_alias_final_state(rows, monkeypatch):
-    monkeypatch.setenv("SSD_STATE_FWD_ROWS", rows)
+def test_init_state_may_alias_final_state(rows, force_path):
+    force_path(rows)
     io = gen.BF16
     inp = gen.make_small(2, 256, 4, 64, 128, 1, io, init_state=True, seed=43)
     t = upload_fwd(inp, io)
@@ -144,8 +144,8 @@ def test_init_state_may_alias_final_state(rows, monkeypatch):
 
 
 @pytest.mark.parametrize("io,rows", [(gen.F32, ""), (gen.BF16, "0"), (gen.BF16, "4")])
-def test_chunk_aligned_split_equals_one_call(io, rows, monkeypatch):
-    monkeypatch.setenv("SSD_STATE_FWD_ROWS", rows)
+def test_chunk_aligned_split_equals_one_call(io, rows, force_path):
+    force_path(rows)
     L = 64
     inp = gen.make_small(2, 5 * L, 4, 64, 64, 2, io, init_state=True, seed=47)
     t = upload_fwd(inp, io)
@@ -163,8 +163,8 @@ def test_chunk_aligned_split_equals_one_call(io, rows, monkeypatch):
 
 
 @pytest.mark.parametrize("io,rows", [(gen.F32, ""), (gen.BF16, "0"), (gen.BF16, "4")])
-def test_empty_sequence_passes_state_through(io, rows, monkeypatch):
-    monkeypatch.setenv("SSD_STATE_FWD_ROWS", rows)
+def test_empty_sequence_passes_state_through(io, rows, force_path):
+    force_path(rows)
     dt = torch.bfloat16 if io == gen.BF16 else torch.float32
     x = torch.empty((2, 0, 4, 64), dtype=dt, device="cuda")
     B = torch.empty((2, 0, 1, 64), dtype=dt, device="cuda")
@@ -211,34 +211,13 @@ def test_strong_decay_does_not_overflow():
     assert_close(host(y), yr, io, "strong decay y")
 
 
-# --- the full-size workloads, on sampled (b, h) pairs -------------------------------
+# --- the full-size workloads, every (b, h) pair ----------------------------------
 
-def _sample_pairs(Bt, H, k, seed=0):
-    rng = np.random.default_rng(seed)
-    pr = {0, Bt * H - 1}
-    while len(pr) < min(k, Bt * H):
-        pr.add(int(rng.integers(Bt * H)))
-    return sorted(pr)
-
-
-def _check_sampled(w, inp, y, fin, npairs=12):
-    Bt, T, H, P = inp.x.shape
-    pairs = _sample_pairs(Bt, H, npairs)
-    log("  oracle on %d sampled (b, h) pairs of %d" % (len(pairs), Bt * H))
-    yr, fr, nth = oracle.token_fwd(inp.x, inp.dt, inp.A, inp.B, inp.C, inp.D, inp.init_state,
-                                   pairs=pairs)
-    yg = np.stack([host(y[b, :, h]) for b, h in (divmod(p, H) for p in pairs)])
-    fg = np.stack([host(fin[b, h]) for b, h in (divmod(p, H) for p in pairs)])
-    assert_close(yg, yr, w.io_dtype, "%s y" % w.name)
-    assert_close(fg, fr, w.io_dtype, "%s final" % w.name)
-
-
-@pytest.mark.parametrize("idx,rows", [(1, ""), (1, "0"), (2, ""), (2, "0"), (3, "")])
-def test_full_size_workload(idx, rows, monkeypatch):
-    # rows "" = the path the shape selects (the one-pass state stage, with
-    # two row sets per workgroup for 1 and 3 and all four for 2); "0" = the
-    # two-stage state path
-    monkeypatch.setenv("SSD_STATE_FWD_ROWS", rows)
+@pytest.mark.parametrize("idx,rows", [(1, ""), (1, "0"), (2, ""), (2, "0"), (2, "4"), (3, "")])
+def test_full_size_workload(idx, rows, force_path):
+    # rows "" = the path the shape selects; "0" = the four stages; "4" = the
+    # one-pass state stage with all four row sets per workgroup
+    force_path(rows)
     w = gen.WORKLOADS[idx]
     log("workload", w.name, w.description, "rows", rows or "auto")
     inp = gen.make_fwd(w, 0)
@@ -246,7 +225,8 @@ def test_full_size_workload(idx, rows, monkeypatch):
     y, fin = ssd.ssd_chunked_fwd(t["x"], t["dt"], t["A"], t["B"], t["C"], t["D"], w.chunk_size,
                                  t["init_state"])
     torch.cuda.synchronize()
-    _check_sampled(w, inp, y, fin)
+    compare_all_pairs(oracle, inp, y, fin, w.io_dtype, w.name,
+                      pairs_per_batch=16 if idx == 3 else 64)
     if idx == 3:
         # two halves of 32768 tokens in sequence give the same final state
         T1 = w.seqlen // 2
@@ -260,3 +240,52 @@ def test_full_size_workload(idx, rows, monkeypatch):
         assert torch.equal(f2, fin), "split-halves final state differs from one call"
         assert torch.equal(y2, y[:, T1:]), "split-halves second-half y differs from one call"
         log("  two 32768-token halves reproduce the single call bitwise")
+
+
+def test_full_size_y_in_io_dtype():
+    # the 2.7B layer with y stored in bf16: the same call as the fp32 output
+    # rounded to nearest even, and within the bar plus that rounding of the oracle
+    w = gen.WORKLOADS[2]
+    log("workload", w.name, "y in bf16")
+    inp = gen.make_fwd(w, 0)
+    t = upload_fwd(inp, w.io_dtype)
+    y32, f32 = ssd.ssd_chunked_fwd(t["x"], t["dt"], t["A"], t["B"], t["C"], t["D"],
+                                   w.chunk_size, t["init_state"])
+    y16, f16 = ssd.ssd_chunked_fwd(t["x"], t["dt"], t["A"], t["B"], t["C"], t["D"],
+                                   w.chunk_size, t["init_state"], y_io_dtype=True)
+    torch.cuda.synchronize()
+    assert y16.dtype == torch.bfloat16
+    assert torch.equal(y16, y32.to(torch.bfloat16)), "bf16 y is not the fp32 y rounded"
+    assert torch.equal(f16, f32)
+    compare_all_pairs(oracle, inp, y16, f16, w.io_dtype, w.name, y_io=True)
+
+
+@pytest.mark.parametrize("io", [gen.F32, gen.BF16])
+def test_one_head_per_group(io):
+    # G = H: every head has its own B and C (no sharing across heads)
+    L = 128
+    inp = gen.make_small(2, 3 * L + 11, 8, 64, 128, 8, io, init_state=True, seed=89)
+    log("one head per group", io)
+    y, fin = run_fwd(inp, io, L)
+    yr, fr = oracle_full(inp)
+    assert_close(host(y), yr, io, "G=H y")
+    assert_close(host(fin), fr, io, "G=H final")
+
+
+@pytest.mark.parametrize("rows", ["", "0", "4"])
+def test_partial_last_head_block(rows, force_path):
+    # chunk_scan sizes its head blocks for about 256 workgroups: 3 sequences of
+    # 3 chunks (one group) give blocks of 3 heads, so the last block of the 80
+    # heads holds 2 (the ragged block); the other paths see the same inputs
+    force_path(rows)
+    Bt, T, H = 3, 2 * 256 + 19, 80
+    inp = gen.make_small(Bt, T, H, 64, 128, 1, gen.BF16, init_state=True, seed=97)
+    nc = -(-T // 256)
+    groups = Bt * nc
+    nh = max(1, min(H, -(-groups * H // 256)))
+    assert H % nh != 0
+    log("partial head block: heads per block", nh, "last block", H % nh)
+    y, fin = run_fwd(inp, gen.BF16, 256)
+    yr, fr = oracle_full(inp)
+    assert_close(host(y), yr, gen.BF16, "partial head block y")
+    assert_close(host(fin), fr, gen.BF16, "partial head block final")

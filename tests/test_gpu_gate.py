@@ -10,7 +10,7 @@ import oracle
 from selective_state_space_amd import inputs as gen
 from selective_state_space_amd import ssd
 
-from _gpu import assert_close, dev_tensor, host, log, upload_fwd
+from _gpu import assert_close, compare_all_pairs, dev_tensor, host, log, upload_fwd
 
 pytestmark = pytest.mark.gpu
 
@@ -57,9 +57,9 @@ def gated_case(io, Bt, T, H, N, G, L, seed, bias=True, softplus=True, gate=True,
 @pytest.mark.parametrize("io", [gen.F32, gen.BF16])
 @pytest.mark.parametrize("L,N", [(64, 64), (128, 128), (256, 128)])
 @pytest.mark.parametrize("rows", ["", "0"])
-def test_gated_forward(io, L, N, rows, monkeypatch):
+def test_gated_forward(io, L, N, rows, force_path):
     """rows "" lets the library pick the state path; "0" forces the two-stage one."""
-    monkeypatch.setenv("SSD_STATE_FWD_ROWS", rows)
+    force_path(rows)
     T = 2 * L + 29
     log("gated forward", io, "L", L, "N", N, "rows", rows or "auto")
     # Steps above the threshold only in fp32: the step preparation is the same
@@ -121,8 +121,8 @@ def test_gated_decode(io):
     assert_close(host(state).reshape(Bt * H, P, N), ref, io, "state after %d steps" % steps)
 
 
-def test_gated_full_size_sampled():
-    """The 2.7B shape with all options, on 6 sampled (b, h) pairs."""
+def test_gated_full_size_all_pairs():
+    """The 2.7B shape with all options, every (b, h) pair."""
     w = gen.WORKLOADS[2]
     inp = gen.make_fwd(w, 0)
     raw = raw_dt(inp.dt.shape, 5)
@@ -133,11 +133,5 @@ def test_gated_full_size_sampled():
                                  w.chunk_size, t["init_state"], dt_bias=dev_tensor(b),
                                  dt_softplus=True, z=dev_tensor(z, torch.bfloat16))
     torch.cuda.synchronize()
-    pairs = [0, 79, 81, 333, 560, 639]
-    yr, fr, _ = oracle.token_fwd(inp.x, raw, inp.A, inp.B, inp.C, inp.D, inp.init_state,
-                                 pairs=pairs, dt_bias=b, dt_softplus=True, z=z)
-    H = w.nheads
-    yg = np.stack([host(y[p // H, :, p % H]) for p in pairs])
-    fg = np.stack([host(fin[p // H, p % H]) for p in pairs])
-    assert_close(yg, yr, gen.BF16, "y (gated, sampled)")
-    assert_close(fg, fr, gen.BF16, "final (sampled)")
+    compare_all_pairs(oracle, inp, y, fin, gen.BF16, "gated 2.7B", dt=raw, dt_bias=b,
+                      dt_softplus=True, z=z)

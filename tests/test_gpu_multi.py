@@ -10,7 +10,7 @@ import oracle
 from selective_state_space_amd import inputs as gen
 from selective_state_space_amd import ssd
 
-from _gpu import assert_close, dev_tensor, host, log
+from _gpu import assert_close, dev_tensor, host, log, row_pairs
 
 pytestmark = pytest.mark.gpu
 
@@ -132,9 +132,9 @@ def test_zero_tokens_and_empty_batch():
     assert torch.equal(s.cpu(), torch.from_numpy(st)) and y.numel() == 0
 
 
-def test_verify_workload_full_size_sampled():
+def test_verify_workload_full_size():
     """The multi-token decode workload at full size (snapshots, no state
-    update), on 12 sampled (b, h) pairs."""
+    update), on every head of 8 batch rows (1024 of 32768 (b, h) pairs)."""
     w = gen.BY_NAME["mtp_verify_b256_k4"]
     prm = gen.decode_params(w, 0)
     m = gen.make_decode_multi(w, prm, 0)
@@ -148,12 +148,15 @@ def test_verify_workload_full_size_sampled():
                                  snapshots=True, update_state=False)
     torch.cuda.synchronize()
     H = w.nheads
-    pairs = [0, 1, 127, 128, 1000, 5000, 12345, 20000, 25000, 30001, 32766, 32767]
+    pairs = row_pairs(w.batch, H, 8)
+    log("  %d (b, h) pairs" % len(pairs))
     ref = st.reshape(-1, 64, w.dstate)[pairs].astype(np.float64)
     yr, sr = oracle.token_decode_multi(ref, m.x, m.dt, m.B, m.C, prm.A, prm.D, pairs=pairs,
                                        update_state=False)
-    yg = np.stack([host(y[p // H, :, p % H]) for p in pairs])
-    sg = np.stack([host(sn[p // H, :, p % H]) for p in pairs])
-    assert_close(yg, yr, gen.BF16, "y (sampled)")
-    assert_close(sg, sr, gen.BF16, "snapshots (sampled)")
+    bi = torch.tensor([p // H for p in pairs], device=y.device)
+    hi = torch.tensor([p % H for p in pairs], device=y.device)
+    yg = host(y[bi, :, hi])
+    sg = host(sn[bi, :, hi])
+    assert_close(yg, yr, gen.BF16, "y (8 batch rows)")
+    assert_close(sg, sr, gen.BF16, "snapshots (8 batch rows)")
     assert torch.equal(s.cpu(), torch.from_numpy(st))
