@@ -239,6 +239,32 @@ ssd_status ssd_chunked_fwd_opts(const void *x, const float *dt, const float *A, 
                                 void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * ssd_chunked_fwd_opts without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): the workspace is a static device array of
+ * SSD_NOALLOC_SCRATCH_BYTES built into the library, one per GPU, held until
+ * the process ends.  The call allocates and frees nothing.  The array of the
+ * CURRENT device is used (stream must belong to it); its address is looked up
+ * on the first call on each device.
+ *   - Shapes whose workspace (ssd_chunked_fwd_workspace_size) exceeds
+ *     SSD_NOALLOC_SCRATCH_BYTES are rejected with SSD_ERR_WORKSPACE before any
+ *     HIP call; nothing is launched or written.  64 MiB holds, e.g., the
+ *     370M-layer shape (4 x 2048 tokens, 32 heads, N 128, chunk 256).
+ *   - Every call on one GPU shares that GPU's array: calls that overlap in
+ *     time on one GPU (other streams or threads) race and give undefined
+ *     results.  Calls in order on one stream are safe; every region a call
+ *     reads is written earlier in the same call, so nothing needs clearing
+ *     between calls.
+ * Other arguments, results and errors as for ssd_chunked_fwd_opts.
+ */
+#define SSD_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+ssd_status ssd_chunked_fwd_noalloc(const void *x, const float *dt, const float *A,
+                                   const void *B, const void *C, const float *D,
+                                   int64_t chunk_size, const float *init_state, void *y,
+                                   float *final_state, const ssd_layer_opts *opts,
+                                   const ssd_dims *dims, void *stream);
+
+/*
  * One recurrent decode step ("Optimizing Nemotron v3 Super in TensorRT-LLM",
  * section 6.1; "mamba-metal: running Mamba on Apple Silicon", section on
  * O(L) incremental decoding): for every (b, h),

@@ -12,13 +12,21 @@
 
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cstdarg>
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 
 #include "../../include/ssd.h"
 #include "ssd_launch.h"
+
+// The workspace of ssd_chunked_fwd_noalloc: a file-scope device array, one
+// copy per GPU, held until the process ends.  Host code never passes its
+// name to a kernel (on the host the name is only a stand-in): the device
+// address comes from hipGetSymbolAddress, once per device.
+static __device__ __align__(256) unsigned char scratch[SSD_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -174,6 +182,36 @@ ssd_status hip_result(hipError_t e, const char *what, hipStream_t st) {
         if (e == hipSuccess) e = hipGetLastError();
     }
     if (e != hipSuccess) return fail(SSD_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+    return SSD_OK;
+}
+
+// The device address of `scratch` on the current device, looked up once per
+// device (with that device current) and kept; later calls read it without a
+// lock.
+constexpr int kMaxDevices = 64;
+std::atomic<void *> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+ssd_status scratch_of_current_device(void **out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(SSD_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices)
+        return fail(SSD_ERR_UNSUPPORTED, "device %d: the scratch table holds %d devices", dev,
+                    kMaxDevices);
+    void *p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (!p) {
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+        if (!p) {
+            e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+            if (e != hipSuccess || !p)
+                return fail(SSD_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev,
+                            hipGetErrorString(e));
+            g_scratch_ptr[dev].store(p, std::memory_order_release);
+        }
+    }
+    *out = p;
     return SSD_OK;
 }
 
@@ -427,6 +465,31 @@ ssd_status ssd_chunked_fwd(const void *x, const float *dt, const float *A, const
                            void *stream) {
     return ssd_chunked_fwd_opts(x, dt, A, B, C, D, chunk_size, init_state, y, final_state,
                                 nullptr, dims, workspace, workspace_bytes, stream);
+}
+
+ssd_status ssd_chunked_fwd_noalloc(const void *x, const float *dt, const float *A,
+                                   const void *B, const void *C, const float *D,
+                                   int64_t chunk_size, const float *init_state, void *y,
+                                   float *final_state, const ssd_layer_opts *opts,
+                                   const ssd_dims *dims, void *stream) {
+    ssd::Shape s;
+    ssd_status r = check_dims(dims, chunk_size, true, &s);
+    if (r != SSD_OK) return r;
+    // the size check is host arithmetic only: a shape that does not fit is
+    // rejected before any HIP call
+    const size_t need = layout_of(s).total;
+    if (need > (size_t)SSD_NOALLOC_SCRATCH_BYTES)
+        return fail(SSD_ERR_WORKSPACE,
+                    "this shape needs %zu bytes of workspace; the static scratch of "
+                    "ssd_chunked_fwd_noalloc holds %zu",
+                    need, (size_t)SSD_NOALLOC_SCRATCH_BYTES);
+    if (s.Bt == 0 || need == 0)   // nothing to compute (the usual checks still apply)
+        return ssd_chunked_fwd_opts(x, dt, A, B, C, D, chunk_size, init_state, y, final_state,
+                                    opts, dims, nullptr, 0, stream);
+    void *ws = nullptr;
+    if ((r = scratch_of_current_device(&ws)) != SSD_OK) return r;
+    return ssd_chunked_fwd_opts(x, dt, A, B, C, D, chunk_size, init_state, y, final_state, opts,
+                                dims, ws, (size_t)SSD_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 ssd_status ssd_decode_step_opts(float *state, const void *x_t, const float *dt_t,

@@ -95,6 +95,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                   vp], st),
         "ssd_chunked_fwd_path": ([dp, i64, ctypes.POINTER(ctypes.c_int)], st),
         "ssd_set_path_override": ([ctypes.c_int32, ctypes.c_int32, ctypes.c_int32], st),
+        "ssd_chunked_fwd_noalloc": ([vp, vp, vp, vp, vp, vp, i64, vp, vp, vp,
+                                     ctypes.POINTER(LayerOpts), dp, vp], st),
         "ssd_decode_step": ([vp, vp, vp, vp, vp, vp, vp, vp, dp, vp], st),
         "ssd_decode_multi": ([vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_uint32,
                               ctypes.POINTER(LayerOpts), dp, vp], st),
@@ -269,6 +271,27 @@ def ssd_chunked_fwd(x, dt=None, A=None, B=None, C=None, D=None, chunk_size=None,
                                       ctypes.byref(opts), ctypes.byref(a.dims), _ptr(a.ws),
                                       a.ws.numel(), _stream(a.device))
         _check("ssd_chunked_fwd_opts", st)
+    return a.y, a.final
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20   # SSD_NOALLOC_SCRATCH_BYTES
+
+
+def ssd_chunked_fwd_noalloc(x, dt, A, B, C, D, chunk_size, init_state=None, y=None,
+                            final_state=None, want_final: bool = True, dt_bias=None,
+                            dt_softplus: bool = False, z=None, y_io_dtype: bool = False):
+    """ssd_chunked_fwd on the library's static scratch (no workspace is
+    allocated or passed).  Returns (y, final_state or None).  Shapes whose
+    workspace exceeds NOALLOC_SCRATCH_BYTES raise SSDError (SSD_ERR_WORKSPACE)."""
+    a = FwdArgs(x, dt, A, B, C, D, chunk_size, init_state, y, final_state, want_final,
+                torch.empty(0, dtype=torch.uint8, device=x.device), dt_bias, dt_softplus, z,
+                y_io_dtype)
+    opts = _layer_opts(a.dt_bias, a.dt_softplus, a.z, a.y_io_dtype)
+    st = load_library().ssd_chunked_fwd_noalloc(
+        _ptr(a.x), _ptr(a.dt), _ptr(a.A), _ptr(a.B), _ptr(a.C), _ptr(a.D), a.L, _ptr(a.init),
+        _ptr(a.y), _ptr(a.final), None if opts is None else ctypes.byref(opts),
+        ctypes.byref(a.dims), _stream(a.device))
+    _check("ssd_chunked_fwd_noalloc", st)
     return a.y, a.final
 
 

@@ -325,3 +325,20 @@ def test_chunked_bwd_workspace_and_validation():
                              None) == -3
     # empty batch: no HIP call is made
     assert call(args, dd=dims(Bt=0)) == 0
+
+
+def test_noalloc_refuses_large_shapes_before_any_hip_call():
+    # host arithmetic only: runs without a GPU
+    L = lib()
+    d = dims(Bt=8, T=4096, H=80, G=1)   # the 2.7B layer: about 0.5 GB of workspace
+    st = L.ssd_chunked_fwd_noalloc(P16, P16, P16, P16, P16, P16, 256, None, P16, None, None,
+                                   ctypes.byref(d), None)
+    assert st == -5
+    assert "scratch" in L.ssd_last_error_detail().decode()
+    assert L.ssd_chunked_fwd_noalloc(P16, P16, P16, P16, P16, P16, 100, None, P16, None, None,
+                                     ctypes.byref(d), None) == -3
+    assert L.ssd_chunked_fwd_noalloc(P16, P16, P16, P16, P16, P16, 256, None, P16, None, None,
+                                     None, None) == -1
+    # nothing to compute: no HIP call either
+    assert L.ssd_chunked_fwd_noalloc(None, None, None, None, None, None, 256, None, None, None,
+                                     None, ctypes.byref(dims(Bt=0)), None) == 0
