@@ -45,7 +45,7 @@ def log(*a):
 
 # ---- algorithmic work (what the method must move / compute, per launch) -----------
 
-def algorithmic(w, io_bytes: int):
+def algorithmic(w, io_bytes: int, y_bytes: int = 4):
     """Bytes and useful flops each stage must move/compute for workload w.
 
     Per (b, h, chunk) unit, L tokens, P = 64, N: the bytes each stage must
@@ -70,7 +70,7 @@ def algorithmic(w, io_bytes: int):
         + (state if w.init_state else 0) + state,
         flops=2 * units * P * N)
     tri = L * (L + 1) // 2
-    tok_y = Bt * T * H * P * 4           # y is written fp32
+    tok_y = Bt * T * H * P * y_bytes     # y: fp32, or the io dtype on request
     # one pass: x, B (as MFMA fragments), G and DT in, h_prev out, init/final
     # state; S never exists.  The stage also runs b_fragments (B re-laid out:
     # read once, written once), counted in the stage's bytes.
@@ -299,14 +299,62 @@ def summarize_counters(pdir: str, workload: str):
 
 # ---- the GPU legs ----------------------------------------------------------------------
 
-def run_forward(w, steps: int, warmup: int):
+def kernel_table(kern, alg):
+    """Per-kernel time, bandwidth and fractions of the HBM and bf16 MFMA peaks."""
+    out = {}
+    for name, ms in kern.items():
+        a = alg[name]
+        out[name] = dict(
+            us=round(ms * 1e3, 2),
+            GBps=round(a["bytes"] / (ms * 1e-3) / 1e9, 1),
+            hbm_frac=round(a["bytes"] / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+            TFLOPs=round(a["flops"] / (ms * 1e-3) / 1e12, 2),
+            bf16_mfma_frac=round(a["flops"] / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+            alg_bytes=int(a["bytes"]), alg_flops=int(a["flops"]))
+    return out
+
+
+def _settle(fn, ms: float):
+    """Runs fn back to back for about ms milliseconds of wall time (the GPU's
+    clocks ramp up over the first few milliseconds of work after idle);
+    returns the calls made and the wall time taken."""
+    import torch
+    n, t0 = 0, time.perf_counter()
+    while (time.perf_counter() - t0) * 1e3 < ms:
+        for _ in range(4):
+            fn()
+        n += 4
+        torch.cuda.synchronize()
+    return n, (time.perf_counter() - t0) * 1e3
+
+
+STAGES = {
+    # ssd_fwd_path -> the stage calls that time that path's kernels, in order
+    # (path 1: ssd_state_fwd called alone lays B out itself, work the whole
+    # call does inside the cumsum's launch, so its time and bytes include it)
+    0: ("chunk_cumsum", "chunk_state", "state_passing", "chunk_scan"),
+    1: ("chunk_cumsum", "state_fwd", "chunk_scan"),
+}
+PATH_NAMES = {0: "four-stage (chunk_state + state_passing)", 1: "one-pass state_fwd",
+              2: "fused state and output pass"}
+
+
+def run_forward(w, steps: int, warmup: int, settle_ms: float = 300.0, path: int = -1,
+                y_io: bool = False, stages: bool = True, inp=None):
+    """K timed ssd_chunked_fwd calls of workload w (after a clock-settling
+    pre-roll and W warm-up calls) on torch's current stream, between two
+    synchronizations; each call is also bracketed by HIP events for the
+    median and minimum.  With stages, the same path's stage calls are then
+    timed one at a time with events between them (the fused path's two
+    launches are not separately callable: its stages are left out)."""
     import torch
     from selective_state_space_amd import inputs as gen
     from selective_state_space_amd import ssd
 
     dev = torch.device("cuda:0")
     t0 = time.time()
-    inp = gen.make_fwd(w, 0)
+    if inp is None:
+        inp = gen.make_fwd(w, 0)
     bf = torch.bfloat16 if w.io_dtype == gen.BF16 else torch.float32
 
     def up(a, dt=torch.float32):
@@ -314,58 +362,70 @@ def run_forward(w, steps: int, warmup: int):
 
     a = ssd.FwdArgs(up(inp.x, bf), up(inp.dt), up(inp.A), up(inp.B, bf), up(inp.C, bf),
                     up(inp.D), w.chunk_size,
-                    None if inp.init_state is None else up(inp.init_state))
-    log("inputs generated and resident in HBM (%.1f s)" % (time.time() - t0))
-    one_pass = ssd.fwd_path(a.dims, w.chunk_size) == ssd.PATH_STATE_FWD
+                    None if inp.init_state is None else up(inp.init_state), y_io_dtype=y_io)
+    log("%s: inputs resident in HBM (%.1f s)" % (w.name, time.time() - t0))
+    ssd.set_path_override(path, 0, 0)
+    try:
+        taken = ssd.fwd_path(a.dims, w.chunk_size)
 
-    # the boundary call, K steps between two synchronizations
-    def step():
-        ssd.ssd_chunked_fwd(a)
-    for _ in range(warmup):
-        step()
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t_start = time.perf_counter()
-    e0.record()
-    for _ in range(steps):
-        step()
-    e1.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t_start
-    step_ms = e0.elapsed_time(e1) / steps
-
-    # the same stages one call at a time, HIP events between them
-    mid = ([("state_fwd", ssd.ssd_state_fwd)] if one_pass else
-           [("chunk_state", ssd.ssd_chunk_state), ("state_passing", ssd.ssd_state_passing)])
-    stages = [("chunk_cumsum", ssd.ssd_chunk_cumsum)] + mid + [("chunk_scan", ssd.ssd_chunk_scan)]
-    for _ in range(warmup):
-        for _, f in stages:
-            f(a)
-    torch.cuda.synchronize()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)]
-          for _ in range(steps)]
-    for k in range(steps):
-        ev[k][0].record()
-        for i, (_, f) in enumerate(stages):
-            f(a)
-            ev[k][i + 1].record()
-    torch.cuda.synchronize()
-    per = np.array([[ev[k][i].elapsed_time(ev[k][i + 1]) for i in range(len(stages))]
-                    for k in range(steps)])          # ms
-    kern = {name: float(per[:, i].mean()) for i, (name, _) in enumerate(stages)}
+        def step():
+            ssd.ssd_chunked_fwd(a)
+        n_settle, settle_wall = _settle(step, settle_ms)
+        for _ in range(warmup):
+            step()
+        torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+        t_start = time.perf_counter()
+        ev[0].record()
+        for k in range(steps):
+            step()
+            ev[k + 1].record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t_start
+        per_step = np.array([ev[k].elapsed_time(ev[k + 1]) for k in range(steps)])   # ms
+        kern = {}
+        if stages and taken in (0, 1):
+            fns = {"chunk_cumsum": ssd.ssd_chunk_cumsum, "chunk_state": ssd.ssd_chunk_state,
+                   "state_passing": ssd.ssd_state_passing, "state_fwd": ssd.ssd_state_fwd,
+                   "chunk_scan": ssd.ssd_chunk_scan}
+            seq = [(nm, fns[nm]) for nm in STAGES[taken]]
+            for _ in range(warmup):
+                for _, f in seq:
+                    f(a)
+            torch.cuda.synchronize()
+            evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(seq) + 1)]
+                   for _ in range(steps)]
+            for k in range(steps):
+                evs[k][0].record()
+                for i, (_, f) in enumerate(seq):
+                    f(a)
+                    evs[k][i + 1].record()
+            torch.cuda.synchronize()
+            per = np.array([[evs[k][i].elapsed_time(evs[k][i + 1]) for i in range(len(seq))]
+                            for k in range(steps)])
+            kern = {nm: float(per[:, i].mean()) for i, (nm, _) in enumerate(seq)}
+    finally:
+        ssd.set_path_override(-1, 0, 0)
     del a
     torch.cuda.empty_cache()
-    return wall, step_ms, kern, one_pass
+    return dict(wall=wall, mean_ms=float(per_step.mean()), median_ms=float(np.median(per_step)),
+                min_ms=float(per_step.min()), kern=kern, path=taken, settle_calls=n_settle,
+                settle_ms=round(settle_wall, 1))
 
 
-def run_decode(w, steps: int, warmup: int):
+def run_decode(w, steps: int, warmup: int, settle_ms: float = 300.0, nset: int = 32):
+    """The decode workload's step stream: ``steps`` consecutive steps (512 =
+    the workload's length) with the fp32 state carried from step to step,
+    every step timed between HIP events.  The per-token inputs are nset
+    distinct generated steps used in turn (generating all 512 on the host
+    takes ~35 s; they are 0.25% of a step's bytes).  Returns the median,
+    mean and minimum milliseconds per step."""
     import torch
     from selective_state_space_amd import inputs as gen
     from selective_state_space_amd import ssd
 
     dev = torch.device("cuda:0")
     prm = gen.decode_params(w, 0)
-    nset = 8   # distinct per-token input sets, cycled
 
     def up(a, dt=torch.float32):
         return torch.from_numpy(np.ascontiguousarray(a)).to(dt).to(dev)
@@ -378,8 +438,11 @@ def run_decode(w, steps: int, warmup: int):
     A, D = up(prm.A), up(prm.D)
     state = torch.zeros((w.batch, w.nheads, w.headdim, w.dstate), device=dev)
     y = torch.empty((w.batch, w.nheads, w.headdim), dtype=torch.float32, device=dev)
+    _settle(lambda: ssd.ssd_decode_step(state, *sets[0], A, D, y_t=y), settle_ms)
+    state.zero_()
     for k in range(warmup):
         ssd.ssd_decode_step(state, *sets[k % nset], A, D, y_t=y)
+    state.zero_()   # the stream starts from the zero state
     torch.cuda.synchronize()
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     ev[0].record()
@@ -390,7 +453,7 @@ def run_decode(w, steps: int, warmup: int):
     t = np.array([ev[k].elapsed_time(ev[k + 1]) for k in range(steps)])
     del state
     torch.cuda.empty_cache()
-    return float(np.median(t)), float(np.mean(t))
+    return float(np.median(t)), float(np.mean(t)), float(np.min(t))
 
 
 def multi_bytes(w, snapshots: bool, update: bool, io_bytes=2):
@@ -512,6 +575,7 @@ def run_backward(w, steps: int, warmup: int):
     ws = torch.empty(ssd.ssd_chunked_bwd_workspace_size(a.dims, w.chunk_size), dtype=torch.uint8,
                      device=dev)
     del a
+    _settle(lambda: ssd.ssd_chunked_bwd(*args, workspace=ws), 300.0)
     for _ in range(warmup):
         ssd.ssd_chunked_bwd(*args, workspace=ws)
     torch.cuda.synchronize()
@@ -546,6 +610,7 @@ def run_layer_interface(w, wd, steps: int, warmup: int):
         return np.log(np.expm1(d)).astype(np.float32)
 
     def timed(fn, n, k0):
+        _settle(fn, 300.0)
         for _ in range(k0):
             fn()
         torch.cuda.synchronize()
@@ -651,9 +716,14 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--workload", default="mamba2_2p7b")
-    ap.add_argument("--decode-steps", type=int, default=50)
+    ap.add_argument("--decode-steps", type=int, default=512)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the 370M and long-context forward legs and the path comparison")
+    ap.add_argument("--settle-ms", type=float, default=300.0,
+                    help="clock-settling pre-roll before each leg's counted warm-up (ms of "
+                         "back-to-back calls)")
     ap.add_argument("--summarize-rocprof", metavar="DIR",
                     help="write the profiles/ summaries from a rocprofv3 output directory "
                          "(host only, no GPU)")
@@ -698,45 +768,112 @@ def main():
     io_bytes = 2 if w.io_dtype == gen.BF16 else 4
     log("workload %s: %s" % (w.name, w.description))
 
-    wall, step_ms, kern, one_pass = run_forward(w, args.steps, args.warmup)
+    inp = gen.make_fwd(w, 0)
+    fw = run_forward(w, args.steps, args.warmup, args.settle_ms, inp=inp)
+    wall, kern = fw["wall"], fw["kern"]
+    step_ms = wall / args.steps * 1e3
     tokens = w.batch * w.seqlen
     value = tokens * args.steps / wall
     alg = algorithmic(w, io_bytes)
-    kernels = {}
-    for name, ms in kern.items():
-        a = alg[name]
-        kernels[name] = dict(
-            us=round(ms * 1e3, 2),
-            GBps=round(a["bytes"] / (ms * 1e-3) / 1e9, 1),
-            hbm_frac=round(a["bytes"] / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
-            TFLOPs=round(a["flops"] / (ms * 1e-3) / 1e12, 2),
-            bf16_mfma_frac=round(a["flops"] / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
-            alg_bytes=int(a["bytes"]), alg_flops=int(a["flops"]))
+    kernels = kernel_table(kern, alg)
     dom = max(kern, key=kern.get)
     dms = kern[dom]
     achieved = alg[dom]["bytes"] / (dms * 1e-3) / 1e9
+    # the same launch against the byte count with y stored in the io dtype
+    # (what the pages' interfaces return): the bf16 y store is a third of
+    # chunk_scan's bytes smaller
+    alg_yio = algorithmic(w, io_bytes, y_bytes=io_bytes)
     roofline = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1),
                 "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                 "traffic": measured_traffic(dom, w.name),
-                "avg_launch_us": round(dms * 1e3, 2), "alg_bytes_per_launch": int(alg[dom]["bytes"])}
+                "avg_launch_us": round(dms * 1e3, 2), "alg_bytes_per_launch": int(alg[dom]["bytes"]),
+                "alg_bytes_per_launch_y_io_dtype": int(alg_yio[dom]["bytes"]),
+                "frac_y_io_dtype_bytes": round(alg_yio[dom]["bytes"] / (dms * 1e-3) / 1e9
+                                               / HBM_PEAK_GBPS, 4)}
     mfma_kernels = [k for k in ("chunk_state", "state_fwd", "chunk_scan") if k in kern]
     chunk_flops = sum(alg[k]["flops"] for k in mfma_kernels)
     chunk_ms = sum(kern[k] for k in mfma_kernels)
     fwd_flops = sum(alg[k]["flops"] for k in kern)
-    log("forward: %.1f us/step (ssd_chunked_fwd), %.3e tokens/s; stages %s; dominant %s %.1f us"
-        % (step_ms * 1e3, value, " ".join("%s %.1f" % (k, v * 1e3) for k, v in kern.items()),
-           dom, dms * 1e3))
+    log("forward: %.1f us/step (wall; median %.1f, min %.1f), %.3e tokens/s; stages %s"
+        % (step_ms * 1e3, fw["median_ms"] * 1e3, fw["min_ms"] * 1e3, value,
+           " ".join("%s %.1f" % (k, v * 1e3) for k, v in kern.items())))
+
+    # y in the io dtype (bf16): the same call with ssd_layer_opts.y_io_dtype.
+    # The stage calls take no options (their y is float32), so chunk_scan's
+    # time with bf16 stores is the whole call less the other two stages of
+    # the leg above (rocprofv3's kernel trace gives it directly)
+    fy = run_forward(w, args.steps, args.warmup, args.settle_ms, y_io=True, stages=False, inp=inp)
+    yio_us = fy["median_ms"] * 1e3
+    scan_us = yio_us - sum(v for k, v in kern.items() if k != "chunk_scan") * 1e3
+    y_io = dict(us=round(fy["wall"] / args.steps * 1e6, 2),
+                median_us=round(yio_us, 2), min_us=round(fy["min_ms"] * 1e3, 2),
+                tokens_per_s=round(tokens * args.steps / fy["wall"], 1),
+                y_bytes_saved=int(alg["chunk_scan"]["bytes"] - alg_yio["chunk_scan"]["bytes"]),
+                chunk_scan_us_by_difference=round(scan_us, 2),
+                chunk_scan_hbm_frac_by_difference=round(
+                    alg_yio["chunk_scan"]["bytes"] / (scan_us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4))
+    log("forward, bf16 y: %.1f us/step (median %.1f); chunk_scan ~%.1f us"
+        % (y_io["us"], yio_us, scan_us))
+
+    # every path on this workload, then the other forward configurations
+    paths = {}
+    for pth in (0, 1, 2):
+        if pth == fw["path"]:
+            r = fw
+        else:
+            r = run_forward(w, max(10, args.steps // 2), args.warmup, args.settle_ms, path=pth,
+                            stages=False, inp=inp)
+        paths[PATH_NAMES[r["path"]]] = dict(median_us=round(r["median_ms"] * 1e3, 2),
+                                           min_us=round(r["min_ms"] * 1e3, 2))
+    log("paths: " + ", ".join("%s %.1f us" % (k, v["median_us"]) for k, v in paths.items()))
+    del inp
+    configs = {w.name: dict(tokens_per_s=round(value, 1), median_us=round(fw["median_ms"] * 1e3, 2),
+                            path=PATH_NAMES[fw["path"]], paths=paths)}
+    if not args.no_configs:
+        for idx, (nsteps, nwarm) in ((1, (args.steps, args.warmup)), (3, (10, 3))):
+            wc = gen.WORKLOADS[idx]
+            if wc.name == w.name:
+                continue
+            ic = gen.make_fwd(wc, 0)
+            rc = run_forward(wc, nsteps, nwarm, args.settle_ms, inp=ic)
+            ac = algorithmic(wc, 2 if wc.io_dtype == gen.BF16 else 4)
+            kc = kernel_table(rc["kern"], ac)
+            cflops = sum(ac[k]["flops"] for k in rc["kern"])
+            cp = {PATH_NAMES[rc["path"]]: dict(median_us=round(rc["median_ms"] * 1e3, 2),
+                                                min_us=round(rc["min_ms"] * 1e3, 2))}
+            for pth in (0, 1, 2):
+                if pth != rc["path"]:
+                    r = run_forward(wc, nsteps, nwarm, args.settle_ms, path=pth, stages=False,
+                                    inp=ic)
+                    cp[PATH_NAMES[r["path"]]] = dict(median_us=round(r["median_ms"] * 1e3, 2),
+                                                     min_us=round(r["min_ms"] * 1e3, 2))
+            del ic
+            configs[wc.name] = dict(
+                tokens=wc.batch * wc.seqlen,
+                us=round(rc["wall"] / nsteps * 1e6, 2), median_us=round(rc["median_ms"] * 1e3, 2),
+                min_us=round(rc["min_ms"] * 1e3, 2),
+                tokens_per_s=round(wc.batch * wc.seqlen * nsteps / rc["wall"], 1),
+                steps=nsteps, warmup=nwarm, path=PATH_NAMES[rc["path"]], kernels=kc,
+                forward_bf16_mfma_frac=round(cflops / (rc["median_ms"] * 1e-3) / 1e12
+                                             / BF16_PEAK_TFLOPS, 4),
+                paths=cp)
+            log("%s: %.1f us/call (median), %.3e tokens/s; %s" % (
+                wc.name, rc["median_ms"] * 1e3, configs[wc.name]["tokens_per_s"],
+                ", ".join("%s %.1f" % (k, v["median_us"]) for k, v in cp.items())))
 
     decode = None
     if not args.no_decode:
         wd = gen.WORKLOADS[4]
-        med, mean = run_decode(wd, args.decode_steps, 5)
+        med, mean, mn = run_decode(wd, args.decode_steps, 5, args.settle_ms)
         byt = decode_bytes(wd)
         decode = dict(workload=wd.name, us_per_step=round(med * 1e3, 2),
+                      mean_us=round(mean * 1e3, 2), min_us=round(mn * 1e3, 2),
                       GBps=round(byt / (med * 1e-3) / 1e9, 1),
                       hbm_frac=round(byt / (med * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
                       tokens_per_s=round(wd.batch / (med * 1e-3), 1),
-                      alg_bytes_per_step=int(byt), steps_timed=args.decode_steps)
+                      alg_bytes_per_step=int(byt), steps_timed=args.decode_steps,
+                      inputs="%d consecutive steps, state carried, 32 generated input sets in turn"
+                             % args.decode_steps)
         log("decode: %.1f us/step, %.0f GB/s" % (med * 1e3, decode["GBps"]))
     multi = None
     if not args.no_decode:
@@ -820,11 +957,17 @@ def main():
                    "init_state": w.init_state, "parallelism": "single GPU"},
         "roofline": roofline,
         "cpu_baseline": cpu,
-        "state_path": "one-pass state_fwd" if one_pass else "chunk_state + state_passing",
+        "median_ms_per_step": round(fw["median_ms"], 4),
+        "min_ms_per_step": round(fw["min_ms"], 4),
+        "settle_ms": fw["settle_ms"],
+        "settle_calls": fw["settle_calls"],
+        "state_path": PATH_NAMES[fw["path"]],
         "forward_bf16_mfma_frac": round(fwd_flops / (step_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
         "chunk_kernels_bf16_mfma_frac": round(chunk_flops / (chunk_ms * 1e-3) / 1e12
                                               / BF16_PEAK_TFLOPS, 4),
         "kernels": kernels,
+        "forward_y_io_dtype": y_io,
+        "configs": configs,
         "decode": decode,
         "backward": bwd,
         "decode_multi": multi,

@@ -128,8 +128,8 @@ ssd_status ssd_chunked_fwd_workspace_layout(const ssd_dims *dims, int64_t chunk_
  * workspace): chunk_cumsum, chunk_state, state_passing, chunk_scan in this
  * order give y, final_state and every intermediate.  ssd_chunked_fwd takes
  * one of three paths (ssd_chunked_fwd_path says which): the four stages
- * (fp32 io), chunk_cumsum + the one-pass ssd_state_fwd stage + chunk_scan,
- * or the fused pass described at ssd_fwd_path (bf16 io, the default).
+ * (fp32 io), chunk_cumsum + the one-pass ssd_state_fwd stage + chunk_scan
+ * (bf16 io, the default), or the fused pass described at ssd_fwd_path.
  *
  * chunk_cumsum: reads dt, A; writes G and DT.  One wavefront-level prefix
  *   sum per (b, h, chunk) ("Accelerating Mamba-2 ...", section "Kernel 1").
@@ -180,7 +180,10 @@ ssd_status ssd_state_fwd(const void *x, const void *B, const float *init_state,
  *   SSD_PATH_FUSED       chunk_cumsum with the per-chunk C B^T tiles, then one
  *                        pass per (b, h) that carries the state through the
  *                        chunks in registers and writes y as it goes (neither
- *                        S nor h_prev exists; x is read once).  bf16 io.
+ *                        S nor h_prev exists; x is read once; the chunk-state
+ *                        product is taken in fp16, so |B| and |x dt| must stay
+ *                        below 65504).  bf16 io; selected only through
+ *                        ssd_set_path_override (slower on the shapes measured).
  * All three give y and final_state within the same tolerances; they are
  * not bitwise equal to one another (fp32 summation order).
  */

@@ -22,7 +22,7 @@ LIB = os.path.join(PKG, "libssd.so")
 ARCH = "gfx950"
 
 SOURCES = ["chunk_cumsum.hip", "chunk_state.hip", "state_passing.hip", "state_fwd.hip",
-           "chunk_scan.hip", "chunk_bwd.hip",
+           "chunk_scan.hip", "fused_fwd.hip", "chunk_bwd.hip",
            "decode_step.hip", "decode_lowp.hip", "ssd_api.cpp"]
 
 # -packed-fp32-ops: keep the compiler from emitting packed fp32 VALU ops.

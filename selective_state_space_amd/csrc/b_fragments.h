@@ -11,11 +11,16 @@ namespace ssd {
 
 // B of one (b, chunk, group) laid out as the MFMA B operand of the state
 // product: fragment (slab js, n-tile nt) is 64 lanes x 16 bytes, lane
-// (m, q) holding B[32 js + 8 q + e][n] for e = 0..7 and
-// n = 64 (nt / 4) + 4 m + nt % 4.  Tokens past T are zero.  One workgroup per
-// (b, chunk, group, slab) stages the 32 x N slab in LDS with coalesced 16-byte
-// row loads and writes the N/16 fragments with 16-byte stores.
-template <int L, int N>
+// (m, q) holding B[32 js + r(q, e)][n] for e = 0..7 and
+// n = 64 (nt / 4) + 4 m + nt % 4, with the slab row r(q, e) = 8 q + e (plain
+// order), or with PERM r(q, e) = 16 [e >= 4] + 4 q + e % 4, the K order of
+// the fused forward's x fragments; with F16 the values are converted to fp16
+// (round to nearest even, exact for bf16 values of fp16's normal range;
+// magnitudes above 65504 saturate there).  Tokens past T are zero.  One
+// workgroup per (b, chunk, group, slab) stages the 32 x N slab in LDS with
+// coalesced 16-byte row loads and writes the N/16 fragments with 16-byte
+// stores.
+template <int L, int N, bool PERM = false, bool F16 = false>
 __device__ __forceinline__ void b_fragments_block(const uint16_t *__restrict__ B,
                                                   uint4 *__restrict__ BF, int64_t T, int32_t G,
                                                   int32_t nc, int64_t blk) {
@@ -43,8 +48,19 @@ __device__ __forceinline__ void b_fragments_block(const uint16_t *__restrict__ B
         uint4 v;
         uint32_t *vw = reinterpret_cast<uint32_t *>(&v);
 #pragma unroll
-        for (int rr = 0; rr < 4; ++rr)
-            vw[rr] = (uint32_t)tile[8 * q + 2 * rr][n] | ((uint32_t)tile[8 * q + 2 * rr + 1][n] << 16);
+        for (int rr = 0; rr < 4; ++rr) {
+            const int e0 = 2 * rr, e1 = 2 * rr + 1;
+            const int r0 = PERM ? 16 * (e0 >> 2) + 4 * q + (e0 & 3) : 8 * q + e0;
+            const int r1 = PERM ? 16 * (e1 >> 2) + 4 * q + (e1 & 3) : 8 * q + e1;
+            if constexpr (F16) {
+                const float f0 = fminf(fmaxf(bf16_to_f32(tile[r0][n]), -65504.f), 65504.f);
+                const float f1 = fminf(fmaxf(bf16_to_f32(tile[r1][n]), -65504.f), 65504.f);
+                const f16x2_t hv = {(_Float16)f0, (_Float16)f1};
+                vw[rr] = __builtin_bit_cast(uint32_t, hv);
+            } else {
+                vw[rr] = (uint32_t)tile[r0][n] | ((uint32_t)tile[r1][n] << 16);
+            }
+        }
         BF[blk * (NT * 64) + k] = v;
     }
 }

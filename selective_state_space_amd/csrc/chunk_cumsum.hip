@@ -24,6 +24,7 @@
 // adds its exclusive prefix back.
 
 #include "b_fragments.h"
+#include "cb_tiles.h"
 #include "ssd_device.h"
 #include "ssd_launch.h"
 
@@ -159,7 +160,64 @@ hipError_t launch_cumsum_bfrag(const Shape &s, const float *dt, const float *A, 
     return hipGetLastError();
 }
 
+// Everything the fused forward needs before its sequential pass, in one
+// launch of independent workgroups: the cumsum (first ncum), B in the fused
+// pass's fragment order and in fp16 (next nbf), and the C B^T tiles (the rest).
+template <int L, int N>
+__global__ __launch_bounds__(256) void fused_prep_kernel(
+    const float *__restrict__ dt, const float *__restrict__ A, float *__restrict__ Gws,
+    float *__restrict__ DTws, const float *__restrict__ dt_bias, int32_t softplus, int64_t T,
+    int32_t H, int32_t nc, int32_t nhb, uint32_t ncum, uint32_t nbf,
+    const uint16_t *__restrict__ B, const uint16_t *__restrict__ C, uint4 *__restrict__ BF,
+    uint4 *__restrict__ CBT, int32_t G) {
+    if (blockIdx.x < ncum)   // workgroup-uniform
+        cumsum_block<L>(dt, A, Gws, DTws, dt_bias, softplus, T, H, nc, nhb,
+                        xcd_remap(blockIdx.x, ncum));
+    else if (blockIdx.x < ncum + nbf)
+        b_fragments_block<L, N, true, true>(B, BF, T, G, nc, (int64_t)(blockIdx.x - ncum));
+    else
+        cb_tiles_block<L, N>(B, C, CBT, T, G, nc, (int64_t)(blockIdx.x - ncum - nbf));
+}
+
+template <int L>
+hipError_t launch_fused_prep_l(const Shape &s, const float *dt, const float *A, float *Gws,
+                               float *DTws, const float *dt_bias, int softplus, const void *B,
+                               const void *C, void *bfrag, void *cbt, hipStream_t st) {
+    const int32_t nhb = (int32_t)((s.H + kHeadsPerBlock - 1) / kHeadsPerBlock);
+    const uint64_t ncum = (uint64_t)s.Bt * s.nc * nhb;
+    const uint64_t bcg = (uint64_t)s.Bt * s.nc * s.G;
+    const uint64_t nbf = bcg * (L / 32);
+    const uint64_t ncb = bcg * ((L / 32 + 3) / 4);
+    const uint64_t total = ncum + nbf + ncb;
+    if (total > 0x7fffffffull) return hipErrorInvalidValue;
+    auto go = [&](auto kern) {
+        hipLaunchKernelGGL(kern, dim3((uint32_t)total), dim3(256), 0, st, dt, A, Gws, DTws,
+                           dt_bias, (int32_t)softplus, s.T, (int32_t)s.H, (int32_t)s.nc, nhb,
+                           (uint32_t)ncum, (uint32_t)nbf, (const uint16_t *)B,
+                           (const uint16_t *)C, (uint4 *)bfrag, (uint4 *)cbt, (int32_t)s.G);
+    };
+    if (s.N == 64) go(fused_prep_kernel<L, 64>);
+    else if (s.N == 128) go(fused_prep_kernel<L, 128>);
+    else return hipErrorInvalidValue;
+    return hipGetLastError();
+}
+
 }  // namespace
+
+hipError_t launch_fused_prep(const Shape &s, const float *dt, const float *A, float *Gws,
+                             float *DTws, const float *dt_bias, int softplus, const void *B,
+                             const void *C, void *bfrag, void *cbt, hipStream_t st) {
+    if (s.Bt == 0 || s.nc == 0) return hipSuccess;
+    switch (s.L) {
+    case 64: return launch_fused_prep_l<64>(s, dt, A, Gws, DTws, dt_bias, softplus, B, C, bfrag,
+                                            cbt, st);
+    case 128: return launch_fused_prep_l<128>(s, dt, A, Gws, DTws, dt_bias, softplus, B, C,
+                                              bfrag, cbt, st);
+    case 256: return launch_fused_prep_l<256>(s, dt, A, Gws, DTws, dt_bias, softplus, B, C,
+                                              bfrag, cbt, st);
+    default: return hipErrorInvalidValue;
+    }
+}
 
 hipError_t launch_chunk_cumsum(const Shape &s, const float *dt, const float *A, float *Gws,
                                float *DTws, const float *dt_bias, int softplus, hipStream_t st,

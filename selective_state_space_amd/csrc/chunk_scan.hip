@@ -230,7 +230,7 @@ __device__ __forceinline__ void chunk_scan_group(ScanSmem<L, N> &sm, const ScanA
             sm.CF[pc / NK][pc % NK][lane] = cv[k];
         }
     }
-    __syncthreads();
+    lds_barrier();
     // (C B^T)^T tiles, kept for all heads as packed bf16: tile t, element e =
     // C_i . B_j with i = 16I + m, j = 16J + 4q + e (words: e = 0,1 | 2,3)
     uint2 cbt[NT];
@@ -247,10 +247,10 @@ __device__ __forceinline__ void chunk_scan_group(ScanSmem<L, N> &sm, const ScanA
             if (J & 1) __builtin_amdgcn_sched_barrier(0);
         }
     }
-    __syncthreads();   // BF is dead; the head buffer takes its place
+    lds_barrier();   // BF is dead; the head buffer takes its place
     head_store<L, N>(sm.hd, pre, W, lane);
     float dh = pre.dh;   // D of the head being computed (pre is refilled ahead)
-    __syncthreads();
+    lds_barrier();
 
     for (int hh = 0; hh < nh; ++hh) {
         const int h = h0 + hh;
@@ -406,10 +406,10 @@ __device__ __forceinline__ void chunk_scan_group(ScanSmem<L, N> &sm, const ScanA
             }
         }
         if (hh + 1 < nh) {
-            __syncthreads();   // every wavefront is done with this head's buffer
+            lds_barrier();   // every wavefront is done with this head's buffer
             head_store<L, N>(sm.hd, pre, W, lane);
             dh = pre.dh;
-            __syncthreads();
+            lds_barrier();
         }
     }
 }

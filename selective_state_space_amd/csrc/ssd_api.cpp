@@ -124,7 +124,9 @@ Layout layout_of(const ssd::Shape &s) {
     // S, or on the one-pass state path B in MFMA fragment order
     size_t st = units * s.P * s.N * sizeof(float);
     if (ssd::state_fwd_bfrag_bytes(s) > st) st = ssd::state_fwd_bfrag_bytes(s);
-    const size_t hp = units * s.P * s.N * (s.bf16 ? 2 : 4);
+    // h_prev, or on the fused path the C B^T tiles
+    size_t hp = units * s.P * s.N * (s.bf16 ? 2 : 4);
+    if (s.bf16 && ssd::fused_cbt_bytes(s) > hp) hp = ssd::fused_cbt_bytes(s);
     l.off[0] = 0;
     l.off[1] = align256(l.off[0] + g);
     l.off[2] = align256(l.off[1] + g);
@@ -247,14 +249,19 @@ int state_fwd_rows() { return g_override.state_rows; }
 int state_adj_rows() { return g_override.adj_rows; }
 
 // The forward path a call takes: the override where the shape supports it,
-// else the shape's own choice (the one-pass state stage for bf16 io, the
-// four stages for fp32 io).
+// else the shape's own choice: the one-pass state stage for bf16 io (measured
+// fastest at the 370M, 2.7B and long-context shapes, ahead of the four stages
+// and of the fused pass), the four stages for fp32 io.
 int fwd_path(const ssd::Shape &s) {
     const bool one_pass_ok = ssd::state_fwd_supported(s);
+    const bool fused_ok = ssd::fused_fwd_supported(s);
     switch (g_override.fwd_path) {
     case SSD_PATH_FOUR_STAGE: return SSD_PATH_FOUR_STAGE;
     case SSD_PATH_STATE_FWD:
         if (one_pass_ok) return SSD_PATH_STATE_FWD;
+        break;
+    case SSD_PATH_FUSED:
+        if (fused_ok) return SSD_PATH_FUSED;
         break;
     default: break;
     }
@@ -444,7 +451,21 @@ ssd_status ssd_chunked_fwd_opts(const void *x, const float *dt, const float *A, 
     if ((r = check_ws(s, workspace, workspace_bytes, &w)) != SSD_OK) return r;
     if (s.Bt == 0) return ok();
     hipStream_t st = static_cast<hipStream_t>(stream);
-    const bool one_pass = use_state_fwd(s);
+    const int path = fwd_path(s);
+    if (path == SSD_PATH_FUSED) {
+        // the cumsum, B fragments and C B^T tiles in one launch, then the pass
+        r = hip_result(ssd::launch_fused_prep(s, dt, A, w.G, w.DT, opts ? opts->dt_bias : nullptr,
+                                              opts ? opts->dt_softplus : 0, B, C, w.S, w.hprev,
+                                              st),
+                       "fused_prep", st);
+        if (r != SSD_OK) return r;
+        r = hip_result(ssd::launch_fused_fwd(s, x, C, D, w.G, w.DT, w.S, w.hprev, init_state,
+                                             final_state, y, opts ? opts->z : nullptr, st),
+                       "fused_fwd", st);
+        if (r != SSD_OK) return r;
+        return ok();
+    }
+    const bool one_pass = path == SSD_PATH_STATE_FWD;
     // the one-pass state stage's B fragments are built in the cumsum's launch
     if ((r = run_cumsum(s, dt, A, w, st, opts, one_pass ? B : nullptr)) != SSD_OK) return r;
     if (one_pass) {

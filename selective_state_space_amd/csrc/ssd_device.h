@@ -27,6 +27,14 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
     return pack_bf16x2(f, 0.f) & 0xffffu;
 }
 
+// fp16 operands (the fused forward's chunk-state product)
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));   // 8 fp16, 4 VGPRs
+__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
+    const f16x2_t v = {(_Float16)lo, (_Float16)hi};   // round to nearest even
+    return __builtin_bit_cast(uint32_t, v);
+}
+
 // Streaming 16/8-byte accesses (nontemporal hint) for data that one call
 // touches exactly once: the state slabs S, h_prev, y and the decode state.
 // They keep such streams from displacing reused lines in L2 / the MALL.
@@ -75,6 +83,17 @@ __device__ __forceinline__ void store_y4(void *y, int64_t i, float4 v, bool ybf)
         store_nt(static_cast<float *>(y) + i, v);
 }
 
+// Workgroup barrier for LDS hand-offs only: the wavefront's LDS operations
+// have completed (lgkmcnt 0), then s_barrier.  __syncthreads() also waits for
+// every outstanding global load and store of the wavefront (vmcnt 0: its
+// workgroup-scope fence), which would end every prefetch in flight at each
+// barrier; kernels that exchange only LDS data between wavefronts use this.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+}
+
 // 2^x on the transcendental unit (v_exp_f32).
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -119,6 +138,9 @@ __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) {
 
 __device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma16x16x32(f16x8 a, f16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
 
 // Transpose helpers for building MFMA operands from row-major tiles.

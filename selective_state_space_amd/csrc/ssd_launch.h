@@ -37,6 +37,20 @@ hipError_t launch_state_fwd(const Shape &s, const void *x, const void *B, const 
                             const float *DTws, const float *init, void *hprev, float *fin,
                             void *bfrag, int rows_per_block, bool hprev_f32, hipStream_t st,
                             bool bfrag_ready = false);
+// The fused forward (bf16 io): launch_fused_prep runs the cumsum (G, DT), lays
+// B out in the fused pass's fragment order (bfrag, state_fwd_bfrag_bytes(s))
+// and forms the causal C B^T tiles (cbt, fused_cbt_bytes(s)), in one launch;
+// launch_fused_fwd then carries the state through the chunks of every (b, h)
+// and writes y (and the final state) in one pass.
+bool fused_fwd_supported(const Shape &s);
+size_t fused_cbt_bytes(const Shape &s);
+hipError_t launch_fused_prep(const Shape &s, const float *dt, const float *A, float *Gws,
+                             float *DTws, const float *dt_bias, int softplus, const void *B,
+                             const void *C, void *bfrag, void *cbt, hipStream_t st);
+hipError_t launch_fused_fwd(const Shape &s, const void *x, const void *C, const float *D,
+                            const float *Gws, const float *DTws, const void *bfrag,
+                            const void *cbt, const float *init, float *fin, void *y,
+                            const void *z, hipStream_t st);
 // The backward's adjoint scan in the same one-pass form, chunks last to
 // first: ghat[c] (fp32, the adjoint of the state leaving chunk c) and dinit
 // (NULL = not written) from dy (fp32), C (bf16) and dfinal (NULL = zero);

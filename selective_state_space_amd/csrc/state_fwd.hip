@@ -426,7 +426,7 @@ __global__ __launch_bounds__(256, 2) void state_fwd_kernel(FwdArgs a, uint32_t n
     float glc = glv;                 // last G of the chunk being multiplied
     if (tid < L) sm.w[0][tid] = ADJ ? fast_exp2(gv) : dtv * fast_exp2(glc - gv);
     load_g(c1);
-    __syncthreads();
+    lds_barrier();
     if (builds) {
         build(0, 0);
         load_x(c1, 0);
@@ -440,7 +440,7 @@ __global__ __launch_bounds__(256, 2) void state_fwd_kernel(FwdArgs a, uint32_t n
     for (int32_t c = 0; c < a.nc; ++c) {
         const int32_t cn = c + 1, cnn = c + 2;   // may run past the end (zero-range loads)
         // ---- first half of chunk c (fragments in AF[0]) ----
-        __syncthreads();
+        lds_barrier();
         store_hprev(c);              // the state entering chunk c
         const float dec = fast_exp2(glc);
 #pragma unroll
@@ -453,7 +453,7 @@ __global__ __launch_bounds__(256, 2) void state_fwd_kernel(FwdArgs a, uint32_t n
         mfma_half(0, c, cn, 1, c & 1);   // and build the second half of chunk c
         if (builds) load_x(cn, 1);
         // ---- second half of chunk c (fragments in AF[1]) ----
-        __syncthreads();
+        lds_barrier();
         mfma_half(1, c, cn, 0, (c + 1) & 1);   // and build the first half of chunk c + 1
         if (builds) load_x(cnn, 0);
         glc = gln;

@@ -342,6 +342,10 @@ def set_path_override(fwd: int = -1, state_rows: int = 0, adj_rows: int = 0):
 
 
 def ssd_chunk_scan(a: FwdArgs):
+    """The chunk_scan stage (no layer options): writes y in float32."""
+    if a.y.dtype != torch.float32:
+        raise ValueError("the stage call ssd_chunk_scan writes y in float32; these arguments "
+                         "hold a %s y (y_io_dtype): use ssd_chunked_fwd" % a.y.dtype)
     lib = load_library()
     _check("ssd_chunk_scan", lib.ssd_chunk_scan(_ptr(a.x), _ptr(a.B), _ptr(a.C), _ptr(a.D),
                                                 _ptr(a.y), a.L, ctypes.byref(a.dims), _ptr(a.ws),

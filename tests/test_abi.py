@@ -151,6 +151,8 @@ def test_path_query_and_override():
         assert q(dims(Bt=8, T=4096, H=80, G=1, io=ssd.SSD_F32)) == 0 and out.value == 0
         ssd.set_path_override(ssd.PATH_FOUR_STAGE)
         assert q(dims(Bt=8, T=4096, H=80, G=1)) == 0 and out.value == 0
+        ssd.set_path_override(ssd.PATH_FUSED)
+        assert q(dims(Bt=8, T=4096, H=80, G=1)) == 0 and out.value == ssd.PATH_FUSED
         ssd.set_path_override(ssd.PATH_STATE_FWD, 2)
         assert q(dims(Bt=1, T=4096, H=8, G=1)) == 0 and out.value == ssd.PATH_STATE_FWD
         # an override the shape does not support is ignored (fp32 io: four stages only)

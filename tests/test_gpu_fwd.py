@@ -51,6 +51,20 @@ def test_small_shapes(io, L, N):
     assert_close(host(fin), fr, io, "final")
 
 
+@pytest.mark.parametrize("L", [64, 128, 256])
+@pytest.mark.parametrize("N", [64, 128])
+def test_small_shapes_fused_path(L, N, force_path):
+    # every (L, N) instantiation of the fused pass, ragged last chunk, init state
+    force_path("fused")
+    T = 2 * L + 37
+    log("small fused", "L", L, "N", N, "T", T)
+    inp = gen.make_small(2, T, 4, 64, N, 2, gen.BF16, init_state=True, seed=L + N + 1)
+    y, fin = run_fwd(inp, gen.BF16, L)
+    yr, fr = oracle_full(inp)
+    assert_close(host(y), yr, gen.BF16, "fused y")
+    assert_close(host(fin), fr, gen.BF16, "fused final")
+
+
 @pytest.mark.parametrize("io", [gen.F32, gen.BF16])
 def test_single_chunk_and_short_sequences(io):
     for T in (1, 5, 63, 64, 65):
@@ -89,7 +103,7 @@ def test_intermediates_against_chunked_reference(io):
 
 
 @pytest.mark.parametrize("io,path", [(gen.F32, "auto"), (gen.BF16, "0"), (gen.BF16, "4")])
-def test_fused_call_equals_stage_calls_bitwise(io, path, force_path):
+def test_whole_call_equals_stage_calls_bitwise(io, path, force_path):
     # ssd_chunked_fwd is cumsum, state + passing or the one-pass state stage, scan
     if path != "auto":
         force_path(path)
@@ -105,9 +119,9 @@ def test_fused_call_equals_stage_calls_bitwise(io, path, force_path):
     assert torch.equal(y1, a.y) and torch.equal(f1, a.final)
 
 
-@pytest.mark.parametrize("rows", ["0", "4", "2", "1"])
-def test_both_state_paths_against_oracle(rows, force_path):
-    # the same forward through the two stages and through each one-pass split
+@pytest.mark.parametrize("rows", ["0", "4", "2", "1", "fused"])
+def test_every_path_against_oracle(rows, force_path):
+    # the same forward through the four stages, each one-pass split and the fused pass
     force_path(rows)
     inp = gen.make_small(2, 3 * 128 + 21, 4, 64, 128, 2, gen.BF16, init_state=True, seed=83)
     y, fin = run_fwd(inp, gen.BF16, 128)
@@ -127,7 +141,7 @@ def test_reruns_are_bitwise_identical(io):
         assert torch.equal(y, outs[0][0]) and torch.equal(f, outs[0][1])
 
 
-@pytest.mark.parametrize("rows", ["0", "4"])
+@pytest.mark.parametrize("rows", ["0", "4", "fused"])
 def test_init_state_may_alias_final_state(rows, force_path):
     force_path(rows)
     io = gen.BF16
@@ -143,7 +157,8 @@ def test_init_state_may_alias_final_state(rows, force_path):
     assert torch.equal(y1, y2) and torch.equal(f1, st)
 
 
-@pytest.mark.parametrize("io,rows", [(gen.F32, ""), (gen.BF16, "0"), (gen.BF16, "4")])
+@pytest.mark.parametrize("io,rows", [(gen.F32, ""), (gen.BF16, "0"), (gen.BF16, "4"),
+                                     (gen.BF16, "fused")])
 def test_chunk_aligned_split_equals_one_call(io, rows, force_path):
     force_path(rows)
     L = 64
@@ -162,7 +177,8 @@ def test_chunk_aligned_split_equals_one_call(io, rows, force_path):
     assert torch.equal(fb, f)
 
 
-@pytest.mark.parametrize("io,rows", [(gen.F32, ""), (gen.BF16, "0"), (gen.BF16, "4")])
+@pytest.mark.parametrize("io,rows", [(gen.F32, ""), (gen.BF16, "0"), (gen.BF16, "4"),
+                                     (gen.BF16, "fused")])
 def test_empty_sequence_passes_state_through(io, rows, force_path):
     force_path(rows)
     dt = torch.bfloat16 if io == gen.BF16 else torch.float32
@@ -213,10 +229,11 @@ def test_strong_decay_does_not_overflow():
 
 # --- the full-size workloads, every (b, h) pair ----------------------------------
 
-@pytest.mark.parametrize("idx,rows", [(1, ""), (1, "0"), (2, ""), (2, "0"), (2, "4"), (3, "")])
+@pytest.mark.parametrize("idx,rows", [(1, ""), (1, "0"), (1, "fused"), (2, ""), (2, "0"),
+                                      (2, "fused"), (3, ""), (3, "fused")])
 def test_full_size_workload(idx, rows, force_path):
-    # rows "" = the path the shape selects; "0" = the four stages; "4" = the
-    # one-pass state stage with all four row sets per workgroup
+    # rows "" = the path the shape selects (the one-pass state stage for
+    # bf16); "0" = the four stages; "fused" = the fused pass
     force_path(rows)
     w = gen.WORKLOADS[idx]
     log("workload", w.name, w.description, "rows", rows or "auto")
@@ -260,9 +277,21 @@ def test_full_size_y_in_io_dtype():
     compare_all_pairs(oracle, inp, y16, f16, w.io_dtype, w.name, y_io=True)
 
 
-@pytest.mark.parametrize("io", [gen.F32, gen.BF16])
-def test_one_head_per_group(io):
+def test_stage_call_refuses_io_dtype_y():
+    # the stage calls write y in float32: a y allocated in bf16 for the
+    # y_io_dtype option is refused on the host, before anything is launched
+    inp = gen.make_small(1, 64, 2, 64, 64, 1, gen.BF16, seed=3)
+    t = upload_fwd(inp, gen.BF16)
+    a = ssd.FwdArgs(t["x"], t["dt"], t["A"], t["B"], t["C"], t["D"], 64, y_io_dtype=True)
+    assert a.y.dtype == torch.bfloat16
+    with pytest.raises(ValueError):
+        ssd.ssd_chunk_scan(a)
+
+
+@pytest.mark.parametrize("io,rows", [(gen.F32, ""), (gen.BF16, ""), (gen.BF16, "fused")])
+def test_one_head_per_group(io, rows, force_path):
     # G = H: every head has its own B and C (no sharing across heads)
+    force_path(rows)
     L = 128
     inp = gen.make_small(2, 3 * L + 11, 8, 64, 128, 8, io, init_state=True, seed=89)
     log("one head per group", io)
@@ -272,7 +301,7 @@ def test_one_head_per_group(io):
     assert_close(host(fin), fr, io, "G=H final")
 
 
-@pytest.mark.parametrize("rows", ["", "0", "4"])
+@pytest.mark.parametrize("rows", ["", "0", "fused"])
 def test_partial_last_head_block(rows, force_path):
     # chunk_scan sizes its head blocks for about 256 workgroups: 3 sequences of
     # 3 chunks (one group) give blocks of 3 heads, so the last block of the 80

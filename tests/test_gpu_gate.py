@@ -56,9 +56,11 @@ def gated_case(io, Bt, T, H, N, G, L, seed, bias=True, softplus=True, gate=True,
 
 @pytest.mark.parametrize("io", [gen.F32, gen.BF16])
 @pytest.mark.parametrize("L,N", [(64, 64), (128, 128), (256, 128)])
-@pytest.mark.parametrize("rows", ["", "0"])
+@pytest.mark.parametrize("rows", ["", "0", "fused"])
 def test_gated_forward(io, L, N, rows, force_path):
-    """rows "" lets the library pick the state path; "0" forces the two-stage one."""
+    """rows "" lets the library pick the path (the one-pass state stage for
+    bf16); "0" forces the four stages, "fused" the fused pass (bf16 only; fp32
+    ignores it)."""
     force_path(rows)
     T = 2 * L + 29
     log("gated forward", io, "L", L, "N", N, "rows", rows or "auto")
