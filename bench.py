@@ -87,6 +87,16 @@ def algorithmic(w, io_bytes: int, y_bytes: int = 4):
     out["chunk_scan"] = dict(
         bytes=tok_x + tok_y + 2 * tok_bc + units * P * N * io_bytes + gdt,
         flops=units * (2 * L * P * N + 2 * tri * P) + (Bt * G * nc) * 2 * tri * N)
+    # the fused path: one prepass launch (cumsum; B in fp16 fragment order; the
+    # causal C B^T tiles in pairs, 16 bytes a lane, 64 lanes per pair of 16x16
+    # tiles) and the pass itself (per-group operands counted once)
+    nb = L // 16
+    cbt = Bt * nc * G * ((nb + 1) // 2) * ((nb + 2) // 2) * 64 * 16
+    out["fused_prep"] = dict(bytes=Bt * T * H * 4 + gdt + 3 * tok_bc + cbt,
+                             flops=2 * Bt * T * H + (Bt * G * nc) * 2 * tri * N)
+    out["fused_fwd"] = dict(
+        bytes=tok_x + tok_y + 2 * tok_bc + cbt + gdt + (state if w.init_state else 0) + state,
+        flops=units * (4 * L * P * N + 2 * tri * P + 2 * P * N))
     return out
 
 
@@ -115,7 +125,9 @@ def kernel_source_sha(kernel: str) -> str:
     csrc = os.path.join(ROOT, "selective_state_space_amd", "csrc")
     h = hashlib.sha256()
     files = {"b_fragments": ("state_fwd.hip", "b_fragments.h"),
-             "cumsum_bfrag": ("chunk_cumsum.hip", "b_fragments.h")}.get(kernel, (kernel + ".hip",))
+             "cumsum_bfrag": ("chunk_cumsum.hip", "b_fragments.h"),
+             "fused_prep": ("chunk_cumsum.hip", "b_fragments.h", "cb_tiles.h"),
+             "fused_fwd": ("fused_fwd.hip", "cb_tiles.h")}.get(kernel, (kernel + ".hip",))
     for f in files + ("ssd_device.h",):
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(fh.read())
@@ -136,21 +148,30 @@ def measured_traffic(kernel: str, workload: str):
     return int(k["hbm_bytes_per_launch"])
 
 
-PROFILE_CMD = "python3 bench.py --steps 10 --warmup 3 --no-cpu-baseline --no-decode"
+PROFILE_CMD = ("python3 bench.py --forward-only --path=-1,2 --y-dtype both --steps 10 --warmup 3 "
+               "--settle-ms 0")
+TRACE_CMD = "python3 bench.py --no-cpu-baseline --no-configs"
 
 
 def profile_kind(name: str):
     """The algorithmic-bytes entry of a forward kernel's (demangled) name; None
     for every other kernel (the gated chunk_scan included)."""
     if "chunk_scan_bf16_kernel" in name:
-        args = name[name.index("<") + 1:name.index(">")].split(",")
-        return "chunk_scan" if args[-1].strip() == "false" else None
+        # <L, N, GATE, YBF>: the plain forward's launch, with y in fp32 or bf16
+        args = [v.strip() for v in name[name.index("<") + 1:name.index(">")].split(",")]
+        if args[2] != "false":
+            return None
+        return "chunk_scan_ybf" if len(args) > 3 and args[3] == "true" else "chunk_scan"
     if "state_fwd_kernel" in name:
         # the forward's mode (bf16 h_prev) only: the backward runs the same
         # kernel with fp32 h_prev (mode 1) and as its adjoint scan (mode 2)
         args = name[name.index("<") + 1:name.index(">")].split(",")
         return "state_fwd_kernel" if args[-1].strip() == "0" else None
-    for k in ("chunk_cumsum", "chunk_state", "state_passing", "b_fragments", "cumsum_bfrag"):
+    if "fused_fwd_kernel" in name:
+        args = name[name.index("<") + 1:name.index(">")].split(",")
+        return "fused_fwd" if args[-1].strip() == "false" else None
+    for k in ("chunk_cumsum", "chunk_state", "state_passing", "b_fragments", "cumsum_bfrag",
+              "fused_prep"):
         if k + "_kernel" in name:
             return k
     return None
@@ -173,13 +194,35 @@ def summarize_rocprof(pdir: str, workload: str):
     rows = list(csv.DictReader(open(os.path.join(pdir, "trace", "trace_kernel_stats.csv"))))
     out = ["# Kernel trace: %s forward, decode legs and copy reference" % workload, "",
            "Command (from the repo root, on one MI355X):", "",
-           "    rocprofv3 --kernel-trace --stats -f csv -d <dir> -o trace -- python3 bench.py", "",
+           "    rocprofv3 --kernel-trace --stats -f csv -d <dir> -o trace -- " + TRACE_CMD, "",
            "| kernel | calls | avg us | min us | max us | % of GPU time |",
            "|---|---|---|---|---|---|"]
     for r in rows:
         out.append("| %s | %s | %.1f | %.1f | %.1f | %s |" % (
             short(r["Name"]), r["Calls"], float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3,
             float(r["MaxNs"]) / 1e3, r["Percentage"]))
+    # The same launches split by grid: each leg of the bench (the three
+    # forward workloads, the paths, the decode formats) launches a kernel at a
+    # grid of its own, so a (kernel, grid) row is one leg's launches.
+    tpath = os.path.join(pdir, "trace", "trace_kernel_trace.csv")
+    if os.path.exists(tpath):
+        groups = collections.defaultdict(list)
+        for r in csv.DictReader(open(tpath)):
+            key = (short(r["Kernel_Name"]), int(r["Grid_Size_X"]) // int(r["Workgroup_Size_X"]),
+                   int(r["Workgroup_Size_X"]))
+            groups[key].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+        total = sum(sum(v) for v in groups.values())
+        out += ["", "The same launches by (kernel, grid): one row per leg's launch shape, rows "
+                "above 0.5% of GPU time.", "",
+                "| kernel | workgroups x threads | calls | avg us | median us | min us | % of GPU time |",
+                "|---|---|---|---|---|---|---|"]
+        for (name, nwg, wgs), v in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
+            if sum(v) < 0.005 * total:
+                continue
+            sv = sorted(v)
+            out.append("| %s | %d x %d | %d | %.1f | %.1f | %.1f | %.2f |" % (
+                name, nwg, wgs, len(v), sum(v) / len(v), sv[len(sv) // 2], sv[0],
+                100.0 * sum(v) / total))
     with open(os.path.join(ROOT, "profiles", "kernel_trace_%s.md" % workload), "w") as fh:
         fh.write("\n".join(out) + "\n")
 
@@ -195,7 +238,8 @@ def summarize_rocprof(pdir: str, workload: str):
     cw = [v for k, vs in counters("copyw").items() if "copyBuffer" in k for v in vs if v > 1e5]
     f_fetch, f_write = copy_kib / (sum(cf) / len(cf)), copy_kib / (sum(cw) / len(cw))
     w = gen.BY_NAME[workload]
-    alg = algorithmic(w, 2 if w.io_dtype == gen.BF16 else 4)
+    io = 2 if w.io_dtype == gen.BF16 else 4
+    alg, alg_ybf = algorithmic(w, io), algorithmic(w, io, y_bytes=io)
     res = {"workload": workload,
            "command": "rocprofv3 --pmc FETCH_SIZE (then WRITE_SIZE) -f csv -- " + PROFILE_CMD,
            "copy_calibration": {"bytes_read": 1 << 30, "bytes_written": 1 << 30,
@@ -225,8 +269,8 @@ def summarize_rocprof(pdir: str, workload: str):
         fk = sum(fetch[name]) / len(fetch[name])
         wk = sum(write[name]) / len(write[name])
         hbm = fk * 1024 * f_fetch + wk * 1024 * f_write
-        a = alg[k]["bytes"]
-        src = {"state_fwd_kernel": "state_fwd"}.get(k, k)
+        a = alg_ybf["chunk_scan"]["bytes"] if k == "chunk_scan_ybf" else alg[k]["bytes"]
+        src = {"state_fwd_kernel": "state_fwd", "chunk_scan_ybf": "chunk_scan"}.get(k, k)
         res["kernels"][k] = {"fetch_kib": fk, "write_kib": wk, "hbm_bytes_per_launch": int(hbm),
                              "alg_bytes": a, "source_sha": kernel_source_sha(src)}
         md.append("| %s | %.0f | %.0f | %.4g | %.4g | %.3f |" % (k, fk, wk, hbm, a, hbm / a))
@@ -255,7 +299,8 @@ def summarize_counters(pdir: str, workload: str):
     import re
     cmds = {"fwd": PROFILE_CMD, "bwd": "python3 bench.py --backward-only"}
     keep = re.compile(r"chunk_scan_bf16_kernel<256, 128, false>|state_fwd_kernel<256, 128, 4, [012]>|"
-                      r"chunk_cumsum|cumsum_bfrag|bwd_\w+_kernel")
+                      r"chunk_cumsum|cumsum_bfrag|fused_prep|fused_fwd_kernel<256, 128, false>|"
+                      r"bwd_\w+_kernel")
     out = ["# SQ counters per kernel: %s" % workload, "",
            "Two counter passes (rocprofv3 takes at most 8 SQ counters per pass) for each of",
            "the forward and the backward, from the repo root on one MI355X:", ""]
@@ -731,6 +776,14 @@ def main():
                     help="write profiles/counters_<workload>.md from SQ-counter passes (host only)")
     ap.add_argument("--backward-only", action="store_true",
                     help="only the backward leg (for profiling): prints its mean time per call")
+    ap.add_argument("--forward-only", action="store_true",
+                    help="only the forward leg of --workload (for profiling): prints its median "
+                         "time per call; --path picks the forward path (-1 = the default)")
+    ap.add_argument("--path", default="-1",
+                    help="forward path(s) for --forward-only, comma-separated ssd_fwd_path "
+                         "values (-1 = the default)")
+    ap.add_argument("--y-dtype", choices=("f32", "io", "both"), default="f32",
+                    help="--forward-only: y in fp32, in the io dtype, or one leg of each")
     ap.add_argument("--copy-reference-only", action="store_true",
                     help="only the 1 GiB device copy (calibrates HBM byte counters)")
     args = ap.parse_args()
@@ -760,6 +813,17 @@ def main():
     ssd.load_library()   # fails loudly if libssd.so is missing
 
     w = gen.BY_NAME[args.workload]
+    if args.forward_only:
+        inp = gen.make_fwd(w, 0)
+        yio = {"f32": (False,), "io": (True,), "both": (False, True)}[args.y_dtype]
+        for pth, yi in ((int(v), yi) for v in args.path.split(",") for yi in yio):
+            r = run_forward(w, args.steps, args.warmup, args.settle_ms, path=pth,
+                            y_io=yi, stages=False, inp=inp)
+            print(json.dumps({"workload": w.name, "path": PATH_NAMES[r["path"]],
+                              "y_io_dtype": yi,
+                              "median_us_per_call": round(r["median_ms"] * 1e3, 2),
+                              "min_us_per_call": round(r["min_ms"] * 1e3, 2)}), flush=True)
+        return
     if args.backward_only:
         bms = run_backward(w, 10, 10)
         print(json.dumps({"workload": w.name, "backward_us_per_call": round(bms * 1e3, 2)}),
