@@ -99,9 +99,9 @@ struct ScanArgs {
     const uint16_t *x, *Bm, *Cm, *hprev;
     const uint16_t *z;   // output gate (GATE instantiations only)
     const float *D, *Gws, *DTws;
-    void *y;             // float32, or bf16 when ybf
+    void *y;             // float32, or bf16 in the YBF instantiations
     int64_t T;
-    int32_t H, G, nc, hpg, NH, nhb, ybf;
+    int32_t H, G, nc, hpg, NH, nhb;
 };
 
 // Everything one head of the workgroup needs, loaded into registers (issued
@@ -192,7 +192,7 @@ __device__ __forceinline__ void head_store(typename ScanSmem<L, N>::Head &hd,
     }
 }
 
-template <int L, int N, bool RAGGED, bool GATE, int W>
+template <int L, int N, bool RAGGED, bool GATE, bool YBF, int W>
 __device__ __forceinline__ void chunk_scan_group(ScanSmem<L, N> &sm, const ScanArgs<L, N> &a,
                                                  int64_t b, int32_t c, int32_t g, int32_t h0,
                                                  int32_t nh, int32_t nvalid) {
@@ -400,8 +400,7 @@ __device__ __forceinline__ void chunk_scan_group(ScanSmem<L, N> &sm, const ScanA
 #pragma unroll
                         for (int s = 0; s < 4; ++s) o[s] *= fast_silu(zf[s]);
                     }
-                    store_y4(a.y, yb + il * XR + 4 * m, make_float4(o[0], o[1], o[2], o[3]),
-                             a.ybf != 0);
+                    store_y4(a.y, yb + il * XR + 4 * m, make_float4(o[0], o[1], o[2], o[3]), YBF);
                 }
             }
         }
@@ -414,33 +413,33 @@ __device__ __forceinline__ void chunk_scan_group(ScanSmem<L, N> &sm, const ScanA
     }
 }
 
-template <int L, int N, bool RAGGED, bool GATE>
+template <int L, int N, bool RAGGED, bool GATE, bool YBF>
 __device__ __forceinline__ void chunk_scan_dispatch(ScanSmem<L, N> &sm, const ScanArgs<L, N> &a,
                                                     int64_t b, int32_t c, int32_t g, int32_t h0,
                                                     int32_t nh, int32_t nvalid) {
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     if constexpr (ScanWaves<L>::NW == 8) {
         switch (w) {
-        case 0: chunk_scan_group<L, N, RAGGED, GATE, 0>(sm, a, b, c, g, h0, nh, nvalid); break;
-        case 1: chunk_scan_group<L, N, RAGGED, GATE, 1>(sm, a, b, c, g, h0, nh, nvalid); break;
-        case 2: chunk_scan_group<L, N, RAGGED, GATE, 2>(sm, a, b, c, g, h0, nh, nvalid); break;
-        case 3: chunk_scan_group<L, N, RAGGED, GATE, 3>(sm, a, b, c, g, h0, nh, nvalid); break;
-        case 4: chunk_scan_group<L, N, RAGGED, GATE, 4>(sm, a, b, c, g, h0, nh, nvalid); break;
-        case 5: chunk_scan_group<L, N, RAGGED, GATE, 5>(sm, a, b, c, g, h0, nh, nvalid); break;
-        case 6: chunk_scan_group<L, N, RAGGED, GATE, 6>(sm, a, b, c, g, h0, nh, nvalid); break;
-        default: chunk_scan_group<L, N, RAGGED, GATE, 7>(sm, a, b, c, g, h0, nh, nvalid); break;
+        case 0: chunk_scan_group<L, N, RAGGED, GATE, YBF, 0>(sm, a, b, c, g, h0, nh, nvalid); break;
+        case 1: chunk_scan_group<L, N, RAGGED, GATE, YBF, 1>(sm, a, b, c, g, h0, nh, nvalid); break;
+        case 2: chunk_scan_group<L, N, RAGGED, GATE, YBF, 2>(sm, a, b, c, g, h0, nh, nvalid); break;
+        case 3: chunk_scan_group<L, N, RAGGED, GATE, YBF, 3>(sm, a, b, c, g, h0, nh, nvalid); break;
+        case 4: chunk_scan_group<L, N, RAGGED, GATE, YBF, 4>(sm, a, b, c, g, h0, nh, nvalid); break;
+        case 5: chunk_scan_group<L, N, RAGGED, GATE, YBF, 5>(sm, a, b, c, g, h0, nh, nvalid); break;
+        case 6: chunk_scan_group<L, N, RAGGED, GATE, YBF, 6>(sm, a, b, c, g, h0, nh, nvalid); break;
+        default: chunk_scan_group<L, N, RAGGED, GATE, YBF, 7>(sm, a, b, c, g, h0, nh, nvalid); break;
         }
     } else {
         switch (w) {
-        case 0: chunk_scan_group<L, N, RAGGED, GATE, 0>(sm, a, b, c, g, h0, nh, nvalid); break;
-        case 1: chunk_scan_group<L, N, RAGGED, GATE, 1>(sm, a, b, c, g, h0, nh, nvalid); break;
-        case 2: chunk_scan_group<L, N, RAGGED, GATE, 2>(sm, a, b, c, g, h0, nh, nvalid); break;
-        default: chunk_scan_group<L, N, RAGGED, GATE, 3>(sm, a, b, c, g, h0, nh, nvalid); break;
+        case 0: chunk_scan_group<L, N, RAGGED, GATE, YBF, 0>(sm, a, b, c, g, h0, nh, nvalid); break;
+        case 1: chunk_scan_group<L, N, RAGGED, GATE, YBF, 1>(sm, a, b, c, g, h0, nh, nvalid); break;
+        case 2: chunk_scan_group<L, N, RAGGED, GATE, YBF, 2>(sm, a, b, c, g, h0, nh, nvalid); break;
+        default: chunk_scan_group<L, N, RAGGED, GATE, YBF, 3>(sm, a, b, c, g, h0, nh, nvalid); break;
         }
     }
 }
 
-template <int L, int N, bool GATE>
+template <int L, int N, bool GATE, bool YBF>
 __global__ __launch_bounds__(64 * ScanWaves<L>::NW, 1) void chunk_scan_bf16_kernel(
     ScanArgs<L, N> a, uint32_t nblk) {
     __shared__ ScanSmem<L, N> sm;
@@ -456,9 +455,9 @@ __global__ __launch_bounds__(64 * ScanWaves<L>::NW, 1) void chunk_scan_bf16_kern
     const int64_t rem = a.T - (int64_t)c * L;
     const int32_t nvalid = rem < L ? (int32_t)rem : L;
     if (nvalid == L)
-        chunk_scan_dispatch<L, N, false, GATE>(sm, a, b, c, g, h0, nh, nvalid);
+        chunk_scan_dispatch<L, N, false, GATE, YBF>(sm, a, b, c, g, h0, nh, nvalid);
     else
-        chunk_scan_dispatch<L, N, true, GATE>(sm, a, b, c, g, h0, nh, nvalid);
+        chunk_scan_dispatch<L, N, true, GATE, YBF>(sm, a, b, c, g, h0, nh, nvalid);
 }
 
 template <int L, int N>
@@ -562,7 +561,6 @@ hipError_t launch_scan(const Shape &s, const void *x, const void *B, const void 
         a.Gws = Gws;
         a.DTws = DTws;
         a.y = y;
-        a.ybf = s.ybf16 ? 1 : 0;
         a.T = s.T;
         a.H = (int32_t)s.H;
         a.G = (int32_t)s.G;
@@ -571,12 +569,17 @@ hipError_t launch_scan(const Shape &s, const void *x, const void *B, const void 
         a.NH = heads_per_block(s);
         a.nhb = (a.hpg + a.NH - 1) / a.NH;
         const uint64_t nblk = (uint64_t)s.Bt * s.nc * s.G * a.nhb;
-        if (z)
-            hipLaunchKernelGGL((chunk_scan_bf16_kernel<L, N, true>), dim3((uint32_t)nblk),
-                               dim3(64 * ScanWaves<L>::NW), 0, st, a, (uint32_t)nblk);
+        // the gate and the output type are template parameters: no per-element
+        // branch in the epilogue, and each variant carries its own kernel name
+        const dim3 grid((uint32_t)nblk), blk(64 * ScanWaves<L>::NW);
+        if (z && s.ybf16)
+            hipLaunchKernelGGL((chunk_scan_bf16_kernel<L, N, true, true>), grid, blk, 0, st, a, (uint32_t)nblk);
+        else if (z)
+            hipLaunchKernelGGL((chunk_scan_bf16_kernel<L, N, true, false>), grid, blk, 0, st, a, (uint32_t)nblk);
+        else if (s.ybf16)
+            hipLaunchKernelGGL((chunk_scan_bf16_kernel<L, N, false, true>), grid, blk, 0, st, a, (uint32_t)nblk);
         else
-            hipLaunchKernelGGL((chunk_scan_bf16_kernel<L, N, false>), dim3((uint32_t)nblk),
-                               dim3(64 * ScanWaves<L>::NW), 0, st, a, (uint32_t)nblk);
+            hipLaunchKernelGGL((chunk_scan_bf16_kernel<L, N, false, false>), grid, blk, 0, st, a, (uint32_t)nblk);
     } else {
         const uint64_t nblk = (uint64_t)s.Bt * s.nc * s.H;
         hipLaunchKernelGGL((chunk_scan_f32_kernel<L, N>), dim3((uint32_t)nblk), dim3(256), 0, st,
