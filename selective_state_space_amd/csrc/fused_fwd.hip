@@ -20,14 +20,16 @@
 //   - the output row blocks I0 = W and I1 = L/16 - 1 - W (16 tokens each; the
 //     pair holds L/16 + 1 causal C B^T tiles for every W), all 64 columns p;
 //   - SPW x NTW tiles (16 x 16) of the P x N state, held in MFMA accumulators
-//     (v_mfma_f32_16x16x32_bf16) for the workgroup's whole life;
+//     for the workgroup's whole life;
 //   - slab W (32 tokens) of each chunk's x, which it loads and stages.
 // Per chunk, two phases separated by barriers:
 //   A. (reads the chunk's LDS buffers) scale the state by exp2(G_last); the
 //      inter product C h^T from the h fragments (rows then scaled by
 //      exp2(G_i)); then per 32-token slab the state product (x w) B -- w =
-//      dt exp2(G_last - G) carried as a bf16 head and a bf16 remainder, as the
-//      one-pass state stage does -- and the intra product: each cached C B^T
+//      dt exp2(G_last - G), x w rounded once to fp16 and B in fp16
+//      (v_mfma_f32_16x16x32_f16: fp16's 11-bit significand is what lets one
+//      term do here what the one-pass state stage needs a bf16 head and
+//      remainder for) -- and the intra product: each cached C B^T
 //      tile drained in registers (times exp2(G_i - G_j) dt_j, factored through
 //      the block's last token below the diagonal, exact with a causal select
 //      on it) straight into the A operand; finally y = acc + D x (and the
