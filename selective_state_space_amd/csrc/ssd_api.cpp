@@ -218,13 +218,15 @@ ssd_status scratch_of_current_device(void **out) {
 }
 
 // Stage runners on validated arguments.
-// B non-NULL: also lay B out in w.S for the one-pass state stage (bf16 only).
+// B non-NULL: also lay B out for the one-pass state stage (bf16 only), in
+// bfrag (default: w.S).
 ssd_status run_cumsum(const ssd::Shape &s, const float *dt, const float *A, const Ws &w,
                       hipStream_t st, const ssd_layer_opts *o = nullptr,
-                      const void *B = nullptr) {
+                      const void *B = nullptr, void *bfrag = nullptr) {
+    if (B && !bfrag) bfrag = w.S;
     return hip_result(ssd::launch_chunk_cumsum(s, dt, A, w.G, w.DT, o ? o->dt_bias : nullptr,
                                                o ? o->dt_softplus : 0, st, B,
-                                               B ? static_cast<void *>(w.S) : nullptr),
+                                               B ? bfrag : nullptr),
                       "chunk_cumsum", st);
 }
 ssd_status run_state(const ssd::Shape &s, const void *x, const void *B, const Ws &w,
@@ -737,10 +739,28 @@ ssd_status ssd_chunked_bwd(const void *x, const float *dt, const float *A, const
     // for fp32 io
     void *hp32 = s.bf16 ? static_cast<void *>(base + l.hp32) : w.hprev;
     // as in the forward, the one-pass recompute's B fragments come from the
-    // cumsum's launch
+    // cumsum's launch.  Where both scans take the one-pass form with the same
+    // row split, they run as one grid (ssd::launch_state_pair); the adjoint
+    // then writes ghat into the S region while the recompute still reads B
+    // fragments, so these go to the C B^T region instead (written only after
+    // both scans).
     const bool one_pass = bwd_one_pass(s);
-    if ((r = run_cumsum(s, dt, A, w, st, nullptr, one_pass ? B : nullptr)) != SSD_OK) return r;
-    if (one_pass) {
+    const bool adj_one_pass = one_pass && ssd::state_adj_supported(s);
+    const int rows_f = state_fwd_rows() > 0 ? state_fwd_rows() : ssd::state_fwd_rows_per_block(s);
+    const int rows_a = state_adj_rows() > 0 ? state_adj_rows() : ssd::state_adj_rows_per_block(s);
+    const bool pair = adj_one_pass && rows_f == rows_a;
+    void *bfrag = pair ? static_cast<void *>(base + l.cb3) : static_cast<void *>(w.S);
+    if ((r = run_cumsum(s, dt, A, w, st, nullptr, one_pass ? B : nullptr, bfrag)) != SSD_OK)
+        return r;
+    if (pair) {
+        r = hip_result(ssd::launch_state_pair(s, x, w.G, w.DT, init_state,
+                                              static_cast<float *>(hp32), fin, bfrag,
+                                              static_cast<const float *>(dy), C,
+                                              static_cast<const float *>(dfinal), w.S,
+                                              static_cast<float *>(dinit), base + l.cfr, rows_f,
+                                              st),
+                       "state_pair", st);
+    } else if (one_pass) {
         r = hip_result(ssd::launch_state_fwd(s, x, B, w.G, w.DT, init_state, hp32, fin, w.S,
                                              state_fwd_rows(), true, st, true),
                        "state_fwd", st);
@@ -760,8 +780,11 @@ ssd_status ssd_chunked_bwd(const void *x, const float *dt, const float *A, const
                    s.bf16 ? reinterpret_cast<float *>(base + l.mt) : nullptr,
                    reinterpret_cast<double *>(base + l.part), false};
     // the state adjoint: the one-pass reverse scan where the forward takes the
-    // one-pass form, else per-chunk sums and a separate reverse scan
-    if (one_pass && ssd::state_adj_supported(s)) {
+    // one-pass form (run above when paired), else per-chunk sums and a
+    // separate reverse scan
+    if (pair) {
+        a.ghat_ready = true;
+    } else if (adj_one_pass) {
         r = hip_result(ssd::launch_state_adj(s, static_cast<const float *>(dy), C, w.G,
                                              static_cast<const float *>(dfinal), w.S,
                                              static_cast<float *>(dinit), base + l.cfr,

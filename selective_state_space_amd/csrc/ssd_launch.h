@@ -56,9 +56,19 @@ hipError_t launch_fused_fwd(const Shape &s, const void *x, const void *C, const 
 // (NULL = not written) from dy (fp32), C (bf16) and dfinal (NULL = zero);
 // cfrag: scratch of state_fwd_bfrag_bytes(s) bytes (C in fragment order).
 bool state_adj_supported(const Shape &s);
+int state_fwd_rows_per_block(const Shape &s);   // the row split chosen for a shape
+int state_adj_rows_per_block(const Shape &s);
 hipError_t launch_state_adj(const Shape &s, const float *dy, const void *C, const float *Gws,
                             const float *dfinal, float *ghat, float *dinit, void *cfrag,
                             int rows_per_block, hipStream_t st);
+// Both one-pass scans of the backward in one grid (the same row split for
+// both): the h_prev (fp32) and final-state recompute from x and the B
+// fragments already in bfrag, and the adjoint scan of launch_state_adj (C
+// laid out into cfrag first).
+hipError_t launch_state_pair(const Shape &s, const void *x, const float *Gws, const float *DTws,
+                             const float *init, float *hprev32, float *fin, const void *bfrag,
+                             const float *dy, const void *C, const float *dfinal, float *ghat,
+                             float *dinit, void *cfrag, int rows_per_block, hipStream_t st);
 // K = s.T tokens per sequence; snaps / parent NULL = none; update = 0 leaves
 // the state unwritten.
 struct MultiArgs {

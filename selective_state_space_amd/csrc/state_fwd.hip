@@ -174,8 +174,10 @@ __global__ __launch_bounds__(256) void b_fragments_kernel(const uint16_t *__rest
     b_fragments_block<L, N>(B, BF, T, G, nc, blockIdx.x);
 }
 
+// One (b, h, row split) chain of the scan: lid is the workgroup's logical id.
 template <int L, int N, int SPB, int MODE>
-__global__ __launch_bounds__(256, 2) void state_fwd_kernel(FwdArgs a, uint32_t nblk) {
+__device__ __forceinline__ void state_pass(const FwdArgs &a, uint32_t lid,
+                                           FwdSmem<L, SPB, 2> &sm) {
     using Cfg = FwdCfg<L, N, SPB>;
     constexpr int P = 64, NS = Cfg::NS, HS = Cfg::HS, SW = Cfg::SW, TW = Cfg::TW;
     constexpr int PSPLIT = 4 / SPB;
@@ -186,11 +188,9 @@ __global__ __launch_bounds__(256, 2) void state_fwd_kernel(FwdArgs a, uint32_t n
     constexpr int NTERM = 2;             // bf16 terms of the x*w (dy*w) operand
     constexpr int ES = ADJ ? 4 : 2;      // bytes per element of x (dy)
     using XP = typename XPiece<ADJ && SPB == 4>::type;
-    __shared__ FwdSmem<L, SPB, NTERM> sm;
     // the chunk a step works on: in order, or last to first for the adjoint
     auto phys = [&](int32_t c) { return ADJ ? a.nc - 1 - c : c; };
 
-    const uint32_t lid = xcd_remap(blockIdx.x, nblk);
     const int32_t ps = lid % PSPLIT;
     const uint32_t bh = lid / PSPLIT;
     const int32_t h = bh % a.H;
@@ -471,6 +471,30 @@ __global__ __launch_bounds__(256, 2) void state_fwd_kernel(FwdArgs a, uint32_t n
     }
 }
 
+template <int L, int N, int SPB, int MODE>
+__global__ __launch_bounds__(256, 2) void state_fwd_kernel(FwdArgs a, uint32_t nblk) {
+    __shared__ FwdSmem<L, SPB, 2> sm;
+    state_pass<L, N, SPB, MODE>(a, xcd_remap(blockIdx.x, nblk), sm);
+}
+
+// The backward's two scans in one grid: workgroups [0, na) run the adjoint
+// scan, [na, na + nf) recompute h_prev (fp32) and the final state.  The two
+// are independent; sharing one grid lets the workgroups of each fill the
+// slots the other leaves at its end, where two separate launches would each
+// finish on a partly empty chip (Bt*H chains against two resident
+// workgroups per CU).  The adjoint chains are the longer ones (fp32 dy), so
+// they go first and the shorter recompute chains make up the last round.
+template <int L, int N, int SPB>
+__global__ __launch_bounds__(256, 2) void state_pair_kernel(FwdArgs af, FwdArgs aa, uint32_t nf,
+                                                           uint32_t na) {
+    __shared__ FwdSmem<L, SPB, 2> sm;
+    const uint32_t bid = blockIdx.x;   // workgroup-uniform branch
+    if (bid < na)
+        state_pass<L, N, SPB, kModeAdjoint>(aa, xcd_remap(bid, na), sm);
+    else
+        state_pass<L, N, SPB, kModeF32>(af, xcd_remap(bid - na, nf), sm);
+}
+
 template <int L, int N, int SPB>
 hipError_t launch_fwd(const Shape &s, const FwdArgs &a, int mode, hipStream_t st) {
     const uint64_t nblk = (uint64_t)s.Bt * s.H * (4 / SPB);
@@ -538,30 +562,27 @@ size_t state_fwd_bfrag_bytes(const Shape &s) {
 // the one-pass scan of either direction: x (or dy) and V = B (or C) in, the
 // state before each chunk step (h_prev, or the adjoint ghat) and the last
 // state (final, or dinit) out
-static hipError_t launch_pass(const Shape &s, const void *x, const void *V, const float *Gws,
-                              const float *DTws, const float *init, void *out, float *fin,
-                              void *vfrag, int spb, int mode, hipStream_t st,
-                              bool vfrag_ready = false) {
-    if (s.Bt == 0 || s.H == 0) return hipSuccess;
-    if (s.nc == 0 && !fin) return hipSuccess;
-    if (s.nc > 0 && !vfrag_ready) {
-        const uint64_t nfb = (uint64_t)s.Bt * s.nc * s.G * (s.L / 32);
-        auto lb = [&](auto kern) {
-            hipLaunchKernelGGL(kern, dim3((uint32_t)nfb), dim3(256), 0, st, (const uint16_t *)V,
-                               (uint4 *)vfrag, s.T, (int32_t)s.G, (int32_t)s.nc);
-        };
-        if (s.N == 64) {
-            if (s.L == 64) lb(b_fragments_kernel<64, 64>);
-            else if (s.L == 128) lb(b_fragments_kernel<128, 64>);
-            else lb(b_fragments_kernel<256, 64>);
-        } else {
-            if (s.L == 64) lb(b_fragments_kernel<64, 128>);
-            else if (s.L == 128) lb(b_fragments_kernel<128, 128>);
-            else lb(b_fragments_kernel<256, 128>);
-        }
-        const hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
+// V (B or C, bf16) laid out in MFMA fragment order into vfrag
+static hipError_t launch_vfrag(const Shape &s, const void *V, void *vfrag, hipStream_t st) {
+    const uint64_t nfb = (uint64_t)s.Bt * s.nc * s.G * (s.L / 32);
+    auto lb = [&](auto kern) {
+        hipLaunchKernelGGL(kern, dim3((uint32_t)nfb), dim3(256), 0, st, (const uint16_t *)V,
+                           (uint4 *)vfrag, s.T, (int32_t)s.G, (int32_t)s.nc);
+    };
+    if (s.N == 64) {
+        if (s.L == 64) lb(b_fragments_kernel<64, 64>);
+        else if (s.L == 128) lb(b_fragments_kernel<128, 64>);
+        else lb(b_fragments_kernel<256, 64>);
+    } else {
+        if (s.L == 64) lb(b_fragments_kernel<64, 128>);
+        else if (s.L == 128) lb(b_fragments_kernel<128, 128>);
+        else lb(b_fragments_kernel<256, 128>);
     }
+    return hipGetLastError();
+}
+
+static FwdArgs pass_args(const Shape &s, const void *x, const void *vfrag, const float *Gws,
+                         const float *DTws, const float *init, void *out, float *fin) {
     FwdArgs a;
     a.x = x;
     a.BF = (const uint4 *)vfrag;
@@ -575,12 +596,45 @@ static hipError_t launch_pass(const Shape &s, const void *x, const void *V, cons
     a.G = (int32_t)s.G;
     a.nc = (int32_t)s.nc;
     a.hpg = (int32_t)(s.H / s.G);
+    return a;
+}
+
+// the one-pass scan of either direction: x (or dy) and V = B (or C) in, the
+// state before each chunk step (h_prev, or the adjoint ghat) and the last
+// state (final, or dinit) out
+static hipError_t launch_pass(const Shape &s, const void *x, const void *V, const float *Gws,
+                              const float *DTws, const float *init, void *out, float *fin,
+                              void *vfrag, int spb, int mode, hipStream_t st,
+                              bool vfrag_ready = false) {
+    if (s.Bt == 0 || s.H == 0) return hipSuccess;
+    if (s.nc == 0 && !fin) return hipSuccess;
+    if (s.nc > 0 && !vfrag_ready) {
+        const hipError_t e = launch_vfrag(s, V, vfrag, st);
+        if (e != hipSuccess) return e;
+    }
+    const FwdArgs a = pass_args(s, x, vfrag, Gws, DTws, init, out, fin);
     switch (s.L) {
     case 64: return launch_fwd_l<64>(s, a, spb, mode, st);
     case 128: return launch_fwd_l<128>(s, a, spb, mode, st);
     case 256: return launch_fwd_l<256>(s, a, spb, mode, st);
     default: return hipErrorInvalidValue;
     }
+}
+
+template <int L, int N>
+static hipError_t launch_pair_n(const Shape &s, const FwdArgs &af, const FwdArgs &aa, int spb,
+                                hipStream_t st) {
+    const uint32_t n = (uint32_t)(s.Bt * s.H * (4 / spb));
+    auto lp = [&](auto kern) {
+        hipLaunchKernelGGL(kern, dim3(2 * n), dim3(256), 0, st, af, aa, n, n);
+    };
+    switch (spb) {
+    case 4: lp(state_pair_kernel<L, N, 4>); break;
+    case 2: lp(state_pair_kernel<L, N, 2>); break;
+    case 1: lp(state_pair_kernel<L, N, 1>); break;
+    default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
 }
 
 hipError_t launch_state_fwd(const Shape &s, const void *x, const void *B, const float *Gws,
@@ -591,6 +645,33 @@ hipError_t launch_state_fwd(const Shape &s, const void *x, const void *B, const 
     if (spb <= 0) spb = state_fwd_rows_per_block(s);
     return launch_pass(s, x, B, Gws, DTws, init, hprev, fin, bfrag, spb,
                        hprev_f32 ? kModeF32 : kModeBf16, st, bfrag_ready);
+}
+
+hipError_t launch_state_pair(const Shape &s, const void *x, const float *Gws, const float *DTws,
+                             const float *init, float *hprev32, float *fin, const void *bfrag,
+                             const float *dy, const void *C, const float *dfinal, float *ghat,
+                             float *dinit, void *cfrag, int spb, hipStream_t st) {
+    if (!state_adj_supported(s)) return hipErrorInvalidValue;
+    if (spb <= 0) spb = state_fwd_rows_per_block(s);
+    if (s.Bt == 0 || s.H == 0 || s.nc == 0) {   // nothing to overlap: the two scans alone
+        hipError_t e = launch_pass(s, x, nullptr, Gws, DTws, init, hprev32, fin,
+                                   const_cast<void *>(bfrag), spb, kModeF32, st, true);
+        if (e != hipSuccess) return e;
+        return launch_pass(s, dy, C, Gws, Gws, dfinal, ghat, dinit, cfrag, spb, kModeAdjoint, st);
+    }
+    hipError_t e = launch_vfrag(s, C, cfrag, st);
+    if (e != hipSuccess) return e;
+    const FwdArgs af = pass_args(s, x, bfrag, Gws, DTws, init, hprev32, fin);
+    const FwdArgs aa = pass_args(s, dy, cfrag, Gws, Gws, dfinal, ghat, dinit);
+    switch (s.L * 1000 + s.N) {
+    case 64064: return launch_pair_n<64, 64>(s, af, aa, spb, st);
+    case 64128: return launch_pair_n<64, 128>(s, af, aa, spb, st);
+    case 128064: return launch_pair_n<128, 64>(s, af, aa, spb, st);
+    case 128128: return launch_pair_n<128, 128>(s, af, aa, spb, st);
+    case 256064: return launch_pair_n<256, 64>(s, af, aa, spb, st);
+    case 256128: return launch_pair_n<256, 128>(s, af, aa, spb, st);
+    default: return hipErrorInvalidValue;
+    }
 }
 
 bool state_adj_supported(const Shape &s) {
