@@ -168,8 +168,11 @@ def profile_kind(name: str):
         args = name[name.index("<") + 1:name.index(">")].split(",")
         return "state_fwd_kernel" if args[-1].strip() == "0" else None
     if "fused_fwd_kernel" in name:
-        args = name[name.index("<") + 1:name.index(">")].split(",")
-        return "fused_fwd" if args[-1].strip() == "false" else None
+        # <L, N, GATE, YBF>, as chunk_scan
+        args = [v.strip() for v in name[name.index("<") + 1:name.index(">")].split(",")]
+        if args[2] != "false":
+            return None
+        return "fused_fwd_ybf" if len(args) > 3 and args[3] == "true" else "fused_fwd"
     for k in ("chunk_cumsum", "chunk_state", "state_passing", "b_fragments", "cumsum_bfrag",
               "fused_prep"):
         if k + "_kernel" in name:
@@ -269,8 +272,9 @@ def summarize_rocprof(pdir: str, workload: str):
         fk = sum(fetch[name]) / len(fetch[name])
         wk = sum(write[name]) / len(write[name])
         hbm = fk * 1024 * f_fetch + wk * 1024 * f_write
-        a = alg_ybf["chunk_scan"]["bytes"] if k == "chunk_scan_ybf" else alg[k]["bytes"]
-        src = {"state_fwd_kernel": "state_fwd", "chunk_scan_ybf": "chunk_scan"}.get(k, k)
+        a = (alg_ybf[k[:-4]]["bytes"] if k.endswith("_ybf") else alg[k]["bytes"])
+        src = {"state_fwd_kernel": "state_fwd", "chunk_scan_ybf": "chunk_scan",
+               "fused_fwd_ybf": "fused_fwd"}.get(k, k)
         res["kernels"][k] = {"fetch_kib": fk, "write_kib": wk, "hbm_bytes_per_launch": int(hbm),
                              "alg_bytes": a, "source_sha": kernel_source_sha(src)}
         md.append("| %s | %.0f | %.0f | %.4g | %.4g | %.3f |" % (k, fk, wk, hbm, a, hbm / a))
@@ -298,9 +302,10 @@ def summarize_counters(pdir: str, workload: str):
     import csv
     import re
     cmds = {"fwd": PROFILE_CMD, "bwd": "python3 bench.py --backward-only"}
-    keep = re.compile(r"chunk_scan_bf16_kernel<256, 128, false>|state_fwd_kernel<256, 128, 4, [012]>|"
-                      r"chunk_cumsum|cumsum_bfrag|fused_prep|fused_fwd_kernel<256, 128, false>|"
-                      r"bwd_\w+_kernel")
+    keep = re.compile(r"chunk_scan_bf16_kernel<256, 128, false, (?:false|true)>|"
+                      r"state_fwd_kernel<256, 128, 4, [012]>|state_pair_kernel<256, 128, 4>|"
+                      r"chunk_cumsum|cumsum_bfrag|fused_prep|"
+                      r"fused_fwd_kernel<256, 128, false, (?:false|true)>|bwd_\w+_kernel")
     out = ["# SQ counters per kernel: %s" % workload, "",
            "Two counter passes (rocprofv3 takes at most 8 SQ counters per pass) for each of",
            "the forward and the backward, from the repo root on one MI355X:", ""]

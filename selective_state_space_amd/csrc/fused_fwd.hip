@@ -98,9 +98,9 @@ struct FusedArgs {
     const uint4 *CBT;         // C B^T tile pairs [b][chunk][group][pair slot][64]
     const float *D, *Gws, *DTws, *init;
     float *fin;
-    void *y;                  // float32, or bf16 when ybf
+    void *y;                  // float32, or bf16 in the YBF instantiations
     int64_t T;
-    int32_t H, G, nc, hpg, ybf;
+    int32_t H, G, nc, hpg;
 };
 
 constexpr int kStream = 2;   // buffer-load cache policy: nontemporal (data read once)
@@ -108,7 +108,7 @@ constexpr int kStream = 2;   // buffer-load cache policy: nontemporal (data read
 __device__ __forceinline__ f16x8 as_f16x8(uint4 v) { return __builtin_bit_cast(f16x8, v); }
 
 
-template <int L, int N, bool GATE, int W>
+template <int L, int N, bool GATE, bool YBF, int W>
 __device__ __forceinline__ void fused_body(FusedSmem<L, N> &sm, FusedCbSmem<L> &cbs,
                                            const FusedArgs &a, int64_t b, int32_t h) {
     using Cfg = FusedCfg<L, N>;
@@ -489,7 +489,7 @@ __device__ __forceinline__ void fused_body(FusedSmem<L, N> &sm, FusedCbSmem<L> &
                         for (int s = 0; s < 4; ++s) o[s] *= fast_silu(zf[s]);
                     }
                     store_y4(a.y, yb + (int64_t)il * XR + 4 * m,
-                             make_float4(o[0], o[1], o[2], o[3]), a.ybf != 0);
+                             make_float4(o[0], o[1], o[2], o[3]), YBF);
                 }
             }
         }
@@ -504,7 +504,7 @@ __device__ __forceinline__ void fused_body(FusedSmem<L, N> &sm, FusedCbSmem<L> &
     if (a.fin) store_final();
 }
 
-template <int L, int N, bool GATE>
+template <int L, int N, bool GATE, bool YBF>
 __global__ __launch_bounds__(64 * (L / 32), 1) void fused_fwd_kernel(FusedArgs a, uint32_t nblk) {
     __shared__ FusedSmem<L, N> sm;
     __shared__ FusedCbSmem<L> cbs;
@@ -515,26 +515,30 @@ __global__ __launch_bounds__(64 * (L / 32), 1) void fused_fwd_kernel(FusedArgs a
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     constexpr int NW = L / 32;
     switch (w) {
-    case 0: fused_body<L, N, GATE, 0>(sm, cbs, a, b, h); break;
-    case 1: fused_body<L, N, GATE, 1>(sm, cbs, a, b, h); break;
-    case 2: if constexpr (NW > 2) fused_body<L, N, GATE, 2>(sm, cbs, a, b, h); break;
-    case 3: if constexpr (NW > 2) fused_body<L, N, GATE, 3>(sm, cbs, a, b, h); break;
-    case 4: if constexpr (NW > 4) fused_body<L, N, GATE, 4>(sm, cbs, a, b, h); break;
-    case 5: if constexpr (NW > 4) fused_body<L, N, GATE, 5>(sm, cbs, a, b, h); break;
-    case 6: if constexpr (NW > 4) fused_body<L, N, GATE, 6>(sm, cbs, a, b, h); break;
-    default: if constexpr (NW > 4) fused_body<L, N, GATE, 7>(sm, cbs, a, b, h); break;
+    case 0: fused_body<L, N, GATE, YBF, 0>(sm, cbs, a, b, h); break;
+    case 1: fused_body<L, N, GATE, YBF, 1>(sm, cbs, a, b, h); break;
+    case 2: if constexpr (NW > 2) fused_body<L, N, GATE, YBF, 2>(sm, cbs, a, b, h); break;
+    case 3: if constexpr (NW > 2) fused_body<L, N, GATE, YBF, 3>(sm, cbs, a, b, h); break;
+    case 4: if constexpr (NW > 4) fused_body<L, N, GATE, YBF, 4>(sm, cbs, a, b, h); break;
+    case 5: if constexpr (NW > 4) fused_body<L, N, GATE, YBF, 5>(sm, cbs, a, b, h); break;
+    case 6: if constexpr (NW > 4) fused_body<L, N, GATE, YBF, 6>(sm, cbs, a, b, h); break;
+    default: if constexpr (NW > 4) fused_body<L, N, GATE, YBF, 7>(sm, cbs, a, b, h); break;
     }
 }
 
 template <int L, int N>
 hipError_t launch_fused_ln(const Shape &s, const FusedArgs &a, hipStream_t st) {
     const uint64_t nblk = (uint64_t)s.Bt * s.H;
-    if (a.z)
-        hipLaunchKernelGGL((fused_fwd_kernel<L, N, true>), dim3((uint32_t)nblk), dim3(64 * (L / 32)),
-                           0, st, a, (uint32_t)nblk);
+    // the gate and the output type are template parameters, as in chunk_scan
+    const dim3 grid((uint32_t)nblk), blk(64 * (L / 32));
+    if (a.z && s.ybf16)
+        hipLaunchKernelGGL((fused_fwd_kernel<L, N, true, true>), grid, blk, 0, st, a, (uint32_t)nblk);
+    else if (a.z)
+        hipLaunchKernelGGL((fused_fwd_kernel<L, N, true, false>), grid, blk, 0, st, a, (uint32_t)nblk);
+    else if (s.ybf16)
+        hipLaunchKernelGGL((fused_fwd_kernel<L, N, false, true>), grid, blk, 0, st, a, (uint32_t)nblk);
     else
-        hipLaunchKernelGGL((fused_fwd_kernel<L, N, false>), dim3((uint32_t)nblk),
-                           dim3(64 * (L / 32)), 0, st, a, (uint32_t)nblk);
+        hipLaunchKernelGGL((fused_fwd_kernel<L, N, false, false>), grid, blk, 0, st, a, (uint32_t)nblk);
     return hipGetLastError();
 }
 
@@ -582,7 +586,6 @@ hipError_t launch_fused_fwd(const Shape &s, const void *x, const void *C, const 
     a.G = (int32_t)s.G;
     a.nc = (int32_t)s.nc;
     a.hpg = (int32_t)(s.H / s.G);
-    a.ybf = s.ybf16 ? 1 : 0;
     switch (s.L) {
     case 64: return launch_fused_l<64>(s, a, st);
     case 128: return launch_fused_l<128>(s, a, st);
