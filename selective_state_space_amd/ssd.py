@@ -242,7 +242,7 @@ def ssd_chunked_fwd(x, dt=None, A=None, B=None, C=None, D=None, chunk_size=None,
 
     x [Bt,T,H,P] (float32 or bfloat16), dt [Bt,T,H] f32, A/D [H] f32,
     B/C [Bt,T,G,N] (x's dtype), init_state [Bt,H,P,N] f32 or None.  y is
-    float32 [Bt,T,H,P] whatever the input dtype.  ``y``,
+    [Bt,T,H,P], float32 whatever the input dtype unless ``y_io_dtype``.  ``y``,
     ``final_state`` and ``workspace`` may be passed in to avoid allocation;
     ``final_state`` may be the same tensor as ``init_state``.  ``x`` may
     instead be a prepared FwdArgs (then the other arguments are ignored).

@@ -318,3 +318,32 @@ def test_partial_last_head_block(rows, force_path):
     yr, fr = oracle_full(inp)
     assert_close(host(y), yr, gen.BF16, "partial head block y")
     assert_close(host(fin), fr, gen.BF16, "partial head block final")
+
+
+@pytest.mark.parametrize("rows", ["", "0", "fused"])
+@pytest.mark.parametrize("gate", [False, True])
+@pytest.mark.parametrize("L,N", [(64, 64), (256, 128)])
+def test_y_in_io_dtype_every_path(rows, gate, L, N, force_path):
+    """y stored in bf16 (ssd_layer_opts.y_io_dtype) on every forward path,
+    with and without the output gate: the same call's fp32 y rounded to
+    nearest even, bit for bit (the output type is a template parameter of
+    the kernels that store y, so each instantiation is exercised), and the
+    final state unchanged."""
+    force_path(rows)
+    Bt, T, H, G = 2, 2 * L + 37, 8, 2
+    inp = gen.make_small(Bt, T, H, 64, N, G, gen.BF16, init_state=True, seed=131 + L)
+    t = upload_fwd(inp, gen.BF16)
+    z = None
+    if gate:
+        rng = np.random.default_rng(7)
+        z = torch.from_numpy(gen.bf16_round(rng.normal(0, 1.5, inp.x.shape).astype(np.float32)))
+        z = z.to(torch.bfloat16).cuda()
+    log("y in bf16: path", rows or "auto", "gate", gate, "L", L, "N", N)
+    y32, f32 = ssd.ssd_chunked_fwd(t["x"], t["dt"], t["A"], t["B"], t["C"], t["D"], L,
+                                   t["init_state"], z=z)
+    y16, f16 = ssd.ssd_chunked_fwd(t["x"], t["dt"], t["A"], t["B"], t["C"], t["D"], L,
+                                   t["init_state"], z=z, y_io_dtype=True)
+    torch.cuda.synchronize()
+    assert y16.dtype == torch.bfloat16
+    assert torch.equal(y16, y32.to(torch.bfloat16)), "bf16 y is not the fp32 y rounded"
+    assert torch.equal(f16, f32)
