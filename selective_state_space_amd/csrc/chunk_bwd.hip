@@ -1355,17 +1355,23 @@ __global__ __launch_bounds__(4 * L) void bwd_dx_mfma_kernel(
     // allocator spills with them live; there the epilogue loads them itself)
     constexpr bool kEpiPrefetch = N >= 128;
     float edy[4][NP];
+    // dy, x and dx of this (b, c, h) through buffers whose range ends at the
+    // sequence end: rows past it read 0 and drop their stores without a
+    // branch, so all of a lane's epilogue loads go out before any is used
+    const int64_t tok0 = ((b * T + tc) * H + h) * P;
+    const uint32_t nvt = (uint32_t)(T - tc < L ? T - tc : L), hpb = (uint32_t)(H * P);
+    const auto rdy = make_rsrc(dy + tok0, nvt * hpb * 4u);
+    const auto rxx = make_rsrc(x + tok0, nvt * hpb * 2u);
+    const auto rdx = make_rsrc(dx + tok0, nvt * hpb * 4u);
+    auto eo = [&](int e, int pt) {
+        return (uint32_t)(16 * w + 4 * q + e) * hpb + (uint32_t)(16 * pt + m);
+    };
     auto load_epilogue = [&]() {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int64_t t = tc + 16 * w + 4 * q + e;
-            const bool real = t < T;
+        for (int e = 0; e < 4; ++e)
 #pragma unroll
-            for (int pt = 0; pt < NP; ++pt) {
-                const int64_t o = ((b * T + (real ? t : 0)) * H + h) * P + 16 * pt + m;
-                edy[e][pt] = real ? dy[o] : 0.f;
-            }
-        }
+            for (int pt = 0; pt < NP; ++pt)
+                edy[e][pt] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rdy, 4u * eo(e, pt), 0, 0));
     };
 
     __syncthreads();
@@ -1416,24 +1422,27 @@ __global__ __launch_bounds__(4 * L) void bwd_dx_mfma_kernel(
     }
     // ---- epilogue: rows i = 16w + 4q + e, columns p = 16 pt + m
     const float Dh = D[h], glast = Gs[L - 1];
-    float *tokc = tok + unit * (int64_t)L;
+    if constexpr (!kEpiPrefetch) load_epilogue();
+    uint32_t xr[4][NP];
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+#pragma unroll
+        for (int pt = 0; pt < NP; ++pt)
+            xr[e][pt] = __builtin_amdgcn_raw_buffer_load_b16(rxx, 2u * eo(e, pt), 0, 0);
+    float rowv[3][4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
         const int i = 16 * w + 4 * q + e;
-        const int64_t t = tc + i;
-        const bool real = t < T;
-        const int64_t tt = real ? t : 0;
         const float su = fast_exp2(glast - Gs[i]), sy = fast_exp2(Gs[i]), dti = DTs[i];
         float xu = 0.f, dyy = 0.f, dyx = 0.f;
 #pragma unroll
         for (int pt = 0; pt < NP; ++pt) {
-            const int p = 16 * pt + m;
-            const int64_t o = ((b * T + tt) * H + h) * P + p;
-            const float dyv = kEpiPrefetch ? edy[e][pt] : (real ? dy[o] : 0.f);
-            const float xv = real ? bf16_to_f32(x[o]) : 0.f;
+            const float dyv = edy[e][pt];
+            const float xv = bf16_to_f32((uint16_t)xr[e][pt]);
             const float u = U[pt][e] + su * Ui[pt][e];
             const float yv = Y[pt][e] + sy * Yi[pt][e];
-            if (real) dx[o] = Dh * dyv + dti * u;
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(Dh * dyv + dti * u), rdx,
+                                                  4u * eo(e, pt), 0, 0);
             xu = fmaf(xv, u, xu);
             dyy = fmaf(dyv, yv, dyy);
             dyx = fmaf(dyv, xv, dyx);
@@ -1441,11 +1450,18 @@ __global__ __launch_bounds__(4 * L) void bwd_dx_mfma_kernel(
         xu = group_sum<16>(xu);                       // over the 16 lanes of one q
         dyy = group_sum<16>(dyy);
         dyx = group_sum<16>(dyx);
-        if (m == 0) {
-            tokc[i] = xu;
-            tokc[ntok + i] = dyy - dti * xu;
-            tokc[2 * ntok + i] = dyx;
-        }
+        rowv[0][e] = xu;
+        rowv[1][e] = dyy - dti * xu;
+        rowv[2][e] = dyx;
+    }
+    // lane m < 4 stores row e = m of each plane; the others aim past the
+    // buffer's range and are dropped
+    const uint32_t to = m < 4 ? (uint32_t)(16 * w + 4 * q + m) * 4u : 0x7fffffffu;
+#pragma unroll
+    for (int k = 0; k < 3; ++k) {
+        const float v = m == 0 ? rowv[k][0] : m == 1 ? rowv[k][1] : m == 2 ? rowv[k][2] : rowv[k][3];
+        const auto rt = make_rsrc(tok + k * ntok + unit * (int64_t)L, L * 4u);
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), rt, to, 0, 0);
     }
 }
 

@@ -102,11 +102,23 @@ def test_without_init_and_dfinal(io):
         assert torch.equal(g[k], g2[k]), k
 
 
-def test_reruns_are_bitwise_identical():
+@pytest.mark.parametrize("H,G,T", [(8, 1, 700), (8, 8, 513), (6, 3, 1024), (12, 2, 300)])
+def test_chunk256_heads_and_groups(H, G, T):
+    """256-token chunks (the persistent dx kernel) over head and group
+    counts, one head per group included, and ragged and whole last chunks."""
+    log("bwd L256", "H", H, "G", G, "T", T)
+    inp = gen.make_small(2, T, H, 64, 128, G, gen.BF16, init_state=True, seed=H + G + T)
+    dy, dfin = grads_inputs(inp, 7)
+    g, ref = run_both(inp, gen.BF16, 256, dy, dfin)
+    compare(g, ref, gen.BF16)
+
+
+@pytest.mark.parametrize("L", [128, 256])
+def test_reruns_are_bitwise_identical(L):
     inp = gen.make_small(2, 333, 8, 64, 128, 2, gen.BF16, init_state=True, seed=8)
     dy, dfin = grads_inputs(inp, 4)
     t = upload_fwd(inp, gen.BF16)
-    args = (t["x"], t["dt"], t["A"], t["B"], t["C"], t["D"], 128, dev_tensor(dy), t["init_state"],
+    args = (t["x"], t["dt"], t["A"], t["B"], t["C"], t["D"], L, dev_tensor(dy), t["init_state"],
             dev_tensor(dfin))
     a = ssd.ssd_chunked_bwd(*args)
     b = ssd.ssd_chunked_bwd(*args)
