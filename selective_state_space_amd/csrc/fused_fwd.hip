@@ -121,7 +121,10 @@ __device__ __forceinline__ void fused_body(FusedSmem<L, N> &sm, FusedCbSmem<L> &
     // in-loop issue point (slab index) of the next x: after the last B load
     // of this chunk
     constexpr int XLOAD_AT = NS > R ? NS - R - 1 : 0;
-    const int lane = threadIdx.x & 63, m = lane & 15, q = lane >> 4;
+    // the lane index, refreshed through an opaque copy in each chunk (below):
+    // the per-lane offsets derived from it are recomputed there instead of
+    // being hoisted out of the chunk loop, where they would all stay live
+    int lane = threadIdx.x & 63, m = lane & 15, q = lane >> 4;
     const int32_t g = h / a.hpg;
     const int64_t bh = b * a.H + h;
     const int32_t XR = a.H * P;                   // elements between token rows of x (and y, z)
@@ -129,7 +132,7 @@ __device__ __forceinline__ void fused_body(FusedSmem<L, N> &sm, FusedCbSmem<L> &
     const float Dh = a.D[h];
     // the first of this lane's NTW adjacent state columns; its state rows are
     // p = 4 (4q + e) + S0 + i
-    const int ncol = 64 * (NT0 >> 2) + 4 * m + (NT0 & 3);
+    int ncol = 64 * (NT0 >> 2) + 4 * m + (NT0 & 3);
     auto nvalid_of = [&](int32_t c) -> int32_t {
         const int64_t rem = a.T - (int64_t)c * L;
         return rem < L ? (int32_t)rem : L;
@@ -333,6 +336,14 @@ __device__ __forceinline__ void fused_body(FusedSmem<L, N> &sm, FusedCbSmem<L> &
     lds_barrier();
 
     for (int32_t c = 0; c < a.nc; ++c) {
+        {
+            int t = threadIdx.x;
+            asm volatile("" : "+v"(t));
+            lane = t & 63;
+            m = lane & 15;
+            q = lane >> 4;
+            ncol = 64 * (NT0 >> 2) + 4 * m + (NT0 & 3);
+        }
         const int32_t nvalid = nvalid_of(c);
         const int64_t t0 = (int64_t)c * L;
         // ======== phase A: chunk c from the LDS buffers ========
