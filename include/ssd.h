@@ -338,13 +338,14 @@ ssd_status ssd_decode_multi(float *state, const void *x, const float *dt, const 
  * Super in TensorRT-LLM", section 6.5, and the state types of section 6.6):
  *   SSD_STATE_F16    fp16; round to nearest even, or, with philox_rounds in
  *                    1..10, stochastic rounding: |x| + (r / 2^13) ulp16(|x|)
- *                    rounded toward zero and saturated at 65504, r the low 13
- *                    bits of a word of Philox-4x32 with that many rounds (10
+ *                    rounded toward zero and saturated at 65504, r a 13-bit
+ *                    field of a word of Philox-4x32 with that many rounds (10
  *                    is the generator's standard; Salmon et al., SC'11): one block
- *                    per 4 consecutive elements of a row, counter = flat index
+ *                    per 8 consecutive elements of a row, counter = flat index
  *                    (b, h, p, n) of the first (low word, high word, 0, 0),
  *                    key = seed (low word, high word); element n takes word
- *                    n mod 4.  Vary the seed from call to call.
+ *                    (n mod 8) / 2, its bits 0..12 for even n and 16..28 for
+ *                    odd n.  Vary the seed from call to call.
  *   SSD_STATE_BF16   bf16, round to nearest even.
  *   SSD_STATE_INT16  int16 codes plus one fp32 decode scale per row (b, h, p)
  *                    in `scale` [Bt, H, P]: the stored value is code * scale;

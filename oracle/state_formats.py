@@ -9,8 +9,9 @@
   beside them;
 * fp16, rounded to nearest or stochastically, with the random bits taken
   from a Philox-4x32 counter-based generator (13 bits per element: the bits
-  fp32 carries below fp16's last place) whose round count is a parameter of
-  the kernels (zero rounds meaning no stochastic rounding);
+  fp32 carries below fp16's last place; a 32-bit word serves two elements)
+  whose round count is a parameter of the kernels (zero rounds meaning no
+  stochastic rounding);
 * and, as the same section's dispatch table lists, bf16 (round to nearest).
 
 The update itself is the plain fp64 decode step of the oracle (section 6.1)
@@ -29,11 +30,12 @@ generator's standard count.
 Readings where the page is silent: the abs-max is over
 the N values of a row; codes round half to even and are clipped to
 [-32767, 32767]; an all-zero row stores codes 0 and decode scale 0; one
-Philox block serves 4 consecutive elements of a row, its counter being the
+Philox block serves 8 consecutive elements of a row, its counter being the
 flat index (b, h, p, n) of the first of them (low word, high word, 0, 0) and
-its key the 64-bit seed (low word, high word); element n takes word n mod 4,
-masked to 13 bits; stochastic rounding of x adds (r / 2^13) of fp16's unit
-in the last place at |x| to |x| and rounds toward zero, saturating at 65504.
+its key the 64-bit seed (low word, high word); element n takes word
+(n mod 8) // 2, its bits 0..12 for even n and 16..28 for odd n; stochastic
+rounding of x adds (r / 2^13) of fp16's unit in the last place at |x| to |x|
+and rounds toward zero, saturating at 65504.
 """
 
 from __future__ import annotations
@@ -70,15 +72,17 @@ def philox4x32(counter, key, rounds: int = 10):
 
 def state_random_bits(nelem: int, seed: int, start: int = 0, rounds: int = 10):
     """13 random bits for the state elements of flat indices start ..
-    start + nelem - 1 (start a multiple of 4), from one Philox block per 4
-    consecutive elements."""
-    assert start % 4 == 0
-    first = np.arange(start, start + nelem, 4, dtype=np.uint64)
+    start + nelem - 1 (start a multiple of 8), from one Philox block per 8
+    consecutive elements: element k of a block takes word k // 2, its low
+    half's 13 low bits for even k and its high half's for odd k."""
+    assert start % 8 == 0
+    first = np.arange(start, start + nelem, 8, dtype=np.uint64)
     ctr = np.stack([first & np.uint64(MASK32), first >> np.uint64(32),
                     np.zeros_like(first), np.zeros_like(first)], axis=-1)
     key = np.array([seed & MASK32, (seed >> 32) & MASK32], dtype=np.uint64)
-    words = philox4x32(ctr, key, rounds)               # [nelem/4, 4]
-    return (words.reshape(-1)[:nelem] & np.uint32(0x1FFF)).astype(np.int64)
+    words = philox4x32(ctr, key, rounds).astype(np.uint32)      # [nblocks, 4]
+    halves = np.stack([words & np.uint32(0xFFFF), words >> np.uint32(16)], axis=-1)
+    return (halves.reshape(-1)[:nelem] & np.uint32(0x1FFF)).astype(np.int64)
 
 
 def _ulp16(a):

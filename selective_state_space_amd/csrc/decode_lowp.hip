@@ -3,10 +3,12 @@
 // state types of section 6.6's dispatch table):
 //   FMT_F16_RN  fp16, round to nearest even;
 //   FMT_F16_SR  fp16, stochastic rounding: |x| + (r / 2^13) ulp16(|x|),
-//               rounded toward zero and saturated at 65504, with r the low 13
-//               bits of a Philox-4x32 word (the round count is a parameter; one
-//               block per 4 consecutive elements of a row, counter = the flat
-//               index (b, h, p, n) of the first, key = the 64-bit seed);
+//               rounded toward zero and saturated at 65504, with r a 13-bit
+//               field of a Philox-4x32 word (the round count is a parameter;
+//               one block per 8 consecutive elements of a row, counter = the
+//               flat index (b, h, p, n) of the first, key = the 64-bit seed;
+//               element n takes word (n mod 8) / 2, bits 0..12 for even n and
+//               16..28 for odd n);
 //   FMT_BF16    bf16, round to nearest even;
 //   FMT_INT16   int16 codes with one fp32 decode scale per row p: after the
 //               update, encode = 32767 / max|row| and decode = 1 / encode (both
@@ -15,17 +17,17 @@
 // The update and y are those of the fp32 decode step (y from the updated
 // state before it is rounded for storage); only the load and the store of the
 // state change, so the step moves 2 bytes per state element each way instead
-// of 4.  Work split as in decode_step: a workgroup per (b, h), a row of N
-// elements over N/4 lanes with 8-byte accesses; the int16 row maximum is a
-// xor-shuffle reduction over those lanes.
+// of 4.  A workgroup per (b, h); a row of N elements over N/8 lanes with
+// 16-byte accesses (8 elements a lane, so one Philox block per lane and row);
+// the row sums and the int16 row maximum are DPP reductions over those
+// lanes.
 //
 // Philox-4x32 follows its published definition (Salmon, Moraes, Dror, Shaw,
 // "Parallel Random Numbers: As Easy as 1, 2, 3", SC'11): rounds of two
 // 32x32 -> 64-bit products (multipliers 0xD2511F53, 0xCD9E8D57), a
 // swap-and-xor with the key and a Weyl increment of the key.  Generating the
-// bits costs more ALU time than the 16-bit state saves in HBM time (ten
-// rounds: about 300 integer multiplies per lane per step), so this variant
-// is issue-bound, not bandwidth-bound.
+// bits costs ALU time (ten rounds: 20 integer multiplies per block, one
+// block per 8 elements), which is why each word serves two elements.
 
 #include "ssd_device.h"
 #include "ssd_launch.h"
@@ -91,7 +93,8 @@ __global__ __launch_bounds__(256) void decode_lowp_kernel(
     const float *__restrict__ dt_bias, int32_t softplus, const Tio *__restrict__ z,
     uint32_t seed_lo, uint32_t seed_hi, int32_t rounds, int32_t H, int32_t G, int32_t ybf) {
     constexpr int P = 64;
-    constexpr int LPR = N / 4;         // lanes per state row
+    constexpr int EPL = 8;             // state elements per lane (16 bytes)
+    constexpr int LPR = N / EPL;       // lanes per state row
     constexpr int RPI = 64 / LPR;      // rows per wavefront iteration
     constexpr int ITER = 16 / RPI;     // rows per lane
     const int64_t bh = blockIdx.x;
@@ -107,26 +110,37 @@ __global__ __launch_bounds__(256) void decode_lowp_kernel(
     if (softplus && dtv <= 20.f) dtv = log1pf(expf(dtv));
     const float dA = fast_exp2(A[h] * dtv * kLog2e);
     const float Dh = D[h];
-    const float4 Bv = load4(B + (b * G + g) * N + 4 * sub);
-    const float4 Cv = load4(C + (b * G + g) * N + 4 * sub);
+    float bb[EPL], cc[EPL];
+    {
+        const Tio *Bp = B + (b * G + g) * N + EPL * sub, *Cp = C + (b * G + g) * N + EPL * sub;
+        const float4 b0 = load4(Bp), b1 = load4(Bp + 4), c0 = load4(Cp), c1 = load4(Cp + 4);
+        const float bv[EPL] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+        const float cv[EPL] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) {
+            bb[e] = bv[e];
+            cc[e] = cv[e];
+        }
+    }
 
     uint16_t *st = state + bh * (int64_t)(P * N);
-    uint2 sv[ITER];
+    uint4 sv[ITER];
     float xv[ITER], zv[ITER], sc[ITER];
 #pragma unroll
     for (int k = 0; k < ITER; ++k) {
         const int p = 16 * wave + RPI * k + rw;
-        sv[k] = load_nt(st + p * N + 4 * sub);
+        sv[k] = load_nt8(st + p * N + EPL * sub);
         xv[k] = load1(x + bh * P + p);
         if constexpr (GATE) zv[k] = load1(z + bh * P + p);
         if constexpr (FMT == FMT_INT16) sc[k] = scale[bh * P + p];
     }
-    // the random bits of this lane's 4 elements in each of its rows
+    // the random bits of this lane's 8 elements in each of its rows: one
+    // Philox block per row, each word serving two elements
     uint32_t rb[FMT == FMT_F16_SR ? ITER : 1][4];
     if constexpr (FMT == FMT_F16_SR) {
 #pragma unroll
         for (int k = 0; k < ITER; ++k) {
-            const uint64_t first = (uint64_t)(bh * P + 16 * wave + RPI * k + rw) * N + 4 * sub;
+            const uint64_t first = (uint64_t)(bh * P + 16 * wave + RPI * k + rw) * N + EPL * sub;
             rb[k][0] = (uint32_t)first;
             rb[k][1] = (uint32_t)(first >> 32);
             rb[k][2] = 0u;
@@ -137,54 +151,61 @@ __global__ __launch_bounds__(256) void decode_lowp_kernel(
 #pragma unroll
     for (int k = 0; k < ITER; ++k) {
         const int p = 16 * wave + RPI * k + rw;
-        float s[4];
-        const uint32_t w[4] = {sv[k].x & 0xffffu, sv[k].x >> 16, sv[k].y & 0xffffu,
-                               sv[k].y >> 16};
+        const uint32_t wd[4] = {sv[k].x, sv[k].y, sv[k].z, sv[k].w};
+        float s[EPL];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
+        for (int e = 0; e < EPL; ++e) {
+            const uint32_t w = (e & 1) ? wd[e >> 1] >> 16 : wd[e >> 1] & 0xffffu;
             if constexpr (FMT == FMT_BF16)
-                s[e] = __uint_as_float(w[e] << 16);
+                s[e] = __uint_as_float(w << 16);
             else if constexpr (FMT == FMT_INT16)
-                s[e] = (float)(int16_t)w[e] * sc[k];
+                s[e] = (float)(int16_t)w * sc[k];
             else
-                s[e] = half_bits_to_f32(w[e]);
+                s[e] = half_bits_to_f32(w);
         }
         const float u = dtv * xv[k];
-        const float bb[4] = {Bv.x, Bv.y, Bv.z, Bv.w};
+        float part = 0.f;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) s[e] = dA * s[e] + u * bb[e];
-        float part = s[0] * Cv.x + s[1] * Cv.y + s[2] * Cv.z + s[3] * Cv.w;
-        part = group_sum<LPR>(part);   // the row's sum, in its last lane
+        for (int e = 0; e < EPL; ++e) {
+            s[e] = dA * s[e] + u * bb[e];
+            part = fmaf(s[e], cc[e], part);
+        }
+        part = group_sum<LPR>(part);   // the row's sum, in every lane of the row
         float out = part + Dh * xv[k];
         if constexpr (GATE) out *= fast_silu(zv[k]);
         if (sub == LPR - 1) store_y1(y, bh * P + p, out, ybf != 0);
 
-        uint32_t o[4];
+        uint32_t o[EPL];
         if constexpr (FMT == FMT_BF16) {
-            const uint32_t lo = pack_bf16x2(s[0], s[1]), hi = pack_bf16x2(s[2], s[3]);
-            o[0] = lo & 0xffffu;
-            o[1] = lo >> 16;
-            o[2] = hi & 0xffffu;
-            o[3] = hi >> 16;
+#pragma unroll
+            for (int e = 0; e < EPL; e += 2) {
+                const uint32_t w = pack_bf16x2(s[e], s[e + 1]);
+                o[e] = w & 0xffffu;
+                o[e + 1] = w >> 16;
+            }
         } else if constexpr (FMT == FMT_F16_RN) {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) o[e] = f32_to_half_rn(s[e]);
+            for (int e = 0; e < EPL; ++e) o[e] = f32_to_half_rn(s[e]);
         } else if constexpr (FMT == FMT_F16_SR) {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) o[e] = f32_to_half_sr(s[e], rb[k][e] & 0x1FFFu);
+            for (int e = 0; e < EPL; ++e)
+                o[e] = f32_to_half_sr(s[e], (rb[k][e >> 1] >> (16 * (e & 1))) & 0x1FFFu);
         } else {   // FMT_INT16
-            float m = fmaxf(fmaxf(fabsf(s[0]), fabsf(s[1])), fmaxf(fabsf(s[2]), fabsf(s[3])));
+            float m = 0.f;
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) m = fmaxf(m, fabsf(s[e]));
             m = group_max<LPR>(m);
             const bool zero = m == 0.f;
             const float enc = 32767.f / (zero ? 1.f : m);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
+            for (int e = 0; e < EPL; ++e) {
                 const float q = fminf(fmaxf(rintf(s[e] * enc), -32767.f), 32767.f);
                 o[e] = zero ? 0u : (uint32_t)(uint16_t)(int16_t)q;
             }
             if (sub == 0) scale[bh * P + p] = zero ? 0.f : 1.f / enc;
         }
-        store_nt(st + p * N + 4 * sub, make_uint2(o[0] | (o[1] << 16), o[2] | (o[3] << 16)));
+        store_nt(st + p * N + EPL * sub, make_uint4(o[0] | (o[1] << 16), o[2] | (o[3] << 16),
+                                                    o[4] | (o[5] << 16), o[6] | (o[7] << 16)));
     }
 }
 

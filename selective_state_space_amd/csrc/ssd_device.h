@@ -65,6 +65,10 @@ __device__ __forceinline__ void store_nt(uint16_t *p, uint2 v) {
     const u32x2 w = {v.x, v.y};
     __builtin_nontemporal_store(w, reinterpret_cast<u32x2 *>(p));
 }
+__device__ __forceinline__ void store_nt(uint16_t *p, uint4 v) {   // 8 16-bit elements
+    const u32x4 w = {v.x, v.y, v.z, v.w};
+    __builtin_nontemporal_store(w, reinterpret_cast<u32x4 *>(p));
+}
 
 // Output stores: y in float32, or in bf16 (round to nearest even) when the
 // caller asked for y in the io dtype.  ybf is uniform over the launch.
@@ -163,12 +167,12 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, ui
                                              0x00020000);
 }
 
-// Sum over each group of LPR = 16 or 32 consecutive lanes by DPP moves (VALU
-// operand modifiers, no LDS crossbar round trip): butterflies inside quads,
-// then the half-row and row mirrors leave every lane of a 16-lane row with the
-// row's sum; for 32-lane groups, row_bcast:15 adds row 0's (row 2's) sum into
-// row 1 (row 3).  The group's sum is valid in its last lane, LPR - 1 (for
-// LPR = 16, in every lane).
+// Sum over each group of LPR = 8, 16 or 32 consecutive lanes by DPP moves
+// (VALU operand modifiers, no LDS crossbar round trip): butterflies inside
+// quads, then the half-row mirror leaves every lane of an 8-lane group with
+// its sum, the row mirror every lane of a 16-lane row; for 32-lane groups,
+// row_bcast:15 adds row 0's (row 2's) sum into row 1 (row 3).  The group's sum
+// is valid in its last lane, LPR - 1 (for LPR = 8 and 16, in every lane).
 template <int CTRL, int ROW_MASK = 0xf>
 __device__ __forceinline__ float dpp_mov(float v) {
     return __int_as_float(
@@ -176,11 +180,11 @@ __device__ __forceinline__ float dpp_mov(float v) {
 }
 template <int LPR>
 __device__ __forceinline__ float group_sum(float v) {
-    static_assert(LPR == 16 || LPR == 32, "16- or 32-lane groups");
+    static_assert(LPR == 8 || LPR == 16 || LPR == 32, "8-, 16- or 32-lane groups");
     v += dpp_mov<0xB1>(v);    // quad_perm [1,0,3,2]
     v += dpp_mov<0x4E>(v);    // quad_perm [2,3,0,1]
     v += dpp_mov<0x141>(v);   // row_half_mirror
-    v += dpp_mov<0x140>(v);   // row_mirror
+    if constexpr (LPR >= 16) v += dpp_mov<0x140>(v);   // row_mirror
     if constexpr (LPR == 32) v += dpp_mov<0x142, 0xa>(v);   // row_bcast:15 into rows 1, 3
     return v;
 }
@@ -197,15 +201,16 @@ __device__ __forceinline__ float wave_inclusive_sum(float v) {
     v += dpp_mov<0x143, 0xc>(v);    // row_bcast:31 into rows 2, 3
     return v;
 }
-// The maximum over each group of LPR = 16 or 32 lanes, in every lane of it:
-// the same DPP steps within 16-lane rows, then one swap of neighbouring rows.
+// The maximum over each group of LPR = 8, 16 or 32 lanes, in every lane of it:
+// the same DPP steps within 8- or 16-lane groups, then one swap of
+// neighbouring rows.
 template <int LPR>
 __device__ __forceinline__ float group_max(float v) {
-    static_assert(LPR == 16 || LPR == 32, "16- or 32-lane groups");
+    static_assert(LPR == 8 || LPR == 16 || LPR == 32, "8-, 16- or 32-lane groups");
     v = fmaxf(v, dpp_mov<0xB1>(v));
     v = fmaxf(v, dpp_mov<0x4E>(v));
     v = fmaxf(v, dpp_mov<0x141>(v));
-    v = fmaxf(v, dpp_mov<0x140>(v));
+    if constexpr (LPR >= 16) v = fmaxf(v, dpp_mov<0x140>(v));
     if constexpr (LPR == 32) v = fmaxf(v, __shfl_xor(v, 16, 64));
     return v;
 }

@@ -31,17 +31,29 @@ def test_philox_known_answers(ctr, key, out):
     assert words(sf.philox4x32(np.array(ctr, np.uint64), np.array(key, np.uint64))) == out
 
 
-def test_state_bits_take_one_block_per_four_elements():
+def halves13(blk):
+    """The 8 element fields of one block: word k // 2, low half for even k,
+    high half for odd k, 13 bits each (written out element by element)."""
+    out = []
+    for wd in blk:
+        out.append(int(wd) & 0x1FFF)
+        out.append((int(wd) >> 16) & 0x1FFF)
+    return out
+
+
+def test_state_bits_take_one_block_per_eight_elements():
     seed = 0x123456789ABCDEF0
-    r = sf.state_random_bits(4 * 1000 + 8, seed)
+    r = sf.state_random_bits(8 * 1000 + 16, seed)
     key = np.array([seed & 0xFFFFFFFF, seed >> 32], np.uint64)
-    for first in (0, 4, 1236, 4004):
+    for first in (0, 8, 1240, 8008):
         blk = sf.philox4x32(np.array([first, 0, 0, 0], np.uint64), key)
-        assert [int(v) for v in r[first:first + 4]] == [int(w) & 0x1FFF for w in blk]
+        assert [int(v) for v in r[first:first + 8]] == halves13(blk)
+    # bits 13..15 and 29..31 of each word are never used
+    assert int(r.max()) < 8192
     # past 2^32 elements the index's high word is the counter's second word
-    r = sf.state_random_bits(8, seed, start=(1 << 32) + 4)
-    blk = sf.philox4x32(np.array([8, 1, 0, 0], np.uint64), key)
-    assert [int(v) for v in r[4:]] == [int(w) & 0x1FFF for w in blk]
+    r = sf.state_random_bits(16, seed, start=(1 << 32) + 8)
+    blk = sf.philox4x32(np.array([16, 1, 0, 0], np.uint64), key)
+    assert [int(v) for v in r[8:]] == halves13(blk)
 
 
 ALL_R = np.arange(8192)
