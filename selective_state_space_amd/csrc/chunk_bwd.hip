@@ -632,8 +632,10 @@ __global__ __launch_bounds__(256) void bwd_dbdc_kernel(
 }
 
 // ---- bwd_dc_mfma: dC on bf16 MFMA (bf16 io), and M for bwd_db_mfma ---------
-// One block of 16*WPB rows k of one (b, c, g) per workgroup; wavefront w owns
-// the 16-row strip r0+16w..+15: per head, the strip's dy rows times the x
+// One block of WPB 16-row strips k of one (b, c, g) per workgroup (with two
+// blocks per chunk, the outer strips in one and the middle ones in the other,
+// which balances their causal tiles), one strip per wavefront: per head, the
+// strip's dy rows times the x
 // rows of the chunk (decayed and masked into M), and the inter term
 // exp2(G) dy h_prev^T; after the heads, M B.  Per head the x rows and h_prev
 // (transposed to [n][p]) are staged in LDS; the strip's own rows are the A
@@ -669,12 +671,18 @@ __global__ __launch_bounds__(64 * WPB) void bwd_dc_mfma_kernel(
     const int32_t c = (int32_t)(bc % nc);
     const int64_t b = bc / nc;
     const int hpg = H / G;
-    const int r0 = RB * rb;
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
     const int m = lane & 15, q = lane >> 4;
+    // this wavefront's 16-row strip: with two row blocks per chunk, block 0
+    // takes the first and the last WPB/2 strips and block 1 the middle ones,
+    // so both hold the same number of causal tiles
+    constexpr int NSTRIP = L / 16;
+    const int strip = (L / RB == 2) ? (rb == 0 ? (w < WPB / 2 ? w : NSTRIP - WPB + w) : WPB / 2 + w) : w;
+    const int srow = 16 * strip;
     const int64_t tc = (int64_t)c * L;
-    const int c_hi = r0 + RB;                         // columns [0, c_hi): on or below the diagonal
-    const int arow = r0 + 16 * w + m;                 // this lane's A-operand row
+    // columns [0, c_hi): on or below the diagonal of the block's last strip
+    const int c_hi = (L / RB == 2 && rb == 1) ? 16 * (WPB / 2 + WPB) : L;
+    const int arow = srow + m;                        // this lane's A-operand row
     const int64_t ta = tc + arow;
     f32x4 Macc[NT];
     f32x4 dacc[NN];
@@ -761,10 +769,10 @@ __global__ __launch_bounds__(64 * WPB) void bwd_dc_mfma_kernel(
         // A operands: the strip's dy rows (plain, and times exp2(G) for the inter term)
         const float sc = fast_exp2(Gs[arow]);
         // row factors of the off-diagonal decay, against the strip's first row
-        const float gedge = Gs[r0 + 16 * w];
+        const float gedge = Gs[srow];
         float rowf[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) rowf[e] = fast_exp2(Gs[r0 + 16 * w + 4 * q + e] - gedge);
+        for (int e = 0; e < 4; ++e) rowf[e] = fast_exp2(Gs[srow + 4 * q + e] - gedge);
         bf16x8 aS[2], aSl[2], aI[2], aIl[2];
 #pragma unroll
         for (int st = 0; st < 2; ++st) {
@@ -785,7 +793,7 @@ __global__ __launch_bounds__(64 * WPB) void bwd_dc_mfma_kernel(
         // S tiles on or below the diagonal, decayed and masked into M
 #pragma unroll
         for (int jt = 0; jt < NT; ++jt) {
-            if (16 * jt > r0 + 16 * w) continue;      // wholly masked
+            if (16 * jt > srow) continue;             // wholly masked
             f32x4 s = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int st = 0; st < 2; ++st) {
@@ -796,11 +804,11 @@ __global__ __launch_bounds__(64 * WPB) void bwd_dc_mfma_kernel(
             }
             const int col = 16 * jt + m;
             const float gc = Gs[col], dc = DTs[col];
-            if (16 * jt == r0 + 16 * w) {
+            if (16 * jt == srow) {
                 // the diagonal tile: the exact pairwise decay, masked
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const int row = r0 + 16 * w + 4 * q + e;
+                    const int row = srow + 4 * q + e;
                     Macc[jt][e] += row >= col ? fast_exp2(Gs[row] - gc) * dc * s[e] : 0.f;
                 }
             } else {
@@ -829,7 +837,7 @@ __global__ __launch_bounds__(64 * WPB) void bwd_dc_mfma_kernel(
     // into MT[col][row] for the dB pass: lane (m, q) holds rows 4q..4q+3 of
     // column 16 jt + m
     {
-        float *mt = MT + bcg * (int64_t)(L * L) + r0 + 16 * w + 4 * q;
+        float *mt = MT + bcg * (int64_t)(L * L) + srow + 4 * q;
 #pragma unroll
         for (int jt = 0; jt < NT; ++jt)
             *reinterpret_cast<float4 *>(mt + (int64_t)(16 * jt + m) * L) =
@@ -886,7 +894,7 @@ __global__ __launch_bounds__(64 * WPB) void bwd_dc_mfma_kernel(
     }
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-        const int64_t t = tc + r0 + 16 * w + 4 * q + e;
+        const int64_t t = tc + srow + 4 * q + e;
         if (t < T)
 #pragma unroll
             for (int nt = 0; nt < NN; ++nt)
