@@ -349,24 +349,33 @@ __global__ __launch_bounds__(256) void bwd_cb_mfma_kernel(const uint16_t *__rest
     const int m = lane & 15, q = lane >> 4;
     const int64_t tc = (int64_t)c * L;
     const int k0 = 64 * kb + 16 * w;
-    const int64_t tk = tc + k0 + m;
+    // B and C rows of the chunk through buffers whose range ends at the
+    // sequence end (rows past it read 0), so that every load of the block
+    // goes out before any is used
+    const uint32_t nvt = (uint32_t)(T - tc < L ? T - tc : L), rowb = (uint32_t)(G * N * 2);
+    const int64_t row0 = ((b * T + tc) * G + g) * N;
+    const auto rc = make_rsrc(C + row0, nvt * rowb), rbb = make_rsrc(B + row0, nvt * rowb);
+    auto ld = [&](__amdgpu_buffer_rsrc_t r, int row, int ks) {
+        const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, (uint32_t)row * rowb + 2u * (32 * ks + 8 * q), 0, 0);
+        return __builtin_bit_cast(bf16x8, v);
+    };
     bf16x8 ca[NK];
 #pragma unroll
-    for (int ks = 0; ks < NK; ++ks)
-        ca[ks] = as_bf16x8(tk < T ? *reinterpret_cast<const uint4 *>(C + ((b * T + tk) * G + g) * N + 32 * ks + 8 * q)
-                                  : make_uint4(0u, 0u, 0u, 0u));
+    for (int ks = 0; ks < NK; ++ks) ca[ks] = ld(rc, k0 + m, ks);
     const int64_t plane = (int64_t)gridDim.x / NTRI * L * L;   // Bt*nc*G*L*L
     const int64_t base = bcg * (int64_t)(L * L);
+    bf16x8 bb[4][NK];
+#pragma unroll
+    for (int jt = 0; jt < 4; ++jt)
+#pragma unroll
+        for (int ks = 0; ks < NK; ++ks) bb[jt][ks] = ld(rbb, 64 * jb + 16 * jt + m, ks);
 #pragma unroll
     for (int jt = 0; jt < 4; ++jt) {
         const int j0 = 64 * jb + 16 * jt;
-        const int64_t tj = tc + j0 + m;
         f32x4 d = f32x4{0.f, 0.f, 0.f, 0.f}, dtr = d;
 #pragma unroll
         for (int ks = 0; ks < NK; ++ks) {
-            const bf16x8 bv = as_bf16x8(
-                tj < T ? *reinterpret_cast<const uint4 *>(B + ((b * T + tj) * G + g) * N + 32 * ks + 8 * q)
-                       : make_uint4(0u, 0u, 0u, 0u));
+            const bf16x8 bv = bb[jt][ks];
             d = mfma16x16x32(ca[ks], bv, d);       // rows k, column j
             dtr = mfma16x16x32(bv, ca[ks], dtr);   // rows j, column k
         }
@@ -1572,67 +1581,96 @@ __global__ __launch_bounds__(256) void bwd_scalars_kernel(
     const float *__restrict__ tok, const float *__restrict__ DTws, const float *__restrict__ A,
     const double *__restrict__ bnd, float *__restrict__ ddt, double *__restrict__ part,
     int64_t T, int32_t H, int32_t nc, int64_t ntok, int64_t nbh) {
-    // tiles of 1024 tokens from the last to the first; a thread takes 4
-    // consecutive tokens of a tile (one 16-byte load per plane, coalesced), the
-    // tile's 256 segment sums are suffix-scanned in parallel, and the running
-    // carry holds the boundary term plus everything after the tile
-    constexpr int TT = 1024;
-    __shared__ double sc[2][256];
-    __shared__ double red[2][256];
+    // tiles of 2048 tokens from the last to the first; a thread takes 8
+    // consecutive tokens of a tile (two 16-byte loads per plane, coalesced);
+    // the tile's 256 segment sums are suffix-scanned within each wavefront by
+    // lane shuffles and across the four wavefronts through LDS, and the
+    // running carry holds the boundary term plus everything after the tile.
+    // Each tile's planes are loaded while the previous tile is scanned.
+    constexpr int TPT = 8, TT = 256 * TPT;
+    __shared__ double wsum[2][4];
+    __shared__ double red[2][4];
     const int64_t bh = blockIdx.x;
     const int64_t b = bh / H;
     const int32_t h = (int32_t)(bh % H);
-    const int tid = threadIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int64_t Tp = (int64_t)nc * L;             // padded tokens: r, x.U, dy.x, dt are 0
     const float *xu = tok + bh * Tp, *r = tok + ntok + bh * Tp, *dyx = tok + 2 * ntok + bh * Tp,
                 *DT = DTws + bh * Tp;
     const double Ah = (double)A[h];
     double carry = bnd[bh], da = 0.0, dd = 0.0;
-    for (int64_t tl = (Tp + TT - 1) / TT - 1; tl >= 0; --tl) {
-        const int64_t t0 = tl * TT + 4 * tid;
-        float4 rv = make_float4(0.f, 0.f, 0.f, 0.f), xv = rv, dv = rv, yv = rv;
-        if (t0 < Tp) {                               // Tp is a multiple of 64
-            rv = *reinterpret_cast<const float4 *>(r + t0);
-            xv = *reinterpret_cast<const float4 *>(xu + t0);
-            dv = *reinterpret_cast<const float4 *>(DT + t0);
-            yv = *reinterpret_cast<const float4 *>(dyx + t0);
-        }
-        const double rr[4] = {rv.x, rv.y, rv.z, rv.w}, xx[4] = {xv.x, xv.y, xv.z, xv.w},
-                     dtt[4] = {dv.x, dv.y, dv.z, dv.w}, yy[4] = {yv.x, yv.y, yv.z, yv.w};
-        sc[0][tid] = ((rr[0] + rr[1]) + rr[2]) + rr[3];
-        __syncthreads();
-        int cur = 0;
-        for (int d = 1; d < 256; d <<= 1) {         // inclusive suffix sums (Hillis-Steele)
-            const double v = sc[cur][tid] + (tid + d < 256 ? sc[cur][tid + d] : 0.0);
-            sc[cur ^ 1][tid] = v;
-            cur ^= 1;
-            __syncthreads();
-        }
-        double s = carry + (tid + 1 < 256 ? sc[cur][tid + 1] : 0.0);
-        const double total = sc[cur][0];
+    float4 nv[4][2];                                 // planes r, x.U, dt, dy.x of the next tile
+    auto load_tile = [&](int64_t tl) {
+        const int64_t t0 = tl * TT + TPT * tid;
+        const bool ok = tl >= 0 && t0 < Tp;          // Tp is a multiple of 64
+        const float *src[4] = {r, xu, DT, dyx};
 #pragma unroll
-        for (int i = 3; i >= 0; --i) {
-            s += rr[i];
-            if (t0 + i < T) ddt[(b * T + t0 + i) * H + h] = (float)(xx[i] + Ah * s);
-            da += dtt[i] * s;
+        for (int k = 0; k < 4; ++k)
+#pragma unroll
+            for (int u = 0; u < 2; ++u)
+                nv[k][u] = ok ? *reinterpret_cast<const float4 *>(src[k] + t0 + 4 * u)
+                              : make_float4(0.f, 0.f, 0.f, 0.f);
+    };
+    const int64_t ntl = (Tp + TT - 1) / TT;
+    load_tile(ntl - 1);
+    for (int64_t tl = ntl - 1; tl >= 0; --tl) {
+        const int64_t t0 = tl * TT + TPT * tid;
+        double rr[TPT], xx[TPT], dtt[TPT], yy[TPT];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const float4 a = nv[0][u], x4 = nv[1][u], d4 = nv[2][u], y4 = nv[3][u];
+            rr[4 * u] = a.x; rr[4 * u + 1] = a.y; rr[4 * u + 2] = a.z; rr[4 * u + 3] = a.w;
+            xx[4 * u] = x4.x; xx[4 * u + 1] = x4.y; xx[4 * u + 2] = x4.z; xx[4 * u + 3] = x4.w;
+            dtt[4 * u] = d4.x; dtt[4 * u + 1] = d4.y; dtt[4 * u + 2] = d4.z; dtt[4 * u + 3] = d4.w;
+            yy[4 * u] = y4.x; yy[4 * u + 1] = y4.y; yy[4 * u + 2] = y4.z; yy[4 * u + 3] = y4.w;
+        }
+        load_tile(tl - 1);
+        double seg = 0.0;
+#pragma unroll
+        for (int i = 0; i < TPT; ++i) seg += rr[i];
+        // inclusive suffix sum over the wavefront's lanes
+        double v = seg;
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            const double o = __shfl_down(v, d, 64);
+            v += lane + d < 64 ? o : 0.0;
+        }
+        const int buf = (int)(tl & 1);
+        if (lane == 0) wsum[buf][wv] = v;           // the wavefront's total
+        __syncthreads();
+        double after = 0.0, total = 0.0;            // later wavefronts' totals; the tile's
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const double t = wsum[buf][k];
+            total += t;
+            after += k > wv ? t : 0.0;
+        }
+        // the sum over every token after this thread's segment, then its tokens last to first
+        double sfx = carry + after + (v - seg);
+#pragma unroll
+        for (int i = TPT - 1; i >= 0; --i) {
+            sfx += rr[i];
+            if (t0 + i < T) ddt[(b * T + t0 + i) * H + h] = (float)(xx[i] + Ah * sfx);
+            da += dtt[i] * sfx;
             dd += yy[i];
         }
         carry += total;
-        __syncthreads();                             // sc is rewritten by the next tile
     }
-    red[0][tid] = da;
-    red[1][tid] = dd;
+    // block sums of the dA and dD parts: wavefront shuffles, then the four
+    // wavefronts in order
+#pragma unroll
+    for (int d = 32; d > 0; d >>= 1) {
+        da += __shfl_down(da, d, 64);
+        dd += __shfl_down(dd, d, 64);
+    }
+    if (lane == 0) {
+        red[0][wv] = da;
+        red[1][wv] = dd;
+    }
     __syncthreads();
-    for (int st = 128; st > 0; st >>= 1) {
-        if (tid < st) {
-            red[0][tid] += red[0][tid + st];
-            red[1][tid] += red[1][tid + st];
-        }
-        __syncthreads();
-    }
     if (tid == 0) {
-        part[bh] = red[0][0];
-        part[nbh + bh] = red[1][0];
+        part[bh] = ((red[0][0] + red[0][1]) + red[0][2]) + red[0][3];
+        part[nbh + bh] = ((red[1][0] + red[1][1]) + red[1][2]) + red[1][3];
     }
 }
 
