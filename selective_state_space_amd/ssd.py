@@ -9,11 +9,22 @@ it never falls back to another implementation.
 
 The functions carry the C names:
 
-* :func:`ssd_chunked_fwd` -- chunked forward (the four stages in order);
+* :func:`ssd_chunked_fwd` -- chunked forward, with the layer options (dt bias,
+  softplus, z gate, y in the io dtype) when given;
+* :func:`ssd_chunked_fwd_noalloc` -- the same on the library's static
+  workspace (no allocation in the library);
 * :func:`ssd_chunk_cumsum`, :func:`ssd_chunk_state`, :func:`ssd_state_passing`,
-  :func:`ssd_chunk_scan` -- the stages one at a time, on a shared workspace;
+  :func:`ssd_state_fwd`, :func:`ssd_chunk_scan` -- the stages one at a time,
+  on a shared workspace;
 * :func:`ssd_decode_step` -- one recurrent token, state updated in place;
-* :func:`ssd_chunked_fwd_workspace_size`, :func:`ssd_chunked_fwd_workspace_layout`.
+* :func:`ssd_decode_multi` -- K tokens per sequence, with snapshots and
+  draft-tree parents;
+* :func:`ssd_decode_step_lp` -- the decode step on a 16-bit state;
+* :func:`ssd_chunked_bwd` -- every gradient of the chunked forward;
+* :func:`ssd_chunked_fwd_workspace_size`, :func:`ssd_chunked_fwd_workspace_layout`,
+  :func:`ssd_chunked_bwd_workspace_size`, :func:`fwd_path` and
+  :func:`set_path_override` (which path the forward takes, and a switch for
+  tests).
 """
 
 from __future__ import annotations
