@@ -53,6 +53,55 @@ def test_backward_against_oracle(io, L, N):
     compare(g, ref, io)
 
 
+# --- the method's degenerate cases: decay so strong that exp underflows
+# within a token, no decay at all (causal linear attention), and dt = 0 ----
+
+@pytest.mark.parametrize("io", [gen.F32, gen.BF16])
+@pytest.mark.parametrize("L", [64, 256])
+def test_backward_strong_decay(io, L):
+    # heads from no decay to exp(-1000) per token: every factored decay and
+    # the per-element diagonal ones must stay finite where exp2 underflows
+    log("bwd strong decay", io, "L", L)
+    inp = gen.make_small(1, 2 * L + 11, 4, 64, 128, 1, io, init_state=True, seed=71 + L)
+    inp.A[:] = np.array([-2000.0, -30.0, -1.0, -1e-3], np.float32)
+    inp.dt[:] = 0.5
+    dy, dfin = grads_inputs(inp, 7)
+    g, ref = run_both(inp, io, L, dy, dfin)
+    for k in NAMES:
+        assert torch.isfinite(g[k]).all(), k
+    compare(g, ref, io)
+
+
+@pytest.mark.parametrize("io", [gen.F32, gen.BF16])
+@pytest.mark.parametrize("L", [64, 256])
+def test_backward_no_decay(io, L):
+    # A = 0: the forward is causal linear attention, every decay factor is 1
+    log("bwd A = 0", io, "L", L)
+    inp = gen.make_small(2, L + 37, 4, 64, 64, 2, io, init_state=True, seed=73 + L)
+    inp.A[:] = 0
+    dy, dfin = grads_inputs(inp, 9)
+    g, ref = run_both(inp, io, L, dy, dfin)
+    compare(g, ref, io)
+
+
+@pytest.mark.parametrize("io", [gen.F32, gen.BF16])
+def test_backward_zero_dt(io):
+    # dt = 0: the state stays init_state at every token, so y_t = C_t init +
+    # D x_t, and in closed form dinit = dfinal + sum_t dy_t (outer) C_t and
+    # dx = D dy; ddt, dA, dB and dC are still defined (against the oracle)
+    log("bwd dt = 0", io)
+    inp = gen.make_small(1, 300, 4, 64, 128, 2, io, init_state=True, seed=79)
+    inp.dt[:] = 0
+    dy, dfin = grads_inputs(inp, 11)
+    g, ref = run_both(inp, io, 128, dy, dfin)
+    compare(g, ref, io)
+    H = inp.x.shape[2]
+    Cg = np.repeat(inp.C.astype(np.float64), H // inp.C.shape[2], axis=2)   # [Bt, T, H, N]
+    closed = dfin + np.einsum("bthp,bthn->bhpn", dy.astype(np.float64), Cg)
+    assert_close(host(g["dinit"]), closed, io, "dinit closed form")
+    assert_close(host(g["dx"]), dy * inp.D.reshape(1, 1, -1, 1), io, "dx = D dy")
+
+
 @pytest.mark.parametrize("fwd_rows,adj_rows", [("0", ""), ("4", "1"), ("2", "2"), ("1", "4")])
 @pytest.mark.parametrize("L", [64, 256])
 def test_state_stage_paths(force_path, fwd_rows, adj_rows, L):

@@ -118,3 +118,26 @@ def test_scalar_closed_form():
                dinit=dy * C * a)
     for k, v in exp.items():
         assert abs(float(g[k].reshape(-1)[0]) - v) <= 1e-12 * max(1.0, abs(v)), (k, g[k], v)
+
+
+def test_zero_dt_closed_form():
+    """dt = 0 at every token: the state is init_state throughout, so
+    y_t = C_t . init + D x_t.  Then dinit = dfinal + sum_t dy_t (outer) C_t,
+    dx = D dy, dD = sum dy . x, dB = 0 (B enters only through dt), and
+    dC_t = sum over the group's heads of dy_t . init."""
+    th, dy, dfin = problem(Bt=2, T=9, H=4, P=3, N=5, G=2, seed=3)
+    th["dt"][:] = 0
+    g = oracle.token_bwd(th["x"], th["dt"], th["A"], th["B"], th["C"], th["D"], dy,
+                         th["init"], dfin)
+    Bt, T, H, P = th["x"].shape
+    G, N = th["C"].shape[2], th["C"].shape[3]
+    hpg = H // G
+    dy64, x64, C64 = (a.astype(np.float64) for a in (dy, th["x"], th["C"]))
+    Cg = np.repeat(C64, hpg, axis=2)                             # [Bt, T, H, N]
+    dinit = dfin + np.einsum("bthp,bthn->bhpn", dy64, Cg)
+    dC = np.einsum("bthp,bhpn->bthn", dy64, th["init"]).reshape(Bt, T, G, hpg, N).sum(axis=3)
+    exp = dict(dinit=dinit, dx=dy64 * th["D"].astype(np.float64).reshape(1, 1, H, 1),
+               dD=np.einsum("bthp,bthp->h", dy64, x64), dB=np.zeros((Bt, T, G, N)), dC=dC)
+    for k, v in exp.items():
+        np.testing.assert_allclose(np.asarray(g[k], np.float64).reshape(v.shape), v,
+                                   rtol=1e-12, atol=1e-12, err_msg=k)
