@@ -41,6 +41,36 @@ def test_decode_steps_against_oracle(io, N):
 
 
 @pytest.mark.parametrize("io", [gen.F32, gen.BF16])
+def test_decode_degenerate_decay(io):
+    # heads from exp(-1000) per token (the state is replaced each step) to no
+    # decay (A = 0), and one step with dt = 0 everywhere (the state is kept)
+    w = gen.Workload("dec", 2, 1, 8, 64, 128, 2, 64, io, kind="decode")
+    prm = gen.decode_params(w, 3)
+    prm.A[:] = np.array([-2000.0, -30.0, -1.0, -1e-3, 0.0, 0.0, -1.0, -2000.0], np.float32)
+    rng = np.random.default_rng(13)
+    st0 = (rng.standard_normal((2, 8, 64, 128)) * 0.1).astype(np.float32)
+    state = dev_tensor(st0)
+    ref = st0.astype(np.float64).reshape(16, 64, 128).copy()
+    A, D = dev_tensor(prm.A), dev_tensor(prm.D)
+    ys, yrs = [], []
+    for k in range(5):
+        s = gen.make_decode_step(w, k, prm, 3)
+        if k == 2:
+            s.dt_t[:] = 0
+        else:
+            s.dt_t[:] = 0.5
+        y = ssd.ssd_decode_step(state, dev_tensor(s.x_t, _tdt(io)), dev_tensor(s.dt_t),
+                                dev_tensor(s.B_t, _tdt(io)), dev_tensor(s.C_t, _tdt(io)), A, D)
+        yr = oracle.token_decode(ref, s.x_t, s.dt_t, s.B_t, s.C_t, prm.A, prm.D)
+        ys.append(host(y).reshape(16, 64))
+        yrs.append(yr)
+    torch.cuda.synchronize()
+    assert torch.isfinite(state).all()
+    assert_close(np.stack(ys), np.stack(yrs), io, "degenerate decay y (5 steps)")
+    assert_close(host(state).reshape(16, 64, 128), ref, io, "degenerate decay state")
+
+
+@pytest.mark.parametrize("io", [gen.F32, gen.BF16])
 def test_decode_steps_equal_forward(io):
     # T decode steps from h0 == one chunked forward over the same T tokens
     T = 40

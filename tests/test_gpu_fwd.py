@@ -204,27 +204,40 @@ def test_zero_dt_keeps_state():
     assert torch.equal(fin, torch.from_numpy(inp.init_state).cuda())
 
 
-def test_no_decay_is_causal_linear_attention():
+PATHS = ["0", "4", "fused"]   # four stages, one-pass state stage, fused pass
+
+
+@pytest.mark.parametrize("rows", PATHS)
+@pytest.mark.parametrize("L", [64, 256])
+def test_no_decay_is_causal_linear_attention(rows, L, force_path):
     # A = 0: y = ((C B^T) . M) diag(dt) X + D X, checked against the oracle
+    force_path(rows)
     io = gen.BF16
-    inp = gen.make_small(1, 256, 4, 64, 64, 1, io, seed=59)
+    log("A = 0, path", rows, "L", L)
+    inp = gen.make_small(1, 2 * L + 13, 4, 64, 64, 1, io, init_state=True, seed=59)
     inp.A[:] = 0
-    y, fin = run_fwd(inp, io, 128)
+    y, fin = run_fwd(inp, io, L)
     yr, fr = oracle_full(inp)
     assert_close(host(y), yr, io, "A=0 y")
     assert_close(host(fin), fr, io, "A=0 final")
 
 
-def test_strong_decay_does_not_overflow():
-    # exp2 of the masked (positive) exponents is huge; they must be discarded
+@pytest.mark.parametrize("rows", PATHS)
+@pytest.mark.parametrize("L", [64, 256])
+def test_strong_decay_does_not_overflow(rows, L, force_path):
+    # exp2 of the masked (positive) exponents is huge; they must be discarded,
+    # and heads from no decay to exp(-1000) per token share each launch
+    force_path(rows)
     io = gen.BF16
-    inp = gen.make_small(1, 256, 2, 64, 128, 1, io, seed=61)
-    inp.A[:] = -2000.0
+    log("strong decay, path", rows, "L", L)
+    inp = gen.make_small(1, 2 * L + 13, 4, 64, 128, 1, io, init_state=True, seed=61)
+    inp.A[:] = np.array([-2000.0, -30.0, -1.0, -1e-3], np.float32)
     inp.dt[:] = 0.5
-    y, fin = run_fwd(inp, io, 256)
+    y, fin = run_fwd(inp, io, L)
     yr, fr = oracle_full(inp)
-    assert torch.isfinite(y.float()).all()
+    assert torch.isfinite(y.float()).all() and torch.isfinite(fin).all()
     assert_close(host(y), yr, io, "strong decay y")
+    assert_close(host(fin), fr, io, "strong decay final")
 
 
 # --- the full-size workloads, every (b, h) pair ----------------------------------
