@@ -100,6 +100,41 @@ def test_one_step_bits(fmt, stoch, N):
 
 
 @pytest.mark.parametrize("fmt,stoch", FORMATS)
+def test_degenerate_rows(fmt, stoch):
+    # heads 0 and 3 decay by exp(-1000) (the old state vanishes) and have x = 0
+    # on rows 0..7 of head 0, so those rows become exactly zero (int16: codes 0
+    # and decode scale 0); head 1 has A = 0, head 2 dt = 0 (the state is kept)
+    Bt, H, P, N, G, io = 2, 4, 64, 128, 2, gen.BF16
+    log("lowp degenerate rows", fmt, "stochastic" if stoch else "")
+    st, scale, vals = initial_state(fmt, (Bt, H, P, N), seed=17)
+    rng = np.random.default_rng(3)
+    A = np.array([-2000.0, 0.0, -1.0, -2000.0], np.float32)
+    D = rng.normal(0, 1, H).astype(np.float32)
+    x, dt, B, C = step_inputs(rng, Bt, H, P, N, G, io)
+    dt[:] = np.array([0.5, 0.5, 0.0, 0.5], np.float32)
+    x[:, 0, :8] = 0
+    bf = torch.bfloat16
+    y = ssd.ssd_decode_step_lp(st, dev_tensor(x, bf), dev_tensor(dt), dev_tensor(B, bf),
+                               dev_tensor(C, bf), dev_tensor(A), dev_tensor(D), fmt, scale=scale,
+                               philox_rounds=10 * stoch, seed=77)
+    torch.cuda.synchronize()
+    yr, new, extra = sf.decode_step_lowp(vals, x, dt, B, C, A, D, fmt, seed=77,
+                                         philox_rounds=10 * stoch)
+    assert_close(host(y), yr, io, "y")
+    got = decoded(fmt, st, scale)
+    assert np.all(np.isfinite(got))
+    assert np.all(got[:, 0, :8] == 0) and np.all(new[:, 0, :8] == 0), "zero rows"
+    if fmt == "int16":
+        codes, dec = extra
+        assert np.all(scale.cpu().numpy()[:, 0, :8] == 0) and np.all(dec[:, 0, :8] == 0)
+        dc = np.abs(st.cpu().numpy().astype(np.int64) - codes.astype(np.int64))
+        assert dc.max() <= 1 and float(np.mean(dc != 0)) < 1e-3
+    else:
+        assert float(np.mean(got != new)) < 1e-3
+        assert np.all(np.abs(got - new) <= unit(fmt, new) * (1 + 1e-9))
+
+
+@pytest.mark.parametrize("fmt,stoch", FORMATS)
 @pytest.mark.parametrize("io", [gen.F32, gen.BF16])
 def test_steps_against_oracle(fmt, stoch, io):
     Bt, H, P, N, G, steps = 2, 8, 64, 128, 2, 6

@@ -72,6 +72,24 @@ def test_chain(io, N):
 
 
 @pytest.mark.parametrize("io", [gen.F32, gen.BF16])
+def test_degenerate_decay(io):
+    # heads from exp(-1000) per token to no decay (A = 0), and a token with
+    # dt = 0 (the state is carried unchanged through it), on a chain and on a tree
+    log("multi degenerate decay", io)
+    Bt, K, H = 2, 5, 8
+    x, dt, B, C, A, D, st = small(io, Bt, K, H, 128, 2, seed=23)
+    A[:] = np.array([-2000.0, -30.0, -1.0, -1e-3, 0.0, 0.0, -1.0, -2000.0], np.float32)
+    dt[:] = 0.5
+    dt[:, 2] = 0.0
+    inp = (x, dt, B, C, A, D, st)
+    got = run(io, *inp)
+    assert torch.isfinite(got[1].float()).all() and torch.isfinite(got[2]).all()
+    compare(io, Bt, H, got, reference(*inp))
+    par = np.array([[-1, 0, 0, 2, 1], [-1, 0, 1, 1, 3]], np.int32)
+    compare(io, Bt, H, run(io, *inp, parent=par), reference(*inp, parent=par))
+
+
+@pytest.mark.parametrize("io", [gen.F32, gen.BF16])
 @pytest.mark.parametrize("update", [True, False])
 def test_tree(io, update):
     log("multi tree", io, "update", update)
